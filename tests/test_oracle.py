@@ -1,0 +1,381 @@
+"""Pins for the fp64 oracle (CPU only).
+
+Each test ties the oracle to something other than itself: the scalar brute-force loops,
+closed forms, invariants the layer must satisfy, values fixed by the mathematics
+(tests/golden/), and independent library routines.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+
+from hstu_pointwise_attention_jagged_amd import workloads as wl
+from oracle import brute, hstu_ref as ref
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def _layer(w, x, seq, dims, **kw):
+    return ref.layer_fwd(x, w.weights if hasattr(w, "weights") else w, seq.offsets, seq.timestamps,
+                         dims.num_heads, dims.dqk, dims.dv, dims.ln_eps, **kw)
+
+
+# ----------------------------------------------------------------------------------
+# Brute force
+# ----------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bias,affine", [(False, False), (True, True)])
+def test_brute_matches_vectorised_tiny_config(bias, affine):
+    w = wl.config(0)
+    if bias or affine:
+        w.weights = wl.draw_weights(np.random.default_rng(7), w.dims, bias=bias, affine=affine)
+    d = w.dims
+    y, mid = _layer(w, w.x, w.seq, d, intermediates=True)
+    yb, midb = brute.layer_fwd(w.x, w.weights, w.seq.offsets, w.seq.timestamps,
+                               d.num_heads, d.dqk, d.dv, d.ln_eps, intermediates=True)
+    yb = np.array(yb)
+    assert np.abs(y - yb).max() <= 1e-9 * max(1.0, np.abs(yb).max())
+    o, ob = mid["o"], np.array(midb["o"])
+    assert np.abs(o - ob).max() <= 1e-9 * np.abs(ob).max()
+
+
+@pytest.mark.parametrize("seed", [11, 12, 13])
+def test_brute_matches_vectorised_random(seed):
+    rng = np.random.default_rng(seed)
+    H = int(rng.integers(1, 4))
+    dh = int(rng.choice([2, 4, 8]))
+    dims = wl.LayerDims(d_model=12, num_heads=H, dqk=dh, dv=dh,
+                        pos_buckets=int(rng.integers(2, 9)), time_buckets=int(rng.integers(2, 9)),
+                        rab_heads=int(rng.choice([1, H])))
+    lengths = rng.integers(0, 9, size=5)
+    lengths[1] = 0
+    w = wl.random_layer(seed, lengths, dims, bias=True, affine=True, rab_std=0.5)
+    # large time gaps so the clamp of the log bucket is hit too
+    w.seq.timestamps = (w.seq.timestamps.astype(np.int64) * 37).astype(np.int32)
+    y = _layer(w, w.x, w.seq, dims)
+    yb = np.array(brute.layer_fwd(w.x, w.weights, w.seq.offsets, w.seq.timestamps,
+                                  H, dh, dh, dims.ln_eps))
+    if yb.size:
+        assert np.abs(y - yb).max() <= 1e-9 * max(1.0, np.abs(yb).max())
+
+
+# ----------------------------------------------------------------------------------
+# Jagged handling and causality
+# ----------------------------------------------------------------------------------
+
+def _small_dims():
+    return wl.LayerDims(d_model=32, num_heads=2, dqk=16, dv=16)
+
+
+def test_jagged_equals_each_sequence_alone():
+    dims = _small_dims()
+    lengths = [7, 0, 33, 1, 60, 12]
+    w = wl.random_layer(21, lengths, dims, bias=True, affine=True)
+    y = _layer(w, w.x, w.seq, dims)
+    off = w.seq.offsets
+    for b in range(len(lengths)):
+        s0, s1 = off[b], off[b + 1]
+        if s1 == s0:
+            continue
+        sub = wl.Jagged(offsets=np.array([0, s1 - s0], dtype=np.int32),
+                        timestamps=w.seq.timestamps[s0:s1])
+        yb = _layer(w, w.x[s0:s1], sub, dims)
+        np.testing.assert_allclose(y[s0:s1], yb, rtol=0, atol=1e-12)
+
+
+def test_jagged_equals_padded_batch():
+    """Padding every sequence to the longest with junk rows changes none of the real rows."""
+    dims = _small_dims()
+    lengths = np.array([5, 19, 11, 0, 26])
+    w = wl.random_layer(22, lengths, dims)
+    y = _layer(w, w.x, w.seq, dims)
+    L = int(lengths.max())
+    rng = np.random.default_rng(99)
+    xs, tss, idx = [], [], []
+    for b, n in enumerate(lengths):
+        s0 = w.seq.offsets[b]
+        pad = L - n
+        xs.append(np.concatenate([w.x[s0:s0 + n], rng.standard_normal((pad, dims.d_model))]))
+        last = w.seq.timestamps[s0 + n - 1] if n else 0
+        tss.append(np.concatenate([w.seq.timestamps[s0:s0 + n],
+                                   last + 1 + np.arange(pad)]).astype(np.int32))
+        idx.append(b * L + np.arange(n))
+    padded = wl.Jagged(offsets=(np.arange(len(lengths) + 1) * L).astype(np.int32),
+                       timestamps=np.concatenate(tss))
+    yp = _layer(w, np.concatenate(xs), padded, dims)
+    np.testing.assert_allclose(yp[np.concatenate(idx)], y, rtol=0, atol=1e-12)
+
+
+def test_causality_future_tokens_do_not_leak():
+    dims = _small_dims()
+    w = wl.random_layer(23, [40], dims, bias=True)
+    y = _layer(w, w.x, w.seq, dims)
+    i = 17
+    x2 = w.x.copy()
+    x2[i + 1:] = np.random.default_rng(5).standard_normal(x2[i + 1:].shape)
+    ts2 = w.seq.timestamps.copy()
+    ts2[i + 1:] = ts2[i + 1:] + 12345
+    y2 = _layer(w, x2, wl.Jagged(w.seq.offsets, ts2), dims)
+    np.testing.assert_allclose(y2[:i + 1], y[:i + 1], rtol=0, atol=1e-12)
+    assert np.abs(y2[i + 1:] - y[i + 1:]).max() > 1e-3
+    # perturbing token i changes row i
+    x3 = w.x.copy()
+    x3[i] += 0.5
+    y3 = _layer(w, x3, w.seq, dims)
+    assert np.abs(y3[i] - y[i]).max() > 1e-3
+    np.testing.assert_allclose(y3[:i], y[:i], rtol=0, atol=1e-12)
+
+
+def test_rows_mode_matches_full_run():
+    dims = _small_dims()
+    w = wl.random_layer(24, [9, 30, 0, 14], dims, bias=True, affine=True)
+    y = _layer(w, w.x, w.seq, dims)
+    rows = [0, 8, 9, 25, 38, 52]
+    yr = _layer(w, w.x, w.seq, dims, rows=rows)
+    np.testing.assert_allclose(yr[rows], y[rows], rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------------
+# M-FALCON
+# ----------------------------------------------------------------------------------
+
+def _mfalcon_case(seed=31, B=3, n_h=(12, 20, 7), n_c=(5, 3, 6)):
+    dims = _small_dims()
+    rng = np.random.default_rng(seed)
+    w = wl.random_layer(seed, list(n_h), dims, bias=True, affine=True)
+    c_off = wl.offsets_from_lengths(n_c)
+    last = w.seq.timestamps[w.seq.offsets[1:] - 1].astype(np.int64)
+    cts = np.concatenate([last[b] + 1 + rng.integers(0, 300, size=n_c[b]) for b in range(B)])
+    cand = wl.Jagged(offsets=c_off, timestamps=cts.astype(np.int32))
+    xc = wl.round_bf16(rng.standard_normal((int(c_off[-1]), dims.d_model)).astype(np.float32))
+    return dims, w, cand, xc
+
+
+def _mf(dims, w, cand, xc):
+    return ref.mfalcon_fwd(w.x, w.seq.offsets, w.seq.timestamps, xc, cand.offsets, cand.timestamps,
+                           w.weights, dims.num_heads, dims.dqk, dims.dv, dims.ln_eps)
+
+
+def test_mfalcon_candidate_equals_last_row_of_causal_on_history_plus_candidate():
+    dims, w, cand, xc = _mfalcon_case()
+    y_hist, y_cand = _mf(dims, w, cand, xc)
+    np.testing.assert_allclose(y_hist, _layer(w, w.x, w.seq, dims), rtol=0, atol=1e-12)
+    for b in range(cand.batch):
+        h0, h1 = w.seq.offsets[b], w.seq.offsets[b + 1]
+        for c in range(cand.offsets[b], cand.offsets[b + 1]):
+            xs = np.concatenate([w.x[h0:h1], xc[c:c + 1]])
+            ts = np.concatenate([w.seq.timestamps[h0:h1], cand.timestamps[c:c + 1]])
+            one = wl.Jagged(offsets=np.array([0, h1 - h0 + 1], dtype=np.int32), timestamps=ts)
+            y1 = _layer(w, xs, one, dims)
+            np.testing.assert_allclose(y_cand[c], y1[-1], rtol=0, atol=1e-11)
+
+
+def test_mfalcon_microbatch_and_permutation_invariance():
+    dims, w, cand, xc = _mfalcon_case(n_c=(6, 6, 6))
+    _, y_all = _mf(dims, w, cand, xc)
+    # micro-batches of b_m = 2 candidates per user
+    for start in range(0, 6, 2):
+        sel = np.concatenate([cand.offsets[b] + np.arange(start, start + 2) for b in range(3)])
+        mc = wl.Jagged(offsets=wl.offsets_from_lengths([2, 2, 2]), timestamps=cand.timestamps[sel])
+        _, y_mb = _mf(dims, w, mc, xc[sel])
+        np.testing.assert_allclose(y_mb, y_all[sel], rtol=0, atol=1e-12)
+    # permuting candidates inside each user permutes the outputs
+    perm = np.concatenate([cand.offsets[b] + np.random.default_rng(b).permutation(6) for b in range(3)])
+    pc = wl.Jagged(offsets=cand.offsets, timestamps=cand.timestamps[perm])
+    _, y_p = _mf(dims, w, pc, xc[perm])
+    np.testing.assert_allclose(y_p, y_all[perm], rtol=0, atol=1e-12)
+    # perturbing another candidate leaves this one unchanged
+    xc2 = xc.copy()
+    xc2[1] += 1.0
+    _, y2 = _mf(dims, w, cand, xc2)
+    np.testing.assert_allclose(np.delete(y2, 1, axis=0), np.delete(y_all, 1, axis=0), rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------------
+# rab indices: golden buckets and decodable probes
+# ----------------------------------------------------------------------------------
+
+def test_time_bucket_golden():
+    rows = _read_golden("time_buckets.txt")
+    dt = np.array([int(r[0]) for r in rows], dtype=np.int64)
+    want = np.array([int(r[1]) for r in rows], dtype=np.int64)
+    got = ref.time_bucket(dt, np.zeros_like(dt), 32)
+    np.testing.assert_array_equal(got, want)
+    # negative gaps count as zero
+    assert ref.time_bucket(np.array([3]), np.array([10]), 32)[0] == 0
+    # brute-force integer definition on a dense range
+    r = np.arange(0, 5000)
+    np.testing.assert_array_equal(ref.log2_floor_plus1(r),
+                                  [int(v + 1).bit_length() - 1 for v in r])
+
+
+def _decode(values, table):
+    """Nearest SiLU(table) entry for each value (values from a one-hot V probe)."""
+    cand = ref.silu(np.asarray(table, dtype=np.float64))
+    return np.abs(values[..., None] - cand).argmin(axis=-1)
+
+
+def test_probe_position_indices():
+    """Q = K = 0 and one-hot V: out[i][j] = SiLU(P[min(i-j,63)]) on allowed pairs, 0 else."""
+    n = 80
+    ptab = 1.0 + np.arange(64) / 8.0
+    q = np.zeros((n, 1)); k = np.zeros((n, 1))
+    v = np.eye(n)
+    off = np.array([0, n])
+    o = ref.attention(q, k, v, off, None, 1, 1, n, rab_pos=ptab[None, :])
+    i, j = np.meshgrid(np.arange(n), np.arange(n), indexing="ij")
+    allowed = j <= i
+    assert np.all(o[~allowed] == 0.0)
+    got = _decode(o[allowed], ptab)
+    np.testing.assert_array_equal(got, np.minimum(i - j, 63)[allowed])
+
+
+def test_probe_time_indices():
+    rows = _read_golden("time_buckets.txt")
+    gaps = [int(r[0]) for r in rows if int(r[0]) < 2**31 - 1]
+    want = {int(r[0]): int(r[1]) for r in rows}
+    # sequence: token 0 at time 0, then one token at each gap; query = last-but-one rows
+    ts = np.array([0] + gaps, dtype=np.int64)
+    n = ts.size
+    ttab = 1.0 + np.arange(32) / 4.0
+    o = ref.attention(np.zeros((n, 1)), np.zeros((n, 1)), np.eye(n), np.array([0, n]), ts,
+                      1, 1, n, rab_time=ttab[None, :])
+    got = _decode(o[1:, 0], ttab)  # row i (ts = gaps[i-1]) against key 0 (ts = 0)
+    np.testing.assert_array_equal(got, [want[g] for g in gaps])
+
+
+# ----------------------------------------------------------------------------------
+# Closed forms and special cases
+# ----------------------------------------------------------------------------------
+
+def test_zero_scores_constant_bias_is_prefix_sum():
+    n, dv, c = 50, 6, 0.7
+    rng = np.random.default_rng(3)
+    v = rng.standard_normal((n, dv))
+    o = ref.attention(np.zeros((n, 4)), np.zeros((n, 4)), v, np.array([0, n]),
+                      np.arange(n) * 10, 1, 4, dv, rab_pos=np.full((1, 64), c),
+                      rab_time=np.zeros((1, 32)))
+    silu_c = c / (1 + math.exp(-c))
+    np.testing.assert_allclose(o, silu_c * np.cumsum(v, axis=0), rtol=1e-13, atol=1e-13)
+
+
+def test_single_token_and_two_token_closed_forms():
+    rng = np.random.default_rng(4)
+    dqk = dv = 5
+    q = rng.standard_normal((2, dqk)); k = rng.standard_normal((2, dqk)); v = rng.standard_normal((2, dv))
+    P = rng.standard_normal(64); Tt = rng.standard_normal(32)
+    ts = np.array([100, 100 + 37])
+
+    def silu(z):
+        return z / (1 + math.exp(-z))
+
+    o1 = ref.attention(q[:1], k[:1], v[:1], np.array([0, 1]), ts[:1], 1, dqk, dv, P[None], Tt[None])
+    np.testing.assert_allclose(o1[0], silu(q[0] @ k[0] + P[0] + Tt[0]) * v[0], rtol=1e-13)
+    o2 = ref.attention(q, k, v, np.array([0, 2]), ts, 1, dqk, dv, P[None], Tt[None])
+    # row 1 sees key 0 (relative position 1, gap 37 -> bucket 5) and itself
+    want = silu(q[1] @ k[0] + P[1] + Tt[5]) * v[0] + silu(q[1] @ k[1] + P[0] + Tt[0]) * v[1]
+    np.testing.assert_allclose(o2[1], want, rtol=1e-13)
+    np.testing.assert_allclose(o2[0], o1[0], rtol=1e-13)
+
+
+def test_norm_is_scale_invariant_in_values():
+    rng = np.random.default_rng(5)
+    n, H, dh = 30, 2, 8
+    q, k, v, u = (rng.standard_normal((n, H * dh)) for _ in range(4))
+    off = np.array([0, 12, 30])
+    g1 = ref.norm_gate(ref.attention(q, k, v, off, None, H, dh, dh), u, eps=0.0)
+    g2 = ref.norm_gate(ref.attention(q, k, 3.5 * v, off, None, H, dh, dh), u, eps=0.0)
+    np.testing.assert_allclose(g1, g2, rtol=1e-10, atol=1e-10)
+
+
+def test_null_rab_equals_zero_tables():
+    dims = _small_dims()
+    w = wl.random_layer(25, [10, 21], dims, rab=False)
+    y0 = _layer(w, w.x, w.seq, dims)
+    w.weights.rab_pos = np.zeros((1, 64), np.float32)
+    w.weights.rab_time = np.zeros((1, 32), np.float32)
+    np.testing.assert_array_equal(_layer(w, w.x, w.seq, dims), y0)
+
+
+def test_norm_rows_are_standardised_over_full_row():
+    dims = _small_dims()
+    w = wl.random_layer(26, [25, 9], dims)
+    _, mid = _layer(w, w.x, w.seq, dims, intermediates=True)
+    nrm = mid["g"] / mid["u"]
+    np.testing.assert_allclose(nrm.mean(axis=1), 0.0, atol=1e-9)
+    var = mid["o"].var(axis=1)
+    np.testing.assert_allclose(nrm.var(axis=1), var / (var + dims.ln_eps), rtol=1e-9)
+
+
+def test_silu_and_layernorm_match_torch_fp64():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(6)
+    z = rng.standard_normal(1000) * 20
+    np.testing.assert_allclose(ref.silu(z), torch.nn.functional.silu(torch.from_numpy(z)).numpy(),
+                               rtol=1e-14, atol=1e-300)
+    o = rng.standard_normal((7, 48)) * 300 + 1e4
+    u = np.ones_like(o)
+    gam, bet = rng.standard_normal(48), rng.standard_normal(48)
+    want = torch.nn.functional.layer_norm(torch.from_numpy(o), (48,), torch.from_numpy(gam),
+                                          torch.from_numpy(bet), eps=1e-5).numpy()
+    np.testing.assert_allclose(ref.norm_gate(o, u, gam, bet, 1e-5), want, rtol=1e-10, atol=1e-10)
+
+
+def test_split_order_u_v_q_k():
+    """W1 = 0 with per-block biases: each block becomes a known constant vector.
+
+    U block zero bias => U = SiLU(0) = 0 => G = 0 => Y = b2 exactly.  A layout that took U
+    from any other block would give a non-zero gate.
+    """
+    dims = wl.LayerDims(d_model=8, num_heads=2, dqk=3, dv=4, ln_eps=0.0)
+    rng = np.random.default_rng(8)
+    w = wl.random_layer(27, [6, 4], dims, bias=True)
+    w.weights.w1 = np.zeros_like(w.weights.w1)
+    hv, hq = dims.hdv, dims.num_heads * dims.dqk
+    # identical Q and K biases in every head, so every head has the same scores
+    bq = np.tile(rng.uniform(0.5, 2, dims.dqk), dims.num_heads)
+    bk = np.tile(rng.uniform(0.5, 2, dims.dqk), dims.num_heads)
+    b1 = np.concatenate([np.zeros(hv), rng.uniform(0.5, 2, hv), bq, bk]).astype(np.float32)
+    w.weights.b1 = b1
+    y = _layer(w, w.x, w.seq, dims)
+    np.testing.assert_array_equal(y, np.broadcast_to(w.weights.b2.astype(np.float64), y.shape))
+    # With U constant and V constant per feature, every row's Norm(AV) is Norm(SiLU(b_V))
+    # (AV_i = (sum_j a_ij) * SiLU(b_V), the same sum in every head), so all rows of Y
+    # coincide.
+    b1[:hv] = 3.0
+    w.weights.b1 = b1
+    y = _layer(w, w.x, w.seq, dims)
+    np.testing.assert_allclose(y, np.broadcast_to(y[0], y.shape), rtol=1e-9, atol=1e-9)
+    sv = ref.silu(b1[hv:2 * hv].astype(np.float64))
+    n = (sv - sv.mean()) / np.sqrt(sv.var() + 0.0)
+    want = (n * ref.silu(np.float64(3.0))) @ w.weights.w2.T.astype(np.float64) + w.weights.b2
+    np.testing.assert_allclose(y[0], want, rtol=1e-9, atol=1e-9)
+
+
+def test_query_side_is_q_block():
+    """Q random, K constant (zero K weights, bias c): scores depend on the query only.
+
+    With one-hot V over a single sequence, out[i][j] must then be constant in j on the
+    allowed pairs, and vary with i.  Swapping the Q and K blocks would flip that.
+    """
+    n, dqk = 9, 4
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((n, dqk))
+    k = np.full((n, dqk), 0.8)
+    o = ref.attention(q, k, np.eye(n), np.array([0, n]), None, 1, dqk, n)
+    for i in range(n):
+        row = o[i, :i + 1]
+        np.testing.assert_allclose(row, row[0], rtol=1e-14)
+        assert row[0] == pytest.approx(float(ref.silu(q[i] @ k[0])), rel=1e-14)
