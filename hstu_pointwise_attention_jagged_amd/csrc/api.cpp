@@ -1,0 +1,399 @@
+// C ABI of libhstu: argument checks, workspace layout, launch order and optional
+// per-kernel event timing.  Every numeric step runs in the HIP kernels; this file only
+// validates, carves the caller's workspace and enqueues launches on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <mutex>
+#include <vector>
+
+#include "../../include/hstu.h"
+#include "kernels.h"
+
+using namespace hstu;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// ---------------------------------------------------------------- profiling ---------
+constexpr int kNumKernels = 5;
+const char *kKernelNames[kNumKernels] = {"schedule", "f1_gemm_silu", "attention", "norm_gate",
+                                         "f2_gemm"};
+
+struct ProfRecord {
+  int id;
+  hipEvent_t start, stop;
+};
+
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRecord> g_prof_records;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t pool_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs `launch` on `stream`, bracketed by events when profiling is on.
+template <typename F>
+hipError_t timed(int id, hipStream_t stream, F &&launch) {
+  hipEvent_t a = nullptr, b = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (g_prof_on) {
+      a = pool_event();
+      b = pool_event();
+    }
+  }
+  if (a && b) (void)hipEventRecord(a, stream);
+  hipError_t err = launch();
+  if (a && b) {
+    (void)hipEventRecord(b, stream);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_records.push_back({id, a, b});
+  }
+  return err;
+}
+
+hstu_status_t hip_fail(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return HSTU_ERR_HIP;
+}
+
+// ---------------------------------------------------------------- checks ------------
+// Shape rules of the attention kernel alone.
+hstu_status_t check_attn_dims(const hstu_dims_t *d) {
+  if (d == nullptr) return HSTU_ERR_INVALID_ARG;
+  if (d->num_heads <= 0 || d->dqk <= 0 || d->dv <= 0) return HSTU_ERR_INVALID_ARG;
+  if (d->pos_buckets < 1 || d->time_buckets < 1) return HSTU_ERR_INVALID_ARG;
+  if (d->rab_heads != 1 && d->rab_heads != d->num_heads) return HSTU_ERR_INVALID_ARG;
+  if (d->dqk != d->dv) return HSTU_ERR_UNSUPPORTED;
+  if (d->dqk != 32 && d->dqk != 64 && d->dqk != 128) return HSTU_ERR_UNSUPPORTED;
+  if (d->pos_buckets > 1024 || d->time_buckets > 64) return HSTU_ERR_UNSUPPORTED;
+  return HSTU_OK;
+}
+
+// Shape rules of the whole layer (projections and norm-gate too).
+hstu_status_t check_dims(const hstu_dims_t *d) {
+  if (d == nullptr) return HSTU_ERR_INVALID_ARG;
+  if (d->d_model <= 0 || d->num_heads <= 0 || d->dqk <= 0 || d->dv <= 0) return HSTU_ERR_INVALID_ARG;
+  if (d->pos_buckets < 1 || d->time_buckets < 1) return HSTU_ERR_INVALID_ARG;
+  if (d->rab_heads != 1 && d->rab_heads != d->num_heads) return HSTU_ERR_INVALID_ARG;
+  if (!(d->ln_eps >= 0.0f) || !std::isfinite(d->ln_eps)) return HSTU_ERR_INVALID_ARG;
+  if (d->dqk != d->dv) return HSTU_ERR_UNSUPPORTED;
+  if (d->dqk != 32 && d->dqk != 64 && d->dqk != 128) return HSTU_ERR_UNSUPPORTED;
+  if (d->d_model % 64 != 0) return HSTU_ERR_UNSUPPORTED;
+  const int64_t hdv = (int64_t)d->num_heads * d->dv;
+  if (hdv % 64 != 0 || hdv > 2048) return HSTU_ERR_UNSUPPORTED;
+  if (d->pos_buckets > 1024 || d->time_buckets > 64) return HSTU_ERR_UNSUPPORTED;
+  return HSTU_OK;
+}
+
+hstu_status_t check_seq(const hstu_jagged_t *s) {
+  if (s == nullptr) return HSTU_ERR_INVALID_ARG;
+  if (s->batch < 0 || s->total_tokens < 0 || s->max_seq_len < 0) return HSTU_ERR_INVALID_ARG;
+  if (s->seq_offsets == nullptr) return HSTU_ERR_INVALID_ARG;
+  if (s->batch == 0 && s->total_tokens != 0) return HSTU_ERR_INVALID_ARG;
+  if (s->total_tokens > 0 && s->max_seq_len == 0) return HSTU_ERR_INVALID_ARG;
+  return HSTU_OK;
+}
+
+size_t sched_bytes(const hstu_jagged_t *s) {
+  const int64_t cap = attn_work_capacity(s->batch, s->total_tokens);
+  return align_up((size_t)cap * 2 * sizeof(int32_t)) + kAlign;
+}
+
+size_t layer_ws_bytes(const hstu_dims_t *d, const hstu_jagged_t *s) {
+  const size_t T = (size_t)s->total_tokens, hdv = (size_t)d->num_heads * d->dv;
+  return align_up(T * hdv * sizeof(float)) + align_up(T * hdv * sizeof(uint16_t)) + sched_bytes(s);
+}
+
+struct LayerWs {
+  float *o;
+  uint16_t *g;
+  int32_t *work;
+  int32_t *n_work;
+};
+
+LayerWs carve_layer(void *ws, const hstu_dims_t *d, const hstu_jagged_t *s) {
+  const size_t T = (size_t)s->total_tokens, hdv = (size_t)d->num_heads * d->dv;
+  char *p = (char *)ws;
+  LayerWs w;
+  w.o = (float *)p;
+  p += align_up(T * hdv * sizeof(float));
+  w.g = (uint16_t *)p;
+  p += align_up(T * hdv * sizeof(uint16_t));
+  w.n_work = (int32_t *)p;
+  w.work = (int32_t *)(p + kAlign);
+  return w;
+}
+
+hstu_status_t check_ws(void *ws, size_t have, size_t need) {
+  if (need > 0 && (ws == nullptr || have < need)) return HSTU_ERR_WORKSPACE;
+  if (((uintptr_t)ws & (kAlign - 1)) != 0) return HSTU_ERR_WORKSPACE;
+  return HSTU_OK;
+}
+
+AttnArgs attn_args(const hstu_dims_t *d, const float *rab_pos, const float *rab_time,
+                   const hstu_jagged_t *s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                   int64_t stride, float *out, const LayerWs &w) {
+  AttnArgs a{};
+  a.offsets = s->seq_offsets;
+  a.ts = s->timestamps;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.stride = stride;
+  a.rab_pos = rab_pos;
+  a.rab_time = rab_time;
+  a.pos_buckets = d->pos_buckets;
+  a.time_buckets = d->time_buckets;
+  a.rab_per_head = d->rab_heads == d->num_heads && d->num_heads > 1;
+  a.out = out;
+  a.out_stride = (int64_t)d->num_heads * d->dv;
+  a.work = w.work;
+  a.n_work = w.n_work;
+  a.num_heads = d->num_heads;
+  a.mask = 0;
+  return a;
+}
+
+// f1 -> attention -> norm-gate -> f2 for one batch whose attention args are ready.
+hstu_status_t run_layer(const hstu_dims_t *d, const hstu_weights_t *w, const hstu_jagged_t *s,
+                        const uint16_t *x, uint16_t *y, uint16_t *uvqk, const AttnArgs &aa,
+                        const LayerWs &lw, int max_prefix, hipStream_t st) {
+  const int T = s->total_tokens;
+  const int hdv = d->num_heads * d->dv;
+  const int n1 = 2 * d->num_heads * (d->dqk + d->dv);
+  hipError_t e;
+  e = timed(0, st, [&] {
+    return launch_schedule(s->seq_offsets, aa.p_offsets, s->batch, aa.mask, s->max_seq_len,
+                           max_prefix, lw.work, lw.n_work, st);
+  });
+  if (e != hipSuccess) return hip_fail(e);
+  e = timed(1, st, [&] { return launch_gemm(x, w->w1, w->b1, uvqk, T, n1, d->d_model, ACT_SILU, st); });
+  if (e != hipSuccess) return hip_fail(e);
+  const int64_t cap = attn_work_capacity(s->batch, T);
+  e = timed(2, st, [&] { return launch_attention(aa, d->dqk, cap, st); });
+  if (e != hipSuccess) return hip_fail(e);
+  e = timed(3, st, [&] {
+    return launch_norm_gate(lw.o, uvqk, n1, w->ln_gamma, w->ln_beta, d->ln_eps, lw.g, T, hdv, st);
+  });
+  if (e != hipSuccess) return hip_fail(e);
+  e = timed(4, st, [&] { return launch_gemm(lw.g, w->w2, w->b2, y, T, d->d_model, hdv, ACT_NONE, st); });
+  if (e != hipSuccess) return hip_fail(e);
+  return HSTU_OK;
+}
+
+hstu_status_t check_weights(const hstu_weights_t *w) {
+  if (w == nullptr || w->w1 == nullptr || w->w2 == nullptr) return HSTU_ERR_INVALID_ARG;
+  if (!aligned16(w->w1) || !aligned16(w->w2)) return HSTU_ERR_INVALID_ARG;
+  if ((w->b1 && !aligned16(w->b1)) || (w->b2 && !aligned16(w->b2))) return HSTU_ERR_INVALID_ARG;
+  return HSTU_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hstu_layer_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_t *seq) {
+  if (check_dims(dims) != HSTU_OK || check_seq(seq) != HSTU_OK) return 0;
+  return layer_ws_bytes(dims, seq);
+}
+
+size_t hstu_attn_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_t *seq) {
+  if (check_attn_dims(dims) != HSTU_OK || check_seq(seq) != HSTU_OK) return 0;
+  return sched_bytes(seq);
+}
+
+hstu_status_t hstu_layer_fwd(const hstu_dims_t *dims, const hstu_weights_t *w,
+                             const hstu_jagged_t *seq, const uint16_t *x, uint16_t *y,
+                             uint16_t *uvqk, void *ws, size_t ws_bytes, void *stream) {
+  hstu_status_t st;
+  if ((st = check_dims(dims)) != HSTU_OK) return st;
+  if ((st = check_seq(seq)) != HSTU_OK) return st;
+  if ((st = check_weights(w)) != HSTU_OK) return st;
+  if (seq->total_tokens > 0 && (x == nullptr || y == nullptr || uvqk == nullptr))
+    return HSTU_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(uvqk)) return HSTU_ERR_INVALID_ARG;
+  if ((void *)x == (void *)y) return HSTU_ERR_INVALID_ARG;
+  if (seq->batch == 0 || seq->total_tokens == 0) return HSTU_OK;
+  if ((st = check_ws(ws, ws_bytes, layer_ws_bytes(dims, seq))) != HSTU_OK) return st;
+
+  const LayerWs lw = carve_layer(ws, dims, seq);
+  const int hdv = dims->num_heads * dims->dv, hqk = dims->num_heads * dims->dqk;
+  const int64_t n1 = 2 * (int64_t)(hdv + hqk);
+  AttnArgs aa = attn_args(dims, w->rab_pos, w->rab_time, seq, uvqk + 2 * hdv,
+                          uvqk + 2 * hdv + hqk, uvqk + hdv, n1, lw.o, lw);
+  return run_layer(dims, w, seq, x, y, uvqk, aa, lw, 0, (hipStream_t)stream);
+}
+
+hstu_status_t hstu_layer_fwd_mfalcon(const hstu_dims_t *dims, const hstu_weights_t *w,
+                                     const hstu_jagged_t *hist, const uint16_t *hist_uvqk,
+                                     const hstu_jagged_t *cand, const uint16_t *x_cand,
+                                     uint16_t *y_cand, uint16_t *uvqk_cand, void *ws,
+                                     size_t ws_bytes, void *stream) {
+  hstu_status_t st;
+  if ((st = check_dims(dims)) != HSTU_OK) return st;
+  if ((st = check_seq(hist)) != HSTU_OK) return st;
+  if ((st = check_seq(cand)) != HSTU_OK) return st;
+  if ((st = check_weights(w)) != HSTU_OK) return st;
+  if (hist->batch != cand->batch) return HSTU_ERR_INVALID_ARG;
+  if (hist->total_tokens > 0 && hist_uvqk == nullptr) return HSTU_ERR_INVALID_ARG;
+  if (cand->total_tokens > 0 && (x_cand == nullptr || y_cand == nullptr || uvqk_cand == nullptr))
+    return HSTU_ERR_INVALID_ARG;
+  if (!aligned16(hist_uvqk) || !aligned16(x_cand) || !aligned16(y_cand) || !aligned16(uvqk_cand))
+    return HSTU_ERR_INVALID_ARG;
+  if ((void *)x_cand == (void *)y_cand) return HSTU_ERR_INVALID_ARG;
+  if ((cand->timestamps == nullptr) != (hist->timestamps == nullptr)) return HSTU_ERR_INVALID_ARG;
+  if (cand->batch == 0 || cand->total_tokens == 0) return HSTU_OK;
+  if ((st = check_ws(ws, ws_bytes, layer_ws_bytes(dims, cand))) != HSTU_OK) return st;
+
+  const LayerWs lw = carve_layer(ws, dims, cand);
+  const int hdv = dims->num_heads * dims->dv, hqk = dims->num_heads * dims->dqk;
+  const int64_t n1 = 2 * (int64_t)(hdv + hqk);
+  AttnArgs aa = attn_args(dims, w->rab_pos, w->rab_time, cand, uvqk_cand + 2 * hdv,
+                          uvqk_cand + 2 * hdv + hqk, uvqk_cand + hdv, n1, lw.o, lw);
+  aa.mask = 1;
+  aa.p_offsets = hist->seq_offsets;
+  aa.p_ts = hist->timestamps;
+  aa.pk = hist_uvqk + 2 * hdv + hqk;
+  aa.pv = hist_uvqk + hdv;
+  aa.p_stride = n1;
+  return run_layer(dims, w, cand, x_cand, y_cand, uvqk_cand, aa, lw, hist->max_seq_len,
+                   (hipStream_t)stream);
+}
+
+hstu_status_t hstu_attn_fwd(const hstu_dims_t *dims, const float *rab_pos, const float *rab_time,
+                            const hstu_jagged_t *seq, const uint16_t *q, const uint16_t *k,
+                            const uint16_t *v, int64_t row_stride, const hstu_prefix_t *prefix,
+                            hstu_mask_t mask, float *out, void *ws, size_t ws_bytes,
+                            void *stream) {
+  hstu_status_t st;
+  if ((st = check_attn_dims(dims)) != HSTU_OK) return st;
+  if ((st = check_seq(seq)) != HSTU_OK) return st;
+  if (mask != HSTU_MASK_CAUSAL && mask != HSTU_MASK_SELF_ONLY) return HSTU_ERR_INVALID_ARG;
+  const int64_t hq = (int64_t)dims->num_heads * dims->dqk;
+  if (seq->total_tokens > 0 && (q == nullptr || k == nullptr || v == nullptr || out == nullptr))
+    return HSTU_ERR_INVALID_ARG;
+  if (row_stride < hq || row_stride % 8 != 0) return HSTU_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return HSTU_ERR_INVALID_ARG;
+  int max_prefix = 0;
+  if (prefix != nullptr) {
+    if ((st = check_seq(prefix->seq)) != HSTU_OK) return st;
+    if (prefix->seq->batch != seq->batch) return HSTU_ERR_INVALID_ARG;
+    if (prefix->seq->total_tokens > 0 && (prefix->k == nullptr || prefix->v == nullptr))
+      return HSTU_ERR_INVALID_ARG;
+    if (prefix->row_stride < hq || prefix->row_stride % 8 != 0) return HSTU_ERR_INVALID_ARG;
+    if (!aligned16(prefix->k) || !aligned16(prefix->v)) return HSTU_ERR_INVALID_ARG;
+    if ((prefix->seq->timestamps == nullptr) != (seq->timestamps == nullptr))
+      return HSTU_ERR_INVALID_ARG;
+    max_prefix = prefix->seq->max_seq_len;
+  }
+  if (seq->batch == 0 || seq->total_tokens == 0) return HSTU_OK;
+  if ((st = check_ws(ws, ws_bytes, sched_bytes(seq))) != HSTU_OK) return st;
+
+  LayerWs lw{};
+  lw.n_work = (int32_t *)ws;
+  lw.work = (int32_t *)((char *)ws + kAlign);
+  AttnArgs aa = attn_args(dims, rab_pos, rab_time, seq, q, k, v, row_stride, out, lw);
+  aa.mask = mask == HSTU_MASK_CAUSAL ? 0 : 1;
+  if (prefix != nullptr) {
+    aa.p_offsets = prefix->seq->seq_offsets;
+    aa.p_ts = prefix->seq->timestamps;
+    aa.pk = prefix->k;
+    aa.pv = prefix->v;
+    aa.p_stride = prefix->row_stride;
+  }
+  hipStream_t sst = (hipStream_t)stream;
+  hipError_t e = timed(0, sst, [&] {
+    return launch_schedule(seq->seq_offsets, aa.p_offsets, seq->batch, aa.mask, seq->max_seq_len,
+                           max_prefix, lw.work, lw.n_work, sst);
+  });
+  if (e != hipSuccess) return hip_fail(e);
+  const int64_t cap = attn_work_capacity(seq->batch, seq->total_tokens);
+  e = timed(2, sst, [&] { return launch_attention(aa, dims->dqk, cap, sst); });
+  if (e != hipSuccess) return hip_fail(e);
+  return HSTU_OK;
+}
+
+hstu_status_t hstu_validate_jagged(const hstu_jagged_t *seq, void *stream) {
+  hstu_status_t st;
+  if ((st = check_seq(seq)) != HSTU_OK) return st;
+  std::vector<int32_t> off((size_t)seq->batch + 1);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(off.data(), seq->seq_offsets, off.size() * sizeof(int32_t),
+                                hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e);
+  if (off[0] != 0 || off[seq->batch] != seq->total_tokens) return HSTU_ERR_INVALID_ARG;
+  for (int b = 0; b < seq->batch; ++b) {
+    const int64_t n = (int64_t)off[b + 1] - off[b];
+    if (n < 0 || n > seq->max_seq_len) return HSTU_ERR_INVALID_ARG;
+  }
+  return HSTU_OK;
+}
+
+const char *hstu_status_str(hstu_status_t s) {
+  switch (s) {
+    case HSTU_OK: return "ok";
+    case HSTU_ERR_INVALID_ARG: return "invalid argument";
+    case HSTU_ERR_UNSUPPORTED: return "unsupported shape";
+    case HSTU_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case HSTU_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+int hstu_last_hip_error(void) { return g_last_hip_error; }
+
+void hstu_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = on != 0;
+}
+
+void hstu_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto &r : g_prof_records) {
+    g_event_pool.push_back(r.start);
+    g_event_pool.push_back(r.stop);
+  }
+  g_prof_records.clear();
+}
+
+hstu_status_t hstu_profile_collect(double *total_ms, int64_t *launches) {
+  if (total_ms == nullptr || launches == nullptr) return HSTU_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (int i = 0; i < kNumKernels; ++i) {
+    total_ms[i] = 0.0;
+    launches[i] = 0;
+  }
+  for (auto &r : g_prof_records) {
+    hipError_t e = hipEventSynchronize(r.stop);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess) return hip_fail(e);
+    total_ms[r.id] += ms;
+    launches[r.id] += 1;
+  }
+  return HSTU_OK;
+}
+
+const char *hstu_kernel_name(int id) {
+  return (id >= 0 && id < kNumKernels) ? kKernelNames[id] : "unknown";
+}
+
+}  // extern "C"

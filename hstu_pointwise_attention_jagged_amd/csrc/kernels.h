@@ -1,0 +1,57 @@
+// Internal launchers of libhstu (C++ linkage, not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hstu {
+
+enum Act { ACT_NONE = 0, ACT_SILU = 1 };
+
+// out[M][N] = act(A[M][K] . W[N][K]^T + bias[N]) in bf16 with fp32 accumulation.
+// Requires K % 64 == 0 and N % 64 == 0; any M >= 0.
+hipError_t launch_gemm(const uint16_t *A, const uint16_t *W, const float *bias, uint16_t *out,
+                       int M, int N, int K, Act act, hipStream_t stream);
+
+// Attention parameters (device pointers unless noted).
+struct AttnArgs {
+  const int32_t *offsets;   // [B+1]
+  const int32_t *ts;        // [T] or nullptr
+  const uint16_t *q, *k, *v;
+  int64_t stride;           // elements between rows of q/k/v
+  const int32_t *p_offsets; // prefix [B+1] or nullptr
+  const int32_t *p_ts;      // prefix timestamps or nullptr
+  const uint16_t *pk, *pv;
+  int64_t p_stride;
+  const float *rab_pos;     // [rab_heads][pos_buckets] or nullptr
+  const float *rab_time;    // [rab_heads][time_buckets] or nullptr
+  int pos_buckets, time_buckets, rab_per_head;
+  float *out;               // [T][H*dv]
+  int64_t out_stride;
+  const int32_t *work;      // [2*cap] (b, q-tile) pairs, longest first
+  const int32_t *n_work;    // [1]
+  int num_heads;
+  int mask;                 // 0 causal, 1 self-only
+};
+
+constexpr int kAttnBlockM = 128;  // query rows per workgroup
+constexpr int kAttnBlockN = 64;   // keys per LDS stage
+
+// Work list capacity (items) for a batch of B sequences and T tokens.
+inline int64_t attn_work_capacity(int64_t B, int64_t T) {
+  return (T + kAttnBlockM - 1) / kAttnBlockM + B + 1;
+}
+
+// Builds the longest-first (sequence, q-tile) list into work[0 .. 2*cap) and n_work.
+hipError_t launch_schedule(const int32_t *offsets, const int32_t *p_offsets, int B, int mask,
+                           int max_seq_len, int max_prefix_len, int32_t *work, int32_t *n_work,
+                           hipStream_t stream);
+
+hipError_t launch_attention(const AttnArgs &a, int dh, int64_t cap, hipStream_t stream);
+
+// G[T][HDV] = LayerNorm(O) * gamma + beta, times U (bf16 row of uvqk), as bf16.
+hipError_t launch_norm_gate(const float *O, const uint16_t *U, int64_t u_stride,
+                            const float *gamma, const float *beta, float eps, uint16_t *G,
+                            int T, int HDV, hipStream_t stream);
+
+}  // namespace hstu

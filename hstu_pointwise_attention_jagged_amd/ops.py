@@ -1,0 +1,253 @@
+"""Python entry points over libhstu's C ABI (same names as the C functions).
+
+PyTorch supplies device memory and the stream; these wrappers only check tensor
+dtypes/devices, fill the ctypes structures, allocate outputs and workspace when the
+caller does not pass them, and call the library.  Every step of the computation runs in
+the HIP kernels behind ``include/hstu.h``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+__all__ = ["HSTUError", "LayerDims", "DeviceWeights", "DeviceJagged", "hstu_layer_fwd",
+           "hstu_layer_fwd_mfalcon", "hstu_attn_fwd", "hstu_layer_workspace_bytes",
+           "hstu_attn_workspace_bytes", "hstu_validate_jagged", "profile_enable", "profile_reset",
+           "profile_collect"]
+
+
+class HSTUError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = _lib.load()
+        msg = lib.hstu_status_str(status).decode()
+        if status == _lib.HSTU_ERR_HIP:
+            msg += f" (hip error {lib.hstu_last_hip_error()})"
+        super().__init__(f"{where}: {msg}")
+        self.status = status
+
+
+@dataclasses.dataclass
+class LayerDims:
+    d_model: int
+    num_heads: int
+    dqk: int
+    dv: int
+    pos_buckets: int = 64
+    time_buckets: int = 32
+    rab_heads: int = 1
+    ln_eps: float = 1e-5
+
+    def c(self) -> _lib.Dims:
+        return _lib.Dims(self.d_model, self.num_heads, self.dqk, self.dv, self.pos_buckets,
+                         self.time_buckets, self.rab_heads, self.ln_eps)
+
+    @property
+    def uvqk_width(self) -> int:
+        return 2 * self.num_heads * (self.dqk + self.dv)
+
+    @property
+    def hdv(self) -> int:
+        return self.num_heads * self.dv
+
+
+@dataclasses.dataclass
+class DeviceWeights:
+    w1: torch.Tensor                        # bf16 [2H(dv+dqk)][d]
+    w2: torch.Tensor                        # bf16 [d][H*dv]
+    b1: Optional[torch.Tensor] = None       # fp32
+    b2: Optional[torch.Tensor] = None
+    ln_gamma: Optional[torch.Tensor] = None
+    ln_beta: Optional[torch.Tensor] = None
+    rab_pos: Optional[torch.Tensor] = None  # fp32 [rab_heads][pos_buckets]
+    rab_time: Optional[torch.Tensor] = None
+
+    def c(self) -> _lib.Weights:
+        _check(self.w1, torch.bfloat16, "w1")
+        _check(self.w2, torch.bfloat16, "w2")
+        for n in ("b1", "b2", "ln_gamma", "ln_beta", "rab_pos", "rab_time"):
+            t = getattr(self, n)
+            if t is not None:
+                _check(t, torch.float32, n)
+        return _lib.Weights(*(_ptr(getattr(self, n)) for n in
+                              ("w1", "b1", "w2", "b2", "ln_gamma", "ln_beta", "rab_pos", "rab_time")))
+
+
+@dataclasses.dataclass
+class DeviceJagged:
+    offsets: torch.Tensor                   # int32 [B+1] on the device
+    total_tokens: int                       # host copy of offsets[B]
+    max_seq_len: int                        # host upper bound on lengths
+    timestamps: Optional[torch.Tensor] = None  # int32 [T] on the device
+
+    @property
+    def batch(self) -> int:
+        return int(self.offsets.shape[0]) - 1
+
+    def c(self) -> _lib.Jagged:
+        _check(self.offsets, torch.int32, "seq_offsets")
+        if self.timestamps is not None:
+            _check(self.timestamps, torch.int32, "timestamps")
+        return _lib.Jagged(self.batch, int(self.total_tokens), int(self.max_seq_len),
+                           _ptr(self.offsets), _ptr(self.timestamps))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _check(t: torch.Tensor, dtype, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name}: expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _raise(status: int, where: str):
+    if status != _lib.HSTU_OK:
+        raise HSTUError(status, where)
+
+
+def hstu_layer_workspace_bytes(dims: LayerDims, seq: DeviceJagged) -> int:
+    lib = _lib.load()
+    d, s = dims.c(), seq.c()
+    return int(lib.hstu_layer_workspace_bytes(ctypes.byref(d), ctypes.byref(s)))
+
+
+def hstu_attn_workspace_bytes(dims: LayerDims, seq: DeviceJagged) -> int:
+    lib = _lib.load()
+    d, s = dims.c(), seq.c()
+    return int(lib.hstu_attn_workspace_bytes(ctypes.byref(d), ctypes.byref(s)))
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
+    if ws is not None:
+        return ws
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def hstu_layer_fwd(dims: LayerDims, w: DeviceWeights, seq: DeviceJagged, x: torch.Tensor, *,
+                   y: Optional[torch.Tensor] = None, uvqk: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None):
+    """One HSTU layer (causal).  Returns (y bf16 [T][d], uvqk bf16 [T][2H(dv+dqk)])."""
+    lib = _lib.load()
+    _check(x, torch.bfloat16, "x")
+    T = seq.total_tokens
+    if y is None:
+        y = torch.empty((T, dims.d_model), dtype=torch.bfloat16, device=x.device)
+    if uvqk is None:
+        uvqk = torch.empty((T, dims.uvqk_width), dtype=torch.bfloat16, device=x.device)
+    _check(y, torch.bfloat16, "y")
+    _check(uvqk, torch.bfloat16, "uvqk")
+    d, wc, s = dims.c(), w.c(), seq.c()
+    need = int(lib.hstu_layer_workspace_bytes(ctypes.byref(d), ctypes.byref(s)))
+    ws = _workspace(need, x.device, workspace)
+    st = lib.hstu_layer_fwd(ctypes.byref(d), ctypes.byref(wc), ctypes.byref(s), _ptr(x), _ptr(y),
+                            _ptr(uvqk), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _raise(st, "hstu_layer_fwd")
+    return y, uvqk
+
+
+def hstu_layer_fwd_mfalcon(dims: LayerDims, w: DeviceWeights, hist: DeviceJagged,
+                           hist_uvqk: torch.Tensor, cand: DeviceJagged, x_cand: torch.Tensor, *,
+                           y_cand: Optional[torch.Tensor] = None,
+                           uvqk_cand: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None, stream=None):
+    """M-FALCON candidate micro-batch against a cached history.  Returns (y_cand, uvqk_cand)."""
+    lib = _lib.load()
+    _check(x_cand, torch.bfloat16, "x_cand")
+    _check(hist_uvqk, torch.bfloat16, "hist_uvqk")
+    T = cand.total_tokens
+    if y_cand is None:
+        y_cand = torch.empty((T, dims.d_model), dtype=torch.bfloat16, device=x_cand.device)
+    if uvqk_cand is None:
+        uvqk_cand = torch.empty((T, dims.uvqk_width), dtype=torch.bfloat16, device=x_cand.device)
+    d, wc, hs, cs = dims.c(), w.c(), hist.c(), cand.c()
+    need = int(lib.hstu_layer_workspace_bytes(ctypes.byref(d), ctypes.byref(cs)))
+    ws = _workspace(need, x_cand.device, workspace)
+    st = lib.hstu_layer_fwd_mfalcon(ctypes.byref(d), ctypes.byref(wc), ctypes.byref(hs),
+                                    _ptr(hist_uvqk), ctypes.byref(cs), _ptr(x_cand), _ptr(y_cand),
+                                    _ptr(uvqk_cand), _ptr(ws), ws.numel() * ws.element_size(),
+                                    _stream(stream))
+    _raise(st, "hstu_layer_fwd_mfalcon")
+    return y_cand, uvqk_cand
+
+
+def hstu_attn_fwd(dims: LayerDims, seq: DeviceJagged, q: torch.Tensor, k: torch.Tensor,
+                  v: torch.Tensor, *, row_stride: Optional[int] = None,
+                  rab_pos: Optional[torch.Tensor] = None, rab_time: Optional[torch.Tensor] = None,
+                  prefix: Optional[tuple] = None, mask: str = "causal",
+                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """Equation 2 alone, fp32 output [T][H*dv].
+
+    q, k, v: bf16 views whose rows are ``row_stride`` elements apart (they may be column
+    slices of one buffer).  prefix: (DeviceJagged, k_p, v_p, p_row_stride) or None.
+    """
+    lib = _lib.load()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise TypeError(f"{n}: expected a bf16 device tensor")
+    if row_stride is None:
+        row_stride = q.stride(0)
+    T = seq.total_tokens
+    if out is None:
+        out = torch.empty((T, dims.hdv), dtype=torch.float32, device=q.device)
+    _check(out, torch.float32, "out")
+    d, s = dims.c(), seq.c()
+    pref = None
+    keep = []
+    if prefix is not None:
+        pseq, kp, vp, pstride = prefix
+        ps = pseq.c()
+        keep.append(ps)
+        pref = _lib.Prefix(ctypes.pointer(ps), _ptr(kp), _ptr(vp), int(pstride))
+    need = int(lib.hstu_attn_workspace_bytes(ctypes.byref(d), ctypes.byref(s)))
+    ws = _workspace(need, q.device, workspace)
+    m = {"causal": _lib.MASK_CAUSAL, "self_only": _lib.MASK_SELF_ONLY}[mask]
+    st = lib.hstu_attn_fwd(ctypes.byref(d), _ptr(rab_pos), _ptr(rab_time), ctypes.byref(s),
+                           _ptr(q), _ptr(k), _ptr(v), int(row_stride),
+                           ctypes.byref(pref) if pref is not None else None, m, _ptr(out),
+                           _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _raise(st, "hstu_attn_fwd")
+    return out
+
+
+def hstu_validate_jagged(seq: DeviceJagged, stream=None) -> bool:
+    lib = _lib.load()
+    s = seq.c()
+    st = lib.hstu_validate_jagged(ctypes.byref(s), _stream(stream))
+    if st == _lib.HSTU_ERR_INVALID_ARG:
+        return False
+    _raise(st, "hstu_validate_jagged")
+    return True
+
+
+def profile_enable(on: bool = True):
+    _lib.load().hstu_profile_enable(1 if on else 0)
+
+
+def profile_reset():
+    _lib.load().hstu_profile_reset()
+
+
+def profile_collect() -> dict:
+    """{kernel name: (total ms, launches)} over the records since the last reset."""
+    lib = _lib.load()
+    tot = (ctypes.c_double * 5)()
+    cnt = (ctypes.c_int64 * 5)()
+    _raise(lib.hstu_profile_collect(tot, cnt), "hstu_profile_collect")
+    return {lib.hstu_kernel_name(i).decode(): (tot[i], cnt[i]) for i in range(5)}

@@ -1,0 +1,181 @@
+/*
+ * hstu.h -- C ABI of the MI355X (gfx950) HSTU layer forward library (libhstu.so).
+ *
+ * The layer is the one written in "Actions Speak Louder than Words" as retold on
+ * chenhuiyu.github.io ("生成式推荐 16: HSTU", section "HSTU Layer 到底改了什么",
+ * equations 1-3):
+ *
+ *     U, V, Q, K = Split(SiLU(f1(X)))                                   (1)
+ *     A(X)V      = SiLU(Q K^T + rab^{p,t}) V      pointwise, no softmax  (2)
+ *     Y          = f2(LayerNorm(A(X)V) * U)                              (3)
+ *
+ * computed on jagged batches at their true lengths (same page, section "另外三块拼图",
+ * item 1) under a causal mask, or under the M-FALCON candidate mask (same section,
+ * item 3; ltzyclt.github.io section 5.2).
+ *
+ * Conventions for every entry point
+ *  - Pointers marked (device) are HIP device pointers; everything else is host memory
+ *    read during the call only.  bf16 tensors are passed as uint16_t bit patterns.
+ *  - Row-major layouts.  Weights are "out x in": f1(X) = X w1^T + b1, f2(G) = G w2^T + b2.
+ *  - U|V|Q|K layout of the f1 output: columns [0,H*dv) = U, [H*dv,2H*dv) = V,
+ *    then H*dqk columns of Q and H*dqk of K; head h owns columns [h*dh,(h+1)*dh) of
+ *    each block.
+ *  - rab^{p,t}(i,j) = rab_pos[r][min(i-j, pos_buckets-1)]
+ *                   + rab_time[r][min(time_buckets-1, floor(log2(1 + max(0, ts_i-ts_j))))]
+ *    with r = h if rab_heads == num_heads else 0; the bias is added before SiLU.  The
+ *    time gap is taken over the full int32 range without overflow.
+ *  - Ownership: the caller owns every buffer.  The library allocates no device memory
+ *    and keeps no pointer after a call returns; scratch memory comes from the caller's
+ *    workspace.  Calls are asynchronous on `stream` (a hipStream_t, NULL = default
+ *    stream) and never synchronise, except hstu_validate_jagged.
+ *  - Errors: host-checkable problems return a status before anything is launched and
+ *    leave all outputs untouched; a failed launch returns HSTU_ERR_HIP and the HIP
+ *    error code is available from hstu_last_hip_error().  No exception crosses the ABI.
+ *  - Device-side jagged offsets are a precondition (0 = off[0] <= ... <= off[B] = T,
+ *    max length <= max_seq_len); they are not re-validated on the hot path.  Use
+ *    hstu_validate_jagged when in doubt.  Zero-length sequences are legal.
+ *  - Supported shapes: dqk == dv in {32, 64, 128}; 1 <= pos_buckets <= 1024;
+ *    1 <= time_buckets <= 64; rab_heads 1 or num_heads.  The layer entry points also
+ *    need d_model and num_heads*dv to be multiples of 64, and num_heads*dv <= 2048
+ *    (hstu_attn_fwd ignores d_model).
+ */
+#ifndef HSTU_H_
+#define HSTU_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HSTU_OK = 0,
+  HSTU_ERR_INVALID_ARG = 1, /* null pointer, negative size, inconsistent sizes        */
+  HSTU_ERR_UNSUPPORTED = 2, /* shape outside the supported set listed above           */
+  HSTU_ERR_WORKSPACE = 3,   /* workspace pointer null or smaller than required        */
+  HSTU_ERR_HIP = 4          /* a HIP call or kernel launch failed                     */
+} hstu_status_t;
+
+typedef enum {
+  /* Query i of a sequence (position n_p + i) sees every prefix key (positions
+   * 0..n_p-1) and its own sequence's keys j <= i (positions n_p + j).             */
+  HSTU_MASK_CAUSAL = 0,
+  /* M-FALCON candidates: every query sits at position n_p, sees every prefix key
+   * (the user's history) and itself (position gap 0, time gap 0), nothing else.   */
+  HSTU_MASK_SELF_ONLY = 1
+} hstu_mask_t;
+
+typedef struct {
+  int32_t d_model;      /* d: width of X and Y                                      */
+  int32_t num_heads;    /* H                                                        */
+  int32_t dqk;          /* per-head width of Q and K                                */
+  int32_t dv;           /* per-head width of V and U                                */
+  int32_t pos_buckets;  /* entries per row of rab_pos (64 in the configs)           */
+  int32_t time_buckets; /* entries per row of rab_time (32 in the configs)          */
+  int32_t rab_heads;    /* rows of each rab table: 1 (shared) or num_heads          */
+  float ln_eps;         /* LayerNorm epsilon (1e-5)                                 */
+} hstu_dims_t;
+
+typedef struct {
+  const uint16_t *w1;      /* (device) bf16 [2H(dv+dqk)][d]                         */
+  const float *b1;         /* (device) [2H(dv+dqk)] or NULL (no bias)               */
+  const uint16_t *w2;      /* (device) bf16 [d][H*dv]                               */
+  const float *b2;         /* (device) [d] or NULL                                  */
+  const float *ln_gamma;   /* (device) [H*dv] or NULL (= 1)                          */
+  const float *ln_beta;    /* (device) [H*dv] or NULL (= 0)                          */
+  const float *rab_pos;    /* (device) [rab_heads][pos_buckets] or NULL (no term)   */
+  const float *rab_time;   /* (device) [rab_heads][time_buckets] or NULL (no term)  */
+} hstu_weights_t;
+
+typedef struct {
+  int32_t batch;              /* B >= 0                                                */
+  int32_t total_tokens;       /* T = seq_offsets[B] (host copy)                        */
+  int32_t max_seq_len;        /* upper bound on every sequence length (host)           */
+  const int32_t *seq_offsets; /* (device) [B+1], non-decreasing, off[0] = 0            */
+  const int32_t *timestamps;  /* (device) [T] or NULL (time term off)                  */
+} hstu_jagged_t;
+
+/* Keys that precede each sequence's own tokens: the M-FALCON user history.  Sequence
+ * b of the query batch sees rows [seq->seq_offsets[b], seq->seq_offsets[b+1]) of k/v. */
+typedef struct {
+  const hstu_jagged_t *seq;   /* same batch size as the query batch                   */
+  const uint16_t *k;          /* (device) bf16, row r at k + r*row_stride               */
+  const uint16_t *v;          /* (device) bf16, row r at v + r*row_stride               */
+  int64_t row_stride;         /* elements between consecutive rows                     */
+} hstu_prefix_t;
+
+/* Workspace (bytes) needed by hstu_layer_fwd / hstu_layer_fwd_mfalcon for this batch;
+ * 0 when the arguments are invalid.  Alignment: 256 bytes.                           */
+size_t hstu_layer_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_t *seq);
+
+/* Workspace (bytes) needed by hstu_attn_fwd (the jagged tile schedule only).          */
+size_t hstu_attn_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_t *seq);
+
+/* One HSTU layer, equations (1)-(3), causal mask.
+ *   x    (device) bf16 [T][d]                       input rows
+ *   y    (device) bf16 [T][d]                       output rows (may not alias x)
+ *   uvqk (device) bf16 [T][2H(dv+dqk)]              f1 output, written; the caller may
+ *                                                   keep it as the K/V cache of an
+ *                                                   M-FALCON history
+ *   ws   (device) workspace of ws_bytes >= hstu_layer_workspace_bytes(dims, seq)    */
+hstu_status_t hstu_layer_fwd(const hstu_dims_t *dims, const hstu_weights_t *w,
+                             const hstu_jagged_t *seq, const uint16_t *x, uint16_t *y,
+                             uint16_t *uvqk, void *ws, size_t ws_bytes, void *stream);
+
+/* M-FALCON candidate micro-batch (ltzyclt.github.io section 5.2): f1 on the candidate
+ * rows, then each candidate of user b attends to the cached K/V of that user's history
+ * (hist_uvqk, the uvqk buffer written by hstu_layer_fwd on the history batch `hist`)
+ * and to itself only, then LayerNorm, gate and f2.  cand->timestamps are the
+ * candidates' request times.  The results of one candidate do not depend on which
+ * other candidates share its micro-batch.
+ *   hist_uvqk (device) bf16 [T_hist][2H(dv+dqk)]
+ *   x_cand    (device) bf16 [T_cand][d];   y_cand (device) bf16 [T_cand][d]
+ *   uvqk_cand (device) bf16 [T_cand][2H(dv+dqk)]
+ *   ws        >= hstu_layer_workspace_bytes(dims, cand)                              */
+hstu_status_t hstu_layer_fwd_mfalcon(const hstu_dims_t *dims, const hstu_weights_t *w,
+                                     const hstu_jagged_t *hist, const uint16_t *hist_uvqk,
+                                     const hstu_jagged_t *cand, const uint16_t *x_cand,
+                                     uint16_t *y_cand, uint16_t *uvqk_cand, void *ws,
+                                     size_t ws_bytes, void *stream);
+
+/* Equation (2) alone: out[t][h*dv + f] = sum_j SiLU(q_t.k_j + rab(t,j)) v_j[f] over the
+ * keys allowed by `mask` (see hstu_mask_t), fp32, no normalisation.
+ *   q, k, v (device) bf16; row t of head h at q + t*row_stride + h*dqk (same for k,v
+ *           with dqk / dv)
+ *   prefix  NULL or the keys preceding each sequence (required for SELF_ONLY)
+ *   out     (device) fp32 [T][H*dv], every row written
+ *   ws      >= hstu_attn_workspace_bytes(dims, seq)                                  */
+hstu_status_t hstu_attn_fwd(const hstu_dims_t *dims, const float *rab_pos,
+                            const float *rab_time, const hstu_jagged_t *seq,
+                            const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                            int64_t row_stride, const hstu_prefix_t *prefix,
+                            hstu_mask_t mask, float *out, void *ws, size_t ws_bytes,
+                            void *stream);
+
+/* Debug check of device offsets: off[0] == 0, non-decreasing, off[B] == total_tokens,
+ * every length <= max_seq_len.  Synchronises the stream.  Returns HSTU_OK or
+ * HSTU_ERR_INVALID_ARG.                                                              */
+hstu_status_t hstu_validate_jagged(const hstu_jagged_t *seq, void *stream);
+
+/* Static description of a status code.                                              */
+const char *hstu_status_str(hstu_status_t status);
+
+/* HIP error code of the last HSTU_ERR_HIP returned on this thread (0 if none).       */
+int hstu_last_hip_error(void);
+
+/* Optional per-kernel timing with HIP events on the launch stream (off by default).
+ * While enabled, every kernel the library launches is bracketed by two events; the
+ * durations are collected by hstu_profile_collect, which synchronises the events.
+ * Kernel ids: 0 schedule, 1 f1 GEMM, 2 attention, 3 norm-gate, 4 f2 GEMM.          */
+void hstu_profile_enable(int on);
+void hstu_profile_reset(void);
+/* Adds up finished records: total_ms[k] and launches[k] for k in [0, 5).           */
+hstu_status_t hstu_profile_collect(double *total_ms, int64_t *launches);
+const char *hstu_kernel_name(int kernel_id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSTU_H_ */

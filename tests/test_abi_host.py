@@ -1,0 +1,143 @@
+"""Host-side checks of the C ABI (CPU only: nothing here launches a kernel).
+
+The library must load without a GPU, export every function declared in include/hstu.h,
+and reject bad arguments with the documented status before touching the device.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from hstu_pointwise_attention_jagged_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hstu.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hstu_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.EXPORTS), "binding and header disagree"
+
+
+def test_struct_layouts_match_header():
+    assert ctypes.sizeof(_lib.Dims) == 32
+    assert ctypes.sizeof(_lib.Weights) == 64
+    assert _lib.Jagged.seq_offsets.offset == 16 and ctypes.sizeof(_lib.Jagged) == 32
+    assert ctypes.sizeof(_lib.Prefix) == 32
+
+
+def _dims(**kw):
+    base = dict(d_model=64, num_heads=2, dqk=32, dv=32, pos_buckets=64, time_buckets=32,
+                rab_heads=1, ln_eps=1e-5)
+    base.update(kw)
+    return _lib.Dims(*base.values())
+
+
+FAKE = 0x7f0000000000  # aligned, never dereferenced: every call below fails validation
+
+
+def _seq(B=4, T=118, L=64):
+    return _lib.Jagged(B, T, L, FAKE, FAKE)
+
+
+def _call_layer(lib, dims, seq=None, ws_bytes=1 << 30, x=FAKE, y=FAKE + 4096, uvqk=FAKE,
+                w=None, ws=FAKE):
+    w = w or _lib.Weights(FAKE, None, FAKE, None, None, None, None, None)
+    seq = seq or _seq()
+    return lib.hstu_layer_fwd(ctypes.byref(dims) if dims is not None else None, ctypes.byref(w),
+                              ctypes.byref(seq), x, y, uvqk, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dqk=48, dv=48), _lib.HSTU_ERR_UNSUPPORTED),
+    (dict(dqk=32, dv=64), _lib.HSTU_ERR_UNSUPPORTED),
+    (dict(d_model=96), _lib.HSTU_ERR_UNSUPPORTED),
+    (dict(num_heads=3, dqk=32, dv=32), _lib.HSTU_ERR_UNSUPPORTED),  # H*dv = 96
+    (dict(num_heads=0), _lib.HSTU_ERR_INVALID_ARG),
+    (dict(rab_heads=3), _lib.HSTU_ERR_INVALID_ARG),
+    (dict(pos_buckets=0), _lib.HSTU_ERR_INVALID_ARG),
+    (dict(pos_buckets=2000), _lib.HSTU_ERR_UNSUPPORTED),
+    (dict(time_buckets=65), _lib.HSTU_ERR_UNSUPPORTED),
+    (dict(ln_eps=-1.0), _lib.HSTU_ERR_INVALID_ARG),
+    (dict(ln_eps=float("nan")), _lib.HSTU_ERR_INVALID_ARG),
+])
+def test_bad_dims_rejected(lib, kw, status):
+    assert _call_layer(lib, _dims(**kw)) == status
+
+
+def test_bad_arguments_rejected(lib):
+    assert _call_layer(lib, None) == _lib.HSTU_ERR_INVALID_ARG
+    assert _call_layer(lib, _dims(), seq=_lib.Jagged(-1, 0, 0, FAKE, None)) == _lib.HSTU_ERR_INVALID_ARG
+    assert _call_layer(lib, _dims(), seq=_lib.Jagged(0, 5, 5, FAKE, None)) == _lib.HSTU_ERR_INVALID_ARG
+    assert _call_layer(lib, _dims(), seq=_lib.Jagged(2, 10, 5, None, None)) == _lib.HSTU_ERR_INVALID_ARG
+    assert _call_layer(lib, _dims(), x=None) == _lib.HSTU_ERR_INVALID_ARG
+    assert _call_layer(lib, _dims(), x=FAKE + 2) == _lib.HSTU_ERR_INVALID_ARG  # misaligned
+    assert _call_layer(lib, _dims(), y=FAKE) == _lib.HSTU_ERR_INVALID_ARG      # y aliases x
+    assert _call_layer(lib, _dims(),
+                       w=_lib.Weights(None, None, FAKE, None, None, None, None, None)) == _lib.HSTU_ERR_INVALID_ARG
+
+
+def test_workspace_checks(lib):
+    d, s = _dims(), _seq()
+    need = lib.hstu_layer_workspace_bytes(ctypes.byref(d), ctypes.byref(s))
+    T, hdv = 118, 64
+    assert need >= T * hdv * 6
+    assert need % 256 == 0
+    assert _call_layer(lib, d, ws_bytes=need - 1) == _lib.HSTU_ERR_WORKSPACE
+    assert _call_layer(lib, d, ws=None) == _lib.HSTU_ERR_WORKSPACE
+    assert _call_layer(lib, d, ws=FAKE + 16) == _lib.HSTU_ERR_WORKSPACE  # not 256-aligned
+    bad = _dims(dqk=48, dv=48)
+    assert lib.hstu_layer_workspace_bytes(ctypes.byref(bad), ctypes.byref(s)) == 0
+    a = lib.hstu_attn_workspace_bytes(ctypes.byref(d), ctypes.byref(s))
+    assert 0 < a < need
+
+
+def test_empty_batch_is_a_no_op(lib):
+    # B = 0 returns OK without launching anything (nothing to compute)
+    s = _lib.Jagged(0, 0, 0, FAKE, None)
+    assert _call_layer(lib, _dims(), seq=s) == _lib.HSTU_OK
+
+
+def test_attn_and_mfalcon_argument_checks(lib):
+    d, s = _dims(), _seq()
+    ws = 1 << 20
+    # row stride smaller than H*dqk
+    assert lib.hstu_attn_fwd(ctypes.byref(d), None, None, ctypes.byref(s), FAKE, FAKE, FAKE, 32,
+                             None, 0, FAKE, FAKE, ws, None) == _lib.HSTU_ERR_INVALID_ARG
+    # unknown mask
+    assert lib.hstu_attn_fwd(ctypes.byref(d), None, None, ctypes.byref(s), FAKE, FAKE, FAKE, 256,
+                             None, 7, FAKE, FAKE, ws, None) == _lib.HSTU_ERR_INVALID_ARG
+    # prefix batch size mismatch
+    ps = _seq(B=3)
+    pref = _lib.Prefix(ctypes.pointer(ps), FAKE, FAKE, 256)
+    assert lib.hstu_attn_fwd(ctypes.byref(d), None, None, ctypes.byref(s), FAKE, FAKE, FAKE, 256,
+                             ctypes.byref(pref), 1, FAKE, FAKE, ws, None) == _lib.HSTU_ERR_INVALID_ARG
+    w = _lib.Weights(FAKE, None, FAKE, None, None, None, None, None)
+    h = _seq(B=3)
+    assert lib.hstu_layer_fwd_mfalcon(ctypes.byref(d), ctypes.byref(w), ctypes.byref(h), FAKE,
+                                      ctypes.byref(s), FAKE, FAKE + 4096, FAKE, FAKE, 1 << 30,
+                                      None) == _lib.HSTU_ERR_INVALID_ARG
+
+
+def test_status_strings_and_kernel_names(lib):
+    for code in range(5):
+        assert lib.hstu_status_str(code)
+    assert lib.hstu_status_str(99) == b"unknown status"
+    assert [lib.hstu_kernel_name(i).decode() for i in range(5)] == list(_lib.KERNEL_IDS)
+    assert lib.hstu_last_hip_error() == 0

@@ -1,0 +1,344 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Bars (from the layer's contract): bf16 layer outputs within max-abs 2e-2 and mean-abs
+2e-3 of the oracle; the raw fp32 attention output within the same bounds after dividing
+by the oracle's row standard deviation; integer paths (offsets, masks, rab indices)
+bit-exact, checked by decodable probes whose every (i, j) entry must recover the
+oracle's table index exactly and whose masked entries must be exactly 0.
+"""
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from hstu_pointwise_attention_jagged_amd import device as dev  # noqa: E402
+from hstu_pointwise_attention_jagged_amd import ops  # noqa: E402
+from hstu_pointwise_attention_jagged_amd import workloads as wl  # noqa: E402
+from oracle import hstu_ref as ref  # noqa: E402
+from oracle import stochastic_length as sl  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, MEAN_ABS = 2e-2, 2e-3
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from hstu_pointwise_attention_jagged_amd import _lib
+    _lib.load()
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+# ----------------------------------------------------------------------------------
+# helpers
+# ----------------------------------------------------------------------------------
+
+def _layer_check(w, *, rows=None, tag=""):
+    d = w.dims
+    say(f"[layer] {tag} {w.name} B={w.seq.batch} T={w.seq.total} d={d.d_model} H={d.num_heads} dh={d.dqk}")
+    y, uvqk = ops.hstu_layer_fwd(dev.dims_of(d), dev.weights_of(w.weights), dev.jagged_of(w.seq),
+                                 dev.bf16_tensor(w.x))
+    torch.cuda.synchronize()
+    got = dev.bf16_to_numpy(y).astype(np.float64)
+    want = ref.layer_fwd(w.x, w.weights, w.seq.offsets, w.seq.timestamps, d.num_heads, d.dqk,
+                         d.dv, d.ln_eps, rows=rows)
+    if rows is not None:
+        got, want = got[rows], want[rows]
+    err = np.abs(got - want)
+    say(f"        max_abs={err.max():.3e} mean_abs={err.mean():.3e}")
+    assert np.all(np.isfinite(got))
+    assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS
+    return y, uvqk
+
+
+def _attn_inputs(seed, lengths, H, dh, *, ts_scale=1):
+    rng = np.random.default_rng(seed)
+    seq = wl.jagged_from_lengths(rng, lengths)
+    if ts_scale != 1:
+        seq.timestamps = (seq.timestamps.astype(np.int64) * ts_scale).astype(np.int32)
+    T = seq.total
+    q, k, v = (wl.round_bf16(rng.standard_normal((T, H * dh), dtype=np.float32)) for _ in range(3))
+    P = (0.5 * rng.standard_normal((1, 64))).astype(np.float32)
+    Tt = (0.5 * rng.standard_normal((1, 32))).astype(np.float32)
+    return seq, q, k, v, P, Tt
+
+
+def _attn_gpu(seq, q, k, v, H, dh, P, Tt, *, prefix=None, mask="causal", with_time=True):
+    dims = ops.LayerDims(d_model=max(64, H * dh), num_heads=H, dqk=dh, dv=dh,
+                         pos_buckets=P.shape[1] if P is not None else 64,
+                         time_buckets=Tt.shape[1] if Tt is not None else 32,
+                         rab_heads=P.shape[0] if P is not None else 1)
+    qkv = np.concatenate([q, k, v], axis=1)
+    buf = dev.bf16_tensor(qkv)
+    hq = H * dh
+    pref = None
+    if prefix is not None:
+        pseq, kp, vp = prefix
+        pbuf = dev.bf16_tensor(np.concatenate([kp, vp], axis=1))
+        pref = (dev.jagged_of(pseq, with_time=with_time), pbuf[:, :hq], pbuf[:, hq:], pbuf.stride(0))
+    out = ops.hstu_attn_fwd(dims, dev.jagged_of(seq, with_time=with_time), buf[:, :hq],
+                            buf[:, hq:2 * hq], buf[:, 2 * hq:], row_stride=buf.stride(0),
+                            rab_pos=dev.f32_tensor(P), rab_time=dev.f32_tensor(Tt), prefix=pref,
+                            mask=mask)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def _rel_err(got, want):
+    scale = np.maximum(want.std(axis=1, keepdims=True), 1e-30)
+    return np.abs(got - want) / scale
+
+
+# ----------------------------------------------------------------------------------
+# attention alone
+# ----------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("H,dh,lengths", [
+    (2, 32, [5, 17, 32, 64]),
+    (2, 64, [0, 1, 130, 0, 257, 63, 64, 65]),
+    (2, 128, [1, 300, 129, 700]),
+    (1, 128, [2000]),
+])
+def test_attention_causal_matches_oracle(H, dh, lengths):
+    say(f"[attn] causal H={H} dh={dh} lengths={lengths}")
+    seq, q, k, v, P, Tt = _attn_inputs(40 + dh, lengths, H, dh)
+    got = _attn_gpu(seq, q, k, v, H, dh, P, Tt)
+    want = ref.attention(q, k, v, seq.offsets, seq.timestamps, H, dh, dh, P, Tt)
+    e = _rel_err(got, want)
+    say(f"        max_rel={e.max():.3e} mean_rel={e.mean():.3e}")
+    assert e.max() <= MAX_ABS and e.mean() <= MEAN_ABS
+
+
+def test_attention_per_head_tables_and_no_time():
+    H, dh = 4, 64
+    seq, q, k, v, _, _ = _attn_inputs(51, [33, 90, 0, 200], H, dh)
+    rng = np.random.default_rng(5)
+    P = (0.5 * rng.standard_normal((H, 48))).astype(np.float32)
+    Tt = (0.5 * rng.standard_normal((H, 20))).astype(np.float32)
+    say("[attn] per-head tables")
+    got = _attn_gpu(seq, q, k, v, H, dh, P, Tt)
+    want = ref.attention(q, k, v, seq.offsets, seq.timestamps, H, dh, dh, P, Tt)
+    assert _rel_err(got, want).max() <= MAX_ABS
+    say("[attn] no timestamps")
+    got = _attn_gpu(seq, q, k, v, H, dh, P, Tt, with_time=False)
+    want = ref.attention(q, k, v, seq.offsets, None, H, dh, dh, P, None)
+    assert _rel_err(got, want).max() <= MAX_ABS
+
+
+def test_attention_self_only_with_prefix_matches_oracle():
+    H, dh = 2, 64
+    rng = np.random.default_rng(61)
+    n_h, n_c = [100, 0, 257, 64], [7, 3, 130, 1]
+    hist = wl.jagged_from_lengths(rng, n_h)
+    T_h = hist.total
+    kp, vp = (wl.round_bf16(rng.standard_normal((T_h, H * dh), dtype=np.float32)) for _ in range(2))
+    seq, q, k, v, P, Tt = _attn_inputs(62, n_c, H, dh)
+    # candidates ask at a request time after the user's history
+    last = np.array([hist.timestamps[hist.offsets[b + 1] - 1] if n_h[b] else 0 for b in range(4)])
+    seq.timestamps = np.repeat(last + 50, n_c).astype(np.int32)
+    say("[attn] self-only + prefix")
+    got = _attn_gpu(seq, q, k, v, H, dh, P, Tt, prefix=(hist, kp, vp), mask="self_only")
+    want = ref.attention(q, k, v, seq.offsets, seq.timestamps, H, dh, dh, P, Tt,
+                         prefix=(kp, vp, hist.offsets, hist.timestamps), mask=ref.SELF_ONLY)
+    e = _rel_err(got, want)
+    say(f"        max_rel={e.max():.3e} mean_rel={e.mean():.3e}")
+    assert e.max() <= MAX_ABS and e.mean() <= MEAN_ABS
+
+
+# ----------------------------------------------------------------------------------
+# bit-exact integer paths: decodable probes
+# ----------------------------------------------------------------------------------
+
+def _decode(values, table):
+    cand = ref.silu(np.asarray(table, dtype=np.float64))
+    return np.abs(values[..., None] - cand).argmin(axis=-1)
+
+
+def _probe(lengths, *, kind, dh=128, seed=0, prefix_lengths=None):
+    """Q = K = 0, V one-hot over key index (mod dh): out = SiLU(rab) exactly on allowed pairs."""
+    rng = np.random.default_rng(seed)
+    H = 1
+    seq = wl.jagged_from_lengths(rng, lengths)
+    # wide, unsorted timestamps: gaps of any size and sign, up to the int32 range
+    seq.timestamps = rng.integers(-2**31, 2**31, size=seq.total, dtype=np.int64).astype(np.int32)
+    if kind == "pos":
+        P = (1.0 + np.arange(64) / 8.0)[None].astype(np.float32)
+        Tt = None
+    else:
+        P = None
+        Tt = (1.0 + np.arange(32) / 4.0)[None].astype(np.float32)
+        # a dense band of small gaps too
+        for b in range(seq.batch):
+            s0, s1 = seq.offsets[b], seq.offsets[b + 1]
+            if s1 - s0 > 4 and b % 2 == 0:
+                seq.timestamps[s0:s1] = np.cumsum(rng.integers(0, 40, size=s1 - s0)).astype(np.int32)
+    T = seq.total
+    q = np.zeros((T, dh), np.float32)
+    k = np.zeros((T, dh), np.float32)
+    v = np.zeros((T, dh), np.float32)
+    # own keys one-hot on columns base + i; prefix keys (if any) on columns j < base
+    base = 64 if prefix_lengths is not None else 0
+    for b in range(seq.batch):
+        s0, s1 = seq.offsets[b], seq.offsets[b + 1]
+        v[s0 + np.arange(s1 - s0), (base + np.arange(s1 - s0)) % dh] = 1.0
+    prefix = None
+    pre_ref = None
+    mask = "causal"
+    if prefix_lengths is not None:
+        hist = wl.jagged_from_lengths(rng, prefix_lengths)
+        hist.timestamps = rng.integers(-2**31, 2**31, size=hist.total, dtype=np.int64).astype(np.int32)
+        kp = np.zeros((hist.total, dh), np.float32)
+        vp = np.zeros((hist.total, dh), np.float32)
+        for b in range(hist.batch):
+            s0, s1 = hist.offsets[b], hist.offsets[b + 1]
+            vp[s0 + np.arange(s1 - s0), np.arange(s1 - s0) % dh] = 1.0
+        prefix = (hist, kp, vp)
+        pre_ref = (kp, vp, hist.offsets, hist.timestamps)
+        mask = "self_only"
+    got = _attn_gpu(seq, q, k, v, H, dh, P, Tt, prefix=prefix, mask=mask)
+    want = ref.attention(q, k, v, seq.offsets, seq.timestamps, H, dh, dh, P, Tt, prefix=pre_ref,
+                         mask=ref.SELF_ONLY if prefix is not None else ref.CAUSAL)
+    return got, want, (P if kind == "pos" else Tt)[0]
+
+
+@pytest.mark.parametrize("kind", ["pos", "time"])
+@pytest.mark.parametrize("lengths", [[5, 17, 32, 64], [0, 1, 128, 0, 100, 127, 3]])
+def test_probe_rab_indices_bit_exact(kind, lengths):
+    say(f"[probe] {kind} lengths={lengths}")
+    got, want, table = _probe(lengths, kind=kind, seed=len(lengths))
+    zero = want == 0.0
+    assert np.all(got[zero] == 0.0), "masked pairs must be exactly zero"
+    nz = ~zero
+    np.testing.assert_array_equal(_decode(got[nz], table), _decode(want[nz], table))
+
+
+@pytest.mark.parametrize("kind", ["pos", "time"])
+def test_probe_mfalcon_indices_bit_exact(kind):
+    say(f"[probe] mfalcon {kind}")
+    got, want, table = _probe([3, 60, 1, 0], kind=kind, seed=9, prefix_lengths=[40, 64, 0, 20])
+    zero = want == 0.0
+    assert np.all(got[zero] == 0.0)
+    np.testing.assert_array_equal(_decode(got[~zero], table), _decode(want[~zero], table))
+
+
+# ----------------------------------------------------------------------------------
+# whole layer
+# ----------------------------------------------------------------------------------
+
+def test_layer_tiny_config():
+    _layer_check(wl.config(0))
+
+
+def test_layer_tiny_with_bias_affine_per_head_rab():
+    w = wl.config(0)
+    d = w.dims
+    d.rab_heads = d.num_heads
+    w.weights = wl.draw_weights(np.random.default_rng(3), d, bias=True, affine=True, rab_std=0.3)
+    _layer_check(w, tag="bias+affine+per-head-rab")
+
+
+def test_layer_ragged_with_empty_sequences():
+    dims = wl.LayerDims(d_model=128, num_heads=2, dqk=64, dv=64)
+    _layer_check(wl.random_layer(5, [0, 1, 127, 128, 129, 0, 300, 2], dims, bias=True), tag="ragged")
+
+
+def test_layer_zipf_config():
+    _layer_check(wl.config(1))
+
+
+def test_layer_long_uniform_config_sampled_rows():
+    w = wl.config(2)
+    rng = np.random.default_rng(0)
+    off = w.seq.offsets
+    rows = sorted(set([0, 1, 127, 128, 8191]) | set(rng.integers(0, 8192, 11).tolist()) |
+                  set((off[7] + np.array([0, 8191, 4000])).tolist()))
+    _layer_check(w, rows=rows, tag="full size, sampled rows")
+
+
+def test_layer_stochastic_length_batch_sampled_rows():
+    w = wl.config(3)
+    kept, new_off = sl.select(w.raw.seq.offsets, w.raw.u_keep, w.raw.keys, w.raw.n_target, w.raw.alpha)
+    w.seq = wl.Jagged(offsets=new_off, timestamps=w.raw.seq.timestamps[kept])
+    w.x = w.raw.x[kept]
+    lens = np.diff(new_off)
+    say(f"[sl] kept T={new_off[-1]} of {w.raw.seq.total}; full users={int(np.sum(lens > 776))}")
+    b_long = int(np.argmax(lens))
+    rows = [int(new_off[b_long]), int(new_off[b_long + 1] - 1), int(new_off[5] + 3), int(new_off[-1] - 1)]
+    _layer_check(w, rows=rows, tag="stochastic length")
+
+
+def test_layer_deterministic_and_guard_band():
+    w = wl.config(1, batch=16)
+    d = w.dims
+    T = w.seq.total
+    dims, wts, seq = dev.dims_of(d), dev.weights_of(w.weights), dev.jagged_of(w.seq)
+    x = dev.bf16_tensor(w.x)
+    big = torch.full((T + 64, d.d_model), 7.0, dtype=torch.bfloat16, device="cuda")
+    ubig = torch.full((T + 64, d.uvqk_width), 7.0, dtype=torch.bfloat16, device="cuda")
+    say("[layer] determinism + guard band")
+    ops.hstu_layer_fwd(dims, wts, seq, x, y=big[:T], uvqk=ubig[:T])
+    y1 = big[:T].clone()
+    ops.hstu_layer_fwd(dims, wts, seq, x, y=big[:T], uvqk=ubig[:T])
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), big[:T].view(torch.int16))
+    assert torch.all(big[T:] == 7.0) and torch.all(ubig[T:] == 7.0)
+
+
+def test_validate_jagged():
+    good = wl.jagged_from_lengths(np.random.default_rng(1), [3, 0, 9])
+    j = dev.jagged_of(good)
+    assert ops.hstu_validate_jagged(j)
+    bad = dev.jagged_of(good)
+    bad.offsets = dev.i32_tensor(np.array([0, 3, 2, 12]))
+    assert not ops.hstu_validate_jagged(bad)
+    short = dev.jagged_of(good)
+    short.max_seq_len = 5
+    assert not ops.hstu_validate_jagged(short)
+
+
+# ----------------------------------------------------------------------------------
+# M-FALCON
+# ----------------------------------------------------------------------------------
+
+def _mfalcon(w, cand, xc, bm):
+    """History pass once, then candidates in micro-batches of bm per user."""
+    d = w.dims
+    dims, wts = dev.dims_of(d), dev.weights_of(w.weights)
+    hist = dev.jagged_of(w.seq)
+    y_h, uvqk_h = ops.hstu_layer_fwd(dims, wts, hist, dev.bf16_tensor(w.x))
+    n_c = np.diff(cand.offsets.astype(np.int64))
+    assert np.all(n_c == n_c[0])
+    outs = np.zeros((cand.total, d.d_model), np.float32)
+    for start in range(0, int(n_c[0]), bm):
+        m = min(bm, int(n_c[0]) - start)
+        sel = np.concatenate([cand.offsets[b] + start + np.arange(m) for b in range(cand.batch)])
+        mc = wl.Jagged(offsets=wl.offsets_from_lengths(np.full(cand.batch, m)),
+                       timestamps=cand.timestamps[sel])
+        y_c, _ = ops.hstu_layer_fwd_mfalcon(dims, wts, hist, uvqk_h, dev.jagged_of(mc),
+                                            dev.bf16_tensor(xc[sel]))
+        torch.cuda.synchronize()
+        outs[sel] = dev.bf16_to_numpy(y_c)
+    return dev.bf16_to_numpy(y_h), outs
+
+
+def test_mfalcon_matches_oracle_and_microbatch_bitwise():
+    w = wl.config(4, batch=4, seq_len=512)  # 4 users x (512 history + 128 candidates)
+    d = w.dims
+    say(f"[mfalcon] B={w.seq.batch} hist={w.seq.lengths[0]} cand={w.cand.lengths[0]}")
+    y_h, y_c = _mfalcon(w, w.cand, w.x_cand, bm=128)
+    _, y_c16 = _mfalcon(w, w.cand, w.x_cand, bm=16)
+    assert np.array_equal(y_c.view(np.uint32), y_c16.view(np.uint32)), "b_m changed the result"
+    want_h, want_c = ref.mfalcon_fwd(w.x, w.seq.offsets, w.seq.timestamps, w.x_cand, w.cand.offsets,
+                                     w.cand.timestamps, w.weights, d.num_heads, d.dqk, d.dv, d.ln_eps)
+    for name, got, want in (("history", y_h, want_h), ("candidates", y_c, want_c)):
+        err = np.abs(got.astype(np.float64) - want)
+        say(f"        {name}: max_abs={err.max():.3e} mean_abs={err.mean():.3e}")
+        assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS
