@@ -1,0 +1,203 @@
+"""Benchmark: jagged HSTU layer forward on one MI355X.
+
+A step is one forward pass of a 24-layer HSTU stack (independent random weights per
+layer, Y of layer l is X of layer l+1) over the 8 x 8192-token batch, d = 1024, 8 heads
+of 128, causal mask with positional + log-time relative bias: every kernel of the hot
+path (jagged schedule, f1 + SiLU, pointwise attention, LayerNorm + gate, f2) runs once
+per layer.  Inputs and weights are resident in HBM before the timed region.
+
+Prints one JSON line on stdout; progress goes to stderr.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers 24] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "HSTU jagged attn+layer fwd TFLOP/s (bf16) and % MFMA peak at N=8192, 1 GPU"
+PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 MFMA
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attention_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "hstu_pointwise_attention_jagged_amd", "csrc", "attention.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def useful_flops(lengths, d, H, dqk, dv):
+    """MFMA work of one layer over unpadded sequences (elementwise work not counted).
+
+    f1: 2 T d 2H(dqk+dv); attention: H (dqk+dv) n (n+1) per sequence (QK^T and AV over
+    the causal triangle, diagonal included); f2: 2 T H dv d.
+    """
+    T = int(sum(lengths))
+    f1 = 2 * T * d * 2 * H * (dqk + dv)
+    att = sum(H * (dqk + dv) * int(n) * (int(n) + 1) for n in lengths)
+    f2 = 2 * T * H * dv * d
+    return f1, att, f2
+
+
+def file_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_record():
+    """HBM bytes per attention launch from committed counter runs, if still current."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("attention_hip_sha256") != file_sha(ATTN_SRC):
+        return None  # kernel changed since the counters were taken
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, layers):
+    """fp64 oracle on one 8192-token sequence of the same batch, one layer."""
+    import numpy as np
+    from oracle import hstu_ref
+
+    d = w.dims
+    cores = min(os.cpu_count() or 1, 16)
+    s0, s1 = int(w.seq.offsets[0]), int(w.seq.offsets[1])
+    x = w.x[s0:s1]
+    off = np.array([0, s1 - s0], dtype=np.int32)
+    ts = w.seq.timestamps[s0:s1]
+    t0 = time.perf_counter()
+    hstu_ref.layer_fwd(x, w.weights, off, ts, d.num_heads, d.dqk, d.dv, d.ln_eps, workers=cores)
+    dt = time.perf_counter() - t0
+    f1, att, f2 = useful_flops([s1 - s0], d.d_model, d.num_heads, d.dqk, d.dv)
+    return {"value": round((f1 + att + f2) / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"one layer (not the {layers}-layer stack) on 1 of the 8 sequences "
+                      f"(8192 tokens), fp64 NumPy, {dt:.1f} s",
+            "seconds": round(dt, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--layers", type=int, default=24)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); the jagged batch would "
+              "shard by sequence with no exchange across GPUs, which this build does not run.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from hstu_pointwise_attention_jagged_amd import device as dev
+    from hstu_pointwise_attention_jagged_amd import ops
+    from hstu_pointwise_attention_jagged_amd import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    log("building inputs (8 x 8192 tokens, d=1024, 8x128 heads)")
+    w = wl.config(2)
+    d = w.dims
+    dims = dev.dims_of(d)
+    seq = dev.jagged_of(w.seq)
+    T = w.seq.total
+    rng = np.random.default_rng(1000)
+    layer_w = [dev.weights_of(w.weights)]
+    for _ in range(args.layers - 1):
+        layer_w.append(dev.weights_of(wl.draw_weights(rng, d)))
+    x0 = dev.bf16_tensor(w.x)
+    bufs = [torch.empty_like(x0), torch.empty_like(x0)]
+    uvqk = torch.empty((T, d.uvqk_width), dtype=torch.float16, device="cuda")
+    ws = torch.empty(ops.hstu_layer_workspace_bytes(dims, seq), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        x = x0
+        for l in range(args.layers):
+            y = bufs[l & 1]
+            ops.hstu_layer_fwd(dims, layer_w[l], seq, x, y=y, uvqk=uvqk, workspace=ws, stream=stream)
+            x = y
+        return x
+
+    log(f"warmup {args.warmup} steps of {args.layers} layers")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ops.profile_reset()
+    ops.profile_enable(True)
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ops.profile_enable(False)
+    kern = ops.profile_collect()
+    ops.profile_reset()
+
+    lengths = w.seq.lengths.tolist()
+    f1, att, f2 = useful_flops(lengths, d.d_model, d.num_heads, d.dqk, d.dv)
+    flops_step = (f1 + att + f2) * args.layers
+    ms = elapsed / args.steps * 1e3
+    tflops = flops_step / (elapsed / args.steps) / 1e12
+
+    att_ms, att_n = kern["attention"]
+    att_avg_ms = att_ms / max(att_n, 1)
+    achieved = att / (att_avg_ms * 1e-3) / 1e12
+    per_kernel = {k: round(v[0] / max(v[1], 1), 4) for k, v in kern.items()}
+    traffic = traffic_record()
+    log(f"step {ms:.2f} ms, {tflops:.1f} TFLOP/s; per-kernel avg ms {per_kernel}")
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 I/O and f1/f2 operands, fp16 attention operands, fp32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": f"uniform 8x8192 jagged batch, d=1024, 8 heads x 128, causal, "
+                               f"rab pos+time, {args.layers}-layer stack",
+                   "batch": 8, "seq_len": 8192, "d_model": 1024, "num_heads": 8, "head_dim": 128,
+                   "layers": args.layers, "parallelism": "single GPU"},
+        "pct_mfma_peak": round(100 * tflops / PEAK_MFMA_TFLOPS, 2),
+        "useful_tflop_per_layer": round((f1 + att + f2) / 1e12, 4),
+        "kernel_avg_ms": per_kernel,
+        "roofline": {"kernel": "attention", "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
+                     "traffic": traffic,
+                     "algorithmic_flops_per_launch": att, "avg_launch_ms": round(att_avg_ms, 4)},
+        "cpu_baseline": None,
+        "host": platform.node(),
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline: fp64 oracle, one layer on one 8192-token sequence")
+        out["cpu_baseline"] = cpu_baseline(w, args.layers)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

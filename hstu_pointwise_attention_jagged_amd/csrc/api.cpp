@@ -184,7 +184,7 @@ hstu_status_t run_layer(const hstu_dims_t *d, const hstu_weights_t *w, const hst
                            max_prefix, lw.work, lw.n_work, st);
   });
   if (e != hipSuccess) return hip_fail(e);
-  e = timed(1, st, [&] { return launch_gemm(x, w->w1, w->b1, uvqk, T, n1, d->d_model, ACT_SILU, st); });
+  e = timed(1, st, [&] { return launch_gemm(x, w->w1, w->b1, uvqk, T, n1, d->d_model, ACT_SILU, OUT_F16, st); });
   if (e != hipSuccess) return hip_fail(e);
   const int64_t cap = attn_work_capacity(s->batch, T);
   e = timed(2, st, [&] { return launch_attention(aa, d->dqk, cap, st); });
@@ -193,7 +193,7 @@ hstu_status_t run_layer(const hstu_dims_t *d, const hstu_weights_t *w, const hst
     return launch_norm_gate(lw.o, uvqk, n1, w->ln_gamma, w->ln_beta, d->ln_eps, lw.g, T, hdv, st);
   });
   if (e != hipSuccess) return hip_fail(e);
-  e = timed(4, st, [&] { return launch_gemm(lw.g, w->w2, w->b2, y, T, d->d_model, hdv, ACT_NONE, st); });
+  e = timed(4, st, [&] { return launch_gemm(lw.g, w->w2, w->b2, y, T, d->d_model, hdv, ACT_NONE, OUT_BF16, st); });
   if (e != hipSuccess) return hip_fail(e);
   return HSTU_OK;
 }

@@ -12,10 +12,11 @@
 //    stored row-major; V is stored transposed (feature-major) with a key permutation
 //    inside each 16-key group, so the MFMA A operand of the P.V product is one 16-byte
 //    LDS read per lane.
-//  * Scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16), so that each
+//  * Scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_f16), so that each
 //    lane's accumulator holds 16 keys of one query; after bias, SiLU and masking these
 //    16 values are exactly the lane's B operand (8 keys per k-step) of O^T += V^T P^T,
-//    with no trip through LDS.  A is rounded to bf16 for that MFMA; O stays fp32.
+//    with no trip through LDS.  Q, K, V and A are fp16 operands (the same MFMA rate as
+//    bf16 on gfx950, 3 more mantissa bits); accumulation and O stay fp32.
 //  * The rab index math is integer only: relative position clamp, and the log2 time
 //    bucket from the bit length of (1 + gap); table values come from LDS.
 //  * Tiles are skipped from the jagged offsets and the mask: a wave never multiplies a
@@ -34,7 +35,7 @@ constexpr int kBN = kAttnBlockN;  // 64 keys per stage
 constexpr int kThreads = 256;
 constexpr int kMaxPos = 1024;
 constexpr int kMaxTime = 64;
-constexpr int kVtPitch = kBN + 8;  // transposed V row pitch (bf16): 144 bytes
+constexpr int kVtPitch = kBN + 8;  // transposed V row pitch (fp16): 144 bytes
 
 // Physical slot of key kk (0..63) inside a transposed V stage: within each group of 16
 // keys the order is [0-3, 8-11, 4-7, 12-15], which puts the 8 keys a lane multiplies in
@@ -46,7 +47,7 @@ __device__ __forceinline__ int vt_slot(int kk) {
 
 template <int DH, int MASK>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs p) {
-  constexpr int KPITCH = DH + 8;        // K row pitch (bf16)
+  constexpr int KPITCH = DH + 8;        // K row pitch (fp16)
   constexpr int KS = DH / 16;           // k-steps of the score MFMA
   constexpr int FT = DH / 32;           // 32-wide feature tiles of the output
   constexpr int K_CHUNKS = (kBN * DH / 8) / kThreads;  // 16B chunks of K per thread
@@ -94,13 +95,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs p) {
   const bool q_ok = qi < n;
   const int qpos = MASK == 0 ? n_p + qi : n_p;
   const int32_t qts = use_time ? p.ts[s0 + (q_ok ? qi : n - 1)] : 0;
-  bf16x8 qf[KS];
+  f16x8 qf[KS];
   {
     const uint16_t *qrow = p.q + (int64_t)(s0 + qi) * p.stride + h * DH + half * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 v = q_ok ? *reinterpret_cast<const u32x4 *>(qrow + ks * 16) : u32x4{0, 0, 0, 0};
-      qf[ks] = as_bf16x8(v);
+      qf[ks] = as_f16x8(v);
     }
   }
 
@@ -229,9 +230,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs p) {
       f32x16 s = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4 *>(
+        const f16x8 kf = as_f16x8(*reinterpret_cast<const u32x4 *>(
             &ks_lds[buf][(kb * 32 + lrow) * KPITCH + ks * 16 + half * 8]));
-        s = mfma32(kf, qf[ks], s);
+        s = mfma32_f16(kf, qf[ks], s);
       }
       float a[16];
 #pragma unroll
@@ -265,21 +266,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs p) {
         }
       }
       // P^T operand: k-step s2 takes values 8*s2 .. 8*s2+7
-      bf16x8 pf[2];
+      f16x8 pf[2];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        u32x4 pk = {pack_bf16(a[8 * s2 + 0], a[8 * s2 + 1]), pack_bf16(a[8 * s2 + 2], a[8 * s2 + 3]),
-                    pack_bf16(a[8 * s2 + 4], a[8 * s2 + 5]), pack_bf16(a[8 * s2 + 6], a[8 * s2 + 7])};
-        pf[s2] = as_bf16x8(pk);
+        u32x4 pk = {pack_f16(a[8 * s2 + 0], a[8 * s2 + 1]), pack_f16(a[8 * s2 + 2], a[8 * s2 + 3]),
+                    pack_f16(a[8 * s2 + 4], a[8 * s2 + 5]), pack_f16(a[8 * s2 + 6], a[8 * s2 + 7])};
+        pf[s2] = as_f16x8(pk);
       }
       // O^T += V^T P^T
 #pragma unroll
       for (int f = 0; f < FT; ++f) {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          const bf16x8 vf = as_bf16x8(*reinterpret_cast<const u32x4 *>(
+          const f16x8 vf = as_f16x8(*reinterpret_cast<const u32x4 *>(
               &vt_lds[buf][(f * 32 + lrow) * kVtPitch + kb * 32 + s2 * 16 + half * 8]));
-          acc_o[f] = mfma32(vf, pf[s2], acc_o[f]);
+          acc_o[f] = mfma32_f16(vf, pf[s2], acc_o[f]);
         }
       }
     }

@@ -7,6 +7,8 @@
 namespace hstu {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -22,14 +24,42 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8 &a, const bf16x8 &b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Same operand layout with fp16 inputs (v_mfma_f32_32x32x16_f16, same rate as bf16).
+__device__ __forceinline__ f32x16 mfma32_f16(const f16x8 &a, const f16x8 &b, const f32x16 &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &v) {
   return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ f16x8 as_f16x8(const u32x4 &v) {
+  return __builtin_bit_cast(f16x8, v);
 }
 
 // Two fp32 -> packed bf16 (round to nearest even; v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   bf16x2 p = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, p);
+}
+
+// Two fp32 -> packed fp16 (round to nearest even; v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  f16x2 p = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, p);
+}
+
+// As pack_f16, saturating to the finite fp16 range first (no infinities).
+__device__ __forceinline__ uint32_t pack_f16_sat(float lo, float hi) {
+  return pack_f16(__builtin_amdgcn_fmed3f(lo, -65504.0f, 65504.0f),
+                  __builtin_amdgcn_fmed3f(hi, -65504.0f, 65504.0f));
+}
+
+__device__ __forceinline__ float f16_lo(uint32_t v) {
+  return (float)__builtin_bit_cast(f16x2, v)[0];
+}
+__device__ __forceinline__ float f16_hi(uint32_t v) {
+  return (float)__builtin_bit_cast(f16x2, v)[1];
 }
 
 // SiLU(x) = x / (1 + 2^(-x log2 e)).  For x << 0 the power overflows to +inf and the

@@ -1,6 +1,6 @@
 // bf16 GEMM with fused epilogue for the two projections of the HSTU layer:
-//   f1: UVQK = SiLU(X W1^T + b1)   (equation 1 of the layer)
-//   f2: Y    = G W2^T + b2         (equation 3)
+//   f1: UVQK = SiLU(X W1^T + b1)   (equation 1 of the layer), written as fp16
+//   f2: Y    = G W2^T + b2         (equation 3), written as bf16
 // Both are dense contractions, so they run on MFMA: v_mfma_f32_32x32x16_bf16 with fp32
 // accumulation.  Operands are "K-contiguous" (X rows and W rows), staged through LDS
 // with a register prefetch of the next K tile (double buffer).  The MFMA takes W as its
@@ -17,7 +17,7 @@ constexpr int kBK = 64;          // K per stage
 constexpr int kPitch = kBK + 8;  // LDS row pitch in bf16 (144 bytes: conflict-free 16B reads)
 constexpr int kThreads = 256;
 
-template <int BM, int BN, int ACT>
+template <int BM, int BN, int ACT, int OUT>
 __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const uint16_t *__restrict__ A,
                                                            const uint16_t *__restrict__ W,
                                                            const float *__restrict__ bias,
@@ -129,19 +129,20 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const uint16_t *__res
         if (ACT == ACT_SILU) {
           v0 = silu_f32(v0); v1 = silu_f32(v1); v2 = silu_f32(v2); v3 = silu_f32(v3);
         }
-        u32x2 pk = {pack_bf16(v0, v1), pack_bf16(v2, v3)};
+        u32x2 pk = OUT == OUT_F16 ? u32x2{pack_f16_sat(v0, v1), pack_f16_sat(v2, v3)}
+                                  : u32x2{pack_bf16(v0, v1), pack_bf16(v2, v3)};
         *reinterpret_cast<u32x2 *>(out + (int64_t)m * N + n) = pk;
       }
     }
   }
 }
 
-template <int BM, int BN, int ACT>
+template <int BM, int BN, int ACT, int OUT>
 hipError_t launch_tile(const uint16_t *A, const uint16_t *W, const float *bias, uint16_t *out,
                        int M, int N, int K, hipStream_t stream) {
   const int tn = N / BN;
   const int tm = (M + BM - 1) / BM;
-  gemm_kernel<BM, BN, ACT><<<dim3(tm * tn), dim3(kThreads), 0, stream>>>(A, W, bias, out, M, N,
+  gemm_kernel<BM, BN, ACT, OUT><<<dim3(tm * tn), dim3(kThreads), 0, stream>>>(A, W, bias, out, M, N,
                                                                          K, tn);
   return hipGetLastError();
 }
@@ -149,15 +150,16 @@ hipError_t launch_tile(const uint16_t *A, const uint16_t *W, const float *bias, 
 }  // namespace
 
 hipError_t launch_gemm(const uint16_t *A, const uint16_t *W, const float *bias, uint16_t *out,
-                       int M, int N, int K, Act act, hipStream_t stream) {
+                       int M, int N, int K, Act act, OutType out_type, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   const bool wide = (N % 128) == 0;
-  if (act == ACT_SILU) {
-    return wide ? launch_tile<128, 128, ACT_SILU>(A, W, bias, out, M, N, K, stream)
-                : launch_tile<128, 64, ACT_SILU>(A, W, bias, out, M, N, K, stream);
-  }
-  return wide ? launch_tile<128, 128, ACT_NONE>(A, W, bias, out, M, N, K, stream)
-              : launch_tile<128, 64, ACT_NONE>(A, W, bias, out, M, N, K, stream);
+  if (act == ACT_SILU && out_type == OUT_F16)
+    return wide ? launch_tile<128, 128, ACT_SILU, OUT_F16>(A, W, bias, out, M, N, K, stream)
+                : launch_tile<128, 64, ACT_SILU, OUT_F16>(A, W, bias, out, M, N, K, stream);
+  if (act == ACT_NONE && out_type == OUT_BF16)
+    return wide ? launch_tile<128, 128, ACT_NONE, OUT_BF16>(A, W, bias, out, M, N, K, stream)
+                : launch_tile<128, 64, ACT_NONE, OUT_BF16>(A, W, bias, out, M, N, K, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace hstu

@@ -8,20 +8,22 @@ namespace hstu {
 
 enum Act { ACT_NONE = 0, ACT_SILU = 1 };
 
-// out[M][N] = act(A[M][K] . W[N][K]^T + bias[N]) in bf16 with fp32 accumulation.
-// Requires K % 64 == 0 and N % 64 == 0; any M >= 0.
+enum OutType { OUT_BF16 = 0, OUT_F16 = 1 };
+
+// out[M][N] = act(A[M][K] . W[N][K]^T + bias[N]): bf16 inputs, fp32 accumulation, output
+// bf16 or fp16 (saturated to the finite range).  Requires K % 64 == 0, N % 64 == 0.
 hipError_t launch_gemm(const uint16_t *A, const uint16_t *W, const float *bias, uint16_t *out,
-                       int M, int N, int K, Act act, hipStream_t stream);
+                       int M, int N, int K, Act act, OutType out_type, hipStream_t stream);
 
 // Attention parameters (device pointers unless noted).
 struct AttnArgs {
   const int32_t *offsets;   // [B+1]
   const int32_t *ts;        // [T] or nullptr
-  const uint16_t *q, *k, *v;
+  const uint16_t *q, *k, *v;  // fp16
   int64_t stride;           // elements between rows of q/k/v
   const int32_t *p_offsets; // prefix [B+1] or nullptr
   const int32_t *p_ts;      // prefix timestamps or nullptr
-  const uint16_t *pk, *pv;
+  const uint16_t *pk, *pv;  // fp16
   int64_t p_stride;
   const float *rab_pos;     // [rab_heads][pos_buckets] or nullptr
   const float *rab_time;    // [rab_heads][time_buckets] or nullptr
@@ -49,7 +51,7 @@ hipError_t launch_schedule(const int32_t *offsets, const int32_t *p_offsets, int
 
 hipError_t launch_attention(const AttnArgs &a, int dh, int64_t cap, hipStream_t stream);
 
-// G[T][HDV] = LayerNorm(O) * gamma + beta, times U (bf16 row of uvqk), as bf16.
+// G[T][HDV] = LayerNorm(O) * gamma + beta, times U (fp16 row of uvqk), as bf16.
 hipError_t launch_norm_gate(const float *O, const uint16_t *U, int64_t u_stride,
                             const float *gamma, const float *beta, float eps, uint16_t *G,
                             int T, int HDV, hipStream_t stream);

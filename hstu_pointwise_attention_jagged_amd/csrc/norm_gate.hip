@@ -6,8 +6,8 @@
 // One wave per token row: the fp32 attention output row (H*dv values) is held in
 // registers, mean and biased variance come from two wave reductions (two-pass, so the
 // large row mean of an unnormalised aggregation does not cancel digits), then the
-// normalised value times gamma plus beta is multiplied by the bf16 gate U and written
-// as bf16.  HBM-bound: 4 B read + 2 B read + 2 B written per element.
+// normalised value times gamma plus beta is multiplied by the fp16 gate U and written
+// as bf16 (the f2 operand).  HBM-bound: 4 B + 2 B read, 2 B written per element.
 #include "common.h"
 #include "kernels.h"
 
@@ -63,8 +63,7 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void norm_gate_kernel(
     const int e = (lane + 64 * c) * 4;
     if (e >= HDV) continue;
     const u32x2 uu = *reinterpret_cast<const u32x2 *>(urow + e);
-    float u[4] = {__builtin_bit_cast(float, uu[0] << 16), __builtin_bit_cast(float, uu[0] & 0xffff0000u),
-                  __builtin_bit_cast(float, uu[1] << 16), __builtin_bit_cast(float, uu[1] & 0xffff0000u)};
+    float u[4] = {f16_lo(uu[0]), f16_hi(uu[0]), f16_lo(uu[1]), f16_hi(uu[1])};
     float g[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {

@@ -20,6 +20,11 @@ def bf16_tensor(x_f32: np.ndarray, device="cuda") -> torch.Tensor:
     return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(device)
 
 
+def f16_tensor(x: np.ndarray, device="cuda") -> torch.Tensor:
+    """fp16 device tensor of the fp16-exact array ``x``."""
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float16)).to(device)
+
+
 def f32_tensor(a: Optional[np.ndarray], device="cuda") -> Optional[torch.Tensor]:
     if a is None:
         return None

@@ -142,16 +142,16 @@ def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
 def hstu_layer_fwd(dims: LayerDims, w: DeviceWeights, seq: DeviceJagged, x: torch.Tensor, *,
                    y: Optional[torch.Tensor] = None, uvqk: Optional[torch.Tensor] = None,
                    workspace: Optional[torch.Tensor] = None, stream=None):
-    """One HSTU layer (causal).  Returns (y bf16 [T][d], uvqk bf16 [T][2H(dv+dqk)])."""
+    """One HSTU layer (causal).  Returns (y bf16 [T][d], uvqk fp16 [T][2H(dv+dqk)])."""
     lib = _lib.load()
     _check(x, torch.bfloat16, "x")
     T = seq.total_tokens
     if y is None:
         y = torch.empty((T, dims.d_model), dtype=torch.bfloat16, device=x.device)
     if uvqk is None:
-        uvqk = torch.empty((T, dims.uvqk_width), dtype=torch.bfloat16, device=x.device)
+        uvqk = torch.empty((T, dims.uvqk_width), dtype=torch.float16, device=x.device)
     _check(y, torch.bfloat16, "y")
-    _check(uvqk, torch.bfloat16, "uvqk")
+    _check(uvqk, torch.float16, "uvqk")
     d, wc, s = dims.c(), w.c(), seq.c()
     need = int(lib.hstu_layer_workspace_bytes(ctypes.byref(d), ctypes.byref(s)))
     ws = _workspace(need, x.device, workspace)
@@ -169,12 +169,14 @@ def hstu_layer_fwd_mfalcon(dims: LayerDims, w: DeviceWeights, hist: DeviceJagged
     """M-FALCON candidate micro-batch against a cached history.  Returns (y_cand, uvqk_cand)."""
     lib = _lib.load()
     _check(x_cand, torch.bfloat16, "x_cand")
-    _check(hist_uvqk, torch.bfloat16, "hist_uvqk")
+    _check(hist_uvqk, torch.float16, "hist_uvqk")
     T = cand.total_tokens
     if y_cand is None:
         y_cand = torch.empty((T, dims.d_model), dtype=torch.bfloat16, device=x_cand.device)
     if uvqk_cand is None:
-        uvqk_cand = torch.empty((T, dims.uvqk_width), dtype=torch.bfloat16, device=x_cand.device)
+        uvqk_cand = torch.empty((T, dims.uvqk_width), dtype=torch.float16, device=x_cand.device)
+    _check(y_cand, torch.bfloat16, "y_cand")
+    _check(uvqk_cand, torch.float16, "uvqk_cand")
     d, wc, hs, cs = dims.c(), w.c(), hist.c(), cand.c()
     need = int(lib.hstu_layer_workspace_bytes(ctypes.byref(d), ctypes.byref(cs)))
     ws = _workspace(need, x_cand.device, workspace)
@@ -194,13 +196,14 @@ def hstu_attn_fwd(dims: LayerDims, seq: DeviceJagged, q: torch.Tensor, k: torch.
                   stream=None) -> torch.Tensor:
     """Equation 2 alone, fp32 output [T][H*dv].
 
-    q, k, v: bf16 views whose rows are ``row_stride`` elements apart (they may be column
-    slices of one buffer).  prefix: (DeviceJagged, k_p, v_p, p_row_stride) or None.
+    q, k, v: fp16 views whose rows are ``row_stride`` elements apart (they may be column
+    slices of one buffer).  prefix: (DeviceJagged, k_p, v_p, p_row_stride) or None, k_p
+    and v_p fp16 as well.
     """
     lib = _lib.load()
     for n, t in (("q", q), ("k", k), ("v", v)):
-        if t.dtype != torch.bfloat16 or not t.is_cuda:
-            raise TypeError(f"{n}: expected a bf16 device tensor")
+        if t.dtype != torch.float16 or not t.is_cuda:
+            raise TypeError(f"{n}: expected an fp16 device tensor")
     if row_stride is None:
         row_stride = q.stride(0)
     T = seq.total_tokens
@@ -212,6 +215,9 @@ def hstu_attn_fwd(dims: LayerDims, seq: DeviceJagged, q: torch.Tensor, k: torch.
     keep = []
     if prefix is not None:
         pseq, kp, vp, pstride = prefix
+        for n, t in (("k_p", kp), ("v_p", vp)):
+            if t.dtype != torch.float16 or not t.is_cuda:
+                raise TypeError(f"{n}: expected an fp16 device tensor")
         ps = pseq.c()
         keep.append(ps)
         pref = _lib.Prefix(ctypes.pointer(ps), _ptr(kp), _ptr(vp), int(pstride))

@@ -55,6 +55,11 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     return bf16_to_f32(bf16_bits(x))
 
 
+def round_f16(x: np.ndarray) -> np.ndarray:
+    """fp32 array holding the fp16-rounded (nearest even) values of ``x``."""
+    return np.asarray(x, dtype=np.float32).astype(np.float16).astype(np.float32)
+
+
 # ----------------------------------------------------------------------------------
 # Data classes
 # ----------------------------------------------------------------------------------

@@ -15,7 +15,13 @@
  *
  * Conventions for every entry point
  *  - Pointers marked (device) are HIP device pointers; everything else is host memory
- *    read during the call only.  bf16 tensors are passed as uint16_t bit patterns.
+ *    read during the call only.  bf16 and fp16 tensors are passed as uint16_t bit
+ *    patterns.
+ *  - Precision: X, Y, w1, w2 and the f2 operand are bf16; the f1 output U|V|Q|K and the
+ *    attention weights A are fp16 (same MFMA rate on gfx950, 3 more mantissa bits, which
+ *    the layer needs to stay within 2e-2 / 2e-3 of an fp64 reference); every product
+ *    accumulates in fp32.  f1 outputs saturate at +-65504; A = SiLU(score) must stay
+ *    below 65504 in magnitude.
  *  - Row-major layouts.  Weights are "out x in": f1(X) = X w1^T + b1, f2(G) = G w2^T + b2.
  *  - U|V|Q|K layout of the f1 output: columns [0,H*dv) = U, [H*dv,2H*dv) = V,
  *    then H*dqk columns of Q and H*dqk of K; head h owns columns [h*dh,(h+1)*dh) of
@@ -100,8 +106,8 @@ typedef struct {
  * b of the query batch sees rows [seq->seq_offsets[b], seq->seq_offsets[b+1]) of k/v. */
 typedef struct {
   const hstu_jagged_t *seq;   /* same batch size as the query batch                   */
-  const uint16_t *k;          /* (device) bf16, row r at k + r*row_stride               */
-  const uint16_t *v;          /* (device) bf16, row r at v + r*row_stride               */
+  const uint16_t *k;          /* (device) fp16, row r at k + r*row_stride               */
+  const uint16_t *v;          /* (device) fp16, row r at v + r*row_stride               */
   int64_t row_stride;         /* elements between consecutive rows                     */
 } hstu_prefix_t;
 
@@ -115,7 +121,7 @@ size_t hstu_attn_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_t *s
 /* One HSTU layer, equations (1)-(3), causal mask.
  *   x    (device) bf16 [T][d]                       input rows
  *   y    (device) bf16 [T][d]                       output rows (may not alias x)
- *   uvqk (device) bf16 [T][2H(dv+dqk)]              f1 output, written; the caller may
+ *   uvqk (device) fp16 [T][2H(dv+dqk)]              f1 output, written; the caller may
  *                                                   keep it as the K/V cache of an
  *                                                   M-FALCON history
  *   ws   (device) workspace of ws_bytes >= hstu_layer_workspace_bytes(dims, seq)    */
@@ -129,9 +135,9 @@ hstu_status_t hstu_layer_fwd(const hstu_dims_t *dims, const hstu_weights_t *w,
  * and to itself only, then LayerNorm, gate and f2.  cand->timestamps are the
  * candidates' request times.  The results of one candidate do not depend on which
  * other candidates share its micro-batch.
- *   hist_uvqk (device) bf16 [T_hist][2H(dv+dqk)]
+ *   hist_uvqk (device) fp16 [T_hist][2H(dv+dqk)]
  *   x_cand    (device) bf16 [T_cand][d];   y_cand (device) bf16 [T_cand][d]
- *   uvqk_cand (device) bf16 [T_cand][2H(dv+dqk)]
+ *   uvqk_cand (device) fp16 [T_cand][2H(dv+dqk)]
  *   ws        >= hstu_layer_workspace_bytes(dims, cand)                              */
 hstu_status_t hstu_layer_fwd_mfalcon(const hstu_dims_t *dims, const hstu_weights_t *w,
                                      const hstu_jagged_t *hist, const uint16_t *hist_uvqk,
@@ -141,7 +147,7 @@ hstu_status_t hstu_layer_fwd_mfalcon(const hstu_dims_t *dims, const hstu_weights
 
 /* Equation (2) alone: out[t][h*dv + f] = sum_j SiLU(q_t.k_j + rab(t,j)) v_j[f] over the
  * keys allowed by `mask` (see hstu_mask_t), fp32, no normalisation.
- *   q, k, v (device) bf16; row t of head h at q + t*row_stride + h*dqk (same for k,v
+ *   q, k, v (device) fp16; row t of head h at q + t*row_stride + h*dqk (same for k,v
  *           with dqk / dv)
  *   prefix  NULL or the keys preceding each sequence (required for SELF_ONLY)
  *   out     (device) fp32 [T][H*dv], every row written
