@@ -111,6 +111,12 @@ hstu_status_t check_seq(const hstu_jagged_t *s) {
   return HSTU_OK;
 }
 
+// The attention kernel addresses one sequence's key rows through 32-bit buffer offsets:
+// (longest sequence + one stage) rows of `row_elems` fp16 values must stay below 2^31 bytes.
+bool rows_addressable(int max_seq_len, int64_t row_elems) {
+  return ((int64_t)max_seq_len + 64) * row_elems * 2 < ((int64_t)1 << 31);
+}
+
 size_t sched_bytes(const hstu_jagged_t *s) {
   const int64_t cap = attn_work_capacity(s->batch, s->total_tokens);
   return align_up((size_t)cap * 2 * sizeof(int32_t)) + kAlign;
@@ -187,7 +193,7 @@ hstu_status_t run_layer(const hstu_dims_t *d, const hstu_weights_t *w, const hst
   e = timed(1, st, [&] { return launch_gemm(x, w->w1, w->b1, uvqk, T, n1, d->d_model, ACT_SILU, OUT_F16, st); });
   if (e != hipSuccess) return hip_fail(e);
   const int64_t cap = attn_work_capacity(s->batch, T);
-  e = timed(2, st, [&] { return launch_attention(aa, d->dqk, cap, st); });
+  e = timed(2, st, [&] { return launch_attention(aa, d->dqk, s->max_seq_len, cap, st); });
   if (e != hipSuccess) return hip_fail(e);
   e = timed(3, st, [&] {
     return launch_norm_gate(lw.o, uvqk, n1, w->ln_gamma, w->ln_beta, d->ln_eps, lw.g, T, hdv, st);
@@ -232,6 +238,8 @@ hstu_status_t hstu_layer_fwd(const hstu_dims_t *dims, const hstu_weights_t *w,
   if ((void *)x == (void *)y) return HSTU_ERR_INVALID_ARG;
   if (seq->batch == 0 || seq->total_tokens == 0) return HSTU_OK;
   if ((st = check_ws(ws, ws_bytes, layer_ws_bytes(dims, seq))) != HSTU_OK) return st;
+  if (!rows_addressable(seq->max_seq_len, 2 * (int64_t)dims->num_heads * (dims->dqk + dims->dv)))
+    return HSTU_ERR_UNSUPPORTED;
 
   const LayerWs lw = carve_layer(ws, dims, seq);
   const int hdv = dims->num_heads * dims->dv, hqk = dims->num_heads * dims->dqk;
@@ -261,6 +269,11 @@ hstu_status_t hstu_layer_fwd_mfalcon(const hstu_dims_t *dims, const hstu_weights
   if ((cand->timestamps == nullptr) != (hist->timestamps == nullptr)) return HSTU_ERR_INVALID_ARG;
   if (cand->batch == 0 || cand->total_tokens == 0) return HSTU_OK;
   if ((st = check_ws(ws, ws_bytes, layer_ws_bytes(dims, cand))) != HSTU_OK) return st;
+  {
+    const int64_t n1 = 2 * (int64_t)dims->num_heads * (dims->dqk + dims->dv);
+    if (!rows_addressable(cand->max_seq_len, n1) || !rows_addressable(hist->max_seq_len, n1))
+      return HSTU_ERR_UNSUPPORTED;
+  }
 
   const LayerWs lw = carve_layer(ws, dims, cand);
   const int hdv = dims->num_heads * dims->dv, hqk = dims->num_heads * dims->dqk;
@@ -305,6 +318,9 @@ hstu_status_t hstu_attn_fwd(const hstu_dims_t *dims, const float *rab_pos, const
   }
   if (seq->batch == 0 || seq->total_tokens == 0) return HSTU_OK;
   if ((st = check_ws(ws, ws_bytes, sched_bytes(seq))) != HSTU_OK) return st;
+  if (!rows_addressable(seq->max_seq_len, row_stride) ||
+      (prefix != nullptr && !rows_addressable(prefix->seq->max_seq_len, prefix->row_stride)))
+    return HSTU_ERR_UNSUPPORTED;
 
   LayerWs lw{};
   lw.n_work = (int32_t *)ws;
@@ -325,7 +341,7 @@ hstu_status_t hstu_attn_fwd(const hstu_dims_t *dims, const float *rab_pos, const
   });
   if (e != hipSuccess) return hip_fail(e);
   const int64_t cap = attn_work_capacity(seq->batch, seq->total_tokens);
-  e = timed(2, sst, [&] { return launch_attention(aa, dims->dqk, cap, sst); });
+  e = timed(2, sst, [&] { return launch_attention(aa, dims->dqk, seq->max_seq_len, cap, sst); });
   if (e != hipSuccess) return hip_fail(e);
   return HSTU_OK;
 }

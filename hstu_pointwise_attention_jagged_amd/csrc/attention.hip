@@ -18,11 +18,18 @@
 //    with no trip through LDS.  Q, K, V and A are fp16 operands (the same MFMA rate as
 //    bf16 on gfx950, 3 more mantissa bits); accumulation and O stay fp32.
 //  * The rab index math is integer only: relative position clamp, and the log2 time
-//    bucket from the bit length of (1 + gap); table values come from LDS.
+//    bucket from the bit length of (1 + gap); table values come from LDS.  Far from the
+//    diagonal a whole 32x32 block usually shares one bias value: every relative position
+//    is past the last position bucket and (bucket being monotone in the gap) the
+//    buckets of the smallest and largest possible gap -- from the min/max timestamps of
+//    the block's queries and keys -- coincide.  Such blocks start the score MFMA from
+//    that constant and skip all per-element bias work.
 //  * Tiles are skipped from the jagged offsets and the mask: a wave never multiplies a
 //    32-key block that lies wholly after its queries (causal) or away from them
 //    (candidate self term); only blocks that straddle the diagonal are masked per
 //    element.  Masked pairs contribute exactly 0.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -30,12 +37,11 @@ namespace hstu {
 
 namespace {
 
-constexpr int kBM = kAttnBlockM;  // 128 queries per workgroup
 constexpr int kBN = kAttnBlockN;  // 64 keys per stage
-constexpr int kThreads = 256;
 constexpr int kMaxPos = 1024;
 constexpr int kMaxTime = 64;
 constexpr int kVtPitch = kBN + 8;  // transposed V row pitch (fp16): 144 bytes
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
 
 // Physical slot of key kk (0..63) inside a transposed V stage: within each group of 16
 // keys the order is [0-3, 8-11, 4-7, 12-15], which puts the 8 keys a lane multiplies in
@@ -45,18 +51,30 @@ __device__ __forceinline__ int vt_slot(int kk) {
   return (kk & ~15) + ((k >> 2) & 1) * 8 + (k >> 3) * 4 + (k & 3);
 }
 
-template <int DH, int MASK>
-__global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs p) {
+// Buffer resource over `bytes` bytes at `base`: loads past the end return 0, so rows
+// beyond a sequence's last key are zero without any branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ int sgpr(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+template <int DH, int MASK, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
+  constexpr int NT = 64 * NW;           // threads per workgroup
+  constexpr int BM = 32 * NW;           // query rows per workgroup
   constexpr int KPITCH = DH + 8;        // K row pitch (fp16)
   constexpr int KS = DH / 16;           // k-steps of the score MFMA
   constexpr int FT = DH / 32;           // 32-wide feature tiles of the output
-  constexpr int K_CHUNKS = (kBN * DH / 8) / kThreads;  // 16B chunks of K per thread
-  constexpr int V_THREADS = 16 * (DH / 8);             // threads staging V (4 keys x 8 feat)
-  static_assert(K_CHUNKS >= 1, "DH too small");
+  constexpr int K_UNITS = kBN * DH / 8;  // 16-byte chunks of a K stage
+  constexpr int K_ITERS = (K_UNITS + NT - 1) / NT;
+  constexpr int V_UNITS = 16 * (DH / 8);  // (4 keys x 8 features) units of a V stage
+  static_assert(V_UNITS <= NT, "one V unit per thread");
 
   __shared__ __attribute__((aligned(16))) uint16_t ks_lds[2][kBN * KPITCH];
   __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][DH * kVtPitch];
   __shared__ __attribute__((aligned(16))) int32_t kts_lds[2][kBN];
+  __shared__ int32_t kstat[2][2][2];  // [buf][32-key block][min, max] of valid key timestamps
   __shared__ float ptab[kMaxPos];
   __shared__ float ttab[kMaxTime];
 
@@ -64,12 +82,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs p) {
   if (item >= *p.n_work) return;
   const int h = blockIdx.y;
   const int b = p.work[2 * item], qt = p.work[2 * item + 1];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = sgpr(tid >> 6);
   const int lrow = lane & 31, half = lane >> 5;
 
   const int s0 = p.offsets[b];
   const int n = p.offsets[b + 1] - s0;
-  const int q0 = qt * kBM;
+  const int q0 = qt * BM;
   int p0 = 0, n_p = 0;
   if (p.p_offsets != nullptr) {
     p0 = p.p_offsets[b];
@@ -83,18 +102,29 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs p) {
   {
     const int r = p.rab_per_head ? h : 0;
     if (use_pos)
-      for (int i = tid; i < p.pos_buckets; i += kThreads) ptab[i] = p.rab_pos[r * p.pos_buckets + i];
+      for (int i = tid; i < p.pos_buckets; i += NT) ptab[i] = p.rab_pos[r * p.pos_buckets + i];
     if (use_time)
-      for (int i = tid; i < p.time_buckets; i += kThreads)
-        ttab[i] = p.rab_time[r * p.time_buckets + i];
+      for (int i = tid; i < p.time_buckets; i += NT) ttab[i] = p.rab_time[r * p.time_buckets + i];
   }
 
   // this wave's queries: local index qi, position, timestamp; Q fragments in registers
-  const int qbase = q0 + wave * 32;
+  const int qbase = q0 + wave * 32;  // wave-uniform
   const int qi = qbase + lrow;
   const bool q_ok = qi < n;
+  const bool wave_has_rows = qbase < n;
   const int qpos = MASK == 0 ? n_p + qi : n_p;
   const int32_t qts = use_time ? p.ts[s0 + (q_ok ? qi : n - 1)] : 0;
+  int32_t qts_min = q_ok ? qts : INT32_MAX, qts_max = q_ok ? qts : INT32_MIN;
+  if (use_time) {
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {
+      qts_min = min(qts_min, __shfl_xor(qts_min, o, 64));
+      qts_max = max(qts_max, __shfl_xor(qts_max, o, 64));
+    }
+    qts_min = sgpr(qts_min);
+    qts_max = sgpr(qts_max);
+  }
+  const int qpos_min = MASK == 0 ? n_p + qbase : n_p;
   f16x8 qf[KS];
   {
     const uint16_t *qrow = p.q + (int64_t)(s0 + qi) * p.stride + h * DH + half * 8;
@@ -107,76 +137,74 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs p) {
 
   // key tiles: prefix tiles first, then own tiles
   const int n_pt = (n_p + kBN - 1) / kBN;
-  const int q_end = min(n, q0 + kBM);
+  const int q_end = min(n, q0 + BM);
   const int own_start = MASK == 0 ? 0 : q0;
   const int n_ot = (q_end - own_start + kBN - 1) / kBN;
   const int n_tiles = n_pt + n_ot;
 
+  // buffer resources of the two key segments (prefix rows, own rows)
+  const int64_t own_bytes = (int64_t)n * p.stride * 2;
+  const int64_t pre_bytes = (int64_t)n_p * p.p_stride * 2;
+  const __amdgpu_buffer_rsrc_t k_own = make_rsrc(p.k + (int64_t)s0 * p.stride, (uint32_t)own_bytes);
+  const __amdgpu_buffer_rsrc_t v_own = make_rsrc(p.v + (int64_t)s0 * p.stride, (uint32_t)own_bytes);
+  const __amdgpu_buffer_rsrc_t t_own = make_rsrc(use_time ? p.ts + s0 : p.offsets, use_time ? 4u * n : 0u);
+  __amdgpu_buffer_rsrc_t k_pre = k_own, v_pre = v_own, t_pre = t_own;
+  if (n_p > 0) {
+    k_pre = make_rsrc(p.pk + (int64_t)p0 * p.p_stride, (uint32_t)pre_bytes);
+    v_pre = make_rsrc(p.pv + (int64_t)p0 * p.p_stride, (uint32_t)pre_bytes);
+    t_pre = make_rsrc(use_time ? p.p_ts + p0 : p.offsets, use_time ? 4u * n_p : 0u);
+  }
+
   // staging registers
-  u32x4 rk[K_CHUNKS];
+  u32x4 rk[K_ITERS];
   u32x4 rv[4];
   int32_t rts = 0;
+  bool rts_ok = false;
 
-  auto tile_src = [&](int t, int &kbase, int &limit, const uint16_t *&kb, const uint16_t *&vb,
-                      const int32_t *&tsb, int64_t &stride) {
-    if (t < n_pt) {
-      kbase = t * kBN;
-      limit = n_p;
-      kb = p.pk + (int64_t)p0 * p.p_stride;
-      vb = p.pv + (int64_t)p0 * p.p_stride;
-      tsb = use_time ? p.p_ts + p0 : nullptr;
-      stride = p.p_stride;
-    } else {
-      kbase = own_start + (t - n_pt) * kBN;
-      limit = n;
-      kb = p.k + (int64_t)s0 * p.stride;
-      vb = p.v + (int64_t)s0 * p.stride;
-      tsb = use_time ? p.ts + s0 : nullptr;
-      stride = p.stride;
-    }
-  };
+  // V unit of this thread: key group kg (fastest, so a transposed LDS write of 16 lanes
+  // covers one 128-byte row) and feature chunk fc
+  const int v_kg = tid % 16, v_fc = (tid / 16) * 8;
 
   auto load_tile = [&](int t) {
-    int kbase, limit;
-    const uint16_t *kb, *vb;
-    const int32_t *tsb;
-    int64_t stride;
-    tile_src(t, kbase, limit, kb, vb, tsb, stride);
+    const bool pre = t < n_pt;
+    const int kbase = pre ? t * kBN : own_start + (t - n_pt) * kBN;
+    const int limit = pre ? n_p : n;
+    const int64_t stride = pre ? p.p_stride : p.stride;
+    const __amdgpu_buffer_rsrc_t kr = pre ? k_pre : k_own;
+    const __amdgpu_buffer_rsrc_t vr = pre ? v_pre : v_own;
 #pragma unroll
-    for (int j = 0; j < K_CHUNKS; ++j) {
-      const int c = tid + j * kThreads;
-      const int row = c / (DH / 8), col = (c % (DH / 8)) * 8;
-      const int key = kbase + row;
-      rk[j] = key < limit
-                  ? *reinterpret_cast<const u32x4 *>(kb + (int64_t)key * stride + h * DH + col)
-                  : u32x4{0, 0, 0, 0};
+    for (int j = 0; j < K_ITERS; ++j) {
+      const int c = tid + j * NT;
+      if (K_UNITS % NT == 0 || c < K_UNITS) {
+        const int row = c / (DH / 8), col = (c % (DH / 8)) * 8;
+        const int off = (int)(((int64_t)(kbase + row) * stride + h * DH + col) * 2);
+        rk[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0));
+      }
     }
-    if (tid < V_THREADS) {
-      const int kg = tid / (DH / 8), fc = (tid % (DH / 8)) * 8;
+    if (tid < V_UNITS) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int key = kbase + kg * 4 + r;
-        rv[r] = key < limit
-                    ? *reinterpret_cast<const u32x4 *>(vb + (int64_t)key * stride + h * DH + fc)
-                    : u32x4{0, 0, 0, 0};
+        const int off = (int)(((int64_t)(kbase + v_kg * 4 + r) * stride + h * DH + v_fc) * 2);
+        rv[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0));
       }
     }
     if (use_time && tid < kBN) {
-      const int key = kbase + tid;
-      rts = key < limit ? tsb[key] : 0;
+      rts_ok = kbase + tid < limit;
+      rts = __builtin_amdgcn_raw_buffer_load_b32(pre ? t_pre : t_own, (kbase + tid) * 4, 0, 0);
     }
   };
 
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < K_CHUNKS; ++j) {
-      const int c = tid + j * kThreads;
-      const int row = c / (DH / 8), col = (c % (DH / 8)) * 8;
-      *reinterpret_cast<u32x4 *>(&ks_lds[buf][row * KPITCH + col]) = rk[j];
+    for (int j = 0; j < K_ITERS; ++j) {
+      const int c = tid + j * NT;
+      if (K_UNITS % NT == 0 || c < K_UNITS) {
+        const int row = c / (DH / 8), col = (c % (DH / 8)) * 8;
+        *reinterpret_cast<u32x4 *>(&ks_lds[buf][row * KPITCH + col]) = rk[j];
+      }
     }
-    if (tid < V_THREADS) {
-      const int kg = tid / (DH / 8), fc = (tid % (DH / 8)) * 8;
-      const int slot = vt_slot(kg * 4);
+    if (tid < V_UNITS) {
+      const int slot = vt_slot(v_kg * 4);
       // transpose 4 keys x 8 features into 8 rows of 4 keys
 #pragma unroll
       for (int f = 0; f < 8; ++f) {
@@ -187,10 +215,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs p) {
         uint32_t e2 = hi ? (rv[2][w] >> 16) : (rv[2][w] & 0xffffu);
         uint32_t e3 = hi ? (rv[3][w] >> 16) : (rv[3][w] & 0xffffu);
         u32x2 pk = {e0 | (e1 << 16), e2 | (e3 << 16)};
-        *reinterpret_cast<u32x2 *>(&vt_lds[buf][(fc + f) * kVtPitch + slot]) = pk;
+        *reinterpret_cast<u32x2 *>(&vt_lds[buf][(v_fc + f) * kVtPitch + slot]) = pk;
       }
     }
-    if (use_time && tid < kBN) kts_lds[buf][tid] = rts;
+    if (use_time && tid < kBN) {  // wave 0: timestamps and per-block min / max
+      kts_lds[buf][tid] = rts;
+      int32_t mn = rts_ok ? rts : INT32_MAX, mx = rts_ok ? rts : INT32_MIN;
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) {
+        mn = min(mn, __shfl_xor(mn, o, 64));
+        mx = max(mx, __shfl_xor(mx, o, 64));
+      }
+      if ((tid & 31) == 0) {
+        kstat[buf][tid >> 5][0] = mn;
+        kstat[buf][tid >> 5][1] = mx;
+      }
+    }
   };
 
   f32x16 acc_o[FT];
@@ -203,9 +243,81 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs p) {
   }
   __syncthreads();
 
-  const int qmin = qbase, qmax = qbase + 31;
+  // One 32-key block of this wave: scores, bias, SiLU, mask, aggregation.  The
+  // compile-time flags pick the variant so the common case (constant bias, no mask)
+  // carries no per-element index or mask code.
+  int cur_buf = 0;
+  auto block = [&](int kb, int kbase, bool is_prefix, float bias0, auto uniform_c, auto masked_c) {
+    constexpr bool UNIFORM = decltype(uniform_c)::value;
+    constexpr bool MASKED = decltype(masked_c)::value;
+    const int buf_ = cur_buf;
+    // S^T = K Q^T : lane holds query lrow, keys 8*(i/4) + 4*half + (i%4)
+    f32x16 s;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = UNIFORM ? bias0 : 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const f16x8 kf = as_f16x8(*reinterpret_cast<const u32x4 *>(
+          &ks_lds[buf_][(kb * 32 + lrow) * KPITCH + ks * 16 + half * 8]));
+      s = mfma32_f16(kf, qf[ks], s);
+    }
+    if (!UNIFORM) {
+      // per-element bias: integer indices, table values from LDS
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int kl = kb * 32 + 8 * g + 4 * half;  // first of 4 consecutive keys
+        int4 t4 = {0, 0, 0, 0};
+        if (use_time) t4 = *reinterpret_cast<const int4 *>(&kts_lds[buf_][kl]);
+        const int32_t kt4[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 4 * g + r;
+          float x = s[i];
+          if (use_pos) {
+            const int kidx = kbase + kl + r;
+            const int kpos = is_prefix ? kidx : (MASK == 0 ? n_p + kidx : n_p);
+            x += ptab[min(max(qpos - kpos, 0), p.pos_buckets - 1)];
+          }
+          if (use_time) x += ttab[min(time_log2_bucket(qts, kt4[r]), p.time_buckets - 1)];
+          s[i] = x;
+        }
+      }
+    }
+    float a[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a[i] = silu_f32(s[i]);
+    if (MASKED) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kidx = kbase + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+        const bool allowed = MASK == 0 ? (kidx <= qi) : (kidx == qi);
+        a[i] = allowed ? a[i] : 0.0f;
+      }
+    }
+    // P^T operand: k-step s2 takes values 8*s2 .. 8*s2+7
+    f16x8 pf[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      u32x4 pk = {pack_f16(a[8 * s2 + 0], a[8 * s2 + 1]), pack_f16(a[8 * s2 + 2], a[8 * s2 + 3]),
+                  pack_f16(a[8 * s2 + 4], a[8 * s2 + 5]), pack_f16(a[8 * s2 + 6], a[8 * s2 + 7])};
+      pf[s2] = as_f16x8(pk);
+    }
+    // O^T += V^T P^T
+#pragma unroll
+    for (int f = 0; f < FT; ++f) {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const f16x8 vf = as_f16x8(*reinterpret_cast<const u32x4 *>(
+            &vt_lds[buf_][(f * 32 + lrow) * kVtPitch + kb * 32 + s2 * 16 + half * 8]));
+        acc_o[f] = mfma32_f16(vf, pf[s2], acc_o[f]);
+      }
+    }
+  };
+
+  const int qmax = qbase + 31;
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
+    cur_buf = buf;
     if (t + 1 < n_tiles) load_tile(t + 1);
 
     const bool is_prefix = t < n_pt;
@@ -215,74 +327,45 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs p) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int k0 = kbase + kb * 32;
-      if (k0 >= limit) continue;  // wave-uniform: no valid key in this block
+      // wave-uniform skips: no valid key, no valid query, or a block wholly masked
+      if (k0 >= limit || !wave_has_rows) continue;
       bool need_mask = false;
       if (!is_prefix) {
         if (MASK == 0) {
           if (k0 > qmax) continue;
-          need_mask = k0 + 31 > qmin;
+          need_mask = k0 + 31 > qbase;
         } else {
-          if (k0 > qmax || k0 + 31 < qmin) continue;
+          if (k0 > qmax || k0 + 31 < qbase) continue;
           need_mask = true;
         }
       }
-      // S^T = K Q^T : lane holds query lrow, keys 8*(i/4) + 4*half + (i%4)
-      f32x16 s = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const f16x8 kf = as_f16x8(*reinterpret_cast<const u32x4 *>(
-            &ks_lds[buf][(kb * 32 + lrow) * KPITCH + ks * 16 + half * 8]));
-        s = mfma32_f16(kf, qf[ks], s);
+      // Is the bias one constant over this block?  Positions: every relative position
+      // reaches the last bucket.  Time: the buckets of the extreme gaps coincide.
+      bool uniform = true;
+      float bias0 = 0.0f;
+      if (use_pos) {
+        const int kpos_max = is_prefix ? k0 + 31 : (MASK == 0 ? n_p + k0 + 31 : n_p);
+        uniform = qpos_min - kpos_max >= p.pos_buckets - 1;
+        bias0 = ptab[p.pos_buckets - 1];
       }
-      float a[16];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int kl = kb * 32 + 8 * g + 4 * half;  // first of 4 consecutive keys
-        int32_t kt4[4] = {0, 0, 0, 0};
-        if (use_time) {
-          const int4 t4 = *reinterpret_cast<const int4 *>(&kts_lds[buf][kl]);
-          kt4[0] = t4.x; kt4[1] = t4.y; kt4[2] = t4.z; kt4[3] = t4.w;
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 4 * g + r;
-          const int kidx = kbase + kl + r;
-          float x = s[i];
-          if (use_pos) {
-            const int kpos = is_prefix ? kidx : (MASK == 0 ? n_p + kidx : n_p);
-            const int rel = max(qpos - kpos, 0);
-            x += ptab[min(rel, p.pos_buckets - 1)];
-          }
-          if (use_time) {
-            const int tb = min(time_log2_bucket(qts, kt4[r]), p.time_buckets - 1);
-            x += ttab[tb];
-          }
-          float y = silu_f32(x);
-          if (need_mask) {
-            const bool allowed = MASK == 0 ? (kidx <= qi) : (kidx == qi);
-            y = allowed ? y : 0.0f;
-          }
-          a[i] = y;
-        }
+      if (use_time && uniform) {
+        const int32_t kmin = sgpr(kstat[buf][kb][0]), kmax = sgpr(kstat[buf][kb][1]);
+        const int tb_lo = min(time_log2_bucket(qts_min, kmax), p.time_buckets - 1);
+        const int tb_hi = min(time_log2_bucket(qts_max, kmin), p.time_buckets - 1);
+        uniform = tb_lo == tb_hi;
+        bias0 += ttab[tb_lo];
       }
-      // P^T operand: k-step s2 takes values 8*s2 .. 8*s2+7
-      f16x8 pf[2];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        u32x4 pk = {pack_f16(a[8 * s2 + 0], a[8 * s2 + 1]), pack_f16(a[8 * s2 + 2], a[8 * s2 + 3]),
-                    pack_f16(a[8 * s2 + 4], a[8 * s2 + 5]), pack_f16(a[8 * s2 + 6], a[8 * s2 + 7])};
-        pf[s2] = as_f16x8(pk);
-      }
-      // O^T += V^T P^T
-#pragma unroll
-      for (int f = 0; f < FT; ++f) {
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const f16x8 vf = as_f16x8(*reinterpret_cast<const u32x4 *>(
-              &vt_lds[buf][(f * 32 + lrow) * kVtPitch + kb * 32 + s2 * 16 + half * 8]));
-          acc_o[f] = mfma32_f16(vf, pf[s2], acc_o[f]);
-        }
-      }
+      uniform = sgpr(uniform);
+      bias0 = __builtin_bit_cast(float, sgpr(__builtin_bit_cast(int, bias0)));
+      need_mask = sgpr(need_mask);
+      if (uniform && !need_mask)
+        block(kb, kbase, is_prefix, bias0, std::true_type{}, std::false_type{});
+      else if (uniform)
+        block(kb, kbase, is_prefix, bias0, std::true_type{}, std::true_type{});
+      else if (!need_mask)
+        block(kb, kbase, is_prefix, bias0, std::false_type{}, std::false_type{});
+      else
+        block(kb, kbase, is_prefix, bias0, std::false_type{}, std::true_type{});
     }
 
     if (t + 1 < n_tiles) store_tile(buf ^ 1);
@@ -309,17 +392,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs p) {
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedBins = 4096;
 
-__device__ __forceinline__ int item_cost(int n, int n_p, int t, int mask) {
-  const int q0 = t * kBM;
-  const int q_end = min(n, q0 + kBM);
+__device__ __forceinline__ int item_cost(int n, int n_p, int t, int mask, int bm) {
+  const int q0 = t * bm;
+  const int q_end = min(n, q0 + bm);
   const int own = mask == 0 ? q_end : q_end - q0;
   return (n_p + kBN - 1) / kBN + (own + kBN - 1) / kBN;
 }
 
 __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t *offsets,
                                                                  const int32_t *p_offsets,
-                                                                 int B, int mask, int nbins,
-                                                                 int32_t *work, int32_t *n_work) {
+                                                                 int B, int mask, int bm,
+                                                                 int nbins, int32_t *work,
+                                                                 int32_t *n_work) {
   __shared__ int bins[kSchedBins];
   __shared__ int total;
   const int tid = threadIdx.x;
@@ -328,8 +412,8 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t *
   for (int b = tid; b < B; b += kSchedThreads) {
     const int n = offsets[b + 1] - offsets[b];
     const int n_p = p_offsets ? p_offsets[b + 1] - p_offsets[b] : 0;
-    const int nq = (n + kBM - 1) / kBM;
-    for (int t = 0; t < nq; ++t) atomicAdd(&bins[min(item_cost(n, n_p, t, mask), nbins - 1)], 1);
+    const int nq = (n + bm - 1) / bm;
+    for (int t = 0; t < nq; ++t) atomicAdd(&bins[min(item_cost(n, n_p, t, mask, bm), nbins - 1)], 1);
   }
   __syncthreads();
   if (tid == 0) {  // exclusive scan, most expensive bin first
@@ -345,9 +429,9 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t *
   for (int b = tid; b < B; b += kSchedThreads) {
     const int n = offsets[b + 1] - offsets[b];
     const int n_p = p_offsets ? p_offsets[b + 1] - p_offsets[b] : 0;
-    const int nq = (n + kBM - 1) / kBM;
+    const int nq = (n + bm - 1) / bm;
     for (int t = 0; t < nq; ++t) {
-      const int pos = atomicAdd(&bins[min(item_cost(n, n_p, t, mask), nbins - 1)], 1);
+      const int pos = atomicAdd(&bins[min(item_cost(n, n_p, t, mask, bm), nbins - 1)], 1);
       work[2 * pos] = b;
       work[2 * pos + 1] = t;
     }
@@ -355,33 +439,39 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t *
   if (tid == 0) *n_work = total;
 }
 
-template <int DH>
+template <int DH, int NW>
 hipError_t launch_dh(const AttnArgs &a, int64_t cap, hipStream_t stream) {
   const dim3 grid((unsigned)cap, (unsigned)a.num_heads);
   if (a.mask == 0)
-    attn_kernel<DH, 0><<<grid, dim3(kThreads), 0, stream>>>(a);
+    attn_kernel<DH, 0, NW><<<grid, dim3(64 * NW), 0, stream>>>(a);
   else
-    attn_kernel<DH, 1><<<grid, dim3(kThreads), 0, stream>>>(a);
+    attn_kernel<DH, 1, NW><<<grid, dim3(64 * NW), 0, stream>>>(a);
   return hipGetLastError();
 }
 
 }  // namespace
 
+int attn_block_m(int max_seq_len) { return max_seq_len >= 1024 ? 256 : 128; }
+
 hipError_t launch_schedule(const int32_t *offsets, const int32_t *p_offsets, int B, int mask,
                            int max_seq_len, int max_prefix_len, int32_t *work, int32_t *n_work,
                            hipStream_t stream) {
+  const int bm = attn_block_m(max_seq_len);
   const int64_t max_cost = (int64_t)(max_prefix_len + kBN - 1) / kBN + (max_seq_len + kBN - 1) / kBN + 1;
   const int nbins = (int)(max_cost < kSchedBins ? max_cost : kSchedBins);
-  schedule_kernel<<<1, kSchedThreads, 0, stream>>>(offsets, p_offsets, B, mask, nbins, work, n_work);
+  schedule_kernel<<<1, kSchedThreads, 0, stream>>>(offsets, p_offsets, B, mask, bm, nbins, work,
+                                                   n_work);
   return hipGetLastError();
 }
 
-hipError_t launch_attention(const AttnArgs &a, int dh, int64_t cap, hipStream_t stream) {
+hipError_t launch_attention(const AttnArgs &a, int dh, int max_seq_len, int64_t cap,
+                            hipStream_t stream) {
   if (cap <= 0 || a.num_heads <= 0) return hipSuccess;
+  const bool wide = attn_block_m(max_seq_len) == 256;
   switch (dh) {
-    case 32: return launch_dh<32>(a, cap, stream);
-    case 64: return launch_dh<64>(a, cap, stream);
-    case 128: return launch_dh<128>(a, cap, stream);
+    case 32: return wide ? launch_dh<32, 8>(a, cap, stream) : launch_dh<32, 4>(a, cap, stream);
+    case 64: return wide ? launch_dh<64, 8>(a, cap, stream) : launch_dh<64, 4>(a, cap, stream);
+    case 128: return wide ? launch_dh<128, 8>(a, cap, stream) : launch_dh<128, 4>(a, cap, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -36,12 +36,15 @@ struct AttnArgs {
   int mask;                 // 0 causal, 1 self-only
 };
 
-constexpr int kAttnBlockM = 128;  // query rows per workgroup
-constexpr int kAttnBlockN = 64;   // keys per LDS stage
+constexpr int kAttnBlockMMin = 128;  // query rows per workgroup: 128, or 256 for long rows
+constexpr int kAttnBlockN = 64;      // keys per LDS stage
 
-// Work list capacity (items) for a batch of B sequences and T tokens.
+// Query rows per attention workgroup for a batch whose longest sequence is max_seq_len.
+int attn_block_m(int max_seq_len);
+
+// Work list capacity (items) for a batch of B sequences and T tokens (any block size).
 inline int64_t attn_work_capacity(int64_t B, int64_t T) {
-  return (T + kAttnBlockM - 1) / kAttnBlockM + B + 1;
+  return (T + kAttnBlockMMin - 1) / kAttnBlockMMin + B + 1;
 }
 
 // Builds the longest-first (sequence, q-tile) list into work[0 .. 2*cap) and n_work.
@@ -49,7 +52,8 @@ hipError_t launch_schedule(const int32_t *offsets, const int32_t *p_offsets, int
                            int max_seq_len, int max_prefix_len, int32_t *work, int32_t *n_work,
                            hipStream_t stream);
 
-hipError_t launch_attention(const AttnArgs &a, int dh, int64_t cap, hipStream_t stream);
+hipError_t launch_attention(const AttnArgs &a, int dh, int max_seq_len, int64_t cap,
+                            hipStream_t stream);
 
 // G[T][HDV] = LayerNorm(O) * gamma + beta, times U (fp16 row of uvqk), as bf16.
 hipError_t launch_norm_gate(const float *O, const uint16_t *U, int64_t u_stride,
