@@ -45,7 +45,10 @@ class Prefix(ctypes.Structure):
 
 EXPORTS = {
     "hstu_layer_workspace_bytes": (c_size_t, [ctypes.POINTER(Dims), ctypes.POINTER(Jagged)]),
-    "hstu_attn_workspace_bytes": (c_size_t, [ctypes.POINTER(Dims), ctypes.POINTER(Jagged)]),
+    "hstu_mfalcon_workspace_bytes": (c_size_t, [ctypes.POINTER(Dims), ctypes.POINTER(Jagged),
+                                                ctypes.POINTER(Jagged)]),
+    "hstu_attn_workspace_bytes": (c_size_t, [ctypes.POINTER(Dims), ctypes.POINTER(Jagged),
+                                             ctypes.POINTER(Jagged)]),
     "hstu_layer_fwd": (c_int32, [ctypes.POINTER(Dims), ctypes.POINTER(Weights), ctypes.POINTER(Jagged),
                                  c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "hstu_layer_fwd_mfalcon": (c_int32, [ctypes.POINTER(Dims), ctypes.POINTER(Weights),

@@ -117,14 +117,20 @@ bool rows_addressable(int max_seq_len, int64_t row_elems) {
   return ((int64_t)max_seq_len + 64) * row_elems * 2 < ((int64_t)1 << 31);
 }
 
-size_t sched_bytes(const hstu_jagged_t *s) {
+// Attention scratch: work count, work list, per-token key-block timestamp ranges of the
+// batch and of its prefix (if any).
+size_t attn_ws_bytes(const hstu_jagged_t *s, const hstu_jagged_t *pre) {
   const int64_t cap = attn_work_capacity(s->batch, s->total_tokens);
-  return align_up((size_t)cap * 2 * sizeof(int32_t)) + kAlign;
+  size_t bytes = kAlign + align_up((size_t)cap * 2 * sizeof(int32_t));
+  bytes += align_up((size_t)s->total_tokens * 8);
+  if (pre != nullptr) bytes += align_up((size_t)pre->total_tokens * 8);
+  return bytes;
 }
 
-size_t layer_ws_bytes(const hstu_dims_t *d, const hstu_jagged_t *s) {
+size_t layer_ws_bytes(const hstu_dims_t *d, const hstu_jagged_t *s, const hstu_jagged_t *pre) {
   const size_t T = (size_t)s->total_tokens, hdv = (size_t)d->num_heads * d->dv;
-  return align_up(T * hdv * sizeof(float)) + align_up(T * hdv * sizeof(uint16_t)) + sched_bytes(s);
+  return align_up(T * hdv * sizeof(float)) + align_up(T * hdv * sizeof(uint16_t)) +
+         attn_ws_bytes(s, pre);
 }
 
 struct LayerWs {
@@ -132,9 +138,23 @@ struct LayerWs {
   uint16_t *g;
   int32_t *work;
   int32_t *n_work;
+  int2 *kstat;
+  int2 *p_kstat;
 };
 
-LayerWs carve_layer(void *ws, const hstu_dims_t *d, const hstu_jagged_t *s) {
+void carve_attn(char *p, const hstu_jagged_t *s, const hstu_jagged_t *pre, LayerWs &w) {
+  const int64_t cap = attn_work_capacity(s->batch, s->total_tokens);
+  w.n_work = (int32_t *)p;
+  p += kAlign;
+  w.work = (int32_t *)p;
+  p += align_up((size_t)cap * 2 * sizeof(int32_t));
+  w.kstat = (int2 *)p;
+  p += align_up((size_t)s->total_tokens * 8);
+  w.p_kstat = pre != nullptr ? (int2 *)p : nullptr;
+}
+
+LayerWs carve_layer(void *ws, const hstu_dims_t *d, const hstu_jagged_t *s,
+                    const hstu_jagged_t *pre) {
   const size_t T = (size_t)s->total_tokens, hdv = (size_t)d->num_heads * d->dv;
   char *p = (char *)ws;
   LayerWs w;
@@ -142,9 +162,20 @@ LayerWs carve_layer(void *ws, const hstu_dims_t *d, const hstu_jagged_t *s) {
   p += align_up(T * hdv * sizeof(float));
   w.g = (uint16_t *)p;
   p += align_up(T * hdv * sizeof(uint16_t));
-  w.n_work = (int32_t *)p;
-  w.work = (int32_t *)(p + kAlign);
+  carve_attn(p, s, pre, w);
   return w;
+}
+
+// Key-block timestamp ranges for the batch and its prefix, when the time term is on.
+hipError_t launch_stats(const AttnArgs &aa, const hstu_jagged_t *s, const hstu_jagged_t *pre,
+                        hipStream_t st) {
+  if (aa.rab_time == nullptr || s->timestamps == nullptr) return hipSuccess;
+  hipError_t e = launch_block_stats(s->timestamps, s->seq_offsets, s->batch,
+                                    const_cast<int2 *>(aa.kstat), st);
+  if (e == hipSuccess && pre != nullptr && pre->timestamps != nullptr && pre->total_tokens > 0)
+    e = launch_block_stats(pre->timestamps, pre->seq_offsets, pre->batch,
+                           const_cast<int2 *>(aa.p_kstat), st);
+  return e;
 }
 
 hstu_status_t check_ws(void *ws, size_t have, size_t need) {
@@ -172,6 +203,8 @@ AttnArgs attn_args(const hstu_dims_t *d, const float *rab_pos, const float *rab_
   a.out_stride = (int64_t)d->num_heads * d->dv;
   a.work = w.work;
   a.n_work = w.n_work;
+  a.kstat = w.kstat;
+  a.p_kstat = w.p_kstat;
   a.num_heads = d->num_heads;
   a.mask = 0;
   return a;
@@ -180,7 +213,8 @@ AttnArgs attn_args(const hstu_dims_t *d, const float *rab_pos, const float *rab_
 // f1 -> attention -> norm-gate -> f2 for one batch whose attention args are ready.
 hstu_status_t run_layer(const hstu_dims_t *d, const hstu_weights_t *w, const hstu_jagged_t *s,
                         const uint16_t *x, uint16_t *y, uint16_t *uvqk, const AttnArgs &aa,
-                        const LayerWs &lw, int max_prefix, hipStream_t st) {
+                        const LayerWs &lw, const hstu_jagged_t *pre, hipStream_t st) {
+  const int max_prefix = pre != nullptr ? pre->max_seq_len : 0;
   const int T = s->total_tokens;
   const int hdv = d->num_heads * d->dv;
   const int n1 = 2 * d->num_heads * (d->dqk + d->dv);
@@ -189,6 +223,8 @@ hstu_status_t run_layer(const hstu_dims_t *d, const hstu_weights_t *w, const hst
     return launch_schedule(s->seq_offsets, aa.p_offsets, s->batch, aa.mask, s->max_seq_len,
                            max_prefix, lw.work, lw.n_work, st);
   });
+  if (e != hipSuccess) return hip_fail(e);
+  e = timed(0, st, [&] { return launch_stats(aa, s, pre, st); });
   if (e != hipSuccess) return hip_fail(e);
   e = timed(1, st, [&] { return launch_gemm(x, w->w1, w->b1, uvqk, T, n1, d->d_model, ACT_SILU, OUT_F16, st); });
   if (e != hipSuccess) return hip_fail(e);
@@ -217,12 +253,21 @@ extern "C" {
 
 size_t hstu_layer_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_t *seq) {
   if (check_dims(dims) != HSTU_OK || check_seq(seq) != HSTU_OK) return 0;
-  return layer_ws_bytes(dims, seq);
+  return layer_ws_bytes(dims, seq, nullptr);
 }
 
-size_t hstu_attn_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_t *seq) {
+size_t hstu_mfalcon_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_t *hist,
+                                    const hstu_jagged_t *cand) {
+  if (check_dims(dims) != HSTU_OK || check_seq(hist) != HSTU_OK || check_seq(cand) != HSTU_OK)
+    return 0;
+  return layer_ws_bytes(dims, cand, hist);
+}
+
+size_t hstu_attn_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_t *seq,
+                                 const hstu_jagged_t *prefix_seq) {
   if (check_attn_dims(dims) != HSTU_OK || check_seq(seq) != HSTU_OK) return 0;
-  return sched_bytes(seq);
+  if (prefix_seq != nullptr && check_seq(prefix_seq) != HSTU_OK) return 0;
+  return attn_ws_bytes(seq, prefix_seq);
 }
 
 hstu_status_t hstu_layer_fwd(const hstu_dims_t *dims, const hstu_weights_t *w,
@@ -237,16 +282,16 @@ hstu_status_t hstu_layer_fwd(const hstu_dims_t *dims, const hstu_weights_t *w,
   if (!aligned16(x) || !aligned16(y) || !aligned16(uvqk)) return HSTU_ERR_INVALID_ARG;
   if ((void *)x == (void *)y) return HSTU_ERR_INVALID_ARG;
   if (seq->batch == 0 || seq->total_tokens == 0) return HSTU_OK;
-  if ((st = check_ws(ws, ws_bytes, layer_ws_bytes(dims, seq))) != HSTU_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, layer_ws_bytes(dims, seq, nullptr))) != HSTU_OK) return st;
   if (!rows_addressable(seq->max_seq_len, 2 * (int64_t)dims->num_heads * (dims->dqk + dims->dv)))
     return HSTU_ERR_UNSUPPORTED;
 
-  const LayerWs lw = carve_layer(ws, dims, seq);
+  const LayerWs lw = carve_layer(ws, dims, seq, nullptr);
   const int hdv = dims->num_heads * dims->dv, hqk = dims->num_heads * dims->dqk;
   const int64_t n1 = 2 * (int64_t)(hdv + hqk);
   AttnArgs aa = attn_args(dims, w->rab_pos, w->rab_time, seq, uvqk + 2 * hdv,
                           uvqk + 2 * hdv + hqk, uvqk + hdv, n1, lw.o, lw);
-  return run_layer(dims, w, seq, x, y, uvqk, aa, lw, 0, (hipStream_t)stream);
+  return run_layer(dims, w, seq, x, y, uvqk, aa, lw, nullptr, (hipStream_t)stream);
 }
 
 hstu_status_t hstu_layer_fwd_mfalcon(const hstu_dims_t *dims, const hstu_weights_t *w,
@@ -268,14 +313,14 @@ hstu_status_t hstu_layer_fwd_mfalcon(const hstu_dims_t *dims, const hstu_weights
   if ((void *)x_cand == (void *)y_cand) return HSTU_ERR_INVALID_ARG;
   if ((cand->timestamps == nullptr) != (hist->timestamps == nullptr)) return HSTU_ERR_INVALID_ARG;
   if (cand->batch == 0 || cand->total_tokens == 0) return HSTU_OK;
-  if ((st = check_ws(ws, ws_bytes, layer_ws_bytes(dims, cand))) != HSTU_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, layer_ws_bytes(dims, cand, hist))) != HSTU_OK) return st;
   {
     const int64_t n1 = 2 * (int64_t)dims->num_heads * (dims->dqk + dims->dv);
     if (!rows_addressable(cand->max_seq_len, n1) || !rows_addressable(hist->max_seq_len, n1))
       return HSTU_ERR_UNSUPPORTED;
   }
 
-  const LayerWs lw = carve_layer(ws, dims, cand);
+  const LayerWs lw = carve_layer(ws, dims, cand, hist);
   const int hdv = dims->num_heads * dims->dv, hqk = dims->num_heads * dims->dqk;
   const int64_t n1 = 2 * (int64_t)(hdv + hqk);
   AttnArgs aa = attn_args(dims, w->rab_pos, w->rab_time, cand, uvqk_cand + 2 * hdv,
@@ -286,8 +331,7 @@ hstu_status_t hstu_layer_fwd_mfalcon(const hstu_dims_t *dims, const hstu_weights
   aa.pk = hist_uvqk + 2 * hdv + hqk;
   aa.pv = hist_uvqk + hdv;
   aa.p_stride = n1;
-  return run_layer(dims, w, cand, x_cand, y_cand, uvqk_cand, aa, lw, hist->max_seq_len,
-                   (hipStream_t)stream);
+  return run_layer(dims, w, cand, x_cand, y_cand, uvqk_cand, aa, lw, hist, (hipStream_t)stream);
 }
 
 hstu_status_t hstu_attn_fwd(const hstu_dims_t *dims, const float *rab_pos, const float *rab_time,
@@ -317,14 +361,14 @@ hstu_status_t hstu_attn_fwd(const hstu_dims_t *dims, const float *rab_pos, const
     max_prefix = prefix->seq->max_seq_len;
   }
   if (seq->batch == 0 || seq->total_tokens == 0) return HSTU_OK;
-  if ((st = check_ws(ws, ws_bytes, sched_bytes(seq))) != HSTU_OK) return st;
+  const hstu_jagged_t *pre_seq = prefix != nullptr ? prefix->seq : nullptr;
+  if ((st = check_ws(ws, ws_bytes, attn_ws_bytes(seq, pre_seq))) != HSTU_OK) return st;
   if (!rows_addressable(seq->max_seq_len, row_stride) ||
       (prefix != nullptr && !rows_addressable(prefix->seq->max_seq_len, prefix->row_stride)))
     return HSTU_ERR_UNSUPPORTED;
 
   LayerWs lw{};
-  lw.n_work = (int32_t *)ws;
-  lw.work = (int32_t *)((char *)ws + kAlign);
+  carve_attn((char *)ws, seq, pre_seq, lw);
   AttnArgs aa = attn_args(dims, rab_pos, rab_time, seq, q, k, v, row_stride, out, lw);
   aa.mask = mask == HSTU_MASK_CAUSAL ? 0 : 1;
   if (prefix != nullptr) {
@@ -339,6 +383,8 @@ hstu_status_t hstu_attn_fwd(const hstu_dims_t *dims, const float *rab_pos, const
     return launch_schedule(seq->seq_offsets, aa.p_offsets, seq->batch, aa.mask, seq->max_seq_len,
                            max_prefix, lw.work, lw.n_work, sst);
   });
+  if (e != hipSuccess) return hip_fail(e);
+  e = timed(0, sst, [&] { return launch_stats(aa, seq, pre_seq, sst); });
   if (e != hipSuccess) return hip_fail(e);
   const int64_t cap = attn_work_capacity(seq->batch, seq->total_tokens);
   e = timed(2, sst, [&] { return launch_attention(aa, dims->dqk, seq->max_seq_len, cap, sst); });

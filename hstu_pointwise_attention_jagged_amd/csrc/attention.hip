@@ -6,9 +6,10 @@
 // jagged batches computed at their true lengths (section "另外三块拼图", item 1).
 //
 // gfx950 design
-//  * One workgroup = 4 waves = 128 query rows of one (sequence, head); each wave owns 32
-//    query rows whose Q fragments stay in registers for the whole key loop.
-//  * Keys stream through LDS in stages of 64 (double buffered, register prefetch).  K is
+//  * One workgroup = 4 or 8 waves = 128 or 256 query rows of one (sequence, head); each
+//    wave owns 32 query rows whose Q fragments stay in registers for the whole key loop.
+//  * Keys stream through LDS in stages of 64 (double buffered, register prefetch through
+//    range-checked buffer loads, so keys past a sequence's end read as zero).  K is
 //    stored row-major; V is stored transposed (feature-major) with a key permutation
 //    inside each 16-key group, so the MFMA A operand of the P.V product is one 16-byte
 //    LDS read per lane.
@@ -18,16 +19,21 @@
 //    with no trip through LDS.  Q, K, V and A are fp16 operands (the same MFMA rate as
 //    bf16 on gfx950, 3 more mantissa bits); accumulation and O stay fp32.
 //  * The rab index math is integer only: relative position clamp, and the log2 time
-//    bucket from the bit length of (1 + gap); table values come from LDS.  Far from the
-//    diagonal a whole 32x32 block usually shares one bias value: every relative position
-//    is past the last position bucket and (bucket being monotone in the gap) the
-//    buckets of the smallest and largest possible gap -- from the min/max timestamps of
-//    the block's queries and keys -- coincide.  Such blocks start the score MFMA from
-//    that constant and skip all per-element bias work.
+//    bucket from the bit length of (1 + gap).  Each wave classifies every 32-key block
+//    with scalar arithmetic, from its queries' position / timestamp range and the key
+//    block's timestamp range (precomputed by block_stats_kernel):
+//      - constant bias: every relative position is past the last position bucket and
+//        (the bucket being monotone in the gap) the smallest and largest gap share one
+//        time bucket; the score MFMA then starts from that constant;
+//      - two buckets: positions as above, gaps spanning exactly buckets b and b+1; one
+//        integer compare per element picks between two constants;
+//      - general: per-element indices with table values from LDS.
 //  * Tiles are skipped from the jagged offsets and the mask: a wave never multiplies a
 //    32-key block that lies wholly after its queries (causal) or away from them
 //    (candidate self term); only blocks that straddle the diagonal are masked per
 //    element.  Masked pairs contribute exactly 0.
+//  * When both 32-key blocks of a stage take the constant-bias path, they run as one
+//    basic block so the compiler interleaves the MFMAs of one with the SiLU of the other.
 #include <type_traits>
 
 #include "common.h"
@@ -42,6 +48,8 @@ constexpr int kMaxPos = 1024;
 constexpr int kMaxTime = 64;
 constexpr int kVtPitch = kBN + 8;  // transposed V row pitch (fp16): 144 bytes
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
+
+enum BiasKind { BIAS_CONST = 0, BIAS_TWO = 1, BIAS_GENERAL = 2 };
 
 // Physical slot of key kk (0..63) inside a transposed V stage: within each group of 16
 // keys the order is [0-3, 8-11, 4-7, 12-15], which puts the 8 keys a lane multiplies in
@@ -59,6 +67,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 
 __device__ __forceinline__ int sgpr(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// (gap >= thr) for gap = max(0, ts_q - ts_k) over the full int32 range, thr >= 1.
+__device__ __forceinline__ bool gap_at_least(int32_t ts_q, int32_t ts_k, uint32_t thr) {
+  return ts_q > ts_k && (uint32_t)ts_q - (uint32_t)ts_k >= thr;
+}
+
 template <int DH, int MASK, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
   constexpr int NT = 64 * NW;           // threads per workgroup
@@ -68,13 +81,16 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
   constexpr int FT = DH / 32;           // 32-wide feature tiles of the output
   constexpr int K_UNITS = kBN * DH / 8;  // 16-byte chunks of a K stage
   constexpr int K_ITERS = (K_UNITS + NT - 1) / NT;
-  constexpr int V_UNITS = 16 * (DH / 8);  // (4 keys x 8 features) units of a V stage
+  // V is staged in units of KPU keys x 8 features: 2 keys when that spreads a stage over
+  // all threads of an 8-wave group, else 4
+  constexpr int KPU = (NW == 8 && (kBN / 2) * (DH / 8) <= NT) ? 2 : 4;
+  constexpr int V_GROUPS = kBN / KPU;
+  constexpr int V_UNITS = V_GROUPS * (DH / 8);
   static_assert(V_UNITS <= NT, "one V unit per thread");
 
   __shared__ __attribute__((aligned(16))) uint16_t ks_lds[2][kBN * KPITCH];
   __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][DH * kVtPitch];
   __shared__ __attribute__((aligned(16))) int32_t kts_lds[2][kBN];
-  __shared__ int32_t kstat[2][2][2];  // [buf][32-key block][min, max] of valid key timestamps
   __shared__ float ptab[kMaxPos];
   __shared__ float ttab[kMaxTime];
 
@@ -97,15 +113,15 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
   const bool use_pos = p.rab_pos != nullptr;
   const bool use_time = p.rab_time != nullptr && p.ts != nullptr &&
                         (p.p_offsets == nullptr || p.p_ts != nullptr);
+  const int rrow = p.rab_per_head ? h : 0;
+  const float *rab_pos = use_pos ? p.rab_pos + rrow * p.pos_buckets : nullptr;
+  const float *rab_time = use_time ? p.rab_time + rrow * p.time_buckets : nullptr;
 
-  // relative-bias tables of this head -> LDS
-  {
-    const int r = p.rab_per_head ? h : 0;
-    if (use_pos)
-      for (int i = tid; i < p.pos_buckets; i += NT) ptab[i] = p.rab_pos[r * p.pos_buckets + i];
-    if (use_time)
-      for (int i = tid; i < p.time_buckets; i += NT) ttab[i] = p.rab_time[r * p.time_buckets + i];
-  }
+  // relative-bias tables of this head -> LDS (for the per-element path)
+  if (use_pos)
+    for (int i = tid; i < p.pos_buckets; i += NT) ptab[i] = rab_pos[i];
+  if (use_time)
+    for (int i = tid; i < p.time_buckets; i += NT) ttab[i] = rab_time[i];
 
   // this wave's queries: local index qi, position, timestamp; Q fragments in registers
   const int qbase = q0 + wave * 32;  // wave-uniform
@@ -157,18 +173,16 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
 
   // staging registers
   u32x4 rk[K_ITERS];
-  u32x4 rv[4];
+  u32x4 rv[KPU];
   int32_t rts = 0;
-  bool rts_ok = false;
 
-  // V unit of this thread: key group kg (fastest, so a transposed LDS write of 16 lanes
-  // covers one 128-byte row) and feature chunk fc
-  const int v_kg = tid % 16, v_fc = (tid / 16) * 8;
+  // V unit of this thread: key group (fastest, so a transposed LDS write of a wave's
+  // lanes covers whole 128-byte rows) and feature chunk
+  const int v_kg = tid % V_GROUPS, v_fc = (tid / V_GROUPS) * 8;
 
   auto load_tile = [&](int t) {
     const bool pre = t < n_pt;
     const int kbase = pre ? t * kBN : own_start + (t - n_pt) * kBN;
-    const int limit = pre ? n_p : n;
     const int64_t stride = pre ? p.p_stride : p.stride;
     const __amdgpu_buffer_rsrc_t kr = pre ? k_pre : k_own;
     const __amdgpu_buffer_rsrc_t vr = pre ? v_pre : v_own;
@@ -181,17 +195,15 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
         rk[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0));
       }
     }
-    if (tid < V_UNITS) {
+    if (V_UNITS == NT || tid < V_UNITS) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int off = (int)(((int64_t)(kbase + v_kg * 4 + r) * stride + h * DH + v_fc) * 2);
+      for (int r = 0; r < KPU; ++r) {
+        const int off = (int)(((int64_t)(kbase + v_kg * KPU + r) * stride + h * DH + v_fc) * 2);
         rv[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0));
       }
     }
-    if (use_time && tid < kBN) {
-      rts_ok = kbase + tid < limit;
+    if (use_time && tid < kBN)
       rts = __builtin_amdgcn_raw_buffer_load_b32(pre ? t_pre : t_own, (kbase + tid) * 4, 0, 0);
-    }
   };
 
   auto store_tile = [&](int buf) {
@@ -203,66 +215,53 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
         *reinterpret_cast<u32x4 *>(&ks_lds[buf][row * KPITCH + col]) = rk[j];
       }
     }
-    if (tid < V_UNITS) {
-      const int slot = vt_slot(v_kg * 4);
-      // transpose 4 keys x 8 features into 8 rows of 4 keys
+    if (V_UNITS == NT || tid < V_UNITS) {
+      const int slot = vt_slot(v_kg * KPU);
+      // transpose KPU keys x 8 features into 8 rows of KPU keys
 #pragma unroll
       for (int f = 0; f < 8; ++f) {
         const int w = f >> 1;
         const bool hi = f & 1;
-        uint32_t e0 = hi ? (rv[0][w] >> 16) : (rv[0][w] & 0xffffu);
-        uint32_t e1 = hi ? (rv[1][w] >> 16) : (rv[1][w] & 0xffffu);
-        uint32_t e2 = hi ? (rv[2][w] >> 16) : (rv[2][w] & 0xffffu);
-        uint32_t e3 = hi ? (rv[3][w] >> 16) : (rv[3][w] & 0xffffu);
-        u32x2 pk = {e0 | (e1 << 16), e2 | (e3 << 16)};
-        *reinterpret_cast<u32x2 *>(&vt_lds[buf][(v_fc + f) * kVtPitch + slot]) = pk;
-      }
-    }
-    if (use_time && tid < kBN) {  // wave 0: timestamps and per-block min / max
-      kts_lds[buf][tid] = rts;
-      int32_t mn = rts_ok ? rts : INT32_MAX, mx = rts_ok ? rts : INT32_MIN;
+        uint32_t e[KPU];
 #pragma unroll
-      for (int o = 1; o < 32; o <<= 1) {
-        mn = min(mn, __shfl_xor(mn, o, 64));
-        mx = max(mx, __shfl_xor(mx, o, 64));
-      }
-      if ((tid & 31) == 0) {
-        kstat[buf][tid >> 5][0] = mn;
-        kstat[buf][tid >> 5][1] = mx;
+        for (int r = 0; r < KPU; ++r) e[r] = hi ? (rv[r][w] >> 16) : (rv[r][w] & 0xffffu);
+        if constexpr (KPU == 2) {
+          *reinterpret_cast<uint32_t *>(&vt_lds[buf][(v_fc + f) * kVtPitch + slot]) = e[0] | (e[1] << 16);
+        } else {
+          u32x2 pk = {e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+          *reinterpret_cast<u32x2 *>(&vt_lds[buf][(v_fc + f) * kVtPitch + slot]) = pk;
+        }
       }
     }
+    if (use_time && tid < kBN) kts_lds[buf][tid] = rts;
   };
 
   f32x16 acc_o[FT];
 #pragma unroll
   for (int f = 0; f < FT; ++f) acc_o[f] = f32x16{};
 
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
+  int cur_buf = 0;
 
   // One 32-key block of this wave: scores, bias, SiLU, mask, aggregation.  The
-  // compile-time flags pick the variant so the common case (constant bias, no mask)
-  // carries no per-element index or mask code.
-  int cur_buf = 0;
-  auto block = [&](int kb, int kbase, bool is_prefix, float bias0, auto uniform_c, auto masked_c) {
-    constexpr bool UNIFORM = decltype(uniform_c)::value;
+  // compile-time kind picks the variant, so the common case carries no per-element
+  // index or mask code.
+  auto block = [&](int kb, int kbase, bool is_prefix, float bias_lo, float bias_hi, uint32_t thr,
+                   auto kind_c, auto masked_c) {
+    constexpr int KIND = decltype(kind_c)::value;
     constexpr bool MASKED = decltype(masked_c)::value;
     const int buf_ = cur_buf;
     // S^T = K Q^T : lane holds query lrow, keys 8*(i/4) + 4*half + (i%4)
     f32x16 s;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = UNIFORM ? bias0 : 0.0f;
+    for (int i = 0; i < 16; ++i) s[i] = KIND == BIAS_GENERAL ? 0.0f : bias_lo;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const f16x8 kf = as_f16x8(*reinterpret_cast<const u32x4 *>(
           &ks_lds[buf_][(kb * 32 + lrow) * KPITCH + ks * 16 + half * 8]));
       s = mfma32_f16(kf, qf[ks], s);
     }
-    if (!UNIFORM) {
-      // per-element bias: integer indices, table values from LDS
+    if constexpr (KIND != BIAS_CONST) {
+      const float delta = bias_hi - bias_lo;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int kl = kb * 32 + 8 * g + 4 * half;  // first of 4 consecutive keys
@@ -272,21 +271,25 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = 4 * g + r;
-          float x = s[i];
-          if (use_pos) {
-            const int kidx = kbase + kl + r;
-            const int kpos = is_prefix ? kidx : (MASK == 0 ? n_p + kidx : n_p);
-            x += ptab[min(max(qpos - kpos, 0), p.pos_buckets - 1)];
+          if constexpr (KIND == BIAS_TWO) {
+            s[i] += gap_at_least(qts, kt4[r], thr) ? delta : 0.0f;
+          } else {
+            float x = s[i];
+            if (use_pos) {
+              const int kidx = kbase + kl + r;
+              const int kpos = is_prefix ? kidx : (MASK == 0 ? n_p + kidx : n_p);
+              x += ptab[min(max(qpos - kpos, 0), p.pos_buckets - 1)];
+            }
+            if (use_time) x += ttab[min(time_log2_bucket(qts, kt4[r]), p.time_buckets - 1)];
+            s[i] = x;
           }
-          if (use_time) x += ttab[min(time_log2_bucket(qts, kt4[r]), p.time_buckets - 1)];
-          s[i] = x;
         }
       }
     }
     float a[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) a[i] = silu_f32(s[i]);
-    if (MASKED) {
+    if constexpr (MASKED) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int kidx = kbase + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
@@ -304,9 +307,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
     }
     // O^T += V^T P^T
 #pragma unroll
-    for (int f = 0; f < FT; ++f) {
+    for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
+      for (int f = 0; f < FT; ++f) {
         const f16x8 vf = as_f16x8(*reinterpret_cast<const u32x4 *>(
             &vt_lds[buf_][(f * 32 + lrow) * kVtPitch + kb * 32 + s2 * 16 + half * 8]));
         acc_o[f] = mfma32_f16(vf, pf[s2], acc_o[f]);
@@ -314,6 +317,71 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
     }
   };
 
+  // Both 32-key blocks of a stage with a constant bias and no mask (the common case far
+  // from the diagonal), in one basic block: the score MFMAs of block B can overlap the
+  // SiLU of block A, and the P.V MFMAs of A the SiLU of B.
+  auto pair_const = [&](float bias_a, float bias_b) {
+    const int buf_ = cur_buf;
+    f32x16 sa, sb;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sa[i] = bias_a;
+      sb[i] = bias_b;
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const f16x8 kf = as_f16x8(*reinterpret_cast<const u32x4 *>(
+          &ks_lds[buf_][lrow * KPITCH + ks * 16 + half * 8]));
+      sa = mfma32_f16(kf, qf[ks], sa);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const f16x8 kf = as_f16x8(*reinterpret_cast<const u32x4 *>(
+          &ks_lds[buf_][(32 + lrow) * KPITCH + ks * 16 + half * 8]));
+      sb = mfma32_f16(kf, qf[ks], sb);
+    }
+    f16x8 pa[2], pb[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      u32x4 pk;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        pk[j] = pack_f16(silu_f32(sa[8 * s2 + 2 * j]), silu_f32(sa[8 * s2 + 2 * j + 1]));
+      pa[s2] = as_f16x8(pk);
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      u32x4 pk;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        pk[j] = pack_f16(silu_f32(sb[8 * s2 + 2 * j]), silu_f32(sb[8 * s2 + 2 * j + 1]));
+      pb[s2] = as_f16x8(pk);
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int f = 0; f < FT; ++f) {
+        const f16x8 vf = as_f16x8(*reinterpret_cast<const u32x4 *>(
+            &vt_lds[buf_][(f * 32 + lrow) * kVtPitch + s2 * 16 + half * 8]));
+        acc_o[f] = mfma32_f16(vf, pa[s2], acc_o[f]);
+      }
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int f = 0; f < FT; ++f) {
+        const f16x8 vf = as_f16x8(*reinterpret_cast<const u32x4 *>(
+            &vt_lds[buf_][(f * 32 + lrow) * kVtPitch + 32 + s2 * 16 + half * 8]));
+        acc_o[f] = mfma32_f16(vf, pb[s2], acc_o[f]);
+      }
+  };
+
+  if (n_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  const float pos_last = use_pos ? rab_pos[p.pos_buckets - 1] : 0.0f;
   const int qmax = qbase + 31;
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
@@ -323,49 +391,79 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
     const bool is_prefix = t < n_pt;
     const int kbase = is_prefix ? t * kBN : own_start + (t - n_pt) * kBN;
     const int limit = is_prefix ? n_p : n;
+    const int2 *kstat = is_prefix ? p.p_kstat + p0 : p.kstat + s0;
 
+    // classify both 32-key blocks with scalar arithmetic
+    bool live[2], masked[2];
+    int kind[2];
+    float blo[2], bhi[2];
+    uint32_t thr[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int k0 = kbase + kb * 32;
-      // wave-uniform skips: no valid key, no valid query, or a block wholly masked
-      if (k0 >= limit || !wave_has_rows) continue;
-      bool need_mask = false;
+      bool lv = k0 < limit && wave_has_rows;
+      bool mk = false;
       if (!is_prefix) {
         if (MASK == 0) {
-          if (k0 > qmax) continue;
-          need_mask = k0 + 31 > qbase;
+          lv = lv && k0 <= qmax;
+          mk = k0 + 31 > qbase;
         } else {
-          if (k0 > qmax || k0 + 31 < qbase) continue;
-          need_mask = true;
+          lv = lv && k0 <= qmax && k0 + 31 >= qbase;
+          mk = true;
         }
       }
-      // Is the bias one constant over this block?  Positions: every relative position
-      // reaches the last bucket.  Time: the buckets of the extreme gaps coincide.
-      bool uniform = true;
-      float bias0 = 0.0f;
+      live[kb] = lv;
+      masked[kb] = mk;
+      int kd = BIAS_CONST;
+      float lo = 0.0f, hi = 0.0f;
+      uint32_t th = 1;
       if (use_pos) {
         const int kpos_max = is_prefix ? k0 + 31 : (MASK == 0 ? n_p + k0 + 31 : n_p);
-        uniform = qpos_min - kpos_max >= p.pos_buckets - 1;
-        bias0 = ptab[p.pos_buckets - 1];
+        if (qpos_min - kpos_max >= p.pos_buckets - 1) {
+          lo = hi = pos_last;
+        } else {
+          kd = BIAS_GENERAL;
+        }
       }
-      if (use_time && uniform) {
-        const int32_t kmin = sgpr(kstat[buf][kb][0]), kmax = sgpr(kstat[buf][kb][1]);
-        const int tb_lo = min(time_log2_bucket(qts_min, kmax), p.time_buckets - 1);
-        const int tb_hi = min(time_log2_bucket(qts_max, kmin), p.time_buckets - 1);
-        uniform = tb_lo == tb_hi;
-        bias0 += ttab[tb_lo];
+      if (use_time && kd != BIAS_GENERAL && lv) {
+        const int2 st = kstat[k0];  // (min, max) timestamp of keys k0 .. k0+31
+        const int tb_lo = min(time_log2_bucket(qts_min, st.y), p.time_buckets - 1);
+        const int tb_hi = min(time_log2_bucket(qts_max, st.x), p.time_buckets - 1);
+        lo += rab_time[tb_lo];
+        hi += rab_time[tb_hi];
+        if (tb_hi != tb_lo) {
+          kd = tb_hi == tb_lo + 1 ? BIAS_TWO : BIAS_GENERAL;
+          th = (uint32_t)(((uint64_t)1 << (tb_lo + 1)) - 1);
+        }
       }
-      uniform = sgpr(uniform);
-      bias0 = __builtin_bit_cast(float, sgpr(__builtin_bit_cast(int, bias0)));
-      need_mask = sgpr(need_mask);
-      if (uniform && !need_mask)
-        block(kb, kbase, is_prefix, bias0, std::true_type{}, std::false_type{});
-      else if (uniform)
-        block(kb, kbase, is_prefix, bias0, std::true_type{}, std::true_type{});
-      else if (!need_mask)
-        block(kb, kbase, is_prefix, bias0, std::false_type{}, std::false_type{});
-      else
-        block(kb, kbase, is_prefix, bias0, std::false_type{}, std::true_type{});
+      kind[kb] = kd;
+      blo[kb] = lo;
+      bhi[kb] = hi;
+      thr[kb] = th;
+    }
+    if (live[0] && live[1] && kind[0] == BIAS_CONST && kind[1] == BIAS_CONST && !masked[0] &&
+        !masked[1]) {
+      pair_const(blo[0], blo[1]);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if (!live[kb]) continue;
+        const float lo = blo[kb], hi = bhi[kb];
+        const uint32_t th = thr[kb];
+        if (!masked[kb]) {
+          if (kind[kb] == BIAS_CONST)
+            block(kb, kbase, is_prefix, lo, hi, th, std::integral_constant<int, BIAS_CONST>{}, std::false_type{});
+          else if (kind[kb] == BIAS_TWO)
+            block(kb, kbase, is_prefix, lo, hi, th, std::integral_constant<int, BIAS_TWO>{}, std::false_type{});
+          else
+            block(kb, kbase, is_prefix, lo, hi, th, std::integral_constant<int, BIAS_GENERAL>{}, std::false_type{});
+        } else {
+          if (kind[kb] == BIAS_CONST)
+            block(kb, kbase, is_prefix, lo, hi, th, std::integral_constant<int, BIAS_CONST>{}, std::true_type{});
+          else
+            block(kb, kbase, is_prefix, lo, hi, th, std::integral_constant<int, BIAS_GENERAL>{}, std::true_type{});
+        }
+      }
     }
 
     if (t + 1 < n_tiles) store_tile(buf ^ 1);
@@ -382,6 +480,27 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
         f32x4 v = {acc_o[f][4 * g], acc_o[f][4 * g + 1], acc_o[f][4 * g + 2], acc_o[f][4 * g + 3]};
         *reinterpret_cast<f32x4 *>(orow + f * 32 + g * 8) = v;
       }
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// Timestamp range of every 32-key block: stat[t] = (min, max) of ts over keys
+// [t, min(t + 32, end of t's sequence)).  One workgroup per sequence.
+// ------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void block_stats_kernel(const int32_t *__restrict__ ts,
+                                                          const int32_t *__restrict__ offsets,
+                                                          int2 *__restrict__ stat) {
+  const int b = blockIdx.x;
+  const int s0 = offsets[b], s1 = offsets[b + 1];
+  for (int t = s0 + threadIdx.x; t < s1; t += blockDim.x) {
+    const int e = min(t + 32, s1);
+    int32_t mn = ts[t], mx = mn;
+    for (int j = t + 1; j < e; ++j) {
+      const int32_t v = ts[j];
+      mn = min(mn, v);
+      mx = max(mx, v);
+    }
+    stat[t] = int2{mn, mx};
   }
 }
 
@@ -461,6 +580,13 @@ hipError_t launch_schedule(const int32_t *offsets, const int32_t *p_offsets, int
   const int nbins = (int)(max_cost < kSchedBins ? max_cost : kSchedBins);
   schedule_kernel<<<1, kSchedThreads, 0, stream>>>(offsets, p_offsets, B, mask, bm, nbins, work,
                                                    n_work);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_stats(const int32_t *ts, const int32_t *offsets, int B, int2 *stat,
+                              hipStream_t stream) {
+  if (B <= 0) return hipSuccess;
+  block_stats_kernel<<<B, 256, 0, stream>>>(ts, offsets, stat);
   return hipGetLastError();
 }
 

@@ -18,7 +18,7 @@ from . import _lib
 
 __all__ = ["HSTUError", "LayerDims", "DeviceWeights", "DeviceJagged", "hstu_layer_fwd",
            "hstu_layer_fwd_mfalcon", "hstu_attn_fwd", "hstu_layer_workspace_bytes",
-           "hstu_attn_workspace_bytes", "hstu_validate_jagged", "profile_enable", "profile_reset",
+           "hstu_attn_workspace_bytes", "hstu_mfalcon_workspace_bytes", "hstu_validate_jagged", "profile_enable", "profile_reset",
            "profile_collect"]
 
 
@@ -127,10 +127,19 @@ def hstu_layer_workspace_bytes(dims: LayerDims, seq: DeviceJagged) -> int:
     return int(lib.hstu_layer_workspace_bytes(ctypes.byref(d), ctypes.byref(s)))
 
 
-def hstu_attn_workspace_bytes(dims: LayerDims, seq: DeviceJagged) -> int:
+def hstu_attn_workspace_bytes(dims: LayerDims, seq: DeviceJagged,
+                              prefix_seq: Optional[DeviceJagged] = None) -> int:
     lib = _lib.load()
     d, s = dims.c(), seq.c()
-    return int(lib.hstu_attn_workspace_bytes(ctypes.byref(d), ctypes.byref(s)))
+    ps = prefix_seq.c() if prefix_seq is not None else None
+    return int(lib.hstu_attn_workspace_bytes(ctypes.byref(d), ctypes.byref(s),
+                                             ctypes.byref(ps) if ps is not None else None))
+
+
+def hstu_mfalcon_workspace_bytes(dims: LayerDims, hist: DeviceJagged, cand: DeviceJagged) -> int:
+    lib = _lib.load()
+    d, h, c = dims.c(), hist.c(), cand.c()
+    return int(lib.hstu_mfalcon_workspace_bytes(ctypes.byref(d), ctypes.byref(h), ctypes.byref(c)))
 
 
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
@@ -178,7 +187,7 @@ def hstu_layer_fwd_mfalcon(dims: LayerDims, w: DeviceWeights, hist: DeviceJagged
     _check(y_cand, torch.bfloat16, "y_cand")
     _check(uvqk_cand, torch.float16, "uvqk_cand")
     d, wc, hs, cs = dims.c(), w.c(), hist.c(), cand.c()
-    need = int(lib.hstu_layer_workspace_bytes(ctypes.byref(d), ctypes.byref(cs)))
+    need = int(lib.hstu_mfalcon_workspace_bytes(ctypes.byref(d), ctypes.byref(hs), ctypes.byref(cs)))
     ws = _workspace(need, x_cand.device, workspace)
     st = lib.hstu_layer_fwd_mfalcon(ctypes.byref(d), ctypes.byref(wc), ctypes.byref(hs),
                                     _ptr(hist_uvqk), ctypes.byref(cs), _ptr(x_cand), _ptr(y_cand),
@@ -212,16 +221,16 @@ def hstu_attn_fwd(dims: LayerDims, seq: DeviceJagged, q: torch.Tensor, k: torch.
     _check(out, torch.float32, "out")
     d, s = dims.c(), seq.c()
     pref = None
-    keep = []
+    ps = None
     if prefix is not None:
         pseq, kp, vp, pstride = prefix
         for n, t in (("k_p", kp), ("v_p", vp)):
             if t.dtype != torch.float16 or not t.is_cuda:
                 raise TypeError(f"{n}: expected an fp16 device tensor")
         ps = pseq.c()
-        keep.append(ps)
         pref = _lib.Prefix(ctypes.pointer(ps), _ptr(kp), _ptr(vp), int(pstride))
-    need = int(lib.hstu_attn_workspace_bytes(ctypes.byref(d), ctypes.byref(s)))
+    need = int(lib.hstu_attn_workspace_bytes(ctypes.byref(d), ctypes.byref(s),
+                                             ctypes.byref(ps) if ps is not None else None))
     ws = _workspace(need, q.device, workspace)
     m = {"causal": _lib.MASK_CAUSAL, "self_only": _lib.MASK_SELF_ONLY}[mask]
     st = lib.hstu_attn_fwd(ctypes.byref(d), _ptr(rab_pos), _ptr(rab_time), ctypes.byref(s),

@@ -115,8 +115,15 @@ typedef struct {
  * 0 when the arguments are invalid.  Alignment: 256 bytes.                           */
 size_t hstu_layer_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_t *seq);
 
-/* Workspace (bytes) needed by hstu_attn_fwd (the jagged tile schedule only).          */
-size_t hstu_attn_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_t *seq);
+/* Workspace (bytes) needed by hstu_layer_fwd_mfalcon for this history and candidate
+ * micro-batch; 0 when the arguments are invalid.                                    */
+size_t hstu_mfalcon_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_t *hist,
+                                    const hstu_jagged_t *cand);
+
+/* Workspace (bytes) needed by hstu_attn_fwd (jagged tile schedule and key-block
+ * timestamp ranges); prefix_seq is the prefix batch or NULL.                        */
+size_t hstu_attn_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_t *seq,
+                                 const hstu_jagged_t *prefix_seq);
 
 /* One HSTU layer, equations (1)-(3), causal mask.
  *   x    (device) bf16 [T][d]                       input rows
@@ -138,7 +145,7 @@ hstu_status_t hstu_layer_fwd(const hstu_dims_t *dims, const hstu_weights_t *w,
  *   hist_uvqk (device) fp16 [T_hist][2H(dv+dqk)]
  *   x_cand    (device) bf16 [T_cand][d];   y_cand (device) bf16 [T_cand][d]
  *   uvqk_cand (device) fp16 [T_cand][2H(dv+dqk)]
- *   ws        >= hstu_layer_workspace_bytes(dims, cand)                              */
+ *   ws        >= hstu_mfalcon_workspace_bytes(dims, hist, cand)                      */
 hstu_status_t hstu_layer_fwd_mfalcon(const hstu_dims_t *dims, const hstu_weights_t *w,
                                      const hstu_jagged_t *hist, const uint16_t *hist_uvqk,
                                      const hstu_jagged_t *cand, const uint16_t *x_cand,
@@ -151,7 +158,7 @@ hstu_status_t hstu_layer_fwd_mfalcon(const hstu_dims_t *dims, const hstu_weights
  *           with dqk / dv)
  *   prefix  NULL or the keys preceding each sequence (required for SELF_ONLY)
  *   out     (device) fp32 [T][H*dv], every row written
- *   ws      >= hstu_attn_workspace_bytes(dims, seq)                                  */
+ *   ws      >= hstu_attn_workspace_bytes(dims, seq, prefix ? prefix->seq : NULL)     */
 hstu_status_t hstu_attn_fwd(const hstu_dims_t *dims, const float *rab_pos,
                             const float *rab_time, const hstu_jagged_t *seq,
                             const uint16_t *q, const uint16_t *k, const uint16_t *v,
@@ -173,7 +180,8 @@ int hstu_last_hip_error(void);
 /* Optional per-kernel timing with HIP events on the launch stream (off by default).
  * While enabled, every kernel the library launches is bracketed by two events; the
  * durations are collected by hstu_profile_collect, which synchronises the events.
- * Kernel ids: 0 schedule, 1 f1 GEMM, 2 attention, 3 norm-gate, 4 f2 GEMM.          */
+ * Kernel ids: 0 schedule and key-block timestamp ranges, 1 f1 GEMM, 2 attention,
+ * 3 norm-gate, 4 f2 GEMM.                                                           */
 void hstu_profile_enable(int on);
 void hstu_profile_reset(void);
 /* Adds up finished records: total_ms[k] and launches[k] for k in [0, 5).           */

@@ -104,8 +104,12 @@ def test_workspace_checks(lib):
     assert _call_layer(lib, d, ws=FAKE + 16) == _lib.HSTU_ERR_WORKSPACE  # not 256-aligned
     bad = _dims(dqk=48, dv=48)
     assert lib.hstu_layer_workspace_bytes(ctypes.byref(bad), ctypes.byref(s)) == 0
-    a = lib.hstu_attn_workspace_bytes(ctypes.byref(d), ctypes.byref(s))
+    a = lib.hstu_attn_workspace_bytes(ctypes.byref(d), ctypes.byref(s), None)
     assert 0 < a < need
+    ps = _seq(B=4, T=500, L=200)
+    assert lib.hstu_attn_workspace_bytes(ctypes.byref(d), ctypes.byref(s), ctypes.byref(ps)) >= a + 500 * 8
+    m = lib.hstu_mfalcon_workspace_bytes(ctypes.byref(d), ctypes.byref(ps), ctypes.byref(s))
+    assert m >= need + 500 * 8
 
 
 def test_empty_batch_is_a_no_op(lib):
