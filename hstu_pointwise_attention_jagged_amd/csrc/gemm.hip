@@ -2,10 +2,20 @@
 //   f1: UVQK = SiLU(X W1^T + b1)   (equation 1 of the layer), written as fp16
 //   f2: Y    = G W2^T + b2         (equation 3), written as bf16
 // Both are dense contractions, so they run on MFMA: v_mfma_f32_32x32x16_bf16 with fp32
-// accumulation.  Operands are "K-contiguous" (X rows and W rows), staged through LDS
-// with a register prefetch of the next K tile (double buffer).  The MFMA takes W as its
-// A operand and X as its B operand, so each lane ends with 4 consecutive output columns
-// of one token and stores them as one 8-byte bf16 write.
+// accumulation.  Operands are "K-contiguous" (X rows and W rows).  The MFMA takes W as
+// its A operand and X as its B operand, so each lane ends with 4 consecutive output
+// columns of one token and stores them as one 8-byte write.
+//
+// Two tilings:
+//  * gemm256_kernel (N a multiple of 256): a 256 x 256 output tile per workgroup of 8
+//    waves, each wave 64 tokens x 128 features (8 MFMA tiles, 6 operand reads per k-step).
+//    K slices of 64 arrive by direct-to-LDS buffer loads (no VGPR staging; rows past M
+//    read as zero) into two LDS stages, one stage ahead; 16-byte chunks are
+//    XOR-swizzled by row so the operand reads are bank-conflict free without padding.
+//    Operand fragments are double-buffered in registers across k-steps, and workgroup
+//    ids are remapped so each XCD works through a contiguous range of tiles.
+//  * gemm_kernel (any N multiple of 64): 128 x 128 (or 128 x 64) tiles with register
+//    prefetch, for the small shapes.
 #include "common.h"
 #include "kernels.h"
 
@@ -137,6 +147,181 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const uint16_t *__res
   }
 }
 
+// ---------------------------------------------------------------------------------
+// 256 x 256 tiles, direct-to-LDS staging
+// ---------------------------------------------------------------------------------
+constexpr int kBigTile = 256;
+constexpr int kBigThreads = 512;
+constexpr int kBigBK = 64;      // K per LDS stage
+constexpr int kBigStages = 2;   // ring of stages; loads run kBigStages - 1 stages ahead
+constexpr int kCPR = kBigBK / 8;  // 16-byte chunks per row
+constexpr uint32_t kRsrcWord3 = 0x00020000u;
+
+// LDS byte offset of 16-byte chunk c (0..7) of row r in a [rows][64] bf16 stage; the
+// chunk is XOR-swizzled by row pair so that 16 lanes reading one chunk of 16
+// consecutive rows hit distinct banks.
+__device__ __forceinline__ int swz(int r, int c) { return (r * kCPR + (c ^ ((r >> 1) & 7))) * 16; }
+
+// s_waitcnt vmcnt(n) (n <= 15), not waiting on the other counters.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((15 << 8) | (7 << 4) | N);
+}
+
+template <int ACT, int OUT>
+__global__ __launch_bounds__(kBigThreads, 2) void gemm256_kernel(const uint16_t *__restrict__ A,
+                                                                  const uint16_t *__restrict__ W,
+                                                                  const float *__restrict__ bias,
+                                                                  uint16_t *__restrict__ out, int M,
+                                                                  int N, int K, int n_tiles_n,
+                                                                  int n_tiles_total) {
+  constexpr int TM = 64, TN = 128;  // wave tile: tokens x features
+  constexpr int MT = TM / 32, NT = TN / 32;
+  constexpr int STAGE = kBigTile * kBigBK * 2;  // bytes of one operand stage (32 KB)
+  constexpr int SEGS = STAGE / 1024 / (kBigThreads / 64);  // 1 KB segments per wave
+  constexpr int LOADS = 2 * SEGS;                           // buffer loads per thread per stage
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  unsigned char *xs = smem;                       // [kBigStages][STAGE]
+  unsigned char *wsm = smem + kBigStages * STAGE;  // [kBigStages][STAGE]
+
+  // Workgroups are dealt to the 8 XCDs round-robin; give each XCD a contiguous range of
+  // tiles (feature tile fastest) so that the tiles sharing X rows share one L2.
+  const int nwg = gridDim.x;
+  const int per_xcd = (nwg + 7) / 8;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int lin = xcd * per_xcd + slot;
+  if (slot >= per_xcd || lin >= n_tiles_total) return;
+  const int tile_n = lin % n_tiles_n;
+  const int tile_m = lin / n_tiles_n;
+  const int m0 = tile_m * kBigTile, n0 = tile_n * kBigTile;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 3, wn = wave >> 2;  // 4 wave rows of tokens, 2 of features
+
+  const __amdgpu_buffer_rsrc_t ar =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(A), 0, (int)((int64_t)M * K * 2), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t wr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(W), 0, (int)((int64_t)N * K * 2), kRsrcWord3);
+
+  // Each wave instruction fills 1 KB of LDS = 8 rows x 8 chunks; lane -> (row, chunk)
+  // is fixed by the LDS position, the global chunk is the swizzled one.
+  const int lrow8 = lane / kCPR, lchunk = lane % kCPR;
+  auto issue = [&](int kt) {
+    const int stage = kt % kBigStages, k0 = kt * kBigBK;
+#pragma unroll
+    for (int j = 0; j < SEGS; ++j) {
+      const int seg = j * 8 + wave;          // 8-row segment of the 256-row tile
+      const int r = seg * (64 / kCPR) + lrow8;
+      const int c = lchunk ^ ((r >> 1) & 7);  // global chunk stored at lchunk
+      const int xoff = (int)(((int64_t)(m0 + r) * K + k0 + c * 8) * 2);
+      const int woff = (int)(((int64_t)(n0 + r) * K + k0 + c * 8) * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, xs + stage * STAGE + seg * 1024, 16, xoff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, wsm + stage * STAGE + seg * 1024, 16, woff, 0, 0, 0);
+    }
+  };
+
+  f32x16 acc[NT][MT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i)
+#pragma unroll
+    for (int j = 0; j < MT; ++j) acc[i][j] = f32x16{};
+
+  const int nk = K / kBigBK;
+  // prologue: stages 0 .. kBigStages-2 in flight
+#pragma unroll
+  for (int kt = 0; kt < kBigStages - 1; ++kt)
+    if (kt < nk) issue(kt);
+
+  const int lrow = lane & 31, lk = lane >> 5;
+  for (int kt = 0; kt < nk; ++kt) {
+    // stage kt has landed for this wave once at most (stages issued after it) remain
+    if constexpr (kBigStages == 2) {
+      wait_vmcnt<0>();
+    } else {
+      const int ahead = min(nk - 1 - kt, kBigStages - 2);
+      if (ahead >= 2) wait_vmcnt<2 * LOADS>();
+      else if (ahead == 1) wait_vmcnt<LOADS>();
+      else wait_vmcnt<0>();
+    }
+    // stage kt complete for all waves; stage kt-1 free for reuse.  A bare barrier: the
+    // wait above already covers this wave's direct-to-LDS loads of stage kt, and the
+    // later stages stay in flight.
+    __builtin_amdgcn_s_barrier();
+    if (kt + kBigStages - 1 < nk) issue(kt + kBigStages - 1);
+
+    const unsigned char *xst = xs + (kt % kBigStages) * STAGE;
+    const unsigned char *wst = wsm + (kt % kBigStages) * STAGE;
+    // operand fragments double-buffered in registers: k-step ks+1 is read while the
+    // MFMAs of k-step ks run
+    bf16x8 wf[2][NT], xf[2][MT];
+    auto read_frags = [&](int ks, int set) {
+      const int c = ks * 2 + lk;
+#pragma unroll
+      for (int i = 0; i < NT; ++i)
+        wf[set][i] = as_bf16x8(*reinterpret_cast<const u32x4 *>(wst + swz(wn * TN + i * 32 + lrow, c)));
+#pragma unroll
+      for (int j = 0; j < MT; ++j)
+        xf[set][j] = as_bf16x8(*reinterpret_cast<const u32x4 *>(xst + swz(wm * TM + j * 32 + lrow, c)));
+    };
+    read_frags(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < kBigBK / 16; ++ks) {
+      if (ks + 1 < kBigBK / 16) read_frags(ks + 1, (ks + 1) & 1);
+#pragma unroll
+      for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int j = 0; j < MT; ++j) acc[i][j] = mfma32(wf[ks & 1][i], xf[ks & 1][j], acc[i][j]);
+    }
+  }
+
+  // epilogue: lane holds token (lane % 32) and features 8g + 4*(lane/32) + 0..3
+#pragma unroll
+  for (int j = 0; j < MT; ++j) {
+    const int m = m0 + wm * TM + j * 32 + lrow;
+    if (m >= M) continue;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * TN + i * 32 + 8 * g + 4 * lk;
+        float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
+        float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+        if (bias != nullptr) {
+          const f32x4 bb = *reinterpret_cast<const f32x4 *>(bias + n);
+          v0 += bb[0]; v1 += bb[1]; v2 += bb[2]; v3 += bb[3];
+        }
+        if (ACT == ACT_SILU) {
+          v0 = silu_f32(v0); v1 = silu_f32(v1); v2 = silu_f32(v2); v3 = silu_f32(v3);
+        }
+        u32x2 pk = OUT == OUT_F16 ? u32x2{pack_f16_sat(v0, v1), pack_f16_sat(v2, v3)}
+                                  : u32x2{pack_bf16(v0, v1), pack_bf16(v2, v3)};
+        *reinterpret_cast<u32x2 *>(out + (int64_t)m * N + n) = pk;
+      }
+    }
+  }
+}
+
+template <int ACT, int OUT>
+hipError_t launch_big(const uint16_t *A, const uint16_t *W, const float *bias, uint16_t *out,
+                      int M, int N, int K, hipStream_t stream) {
+  const int tn = N / kBigTile;
+  const int tm = (M + kBigTile - 1) / kBigTile;
+  const int total = tm * tn;
+  const int grid = (total + 7) / 8 * 8;
+  const size_t lds = 2 * (size_t)kBigStages * kBigTile * kBigBK * 2;  // stages x 2 operands
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void *)gemm256_kernel<ACT, OUT>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  gemm256_kernel<ACT, OUT><<<dim3(grid), dim3(kBigThreads), lds, stream>>>(A, W, bias, out, M, N,
+                                                                           K, tn, total);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int ACT, int OUT>
 hipError_t launch_tile(const uint16_t *A, const uint16_t *W, const float *bias, uint16_t *out,
                        int M, int N, int K, hipStream_t stream) {
@@ -152,13 +337,18 @@ hipError_t launch_tile(const uint16_t *A, const uint16_t *W, const float *bias, 
 hipError_t launch_gemm(const uint16_t *A, const uint16_t *W, const float *bias, uint16_t *out,
                        int M, int N, int K, Act act, OutType out_type, hipStream_t stream) {
   if (M == 0) return hipSuccess;
+  const bool big = (N % kBigTile) == 0 && M >= kBigTile;
   const bool wide = (N % 128) == 0;
-  if (act == ACT_SILU && out_type == OUT_F16)
+  if (act == ACT_SILU && out_type == OUT_F16) {
+    if (big) return launch_big<ACT_SILU, OUT_F16>(A, W, bias, out, M, N, K, stream);
     return wide ? launch_tile<128, 128, ACT_SILU, OUT_F16>(A, W, bias, out, M, N, K, stream)
                 : launch_tile<128, 64, ACT_SILU, OUT_F16>(A, W, bias, out, M, N, K, stream);
-  if (act == ACT_NONE && out_type == OUT_BF16)
+  }
+  if (act == ACT_NONE && out_type == OUT_BF16) {
+    if (big) return launch_big<ACT_NONE, OUT_BF16>(A, W, bias, out, M, N, K, stream);
     return wide ? launch_tile<128, 128, ACT_NONE, OUT_BF16>(A, W, bias, out, M, N, K, stream)
                 : launch_tile<128, 64, ACT_NONE, OUT_BF16>(A, W, bias, out, M, N, K, stream);
+  }
   return hipErrorInvalidValue;
 }
 
