@@ -380,8 +380,15 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
     store_tile(0);
   }
   __syncthreads();
+  // Make the Q fragments complete on every path into the key loop.  Otherwise the
+  // wait-count pass sees the Q loads as possibly in flight at the loop header (the
+  // no-tile path skips the staging wait) and puts a full vector-memory drain inside
+  // the loop, which then also waits for each next tile's prefetch.  The empty asm
+  // only names the registers; it touches no memory.
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) asm("" : "+v"(qf[ks]));
 
-  const float pos_last = use_pos ? rab_pos[p.pos_buckets - 1] : 0.0f;
+  const float pos_last = use_pos ? ptab[p.pos_buckets - 1] : 0.0f;
   const int qmax = qbase + 31;
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
@@ -427,10 +434,13 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
       }
       if (use_time && kd != BIAS_GENERAL && lv) {
         const int2 st = kstat[k0];  // (min, max) timestamp of keys k0 .. k0+31
-        const int tb_lo = min(time_log2_bucket(qts_min, st.y), p.time_buckets - 1);
-        const int tb_hi = min(time_log2_bucket(qts_max, st.x), p.time_buckets - 1);
-        lo += rab_time[tb_lo];
-        hi += rab_time[tb_hi];
+        // wave-uniform bucket indices; the values come from the LDS copy of the table so
+        // that no vector-memory wait (which would also drain the next tile's prefetch)
+        // sits on this path
+        const int tb_lo = sgpr(min(time_log2_bucket(qts_min, st.y), p.time_buckets - 1));
+        const int tb_hi = sgpr(min(time_log2_bucket(qts_max, st.x), p.time_buckets - 1));
+        lo += ttab[tb_lo];
+        hi += ttab[tb_hi];
         if (tb_hi != tb_lo) {
           kd = tb_hi == tb_lo + 1 ? BIAS_TWO : BIAS_GENERAL;
           th = (uint32_t)(((uint64_t)1 << (tb_lo + 1)) - 1);
