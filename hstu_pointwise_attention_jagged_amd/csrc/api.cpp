@@ -355,6 +355,7 @@ hstu_status_t hstu_attn_fwd(const hstu_dims_t *dims, const float *rab_pos, const
     if (prefix->seq->total_tokens > 0 && (prefix->k == nullptr || prefix->v == nullptr))
       return HSTU_ERR_INVALID_ARG;
     if (prefix->row_stride < hq || prefix->row_stride % 8 != 0) return HSTU_ERR_INVALID_ARG;
+    if (prefix->row_stride != row_stride) return HSTU_ERR_UNSUPPORTED;  // one row pitch
     if (!aligned16(prefix->k) || !aligned16(prefix->v)) return HSTU_ERR_INVALID_ARG;
     if ((prefix->seq->timestamps == nullptr) != (seq->timestamps == nullptr))
       return HSTU_ERR_INVALID_ARG;

@@ -46,18 +46,9 @@ namespace {
 constexpr int kBN = kAttnBlockN;  // 64 keys per stage
 constexpr int kMaxPos = 1024;
 constexpr int kMaxTime = 64;
-constexpr int kVtPitch = kBN + 8;  // transposed V row pitch (fp16): 144 bytes
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
 
 enum BiasKind { BIAS_CONST = 0, BIAS_TWO = 1, BIAS_GENERAL = 2 };
-
-// Physical slot of key kk (0..63) inside a transposed V stage: within each group of 16
-// keys the order is [0-3, 8-11, 4-7, 12-15], which puts the 8 keys a lane multiplies in
-// one k-step next to each other.
-__device__ __forceinline__ int vt_slot(int kk) {
-  const int k = kk & 15;
-  return (kk & ~15) + ((k >> 2) & 1) * 8 + (k >> 3) * 4 + (k & 3);
-}
 
 // Buffer resource over `bytes` bytes at `base`: loads past the end return 0, so rows
 // beyond a sequence's last key are zero without any branch.
@@ -67,61 +58,135 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 
 __device__ __forceinline__ int sgpr(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// (gap >= thr) for gap = max(0, ts_q - ts_k) over the full int32 range, thr >= 1.
-__device__ __forceinline__ bool gap_at_least(int32_t ts_q, int32_t ts_k, uint32_t thr) {
-  return ts_q > ts_k && (uint32_t)ts_q - (uint32_t)ts_k >= thr;
+// Load of a value that no thread writes while the kernel runs, through the constant
+// address space: with a uniform address it becomes a scalar load.
+template <class T>
+__device__ __forceinline__ T ld_const(const T *ptr) {
+  return *(const __attribute__((address_space(4))) T *)ptr;
 }
+
+// ds_read_b64_tr_b16: transposing 8-byte LDS read (lane layout in the P.V step below)
+__device__ __forceinline__ u32x2 lds_read_tr16(const unsigned char *p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(
+      u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)p));
+}
+
+// For thr >= 1, (max(0, ts_q - ts_k) >= thr) holds exactly when ts_k < key_limit(ts_q,
+// thr) over the full int32 range: the difference is taken in 64 bits, and a limit below
+// INT32_MIN (no key passes) clamps to INT32_MIN, which no int32 is below.
+__device__ __forceinline__ int32_t key_limit(int32_t ts_q, uint32_t thr) {
+  const int64_t lim = (int64_t)ts_q - (int64_t)thr + 1;
+  return (int32_t)(lim < (int64_t)INT32_MIN ? (int64_t)INT32_MIN : lim);
+}
+
+// LDS tiles hold the CPR = DH / 8 chunks of 16 bytes of each key row, unpadded; chunk c
+// of row r sits at chunk position c ^ swz(r), with RPS = 16 / CPR rows per 256-byte bank
+// span:
+//  * K: swz = (r / RPS) % CPR.  A score k-step reads one chunk of 32 consecutive rows;
+//    any 16 of them then fall on 16 different 16-byte bank groups.
+//  * V: swz = 4 ((r / RPS) % (4 / RPS)) (none for DH = 32).  A transposing read takes 4
+//    consecutive rows x 4 chunks per half-wave, which then fall on disjoint bank groups.
+// A stage is filled by 1 KB direct-to-LDS buffer loads (lane l writes bytes [16 l, 16 l +
+// 16) of its KB); each lane loads the global chunk whose swizzled position that is.
+template <int DH>
+struct TileLayout {
+  static constexpr int CPR = DH / 8;
+  static constexpr int RPS = 16 / CPR;
+  static constexpr int ROW = DH * 2;             // bytes per key row
+  static constexpr int K_BYTES = kBN * ROW;
+  static constexpr int V_BYTES = kBN * ROW;
+  static constexpr int NI_K = K_BYTES / 1024;    // loads per K stage
+  static constexpr int NI_V = V_BYTES / 1024;
+  __device__ static int kswz(int r) { return (r / RPS) % CPR; }
+  __device__ static int vswz(int r) { return 4 * ((r / RPS) % (4 / RPS)); }
+};
+
+// Scalar description of one 32-key block as seen by one wave.
+struct BlockInfo {
+  bool live;      // some key of the block is visible to some query of the wave
+  bool masked;    // the mask must be applied per element
+  bool pre;       // the keys are prefix (history) rows
+  int kind;       // BiasKind
+  int k0;         // first key index within its segment
+  float lo, hi;   // bias values (CONST: lo; TWO: lo / hi)
+  uint32_t thr;   // TWO: gaps >= thr take hi
+};
 
 template <int DH, int MASK, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
-  constexpr int NT = 64 * NW;           // threads per workgroup
-  constexpr int BM = 32 * NW;           // query rows per workgroup
-  constexpr int KPITCH = DH + 8;        // K row pitch (fp16)
-  constexpr int KS = DH / 16;           // k-steps of the score MFMA
-  constexpr int FT = DH / 32;           // 32-wide feature tiles of the output
-  constexpr int K_UNITS = kBN * DH / 8;  // 16-byte chunks of a K stage
-  constexpr int K_ITERS = (K_UNITS + NT - 1) / NT;
-  // V is staged in units of KPU keys x 8 features: 2 keys when that spreads a stage over
-  // all threads of an 8-wave group, else 4
-  constexpr int KPU = (NW == 8 && (kBN / 2) * (DH / 8) <= NT) ? 2 : 4;
-  constexpr int V_GROUPS = kBN / KPU;
-  constexpr int V_UNITS = V_GROUPS * (DH / 8);
-  static_assert(V_UNITS <= NT, "one V unit per thread");
+  using L = TileLayout<DH>;
+  constexpr int NT = 64 * NW;          // threads per workgroup
+  constexpr int BM = 32 * NW;          // query rows per workgroup
+  constexpr int KS = DH / 16;          // k-steps of the score MFMA
+  constexpr int FT = DH / 32;          // 32-wide feature tiles of the output
+  // Loads of one batch: the K KBs of a tile and the V KBs of a tile, LPW per wave (load j
+  // of a wave is KB number wave + NW j, K first), and the tile's key timestamps (wave 0).
+  // A batch thus adds LPW to the vector-memory count of every wave but wave 0 (LPW + 1),
+  // and the barrier's count wait (sized for LPW) holds wave 0 slightly longer than needed.
+  constexpr int NL = L::NI_K + L::NI_V;
+  static_assert(NL % NW == 0, "whole loads per wave");
+  constexpr int LPW = NL / NW;
+  constexpr bool K_FIXED = L::NI_K % NW == 0;  // load j's kind is the same in every wave
+  // Stages per ring and how many tiles ahead the loads run: three stages (two tiles of
+  // lead) where LDS allows it, two for the 4-wave groups at DH = 128, which then fit two
+  // workgroups per CU.
+  constexpr int NS = (NW == 8 || DH <= 64) ? 3 : 2;
+  constexpr int LEAD = NS - 1;
 
-  __shared__ __attribute__((aligned(16))) uint16_t ks_lds[2][kBN * KPITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][DH * kVtPitch];
-  __shared__ __attribute__((aligned(16))) int32_t kts_lds[2][kBN];
+  // K and V stages, each its own LDS array: every access names its array at compile time
+  // (the tile loop is unrolled by NS), so the compiler can tell that a read of one stage
+  // does not alias the direct-to-LDS writes in flight to another and puts no
+  // vector-memory wait before it.  It tells apart only a few such destinations, so the
+  // tile's key timestamps ride at the end of its K stage (2 NS arrays in all).
+  constexpr int KT_BYTES = L::K_BYTES + kBN * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char k_st0[KT_BYTES], k_st1[KT_BYTES], k_st2[KT_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char v_st0[L::V_BYTES], v_st1[L::V_BYTES], v_st2[L::V_BYTES];
+  auto kbuf = [&](auto s_c) __attribute__((always_inline)) -> unsigned char * {
+    constexpr int S = decltype(s_c)::value;
+    if constexpr (S == 0) return k_st0;
+    else if constexpr (S == 1) return k_st1;
+    else return k_st2;
+  };
+  auto vbuf = [&](auto s_c) __attribute__((always_inline)) -> unsigned char * {
+    constexpr int S = decltype(s_c)::value;
+    if constexpr (S == 0) return v_st0;
+    else if constexpr (S == 1) return v_st1;
+    else return v_st2;
+  };
+  auto tbuf = [&](auto s_c) __attribute__((always_inline)) -> int32_t * {
+    return reinterpret_cast<int32_t *>(kbuf(s_c) + L::K_BYTES);
+  };
   __shared__ float ptab[kMaxPos];
   __shared__ float ttab[kMaxTime];
 
   const int item = blockIdx.x;
-  if (item >= *p.n_work) return;
+  if (item >= ld_const(p.n_work)) return;
   const int h = blockIdx.y;
-  const int b = p.work[2 * item], qt = p.work[2 * item + 1];
+  const int b = ld_const(p.work + 2 * item), qt = ld_const(p.work + 2 * item + 1);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = sgpr(tid >> 6);
   const int lrow = lane & 31, half = lane >> 5;
 
-  const int s0 = p.offsets[b];
-  const int n = p.offsets[b + 1] - s0;
+  const int s0 = ld_const(p.offsets + b);
+  const int n = ld_const(p.offsets + b + 1) - s0;
   const int q0 = qt * BM;
-  int p0 = 0, n_p = 0;
-  if (p.p_offsets != nullptr) {
-    p0 = p.p_offsets[b];
-    n_p = p.p_offsets[b + 1] - p0;
-  }
+  const bool has_prefix = p.p_offsets != nullptr;
+  const int p0 = has_prefix ? ld_const(p.p_offsets + b) : 0;
+  const int n_p = has_prefix ? ld_const(p.p_offsets + b + 1) - p0 : 0;
   const bool use_pos = p.rab_pos != nullptr;
   const bool use_time = p.rab_time != nullptr && p.ts != nullptr &&
                         (p.p_offsets == nullptr || p.p_ts != nullptr);
   const int rrow = p.rab_per_head ? h : 0;
-  const float *rab_pos = use_pos ? p.rab_pos + rrow * p.pos_buckets : nullptr;
-  const float *rab_time = use_time ? p.rab_time + rrow * p.time_buckets : nullptr;
 
-  // relative-bias tables of this head -> LDS (for the per-element path)
+  // relative-bias tables of this head -> LDS
   if (use_pos)
-    for (int i = tid; i < p.pos_buckets; i += NT) ptab[i] = rab_pos[i];
+    for (int i = tid; i < p.pos_buckets; i += NT) ptab[i] = p.rab_pos[rrow * p.pos_buckets + i];
   if (use_time)
-    for (int i = tid; i < p.time_buckets; i += NT) ttab[i] = rab_time[i];
+    for (int i = tid; i < p.time_buckets; i += NT) ttab[i] = p.rab_time[rrow * p.time_buckets + i];
+  __syncthreads();
+  // bias of every relative position past the last bucket
+  const float pos_last = use_pos ? __builtin_bit_cast(float, sgpr(__builtin_bit_cast(int, ptab[p.pos_buckets - 1]))) : 0.0f;
 
   // this wave's queries: local index qi, position, timestamp; Q fragments in registers
   const int qbase = q0 + wave * 32;  // wave-uniform
@@ -141,6 +206,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
     qts_max = sgpr(qts_max);
   }
   const int qpos_min = MASK == 0 ? n_p + qbase : n_p;
+  const int qmax = qbase + 31;
   f16x8 qf[KS];
   {
     const uint16_t *qrow = p.q + (int64_t)(s0 + qi) * p.stride + h * DH + half * 8;
@@ -150,6 +216,11 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
       qf[ks] = as_f16x8(v);
     }
   }
+  // Complete the Q loads here, on every path: otherwise the wait-count pass can see them
+  // as possibly in flight inside the key loop and drain all vector loads there, which
+  // would also wait for the tile prefetch.  The empty asm only names the registers.
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) asm("" : "+v"(qf[ks]));
 
   // key tiles: prefix tiles first, then own tiles
   const int n_pt = (n_p + kBN - 1) / kBN;
@@ -158,327 +229,338 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
   const int n_ot = (q_end - own_start + kBN - 1) / kBN;
   const int n_tiles = n_pt + n_ot;
 
-  // buffer resources of the two key segments (prefix rows, own rows)
-  const int64_t own_bytes = (int64_t)n * p.stride * 2;
-  const int64_t pre_bytes = (int64_t)n_p * p.p_stride * 2;
-  const __amdgpu_buffer_rsrc_t k_own = make_rsrc(p.k + (int64_t)s0 * p.stride, (uint32_t)own_bytes);
-  const __amdgpu_buffer_rsrc_t v_own = make_rsrc(p.v + (int64_t)s0 * p.stride, (uint32_t)own_bytes);
-  const __amdgpu_buffer_rsrc_t t_own = make_rsrc(use_time ? p.ts + s0 : p.offsets, use_time ? 4u * n : 0u);
-  __amdgpu_buffer_rsrc_t k_pre = k_own, v_pre = v_own, t_pre = t_own;
-  if (n_p > 0) {
-    k_pre = make_rsrc(p.pk + (int64_t)p0 * p.p_stride, (uint32_t)pre_bytes);
-    v_pre = make_rsrc(p.pv + (int64_t)p0 * p.p_stride, (uint32_t)pre_bytes);
-    t_pre = make_rsrc(use_time ? p.p_ts + p0 : p.offsets, use_time ? 4u * n_p : 0u);
-  }
+  // Byte offset, within the tile's rows of pitch rowb bytes, of the global chunk that this
+  // lane's element of load j (KB number id = w + NW j) brings to its swizzled position.
+  auto load_off = [&](int j, uint32_t rowb_, int w) __attribute__((always_inline)) {
+    const int id = w + NW * j;
+    const bool is_k = id < L::NI_K;
+    const int pos = (is_k ? id : id - L::NI_K) * 64 + lane;  // chunk position in the stage
+    const int r = pos / L::CPR;
+    const int c = (pos % L::CPR) ^ (is_k ? L::kswz(r) : L::vswz(r));
+    return r * (int)rowb_ + c * 16;
+  };
+  // The offsets stay in registers that are used for nothing else: the compiler treats the
+  // offset register of a direct-to-LDS load as busy until the load completes, so a copy
+  // that it later reused would stall on the load.  Prefix and own rows share one pitch
+  // (the entry point checks it).
+  const uint32_t rowb = (uint32_t)p.stride * 2;
+  int ld_off[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) ld_off[j] = load_off(j, rowb, wave);
+  const int ts_off = lane * 4;
 
-  // staging registers
-  u32x4 rk[K_ITERS];
-  u32x4 rv[KPU];
-  int32_t rts = 0;
-
-  // V unit of this thread: key group (fastest, so a transposed LDS write of a wave's
-  // lanes covers whole 128-byte rows) and feature chunk
-  const int v_kg = tid % V_GROUPS, v_fc = (tid / V_GROUPS) * 8;
-
-  auto load_tile = [&](int t) {
+  auto seg_of = [&](int t, int &kbase, int &limit) __attribute__((always_inline)) {
     const bool pre = t < n_pt;
-    const int kbase = pre ? t * kBN : own_start + (t - n_pt) * kBN;
-    const int64_t stride = pre ? p.p_stride : p.stride;
-    const __amdgpu_buffer_rsrc_t kr = pre ? k_pre : k_own;
-    const __amdgpu_buffer_rsrc_t vr = pre ? v_pre : v_own;
-#pragma unroll
-    for (int j = 0; j < K_ITERS; ++j) {
-      const int c = tid + j * NT;
-      if (K_UNITS % NT == 0 || c < K_UNITS) {
-        const int row = c / (DH / 8), col = (c % (DH / 8)) * 8;
-        const int off = (int)(((int64_t)(kbase + row) * stride + h * DH + col) * 2);
-        rk[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0));
-      }
-    }
-    if (V_UNITS == NT || tid < V_UNITS) {
-#pragma unroll
-      for (int r = 0; r < KPU; ++r) {
-        const int off = (int)(((int64_t)(kbase + v_kg * KPU + r) * stride + h * DH + v_fc) * 2);
-        rv[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0));
-      }
-    }
-    if (use_time && tid < kBN)
-      rts = __builtin_amdgcn_raw_buffer_load_b32(pre ? t_pre : t_own, (kbase + tid) * 4, 0, 0);
+    kbase = pre ? t * kBN : own_start + (t - n_pt) * kBN;
+    limit = n + (pre ? n_p - n : 0);  // arithmetic, not a select between the captured variables
+    return pre;
   };
 
-  auto store_tile = [&](int buf) {
+  // Buffer resource over the rows of tile t of K (or V) of this head, and over its key
+  // timestamps; rows past the segment end, and every row of a tile past the last, are
+  // outside the range and arrive as zeros.
+  auto tile_rsrc = [&](int t, const uint16_t *own, const uint16_t *pre_base) __attribute__((always_inline)) {
+    const bool valid = t >= 0 && t < n_tiles;
+    int kbase, limit;
+    const bool pre = seg_of(valid ? t : 0, kbase, limit);
+    const int64_t stride = p.stride;
+    const uint16_t *base = (pre ? pre_base + (int64_t)p0 * stride : own + (int64_t)s0 * stride) +
+                           (int64_t)kbase * stride + h * DH;
+    return make_rsrc(base, valid ? (uint32_t)(limit - kbase) * rowb : 0u);
+  };
+  // One batch: K rows and key timestamps of tile tk into K stage kstage_c, V rows of tile
+  // tv into V stage vstage_c.
+  auto issue_batch = [&](int tk, int tv, auto kstage_c, auto vstage_c) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(tk, p.k, p.pk);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(tv, p.v, p.pv);
 #pragma unroll
-    for (int j = 0; j < K_ITERS; ++j) {
-      const int c = tid + j * NT;
-      if (K_UNITS % NT == 0 || c < K_UNITS) {
-        const int row = c / (DH / 8), col = (c % (DH / 8)) * 8;
-        *reinterpret_cast<u32x4 *>(&ks_lds[buf][row * KPITCH + col]) = rk[j];
+    for (int j = 0; j < LPW; ++j) {
+      const int id = wave + NW * j;
+      const bool is_k = K_FIXED ? j < L::NI_K / NW : id < L::NI_K;
+      if (is_k) {
+        unsigned char *lds = kbuf(kstage_c) + id * 1024;
+        const int vo = ld_off[j];  // a local: an array element here loses the kernel's host stub
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, lds, 16, vo, 0, 0, 0);
+      } else {
+        unsigned char *lds = vbuf(vstage_c) + (id - L::NI_K) * 1024;
+        const int vo = ld_off[j];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, lds, 16, vo, 0, 0, 0);
       }
     }
-    if (V_UNITS == NT || tid < V_UNITS) {
-      const int slot = vt_slot(v_kg * KPU);
-      // transpose KPU keys x 8 features into 8 rows of KPU keys
-#pragma unroll
-      for (int f = 0; f < 8; ++f) {
-        const int w = f >> 1;
-        const bool hi = f & 1;
-        uint32_t e[KPU];
-#pragma unroll
-        for (int r = 0; r < KPU; ++r) e[r] = hi ? (rv[r][w] >> 16) : (rv[r][w] & 0xffffu);
-        if constexpr (KPU == 2) {
-          *reinterpret_cast<uint32_t *>(&vt_lds[buf][(v_fc + f) * kVtPitch + slot]) = e[0] | (e[1] << 16);
-        } else {
-          u32x2 pk = {e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
-          *reinterpret_cast<u32x2 *>(&vt_lds[buf][(v_fc + f) * kVtPitch + slot]) = pk;
-        }
+    if (wave == 0) {
+      int kbase = 0, limit = 0;
+      const bool pre = seg_of(tk < n_tiles ? tk : 0, kbase, limit);
+      const int32_t *tb = use_time ? (pre ? p.p_ts + p0 : p.ts + s0) + kbase : p.offsets;
+      const uint32_t bytes = use_time && tk < n_tiles ? (uint32_t)(limit - kbase) * 4u : 0u;
+      unsigned char *lds = reinterpret_cast<unsigned char *>(tbuf(kstage_c));
+      const __amdgpu_buffer_rsrc_t rt = make_rsrc(tb, bytes);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, lds, 4, ts_off, 0, 0, 0);
+    }
+  };
+
+  // (min, max) timestamps of the two 32-key blocks of tile t, as scalar loads.  They are
+  // issued at the end of the iteration before the one that classifies the tile, when no
+  // LDS read is in flight, so their latency passes under the barrier (whose LDS/scalar
+  // wait completes them) instead of stalling the classification.
+  auto block_ranges = [&](int t, uint64_t &r0, uint64_t &r1) __attribute__((always_inline)) {
+    r0 = r1 = 0;
+    if (!use_time || t < 0 || t >= n_tiles) return;
+    int kbase, limit;
+    const bool pre = seg_of(t, kbase, limit);
+    // a select of values, not of the two variables (which would keep them in memory)
+    const int2 *seg = pre ? p.p_kstat + p0 : p.kstat + s0;
+    const uint64_t *sb = reinterpret_cast<const uint64_t *>(seg + kbase);
+    r0 = ld_const(sb);
+    if (kbase + 32 < limit) r1 = ld_const(sb + 32);
+  };
+  // Scalar classification of block blk (0 / 1) of tile t for this wave, with the block's
+  // (min, max) key timestamp packed in rng.
+  auto classify = [&](int t, int blk, uint64_t rng) __attribute__((always_inline)) {
+    BlockInfo bi{false, false, false, BIAS_CONST, 0, 0.0f, 0.0f, 1u};
+    if (t < 0 || t >= n_tiles) return bi;
+    int kbase, limit;
+    const bool pre = seg_of(t, kbase, limit);
+    const int k0 = kbase + blk * 32;
+    bool lv = k0 < limit && wave_has_rows;
+    bool mk = false;
+    if (!pre) {
+      if (MASK == 0) {
+        lv = lv && k0 <= qmax;
+        mk = k0 + 31 > qbase;
+      } else {
+        lv = lv && k0 <= qmax && k0 + 31 >= qbase;
+        mk = true;
       }
     }
-    if (use_time && tid < kBN) kts_lds[buf][tid] = rts;
+    bi.live = lv;
+    bi.masked = mk;
+    bi.pre = pre;
+    bi.k0 = k0;
+    if (!lv) return bi;
+    int kd = BIAS_CONST;
+    float lo = 0.0f, hi = 0.0f;
+    uint32_t th = 1;
+    if (use_pos) {
+      const int kpos_max = pre ? k0 + 31 : (MASK == 0 ? n_p + k0 + 31 : n_p);
+      if (qpos_min - kpos_max >= p.pos_buckets - 1)
+        lo = hi = pos_last;
+      else
+        kd = BIAS_GENERAL;
+    }
+    if (use_time && kd != BIAS_GENERAL) {
+      const int2 st = {(int32_t)(uint32_t)rng, (int32_t)(uint32_t)(rng >> 32)};  // (min, max) ts
+      const int tb_lo = sgpr(min(time_log2_bucket(qts_min, st.y), p.time_buckets - 1));
+      const int tb_hi = sgpr(min(time_log2_bucket(qts_max, st.x), p.time_buckets - 1));
+      lo += ttab[tb_lo];
+      hi += ttab[tb_hi];
+      if (tb_hi != tb_lo) {
+        kd = tb_hi == tb_lo + 1 ? BIAS_TWO : BIAS_GENERAL;
+        th = (uint32_t)(((uint64_t)1 << (tb_lo + 1)) - 1);
+      }
+    }
+    bi.kind = kd;
+    bi.lo = __builtin_bit_cast(float, sgpr(__builtin_bit_cast(int, lo)));
+    bi.hi = __builtin_bit_cast(float, sgpr(__builtin_bit_cast(int, hi)));
+    bi.thr = th;
+    return bi;
   };
 
   f32x16 acc_o[FT];
 #pragma unroll
   for (int f = 0; f < FT; ++f) acc_o[f] = f32x16{};
 
-  int cur_buf = 0;
-
-  // One 32-key block of this wave: scores, bias, SiLU, mask, aggregation.  The
-  // compile-time kind picks the variant, so the common case carries no per-element
-  // index or mask code.
-  auto block = [&](int kb, int kbase, bool is_prefix, float bias_lo, float bias_hi, uint32_t thr,
-                   auto kind_c, auto masked_c) {
+  // ---- the three parts of a step ----
+  // Score accumulator init with the block's bias (CONST / TWO / GENERAL), from the key
+  // timestamps tsb of the K stage.  s^T lane layout: query lrow, keys 8 (i / 4) + 4 half + i % 4.
+  auto s_init = [&](f32x16 &s, const BlockInfo &bi, const int32_t *tsb, int blk, auto kind_c) __attribute__((always_inline)) {
     constexpr int KIND = decltype(kind_c)::value;
-    constexpr bool MASKED = decltype(masked_c)::value;
-    const int buf_ = cur_buf;
-    // S^T = K Q^T : lane holds query lrow, keys 8*(i/4) + 4*half + (i%4)
-    f32x16 s;
+    const int32_t *kts = tsb + blk * 32 + 4 * half;
+    if constexpr (KIND == BIAS_CONST) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = KIND == BIAS_GENERAL ? 0.0f : bias_lo;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const f16x8 kf = as_f16x8(*reinterpret_cast<const u32x4 *>(
-          &ks_lds[buf_][(kb * 32 + lrow) * KPITCH + ks * 16 + half * 8]));
-      s = mfma32_f16(kf, qf[ks], s);
-    }
-    if constexpr (KIND != BIAS_CONST) {
-      const float delta = bias_hi - bias_lo;
+      for (int i = 0; i < 16; ++i) s[i] = bi.lo;
+    } else if constexpr (KIND == BIAS_TWO) {
+      const int32_t klim = key_limit(qts, bi.thr);
+      const float hi = bi.hi, lo = bi.lo;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int kl = kb * 32 + 8 * g + 4 * half;  // first of 4 consecutive keys
+        const int4 t4 = *reinterpret_cast<const int4 *>(kts + 8 * g);
+        s[4 * g + 0] = t4.x < klim ? hi : lo;
+        s[4 * g + 1] = t4.y < klim ? hi : lo;
+        s[4 * g + 2] = t4.z < klim ? hi : lo;
+        s[4 * g + 3] = t4.w < klim ? hi : lo;
+      }
+    } else {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
         int4 t4 = {0, 0, 0, 0};
-        if (use_time) t4 = *reinterpret_cast<const int4 *>(&kts_lds[buf_][kl]);
+        if (use_time) t4 = *reinterpret_cast<const int4 *>(kts + 8 * g);
         const int32_t kt4[4] = {t4.x, t4.y, t4.z, t4.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int i = 4 * g + r;
-          if constexpr (KIND == BIAS_TWO) {
-            s[i] += gap_at_least(qts, kt4[r], thr) ? delta : 0.0f;
-          } else {
-            float x = s[i];
-            if (use_pos) {
-              const int kidx = kbase + kl + r;
-              const int kpos = is_prefix ? kidx : (MASK == 0 ? n_p + kidx : n_p);
-              x += ptab[min(max(qpos - kpos, 0), p.pos_buckets - 1)];
-            }
-            if (use_time) x += ttab[min(time_log2_bucket(qts, kt4[r]), p.time_buckets - 1)];
-            s[i] = x;
+          float x = 0.0f;
+          if (use_pos) {
+            const int kidx = bi.k0 + 8 * g + 4 * half + r;
+            const int kpos = bi.pre ? kidx : (MASK == 0 ? n_p + kidx : n_p);
+            x += ptab[min(max(qpos - kpos, 0), p.pos_buckets - 1)];
           }
+          if (use_time) x += ttab[min(time_log2_bucket(qts, kt4[r]), p.time_buckets - 1)];
+          s[4 * g + r] = x;
         }
       }
     }
-    float a[16];
+  };
+  // S^T += K Q^T over the block's 32 keys (K stage ks_buf).  Lane: row lrow of the block,
+  // logical chunk 2 ks + half at its swizzled position (the swizzle of row blk 32 + lrow
+  // is that of lrow).
+  int k_off[KS];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) a[i] = silu_f32(s[i]);
-    if constexpr (MASKED) {
+  for (int ks = 0; ks < KS; ++ks) k_off[ks] = lrow * L::ROW + (((2 * ks + half) ^ L::kswz(lrow)) * 16);
+  auto s_mma = [&](f32x16 &s, const unsigned char *ks_buf, int blk) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kidx = kbase + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-        const bool allowed = MASK == 0 ? (kidx <= qi) : (kidx == qi);
-        a[i] = allowed ? a[i] : 0.0f;
-      }
-    }
-    // P^T operand: k-step s2 takes values 8*s2 .. 8*s2+7
-    f16x8 pf[2];
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      u32x4 pk = {pack_f16(a[8 * s2 + 0], a[8 * s2 + 1]), pack_f16(a[8 * s2 + 2], a[8 * s2 + 3]),
-                  pack_f16(a[8 * s2 + 4], a[8 * s2 + 5]), pack_f16(a[8 * s2 + 6], a[8 * s2 + 7])};
-      pf[s2] = as_f16x8(pk);
-    }
-    // O^T += V^T P^T
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-      for (int f = 0; f < FT; ++f) {
-        const f16x8 vf = as_f16x8(*reinterpret_cast<const u32x4 *>(
-            &vt_lds[buf_][(f * 32 + lrow) * kVtPitch + kb * 32 + s2 * 16 + half * 8]));
-        acc_o[f] = mfma32_f16(vf, pf[s2], acc_o[f]);
-      }
+    for (int ks = 0; ks < KS; ++ks) {
+      const f16x8 kf = as_f16x8(*reinterpret_cast<const u32x4 *>(ks_buf + blk * 32 * L::ROW + k_off[ks]));
+      s = mfma32_f16(kf, qf[ks], s);
     }
   };
+  // A = SiLU(S) (masked), packed into the P^T operand: k-step s2 takes s[8 s2 .. 8 s2 + 7]
+  auto silu_half = [&](const f32x16 &s, f16x8 &pf, int s2, const BlockInfo &bi, auto masked_c) __attribute__((always_inline)) {
+    (void)bi;
+    (void)masked_c;
+    float a[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = silu_f32(s[8 * s2 + e]);
+    const u32x4 pk = {pack_f16(a[0], a[1]), pack_f16(a[2], a[3]), pack_f16(a[4], a[5]),
+                      pack_f16(a[6], a[7])};
+    pf = as_f16x8(pk);
+  };
+  // O^T += V^T P^T over the block's 32 keys (V stage vs_buf).  The V^T operand comes from
+  // row-major V through transposing reads: in each 16-lane group, lane 4 j + q names row
+  // (key) kb + j at features 4 q .. 4 q + 3 of its 16-feature slice, and lane i receives
+  // keys kb .. kb + 3 of feature i.  Two reads (keys +0 and +8) give the 8 keys of a
+  // lane's k-step in the order of the P^T operand: key 16 s2 + 8 (e / 4) + 4 half + e % 4.
+  // Lane's row 4 half + j (j = (lane % 16) / 4) of each 8-row group, logical chunk
+  // 4 f + 2 ((lane / 16) % 2) + (lane % 4) / 2 of feature tile f, at its swizzled position
+  // (the swizzle depends only on that row within the group), half (lane % 2) of the chunk.
+  int v_off[FT];
+  {
+    const int vr = (lane >> 5) * 4 + ((lane & 15) >> 2);
+#pragma unroll
+    for (int f = 0; f < FT; ++f)
+      v_off[f] = vr * L::ROW + (((4 * f + ((lane >> 4) & 1) * 2 + ((lane & 3) >> 1)) ^ L::vswz(vr)) * 16) +
+                 (lane & 1) * 8;
+  }
+  auto pv = [&](const f16x8 (&pf)[2], const unsigned char *vs_buf, int blk) __attribute__((always_inline)) {
+    const unsigned char *vb = vs_buf + blk * 32 * L::ROW;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int f = 0; f < FT; ++f) {
+        const u32x2 lo = lds_read_tr16(vb + (16 * s2) * L::ROW + v_off[f]);
+        const u32x2 hi = lds_read_tr16(vb + (16 * s2 + 8) * L::ROW + v_off[f]);
+        const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+        acc_o[f] = mfma32_f16(as_f16x8(w), pf[s2], acc_o[f]);
+      }
+  };
 
-  // Both 32-key blocks of a stage with a constant bias and no mask (the common case far
-  // from the diagonal), in one basic block: the score MFMAs of block B can overlap the
-  // SiLU of block A, and the P.V MFMAs of A the SiLU of B.
-  auto pair_const = [&](float bias_a, float bias_b) {
-    const int buf_ = cur_buf;
-    f32x16 sa, sb;
+  using KConst = std::integral_constant<int, BIAS_CONST>;
+  using KTwo = std::integral_constant<int, BIAS_TWO>;
+  using KGen = std::integral_constant<int, BIAS_GENERAL>;
+
+  // Scores of a block that must not contribute (masked elements; every element of a block
+  // outside the wave's range) are set to -1e30: SiLU then gives exactly zero (the exponent
+  // overflows to +inf, its reciprocal is 0, and -1e30 * 0 = -0).
+  auto mask_scores = [&](f32x16 &s, const BlockInfo &bi) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      sa[i] = bias_a;
-      sb[i] = bias_b;
+      const int kidx = bi.k0 + 8 * (i >> 2) + 4 * half + (i & 3);
+      const bool allowed = bi.live && (!bi.masked || (MASK == 0 ? kidx <= qi : kidx == qi));
+      s[i] = allowed ? s[i] : -1e30f;
     }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const f16x8 kf = as_f16x8(*reinterpret_cast<const u32x4 *>(
-          &ks_lds[buf_][lrow * KPITCH + ks * 16 + half * 8]));
-      sa = mfma32_f16(kf, qf[ks], sa);
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const f16x8 kf = as_f16x8(*reinterpret_cast<const u32x4 *>(
-          &ks_lds[buf_][(32 + lrow) * KPITCH + ks * 16 + half * 8]));
-      sb = mfma32_f16(kf, qf[ks], sb);
-    }
-    f16x8 pa[2], pb[2];
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      u32x4 pk;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        pk[j] = pack_f16(silu_f32(sa[8 * s2 + 2 * j]), silu_f32(sa[8 * s2 + 2 * j + 1]));
-      pa[s2] = as_f16x8(pk);
-    }
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      u32x4 pk;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        pk[j] = pack_f16(silu_f32(sb[8 * s2 + 2 * j]), silu_f32(sb[8 * s2 + 2 * j + 1]));
-      pb[s2] = as_f16x8(pk);
-    }
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int f = 0; f < FT; ++f) {
-        const f16x8 vf = as_f16x8(*reinterpret_cast<const u32x4 *>(
-            &vt_lds[buf_][(f * 32 + lrow) * kVtPitch + s2 * 16 + half * 8]));
-        acc_o[f] = mfma32_f16(vf, pa[s2], acc_o[f]);
-      }
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int f = 0; f < FT; ++f) {
-        const f16x8 vf = as_f16x8(*reinterpret_cast<const u32x4 *>(
-            &vt_lds[buf_][(f * 32 + lrow) * kVtPitch + 32 + s2 * 16 + half * 8]));
-        acc_o[f] = mfma32_f16(vf, pb[s2], acc_o[f]);
-      }
   };
 
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-  // Make the Q fragments complete on every path into the key loop.  Otherwise the
-  // wait-count pass sees the Q loads as possibly in flight at the loop header (the
-  // no-tile path skips the staging wait) and puts a full vector-memory drain inside
-  // the loop, which then also waits for each next tile's prefetch.  The empty asm
-  // only names the registers; it touches no memory.
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) asm("" : "+v"(qf[ks]));
-
-  const float pos_last = use_pos ? ptab[p.pos_buckets - 1] : 0.0f;
-  const int qmax = qbase + 31;
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    cur_buf = buf;
-    if (t + 1 < n_tiles) load_tile(t + 1);
-
-    const bool is_prefix = t < n_pt;
-    const int kbase = is_prefix ? t * kBN : own_start + (t - n_pt) * kBN;
-    const int limit = is_prefix ? n_p : n;
-    const int2 *kstat = is_prefix ? p.p_kstat + p0 : p.kstat + s0;
-
-    // classify both 32-key blocks with scalar arithmetic
-    bool live[2], masked[2];
-    int kind[2];
-    float blo[2], bhi[2];
-    uint32_t thr[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int k0 = kbase + kb * 32;
-      bool lv = k0 < limit && wave_has_rows;
-      bool mk = false;
-      if (!is_prefix) {
-        if (MASK == 0) {
-          lv = lv && k0 <= qmax;
-          mk = k0 + 31 > qbase;
-        } else {
-          lv = lv && k0 <= qmax && k0 + 31 >= qbase;
-          mk = true;
-        }
-      }
-      live[kb] = lv;
-      masked[kb] = mk;
-      int kd = BIAS_CONST;
-      float lo = 0.0f, hi = 0.0f;
-      uint32_t th = 1;
-      if (use_pos) {
-        const int kpos_max = is_prefix ? k0 + 31 : (MASK == 0 ? n_p + k0 + 31 : n_p);
-        if (qpos_min - kpos_max >= p.pos_buckets - 1) {
-          lo = hi = pos_last;
-        } else {
-          kd = BIAS_GENERAL;
-        }
-      }
-      if (use_time && kd != BIAS_GENERAL && lv) {
-        const int2 st = kstat[k0];  // (min, max) timestamp of keys k0 .. k0+31
-        // wave-uniform bucket indices; the values come from the LDS copy of the table so
-        // that no vector-memory wait (which would also drain the next tile's prefetch)
-        // sits on this path
-        const int tb_lo = sgpr(min(time_log2_bucket(qts_min, st.y), p.time_buckets - 1));
-        const int tb_hi = sgpr(min(time_log2_bucket(qts_max, st.x), p.time_buckets - 1));
-        lo += ttab[tb_lo];
-        hi += ttab[tb_hi];
-        if (tb_hi != tb_lo) {
-          kd = tb_hi == tb_lo + 1 ? BIAS_TWO : BIAS_GENERAL;
-          th = (uint32_t)(((uint64_t)1 << (tb_lo + 1)) - 1);
-        }
-      }
-      kind[kb] = kd;
-      blo[kb] = lo;
-      bhi[kb] = hi;
-      thr[kb] = th;
+  // One step of the block pipeline: S of block "next", SiLU of block "cur", P.V of block
+  // "prev".  The three parts are independent and always run as one straight-line basic
+  // block (a block outside the wave's range costs its MFMAs but adds exactly zero), so
+  // the compiler overlaps the SiLU arithmetic with the MFMAs and the output accumulators
+  // are updated in one place only.  Only the score initialisation branches on the bias
+  // kind, and a step with all three blocks outside the range only clears the cur block's P.
+  auto step = [&](f32x16 &s_next, const BlockInfo &bn, const unsigned char *kst, const int32_t *tst,
+                  int nblk, f32x16 &s_cur, f16x8 (&p_cur)[2], const BlockInfo &bc,
+                  const f16x8 (&p_prev)[2], const BlockInfo &bp, const unsigned char *vst, int pblk) __attribute__((always_inline)) {
+    if (!bn.live && !bc.live && !bp.live) {
+      // the cur block is outside the range too: a later step multiplies its P by V
+      p_cur[0] = f16x8{};
+      p_cur[1] = f16x8{};
+      return;
     }
-    if (live[0] && live[1] && kind[0] == BIAS_CONST && kind[1] == BIAS_CONST && !masked[0] &&
-        !masked[1]) {
-      pair_const(blo[0], blo[1]);
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if (!live[kb]) continue;
-        const float lo = blo[kb], hi = bhi[kb];
-        const uint32_t th = thr[kb];
-        if (!masked[kb]) {
-          if (kind[kb] == BIAS_CONST)
-            block(kb, kbase, is_prefix, lo, hi, th, std::integral_constant<int, BIAS_CONST>{}, std::false_type{});
-          else if (kind[kb] == BIAS_TWO)
-            block(kb, kbase, is_prefix, lo, hi, th, std::integral_constant<int, BIAS_TWO>{}, std::false_type{});
-          else
-            block(kb, kbase, is_prefix, lo, hi, th, std::integral_constant<int, BIAS_GENERAL>{}, std::false_type{});
-        } else {
-          if (kind[kb] == BIAS_CONST)
-            block(kb, kbase, is_prefix, lo, hi, th, std::integral_constant<int, BIAS_CONST>{}, std::true_type{});
-          else
-            block(kb, kbase, is_prefix, lo, hi, th, std::integral_constant<int, BIAS_GENERAL>{}, std::true_type{});
-        }
-      }
-    }
+    if (!bc.live || bc.masked) mask_scores(s_cur, bc);
+    if (bn.kind == BIAS_TWO)
+      s_init(s_next, bn, tst, nblk, KTwo{});
+    else if (bn.kind == BIAS_GENERAL)
+      s_init(s_next, bn, tst, nblk, KGen{});
+    else
+      s_init(s_next, bn, tst, nblk, KConst{});
+    s_mma(s_next, kst, nblk);
+    silu_half(s_cur, p_cur[0], 0, bc, std::false_type{});
+    pv(p_prev, vst, pblk);
+    silu_half(s_cur, p_cur[1], 1, bc, std::false_type{});
+  };
 
-    if (t + 1 < n_tiles) store_tile(buf ^ 1);
-    __syncthreads();
+  // Tile t's blocks are 2t (blk 0) and 2t + 1 (blk 1).  Iteration t runs steps 2t + 1 and
+  // 2t + 2, which read only K tile t + 1 and V tile t; the loads issued in iteration t
+  // (K of t + 2, V of t + 1) go to the stages that iteration t - 1 finished reading, and
+  // the barrier that opens iteration t + 1 waits for them.
+  f32x16 sc0 = {}, sc1 = {};        // scores of the even / odd block in flight
+  f16x8 pe[2] = {}, po[2] = {};     // P^T of the even / odd block
+  BlockInfo cur0{}, cur1{}, nxt0{}, nxt1{};
+  uint64_t rng0 = 0, rng1 = 0;  // block timestamp ranges of the tile classified next
+  // Batch b (issued in iteration b, or before the loop for b < -1) loads K of tile
+  // b + 1 + LEAD into K stage (b mod NS) and V of tile b + LEAD into V stage
+  // ((b - 1) mod NS): the stages that iteration b - 1 finished reading.  Iteration t
+  // reads K of tile t + 1 and V of tile t, which batch t - LEAD brought; its barrier
+  // waits for that batch and leaves the LEAD - 1 newer batches in flight.
+  auto batch = [&](int b, auto r_c) __attribute__((always_inline)) {  // r_c = b mod NS
+    constexpr int R = decltype(r_c)::value;
+    issue_batch(b + 1 + LEAD, b + LEAD, std::integral_constant<int, R>{},
+                std::integral_constant<int, (R + NS - 1) % NS>{});
+  };
+  auto iteration = [&](int t, auto r_c) __attribute__((always_inline)) {  // r_c = t mod NS
+    constexpr int R = decltype(r_c)::value;
+    constexpr int KR = (R + 1) % NS;
+    // wait for this wave's loads of batch t - LEAD and its LDS reads, then for every wave
+    __builtin_amdgcn_s_waitcnt(((LEAD - 1) * LPW) | (7 << 4));  // vmcnt(N) expcnt(7) lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    batch(t, r_c);
+    cur0 = nxt0;
+    cur1 = nxt1;
+    const unsigned char *kst = kbuf(std::integral_constant<int, KR>{});  // K, ts of tile t + 1
+    const int32_t *tst = tbuf(std::integral_constant<int, KR>{});
+    nxt0 = classify(t + 1, 0, rng0);
+    nxt1 = classify(t + 1, 1, rng1);
+    const unsigned char *vst = vbuf(r_c);                                 // V of tile t
+    step(sc0, nxt0, kst, tst, 0, sc1, po, cur1, pe, cur0, vst, 0);
+    step(sc1, nxt1, kst, tst, 1, sc0, pe, nxt0, po, cur1, vst, 1);
+    block_ranges(t + 2, rng0, rng1);
+  };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using CLast = std::integral_constant<int, NS - 1>;
+  block_ranges(0, rng0, rng1);
+  if constexpr (NS == 3) {
+    batch(-3, C0{});
+    batch(-2, C1{});
+  } else {
+    batch(-2, C0{});
   }
+  for (int t = -1; t < n_tiles; t += NS) {
+    iteration(t, CLast{});
+    if (t + 1 < n_tiles) iteration(t + 1, C0{});
+    if constexpr (NS == 3)
+      if (t + 2 < n_tiles) iteration(t + 2, C1{});
+  }
+  __builtin_amdgcn_s_waitcnt(7 << 4);  // drain the dummy batches before the stores
 
   // epilogue: lane holds query lrow, features 32f + 8g + 4*half + 0..3 -> fp32 rows
   if (q_ok) {
@@ -568,14 +650,16 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t *
   if (tid == 0) *n_work = total;
 }
 
+template <int DH, int MASK, int NW>
+hipError_t launch_one(const AttnArgs &a, int64_t cap, hipStream_t stream) {
+  const dim3 grid((unsigned)cap, (unsigned)a.num_heads);
+  attn_kernel<DH, MASK, NW><<<grid, dim3(64 * NW), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
 template <int DH, int NW>
 hipError_t launch_dh(const AttnArgs &a, int64_t cap, hipStream_t stream) {
-  const dim3 grid((unsigned)cap, (unsigned)a.num_heads);
-  if (a.mask == 0)
-    attn_kernel<DH, 0, NW><<<grid, dim3(64 * NW), 0, stream>>>(a);
-  else
-    attn_kernel<DH, 1, NW><<<grid, dim3(64 * NW), 0, stream>>>(a);
-  return hipGetLastError();
+  return a.mask == 0 ? launch_one<DH, 0, NW>(a, cap, stream) : launch_one<DH, 1, NW>(a, cap, stream);
 }
 
 }  // namespace

@@ -108,7 +108,8 @@ typedef struct {
   const hstu_jagged_t *seq;   /* same batch size as the query batch                   */
   const uint16_t *k;          /* (device) fp16, row r at k + r*row_stride               */
   const uint16_t *v;          /* (device) fp16, row r at v + r*row_stride               */
-  int64_t row_stride;         /* elements between consecutive rows                     */
+  int64_t row_stride;         /* elements between consecutive rows; must equal the     */
+                              /* candidates' row_stride (else HSTU_ERR_UNSUPPORTED)    */
 } hstu_prefix_t;
 
 /* Workspace (bytes) needed by hstu_layer_fwd / hstu_layer_fwd_mfalcon for this batch;

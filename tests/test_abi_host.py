@@ -132,6 +132,10 @@ def test_attn_and_mfalcon_argument_checks(lib):
     pref = _lib.Prefix(ctypes.pointer(ps), FAKE, FAKE, 256)
     assert lib.hstu_attn_fwd(ctypes.byref(d), None, None, ctypes.byref(s), FAKE, FAKE, FAKE, 256,
                              ctypes.byref(pref), 1, FAKE, FAKE, ws, None) == _lib.HSTU_ERR_INVALID_ARG
+    # prefix rows with a pitch of their own
+    pref = _lib.Prefix(ctypes.pointer(_seq()), FAKE, FAKE, 512)
+    assert lib.hstu_attn_fwd(ctypes.byref(d), None, None, ctypes.byref(s), FAKE, FAKE, FAKE, 256,
+                             ctypes.byref(pref), 1, FAKE, FAKE, ws, None) == _lib.HSTU_ERR_UNSUPPORTED
     w = _lib.Weights(FAKE, None, FAKE, None, None, None, None, None)
     h = _seq(B=3)
     assert lib.hstu_layer_fwd_mfalcon(ctypes.byref(d), ctypes.byref(w), ctypes.byref(h), FAKE,

@@ -82,7 +82,8 @@ def _attn_gpu(seq, q, k, v, H, dh, P, Tt, *, prefix=None, mask="causal", with_ti
     pref = None
     if prefix is not None:
         pseq, kp, vp = prefix
-        pbuf = dev.f16_tensor(np.concatenate([kp, vp], axis=1))
+        # prefix rows share the candidates' row pitch (3 H dh: K, V, unused)
+        pbuf = dev.f16_tensor(np.concatenate([kp, vp, np.zeros_like(kp)], axis=1))
         pref = (dev.jagged_of(pseq, with_time=with_time), pbuf[:, :hq], pbuf[:, hq:], pbuf.stride(0))
     out = ops.hstu_attn_fwd(dims, dev.jagged_of(seq, with_time=with_time), buf[:, :hq],
                             buf[:, hq:2 * hq], buf[:, 2 * hq:], row_stride=buf.stride(0),
