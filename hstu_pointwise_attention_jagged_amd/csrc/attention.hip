@@ -195,16 +195,16 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
   const bool wave_has_rows = qbase < n;
   const int qpos = MASK == 0 ? n_p + qi : n_p;
   const int32_t qts = use_time ? p.ts[s0 + (q_ok ? qi : n - 1)] : 0;
-  int32_t qts_min = q_ok ? qts : INT32_MAX, qts_max = q_ok ? qts : INT32_MIN;
+  // timestamp range of the wave's queries, wave-uniform on every path
+  int32_t qmn = q_ok ? qts : INT32_MAX, qmx = q_ok ? qts : INT32_MIN;
   if (use_time) {
 #pragma unroll
     for (int o = 1; o < 32; o <<= 1) {
-      qts_min = min(qts_min, __shfl_xor(qts_min, o, 64));
-      qts_max = max(qts_max, __shfl_xor(qts_max, o, 64));
+      qmn = min(qmn, __shfl_xor(qmn, o, 64));
+      qmx = max(qmx, __shfl_xor(qmx, o, 64));
     }
-    qts_min = sgpr(qts_min);
-    qts_max = sgpr(qts_max);
   }
+  const int32_t qts_min = sgpr(qmn), qts_max = sgpr(qmx);
   const int qpos_min = MASK == 0 ? n_p + qbase : n_p;
   const int qmax = qbase + 31;
   f16x8 qf[KS];
@@ -314,54 +314,42 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
     if (kbase + 32 < limit) r1 = ld_const(sb + 32);
   };
   // Scalar classification of block blk (0 / 1) of tile t for this wave, with the block's
-  // (min, max) key timestamp packed in rng.
+  // (min, max) key timestamp packed in rng.  Straight-line scalar code (no early exits):
+  // the time buckets come from scalar integer operations and the two bias values from
+  // scalar loads of the head's time table, so nothing passes through vector registers.
+  const float *ttab_g = use_time ? p.rab_time + rrow * p.time_buckets : p.rab_pos;
   auto classify = [&](int t, int blk, uint64_t rng) __attribute__((always_inline)) {
-    BlockInfo bi{false, false, false, BIAS_CONST, 0, 0.0f, 0.0f, 1u};
-    if (t < 0 || t >= n_tiles) return bi;
-    int kbase, limit;
-    const bool pre = seg_of(t, kbase, limit);
+    BlockInfo bi;
+    const bool valid = t >= 0 && t < n_tiles;
+    const int tt = valid ? t : 0;
+    const bool pre = tt < n_pt;
+    const int kbase = pre ? tt * kBN : own_start + (tt - n_pt) * kBN;
+    const int limit = n + (pre ? n_p - n : 0);
     const int k0 = kbase + blk * 32;
-    bool lv = k0 < limit && wave_has_rows;
+    bool lv = valid && k0 < limit && wave_has_rows;
     bool mk = false;
-    if (!pre) {
-      if (MASK == 0) {
-        lv = lv && k0 <= qmax;
-        mk = k0 + 31 > qbase;
-      } else {
-        lv = lv && k0 <= qmax && k0 + 31 >= qbase;
-        mk = true;
-      }
+    if (MASK == 0) {
+      lv = lv && (pre || k0 <= qmax);
+      mk = !pre && k0 + 31 > qbase;
+    } else {
+      lv = lv && (pre || (k0 <= qmax && k0 + 31 >= qbase));
+      mk = !pre;
     }
+    const int kpos_max = pre ? k0 + 31 : (MASK == 0 ? n_p + k0 + 31 : n_p);
+    const bool pos_general = use_pos && qpos_min - kpos_max < p.pos_buckets - 1;
+    const int32_t kmin = (int32_t)(uint32_t)rng, kmax = (int32_t)(uint32_t)(rng >> 32);
+    const int tb_lo = use_time ? min(time_log2_bucket(qts_min, kmax), p.time_buckets - 1) : 0;
+    const int tb_hi = use_time ? min(time_log2_bucket(qts_max, kmin), p.time_buckets - 1) : 0;
+    const float base = use_pos ? pos_last : 0.0f;
+    const uint32_t *tg = reinterpret_cast<const uint32_t *>(ttab_g);  // (integer loads stay scalar)
+    bi.lo = base + (use_time ? __builtin_bit_cast(float, ld_const(tg + tb_lo)) : 0.0f);
+    bi.hi = base + (use_time ? __builtin_bit_cast(float, ld_const(tg + tb_hi)) : 0.0f);
+    bi.kind = pos_general || tb_hi > tb_lo + 1 ? BIAS_GENERAL : (tb_hi == tb_lo ? BIAS_CONST : BIAS_TWO);
+    bi.thr = (uint32_t)(((uint64_t)1 << (tb_lo + 1)) - 1);
     bi.live = lv;
     bi.masked = mk;
     bi.pre = pre;
     bi.k0 = k0;
-    if (!lv) return bi;
-    int kd = BIAS_CONST;
-    float lo = 0.0f, hi = 0.0f;
-    uint32_t th = 1;
-    if (use_pos) {
-      const int kpos_max = pre ? k0 + 31 : (MASK == 0 ? n_p + k0 + 31 : n_p);
-      if (qpos_min - kpos_max >= p.pos_buckets - 1)
-        lo = hi = pos_last;
-      else
-        kd = BIAS_GENERAL;
-    }
-    if (use_time && kd != BIAS_GENERAL) {
-      const int2 st = {(int32_t)(uint32_t)rng, (int32_t)(uint32_t)(rng >> 32)};  // (min, max) ts
-      const int tb_lo = sgpr(min(time_log2_bucket(qts_min, st.y), p.time_buckets - 1));
-      const int tb_hi = sgpr(min(time_log2_bucket(qts_max, st.x), p.time_buckets - 1));
-      lo += ttab[tb_lo];
-      hi += ttab[tb_hi];
-      if (tb_hi != tb_lo) {
-        kd = tb_hi == tb_lo + 1 ? BIAS_TWO : BIAS_GENERAL;
-        th = (uint32_t)(((uint64_t)1 << (tb_lo + 1)) - 1);
-      }
-    }
-    bi.kind = kd;
-    bi.lo = __builtin_bit_cast(float, sgpr(__builtin_bit_cast(int, lo)));
-    bi.hi = __builtin_bit_cast(float, sgpr(__builtin_bit_cast(int, hi)));
-    bi.thr = th;
     return bi;
   };
 
@@ -664,7 +652,13 @@ hipError_t launch_dh(const AttnArgs &a, int64_t cap, hipStream_t stream) {
 
 }  // namespace
 
-int attn_block_m(int max_seq_len) { return max_seq_len >= 1024 ? 256 : 128; }
+// 128 query rows (4 waves) per workgroup at every length: two such workgroups share a CU,
+// and since their barriers are independent, one's wait overlaps the other's work (measured
+// faster than 8-wave groups at 8 x 8192 as well).
+int attn_block_m(int max_seq_len) {
+  (void)max_seq_len;
+  return 128;
+}
 
 hipError_t launch_schedule(const int32_t *offsets, const int32_t *p_offsets, int B, int mask,
                            int max_seq_len, int max_prefix_len, int32_t *work, int32_t *n_work,
@@ -687,11 +681,12 @@ hipError_t launch_block_stats(const int32_t *ts, const int32_t *offsets, int B, 
 hipError_t launch_attention(const AttnArgs &a, int dh, int max_seq_len, int64_t cap,
                             hipStream_t stream) {
   if (cap <= 0 || a.num_heads <= 0) return hipSuccess;
-  const bool wide = attn_block_m(max_seq_len) == 256;
+  static_assert(kAttnBlockMMin == 128, "4-wave workgroups");
+  (void)max_seq_len;
   switch (dh) {
-    case 32: return wide ? launch_dh<32, 8>(a, cap, stream) : launch_dh<32, 4>(a, cap, stream);
-    case 64: return wide ? launch_dh<64, 8>(a, cap, stream) : launch_dh<64, 4>(a, cap, stream);
-    case 128: return wide ? launch_dh<128, 8>(a, cap, stream) : launch_dh<128, 4>(a, cap, stream);
+    case 32: return launch_dh<32, 4>(a, cap, stream);
+    case 64: return launch_dh<64, 4>(a, cap, stream);
+    case 128: return launch_dh<128, 4>(a, cap, stream);
     default: return hipErrorInvalidValue;
   }
 }
