@@ -94,6 +94,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--layers", type=int, default=24)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run 4 device-to-device copies of this many bytes (counter "
+                         "calibration for HBM traffic) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); the jagged batch would "
@@ -110,6 +113,16 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_bytes:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE readings give the
+        # bytes-per-count scale of those counters
+        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {args.copy_bytes} bytes 4 times")
+        return
     log("building inputs (8 x 8192 tokens, d=1024, 8x128 heads)")
     w = wl.config(2)
     d = w.dims

@@ -170,10 +170,10 @@ LayerWs carve_layer(void *ws, const hstu_dims_t *d, const hstu_jagged_t *s,
 hipError_t launch_stats(const AttnArgs &aa, const hstu_jagged_t *s, const hstu_jagged_t *pre,
                         hipStream_t st) {
   if (aa.rab_time == nullptr || s->timestamps == nullptr) return hipSuccess;
-  hipError_t e = launch_block_stats(s->timestamps, s->seq_offsets, s->batch,
+  hipError_t e = launch_block_stats(s->timestamps, s->seq_offsets, s->batch, s->max_seq_len,
                                     const_cast<int2 *>(aa.kstat), st);
   if (e == hipSuccess && pre != nullptr && pre->timestamps != nullptr && pre->total_tokens > 0)
-    e = launch_block_stats(pre->timestamps, pre->seq_offsets, pre->batch,
+    e = launch_block_stats(pre->timestamps, pre->seq_offsets, pre->batch, pre->max_seq_len,
                            const_cast<int2 *>(aa.p_kstat), st);
   return e;
 }

@@ -563,81 +563,6 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
   }
 }
 
-// ------------------------------------------------------------------------------------
-// Timestamp range of every 32-key block: stat[t] = (min, max) of ts over keys
-// [t, min(t + 32, end of t's sequence)).  One workgroup per sequence.
-// ------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void block_stats_kernel(const int32_t *__restrict__ ts,
-                                                          const int32_t *__restrict__ offsets,
-                                                          int2 *__restrict__ stat) {
-  const int b = blockIdx.x;
-  const int s0 = offsets[b], s1 = offsets[b + 1];
-  for (int t = s0 + threadIdx.x; t < s1; t += blockDim.x) {
-    const int e = min(t + 32, s1);
-    int32_t mn = ts[t], mx = mn;
-    for (int j = t + 1; j < e; ++j) {
-      const int32_t v = ts[j];
-      mn = min(mn, v);
-      mx = max(mx, v);
-    }
-    stat[t] = int2{mn, mx};
-  }
-}
-
-// ------------------------------------------------------------------------------------
-// Jagged schedule: one workgroup builds the (sequence, q-tile) list, ordered by the
-// number of key tiles each item visits, largest first, with a counting sort.
-// ------------------------------------------------------------------------------------
-constexpr int kSchedThreads = 1024;
-constexpr int kSchedBins = 4096;
-
-__device__ __forceinline__ int item_cost(int n, int n_p, int t, int mask, int bm) {
-  const int q0 = t * bm;
-  const int q_end = min(n, q0 + bm);
-  const int own = mask == 0 ? q_end : q_end - q0;
-  return (n_p + kBN - 1) / kBN + (own + kBN - 1) / kBN;
-}
-
-__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t *offsets,
-                                                                 const int32_t *p_offsets,
-                                                                 int B, int mask, int bm,
-                                                                 int nbins, int32_t *work,
-                                                                 int32_t *n_work) {
-  __shared__ int bins[kSchedBins];
-  __shared__ int total;
-  const int tid = threadIdx.x;
-  for (int i = tid; i < nbins; i += kSchedThreads) bins[i] = 0;
-  __syncthreads();
-  for (int b = tid; b < B; b += kSchedThreads) {
-    const int n = offsets[b + 1] - offsets[b];
-    const int n_p = p_offsets ? p_offsets[b + 1] - p_offsets[b] : 0;
-    const int nq = (n + bm - 1) / bm;
-    for (int t = 0; t < nq; ++t) atomicAdd(&bins[min(item_cost(n, n_p, t, mask, bm), nbins - 1)], 1);
-  }
-  __syncthreads();
-  if (tid == 0) {  // exclusive scan, most expensive bin first
-    int run = 0;
-    for (int i = nbins - 1; i >= 0; --i) {
-      const int c = bins[i];
-      bins[i] = run;
-      run += c;
-    }
-    total = run;
-  }
-  __syncthreads();
-  for (int b = tid; b < B; b += kSchedThreads) {
-    const int n = offsets[b + 1] - offsets[b];
-    const int n_p = p_offsets ? p_offsets[b + 1] - p_offsets[b] : 0;
-    const int nq = (n + bm - 1) / bm;
-    for (int t = 0; t < nq; ++t) {
-      const int pos = atomicAdd(&bins[min(item_cost(n, n_p, t, mask, bm), nbins - 1)], 1);
-      work[2 * pos] = b;
-      work[2 * pos + 1] = t;
-    }
-  }
-  if (tid == 0) *n_work = total;
-}
-
 template <int DH, int MASK, int NW>
 hipError_t launch_one(const AttnArgs &a, int64_t cap, hipStream_t stream) {
   const dim3 grid((unsigned)cap, (unsigned)a.num_heads);
@@ -651,32 +576,6 @@ hipError_t launch_dh(const AttnArgs &a, int64_t cap, hipStream_t stream) {
 }
 
 }  // namespace
-
-// 128 query rows (4 waves) per workgroup at every length: two such workgroups share a CU,
-// and since their barriers are independent, one's wait overlaps the other's work (measured
-// faster than 8-wave groups at 8 x 8192 as well).
-int attn_block_m(int max_seq_len) {
-  (void)max_seq_len;
-  return 128;
-}
-
-hipError_t launch_schedule(const int32_t *offsets, const int32_t *p_offsets, int B, int mask,
-                           int max_seq_len, int max_prefix_len, int32_t *work, int32_t *n_work,
-                           hipStream_t stream) {
-  const int bm = attn_block_m(max_seq_len);
-  const int64_t max_cost = (int64_t)(max_prefix_len + kBN - 1) / kBN + (max_seq_len + kBN - 1) / kBN + 1;
-  const int nbins = (int)(max_cost < kSchedBins ? max_cost : kSchedBins);
-  schedule_kernel<<<1, kSchedThreads, 0, stream>>>(offsets, p_offsets, B, mask, bm, nbins, work,
-                                                   n_work);
-  return hipGetLastError();
-}
-
-hipError_t launch_block_stats(const int32_t *ts, const int32_t *offsets, int B, int2 *stat,
-                              hipStream_t stream) {
-  if (B <= 0) return hipSuccess;
-  block_stats_kernel<<<B, 256, 0, stream>>>(ts, offsets, stat);
-  return hipGetLastError();
-}
 
 hipError_t launch_attention(const AttnArgs &a, int dh, int max_seq_len, int64_t cap,
                             hipStream_t stream) {

@@ -30,7 +30,7 @@ struct AttnArgs {
   int pos_buckets, time_buckets, rab_per_head;
   float *out;               // [T][H*dv]
   int64_t out_stride;
-  const int2 *kstat;        // [T] (min, max) timestamp of keys t .. t+31 (own rows)
+  const int2 *kstat;        // [T] at each 32-key block start: (min, max) ts of the block
   const int2 *p_kstat;      // [T_p] same for prefix rows
   const int32_t *work;      // [2*cap] (b, q-tile) pairs, longest first
   const int32_t *n_work;    // [1]
@@ -57,9 +57,10 @@ hipError_t launch_schedule(const int32_t *offsets, const int32_t *p_offsets, int
 hipError_t launch_attention(const AttnArgs &a, int dh, int max_seq_len, int64_t cap,
                             hipStream_t stream);
 
-// stat[t] = (min, max) of ts over [t, min(t + 32, end of t's sequence)).
-hipError_t launch_block_stats(const int32_t *ts, const int32_t *offsets, int B, int2 *stat,
-                              hipStream_t stream);
+// For each sequence and each 32-key block j of it: stat[s0 + 32 j] = (min, max) of the
+// block's timestamps (other entries are not written).
+hipError_t launch_block_stats(const int32_t *ts, const int32_t *offsets, int B, int max_seq_len,
+                              int2 *stat, hipStream_t stream);
 
 // G[T][HDV] = LayerNorm(O) * gamma + beta, times U (fp16 row of uvqk), as bf16.
 hipError_t launch_norm_gate(const float *O, const uint16_t *U, int64_t u_stride,
