@@ -65,25 +65,66 @@ def traffic_record():
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, layers):
-    """fp64 oracle on one 8192-token sequence of the same batch, one layer."""
+def _counter_kib(db, kernel_substr):
+    """Per-dispatch counter values (KiB) of the kernels whose name contains kernel_substr."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    vals = [v for name, v in con.execute("select name, counter_value from pmc_events")
+            if kernel_substr in name]
+    con.close()
+    return vals
+
+
+def write_traffic_record(d, copy_bytes):
+    """HBM bytes per attention launch, from FETCH_SIZE / WRITE_SIZE scaled by a plain copy."""
+    att_fetch = _counter_kib(os.path.join(d, "pmc_fetch", "pmc_results.db"), "attn_kernel")
+    att_write = _counter_kib(os.path.join(d, "pmc_write", "pmc_results.db"), "attn_kernel")
+    cp_fetch = _counter_kib(os.path.join(d, "pmc_cfetch", "pmc_results.db"), "copyBuffer")
+    cp_write = _counter_kib(os.path.join(d, "pmc_cwrite", "pmc_results.db"), "copyBuffer")
+    fetch_scale = copy_bytes / (1024.0 * sum(cp_fetch) / len(cp_fetch))
+    write_scale = copy_bytes / (1024.0 * sum(cp_write) / len(cp_write))
+    fetch_b = 1024.0 * sum(att_fetch) / len(att_fetch) * fetch_scale
+    write_b = 1024.0 * sum(att_write) / len(att_write) * write_scale
+    rec = {
+        "kernel": "attn_kernel (8 x 8192 tokens, 8 heads x 128, causal, rab pos+time)",
+        "attention_hip_sha256": file_sha(ATTN_SRC),
+        "fetch_kib_per_launch": sum(att_fetch) / len(att_fetch),
+        "write_kib_per_launch": sum(att_write) / len(att_write),
+        "copy_bytes": copy_bytes,
+        "copy_fetch_kib": sum(cp_fetch) / len(cp_fetch),
+        "copy_write_kib": sum(cp_write) / len(cp_write),
+        "fetch_scale": fetch_scale,
+        "write_scale": write_scale,
+        "fetch_bytes_per_launch": fetch_b,
+        "write_bytes_per_launch": write_b,
+        "bytes_per_launch": fetch_b + write_b,
+    }
+    with open(TRAFFIC_RECORD, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    log(f"wrote {TRAFFIC_RECORD}: {rec['bytes_per_launch'] / 1e6:.1f} MB per launch")
+
+
+def cpu_baseline(w, layers, n_seq=2):
+    """fp64 oracle on the first n_seq 8192-token sequences of the same batch, one layer."""
     import numpy as np
     from oracle import hstu_ref
 
     d = w.dims
     cores = min(os.cpu_count() or 1, 16)
-    s0, s1 = int(w.seq.offsets[0]), int(w.seq.offsets[1])
+    s0, s1 = int(w.seq.offsets[0]), int(w.seq.offsets[n_seq])
     x = w.x[s0:s1]
-    off = np.array([0, s1 - s0], dtype=np.int32)
+    off = (w.seq.offsets[: n_seq + 1] - s0).astype(np.int32)
     ts = w.seq.timestamps[s0:s1]
     t0 = time.perf_counter()
     hstu_ref.layer_fwd(x, w.weights, off, ts, d.num_heads, d.dqk, d.dv, d.ln_eps, workers=cores)
     dt = time.perf_counter() - t0
-    f1, att, f2 = useful_flops([s1 - s0], d.d_model, d.num_heads, d.dqk, d.dv)
+    lengths = [int(n) for n in np.diff(off)]
+    f1, att, f2 = useful_flops(lengths, d.d_model, d.num_heads, d.dqk, d.dv)
     return {"value": round((f1 + att + f2) / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"one layer (not the {layers}-layer stack) on 1 of the 8 sequences "
-                      f"(8192 tokens), fp64 NumPy, {dt:.1f} s",
+            "sample": f"one layer (not the {layers}-layer stack) on {n_seq} of the 8 sequences "
+                      f"({sum(lengths)} tokens), fp64 NumPy, {dt:.1f} s",
             "seconds": round(dt, 3)}
 
 
@@ -97,7 +138,15 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run 4 device-to-device copies of this many bytes (counter "
                          "calibration for HBM traffic) and exit")
+    ap.add_argument("--traffic-record", metavar="DIR", default=None,
+                    help="only write profiles/attention_traffic.json from the rocprofv3 counter "
+                         "databases DIR/{pmc_fetch,pmc_write,pmc_cfetch,pmc_cwrite}/pmc_results.db "
+                         "(attention FETCH_SIZE / WRITE_SIZE, then the same counters over a "
+                         "--copy-bytes run) and exit")
     args = ap.parse_args()
+    if args.traffic_record:
+        write_traffic_record(args.traffic_record, args.copy_bytes or (1 << 30))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); the jagged batch would "
               "shard by sequence with no exchange across GPUs, which this build does not run.",
@@ -207,7 +256,7 @@ def main():
         "host": platform.node(),
     }
     if not args.no_cpu_baseline:
-        log("cpu baseline: fp64 oracle, one layer on one 8192-token sequence")
+        log("cpu baseline: fp64 oracle, one layer on two 8192-token sequences")
         out["cpu_baseline"] = cpu_baseline(w, args.layers)
     print(json.dumps(out), flush=True)
 
