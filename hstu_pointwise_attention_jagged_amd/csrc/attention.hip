@@ -398,16 +398,21 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
     }
   };
   // S^T += K Q^T over the block's 32 keys (K stage ks_buf).  Lane: row lrow of the block,
-  // logical chunk 2 ks + half at its swizzled position (the swizzle of row blk 32 + lrow
-  // is that of lrow).
-  int k_off[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) k_off[ks] = lrow * L::ROW + (((2 * ks + half) ^ L::kswz(lrow)) * 16);
+  // logical chunk 2 ks + half at its swizzled position; the swizzle of row blk 32 + lrow
+  // is that of lrow, and it only flips bits below the row pitch, so the address of k-step
+  // ks is k_base ^ (32 ks).  Fragments are read in groups of four ahead of their MFMAs.
+  const int k_base = lrow * L::ROW + ((half ^ L::kswz(lrow)) * 16);
   auto s_mma = [&](f32x16 &s, const unsigned char *ks_buf, int blk) __attribute__((always_inline)) {
+    const unsigned char *kb = ks_buf + blk * 32 * L::ROW;
+    constexpr int G = KS < 4 ? KS : 4;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const f16x8 kf = as_f16x8(*reinterpret_cast<const u32x4 *>(ks_buf + blk * 32 * L::ROW + k_off[ks]));
-      s = mfma32_f16(kf, qf[ks], s);
+    for (int g0 = 0; g0 < KS; g0 += G) {
+      f16x8 kf[G];
+#pragma unroll
+      for (int i = 0; i < G; ++i)
+        kf[i] = as_f16x8(*reinterpret_cast<const u32x4 *>(kb + (k_base ^ ((g0 + i) * 32))));
+#pragma unroll
+      for (int i = 0; i < G; ++i) s = mfma32_f16(kf[i], qf[g0 + i], s);
     }
   };
   // A = SiLU(S) (masked), packed into the P^T operand: k-step s2 takes s[8 s2 .. 8 s2 + 7]
@@ -426,28 +431,30 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
   // (key) kb + j at features 4 q .. 4 q + 3 of its 16-feature slice, and lane i receives
   // keys kb .. kb + 3 of feature i.  Two reads (keys +0 and +8) give the 8 keys of a
   // lane's k-step in the order of the P^T operand: key 16 s2 + 8 (e / 4) + 4 half + e % 4.
-  // Lane's row 4 half + j (j = (lane % 16) / 4) of each 8-row group, logical chunk
-  // 4 f + 2 ((lane / 16) % 2) + (lane % 4) / 2 of feature tile f, at its swizzled position
-  // (the swizzle depends only on that row within the group), half (lane % 2) of the chunk.
-  int v_off[FT];
+  // Lane: row 4 half + j (j = (lane % 16) / 4) of each 8-row group, logical chunk
+  // 4 f + 2 ((lane / 16) % 2) + (lane % 4) / 2 of feature tile f, half (lane % 2) of the
+  // chunk; the swizzle depends only on that row and flips bits below the row pitch, so the
+  // address for feature tile f is v_base ^ (64 f).
+  int v_base;
   {
     const int vr = (lane >> 5) * 4 + ((lane & 15) >> 2);
-#pragma unroll
-    for (int f = 0; f < FT; ++f)
-      v_off[f] = vr * L::ROW + (((4 * f + ((lane >> 4) & 1) * 2 + ((lane & 3) >> 1)) ^ L::vswz(vr)) * 16) +
-                 (lane & 1) * 8;
+    v_base = vr * L::ROW + (((((lane >> 4) & 1) * 2 + ((lane & 3) >> 1)) ^ L::vswz(vr)) * 16) +
+             (lane & 1) * 8;
   }
   auto pv = [&](const f16x8 (&pf)[2], const unsigned char *vs_buf, int blk) __attribute__((always_inline)) {
     const unsigned char *vb = vs_buf + blk * 32 * L::ROW;
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
+    for (int s2 = 0; s2 < 2; ++s2) {
+      u32x4 w[FT];
 #pragma unroll
       for (int f = 0; f < FT; ++f) {
-        const u32x2 lo = lds_read_tr16(vb + (16 * s2) * L::ROW + v_off[f]);
-        const u32x2 hi = lds_read_tr16(vb + (16 * s2 + 8) * L::ROW + v_off[f]);
-        const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-        acc_o[f] = mfma32_f16(as_f16x8(w), pf[s2], acc_o[f]);
+        const u32x2 lo = lds_read_tr16(vb + (16 * s2) * L::ROW + (v_base ^ (64 * f)));
+        const u32x2 hi = lds_read_tr16(vb + (16 * s2 + 8) * L::ROW + (v_base ^ (64 * f)));
+        w[f] = u32x4{lo[0], lo[1], hi[0], hi[1]};
       }
+#pragma unroll
+      for (int f = 0; f < FT; ++f) acc_o[f] = mfma32_f16(as_f16x8(w[f]), pf[s2], acc_o[f]);
+    }
   };
 
   using KConst = std::integral_constant<int, BIAS_CONST>;
