@@ -6,18 +6,25 @@
 // jagged batches computed at their true lengths (section "另外三块拼图", item 1).
 //
 // gfx950 design
-//  * One workgroup = 4 or 8 waves = 128 or 256 query rows of one (sequence, head); each
-//    wave owns 32 query rows whose Q fragments stay in registers for the whole key loop.
-//  * Keys stream through LDS in stages of 64 (double buffered, register prefetch through
-//    range-checked buffer loads, so keys past a sequence's end read as zero).  K is
-//    stored row-major; V is stored transposed (feature-major) with a key permutation
-//    inside each 16-key group, so the MFMA A operand of the P.V product is one 16-byte
-//    LDS read per lane.
+//  * One workgroup = 4 waves = 128 query rows of one (sequence, head), two workgroups per
+//    CU; each wave owns 32 query rows whose Q fragments stay in registers for the whole
+//    key loop.
+//  * Keys stream through LDS in tiles of 64 rows, loaded straight from HBM into LDS
+//    (buffer loads with the LDS destination, no register round trip) two tiles ahead of
+//    their use, into rings of two or three stages.  Rows past a segment's end are outside
+//    the buffer range and arrive as zeros.  K and V are stored row-major and unpadded,
+//    with 16-byte chunks XOR-swizzled by row so the fragment reads are conflict free.
 //  * Scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_f16), so that each
 //    lane's accumulator holds 16 keys of one query; after bias, SiLU and masking these
 //    16 values are exactly the lane's B operand (8 keys per k-step) of O^T += V^T P^T,
-//    with no trip through LDS.  Q, K, V and A are fp16 operands (the same MFMA rate as
-//    bf16 on gfx950, 3 more mantissa bits); accumulation and O stay fp32.
+//    with no trip through LDS.  The V^T operand comes from row-major V through the
+//    transposing LDS read (ds_read_b64_tr_b16).  Q, K, V and A are fp16 operands (the
+//    same MFMA rate as bf16 on gfx950, 3 more mantissa bits); accumulation and O stay
+//    fp32.  Scores are carried scaled by -log2(e) so SiLU costs exp2, add, reciprocal
+//    and multiply per element.
+//  * The key loop is a pipeline over 32-key blocks: each step computes the scores of
+//    block b+1, the weights of block b and the P.V product of block b-1 as one
+//    straight-line basic block, so the SiLU arithmetic overlaps the MFMAs.
 //  * The rab index math is integer only: relative position clamp, and the log2 time
 //    bucket from the bit length of (1 + gap).  Each wave classifies every 32-key block
 //    with scalar arithmetic, from its queries' position / timestamp range and the key
@@ -28,12 +35,10 @@
 //      - two buckets: positions as above, gaps spanning exactly buckets b and b+1; one
 //        integer compare per element picks between two constants;
 //      - general: per-element indices with table values from LDS.
-//  * Tiles are skipped from the jagged offsets and the mask: a wave never multiplies a
-//    32-key block that lies wholly after its queries (causal) or away from them
-//    (candidate self term); only blocks that straddle the diagonal are masked per
-//    element.  Masked pairs contribute exactly 0.
-//  * When both 32-key blocks of a stage take the constant-bias path, they run as one
-//    basic block so the compiler interleaves the MFMAs of one with the SiLU of the other.
+//  * Tiles are skipped from the jagged offsets and the mask: a workgroup never loads a
+//    tile that lies wholly after its queries (causal) or away from them (candidate self
+//    term), and a wave's blocks outside its own range add exactly zero.  Only blocks that
+//    straddle the diagonal are masked per element; masked pairs contribute exactly 0.
 #include <type_traits>
 
 #include "common.h"
@@ -46,6 +51,8 @@ namespace {
 constexpr int kBN = kAttnBlockN;  // 64 keys per stage
 constexpr int kMaxPos = 1024;
 constexpr int kMaxTime = 64;
+constexpr float kNegLog2e = -1.4426950408889634f;  // scores are carried as -log2(e) x
+constexpr float kNegLn2 = -0.6931471805599453f;     // undoes that scale on the output
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
 
 enum BiasKind { BIAS_CONST = 0, BIAS_TWO = 1, BIAS_GENERAL = 2 };
@@ -179,11 +186,17 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
                         (p.p_offsets == nullptr || p.p_ts != nullptr);
   const int rrow = p.rab_per_head ? h : 0;
 
-  // relative-bias tables of this head -> LDS
+  // Scores are carried scaled by -log2(e): t = -log2(e) (q.k + bias), so that
+  // SiLU(x) = x / (1 + e^-x) = -ln(2) t / (1 + 2^t).  Q and the bias tables are scaled
+  // once here, each score element costs exp2, add, reciprocal and multiply, and the
+  // factor -ln(2) is applied to the output accumulators once, at the end.
+  // relative-bias tables of this head, scaled -> LDS
   if (use_pos)
-    for (int i = tid; i < p.pos_buckets; i += NT) ptab[i] = p.rab_pos[rrow * p.pos_buckets + i];
+    for (int i = tid; i < p.pos_buckets; i += NT)
+      ptab[i] = kNegLog2e * p.rab_pos[rrow * p.pos_buckets + i];
   if (use_time)
-    for (int i = tid; i < p.time_buckets; i += NT) ttab[i] = p.rab_time[rrow * p.time_buckets + i];
+    for (int i = tid; i < p.time_buckets; i += NT)
+      ttab[i] = kNegLog2e * p.rab_time[rrow * p.time_buckets + i];
   __syncthreads();
   // bias of every relative position past the last bucket
   const float pos_last = use_pos ? __builtin_bit_cast(float, sgpr(__builtin_bit_cast(int, ptab[p.pos_buckets - 1]))) : 0.0f;
@@ -213,7 +226,13 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 v = q_ok ? *reinterpret_cast<const u32x4 *>(qrow + ks * 16) : u32x4{0, 0, 0, 0};
-      qf[ks] = as_f16x8(v);
+      const f16x8 raw = as_f16x8(v);
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = kNegLog2e * (float)raw[e];
+      const u32x4 sc = {pack_f16_sat(x[0], x[1]), pack_f16_sat(x[2], x[3]),
+                        pack_f16_sat(x[4], x[5]), pack_f16_sat(x[6], x[7])};
+      qf[ks] = as_f16x8(sc);
     }
   }
   // Complete the Q loads here, on every path: otherwise the wait-count pass can see them
@@ -342,8 +361,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
     const int tb_hi = use_time ? min(time_log2_bucket(qts_max, kmin), p.time_buckets - 1) : 0;
     const float base = use_pos ? pos_last : 0.0f;
     const uint32_t *tg = reinterpret_cast<const uint32_t *>(ttab_g);  // (integer loads stay scalar)
-    bi.lo = base + (use_time ? __builtin_bit_cast(float, ld_const(tg + tb_lo)) : 0.0f);
-    bi.hi = base + (use_time ? __builtin_bit_cast(float, ld_const(tg + tb_hi)) : 0.0f);
+    bi.lo = use_time ? fmaf(kNegLog2e, __builtin_bit_cast(float, ld_const(tg + tb_lo)), base) : base;
+    bi.hi = use_time ? fmaf(kNegLog2e, __builtin_bit_cast(float, ld_const(tg + tb_hi)), base) : base;
     bi.kind = pos_general || tb_hi > tb_lo + 1 ? BIAS_GENERAL : (tb_hi == tb_lo ? BIAS_CONST : BIAS_TWO);
     bi.thr = (uint32_t)(((uint64_t)1 << (tb_lo + 1)) - 1);
     bi.live = lv;
@@ -415,13 +434,17 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
       for (int i = 0; i < G; ++i) s = mfma32_f16(kf[i], qf[g0 + i], s);
     }
   };
-  // A = SiLU(S) (masked), packed into the P^T operand: k-step s2 takes s[8 s2 .. 8 s2 + 7]
+  // A / (-ln 2) = t / (1 + 2^t) of the scaled scores t (masked), packed into the P^T
+  // operand: k-step s2 takes s[8 s2 .. 8 s2 + 7]
   auto silu_half = [&](const f32x16 &s, f16x8 &pf, int s2, const BlockInfo &bi, auto masked_c) __attribute__((always_inline)) {
     (void)bi;
     (void)masked_c;
     float a[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) a[e] = silu_f32(s[8 * s2 + e]);
+    for (int e = 0; e < 8; ++e) {
+      const float t = s[8 * s2 + e];
+      a[e] = t * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
+    }
     const u32x4 pk = {pack_f16(a[0], a[1]), pack_f16(a[2], a[3]), pack_f16(a[4], a[5]),
                       pack_f16(a[6], a[7])};
     pf = as_f16x8(pk);
@@ -462,14 +485,15 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
   using KGen = std::integral_constant<int, BIAS_GENERAL>;
 
   // Scores of a block that must not contribute (masked elements; every element of a block
-  // outside the wave's range) are set to -1e30: SiLU then gives exactly zero (the exponent
-  // overflows to +inf, its reciprocal is 0, and -1e30 * 0 = -0).
+  // outside the wave's range) are set to +1e30, a very negative score in the scaled domain:
+  // the weight is then exactly zero (2^t overflows to +inf, its reciprocal is 0, and
+  // 1e30 * 0 = 0).
   auto mask_scores = [&](f32x16 &s, const BlockInfo &bi) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int kidx = bi.k0 + 8 * (i >> 2) + 4 * half + (i & 3);
       const bool allowed = bi.live && (!bi.masked || (MASK == 0 ? kidx <= qi : kidx == qi));
-      s[i] = allowed ? s[i] : -1e30f;
+      s[i] = allowed ? s[i] : 1e30f;
     }
   };
 
@@ -564,7 +588,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
     for (int f = 0; f < FT; ++f)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        f32x4 v = {acc_o[f][4 * g], acc_o[f][4 * g + 1], acc_o[f][4 * g + 2], acc_o[f][4 * g + 3]};
+        f32x4 v = {kNegLn2 * acc_o[f][4 * g], kNegLn2 * acc_o[f][4 * g + 1],
+                   kNegLn2 * acc_o[f][4 * g + 2], kNegLn2 * acc_o[f][4 * g + 3]};
         *reinterpret_cast<f32x4 *>(orow + f * 32 + g * 8) = v;
       }
   }

@@ -1,7 +1,10 @@
 """Rounding-point budget of the layer (CPU only).
 
 Emulates, in float64, where the GPU path rounds: the f1 output U|V|Q|K, the attention
-weights A before the P.V product, the norm-gate output G (the f2 operand) and Y.  It
+weights A before the P.V product, the norm-gate output G (the f2 operand) and Y.  The
+attention kernel carries scores scaled by -log2(e) (Q rounded once more after that
+scaling, weights t / (1 + 2^t) rounded, -ln 2 applied to the output), and the emulation
+takes the same steps.  It
 checks that the built precision (fp16 U|V|Q|K and A, bf16 G and Y) stays within the
 layer's tolerance with margin, and records that rounding U|V|Q|K and A to bf16 instead
 costs markedly more error -- the reason those operands are fp16.  Inputs are the seeded
@@ -29,7 +32,10 @@ def _ident(x):
     return x
 
 
-def _emulate(w, r_uvqk, r_a, r_g, r_y):
+L2E, LN2 = 1.4426950408889634, 0.6931471805599453
+
+
+def _emulate(w, r_uvqk, r_a, r_g, r_y, fold=False):
     d = w.dims
     H, dh = d.num_heads, d.dqk
     u, v, q, k = (r_uvqk(t) for t in ref.f1_split(w.x, w.weights.w1, None, H, dh, dh))
@@ -49,8 +55,14 @@ def _emulate(w, r_uvqk, r_a, r_g, r_y):
         mask = i[None, :] <= i[:, None]
         for h in range(H):
             c = slice(h * dh, (h + 1) * dh)
-            a = r_a(np.where(mask, ref.silu(q[s0:s1, c] @ k[s0:s1, c].T + bias), 0.0))
-            o[s0:s1, c] = a @ v[s0:s1, c]
+            if fold:
+                qs = r_uvqk(-L2E * q[s0:s1, c])
+                t = qs @ k[s0:s1, c].T - L2E * bias
+                a = r_a(np.where(mask, t / (1.0 + np.exp2(t)), 0.0))
+                o[s0:s1, c] = -LN2 * (a @ v[s0:s1, c])
+            else:
+                a = r_a(np.where(mask, ref.silu(q[s0:s1, c] @ k[s0:s1, c].T + bias), 0.0))
+                o[s0:s1, c] = a @ v[s0:s1, c]
     g = r_g(ref.norm_gate(o, u, None, None, d.ln_eps))
     return r_y(g @ w.weights.w2.T.astype(np.float64))
 
@@ -61,19 +73,21 @@ def case():
     exact = _emulate(w, _ident, _ident, _ident, _ident)
     want = ref.layer_fwd(w.x, w.weights, w.seq.offsets, w.seq.timestamps, 4, 64, 64)
     np.testing.assert_allclose(exact, want, rtol=1e-9, atol=1e-9)  # emulator == oracle
+    folded = _emulate(w, _ident, _ident, _ident, _ident, fold=True)
+    np.testing.assert_allclose(folded, want, rtol=1e-9, atol=1e-9)  # the scaling is exact
     return w, exact
 
 
 def test_built_precision_meets_tolerance_with_margin(case):
     w, exact = case
-    err = np.abs(_emulate(w, _f16, _f16, _bf16, _bf16) - exact)
+    err = np.abs(_emulate(w, _f16, _f16, _bf16, _bf16, fold=True) - exact)
     assert err.max() <= 0.8 * MAX_ABS
     assert err.mean() <= 0.7 * MEAN_ABS
 
 
 def test_bf16_attention_operands_cost_more(case):
     w, exact = case
-    built = np.abs(_emulate(w, _f16, _f16, _bf16, _bf16) - exact)
+    built = np.abs(_emulate(w, _f16, _f16, _bf16, _bf16, fold=True) - exact)
     all_bf16 = np.abs(_emulate(w, _bf16, _bf16, _bf16, _bf16) - exact)
     assert all_bf16.mean() > 1.4 * built.mean()
     assert all_bf16.max() > built.max()
