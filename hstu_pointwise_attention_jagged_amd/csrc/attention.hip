@@ -332,11 +332,14 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
     r0 = ld_const(sb);
     if (kbase + 32 < limit) r1 = ld_const(sb + 32);
   };
+  // The bias of a block on the constant or two-bucket path is pos_last plus one entry of
+  // the time table.  Lane i of tsum holds that sum for bucket i (at most 64 buckets), so
+  // the classification reads it with one v_readlane: no memory access in the key loop.
+  float tsum = pos_last;
+  if (use_time && lane < p.time_buckets) tsum += ttab[lane];
+  const int tsum_bits = __builtin_bit_cast(int, tsum);
   // Scalar classification of block blk (0 / 1) of tile t for this wave, with the block's
-  // (min, max) key timestamp packed in rng.  Straight-line scalar code (no early exits):
-  // the time buckets come from scalar integer operations and the two bias values from
-  // scalar loads of the head's time table, so nothing passes through vector registers.
-  const float *ttab_g = use_time ? p.rab_time + rrow * p.time_buckets : p.rab_pos;
+  // (min, max) key timestamp packed in rng.  Straight-line scalar code (no early exits).
   auto classify = [&](int t, int blk, uint64_t rng) __attribute__((always_inline)) {
     BlockInfo bi;
     const bool valid = t >= 0 && t < n_tiles;
@@ -359,10 +362,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
     const int32_t kmin = (int32_t)(uint32_t)rng, kmax = (int32_t)(uint32_t)(rng >> 32);
     const int tb_lo = use_time ? min(time_log2_bucket(qts_min, kmax), p.time_buckets - 1) : 0;
     const int tb_hi = use_time ? min(time_log2_bucket(qts_max, kmin), p.time_buckets - 1) : 0;
-    const float base = use_pos ? pos_last : 0.0f;
-    const uint32_t *tg = reinterpret_cast<const uint32_t *>(ttab_g);  // (integer loads stay scalar)
-    bi.lo = use_time ? fmaf(kNegLog2e, __builtin_bit_cast(float, ld_const(tg + tb_lo)), base) : base;
-    bi.hi = use_time ? fmaf(kNegLog2e, __builtin_bit_cast(float, ld_const(tg + tb_hi)), base) : base;
+    bi.lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(tsum_bits, tb_lo));
+    bi.hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(tsum_bits, tb_hi));
     bi.kind = pos_general || tb_hi > tb_lo + 1 ? BIAS_GENERAL : (tb_hi == tb_lo ? BIAS_CONST : BIAS_TWO);
     bi.thr = (uint32_t)(((uint64_t)1 << (tb_lo + 1)) - 1);
     bi.live = lv;
