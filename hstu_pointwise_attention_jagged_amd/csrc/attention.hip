@@ -275,23 +275,36 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
     return pre;
   };
 
-  // Buffer resource over the rows of tile t of K (or V) of this head, and over its key
-  // timestamps; rows past the segment end, and every row of a tile past the last, are
-  // outside the range and arrive as zeros.
-  auto tile_rsrc = [&](int t, const uint16_t *own, const uint16_t *pre_base) __attribute__((always_inline)) {
+  // Rows of this head in the two key segments: the prefix (history) rows of the sequence
+  // and its own rows.  A tile's loads take a descriptor whose range is its whole segment
+  // and reach the tile through the scalar offset, which the hardware range check includes:
+  // rows past the segment's end arrive as zeros, and a tile outside [0, n_tiles) gets an
+  // empty range.  Per tile this is a few scalar selects and one multiply.
+  const int64_t stride = p.stride;
+  const uint16_t *const k_own = p.k + (int64_t)s0 * stride + h * DH;
+  const uint16_t *const v_own = p.v + (int64_t)s0 * stride + h * DH;
+  const uint16_t *const k_pre = has_prefix ? p.pk + (int64_t)p0 * stride + h * DH : k_own;
+  const uint16_t *const v_pre = has_prefix ? p.pv + (int64_t)p0 * stride + h * DH : v_own;
+  const int32_t *const ts_own = use_time ? p.ts + s0 : p.offsets;
+  const int32_t *const ts_pre = use_time && has_prefix ? p.p_ts + p0 : ts_own;
+  // Segment (pre), first row (kbase) and row count of tile t; false if t is no tile.
+  auto tile_seg = [&](int t, bool &pre, int &kbase, int &rows) __attribute__((always_inline)) {
     const bool valid = t >= 0 && t < n_tiles;
-    int kbase, limit;
-    const bool pre = seg_of(valid ? t : 0, kbase, limit);
-    const int64_t stride = p.stride;
-    const uint16_t *base = (pre ? pre_base + (int64_t)p0 * stride : own + (int64_t)s0 * stride) +
-                           (int64_t)kbase * stride + h * DH;
-    return make_rsrc(base, valid ? (uint32_t)(limit - kbase) * rowb : 0u);
+    int limit;
+    pre = seg_of(valid ? t : 0, kbase, limit);
+    rows = valid ? limit : 0;
+    return valid;
   };
   // One batch: K rows and key timestamps of tile tk into K stage kstage_c, V rows of tile
   // tv into V stage vstage_c.
   auto issue_batch = [&](int tk, int tv, auto kstage_c, auto vstage_c) __attribute__((always_inline)) {
-    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(tk, p.k, p.pk);
-    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(tv, p.v, p.pv);
+    bool pk_, pv_;
+    int kb_k, kb_v, rows_k, rows_v;
+    tile_seg(tk, pk_, kb_k, rows_k);
+    tile_seg(tv, pv_, kb_v, rows_v);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(pk_ ? k_pre : k_own, (uint32_t)rows_k * rowb);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(pv_ ? v_pre : v_own, (uint32_t)rows_v * rowb);
+    const int so_k = kb_k * (int)rowb, so_v = kb_v * (int)rowb;
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
       const int id = wave + NW * j;
@@ -299,21 +312,19 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
       if (is_k) {
         unsigned char *lds = kbuf(kstage_c) + id * 1024;
         const int vo = ld_off[j];  // a local: an array element here loses the kernel's host stub
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, lds, 16, vo, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, lds, 16, vo, so_k, 0, 0);
       } else {
         unsigned char *lds = vbuf(vstage_c) + (id - L::NI_K) * 1024;
         const int vo = ld_off[j];
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, lds, 16, vo, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, lds, 16, vo, so_v, 0, 0);
       }
     }
     if (wave == 0) {
-      int kbase = 0, limit = 0;
-      const bool pre = seg_of(tk < n_tiles ? tk : 0, kbase, limit);
-      const int32_t *tb = use_time ? (pre ? p.p_ts + p0 : p.ts + s0) + kbase : p.offsets;
-      const uint32_t bytes = use_time && tk < n_tiles ? (uint32_t)(limit - kbase) * 4u : 0u;
+      const uint32_t bytes = use_time ? (uint32_t)rows_k * 4u : 0u;
+      const int so_t = kb_k * 4;
       unsigned char *lds = reinterpret_cast<unsigned char *>(tbuf(kstage_c));
-      const __amdgpu_buffer_rsrc_t rt = make_rsrc(tb, bytes);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, lds, 4, ts_off, 0, 0, 0);
+      const __amdgpu_buffer_rsrc_t rt = make_rsrc(pk_ ? ts_pre : ts_own, bytes);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, lds, 4, ts_off, so_t, 0, 0);
     }
   };
 
