@@ -109,15 +109,20 @@ struct TileLayout {
   __device__ static int vswz(int r) { return 4 * ((r / RPS) % (4 / RPS)); }
 };
 
-// Scalar description of one 32-key block as seen by one wave.
+// Scalar description of one 32-key block as seen by one wave, read from the wave's block
+// table (three words) plus the block's index.
 struct BlockInfo {
-  bool live;      // some key of the block is visible to some query of the wave
-  bool masked;    // the mask must be applied per element
-  bool pre;       // the keys are prefix (history) rows
-  int kind;       // BiasKind
-  int k0;         // first key index within its segment
+  uint32_t bits;  // bit 0 live: some key is visible to some query of the wave;
+                  // bit 1 masked: the mask applies per element; bit 2 prefix (history) rows;
+                  // bits 3-4 BiasKind; bits 5-10 the lower time bucket of the block
+  int g;          // block index in the wave's key sequence (prefix blocks first)
   float lo, hi;   // bias values (CONST: lo; TWO: lo / hi)
-  uint32_t thr;   // TWO: gaps >= thr take hi
+  __device__ bool live() const { return bits & 1u; }
+  __device__ bool masked() const { return bits & 2u; }
+  __device__ bool pre() const { return bits & 4u; }
+  __device__ int kind() const { return (int)((bits >> 3) & 3u); }
+  // TWO: keys whose gap reaches thr() (2^(lower bucket + 1) - 1) take hi
+  __device__ uint32_t thr() const { return (uint32_t)(((uint64_t)1 << (((bits >> 5) & 63u) + 1)) - 1); }
 };
 
 template <int DH, int MASK, int NW>
@@ -328,37 +333,30 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
     }
   };
 
-  // (min, max) timestamps of the two 32-key blocks of tile t, as scalar loads.  They are
-  // issued at the end of the iteration before the one that classifies the tile, when no
-  // LDS read is in flight, so their latency passes under the barrier (whose LDS/scalar
-  // wait completes them) instead of stalling the classification.
-  auto block_ranges = [&](int t, uint64_t &r0, uint64_t &r1) __attribute__((always_inline)) {
-    r0 = r1 = 0;
-    if (!use_time || t < 0 || t >= n_tiles) return;
-    int kbase, limit;
-    const bool pre = seg_of(t, kbase, limit);
-    // a select of values, not of the two variables (which would keep them in memory)
-    const int2 *seg = pre ? p.p_kstat + p0 : p.kstat + s0;
-    const uint64_t *sb = reinterpret_cast<const uint64_t *>(seg + kbase);
-    r0 = ld_const(sb);
-    if (kbase + 32 < limit) r1 = ld_const(sb + 32);
-  };
   // The bias of a block on the constant or two-bucket path is pos_last plus one entry of
-  // the time table.  Lane i of tsum holds that sum for bucket i (at most 64 buckets), so
-  // the classification reads it with one v_readlane: no memory access in the key loop.
+  // the time table: lane i of tsum holds that sum for bucket i (at most 64 buckets).
   float tsum = pos_last;
   if (use_time && lane < p.time_buckets) tsum += ttab[lane];
-  const int tsum_bits = __builtin_bit_cast(int, tsum);
-  // Scalar classification of block blk (0 / 1) of tile t for this wave, with the block's
-  // (min, max) key timestamp packed in rng.  Straight-line scalar code (no early exits).
-  auto classify = [&](int t, int blk, uint64_t rng) __attribute__((always_inline)) {
-    BlockInfo bi;
-    const bool valid = t >= 0 && t < n_tiles;
-    const int tt = valid ? t : 0;
-    const bool pre = tt < n_pt;
-    const int kbase = pre ? tt * kBN : own_start + (tt - n_pt) * kBN;
+  // Block table.  Block g of the wave's key sequence covers keys 32 (g mod 2) .. + 31 of
+  // tile g / 2.  Lane i of the table describes block cbase + i: every lane classifies its
+  // block in vector code, from the wave's query position / timestamp range and the
+  // block's key timestamp range (precomputed by block_stats_kernel), once per 64 blocks;
+  // the key loop then reads a block's entry with three v_readlane.  Classes:
+  //   - live: some key is visible to some query of the wave; masked: the mask applies per
+  //     element (the block straddles the diagonal, or the candidate self term);
+  //   - bias kind: CONST when every relative position is past the last position bucket and
+  //     the smallest and largest gap share one time bucket (the bucket being monotone in
+  //     the gap); TWO when the gaps span exactly buckets b and b + 1; GENERAL otherwise.
+  int tab_bits = 0, tab_lo = 0, tab_hi = 0;
+  int cbase = 0;
+  auto build_table = [&](int c0) __attribute__((always_inline)) {
+    const int g = c0 + lane;
+    const int t = g >> 1;
+    const bool valid = t < n_tiles;
+    const bool pre = t < n_pt;
+    const int kbase = pre ? t * kBN : own_start + (t - n_pt) * kBN;
     const int limit = n + (pre ? n_p - n : 0);
-    const int k0 = kbase + blk * 32;
+    const int k0 = kbase + (g & 1) * 32;
     bool lv = valid && k0 < limit && wave_has_rows;
     bool mk = false;
     if (MASK == 0) {
@@ -370,18 +368,32 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
     }
     const int kpos_max = pre ? k0 + 31 : (MASK == 0 ? n_p + k0 + 31 : n_p);
     const bool pos_general = use_pos && qpos_min - kpos_max < p.pos_buckets - 1;
-    const int32_t kmin = (int32_t)(uint32_t)rng, kmax = (int32_t)(uint32_t)(rng >> 32);
-    const int tb_lo = use_time ? min(time_log2_bucket(qts_min, kmax), p.time_buckets - 1) : 0;
-    const int tb_hi = use_time ? min(time_log2_bucket(qts_max, kmin), p.time_buckets - 1) : 0;
-    bi.lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(tsum_bits, tb_lo));
-    bi.hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(tsum_bits, tb_hi));
-    bi.kind = pos_general || tb_hi > tb_lo + 1 ? BIAS_GENERAL : (tb_hi == tb_lo ? BIAS_CONST : BIAS_TWO);
-    bi.thr = (uint32_t)(((uint64_t)1 << (tb_lo + 1)) - 1);
-    bi.live = lv;
-    bi.masked = mk;
-    bi.pre = pre;
-    bi.k0 = k0;
+    int tb_lo = 0, tb_hi = 0;
+    if (use_time) {
+      int2 r = {0, 0};
+      if (lv) r = pre ? p.p_kstat[p0 + k0] : p.kstat[s0 + k0];
+      tb_lo = min(time_log2_bucket(qts_min, r.y), p.time_buckets - 1);
+      tb_hi = min(time_log2_bucket(qts_max, r.x), p.time_buckets - 1);
+    }
+    const int kind = pos_general || tb_hi > tb_lo + 1 ? BIAS_GENERAL : (tb_hi == tb_lo ? BIAS_CONST : BIAS_TWO);
+    tab_bits = (lv ? 1 : 0) | (mk ? 2 : 0) | (pre ? 4 : 0) | (kind << 3) | (tb_lo << 5);
+    tab_lo = __builtin_bit_cast(int, __shfl(tsum, tb_lo, 64));
+    tab_hi = __builtin_bit_cast(int, __shfl(tsum, tb_hi, 64));
+    cbase = c0;
+  };
+  auto fetch = [&](int g) __attribute__((always_inline)) {
+    const int l = g - cbase;
+    BlockInfo bi;
+    bi.bits = (uint32_t)__builtin_amdgcn_readlane(tab_bits, l);
+    bi.lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(tab_lo, l));
+    bi.hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(tab_hi, l));
+    bi.g = g;
     return bi;
+  };
+  // first key index of a block within its segment
+  const int own_k0_shift = own_start - n_pt * kBN;
+  auto k0_of = [&](const BlockInfo &bi) __attribute__((always_inline)) {
+    return bi.g * 32 + (bi.pre() ? 0 : own_k0_shift);
   };
 
   f32x16 acc_o[FT];
@@ -398,7 +410,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = bi.lo;
     } else if constexpr (KIND == BIAS_TWO) {
-      const int32_t klim = key_limit(qts, bi.thr);
+      const int32_t klim = key_limit(qts, bi.thr());
       const float hi = bi.hi, lo = bi.lo;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -418,8 +430,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
         for (int r = 0; r < 4; ++r) {
           float x = 0.0f;
           if (use_pos) {
-            const int kidx = bi.k0 + 8 * g + 4 * half + r;
-            const int kpos = bi.pre ? kidx : (MASK == 0 ? n_p + kidx : n_p);
+            const int kidx = k0_of(bi) + 8 * g + 4 * half + r;
+            const int kpos = bi.pre() ? kidx : (MASK == 0 ? n_p + kidx : n_p);
             x += ptab[min(max(qpos - kpos, 0), p.pos_buckets - 1)];
           }
           if (use_time) x += ttab[min(time_log2_bucket(qts, kt4[r]), p.time_buckets - 1)];
@@ -503,8 +515,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
   auto mask_scores = [&](f32x16 &s, const BlockInfo &bi) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int kidx = bi.k0 + 8 * (i >> 2) + 4 * half + (i & 3);
-      const bool allowed = bi.live && (!bi.masked || (MASK == 0 ? kidx <= qi : kidx == qi));
+      const int kidx = k0_of(bi) + 8 * (i >> 2) + 4 * half + (i & 3);
+      const bool allowed = bi.live() && (!bi.masked() || (MASK == 0 ? kidx <= qi : kidx == qi));
       s[i] = allowed ? s[i] : 1e30f;
     }
   };
@@ -518,16 +530,16 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
   auto step = [&](f32x16 &s_next, const BlockInfo &bn, const unsigned char *kst, const int32_t *tst,
                   int nblk, f32x16 &s_cur, f16x8 (&p_cur)[2], const BlockInfo &bc,
                   const f16x8 (&p_prev)[2], const BlockInfo &bp, const unsigned char *vst, int pblk) __attribute__((always_inline)) {
-    if (!bn.live && !bc.live && !bp.live) {
+    if (!bn.live() && !bc.live() && !bp.live()) {
       // the cur block is outside the range too: a later step multiplies its P by V
       p_cur[0] = f16x8{};
       p_cur[1] = f16x8{};
       return;
     }
-    if (!bc.live || bc.masked) mask_scores(s_cur, bc);
-    if (bn.kind == BIAS_TWO)
+    if (!bc.live() || bc.masked()) mask_scores(s_cur, bc);
+    if (bn.kind() == BIAS_TWO)
       s_init(s_next, bn, tst, nblk, KTwo{});
-    else if (bn.kind == BIAS_GENERAL)
+    else if (bn.kind() == BIAS_GENERAL)
       s_init(s_next, bn, tst, nblk, KGen{});
     else
       s_init(s_next, bn, tst, nblk, KConst{});
@@ -544,7 +556,6 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
   f32x16 sc0 = {}, sc1 = {};        // scores of the even / odd block in flight
   f16x8 pe[2] = {}, po[2] = {};     // P^T of the even / odd block
   BlockInfo cur0{}, cur1{}, nxt0{}, nxt1{};
-  uint64_t rng0 = 0, rng1 = 0;  // block timestamp ranges of the tile classified next
   // Batch b (issued in iteration b, or before the loop for b < -1) loads K of tile
   // b + 1 + LEAD into K stage (b mod NS) and V of tile b + LEAD into V stage
   // ((b - 1) mod NS): the stages that iteration b - 1 finished reading.  Iteration t
@@ -563,22 +574,24 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    // next 64 blocks of the table, once every 32 tiles (before the batch, so that the
+    // wait for the timestamp ranges is not a wait for the batch)
+    if (2 * (t + 1) >= cbase + 64) build_table(cbase + 64);
     batch(t, r_c);
     cur0 = nxt0;
     cur1 = nxt1;
     const unsigned char *kst = kbuf(std::integral_constant<int, KR>{});  // K, ts of tile t + 1
     const int32_t *tst = tbuf(std::integral_constant<int, KR>{});
-    nxt0 = classify(t + 1, 0, rng0);
-    nxt1 = classify(t + 1, 1, rng1);
+    nxt0 = fetch(2 * t + 2);
+    nxt1 = fetch(2 * t + 3);
     const unsigned char *vst = vbuf(r_c);                                 // V of tile t
     step(sc0, nxt0, kst, tst, 0, sc1, po, cur1, pe, cur0, vst, 0);
     step(sc1, nxt1, kst, tst, 1, sc0, pe, nxt0, po, cur1, vst, 1);
-    block_ranges(t + 2, rng0, rng1);
   };
   using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;
   using CLast = std::integral_constant<int, NS - 1>;
-  block_ranges(0, rng0, rng1);
+  build_table(0);
   if constexpr (NS == 3) {
     batch(-3, C0{});
     batch(-2, C1{});
