@@ -245,6 +245,11 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
   // would also wait for the tile prefetch.  The empty asm only names the registers.
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) asm("" : "+v"(qf[ks]));
+  // A operand of one extra k-step that adds a per-block constant to every score: 1 at
+  // k = 0 for every key row (lanes 0-31 hold k = 0..7), 0 elsewhere.  Its B operand holds
+  // the constant (fp16) at k = 0, so a constant-bias block starts its score chain with
+  // one MFMA on a zero accumulator instead of 16 register moves per lane.
+  const f16x8 kf_one = as_f16x8(u32x4{half == 0 ? 0x3C00u : 0u, 0u, 0u, 0u});
 
   // key tiles: prefix tiles first, then own tiles
   const int n_pt = (n_p + kBN - 1) / kBN;
@@ -301,8 +306,13 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
     return valid;
   };
   // One batch: K rows and key timestamps of tile tk into K stage kstage_c, V rows of tile
-  // tv into V stage vstage_c.
-  auto issue_batch = [&](int tk, int tv, auto kstage_c, auto vstage_c) __attribute__((always_inline)) {
+  // tv into V stage vstage_c.  Part 0 issues the first half of the wave's loads (and the
+  // timestamps), part 1 the second half, part 2 all of them: the iteration issues the two
+  // halves at two points, so that the four waves of a workgroup do not queue all their
+  // loads on the CU's vector-memory path at the same moment.
+  auto issue_batch = [&](int tk, int tv, auto kstage_c, auto vstage_c, auto part_c) __attribute__((always_inline)) {
+    constexpr int PART = decltype(part_c)::value;
+    constexpr int J0 = PART == 1 ? LPW / 2 : 0, J1 = PART == 0 ? LPW / 2 : LPW;
     bool pk_, pv_;
     int kb_k, kb_v, rows_k, rows_v;
     tile_seg(tk, pk_, kb_k, rows_k);
@@ -311,7 +321,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(pv_ ? v_pre : v_own, (uint32_t)rows_v * rowb);
     const int so_k = kb_k * (int)rowb, so_v = kb_v * (int)rowb;
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) {
+    for (int j = J0; j < J1; ++j) {
       const int id = wave + NW * j;
       const bool is_k = K_FIXED ? j < L::NI_K / NW : id < L::NI_K;
       if (is_k) {
@@ -324,7 +334,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, lds, 16, vo, so_v, 0, 0);
       }
     }
-    if (wave == 0) {
+    if (PART != 1 && wave == 0) {
       const uint32_t bytes = use_time ? (uint32_t)rows_k * 4u : 0u;
       const int so_t = kb_k * 4;
       unsigned char *lds = reinterpret_cast<unsigned char *>(tbuf(kstage_c));
@@ -407,8 +417,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
     constexpr int KIND = decltype(kind_c)::value;
     const int32_t *kts = tsb + blk * 32 + 4 * half;
     if constexpr (KIND == BIAS_CONST) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = bi.lo;
+      const u32x4 qb = {pack_f16_sat(bi.lo, 0.0f), 0u, 0u, 0u};
+      s = mfma32_f16(kf_one, as_f16x8(qb), f32x16{});
     } else if constexpr (KIND == BIAS_TWO) {
       const int32_t klim = key_limit(qts, bi.thr());
       const float hi = bi.hi, lo = bi.lo;
@@ -561,10 +571,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
   // ((b - 1) mod NS): the stages that iteration b - 1 finished reading.  Iteration t
   // reads K of tile t + 1 and V of tile t, which batch t - LEAD brought; its barrier
   // waits for that batch and leaves the LEAD - 1 newer batches in flight.
-  auto batch = [&](int b, auto r_c) __attribute__((always_inline)) {  // r_c = b mod NS
+  auto batch = [&](int b, auto r_c, auto part_c) __attribute__((always_inline)) {  // r_c = b mod NS
     constexpr int R = decltype(r_c)::value;
     issue_batch(b + 1 + LEAD, b + LEAD, std::integral_constant<int, R>{},
-                std::integral_constant<int, (R + NS - 1) % NS>{});
+                std::integral_constant<int, (R + NS - 1) % NS>{}, part_c);
   };
   auto iteration = [&](int t, auto r_c) __attribute__((always_inline)) {  // r_c = t mod NS
     constexpr int R = decltype(r_c)::value;
@@ -577,7 +587,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
     // next 64 blocks of the table, once every 32 tiles (before the batch, so that the
     // wait for the timestamp ranges is not a wait for the batch)
     if (2 * (t + 1) >= cbase + 64) build_table(cbase + 64);
-    batch(t, r_c);
+    batch(t, r_c, std::integral_constant<int, 0>{});
     cur0 = nxt0;
     cur1 = nxt1;
     const unsigned char *kst = kbuf(std::integral_constant<int, KR>{});  // K, ts of tile t + 1
@@ -586,6 +596,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
     nxt1 = fetch(2 * t + 3);
     const unsigned char *vst = vbuf(r_c);                                 // V of tile t
     step(sc0, nxt0, kst, tst, 0, sc1, po, cur1, pe, cur0, vst, 0);
+    batch(t, r_c, std::integral_constant<int, 1>{});
     step(sc1, nxt1, kst, tst, 1, sc0, pe, nxt0, po, cur1, vst, 1);
   };
   using C0 = std::integral_constant<int, 0>;
@@ -593,10 +604,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
   using CLast = std::integral_constant<int, NS - 1>;
   build_table(0);
   if constexpr (NS == 3) {
-    batch(-3, C0{});
-    batch(-2, C1{});
+    batch(-3, C0{}, std::integral_constant<int, 2>{});
+    batch(-2, C1{}, std::integral_constant<int, 2>{});
   } else {
-    batch(-2, C0{});
+    batch(-2, C0{}, std::integral_constant<int, 2>{});
   }
   for (int t = -1; t < n_tiles; t += NS) {
     iteration(t, CLast{});

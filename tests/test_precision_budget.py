@@ -4,7 +4,8 @@ Emulates, in float64, where the GPU path rounds: the f1 output U|V|Q|K, the atte
 weights A before the P.V product, the norm-gate output G (the f2 operand) and Y.  The
 attention kernel carries scores scaled by -log2(e) (Q rounded once more after that
 scaling, weights t / (1 + 2^t) rounded, -ln 2 applied to the output), and the emulation
-takes the same steps.  It
+takes the same steps.  Blocks whose bias is one constant get it through an fp16 MFMA
+operand; the emulation rounds every scaled bias value to fp16 (an upper bound).  It
 checks that the built precision (fp16 U|V|Q|K and A, bf16 G and Y) stays within the
 layer's tolerance with margin, and records that rounding U|V|Q|K and A to bf16 instead
 costs markedly more error -- the reason those operands are fp16.  Inputs are the seeded
@@ -57,7 +58,7 @@ def _emulate(w, r_uvqk, r_a, r_g, r_y, fold=False):
             c = slice(h * dh, (h + 1) * dh)
             if fold:
                 qs = r_uvqk(-L2E * q[s0:s1, c])
-                t = qs @ k[s0:s1, c].T - L2E * bias
+                t = qs @ k[s0:s1, c].T + r_uvqk(-L2E * bias)
                 a = r_a(np.where(mask, t / (1.0 + np.exp2(t)), 0.0))
                 o[s0:s1, c] = -LN2 * (a @ v[s0:s1, c])
             else:
