@@ -10,7 +10,8 @@
 //  * gemm256_kernel (N a multiple of 256): a 256 x 256 output tile per workgroup of 8
 //    waves, each wave 64 tokens x 128 features (8 MFMA tiles, 6 operand reads per k-step).
 //    K slices of 64 arrive by direct-to-LDS buffer loads (no VGPR staging; rows past M
-//    read as zero) into two LDS stages, one stage ahead; 16-byte chunks are
+//    read as zero) into two LDS stages, one stage ahead, issued beside the MFMAs of the
+//    first half of the previous stage; 16-byte chunks are
 //    XOR-swizzled by row so the operand reads are bank-conflict free without padding.
 //    Operand fragments are double-buffered in registers across k-steps, and workgroup
 //    ids are remapped so each XCD works through a contiguous range of tiles.
@@ -207,18 +208,23 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm256_kernel(const uint16_t 
   // Each wave instruction fills 1 KB of LDS = 8 rows x 8 chunks; lane -> (row, chunk)
   // is fixed by the LDS position, the global chunk is the swizzled one.
   const int lrow8 = lane / kCPR, lchunk = lane % kCPR;
-  auto issue = [&](int kt) {
+  // load j of this wave for stage kt: X segment j (j < SEGS) or W segment j - SEGS
+  auto issue_one = [&](int kt, int j) {
     const int stage = kt % kBigStages, k0 = kt * kBigBK;
-#pragma unroll
-    for (int j = 0; j < SEGS; ++j) {
-      const int seg = j * 8 + wave;          // 8-row segment of the 256-row tile
-      const int r = seg * (64 / kCPR) + lrow8;
-      const int c = lchunk ^ ((r >> 1) & 7);  // global chunk stored at lchunk
+    const int seg = (j % SEGS) * 8 + wave;   // 8-row segment of the 256-row tile
+    const int r = seg * (64 / kCPR) + lrow8;
+    const int c = lchunk ^ ((r >> 1) & 7);  // global chunk stored at lchunk
+    if (j < SEGS) {
       const int xoff = (int)(((int64_t)(m0 + r) * K + k0 + c * 8) * 2);
-      const int woff = (int)(((int64_t)(n0 + r) * K + k0 + c * 8) * 2);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, xs + stage * STAGE + seg * 1024, 16, xoff, 0, 0, 0);
+    } else {
+      const int woff = (int)(((int64_t)(n0 + r) * K + k0 + c * 8) * 2);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, wsm + stage * STAGE + seg * 1024, 16, woff, 0, 0, 0);
     }
+  };
+  auto issue = [&](int kt) {
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) issue_one(kt, j);
   };
 
   f32x16 acc[NT][MT];
@@ -248,7 +254,7 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm256_kernel(const uint16_t 
     // wait above already covers this wave's direct-to-LDS loads of stage kt, and the
     // later stages stay in flight.
     __builtin_amdgcn_s_barrier();
-    if (kt + kBigStages - 1 < nk) issue(kt + kBigStages - 1);
+    const bool more = kt + kBigStages - 1 < nk;
 
     const unsigned char *xst = xs + (kt % kBigStages) * STAGE;
     const unsigned char *wst = wsm + (kt % kBigStages) * STAGE;
@@ -268,6 +274,13 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm256_kernel(const uint16_t 
 #pragma unroll
     for (int ks = 0; ks < kBigBK / 16; ++ks) {
       if (ks + 1 < kBigBK / 16) read_frags(ks + 1, (ks + 1) & 1);
+      // the next stage's loads go out beside the MFMAs of the first two k-steps (half
+      // each) rather than in one burst after the barrier, which stalled every wave of
+      // the workgroup on the CU's vector-memory queue at once
+      if (ks < 2 && more) {
+#pragma unroll
+        for (int j = ks * (LOADS / 2); j < (ks + 1) * (LOADS / 2); ++j) issue_one(kt + kBigStages - 1, j);
+      }
 #pragma unroll
       for (int i = 0; i < NT; ++i)
 #pragma unroll
