@@ -57,6 +57,10 @@ EXPORTS = {
     "hstu_attn_fwd": (c_int32, [ctypes.POINTER(Dims), c_void_p, c_void_p, ctypes.POINTER(Jagged),
                                 c_void_p, c_void_p, c_void_p, c_int64, ctypes.POINTER(Prefix),
                                 c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "hstu_sl_workspace_bytes": (c_size_t, [ctypes.POINTER(Jagged)]),
+    "hstu_stochastic_length": (c_int32, [ctypes.POINTER(Jagged), c_void_p, c_void_p, c_int32, c_double,
+                                         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int64,
+                                         c_void_p, c_size_t, c_void_p]),
     "hstu_validate_jagged": (c_int32, [ctypes.POINTER(Jagged), c_void_p]),
     "hstu_status_str": (ctypes.c_char_p, [c_int32]),
     "hstu_last_hip_error": (ctypes.c_int, []),

@@ -393,6 +393,44 @@ hstu_status_t hstu_attn_fwd(const hstu_dims_t *dims, const float *rab_pos, const
   return HSTU_OK;
 }
 
+size_t hstu_sl_workspace_bytes(const hstu_jagged_t *raw) {
+  if (check_seq(raw) != HSTU_OK) return 0;
+  return align_up((size_t)raw->batch * sizeof(int32_t) + 1);
+}
+
+hstu_status_t hstu_stochastic_length(const hstu_jagged_t *raw, const double *u_keep,
+                                     const uint32_t *keys, int32_t n_target, double alpha,
+                                     int32_t *kept, int32_t *new_offsets, int32_t *new_ts,
+                                     const uint16_t *x_raw, uint16_t *x_out, int64_t row_elems,
+                                     void *ws, size_t ws_bytes, void *stream) {
+  hstu_status_t st;
+  if ((st = check_seq(raw)) != HSTU_OK) return st;
+  if (n_target < 1 || !(alpha > 0.0) || !std::isfinite(alpha)) return HSTU_ERR_INVALID_ARG;
+  // L = floor(N^(alpha/2)); the whole-user threshold numerator N^alpha, both in fp64
+  const double l_real = std::floor(std::pow((double)n_target, alpha / 2.0));
+  const double thr_num = std::pow((double)n_target, alpha);
+  if (!(l_real >= 1.0) || l_real > 2147483647.0 || !std::isfinite(thr_num))
+    return HSTU_ERR_INVALID_ARG;
+  if (new_offsets == nullptr || (raw->batch > 0 && u_keep == nullptr)) return HSTU_ERR_INVALID_ARG;
+  if (raw->total_tokens > 0 && (keys == nullptr || kept == nullptr)) return HSTU_ERR_INVALID_ARG;
+  if (new_ts != nullptr && raw->timestamps == nullptr && raw->total_tokens > 0)
+    return HSTU_ERR_INVALID_ARG;
+  if ((x_raw == nullptr) != (x_out == nullptr)) return HSTU_ERR_INVALID_ARG;
+  if (x_raw != nullptr) {
+    if (row_elems <= 0 || row_elems % 8 != 0) return HSTU_ERR_INVALID_ARG;
+    if (!aligned16(x_raw) || !aligned16(x_out)) return HSTU_ERR_INVALID_ARG;
+    if ((const void *)x_raw == (const void *)x_out) return HSTU_ERR_INVALID_ARG;
+  }
+  // no users: only new_offsets[0] = 0 is written (by the lengths kernel), no workspace
+  if (raw->batch > 0 && (st = check_ws(ws, ws_bytes, hstu_sl_workspace_bytes(raw))) != HSTU_OK)
+    return st;
+  hipError_t e = launch_stochastic_length(raw->seq_offsets, u_keep, keys, raw->batch, (int)l_real,
+                                          thr_num, new_offsets, (int32_t *)ws, raw->timestamps,
+                                          kept, new_ts, x_raw, x_out, row_elems, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return HSTU_OK;
+}
+
 hstu_status_t hstu_validate_jagged(const hstu_jagged_t *seq, void *stream) {
   hstu_status_t st;
   if ((st = check_seq(seq)) != HSTU_OK) return st;

@@ -18,7 +18,8 @@ from . import _lib
 
 __all__ = ["HSTUError", "LayerDims", "DeviceWeights", "DeviceJagged", "hstu_layer_fwd",
            "hstu_layer_fwd_mfalcon", "hstu_attn_fwd", "hstu_layer_workspace_bytes",
-           "hstu_attn_workspace_bytes", "hstu_mfalcon_workspace_bytes", "hstu_validate_jagged", "profile_enable", "profile_reset",
+           "hstu_attn_workspace_bytes", "hstu_mfalcon_workspace_bytes", "hstu_validate_jagged",
+           "hstu_sl_workspace_bytes", "hstu_stochastic_length", "profile_enable", "profile_reset",
            "profile_collect"]
 
 
@@ -239,6 +240,52 @@ def hstu_attn_fwd(dims: LayerDims, seq: DeviceJagged, q: torch.Tensor, k: torch.
                            _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _raise(st, "hstu_attn_fwd")
     return out
+
+
+def hstu_sl_workspace_bytes(raw: DeviceJagged) -> int:
+    lib = _lib.load()
+    s = raw.c()
+    return int(lib.hstu_sl_workspace_bytes(ctypes.byref(s)))
+
+
+def hstu_stochastic_length(raw: DeviceJagged, u_keep: torch.Tensor, keys: torch.Tensor, *,
+                           n_target: int = 4096, alpha: float = 1.6,
+                           x: Optional[torch.Tensor] = None, gather_timestamps: bool = True,
+                           workspace: Optional[torch.Tensor] = None, stream=None):
+    """Stochastic Length over a raw batch (see include/hstu.h).
+
+    u_keep: float64 [B] uniform draws; keys: int32 [T_raw] holding the 32-bit priorities'
+    bit patterns (torch has no uint32 arithmetic dtype); x: optional 16-bit rows
+    [T_raw][d] to gather.  Returns (kept int32 [T_raw], new_offsets int32 [B+1],
+    new_ts int32 [T_raw] or None, x_out [T_raw][d] or None): the first new_offsets[B]
+    entries of kept / new_ts / x_out are the new batch, the rest is left unwritten.
+    """
+    lib = _lib.load()
+    _check(u_keep, torch.float64, "u_keep")
+    _check(keys, torch.int32, "keys")
+    dev = raw.offsets.device
+    T = raw.total_tokens
+    kept = torch.empty(max(T, 1), dtype=torch.int32, device=dev)
+    new_off = torch.empty(raw.batch + 1, dtype=torch.int32, device=dev)
+    new_ts = None
+    if gather_timestamps and raw.timestamps is not None:
+        new_ts = torch.empty(max(T, 1), dtype=torch.int32, device=dev)
+    x_out = None
+    row = 0
+    if x is not None:
+        if x.element_size() != 2 or not x.is_cuda or not x.is_contiguous() or x.dim() != 2:
+            raise TypeError("x: expected a contiguous 2-d 16-bit device tensor")
+        row = int(x.shape[1])
+        x_out = torch.empty((max(T, 1), row), dtype=x.dtype, device=dev)
+    s = raw.c()
+    need = int(lib.hstu_sl_workspace_bytes(ctypes.byref(s)))
+    ws = _workspace(need, dev, workspace)
+    st = lib.hstu_stochastic_length(ctypes.byref(s), _ptr(u_keep), _ptr(keys), int(n_target),
+                                    float(alpha), _ptr(kept), _ptr(new_off), _ptr(new_ts),
+                                    _ptr(x), _ptr(x_out), row, _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream))
+    _raise(st, "hstu_stochastic_length")
+    return kept, new_off, new_ts, x_out
 
 
 def hstu_validate_jagged(seq: DeviceJagged, stream=None) -> bool:

@@ -167,6 +167,39 @@ hstu_status_t hstu_attn_fwd(const hstu_dims_t *dims, const float *rab_pos,
                             hstu_mask_t mask, float *out, void *ws, size_t ws_bytes,
                             void *stream);
 
+/* Workspace (bytes) needed by hstu_stochastic_length for this raw batch (256-byte
+ * aligned); 0 when the batch description is invalid.                               */
+size_t hstu_sl_workspace_bytes(const hstu_jagged_t *raw);
+
+/* Stochastic Length (ltzyclt.github.io section 5.1; chenhuiyu.github.io section
+ * "另外三块拼图", item 2): subsamples each user's raw sequence before the layer.
+ * With L = floor(n_target^(alpha/2)) (fp64), user b of length n keeps all n tokens when
+ * n <= L or u_keep[b] < n_target^alpha / n^2 (fp64 compare); otherwise it keeps the L
+ * tokens whose (keys[t], position) pairs are smallest, in time order.  The random draws
+ * are inputs, so the result is a deterministic function of them.
+ *   raw          the raw batch (raw->timestamps may be NULL unless new_ts is given)
+ *   u_keep       (device) fp64 [B], uniform draws in [0, 1), one per user (may be
+ *                NULL when B == 0)
+ *   keys         (device) uint32 [T_raw], one priority per raw token
+ *   n_target     N >= 1 (4096 in the configs); alpha > 0 (1.6)
+ *   kept         (device) int32 [T_raw]: written with the raw indices of the kept tokens
+ *                in batch order, entries [0, new_offsets[B]); later entries untouched
+ *   new_offsets  (device) int32 [B+1], written (new_offsets[0] = 0)
+ *   new_ts       (device) int32 [T_raw] or NULL: timestamps of the kept tokens
+ *   x_raw, x_out (device) both NULL, or raw rows [T_raw][row_elems] and kept rows
+ *                [T_raw][row_elems] (16-bit values, copied bit for bit); row_elems a
+ *                multiple of 8, both 16-byte aligned, no aliasing
+ *   ws           >= hstu_sl_workspace_bytes(raw) (may be NULL when B == 0)
+ * The new batch's total token count is new_offsets[B] on the device; its longest
+ * sequence is at most max(L, raw->max_seq_len).  Invalid arguments (including N^alpha
+ * or L outside fp64 / int32 range, L < 1) return HSTU_ERR_INVALID_ARG before any
+ * launch.                                                                          */
+hstu_status_t hstu_stochastic_length(const hstu_jagged_t *raw, const double *u_keep,
+                                     const uint32_t *keys, int32_t n_target, double alpha,
+                                     int32_t *kept, int32_t *new_offsets, int32_t *new_ts,
+                                     const uint16_t *x_raw, uint16_t *x_out, int64_t row_elems,
+                                     void *ws, size_t ws_bytes, void *stream);
+
 /* Debug check of device offsets: off[0] == 0, non-decreasing, off[B] == total_tokens,
  * every length <= max_seq_len.  Synchronises the stream.  Returns HSTU_OK or
  * HSTU_ERR_INVALID_ARG.                                                              */

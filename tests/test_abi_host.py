@@ -149,3 +149,49 @@ def test_status_strings_and_kernel_names(lib):
     assert lib.hstu_status_str(99) == b"unknown status"
     assert [lib.hstu_kernel_name(i).decode() for i in range(5)] == list(_lib.KERNEL_IDS)
     assert lib.hstu_last_hip_error() == 0
+
+
+def _call_sl(lib, seq=None, u=FAKE, keys=FAKE, n_target=4096, alpha=1.6, kept=FAKE,
+             new_off=FAKE, new_ts=None, x=None, x_out=None, row=0, ws=FAKE, ws_bytes=1 << 20):
+    seq = seq or _seq(B=4, T=118, L=64)
+    return lib.hstu_stochastic_length(ctypes.byref(seq), u, keys, n_target, alpha, kept, new_off,
+                                      new_ts, x, x_out, row, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(new_off=None),
+    dict(u=None),                            # B = 4 users need their draws
+    dict(keys=None),
+    dict(kept=None),
+    dict(n_target=0),
+    dict(alpha=0.0),
+    dict(alpha=float("nan")),
+    dict(alpha=float("inf")),
+    dict(n_target=4096, alpha=1e6),          # N^alpha overflows fp64
+    dict(n_target=1, alpha=1.6),             # L = 1: allowed ... (checked below)
+    dict(x=FAKE, x_out=None, row=64),        # one of the two row pointers
+    dict(x=FAKE, x_out=FAKE + 4096, row=12),  # row width not a multiple of 8
+    dict(x=FAKE + 8, x_out=FAKE + 4096, row=64),  # misaligned rows
+    dict(x=FAKE, x_out=FAKE, row=64),        # aliasing rows
+])
+def test_sl_bad_arguments_rejected(lib, kw):
+    if kw.get("n_target") == 1 and kw.get("alpha") == 1.6:
+        # L = floor(1^0.8) = 1 is a valid subsample length: only the workspace check is
+        # left, and it fails for a null workspace
+        assert _call_sl(lib, ws=None, ws_bytes=0) == _lib.HSTU_ERR_WORKSPACE
+        return
+    assert _call_sl(lib, **kw) == _lib.HSTU_ERR_INVALID_ARG
+
+
+def test_sl_timestamps_needed_for_gather(lib):
+    seq = _lib.Jagged(4, 118, 64, FAKE, None)
+    assert _call_sl(lib, seq=seq, new_ts=FAKE) == _lib.HSTU_ERR_INVALID_ARG
+
+
+def test_sl_workspace_checked(lib):
+    seq = _seq(B=4, T=118, L=64)
+    need = lib.hstu_sl_workspace_bytes(ctypes.byref(seq))
+    assert need >= 4 * 4 and need % 256 == 0
+    assert _call_sl(lib, seq=seq, ws_bytes=need - 1) == _lib.HSTU_ERR_WORKSPACE
+    assert _call_sl(lib, seq=seq, ws=FAKE + 16) == _lib.HSTU_ERR_WORKSPACE
+    assert lib.hstu_sl_workspace_bytes(ctypes.byref(_lib.Jagged(-1, 0, 0, FAKE, None))) == 0

@@ -1,0 +1,166 @@
+"""GPU parity of Stochastic Length (hstu_stochastic_length) against the oracle's rule.
+
+The selection is integer work, so the bar is bit-exactness: the new offsets, the kept raw
+token indices, the gathered timestamps and the gathered feature rows must equal the
+oracle's (oracle/stochastic_length.py, the same rule applied to the same random draws).
+Cases: the raw batch of the 128-user stochastic-length workload (d = 512 rows gathered),
+small targets with zero-length and short users, heavy priority ties, users of exactly L
+and L + 1 tokens, draws placed exactly at and just below the keep threshold, users longer
+than one 1024-token tile, all users kept, and an empty batch.  The last test runs the
+layer on the batch the device built and checks it against the oracle's layer on the
+oracle's batch.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from hstu_pointwise_attention_jagged_amd import device as dev  # noqa: E402
+from hstu_pointwise_attention_jagged_amd import ops  # noqa: E402
+from hstu_pointwise_attention_jagged_amd import workloads as wl  # noqa: E402
+from oracle import hstu_ref as ref  # noqa: E402
+from oracle import stochastic_length as sl  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def _device_sl(seq, u, keys, n_target, alpha, x=None):
+    raw = dev.jagged_of(seq)
+    ut = torch.from_numpy(np.ascontiguousarray(u, dtype=np.float64)).cuda()
+    kt = torch.from_numpy(np.ascontiguousarray(keys, dtype=np.uint32).view(np.int32)).cuda()
+    xt = dev.bf16_tensor(x) if x is not None else None
+    kept, new_off, new_ts, x_out = ops.hstu_stochastic_length(raw, ut, kt, n_target=n_target,
+                                                              alpha=alpha, x=xt)
+    torch.cuda.synchronize()
+    return kept, new_off, new_ts, x_out, xt
+
+
+def _check(seq, u, keys, n_target=4096, alpha=1.6, x=None, tag=""):
+    say(f"[sl] {tag}: B={seq.batch} T={seq.total} N={n_target} alpha={alpha}")
+    kept, new_off, new_ts, x_out, xt = _device_sl(seq, u, keys, n_target, alpha, x)
+    want_kept, want_off = sl.select(seq.offsets, u, keys, n_target, alpha)
+    got_off = new_off.cpu().numpy()
+    np.testing.assert_array_equal(got_off, want_off)
+    T_new = int(want_off[-1])
+    say(f"     kept {T_new} of {seq.total}")
+    np.testing.assert_array_equal(kept.cpu().numpy()[:T_new], want_kept.astype(np.int32))
+    np.testing.assert_array_equal(new_ts.cpu().numpy()[:T_new], seq.timestamps[want_kept])
+    if x is not None:
+        got_rows = x_out[:T_new].view(torch.int16).cpu().numpy()
+        want_rows = xt.view(torch.int16).cpu().numpy()[want_kept]
+        np.testing.assert_array_equal(got_rows, want_rows)
+    return want_kept, want_off
+
+
+def test_sl_stochastic_length_workload_raw_batch():
+    w = wl.config(3)
+    r = w.raw
+    _check(r.seq, r.u_keep, r.keys, r.n_target, r.alpha, x=r.x, tag="128 users, d=512 rows")
+
+
+def test_sl_small_target_short_and_empty_users():
+    rng = np.random.default_rng(11)
+    lengths = rng.integers(0, 200, size=300)
+    lengths[[0, 7, 299]] = 0
+    seq = wl.jagged_from_lengths(rng, lengths)
+    u = rng.random(seq.batch)
+    keys = rng.integers(0, 2**32, size=seq.total, dtype=np.uint64).astype(np.uint32)
+    _check(seq, u, keys, n_target=64, alpha=1.6, tag="N=64 (L=27), lengths 0..199")
+
+
+def test_sl_priority_ties_break_by_position():
+    rng = np.random.default_rng(12)
+    seq = wl.jagged_from_lengths(rng, [300, 1000, 2500, 64])
+    u = np.ones(seq.batch)  # never kept whole unless short
+    keys = rng.integers(0, 4, size=seq.total).astype(np.uint32)  # priorities 0..3 only
+    keys[seq.offsets[3]:seq.offsets[4]] = 7  # one user with all priorities equal
+    _check(seq, u, keys, n_target=256, alpha=1.6, tag="priorities in 0..3")
+    keys2 = np.full(seq.total, 0xFFFFFFFF, dtype=np.uint32)  # top of the range
+    _check(seq, u, keys2, n_target=256, alpha=1.6, tag="all priorities 2^32 - 1")
+
+
+def test_sl_length_and_threshold_boundaries():
+    n_target, alpha = 4096, 1.6
+    L = sl.subsample_length(n_target, alpha)
+    assert L == 776
+    lengths = [L, L + 1, L + 1, 1000, 1000, 4096, 4096]
+    rng = np.random.default_rng(13)
+    seq = wl.jagged_from_lengths(rng, lengths)
+    u = np.zeros(seq.batch)
+    # exactly at the threshold: not below it, so the user is subsampled
+    u[1] = sl.keep_threshold(L + 1, n_target, alpha)
+    u[2] = np.nextafter(sl.keep_threshold(L + 1, n_target, alpha), 0.0)  # just below: kept
+    u[3] = sl.keep_threshold(1000, n_target, alpha)
+    u[4] = np.nextafter(sl.keep_threshold(1000, n_target, alpha), 0.0)
+    u[5] = sl.keep_threshold(4096, n_target, alpha)
+    u[6] = 0.999
+    keys = rng.integers(0, 2**32, size=seq.total, dtype=np.uint64).astype(np.uint32)
+    _, off = _check(seq, u, keys, n_target, alpha, tag="n = L, L+1; u at / below threshold")
+    lens = np.diff(off)
+    assert list(lens) == [L, L, L + 1, L, 1000, L, L]
+
+
+def test_sl_users_longer_than_one_tile():
+    rng = np.random.default_rng(14)
+    seq = wl.jagged_from_lengths(rng, [20000, 70000, 1500, 5000])
+    u = np.array([0.9, 0.9, 0.9, 1e-9])  # the last is kept whole by its draw
+    keys = rng.integers(0, 2**32, size=seq.total, dtype=np.uint64).astype(np.uint32)
+    x = wl.round_bf16(rng.standard_normal((seq.total, 64), dtype=np.float32))
+    _check(seq, u, keys, 4096, 1.6, x=x, tag="users of 20000 and 70000 tokens, d=64 rows")
+
+
+def test_sl_all_kept_and_empty_batch():
+    rng = np.random.default_rng(15)
+    seq = wl.jagged_from_lengths(rng, [5, 900, 3000, 0, 4096])
+    u = np.zeros(seq.batch)
+    u[:] = -1.0  # below every threshold: everyone kept whole
+    keys = rng.integers(0, 2**32, size=seq.total, dtype=np.uint64).astype(np.uint32)
+    _, off = _check(seq, u, keys, tag="every user kept whole")
+    np.testing.assert_array_equal(off, seq.offsets)
+    empty = wl.Jagged(offsets=np.zeros(1, dtype=np.int32), timestamps=np.zeros(0, dtype=np.int32))
+    raw = dev.jagged_of(empty)
+    kept, new_off, _, _ = ops.hstu_stochastic_length(
+        raw, torch.zeros(0, dtype=torch.float64, device="cuda"),
+        torch.zeros(0, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert new_off.cpu().tolist() == [0]
+
+
+def test_sl_batch_built_on_device_feeds_the_layer():
+    w = wl.config(3)
+    r = w.raw
+    kept, new_off, new_ts, x_out, _ = _device_sl(r.seq, r.u_keep, r.keys, r.n_target, r.alpha, r.x)
+    want_kept, want_off = sl.select(r.seq.offsets, r.u_keep, r.keys, r.n_target, r.alpha)
+    np.testing.assert_array_equal(new_off.cpu().numpy(), want_off)
+    T_new = int(want_off[-1])
+    lens = np.diff(want_off)
+    d = w.dims
+    seq_dev = ops.DeviceJagged(offsets=new_off, total_tokens=T_new, max_seq_len=int(lens.max()),
+                               timestamps=new_ts[:T_new])
+    y, _ = ops.hstu_layer_fwd(dev.dims_of(d), dev.weights_of(w.weights), seq_dev, x_out[:T_new])
+    torch.cuda.synchronize()
+    got = dev.bf16_to_numpy(y).astype(np.float64)
+    b_long = int(np.argmax(lens))
+    rows = [0, int(want_off[b_long]), int(want_off[b_long + 1] - 1), int(want_off[5] + 3), T_new - 1]
+    want = ref.layer_fwd(r.x[want_kept], w.weights, want_off, r.seq.timestamps[want_kept],
+                         d.num_heads, d.dqk, d.dv, d.ln_eps, rows=rows)
+    err = np.abs(got[rows] - want[rows])
+    say(f"[sl] layer on the device-built batch: T={T_new} max_abs={err.max():.3e} "
+        f"mean_abs={err.mean():.3e}")
+    assert np.all(np.isfinite(got))
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3
