@@ -128,6 +128,42 @@ def cpu_baseline(w, layers, n_seq=2):
             "seconds": round(dt, 3)}
 
 
+def sl_measure(torch, np, ops, dev, wl, reps=20):
+    """Stochastic Length on the 128-user raw batch (d = 512 rows gathered), timed alone.
+
+    Algorithmic bytes: the priorities once (4 B per raw token) and, per kept token, its
+    row read and written (2 x 2 d B), its timestamp read and written and its index
+    written (12 B).  Offsets and per-user draws are negligible.
+    """
+    w = wl.config(3)
+    r = w.raw
+    raw = dev.jagged_of(r.seq)
+    u = torch.from_numpy(r.u_keep.astype(np.float64)).cuda()
+    keys = torch.from_numpy(r.keys.view(np.int32)).cuda()
+    x = dev.bf16_tensor(r.x)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        _, new_off, _, _ = ops.hstu_stochastic_length(raw, u, keys, x=x, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        ops.hstu_stochastic_length(raw, u, keys, x=x, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    T_raw, T_new, dm = r.seq.total, int(new_off[-1].item()), w.dims.d_model
+    alg = 4 * T_raw + T_new * (4 * dm + 12)
+    return {"workload": f"stochastic length on {r.seq.batch} users, raw lengths log-uniform on "
+                        f"[256, 4096], N=4096, alpha=1.6, d={dm} rows gathered",
+            "raw_tokens": T_raw, "kept_tokens": T_new, "ms": round(ms, 4),
+            "raw_tokens_per_s": round(T_raw / (ms * 1e-3), 1),
+            "roofline": {"bound": "hbm", "achieved": round(alg / (ms * 1e-3) / 1e9, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(alg / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                         "algorithmic_bytes": alg}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -255,6 +291,8 @@ def main():
         "cpu_baseline": None,
         "host": platform.node(),
     }
+    log("stochastic length on the 128-user raw batch")
+    out["stochastic_length"] = sl_measure(torch, np, ops, dev, wl)
     if not args.no_cpu_baseline:
         log("cpu baseline: fp64 oracle, one layer on two 8192-token sequences")
         out["cpu_baseline"] = cpu_baseline(w, args.layers)

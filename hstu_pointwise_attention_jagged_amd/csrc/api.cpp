@@ -424,7 +424,8 @@ hstu_status_t hstu_stochastic_length(const hstu_jagged_t *raw, const double *u_k
   // no users: only new_offsets[0] = 0 is written (by the lengths kernel), no workspace
   if (raw->batch > 0 && (st = check_ws(ws, ws_bytes, hstu_sl_workspace_bytes(raw))) != HSTU_OK)
     return st;
-  hipError_t e = launch_stochastic_length(raw->seq_offsets, u_keep, keys, raw->batch, (int)l_real,
+  hipError_t e = launch_stochastic_length(raw->seq_offsets, u_keep, keys, raw->batch,
+                                          raw->total_tokens, (int)l_real,
                                           thr_num, new_offsets, (int32_t *)ws, raw->timestamps,
                                           kept, new_ts, x_raw, x_out, row_elems, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e);

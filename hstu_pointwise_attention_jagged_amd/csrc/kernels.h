@@ -69,9 +69,10 @@ hipError_t launch_norm_gate(const float *O, const uint16_t *U, int64_t u_stride,
 
 // Stochastic Length over a raw jagged batch (stochastic_length.hip): new offsets and the
 // raw indices of the kept tokens, plus (if given) their timestamps and feature rows.
-// mode is [B] int32 scratch.
+// mode is [B] int32 scratch; T_upper bounds the new total (the raw total).
 hipError_t launch_stochastic_length(const int32_t *off, const double *u_keep, const uint32_t *keys,
-                                    int B, int L, double thr_num, int32_t *new_off, int32_t *mode,
+                                    int B, int T_upper, int L, double thr_num, int32_t *new_off,
+                                    int32_t *mode,
                                     const int32_t *ts, int32_t *kept, int32_t *new_ts,
                                     const uint16_t *x, uint16_t *x_out, int64_t row_elems,
                                     hipStream_t stream);

@@ -17,8 +17,10 @@
 //    found by an MSB-first radix select over the priorities (four 8-bit digit passes,
 //    256-bin LDS histograms); the kept tokens are then compacted in time order with
 //    wave ballots and a workgroup scan per 1024-token tile, which also ranks the tokens
-//    that share the threshold priority by position.  The workgroup then gathers the
-//    kept tokens' timestamps and feature rows (16-byte copies) into the new batch.
+//    that share the threshold priority by position.
+//  * sl_gather_kernel (grid-stride over the whole GPU): timestamps and feature rows of
+//    the kept tokens, in 16-byte copies; its length is the device-side new total, and
+//    it is launched for the raw total as an upper bound.
 #include "common.h"
 #include "kernels.h"
 
@@ -90,8 +92,7 @@ __global__ __launch_bounds__(kSlThreads) void sl_lengths_kernel(const int32_t *_
 __global__ __launch_bounds__(kSlThreads) void sl_select_kernel(
     const int32_t *__restrict__ off, const uint32_t *__restrict__ keys, int L,
     const int32_t *__restrict__ new_off, const int32_t *__restrict__ mode,
-    const int32_t *__restrict__ ts, int32_t *__restrict__ kept, int32_t *__restrict__ new_ts,
-    const uint16_t *__restrict__ x, uint16_t *__restrict__ x_out, int64_t row_elems) {
+    int32_t *__restrict__ kept) {
   __shared__ int hist[256];
   __shared__ int wave_tot[kSlWaves];
   __shared__ int sel[2];
@@ -150,20 +151,28 @@ __global__ __launch_bounds__(kSlThreads) void sl_select_kernel(
       base_eq += tot_eq;
     }
   }
-  const int cnt = new_off[b + 1] - o0;
-  if (new_ts == nullptr && x_out == nullptr) return;
-  __syncthreads();  // this workgroup's kept[] entries are visible to all its threads
+}
+
+constexpr int kGatherThreads = 256;
+
+__global__ __launch_bounds__(kGatherThreads) void sl_gather_kernel(
+    const int32_t *__restrict__ new_off, int B, const int32_t *__restrict__ kept,
+    const int32_t *__restrict__ ts, int32_t *__restrict__ new_ts, const uint16_t *__restrict__ x,
+    uint16_t *__restrict__ x_out, int64_t row_elems) {
+  const int64_t T_new = new_off[B];
+  const int64_t gid = (int64_t)blockIdx.x * kGatherThreads + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * kGatherThreads;
   if (new_ts != nullptr)
-    for (int r = tid; r < cnt; r += kSlThreads) new_ts[o0 + r] = ts[kept[o0 + r]];
+    for (int64_t r = gid; r < T_new; r += stride) new_ts[r] = ts[kept[r]];
   if (x_out != nullptr) {
     // 16-byte chunks: row_elems is a multiple of 8 (checked by the entry point)
     const int64_t cpr = row_elems / 8;
-    const int64_t total = (int64_t)cnt * cpr;
-    for (int64_t c = tid; c < total; c += kSlThreads) {
-      const int r = (int)(c / cpr);
-      const int64_t e = (c % cpr) * 8;
-      const int64_t src = (int64_t)kept[o0 + r] * row_elems + e;
-      *reinterpret_cast<u32x4 *>(x_out + (int64_t)(o0 + r) * row_elems + e) =
+    const int64_t total = T_new * cpr;
+    for (int64_t c = gid; c < total; c += stride) {
+      const int64_t r = c / cpr;
+      const int64_t e = (c - r * cpr) * 8;
+      const int64_t src = (int64_t)kept[r] * row_elems + e;
+      *reinterpret_cast<u32x4 *>(x_out + r * row_elems + e) =
           *reinterpret_cast<const u32x4 *>(x + src);
     }
   }
@@ -172,7 +181,8 @@ __global__ __launch_bounds__(kSlThreads) void sl_select_kernel(
 }  // namespace
 
 hipError_t launch_stochastic_length(const int32_t *off, const double *u_keep, const uint32_t *keys,
-                                    int B, int L, double thr_num, int32_t *new_off, int32_t *mode,
+                                    int B, int T_upper, int L, double thr_num, int32_t *new_off,
+                                    int32_t *mode,
                                     const int32_t *ts, int32_t *kept, int32_t *new_ts,
                                     const uint16_t *x, uint16_t *x_out, int64_t row_elems,
                                     hipStream_t stream) {
@@ -180,8 +190,16 @@ hipError_t launch_stochastic_length(const int32_t *off, const double *u_keep, co
   sl_lengths_kernel<<<1, kSlThreads, 0, stream>>>(off, u_keep, B, L, thr_num, new_off, mode);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || B == 0) return e;
-  sl_select_kernel<<<B, kSlThreads, 0, stream>>>(off, keys, L, new_off, mode, ts, kept, new_ts, x,
-                                                 x_out, row_elems);
+  sl_select_kernel<<<B, kSlThreads, 0, stream>>>(off, keys, L, new_off, mode, kept);
+  e = hipGetLastError();
+  if (e != hipSuccess || (new_ts == nullptr && x_out == nullptr)) return e;
+  // upper bound on the work: every raw token kept (rows of row_elems / 8 chunks)
+  const int64_t per_row = x_out != nullptr ? row_elems / 8 : 1;
+  const int64_t work = (int64_t)T_upper * per_row;
+  const int64_t want = (work + kGatherThreads - 1) / kGatherThreads;
+  const int grid = (int)(want < 1 ? 1 : (want > 8192 ? 8192 : want));
+  sl_gather_kernel<<<grid, kGatherThreads, 0, stream>>>(new_off, B, kept, ts, new_ts, x, x_out,
+                                                        row_elems);
   return hipGetLastError();
 }
 
