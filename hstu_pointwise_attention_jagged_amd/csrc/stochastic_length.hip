@@ -118,14 +118,27 @@ __global__ __launch_bounds__(kSlThreads) void sl_select_kernel(
         if ((v & pmask) == prefix) atomicAdd(&hist[(v >> sh) & 255u], 1);
       }
       __syncthreads();
-      if (tid == 0) {
-        int cum = 0, bin = 0;
-        for (; bin < 255; ++bin) {
-          if (cum + hist[bin] >= remaining) break;
-          cum += hist[bin];
+      // the bin holding rank `remaining`: prefix sums over the 256 bins (four waves of
+      // 64 bins), and the one thread whose bin covers the rank records it
+      // (every thread passes both barriers; only the first four waves hold bins)
+      const int lane = tid & 63, wave = tid >> 6;
+      const int cnt = tid < 256 ? hist[tid] : 0;
+      int incl = cnt;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+      }
+      if (tid < 256 && lane == 63) wave_tot[wave] = incl;
+      __syncthreads();
+      if (tid < 256) {
+        int before = 0;
+        for (int w = 0; w < wave; ++w) before += wave_tot[w];
+        const int excl = before + incl - cnt;
+        if (cnt > 0 && excl < remaining && remaining <= excl + cnt) {
+          sel[0] = tid;
+          sel[1] = remaining - excl;
         }
-        sel[0] = bin;
-        sel[1] = remaining - cum;
       }
       __syncthreads();
       prefix |= (uint32_t)sel[0] << sh;
