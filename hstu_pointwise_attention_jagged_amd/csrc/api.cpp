@@ -133,6 +133,11 @@ size_t layer_ws_bytes(const hstu_dims_t *d, const hstu_jagged_t *s, const hstu_j
          attn_ws_bytes(s, pre);
 }
 
+// A stack adds one [T][d] bf16 activation buffer (the layers alternate between it and y).
+size_t stack_ws_bytes(const hstu_dims_t *d, const hstu_jagged_t *s, const hstu_jagged_t *pre) {
+  return layer_ws_bytes(d, s, pre) + align_up((size_t)s->total_tokens * d->d_model * sizeof(uint16_t));
+}
+
 struct LayerWs {
   float *o;
   uint16_t *g;
@@ -168,8 +173,8 @@ LayerWs carve_layer(void *ws, const hstu_dims_t *d, const hstu_jagged_t *s,
 
 // Key-block timestamp ranges for the batch and its prefix, when the time term is on.
 hipError_t launch_stats(const AttnArgs &aa, const hstu_jagged_t *s, const hstu_jagged_t *pre,
-                        hipStream_t st) {
-  if (aa.rab_time == nullptr || s->timestamps == nullptr) return hipSuccess;
+                        hipStream_t st, bool force = false) {
+  if ((!force && aa.rab_time == nullptr) || s->timestamps == nullptr) return hipSuccess;
   hipError_t e = launch_block_stats(s->timestamps, s->seq_offsets, s->batch, s->max_seq_len,
                                     const_cast<int2 *>(aa.kstat), st);
   if (e == hipSuccess && pre != nullptr && pre->timestamps != nullptr && pre->total_tokens > 0)
@@ -211,21 +216,34 @@ AttnArgs attn_args(const hstu_dims_t *d, const float *rab_pos, const float *rab_
 }
 
 // f1 -> attention -> norm-gate -> f2 for one batch whose attention args are ready.
-hstu_status_t run_layer(const hstu_dims_t *d, const hstu_weights_t *w, const hstu_jagged_t *s,
-                        const uint16_t *x, uint16_t *y, uint16_t *uvqk, const AttnArgs &aa,
-                        const LayerWs &lw, const hstu_jagged_t *pre, hipStream_t st) {
+// Jagged tile schedule and key-block timestamp ranges of a batch (and its prefix).  They
+// depend only on the batch, so a stack of layers builds them once; `all_stats` asks for
+// the ranges whenever timestamps exist (a later layer of a stack may use the time term).
+hstu_status_t run_setup(const hstu_jagged_t *s, const AttnArgs &aa, const LayerWs &lw,
+                        const hstu_jagged_t *pre, bool all_stats, hipStream_t st) {
   const int max_prefix = pre != nullptr ? pre->max_seq_len : 0;
-  const int T = s->total_tokens;
-  const int hdv = d->num_heads * d->dv;
-  const int n1 = 2 * d->num_heads * (d->dqk + d->dv);
-  hipError_t e;
-  e = timed(0, st, [&] {
+  hipError_t e = timed(0, st, [&] {
     return launch_schedule(s->seq_offsets, aa.p_offsets, s->batch, aa.mask, s->max_seq_len,
                            max_prefix, lw.work, lw.n_work, st);
   });
   if (e != hipSuccess) return hip_fail(e);
-  e = timed(0, st, [&] { return launch_stats(aa, s, pre, st); });
+  e = timed(0, st, [&] { return launch_stats(aa, s, pre, st, all_stats); });
   if (e != hipSuccess) return hip_fail(e);
+  return HSTU_OK;
+}
+
+hstu_status_t run_layer(const hstu_dims_t *d, const hstu_weights_t *w, const hstu_jagged_t *s,
+                        const uint16_t *x, uint16_t *y, uint16_t *uvqk, const AttnArgs &aa,
+                        const LayerWs &lw, const hstu_jagged_t *pre, hipStream_t st,
+                        bool setup = true) {
+  const int T = s->total_tokens;
+  const int hdv = d->num_heads * d->dv;
+  const int n1 = 2 * d->num_heads * (d->dqk + d->dv);
+  hipError_t e;
+  if (setup) {
+    const hstu_status_t r = run_setup(s, aa, lw, pre, false, st);
+    if (r != HSTU_OK) return r;
+  }
   e = timed(1, st, [&] { return launch_gemm(x, w->w1, w->b1, uvqk, T, n1, d->d_model, ACT_SILU, OUT_F16, st); });
   if (e != hipSuccess) return hip_fail(e);
   const int64_t cap = attn_work_capacity(s->batch, T);
@@ -332,6 +350,115 @@ hstu_status_t hstu_layer_fwd_mfalcon(const hstu_dims_t *dims, const hstu_weights
   aa.pv = hist_uvqk + hdv;
   aa.p_stride = n1;
   return run_layer(dims, w, cand, x_cand, y_cand, uvqk_cand, aa, lw, hist, (hipStream_t)stream);
+}
+
+size_t hstu_stack_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_t *seq) {
+  if (check_dims(dims) != HSTU_OK || check_seq(seq) != HSTU_OK) return 0;
+  return stack_ws_bytes(dims, seq, nullptr);
+}
+
+size_t hstu_stack_mfalcon_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_t *hist,
+                                          const hstu_jagged_t *cand) {
+  if (check_dims(dims) != HSTU_OK || check_seq(hist) != HSTU_OK || check_seq(cand) != HSTU_OK)
+    return 0;
+  return stack_ws_bytes(dims, cand, hist);
+}
+
+hstu_status_t hstu_stack_fwd(const hstu_dims_t *dims, int32_t n_layers, const hstu_weights_t *w,
+                             const hstu_jagged_t *seq, const uint16_t *x, uint16_t *y,
+                             uint16_t *uvqk, int32_t keep_caches, void *ws, size_t ws_bytes,
+                             void *stream) {
+  hstu_status_t st;
+  if ((st = check_dims(dims)) != HSTU_OK) return st;
+  if ((st = check_seq(seq)) != HSTU_OK) return st;
+  if (n_layers < 1 || w == nullptr) return HSTU_ERR_INVALID_ARG;
+  for (int l = 0; l < n_layers; ++l)
+    if ((st = check_weights(&w[l])) != HSTU_OK) return st;
+  if (seq->total_tokens > 0 && (x == nullptr || y == nullptr || uvqk == nullptr))
+    return HSTU_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(uvqk)) return HSTU_ERR_INVALID_ARG;
+  if ((void *)x == (void *)y) return HSTU_ERR_INVALID_ARG;
+  if (seq->batch == 0 || seq->total_tokens == 0) return HSTU_OK;
+  if ((st = check_ws(ws, ws_bytes, stack_ws_bytes(dims, seq, nullptr))) != HSTU_OK) return st;
+  const int hdv = dims->num_heads * dims->dv, hqk = dims->num_heads * dims->dqk;
+  const int64_t n1 = 2 * (int64_t)(hdv + hqk);
+  if (!rows_addressable(seq->max_seq_len, n1)) return HSTU_ERR_UNSUPPORTED;
+
+  hipStream_t sst = (hipStream_t)stream;
+  const LayerWs lw = carve_layer(ws, dims, seq, nullptr);
+  uint16_t *act = (uint16_t *)((char *)ws + layer_ws_bytes(dims, seq, nullptr));
+  const size_t cache = (size_t)seq->total_tokens * n1;
+  auto args = [&](int l) {
+    uint16_t *u = uvqk + (keep_caches ? (size_t)l * cache : 0);
+    return attn_args(dims, w[l].rab_pos, w[l].rab_time, seq, u + 2 * hdv, u + 2 * hdv + hqk,
+                     u + hdv, n1, lw.o, lw);
+  };
+  if ((st = run_setup(seq, args(0), lw, nullptr, true, sst)) != HSTU_OK) return st;
+  const uint16_t *in = x;
+  for (int l = 0; l < n_layers; ++l) {
+    // the last layer writes y; earlier layers alternate so that no layer reads its output
+    uint16_t *out = ((n_layers - 1 - l) % 2 == 0) ? y : act;
+    uint16_t *u = uvqk + (keep_caches ? (size_t)l * cache : 0);
+    if ((st = run_layer(dims, &w[l], seq, in, out, u, args(l), lw, nullptr, sst, false)) != HSTU_OK)
+      return st;
+    in = out;
+  }
+  return HSTU_OK;
+}
+
+hstu_status_t hstu_stack_fwd_mfalcon(const hstu_dims_t *dims, int32_t n_layers,
+                                     const hstu_weights_t *w, const hstu_jagged_t *hist,
+                                     const uint16_t *hist_uvqk, const hstu_jagged_t *cand,
+                                     const uint16_t *x_cand, uint16_t *y_cand, uint16_t *uvqk_cand,
+                                     void *ws, size_t ws_bytes, void *stream) {
+  hstu_status_t st;
+  if ((st = check_dims(dims)) != HSTU_OK) return st;
+  if ((st = check_seq(hist)) != HSTU_OK) return st;
+  if ((st = check_seq(cand)) != HSTU_OK) return st;
+  if (n_layers < 1 || w == nullptr) return HSTU_ERR_INVALID_ARG;
+  for (int l = 0; l < n_layers; ++l)
+    if ((st = check_weights(&w[l])) != HSTU_OK) return st;
+  if (hist->batch != cand->batch) return HSTU_ERR_INVALID_ARG;
+  if (hist->total_tokens > 0 && hist_uvqk == nullptr) return HSTU_ERR_INVALID_ARG;
+  if (cand->total_tokens > 0 && (x_cand == nullptr || y_cand == nullptr || uvqk_cand == nullptr))
+    return HSTU_ERR_INVALID_ARG;
+  if (!aligned16(hist_uvqk) || !aligned16(x_cand) || !aligned16(y_cand) || !aligned16(uvqk_cand))
+    return HSTU_ERR_INVALID_ARG;
+  if ((void *)x_cand == (void *)y_cand) return HSTU_ERR_INVALID_ARG;
+  if ((cand->timestamps == nullptr) != (hist->timestamps == nullptr)) return HSTU_ERR_INVALID_ARG;
+  if (cand->batch == 0 || cand->total_tokens == 0) return HSTU_OK;
+  if ((st = check_ws(ws, ws_bytes, stack_ws_bytes(dims, cand, hist))) != HSTU_OK) return st;
+  const int hdv = dims->num_heads * dims->dv, hqk = dims->num_heads * dims->dqk;
+  const int64_t n1 = 2 * (int64_t)(hdv + hqk);
+  if (!rows_addressable(cand->max_seq_len, n1) || !rows_addressable(hist->max_seq_len, n1))
+    return HSTU_ERR_UNSUPPORTED;
+
+  hipStream_t sst = (hipStream_t)stream;
+  const LayerWs lw = carve_layer(ws, dims, cand, hist);
+  uint16_t *act = (uint16_t *)((char *)ws + layer_ws_bytes(dims, cand, hist));
+  const size_t cache = (size_t)hist->total_tokens * n1;
+  auto args = [&](int l) {
+    AttnArgs aa = attn_args(dims, w[l].rab_pos, w[l].rab_time, cand, uvqk_cand + 2 * hdv,
+                            uvqk_cand + 2 * hdv + hqk, uvqk_cand + hdv, n1, lw.o, lw);
+    const uint16_t *hu = hist_uvqk + (size_t)l * cache;
+    aa.mask = 1;
+    aa.p_offsets = hist->seq_offsets;
+    aa.p_ts = hist->timestamps;
+    aa.pk = hu + 2 * hdv + hqk;
+    aa.pv = hu + hdv;
+    aa.p_stride = n1;
+    return aa;
+  };
+  if ((st = run_setup(cand, args(0), lw, hist, true, sst)) != HSTU_OK) return st;
+  const uint16_t *in = x_cand;
+  for (int l = 0; l < n_layers; ++l) {
+    uint16_t *out = ((n_layers - 1 - l) % 2 == 0) ? y_cand : act;
+    if ((st = run_layer(dims, &w[l], cand, in, out, uvqk_cand, args(l), lw, hist, sst, false)) !=
+        HSTU_OK)
+      return st;
+    in = out;
+  }
+  return HSTU_OK;
 }
 
 hstu_status_t hstu_attn_fwd(const hstu_dims_t *dims, const float *rab_pos, const float *rab_time,

@@ -19,7 +19,9 @@ from . import _lib
 __all__ = ["HSTUError", "LayerDims", "DeviceWeights", "DeviceJagged", "hstu_layer_fwd",
            "hstu_layer_fwd_mfalcon", "hstu_attn_fwd", "hstu_layer_workspace_bytes",
            "hstu_attn_workspace_bytes", "hstu_mfalcon_workspace_bytes", "hstu_validate_jagged",
-           "hstu_sl_workspace_bytes", "hstu_stochastic_length", "profile_enable", "profile_reset",
+           "hstu_sl_workspace_bytes", "hstu_stochastic_length", "hstu_stack_fwd",
+           "hstu_stack_fwd_mfalcon", "hstu_stack_workspace_bytes",
+           "hstu_stack_mfalcon_workspace_bytes", "profile_enable", "profile_reset",
            "profile_collect"]
 
 
@@ -196,6 +198,83 @@ def hstu_layer_fwd_mfalcon(dims: LayerDims, w: DeviceWeights, hist: DeviceJagged
                                     _stream(stream))
     _raise(st, "hstu_layer_fwd_mfalcon")
     return y_cand, uvqk_cand
+
+
+def _weights_array(ws):
+    arr = (_lib.Weights * len(ws))()
+    for i, w in enumerate(ws):
+        arr[i] = w.c()
+    return arr
+
+
+def hstu_stack_workspace_bytes(dims: LayerDims, seq: DeviceJagged) -> int:
+    lib = _lib.load()
+    d, s = dims.c(), seq.c()
+    return int(lib.hstu_stack_workspace_bytes(ctypes.byref(d), ctypes.byref(s)))
+
+
+def hstu_stack_mfalcon_workspace_bytes(dims: LayerDims, hist: DeviceJagged, cand: DeviceJagged) -> int:
+    lib = _lib.load()
+    d, hs, cs = dims.c(), hist.c(), cand.c()
+    return int(lib.hstu_stack_mfalcon_workspace_bytes(ctypes.byref(d), ctypes.byref(hs), ctypes.byref(cs)))
+
+
+def hstu_stack_fwd(dims: LayerDims, weights, seq: DeviceJagged, x: torch.Tensor, *,
+                   keep_caches: bool = False, y: Optional[torch.Tensor] = None,
+                   uvqk: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                   stream=None):
+    """A stack of len(weights) causal layers.  Returns (y bf16 [T][d], uvqk): uvqk is
+    [T][2H(dv+dqk)] scratch, or [L][T][2H(dv+dqk)] per-layer caches with keep_caches."""
+    lib = _lib.load()
+    _check(x, torch.bfloat16, "x")
+    L, T = len(weights), seq.total_tokens
+    if y is None:
+        y = torch.empty((T, dims.d_model), dtype=torch.bfloat16, device=x.device)
+    if uvqk is None:
+        shape = (L, T, dims.uvqk_width) if keep_caches else (T, dims.uvqk_width)
+        uvqk = torch.empty(shape, dtype=torch.float16, device=x.device)
+    _check(y, torch.bfloat16, "y")
+    _check(uvqk, torch.float16, "uvqk")
+    arr = _weights_array(weights)
+    d, s = dims.c(), seq.c()
+    need = int(lib.hstu_stack_workspace_bytes(ctypes.byref(d), ctypes.byref(s)))
+    ws = _workspace(need, x.device, workspace)
+    st = lib.hstu_stack_fwd(ctypes.byref(d), L, arr, ctypes.byref(s), _ptr(x), _ptr(y), _ptr(uvqk),
+                            1 if keep_caches else 0, _ptr(ws), ws.numel() * ws.element_size(),
+                            _stream(stream))
+    _raise(st, "hstu_stack_fwd")
+    return y, uvqk
+
+
+def hstu_stack_fwd_mfalcon(dims: LayerDims, weights, hist: DeviceJagged, hist_uvqk: torch.Tensor,
+                           cand: DeviceJagged, x_cand: torch.Tensor, *,
+                           y_cand: Optional[torch.Tensor] = None,
+                           uvqk_cand: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None, stream=None):
+    """Candidates through len(weights) layers against per-layer history caches
+    hist_uvqk [L][T_hist][2H(dv+dqk)].  Returns y_cand bf16 [T_cand][d]."""
+    lib = _lib.load()
+    _check(x_cand, torch.bfloat16, "x_cand")
+    _check(hist_uvqk, torch.float16, "hist_uvqk")
+    L, T = len(weights), cand.total_tokens
+    if hist_uvqk.dim() != 3 or hist_uvqk.shape[0] != L:
+        raise ValueError("hist_uvqk: expected [L][T_hist][2H(dv+dqk)] per-layer caches")
+    if y_cand is None:
+        y_cand = torch.empty((T, dims.d_model), dtype=torch.bfloat16, device=x_cand.device)
+    if uvqk_cand is None:
+        uvqk_cand = torch.empty((T, dims.uvqk_width), dtype=torch.float16, device=x_cand.device)
+    _check(y_cand, torch.bfloat16, "y_cand")
+    _check(uvqk_cand, torch.float16, "uvqk_cand")
+    arr = _weights_array(weights)
+    d, hs, cs = dims.c(), hist.c(), cand.c()
+    need = int(lib.hstu_stack_mfalcon_workspace_bytes(ctypes.byref(d), ctypes.byref(hs),
+                                                      ctypes.byref(cs)))
+    ws = _workspace(need, x_cand.device, workspace)
+    st = lib.hstu_stack_fwd_mfalcon(ctypes.byref(d), L, arr, ctypes.byref(hs), _ptr(hist_uvqk),
+                                    ctypes.byref(cs), _ptr(x_cand), _ptr(y_cand), _ptr(uvqk_cand),
+                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _raise(st, "hstu_stack_fwd_mfalcon")
+    return y_cand
 
 
 def hstu_attn_fwd(dims: LayerDims, seq: DeviceJagged, q: torch.Tensor, k: torch.Tensor,

@@ -153,6 +153,43 @@ hstu_status_t hstu_layer_fwd_mfalcon(const hstu_dims_t *dims, const hstu_weights
                                      uint16_t *y_cand, uint16_t *uvqk_cand, void *ws,
                                      size_t ws_bytes, void *stream);
 
+/* Workspace (bytes) of hstu_stack_fwd / hstu_stack_fwd_mfalcon: a layer's workspace
+ * plus one [T][d] bf16 activation buffer; 0 when the arguments are invalid.          */
+size_t hstu_stack_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_t *seq);
+size_t hstu_stack_mfalcon_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_t *hist,
+                                          const hstu_jagged_t *cand);
+
+/* A stack of n_layers causal layers (the deep configurations of chenhuiyu.github.io,
+ * section on experiments, go to 24 layers): layer l maps X_l to X_{l+1} with its own
+ * weights w[l]; X_0 = x and the last layer's output is written to y.  Every layer is
+ * computed exactly as hstu_layer_fwd would (the results are bit-identical to n_layers
+ * such calls); the batch's tile schedule and key-block timestamp ranges are built once.
+ *   w           (host) array of n_layers weight sets
+ *   x, y        (device) bf16 [T][d]; y may not alias x (x is not written)
+ *   uvqk        (device) fp16: [T][2H(dv+dqk)] reused by every layer when keep_caches is
+ *               0, or [n_layers][T][2H(dv+dqk)] keeping every layer's U|V|Q|K when it is
+ *               1 (the per-layer K/V caches of an M-FALCON history)
+ *   ws          >= hstu_stack_workspace_bytes(dims, seq)                              */
+hstu_status_t hstu_stack_fwd(const hstu_dims_t *dims, int32_t n_layers, const hstu_weights_t *w,
+                             const hstu_jagged_t *seq, const uint16_t *x, uint16_t *y,
+                             uint16_t *uvqk, int32_t keep_caches, void *ws, size_t ws_bytes,
+                             void *stream);
+
+/* M-FALCON serving through a stack (chenhuiyu.github.io, section "另外三块拼图", item 3;
+ * ltzyclt.github.io section 5.2): a candidate micro-batch goes through all n_layers
+ * layers, each attending to that layer's cached history K/V and to itself.  Layer l is
+ * computed exactly as hstu_layer_fwd_mfalcon would with hist_uvqk + l*T_hist*2H(dv+dqk).
+ *   hist_uvqk   (device) fp16 [n_layers][T_hist][2H(dv+dqk)], written by hstu_stack_fwd on
+ *               the history batch with keep_caches = 1 and the same weights
+ *   x_cand, y_cand (device) bf16 [T_cand][d], no aliasing
+ *   uvqk_cand   (device) fp16 [T_cand][2H(dv+dqk)] scratch
+ *   ws          >= hstu_stack_mfalcon_workspace_bytes(dims, hist, cand)                */
+hstu_status_t hstu_stack_fwd_mfalcon(const hstu_dims_t *dims, int32_t n_layers,
+                                     const hstu_weights_t *w, const hstu_jagged_t *hist,
+                                     const uint16_t *hist_uvqk, const hstu_jagged_t *cand,
+                                     const uint16_t *x_cand, uint16_t *y_cand, uint16_t *uvqk_cand,
+                                     void *ws, size_t ws_bytes, void *stream);
+
 /* Equation (2) alone: out[t][h*dv + f] = sum_j SiLU(q_t.k_j + rab(t,j)) v_j[f] over the
  * keys allowed by `mask` (see hstu_mask_t), fp32, no normalisation.
  *   q, k, v (device) fp16; row t of head h at q + t*row_stride + h*dqk (same for k,v

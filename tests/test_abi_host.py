@@ -195,3 +195,28 @@ def test_sl_workspace_checked(lib):
     assert _call_sl(lib, seq=seq, ws_bytes=need - 1) == _lib.HSTU_ERR_WORKSPACE
     assert _call_sl(lib, seq=seq, ws=FAKE + 16) == _lib.HSTU_ERR_WORKSPACE
     assert lib.hstu_sl_workspace_bytes(ctypes.byref(_lib.Jagged(-1, 0, 0, FAKE, None))) == 0
+
+
+def test_stack_bad_arguments_rejected(lib):
+    d = _dims()
+    seq = _seq()
+    w = (_lib.Weights * 2)(_lib.Weights(FAKE, None, FAKE, None, None, None, None, None),
+                           _lib.Weights(FAKE, None, FAKE, None, None, None, None, None))
+    def call(n=2, ws=w, x=FAKE, y=FAKE + 4096, keep=1):
+        return lib.hstu_stack_fwd(ctypes.byref(d), n, ws, ctypes.byref(seq), x, y, FAKE, keep,
+                                  FAKE, 1 << 30, None)
+    assert call(n=0) == _lib.HSTU_ERR_INVALID_ARG
+    assert call(ws=None) == _lib.HSTU_ERR_INVALID_ARG
+    assert call(y=FAKE) == _lib.HSTU_ERR_INVALID_ARG          # y aliases x
+    w[1] = _lib.Weights(None, None, FAKE, None, None, None, None, None)
+    assert call() == _lib.HSTU_ERR_INVALID_ARG                # layer 1 has no w1
+    w[1] = _lib.Weights(FAKE, None, FAKE, None, None, None, None, None)
+    need = lib.hstu_stack_workspace_bytes(ctypes.byref(d), ctypes.byref(seq))
+    act = -(-118 * 64 * 2 // 256) * 256  # one [T][d] bf16 buffer, 256-byte aligned
+    assert need == lib.hstu_layer_workspace_bytes(ctypes.byref(d), ctypes.byref(seq)) + act
+    assert lib.hstu_stack_fwd(ctypes.byref(d), 2, w, ctypes.byref(seq), FAKE, FAKE + 4096, FAKE, 1,
+                              FAKE, need - 1, None) == _lib.HSTU_ERR_WORKSPACE
+    cand = _seq(B=3, T=12, L=4)
+    assert lib.hstu_stack_fwd_mfalcon(ctypes.byref(d), 2, w, ctypes.byref(seq), FAKE,
+                                      ctypes.byref(cand), FAKE, FAKE + 4096, FAKE, FAKE, 1 << 30,
+                                      None) == _lib.HSTU_ERR_INVALID_ARG  # batch sizes differ
