@@ -164,6 +164,76 @@ def sl_measure(torch, np, ops, dev, wl, reps=20):
                          "algorithmic_bytes": alg}}
 
 
+def mfalcon_measure(torch, np, ops, dev, wl, n_layers=4, bm=1024, reps=3):
+    """M-FALCON serving through an n_layers stack on the 16-user workload: the history
+    pass (4096 tokens per user, every layer's K/V kept) and the scoring of 1024
+    candidates per user in micro-batches of bm per user, each through all layers against
+    the cached history.  Useful FLOPs per candidate and layer: f1 2 d 2H(dqk+dv), attention
+    2H(dqk+dv)(n_h + 1) (the history keys and itself), f2 2 H dv d."""
+    w = wl.config(4)
+    d = w.dims
+    rng = np.random.default_rng(4000)
+    lw = [w.weights] + [wl.draw_weights(rng, d) for _ in range(n_layers - 1)]
+    dims, dw = dev.dims_of(d), [dev.weights_of(x) for x in lw]
+    hist = dev.jagged_of(w.seq)
+    T_h = w.seq.total
+    x_h = dev.bf16_tensor(w.x)
+    y_h = torch.empty_like(x_h)
+    caches = torch.empty((n_layers, T_h, d.uvqk_width), dtype=torch.float16, device="cuda")
+    ws_h = torch.empty(ops.hstu_stack_workspace_bytes(dims, hist), dtype=torch.uint8, device="cuda")
+    cand = w.cand
+    n_c = int(cand.offsets[1] - cand.offsets[0])
+    mbs = []
+    for start in range(0, n_c, bm):
+        m = min(bm, n_c - start)
+        sel = np.concatenate([cand.offsets[b] + start + np.arange(m) for b in range(cand.batch)])
+        mc = wl.Jagged(offsets=wl.offsets_from_lengths(np.full(cand.batch, m)),
+                       timestamps=cand.timestamps[sel])
+        mbs.append((dev.jagged_of(mc), dev.bf16_tensor(w.x_cand[sel])))
+    m0 = mbs[0][0]
+    ws_c = torch.empty(ops.hstu_stack_mfalcon_workspace_bytes(dims, hist, m0), dtype=torch.uint8,
+                       device="cuda")
+    y_c = torch.empty((m0.total_tokens, d.d_model), dtype=torch.bfloat16, device="cuda")
+    u_c = torch.empty((m0.total_tokens, d.uvqk_width), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def history():
+        ops.hstu_stack_fwd(dims, dw, hist, x_h, keep_caches=True, y=y_h, uvqk=caches,
+                           workspace=ws_h, stream=stream)
+
+    def score():
+        for mc, xc in mbs:
+            ops.hstu_stack_fwd_mfalcon(dims, dw, hist, caches, mc, xc, y_cand=y_c, uvqk_cand=u_c,
+                                       workspace=ws_c, stream=stream)
+
+    def timed_ms(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    hist_ms = timed_ms(history)
+    score_ms = timed_ms(score)
+    H, dq, dv_, dm = d.num_heads, d.dqk, d.dv, d.d_model
+    n_h = int(w.seq.lengths[0])
+    n_cand = int(cand.total)
+    per_cand = 2 * dm * 2 * H * (dq + dv_) + 2 * H * (dq + dv_) * (n_h + 1) + 2 * H * dv_ * dm
+    f1, att, f2 = useful_flops(w.seq.lengths.tolist(), dm, H, dq, dv_)
+    return {"workload": f"M-FALCON serving, {cand.batch} users x ({n_h} history + {n_c} "
+                        f"candidates), d={dm}, {H} heads x {dq}, {n_layers}-layer stack, "
+                        f"micro-batches of {bm} candidates per user",
+            "layers": n_layers, "b_m": bm, "history_ms": round(hist_ms, 3),
+            "history_tflops": round(n_layers * (f1 + att + f2) / (hist_ms * 1e-3) / 1e12, 1),
+            "score_ms": round(score_ms, 3),
+            "candidates_per_s": round(n_cand / (score_ms * 1e-3), 1),
+            "score_tflops": round(n_layers * n_cand * per_cand / (score_ms * 1e-3) / 1e12, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -219,18 +289,17 @@ def main():
     for _ in range(args.layers - 1):
         layer_w.append(dev.weights_of(wl.draw_weights(rng, d)))
     x0 = dev.bf16_tensor(w.x)
-    bufs = [torch.empty_like(x0), torch.empty_like(x0)]
+    bufs = [torch.empty_like(x0)]
     uvqk = torch.empty((T, d.uvqk_width), dtype=torch.float16, device="cuda")
-    ws = torch.empty(ops.hstu_layer_workspace_bytes(dims, seq), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(ops.hstu_stack_workspace_bytes(dims, seq), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
     def step():
-        x = x0
-        for l in range(args.layers):
-            y = bufs[l & 1]
-            ops.hstu_layer_fwd(dims, layer_w[l], seq, x, y=y, uvqk=uvqk, workspace=ws, stream=stream)
-            x = y
-        return x
+        # the whole stack in one call: the batch's schedule is built once, then every
+        # layer runs f1, attention, norm-gate and f2
+        y, _ = ops.hstu_stack_fwd(dims, layer_w, seq, x0, y=bufs[0], uvqk=uvqk, workspace=ws,
+                                  stream=stream)
+        return y
 
     log(f"warmup {args.warmup} steps of {args.layers} layers")
     for _ in range(args.warmup):
@@ -293,6 +362,8 @@ def main():
     }
     log("stochastic length on the 128-user raw batch")
     out["stochastic_length"] = sl_measure(torch, np, ops, dev, wl)
+    log("M-FALCON serving through a 4-layer stack, micro-batches of 1024 and 128 per user")
+    out["mfalcon_serving"] = [mfalcon_measure(torch, np, ops, dev, wl, bm=bm) for bm in (1024, 128)]
     if not args.no_cpu_baseline:
         log("cpu baseline: fp64 oracle, one layer on two 8192-token sequences")
         out["cpu_baseline"] = cpu_baseline(w, args.layers)
