@@ -1,0 +1,79 @@
+"""Pins of the attention-gradient oracle (CPU only).
+
+oracle/hstu_bwd.attention_bwd must be the derivative of oracle/hstu_ref.attention: every
+gradient entry (q, k, v and both bias tables) is compared with a central finite
+difference of L = sum(attention(...) * G) for a fixed random G, on small jagged batches
+(zero-length, one-token and longer users, shared and per-head tables).  A dropped term,
+a wrong sign, a transposed operand or a wrong mask in the gradient fails these checks.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import hstu_bwd as bwd
+from oracle import hstu_ref as ref
+
+
+def _case(seed, lengths, H=2, dh=4, per_head_time=True):
+    rng = np.random.default_rng(seed)
+    lengths = np.asarray(lengths)
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    T = int(off[-1])
+    ts = np.concatenate([np.cumsum(rng.integers(1, 40, size=n)) if n else np.zeros(0, np.int64)
+                         for n in lengths]).astype(np.int64)
+    q = rng.standard_normal((T, H * dh))
+    k = rng.standard_normal((T, H * dh))
+    v = rng.standard_normal((T, H * dh))
+    P = 0.5 * rng.standard_normal((1, 6))                       # 6 position buckets
+    Tt = 0.5 * rng.standard_normal((H if per_head_time else 1, 5))  # 5 time buckets
+    G = rng.standard_normal((T, H * dh))
+    return off, ts, q, k, v, P, Tt, G, H, dh
+
+
+def _loss(off, ts, q, k, v, P, Tt, G, H, dh):
+    o = ref.attention(q, k, v, off, ts, H, dh, dh, P, Tt, workers=1)
+    return float(np.sum(o * G))
+
+
+@pytest.mark.parametrize("seed,lengths,per_head", [
+    (0, [3, 5, 0, 1, 4], True),
+    (1, [9], False),
+])
+def test_attention_gradient_matches_finite_differences(seed, lengths, per_head):
+    off, ts, q, k, v, P, Tt, G, H, dh = _case(seed, lengths, per_head_time=per_head)
+    dq, dk, dv, dP, dT = bwd.attention_bwd(q, k, v, G, off, ts, H, dh, dh, P, Tt)
+    eps = 1e-6
+    args = dict(q=q, k=k, v=v, P=P, Tt=Tt)
+    grads = dict(q=dq, k=dk, v=dv, P=dP, Tt=dT)
+    for name in args:
+        x = args[name]
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            a_p = dict(args, **{name: xp})
+            a_m = dict(args, **{name: xm})
+            num[idx] = (_loss(off, ts, a_p["q"], a_p["k"], a_p["v"], a_p["P"], a_p["Tt"], G, H, dh) -
+                        _loss(off, ts, a_m["q"], a_m["k"], a_m["v"], a_m["P"], a_m["Tt"], G, H, dh)) / (2 * eps)
+        scale = max(1.0, float(np.abs(num).max()))
+        np.testing.assert_allclose(grads[name], num, rtol=0, atol=2e-6 * scale, err_msg=name)
+
+
+def test_silu_grad_closed_form():
+    x = np.array([-30.0, -2.0, -0.5, 0.0, 0.5, 2.0, 30.0])
+    s = 1.0 / (1.0 + np.exp(-x))
+    np.testing.assert_allclose(bwd.silu_grad(x), s + x * s * (1 - s), rtol=1e-15)
+    assert bwd.silu_grad(np.array([0.0]))[0] == 0.5
+
+
+def test_masked_and_future_tokens_get_no_gradient_from_the_past():
+    # the last token's query sees every key; the first token's key is seen by every query,
+    # but the first query sees only itself: its dq depends on key 0 alone
+    off, ts, q, k, v, P, Tt, G, H, dh = _case(3, [6], per_head_time=False)
+    G2 = np.zeros_like(G)
+    G2[0] = G[0]  # upstream gradient only on row 0
+    dq, dk, dv, _, _ = bwd.attention_bwd(q, k, v, G2, off, ts, H, dh, dh, P, Tt)
+    assert np.all(dk[1:] == 0) and np.all(dv[1:] == 0)  # row 0 attends to key 0 only
+    assert np.all(dq[1:] == 0)
+    assert np.any(dq[0] != 0) and np.any(dk[0] != 0)
