@@ -461,6 +461,75 @@ hstu_status_t hstu_stack_fwd_mfalcon(const hstu_dims_t *dims, int32_t n_layers,
   return HSTU_OK;
 }
 
+size_t hstu_attn_bwd_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_t *seq) {
+  if (check_attn_dims(dims) != HSTU_OK || check_seq(seq) != HSTU_OK) return 0;
+  return attn_ws_bytes(seq, nullptr);
+}
+
+hstu_status_t hstu_attn_bwd(const hstu_dims_t *dims, const float *rab_pos, const float *rab_time,
+                            const hstu_jagged_t *seq, const uint16_t *q, const uint16_t *k,
+                            const uint16_t *v, int64_t row_stride, const float *d_out,
+                            float *dq, float *dk, float *dv, void *ws, size_t ws_bytes,
+                            void *stream) {
+  hstu_status_t st;
+  if ((st = check_attn_dims(dims)) != HSTU_OK) return st;
+  if ((st = check_seq(seq)) != HSTU_OK) return st;
+  const int64_t hq = (int64_t)dims->num_heads * dims->dqk;
+  if (seq->total_tokens > 0 && (q == nullptr || k == nullptr || v == nullptr ||
+                                d_out == nullptr || dq == nullptr || dk == nullptr ||
+                                dv == nullptr))
+    return HSTU_ERR_INVALID_ARG;
+  if (row_stride < hq || row_stride % 8 != 0) return HSTU_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(d_out) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv))
+    return HSTU_ERR_INVALID_ARG;
+  if (seq->total_tokens > 0) {  // three distinct outputs, none of them an input
+    const void *outs[3] = {dq, dk, dv};
+    const void *ins[4] = {q, k, v, d_out};
+    for (int i = 0; i < 3; ++i) {
+      for (int j = i + 1; j < 3; ++j)
+        if (outs[i] == outs[j]) return HSTU_ERR_INVALID_ARG;
+      for (const void *in : ins)
+        if (outs[i] == in) return HSTU_ERR_INVALID_ARG;
+    }
+  }
+  if (seq->batch == 0 || seq->total_tokens == 0) return HSTU_OK;
+  if ((st = check_ws(ws, ws_bytes, attn_ws_bytes(seq, nullptr))) != HSTU_OK) return st;
+  if (attn_block_m(seq->max_seq_len) != 128) return HSTU_ERR_UNSUPPORTED;  // the kernels' tile
+
+  LayerWs lw{};
+  carve_attn((char *)ws, seq, nullptr, lw);
+  AttnBwdArgs a{};
+  a.offsets = seq->seq_offsets;
+  a.ts = seq->timestamps;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.stride = row_stride;
+  a.d_out = d_out;
+  a.d_stride = hq;
+  a.rab_pos = rab_pos;
+  a.rab_time = rab_time;
+  a.pos_buckets = dims->pos_buckets;
+  a.time_buckets = dims->time_buckets;
+  a.rab_per_head = dims->rab_heads == dims->num_heads && dims->num_heads > 1;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.g_stride = hq;
+  a.work = lw.work;
+  a.n_work = lw.n_work;
+  a.num_heads = dims->num_heads;
+  hipStream_t sst = (hipStream_t)stream;
+  hipError_t e = launch_schedule(seq->seq_offsets, nullptr, seq->batch, 0, seq->max_seq_len, 0,
+                                 lw.work, lw.n_work, sst);
+  if (e != hipSuccess) return hip_fail(e);
+  const int64_t cap = attn_work_capacity(seq->batch, seq->total_tokens);
+  e = launch_attention_bwd(a, dims->dqk, cap, sst);
+  if (e != hipSuccess) return hip_fail(e);
+  return HSTU_OK;
+}
+
 hstu_status_t hstu_attn_fwd(const hstu_dims_t *dims, const float *rab_pos, const float *rab_time,
                             const hstu_jagged_t *seq, const uint16_t *q, const uint16_t *k,
                             const uint16_t *v, int64_t row_stride, const hstu_prefix_t *prefix,

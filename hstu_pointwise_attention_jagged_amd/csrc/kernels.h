@@ -38,6 +38,27 @@ struct AttnArgs {
   int mask;                 // 0 causal, 1 self-only
 };
 
+// Attention gradients (attention_bwd.hip), causal mask, no prefix.
+struct AttnBwdArgs {
+  const int32_t *offsets;     // [B+1]
+  const int32_t *ts;          // [T] or nullptr
+  const uint16_t *q, *k, *v;  // fp16 rows, `stride` elements apart
+  int64_t stride;
+  const float *d_out;         // upstream gradient of the attention output [T][H*dv]
+  int64_t d_stride;
+  const float *rab_pos;       // [rab_heads][pos_buckets] or nullptr
+  const float *rab_time;      // [rab_heads][time_buckets] or nullptr
+  int pos_buckets, time_buckets, rab_per_head;
+  float *dq, *dk, *dv;        // [T][H*dh] each
+  int64_t g_stride;
+  const int32_t *work;        // [2*cap] (b, 128-row tile) pairs
+  const int32_t *n_work;      // [1]
+  int num_heads;
+};
+
+// dQ, dK, dV for every row (two kernels; tiles of 128 rows from the schedule's list).
+hipError_t launch_attention_bwd(const AttnBwdArgs &a, int dh, int64_t cap, hipStream_t stream);
+
 constexpr int kAttnBlockMMin = 128;  // query rows per workgroup: 128, or 256 for long rows
 constexpr int kAttnBlockN = 64;      // keys per LDS stage
 

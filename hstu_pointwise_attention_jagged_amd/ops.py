@@ -21,7 +21,7 @@ __all__ = ["HSTUError", "LayerDims", "DeviceWeights", "DeviceJagged", "hstu_laye
            "hstu_attn_workspace_bytes", "hstu_mfalcon_workspace_bytes", "hstu_validate_jagged",
            "hstu_sl_workspace_bytes", "hstu_stochastic_length", "hstu_stack_fwd",
            "hstu_stack_fwd_mfalcon", "hstu_stack_workspace_bytes",
-           "hstu_stack_mfalcon_workspace_bytes", "profile_enable", "profile_reset",
+           "hstu_stack_mfalcon_workspace_bytes", "hstu_attn_bwd", "profile_enable", "profile_reset",
            "profile_collect"]
 
 
@@ -365,6 +365,34 @@ def hstu_stochastic_length(raw: DeviceJagged, u_keep: torch.Tensor, keys: torch.
                                     ws.numel() * ws.element_size(), _stream(stream))
     _raise(st, "hstu_stochastic_length")
     return kept, new_off, new_ts, x_out
+
+
+def hstu_attn_bwd(dims: LayerDims, seq: DeviceJagged, q: torch.Tensor, k: torch.Tensor,
+                  v: torch.Tensor, d_out: torch.Tensor, *, row_stride: Optional[int] = None,
+                  rab_pos: Optional[torch.Tensor] = None, rab_time: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, stream=None):
+    """Gradients of the causal attention for d_out (fp32 [T][H*dv]).  Returns (dq, dk, dv),
+    fp32 [T][H*dh] each."""
+    lib = _lib.load()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.float16 or not t.is_cuda:
+            raise TypeError(f"{n}: expected an fp16 device tensor")
+    _check(d_out, torch.float32, "d_out")
+    if row_stride is None:
+        row_stride = q.stride(0)
+    T = seq.total_tokens
+    dq = torch.empty((T, dims.hdv), dtype=torch.float32, device=q.device)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(dq)
+    d, s = dims.c(), seq.c()
+    need = int(lib.hstu_attn_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(s)))
+    ws = _workspace(need, q.device, workspace)
+    st = lib.hstu_attn_bwd(ctypes.byref(d), _ptr(rab_pos), _ptr(rab_time), ctypes.byref(s),
+                           _ptr(q), _ptr(k), _ptr(v), int(row_stride), _ptr(d_out), _ptr(dq),
+                           _ptr(dk), _ptr(dv), _ptr(ws), ws.numel() * ws.element_size(),
+                           _stream(stream))
+    _raise(st, "hstu_attn_bwd")
+    return dq, dk, dv
 
 
 def hstu_validate_jagged(seq: DeviceJagged, stream=None) -> bool:

@@ -237,6 +237,30 @@ hstu_status_t hstu_stochastic_length(const hstu_jagged_t *raw, const double *u_k
                                      const uint16_t *x_raw, uint16_t *x_out, int64_t row_elems,
                                      void *ws, size_t ws_bytes, void *stream);
 
+/* Workspace (bytes) needed by hstu_attn_bwd; 0 when the arguments are invalid.     */
+size_t hstu_attn_bwd_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_t *seq);
+
+/* Gradients of equation (2) (the causal attention computed by hstu_attn_fwd without a
+ * prefix) for the upstream gradient d_out of its output:
+ *     dA = dO V^T, dS = dA * SiLU'(S) on allowed pairs (0 elsewhere), dQ = dS K,
+ *     dK = dS^T Q, dV = A^T dO,  with S = Q K^T + rab, A = SiLU(S).
+ * The bias tables are inputs only (their gradients are not formed).  Every row of dq,
+ * dk and dv is written; the result is deterministic (no atomics).
+ *   q, k, v    (device) fp16, as for hstu_attn_fwd (row_stride elements between rows)
+ *   d_out      (device) fp32 [T][H*dv]; rounded to fp16 for the matrix products
+ *   dq, dk, dv (device) fp32 [T][H*dqk], [T][H*dqk], [T][H*dv]
+ *   ws         >= hstu_attn_bwd_workspace_bytes(dims, seq)
+ * The caller owns every buffer.  HSTU_ERR_INVALID_ARG for a null or misaligned pointer,
+ * an output equal to another output or to an input, or row_stride < H*dqk or not a
+ * multiple of 8; HSTU_ERR_UNSUPPORTED for dqk != dv or dqk not in {32, 64, 128};
+ * HSTU_ERR_WORKSPACE for a short or misaligned workspace.  An empty batch returns HSTU_OK
+ * without launching anything.                                                       */
+hstu_status_t hstu_attn_bwd(const hstu_dims_t *dims, const float *rab_pos,
+                            const float *rab_time, const hstu_jagged_t *seq,
+                            const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                            int64_t row_stride, const float *d_out, float *dq, float *dk,
+                            float *dv, void *ws, size_t ws_bytes, void *stream);
+
 /* Debug check of device offsets: off[0] == 0, non-decreasing, off[B] == total_tokens,
  * every length <= max_seq_len.  Synchronises the stream.  Returns HSTU_OK or
  * HSTU_ERR_INVALID_ARG.                                                              */

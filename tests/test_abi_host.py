@@ -220,3 +220,25 @@ def test_stack_bad_arguments_rejected(lib):
     assert lib.hstu_stack_fwd_mfalcon(ctypes.byref(d), 2, w, ctypes.byref(seq), FAKE,
                                       ctypes.byref(cand), FAKE, FAKE + 4096, FAKE, FAKE, 1 << 30,
                                       None) == _lib.HSTU_ERR_INVALID_ARG  # batch sizes differ
+
+
+def test_attn_bwd_argument_checks(lib):
+    d, s = _dims(), _seq()
+    need = lib.hstu_attn_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(s))
+    assert need > 0
+
+    def call(dims=d, q=FAKE, dout=FAKE + 8192, dq=FAKE + 16384, dk=FAKE + 32768, dv=FAKE + 65536,
+             stride=192, ws=FAKE, ws_bytes=need, seq=s):
+        return lib.hstu_attn_bwd(ctypes.byref(dims), None, None, ctypes.byref(seq), q, q + 128,
+                                 q + 256, stride, dout, dq, dk, dv, ws, ws_bytes, None)
+    assert call(stride=32) == _lib.HSTU_ERR_INVALID_ARG          # smaller than H*dqk
+    assert call(stride=196) == _lib.HSTU_ERR_INVALID_ARG         # not a multiple of 8
+    assert call(dq=None) == _lib.HSTU_ERR_INVALID_ARG
+    assert call(dout=FAKE + 4) == _lib.HSTU_ERR_INVALID_ARG      # misaligned
+    assert call(dk=FAKE + 16384) == _lib.HSTU_ERR_INVALID_ARG    # dk aliases dq
+    assert call(dv=FAKE + 8192) == _lib.HSTU_ERR_INVALID_ARG     # dv aliases d_out
+    assert call(ws_bytes=need - 1) == _lib.HSTU_ERR_WORKSPACE
+    assert call(dims=_dims(dv=64)) == _lib.HSTU_ERR_UNSUPPORTED
+    assert call(dims=_dims(dqk=48, dv=48)) == _lib.HSTU_ERR_UNSUPPORTED
+    # empty batch: nothing to do, nothing launched
+    assert call(seq=_lib.Jagged(0, 0, 0, FAKE, None), ws=None, ws_bytes=0) == _lib.HSTU_OK
