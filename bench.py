@@ -8,6 +8,9 @@ per layer.  Inputs and weights are resident in HBM before the timed region.
 
 Prints one JSON line on stdout; progress goes to stderr.
 
+Besides the step, the line carries separate measurements of Stochastic Length, M-FALCON
+serving and the attention gradients (hstu_attn_bwd).
+
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers 24] [--no-cpu-baseline]
 """
 
@@ -162,6 +165,55 @@ def sl_measure(torch, np, ops, dev, wl, reps=20):
                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(alg / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                          "algorithmic_bytes": alg}}
+
+
+def bwd_measure(torch, np, ops, dev, wl, reps=10):
+    """Attention gradients (hstu_attn_bwd: dQ, dK, dV) on the 8 x 8192-token batch, 8 heads
+    of 128, causal with positional + log-time bias.  Q, K, V are fp16 N(0.2, 0.6^2), dO
+    fp32 N(0, 1), drawn on the device from a fixed seed.  Algorithmic FLOPs: five
+    products per allowed pair and head (S, dA, dQ, dK, dV), 2 dh each, i.e.
+    10 dh H n (n + 1) / 2 per sequence; the kernels recompute S and dA once more (one
+    pass per side), which is not counted."""
+    w = wl.config(2)
+    d = w.dims
+    H, dh = d.num_heads, d.dqk
+    T = w.seq.total
+    seq = dev.jagged_of(w.seq)
+    dims = dev.dims_of(d)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(3003)
+    qkv = (0.2 + 0.6 * torch.randn((T, 3 * H * dh), generator=gen, device="cuda")).half()
+    g = torch.randn((T, H * dh), generator=gen, device="cuda")
+    rp, rt = dev.f32_tensor(w.weights.rab_pos), dev.f32_tensor(w.weights.rab_time)
+    hq = H * dh
+    stream = torch.cuda.current_stream()
+    ws = torch.empty(int(ops.hstu_attn_bwd_workspace_bytes(dims, seq)), dtype=torch.uint8,
+                     device="cuda")
+
+    def run():
+        return ops.hstu_attn_bwd(dims, seq, qkv[:, :hq], qkv[:, hq:2 * hq], qkv[:, 2 * hq:], g,
+                                 row_stride=qkv.stride(0), rab_pos=rp, rab_time=rt, workspace=ws,
+                                 stream=stream)
+
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = sum(10 * dh * H * int(n) * (int(n) + 1) // 2 for n in w.seq.lengths)
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": f"attention gradients dQ, dK, dV, 8 x 8192 tokens, {H} heads x {dh}, "
+                        "causal, rab pos+time",
+            "ms": round(ms, 4), "algorithmic_flops": flops,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_MFMA_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_MFMA_TFLOPS, 4)},
+            "note": "time of one hstu_attn_bwd call (schedule, dQ kernel, dK/dV kernel), "
+                    "HIP events on the launch stream"}
 
 
 def mfalcon_measure(torch, np, ops, dev, wl, n_layers=4, bm=1024, reps=3):
@@ -364,6 +416,8 @@ def main():
     out["stochastic_length"] = sl_measure(torch, np, ops, dev, wl)
     log("M-FALCON serving through a 4-layer stack, micro-batches of 1024 and 128 per user")
     out["mfalcon_serving"] = [mfalcon_measure(torch, np, ops, dev, wl, bm=bm) for bm in (1024, 128)]
+    log("attention gradients (dQ, dK, dV) on the 8 x 8192 batch")
+    out["attention_backward"] = bwd_measure(torch, np, ops, dev, wl)
     if not args.no_cpu_baseline:
         log("cpu baseline: fp64 oracle, one layer on two 8192-token sequences")
         out["cpu_baseline"] = cpu_baseline(w, args.layers)

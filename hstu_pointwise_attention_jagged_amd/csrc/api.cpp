@@ -461,9 +461,16 @@ hstu_status_t hstu_stack_fwd_mfalcon(const hstu_dims_t *dims, int32_t n_layers,
   return HSTU_OK;
 }
 
+// The schedule and block statistics of the forward, then the fp16 copy of d_out and the
+// word that holds max |d_out|.
+static size_t attn_bwd_ws_bytes(const hstu_dims_t *d, const hstu_jagged_t *s) {
+  return attn_ws_bytes(s, nullptr) +
+         align_up((size_t)s->total_tokens * d->num_heads * d->dv * sizeof(uint16_t)) + kAlign;
+}
+
 size_t hstu_attn_bwd_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_t *seq) {
   if (check_attn_dims(dims) != HSTU_OK || check_seq(seq) != HSTU_OK) return 0;
-  return attn_ws_bytes(seq, nullptr);
+  return attn_bwd_ws_bytes(dims, seq);
 }
 
 hstu_status_t hstu_attn_bwd(const hstu_dims_t *dims, const float *rab_pos, const float *rab_time,
@@ -494,12 +501,17 @@ hstu_status_t hstu_attn_bwd(const hstu_dims_t *dims, const float *rab_pos, const
     }
   }
   if (seq->batch == 0 || seq->total_tokens == 0) return HSTU_OK;
-  if ((st = check_ws(ws, ws_bytes, attn_ws_bytes(seq, nullptr))) != HSTU_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, attn_bwd_ws_bytes(dims, seq))) != HSTU_OK) return st;
   if (attn_block_m(seq->max_seq_len) != 128) return HSTU_ERR_UNSUPPORTED;  // the kernels' tile
 
   LayerWs lw{};
   carve_attn((char *)ws, seq, nullptr, lw);
+  char *tail = (char *)ws + attn_ws_bytes(seq, nullptr);
   AttnBwdArgs a{};
+  a.d_h = (uint16_t *)tail;
+  a.d_max = (uint32_t *)(tail + align_up((size_t)seq->total_tokens * hq * sizeof(uint16_t)));
+  const bool use_time = rab_time != nullptr && seq->timestamps != nullptr;
+  a.stat = use_time ? lw.kstat : nullptr;
   a.offsets = seq->seq_offsets;
   a.ts = seq->timestamps;
   a.q = q;
@@ -524,8 +536,13 @@ hstu_status_t hstu_attn_bwd(const hstu_dims_t *dims, const float *rab_pos, const
   hipError_t e = launch_schedule(seq->seq_offsets, nullptr, seq->batch, 0, seq->max_seq_len, 0,
                                  lw.work, lw.n_work, sst);
   if (e != hipSuccess) return hip_fail(e);
+  if (use_time) {
+    e = launch_block_stats(seq->timestamps, seq->seq_offsets, seq->batch, seq->max_seq_len,
+                           lw.kstat, sst);
+    if (e != hipSuccess) return hip_fail(e);
+  }
   const int64_t cap = attn_work_capacity(seq->batch, seq->total_tokens);
-  e = launch_attention_bwd(a, dims->dqk, cap, sst);
+  e = launch_attention_bwd(a, dims->dqk, cap, seq->total_tokens, sst);
   if (e != hipSuccess) return hip_fail(e);
   return HSTU_OK;
 }

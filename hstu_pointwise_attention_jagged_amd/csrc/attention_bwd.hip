@@ -7,19 +7,28 @@
 //   dV = A^T dO,  SiLU'(x) = sigma(x) (1 + x (1 - sigma(x))).
 //
 // No softmax, so no row statistics: each gradient is a plain sum over pairs, computed
-// by two kernels without atomics (deterministic):
-//  * attn_bwd_dq_kernel: a workgroup of 4 waves owns 128 query rows (32 per wave, their
-//    Q and dO fragments in registers) and streams 32-key tiles of K and V through LDS.
-//    Per block: S^T = K Q^T and dA^T = V dO^T (MFMA, transposed so each lane holds 16
-//    keys of one query), dS^T elementwise, then dQ^T += K^T dS^T, with the K^T operand
-//    read from row-major K by the transposing LDS read.  24 MFMAs per 32 x 32 block.
-//  * attn_bwd_dkv_kernel: a workgroup owns 128 key rows (K and V fragments in registers)
-//    and streams 32-query tiles of Q and dO.  Per block: S = Q K^T and dA = dO V^T (each
-//    lane holds 16 queries of one key), A and dS elementwise, then dV^T += dO^T A and
-//    dK^T += Q^T dS through transposing reads of Q and dO.  32 MFMAs per block.
-// Both kernels walk the (sequence, 128-row tile) list of the forward's schedule.
-// Operands are fp16 (Q, K, V as the forward takes them; dO, A and dS rounded to fp16),
-// accumulation fp32; the bias is formed per element from the two tables.
+// without atomics on the gradients (deterministic) in these launches:
+//  * prep: max |dO| over the batch, then dO x 2^-e in fp16, with 2^e the power of two
+//    that brings that maximum into [0.5, 1).  Every gradient is linear in dO, so the
+//    kernels multiply their results by 2^e (exact); tiny training gradients keep their
+//    fp16 precision and dA, dS stay far from the fp16 range limit.
+//  * attn_bwd_dq_kernel: a workgroup of 4 waves owns 128 query rows (32 per wave, their Q
+//    and dO fragments in registers) and streams key tiles of K and V through LDS.  Per
+//    32 x 32 block: S^T = K Q^T and dA^T = V dO^T (each lane holds 16 keys of one query),
+//    dS^T elementwise, then dQ^T += K^T dS^T with the K^T operand taken from row-major K
+//    by the transposing LDS read.
+//  * attn_bwd_dkv_kernel: a workgroup owns 128 key rows (K fragments in registers, V rows
+//    in LDS) and streams 32-query tiles of Q and dO.  Per block: S = Q K^T and dA = dO V^T
+//    (each lane holds 16 queries of one key), A and dS elementwise, then dV^T += dO^T A
+//    and dK^T += Q^T dS through transposing reads of Q and dO.
+// Both kernels load the next tile into registers while the current one is computed.  The
+// bias of a 32 x 32 block is classified once per wave from the blocks' timestamp ranges
+// and position gap (the log2 time bucket is monotone in the gap): one value for the whole
+// block (CONST), two values split by a time threshold (TWO), or per element (GENERAL,
+// only near the diagonal or across several time buckets).  Operands are fp16 (Q, K, V
+// as the forward takes them; dO, A and dS rounded to fp16), accumulation fp32.
+#include <stdint.h>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -27,12 +36,19 @@ namespace hstu {
 
 namespace {
 
-constexpr int kBwdRows = 32;      // rows per streamed tile
-constexpr int kBwdWaves = 4;
-constexpr int kBwdThreads = 64 * kBwdWaves;
-constexpr int kBwdMaxPos = 1024;
-constexpr int kBwdMaxTime = 64;
-constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kOwnRows = 32 * kWaves;  // rows a workgroup owns: the schedule's tile
+// keys per tile streamed by the dQ kernel (32 at DH = 128, where the prefetch registers
+// of a 64-key tile would not fit beside the wave's Q and dO fragments)
+template <int DH>
+constexpr int dq_keys() { return DH == 128 ? 32 : 64; }
+constexpr int kDkvQueries = 32;        // queries per tile streamed by the dK/dV kernel
+constexpr int kMaxPos = 1024;
+constexpr int kMaxTime = 64;
+constexpr float kNegLog2e = -1.4426950408889634f;
+
+enum BlockKind { KIND_CONST = 0, KIND_TWO = 1, KIND_GENERAL = 2 };
 
 // ds_read_b64_tr_b16: in each 16-lane group, lane 4 j + q gives the address of row j at
 // features 4 q .. 4 q + 3 of a 16-feature slice and receives rows 0..3 of feature lane % 16
@@ -43,7 +59,7 @@ __device__ __forceinline__ u32x2 tr_read(const unsigned char *p) {
 }
 
 // LDS pitches: row copies (16-byte fragment reads of one chunk across 32 rows) and
-// transposed-read copies (4 rows x 4 feature groups per 16 lanes) of a 32-row tile
+// transposed-read copies (4 rows x 4 feature groups per 16 lanes)
 template <int DH>
 struct BwdLayout {
   static constexpr int ROWP = DH * 2 + 16;
@@ -53,45 +69,38 @@ struct BwdLayout {
   static constexpr int CPR = DH / 8;   // 16-byte chunks per row
 };
 
-__device__ __forceinline__ void silu_and_grad(float s, float &a, float &g) {
-  const float sig = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * s));
-  a = s * sig;
-  g = sig * (1.0f + s * (1.0f - sig));
-}
+// Registers of one tile of ROWS rows of an fp16 matrix, spread over the workgroup:
+// chunk tid + 256 c for c < N.  Rows at or past the sequence end read as zero.
+template <int DH, int ROWS>
+struct TileRegs {
+  static constexpr int CHUNKS = ROWS * BwdLayout<DH>::CPR;
+  static constexpr int N = (CHUNKS + kThreads - 1) / kThreads;
+  u32x4 v[N];
 
-// Rows [r0, r0 + 32) of a fp16 matrix (row pitch `stride` elements, head column offset
-// already applied) into an LDS row copy and a transposed-read copy; rows >= n are zero.
-template <int DH>
-__device__ __forceinline__ void stage_f16(const uint16_t *src, int64_t stride, int r0, int n,
-                                          unsigned char *row_copy, unsigned char *tr_copy) {
-  using L = BwdLayout<DH>;
-  for (int c = threadIdx.x; c < kBwdRows * L::CPR; c += kBwdThreads) {
-    const int r = c / L::CPR, ch = c % L::CPR;
-    u32x4 v = {0, 0, 0, 0};
-    if (r0 + r < n) v = *reinterpret_cast<const u32x4 *>(src + (int64_t)(r0 + r) * stride + ch * 8);
-    if (row_copy) *reinterpret_cast<u32x4 *>(row_copy + r * L::ROWP + ch * 16) = v;
-    if (tr_copy) *reinterpret_cast<u32x4 *>(tr_copy + r * L::TRP + ch * 16) = v;
-  }
-}
-
-// Same for an fp32 matrix, rounded to fp16 (saturating)
-template <int DH>
-__device__ __forceinline__ void stage_f32(const float *src, int64_t stride, int r0, int n,
-                                          unsigned char *row_copy, unsigned char *tr_copy) {
-  using L = BwdLayout<DH>;
-  for (int c = threadIdx.x; c < kBwdRows * L::CPR; c += kBwdThreads) {
-    const int r = c / L::CPR, ch = c % L::CPR;
-    u32x4 v = {0, 0, 0, 0};
-    if (r0 + r < n) {
-      const f32x4 a = *reinterpret_cast<const f32x4 *>(src + (int64_t)(r0 + r) * stride + ch * 8);
-      const f32x4 b = *reinterpret_cast<const f32x4 *>(src + (int64_t)(r0 + r) * stride + ch * 8 + 4);
-      v = u32x4{pack_f16_sat(a[0], a[1]), pack_f16_sat(a[2], a[3]), pack_f16_sat(b[0], b[1]),
-                pack_f16_sat(b[2], b[3])};
+  __device__ __forceinline__ void load(const uint16_t *base, int64_t stride, int r0, int n) {
+    constexpr int CPR = BwdLayout<DH>::CPR;
+#pragma unroll
+    for (int c = 0; c < N; ++c) {
+      const int idx = threadIdx.x + c * kThreads;
+      const int r = idx / CPR, ch = idx % CPR;
+      v[c] = u32x4{0, 0, 0, 0};
+      if (idx < CHUNKS && r0 + r < n)
+        v[c] = *reinterpret_cast<const u32x4 *>(base + (int64_t)(r0 + r) * stride + ch * 8);
     }
-    if (row_copy) *reinterpret_cast<u32x4 *>(row_copy + r * L::ROWP + ch * 16) = v;
-    if (tr_copy) *reinterpret_cast<u32x4 *>(tr_copy + r * L::TRP + ch * 16) = v;
   }
-}
+  // into a row copy and/or a transposed-read copy
+  __device__ __forceinline__ void store(unsigned char *row_copy, unsigned char *tr_copy) const {
+    using L = BwdLayout<DH>;
+#pragma unroll
+    for (int c = 0; c < N; ++c) {
+      const int idx = threadIdx.x + c * kThreads;
+      if (idx >= CHUNKS) break;
+      const int r = idx / L::CPR, ch = idx % L::CPR;
+      if (row_copy) *reinterpret_cast<u32x4 *>(row_copy + r * L::ROWP + ch * 16) = v[c];
+      if (tr_copy) *reinterpret_cast<u32x4 *>(tr_copy + r * L::TRP + ch * 16) = v[c];
+    }
+  }
+};
 
 // Fragment of row (lane % 32) of a row copy for k-step ks: 8 features 16 ks + 8 (lane / 32)
 template <int DH>
@@ -101,7 +110,7 @@ __device__ __forceinline__ f16x8 row_frag(const unsigned char *row_copy, int lan
                                                     (2 * ks + (lane >> 5)) * 16));
 }
 
-// Transposed operand for feature tile f and k-step s2 of a 32-row tile: rows
+// Transposed operand for feature tile f and k-step s2 of a 32-row block: rows
 // 16 s2 + 8 (e / 4) + 4 (lane / 32) + e % 4 (e = 0..7) of feature 32 f + lane % 32
 template <int DH>
 __device__ __forceinline__ f16x8 tr_frag(const unsigned char *tr_copy, int lane, int f, int s2) {
@@ -113,25 +122,28 @@ __device__ __forceinline__ f16x8 tr_frag(const unsigned char *tr_copy, int lane,
   return as_f16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 
-// fp32 row of a register fragment: 8 features 16 ks + 8 (lane / 32) of `row`, as fp16
-__device__ __forceinline__ f16x8 f32_row_frag(const float *rowp, bool ok, int lane, int ks) {
-  if (!ok) return as_f16x8(u32x4{0, 0, 0, 0});
-  const float *p = rowp + 16 * ks + 8 * (lane >> 5);
-  const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
-  const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
-  return as_f16x8(u32x4{pack_f16_sat(a[0], a[1]), pack_f16_sat(a[2], a[3]),
-                        pack_f16_sat(b[0], b[1]), pack_f16_sat(b[2], b[3])});
-}
-
 __device__ __forceinline__ f16x8 f16_row_frag(const uint16_t *rowp, bool ok, int lane, int ks) {
   if (!ok) return as_f16x8(u32x4{0, 0, 0, 0});
   return as_f16x8(*reinterpret_cast<const u32x4 *>(rowp + 16 * ks + 8 * (lane >> 5)));
 }
 
-// packs accumulator values v[8 s2 .. 8 s2 + 7] into the fp16 k-step operand
+// packs accumulator values v[0..7] into the fp16 k-step operand
 __device__ __forceinline__ f16x8 pack8(const float *v) {
   return as_f16x8(u32x4{pack_f16(v[0], v[1]), pack_f16(v[2], v[3]), pack_f16(v[4], v[5]),
                         pack_f16(v[6], v[7])});
+}
+
+// SiLU(s) and SiLU'(s) = sigma + a (1 - sigma), a = s sigma
+__device__ __forceinline__ void silu_and_grad(float s, float &a, float &g) {
+  const float sig = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(kNegLog2e * s));
+  a = s * sig;
+  g = __builtin_fmaf(-a, sig, sig + a);
+}
+
+__device__ __forceinline__ float silu_grad(float s) {
+  float a, g;
+  silu_and_grad(s, a, g);
+  return g;
 }
 
 struct BiasCtx {
@@ -148,15 +160,103 @@ __device__ __forceinline__ float rab(const BiasCtx &c, int qi, int kj, int32_t q
   return x;
 }
 
+// Bias class of the block of queries [q_lo, q_lo + 31] x keys [k_lo, k_lo + 31], given
+// the (min, max) timestamps of its query and key rows.  CONST: every pair takes lo.
+// TWO: a pair takes hi when its gap ts_q - ts_k reaches thr, lo otherwise.  The time
+// bucket is at most 32, so thr = 2^(lower bucket + 1) - 1 fits 32 bits whenever TWO is
+// chosen (the lower bucket is then below the upper one, at most 31).
+struct BlockBias {
+  int kind;
+  float lo, hi;
+  uint32_t thr;
+};
+
+__device__ __forceinline__ BlockBias classify(const BiasCtx &c, int q_lo, int k_lo, int2 tq,
+                                              int2 tk) {
+  BlockBias r;
+  const bool pos_const = !c.use_pos || q_lo - (k_lo + 31) >= c.pos_buckets - 1;
+  int tb_lo = 0, tb_hi = 0;
+  if (c.use_time) {
+    tb_lo = min(time_log2_bucket(tq.x, tk.y), c.time_buckets - 1);
+    tb_hi = min(time_log2_bucket(tq.y, tk.x), c.time_buckets - 1);
+  }
+  r.kind = (!pos_const || tb_hi > tb_lo + 1) ? KIND_GENERAL : (tb_hi == tb_lo ? KIND_CONST : KIND_TWO);
+  const float base = c.use_pos ? c.ptab[c.pos_buckets - 1] : 0.0f;
+  r.lo = base + (c.use_time ? c.ttab[tb_lo] : 0.0f);
+  r.hi = base + (c.use_time ? c.ttab[tb_hi] : 0.0f);
+  r.thr = (uint32_t)(((uint64_t)1 << (tb_lo + 1)) - 1);
+  return r;
+}
+
+// Scale of the fp16 copy of dO: 2^-e with max |dO| = m 2^e, m in [0.5, 1) (e clamped to
+// [-100, 120]); 1 when the maximum is 0 or not finite.  Sets inv to the inverse, 2^e.
+__device__ __forceinline__ float d_scale(const uint32_t *d_max, float &inv) {
+  const float m = __builtin_bit_cast(float, *d_max);
+  if (!(m > 0.0f) || !(m <= 3.402823466e38f)) {
+    inv = 1.0f;
+    return 1.0f;
+  }
+  int e;
+  (void)frexpf(m, &e);
+  e = min(max(e, -100), 120);
+  inv = ldexpf(1.0f, e);
+  return ldexpf(1.0f, -e);
+}
+
+__global__ __launch_bounds__(64) void bwd_clear_kernel(uint32_t *d_max) {
+  if (threadIdx.x == 0) *d_max = 0u;
+}
+
+// max |d_out| over n4 groups of 4 floats: wave maxima of the magnitude bits (ordered as
+// unsigned integers for non-negative floats), then one atomic per wave
+__global__ __launch_bounds__(256) void bwd_absmax_kernel(const float *d_out, int64_t n4,
+                                                         uint32_t *d_max) {
+  uint32_t m = 0u;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    const f32x4 v = reinterpret_cast<const f32x4 *>(d_out)[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m = max(m, __builtin_bit_cast(uint32_t, v[j]) & 0x7fffffffu);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  if ((threadIdx.x & 63) == 0) atomicMax(d_max, m);
+}
+
+__global__ __launch_bounds__(256) void bwd_cast_kernel(const float *d_out, int64_t n4,
+                                                       const uint32_t *d_max, uint16_t *d_h) {
+  float inv;
+  const float sc = d_scale(d_max, inv);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    const f32x4 v = reinterpret_cast<const f32x4 *>(d_out)[i];
+    reinterpret_cast<u32x2 *>(d_h)[i] =
+        u32x2{pack_f16(v[0] * sc, v[1] * sc), pack_f16(v[2] * sc, v[3] * sc)};
+  }
+}
+
+__device__ __forceinline__ void load_tables(const AttnBwdArgs &p, int h, float *ptab, float *ttab,
+                                            BiasCtx &bc) {
+  const int rrow = p.rab_per_head ? h : 0;
+  bc = BiasCtx{ptab, ttab, p.pos_buckets, p.time_buckets, p.rab_pos != nullptr,
+               p.rab_time != nullptr && p.ts != nullptr};
+  if (bc.use_pos)
+    for (int i = threadIdx.x; i < p.pos_buckets; i += kThreads) ptab[i] = p.rab_pos[rrow * p.pos_buckets + i];
+  if (bc.use_time)
+    for (int i = threadIdx.x; i < p.time_buckets; i += kThreads) ttab[i] = p.rab_time[rrow * p.time_buckets + i];
+}
+
+// -------------------------------------------------------------------------------------
+// dQ: queries owned, keys streamed
+// -------------------------------------------------------------------------------------
 template <int DH>
-__global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(AttnBwdArgs p) {
+__global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(AttnBwdArgs p) {
   using L = BwdLayout<DH>;
   constexpr int KS = L::KS, FT = L::FT;
-  __shared__ __attribute__((aligned(16))) unsigned char k_row[kBwdRows * L::ROWP];
-  __shared__ __attribute__((aligned(16))) unsigned char k_tr[kBwdRows * L::TRP];
-  __shared__ __attribute__((aligned(16))) unsigned char v_row[kBwdRows * L::ROWP];
-  __shared__ int32_t k_ts[kBwdRows];
-  __shared__ float ptab[kBwdMaxPos], ttab[kBwdMaxTime];
+  constexpr int TK = dq_keys<DH>();
+  __shared__ __attribute__((aligned(16))) unsigned char k_row[TK * L::ROWP];
+  __shared__ __attribute__((aligned(16))) unsigned char k_tr[TK * L::TRP];
+  __shared__ __attribute__((aligned(16))) unsigned char v_row[TK * L::ROWP];
+  __shared__ int32_t k_ts[TK];
+  __shared__ float ptab[kMaxPos], ttab[kMaxTime];
 
   const int item = blockIdx.x;
   if (item >= *p.n_work) return;
@@ -165,90 +265,131 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(AttnBwdArgs
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lrow = lane & 31, half = lane >> 5;
   const int s0 = p.offsets[b], n = p.offsets[b + 1] - s0;
-  const int rrow = p.rab_per_head ? h : 0;
-  BiasCtx bc{ptab, ttab, p.pos_buckets, p.time_buckets, p.rab_pos != nullptr,
-             p.rab_time != nullptr && p.ts != nullptr};
-  if (bc.use_pos)
-    for (int i = tid; i < p.pos_buckets; i += kBwdThreads) ptab[i] = p.rab_pos[rrow * p.pos_buckets + i];
-  if (bc.use_time)
-    for (int i = tid; i < p.time_buckets; i += kBwdThreads) ttab[i] = p.rab_time[rrow * p.time_buckets + i];
+  BiasCtx bc;
+  load_tables(p, h, ptab, ttab, bc);
 
-  const int q0 = qt * 128;
-  const int qbase = q0 + wave * 32;
+  const int q0 = qt * kOwnRows;
+  const int qbase = q0 + wave * 32;  // this wave's 32 queries
+  const bool wave_rows = qbase < n;
   const int qi = qbase + lrow;
   const bool q_ok = qi < n;
   const int32_t qts = bc.use_time ? p.ts[s0 + (q_ok ? qi : 0)] : 0;
+  const int2 tq = (bc.use_time && wave_rows) ? p.stat[s0 + qbase] : int2{0, 0};
   f16x8 qf[KS], dof[KS];
   {
     const uint16_t *qr = p.q + (int64_t)(s0 + qi) * p.stride + h * DH;
-    const float *dr = p.d_out + (int64_t)(s0 + qi) * p.d_stride + h * DH;
+    const uint16_t *dr = p.d_h + (int64_t)(s0 + qi) * p.d_stride + h * DH;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       qf[ks] = f16_row_frag(qr, q_ok, lane, ks);
-      dof[ks] = f32_row_frag(dr, q_ok, lane, ks);
+      dof[ks] = f16_row_frag(dr, q_ok, lane, ks);
     }
   }
   f32x16 acc[FT];
 #pragma unroll
   for (int f = 0; f < FT; ++f) acc[f] = f32x16{};
 
-  const int k_end = min(n, q0 + 128);  // keys j <= i < q0 + 128
-  for (int j0 = 0; j0 < k_end; j0 += kBwdRows) {
+  const uint16_t *kbase_p = p.k + (int64_t)s0 * p.stride + h * DH;
+  const uint16_t *vbase_p = p.v + (int64_t)s0 * p.stride + h * DH;
+  const int k_end = min(n, q0 + kOwnRows);  // keys j <= i < q0 + 128
+  const int n_tiles = (k_end + TK - 1) / TK;
+  TileRegs<DH, TK> rk, rv;
+  int32_t rts = 0;
+  auto prefetch = [&](int j0) __attribute__((always_inline)) {
+    rk.load(kbase_p, p.stride, j0, n);
+    rv.load(vbase_p, p.stride, j0, n);
+    if (tid < TK) rts = (bc.use_time && j0 + tid < n) ? p.ts[s0 + j0 + tid] : 0;
+  };
+  prefetch(0);
+  for (int t = 0; t < n_tiles; ++t) {
+    const int j0 = t * TK;
     __syncthreads();  // the previous tile is no longer read (and the tables are written)
-    stage_f16<DH>(p.k + (int64_t)s0 * p.stride + h * DH, p.stride, j0, n, k_row, k_tr);
-    stage_f16<DH>(p.v + (int64_t)s0 * p.stride + h * DH, p.stride, j0, n, v_row, nullptr);
-    if (tid < kBwdRows) k_ts[tid] = (bc.use_time && j0 + tid < n) ? p.ts[s0 + j0 + tid] : 0;
+    rk.store(k_row, k_tr);
+    rv.store(v_row, nullptr);
+    if (tid < TK) k_ts[tid] = rts;
     __syncthreads();
-    if (j0 > qbase + 31) continue;  // the whole tile is after this wave's queries
-    // S^T (bias first) and dA^T; lane: query lrow, keys 8 (i / 4) + 4 half + i % 4
-    f32x16 s, da = f32x16{};
+    if (t + 1 < n_tiles) prefetch(j0 + TK);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kj = j0 + 8 * (i >> 2) + 4 * half + (i & 3);
-      s[i] = rab(bc, qi, kj, qts, k_ts[8 * (i >> 2) + 4 * half + (i & 3)]);
-    }
+    for (int blk = 0; blk < TK / 32; ++blk) {
+      const int kb = j0 + 32 * blk;
+      if (!wave_rows || kb > qbase + 31 || kb >= n) continue;  // uniform per wave
+      const unsigned char *kr = k_row + blk * 32 * L::ROWP;
+      const unsigned char *ktr = k_tr + blk * 32 * L::TRP;
+      const unsigned char *vr = v_row + blk * 32 * L::ROWP;
+      const int32_t *kts = k_ts + blk * 32 + 4 * half;
+      const int2 tk = bc.use_time ? p.stat[s0 + kb] : int2{0, 0};
+      const BlockBias bb = classify(bc, qbase, kb, tq, tk);
+      // S^T with its bias, dA^T; lane: query lrow, keys 8 (i / 4) + 4 half + i % 4
+      f32x16 s, da = f32x16{};
+      if (bb.kind == KIND_CONST) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      s = mfma32_f16(row_frag<DH>(k_row, lane, ks), qf[ks], s);
-      da = mfma32_f16(row_frag<DH>(v_row, lane, ks), dof[ks], da);
-    }
-    float ds[16];
+        for (int i = 0; i < 16; ++i) s[i] = bb.lo;
+      } else if (bb.kind == KIND_TWO) {
+        const int64_t lim = (int64_t)qts - (int64_t)bb.thr + 1;  // hi when ts_k < lim
+        const int32_t klim = (int32_t)(lim < (int64_t)INT32_MIN ? (int64_t)INT32_MIN : lim);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kj = j0 + 8 * (i >> 2) + 4 * half + (i & 3);
-      float a, g;
-      silu_and_grad(s[i], a, g);
-      ds[i] = (q_ok && kj <= qi) ? da[i] * g : 0.0f;
-    }
-    // dQ^T += K^T dS^T over the tile's 32 keys
+        for (int i = 0; i < 16; ++i) s[i] = kts[8 * (i >> 2) + (i & 3)] < klim ? bb.hi : bb.lo;
+      } else {
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const f16x8 bop = pack8(ds + 8 * s2);
+        for (int i = 0; i < 16; ++i)
+          s[i] = rab(bc, qi, kb + 8 * (i >> 2) + 4 * half + (i & 3), qts, kts[8 * (i >> 2) + (i & 3)]);
+      }
 #pragma unroll
-      for (int f = 0; f < FT; ++f) acc[f] = mfma32_f16(tr_frag<DH>(k_tr, lane, f, s2), bop, acc[f]);
+      for (int ks = 0; ks < KS; ++ks) {
+        s = mfma32_f16(row_frag<DH>(kr, lane, ks), qf[ks], s);
+        da = mfma32_f16(row_frag<DH>(vr, lane, ks), dof[ks], da);
+      }
+      float ds[16];
+      if (kb + 31 > qbase) {  // straddles the diagonal: keys after the query are masked
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kj = kb + 8 * (i >> 2) + 4 * half + (i & 3);
+          ds[i] = kj <= qi ? da[i] * silu_grad(s[i]) : 0.0f;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ds[i] = da[i] * silu_grad(s[i]);
+      }
+      // dQ^T += K^T dS^T over the block's 32 keys
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const f16x8 bop = pack8(ds + 8 * s2);
+#pragma unroll
+        for (int f = 0; f < FT; ++f) acc[f] = mfma32_f16(tr_frag<DH>(ktr, lane, f, s2), bop, acc[f]);
+      }
     }
   }
   if (q_ok) {
+    float inv;
+    (void)d_scale(p.d_max, inv);
     float *orow = p.dq + (int64_t)(s0 + qi) * p.g_stride + h * DH + half * 4;
 #pragma unroll
     for (int f = 0; f < FT; ++f)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
         *reinterpret_cast<f32x4 *>(orow + f * 32 + g * 8) =
-            f32x4{acc[f][4 * g], acc[f][4 * g + 1], acc[f][4 * g + 2], acc[f][4 * g + 3]};
+            f32x4{acc[f][4 * g] * inv, acc[f][4 * g + 1] * inv, acc[f][4 * g + 2] * inv,
+                  acc[f][4 * g + 3] * inv};
   }
 }
 
+// -------------------------------------------------------------------------------------
+// dK, dV: keys owned, queries streamed
+// -------------------------------------------------------------------------------------
+// At DH = 128 the dK and dV accumulators (128 registers) and the K fragments take one
+// workgroup per CU (up to 512 registers per lane); smaller heads fit two.
 template <int DH>
-__global__ __launch_bounds__(kBwdThreads, DH == 128 ? 1 : 2) void attn_bwd_dkv_kernel(AttnBwdArgs p) {
+__global__ __launch_bounds__(kThreads, DH == 128 ? 1 : 2) void attn_bwd_dkv_kernel(AttnBwdArgs p) {
   using L = BwdLayout<DH>;
   constexpr int KS = L::KS, FT = L::FT;
-  __shared__ __attribute__((aligned(16))) unsigned char q_row[kBwdRows * L::ROWP];
-  __shared__ __attribute__((aligned(16))) unsigned char q_tr[kBwdRows * L::TRP];
-  __shared__ __attribute__((aligned(16))) unsigned char d_row[kBwdRows * L::ROWP];
-  __shared__ __attribute__((aligned(16))) unsigned char d_tr[kBwdRows * L::TRP];
-  __shared__ int32_t q_ts[kBwdRows];
-  __shared__ float ptab[kBwdMaxPos], ttab[kBwdMaxTime];
+  constexpr int TQ = kDkvQueries;
+  __shared__ __attribute__((aligned(16))) unsigned char q_row[TQ * L::ROWP];
+  __shared__ __attribute__((aligned(16))) unsigned char q_tr[TQ * L::TRP];
+  __shared__ __attribute__((aligned(16))) unsigned char d_row[TQ * L::ROWP];
+  __shared__ __attribute__((aligned(16))) unsigned char d_tr[TQ * L::TRP];
+  __shared__ __attribute__((aligned(16))) unsigned char v_own[kOwnRows * L::ROWP];
+  __shared__ int32_t q_ts[TQ];
+  __shared__ float ptab[kMaxPos], ttab[kMaxTime];
 
   const int item = blockIdx.x;
   if (item >= *p.n_work) return;
@@ -259,63 +400,95 @@ __global__ __launch_bounds__(kBwdThreads, DH == 128 ? 1 : 2) void attn_bwd_dkv_k
   const int s0 = p.offsets[b], n = p.offsets[b + 1] - s0;
   // the list is ordered for the query tiles (tile t visits t + 1 key tiles); key tile
   // nt - 1 - t visits as many query tiles, so the reversal keeps the longest items first
-  const int kt = (n + 127) / 128 - 1 - p.work[2 * item + 1];
-  const int rrow = p.rab_per_head ? h : 0;
-  BiasCtx bc{ptab, ttab, p.pos_buckets, p.time_buckets, p.rab_pos != nullptr,
-             p.rab_time != nullptr && p.ts != nullptr};
-  if (bc.use_pos)
-    for (int i = tid; i < p.pos_buckets; i += kBwdThreads) ptab[i] = p.rab_pos[rrow * p.pos_buckets + i];
-  if (bc.use_time)
-    for (int i = tid; i < p.time_buckets; i += kBwdThreads) ttab[i] = p.rab_time[rrow * p.time_buckets + i];
+  const int kt = (n + kOwnRows - 1) / kOwnRows - 1 - p.work[2 * item + 1];
+  BiasCtx bc;
+  load_tables(p, h, ptab, ttab, bc);
 
-  const int k0 = kt * 128;
-  const int kbase = k0 + wave * 32;
+  const int k0 = kt * kOwnRows;
+  const int kbase = k0 + wave * 32;  // this wave's 32 keys
+  const bool wave_rows = kbase < n;
   const int kj = kbase + lrow;
   const bool k_ok = kj < n;
   const int32_t kts = bc.use_time ? p.ts[s0 + (k_ok ? kj : 0)] : 0;
-  f16x8 kf[KS], vf[KS];
+  const int2 tk = (bc.use_time && wave_rows) ? p.stat[s0 + kbase] : int2{0, 0};
+  f16x8 kf[KS];
   {
     const uint16_t *kr = p.k + (int64_t)(s0 + kj) * p.stride + h * DH;
-    const uint16_t *vr = p.v + (int64_t)(s0 + kj) * p.stride + h * DH;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      kf[ks] = f16_row_frag(kr, k_ok, lane, ks);
-      vf[ks] = f16_row_frag(vr, k_ok, lane, ks);
-    }
+    for (int ks = 0; ks < KS; ++ks) kf[ks] = f16_row_frag(kr, k_ok, lane, ks);
   }
+  {  // the workgroup's V rows, read as B operands of dA = dO V^T
+    TileRegs<DH, kOwnRows> rv;
+    rv.load(p.v + (int64_t)s0 * p.stride + h * DH, p.stride, k0, n);
+    rv.store(v_own, nullptr);
+  }
+  const unsigned char *vw = v_own + wave * 32 * L::ROWP;
   f32x16 dk_acc[FT], dv_acc[FT];
 #pragma unroll
   for (int f = 0; f < FT; ++f) dk_acc[f] = dv_acc[f] = f32x16{};
 
-  // queries i >= k0 see these keys; tiles of 32 from the first one
-  for (int i0 = k0; i0 < n; i0 += kBwdRows) {
+  const uint16_t *qbase_p = p.q + (int64_t)s0 * p.stride + h * DH;
+  const uint16_t *dbase_p = p.d_h + (int64_t)s0 * p.d_stride + h * DH;
+  const int n_tiles = (n - k0 + TQ - 1) / TQ;  // queries i >= k0 see these keys
+  TileRegs<DH, TQ> rq, rd;
+  int32_t rts = 0;
+  auto prefetch = [&](int i0) __attribute__((always_inline)) {
+    rq.load(qbase_p, p.stride, i0, n);
+    rd.load(dbase_p, p.d_stride, i0, n);
+    if (tid < TQ) rts = (bc.use_time && i0 + tid < n) ? p.ts[s0 + i0 + tid] : 0;
+  };
+  prefetch(k0);
+  for (int t = 0; t < n_tiles; ++t) {
+    const int i0 = k0 + t * TQ;
+    __syncthreads();  // the previous tile is no longer read (tables and V rows written)
+    rq.store(q_row, q_tr);
+    rd.store(d_row, d_tr);
+    if (tid < TQ) q_ts[tid] = rts;
     __syncthreads();
-    stage_f16<DH>(p.q + (int64_t)s0 * p.stride + h * DH, p.stride, i0, n, q_row, q_tr);
-    stage_f32<DH>(p.d_out + (int64_t)s0 * p.d_stride + h * DH, p.d_stride, i0, n, d_row, d_tr);
-    if (tid < kBwdRows) q_ts[tid] = (bc.use_time && i0 + tid < n) ? p.ts[s0 + i0 + tid] : 0;
-    __syncthreads();
-    if (i0 + 31 < kbase) continue;  // every query of the tile precedes this wave's keys
+    if (t + 1 < n_tiles) prefetch(i0 + TQ);
+    if (!wave_rows || i0 + 31 < kbase) continue;  // every query precedes this wave's keys
+    const int2 tq = bc.use_time ? p.stat[s0 + i0] : int2{0, 0};
+    const BlockBias bb = classify(bc, i0, kbase, tq, tk);
+    const int32_t *qtsp = q_ts + 4 * half;
     // S and dA; lane: key lrow, queries 8 (e / 4) + 4 half + e % 4 of the tile
     f32x16 s, da = f32x16{};
+    if (bb.kind == KIND_CONST) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int r = 8 * (e >> 2) + 4 * half + (e & 3);
-      s[e] = rab(bc, i0 + r, kj, q_ts[r], kts);
+      for (int e = 0; e < 16; ++e) s[e] = bb.lo;
+    } else if (bb.kind == KIND_TWO) {
+      // hi when ts_q - ts_k >= thr, i.e. ts_q > ts_k + thr - 1 (never past INT32_MAX)
+      const int64_t gt = (int64_t)kts + (int64_t)bb.thr - 1;
+      const int32_t qgt = (int32_t)(gt > (int64_t)INT32_MAX ? (int64_t)INT32_MAX : gt);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[e] = qtsp[8 * (e >> 2) + (e & 3)] > qgt ? bb.hi : bb.lo;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        s[e] = rab(bc, i0 + 8 * (e >> 2) + 4 * half + (e & 3), kj, qtsp[8 * (e >> 2) + (e & 3)], kts);
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       s = mfma32_f16(row_frag<DH>(q_row, lane, ks), kf[ks], s);
-      da = mfma32_f16(row_frag<DH>(d_row, lane, ks), vf[ks], da);
+      da = mfma32_f16(row_frag<DH>(d_row, lane, ks), row_frag<DH>(vw, lane, ks), da);
     }
     float a[16], ds[16];
+    if (i0 < kbase + 31) {  // straddles the diagonal: queries before the key are masked
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int qi = i0 + 8 * (e >> 2) + 4 * half + (e & 3);
-      const bool ok = k_ok && qi < n && kj <= qi;
-      float av, g;
-      silu_and_grad(s[e], av, g);
-      a[e] = ok ? av : 0.0f;
-      ds[e] = ok ? da[e] * g : 0.0f;
+      for (int e = 0; e < 16; ++e) {
+        const int qi = i0 + 8 * (e >> 2) + 4 * half + (e & 3);
+        float av, g;
+        silu_and_grad(s[e], av, g);
+        const bool ok = kj <= qi;
+        a[e] = ok ? av : 0.0f;
+        ds[e] = ok ? da[e] * g : 0.0f;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float g;
+        silu_and_grad(s[e], a[e], g);
+        ds[e] = da[e] * g;
+      }
     }
     // dV^T += dO^T A and dK^T += Q^T dS over the tile's 32 queries
 #pragma unroll
@@ -329,6 +502,8 @@ __global__ __launch_bounds__(kBwdThreads, DH == 128 ? 1 : 2) void attn_bwd_dkv_k
     }
   }
   if (k_ok) {
+    float inv;
+    (void)d_scale(p.d_max, inv);
     float *kr = p.dk + (int64_t)(s0 + kj) * p.g_stride + h * DH + half * 4;
     float *vr = p.dv + (int64_t)(s0 + kj) * p.g_stride + h * DH + half * 4;
 #pragma unroll
@@ -336,9 +511,11 @@ __global__ __launch_bounds__(kBwdThreads, DH == 128 ? 1 : 2) void attn_bwd_dkv_k
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         *reinterpret_cast<f32x4 *>(kr + f * 32 + g * 8) =
-            f32x4{dk_acc[f][4 * g], dk_acc[f][4 * g + 1], dk_acc[f][4 * g + 2], dk_acc[f][4 * g + 3]};
+            f32x4{dk_acc[f][4 * g] * inv, dk_acc[f][4 * g + 1] * inv, dk_acc[f][4 * g + 2] * inv,
+                  dk_acc[f][4 * g + 3] * inv};
         *reinterpret_cast<f32x4 *>(vr + f * 32 + g * 8) =
-            f32x4{dv_acc[f][4 * g], dv_acc[f][4 * g + 1], dv_acc[f][4 * g + 2], dv_acc[f][4 * g + 3]};
+            f32x4{dv_acc[f][4 * g] * inv, dv_acc[f][4 * g + 1] * inv, dv_acc[f][4 * g + 2] * inv,
+                  dv_acc[f][4 * g + 3] * inv};
       }
   }
 }
@@ -346,22 +523,31 @@ __global__ __launch_bounds__(kBwdThreads, DH == 128 ? 1 : 2) void attn_bwd_dkv_k
 template <int DH>
 hipError_t launch_bwd_dh(const AttnBwdArgs &a, int64_t cap, hipStream_t stream) {
   const dim3 grid((unsigned)cap, (unsigned)a.num_heads);
-  attn_bwd_dq_kernel<DH><<<grid, dim3(kBwdThreads), 0, stream>>>(a);
+  attn_bwd_dq_kernel<DH><<<grid, dim3(kThreads), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  attn_bwd_dkv_kernel<DH><<<grid, dim3(kBwdThreads), 0, stream>>>(a);
+  attn_bwd_dkv_kernel<DH><<<grid, dim3(kThreads), 0, stream>>>(a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attention_bwd(const AttnBwdArgs &a, int dh, int64_t cap, hipStream_t stream) {
-  if (cap <= 0 || a.num_heads <= 0) return hipSuccess;
+hipError_t launch_attention_bwd(const AttnBwdArgs &a, int dh, int64_t cap, int64_t total_rows,
+                                hipStream_t stream) {
+  if (cap <= 0 || a.num_heads <= 0 || total_rows <= 0) return hipSuccess;
+  if (dh != 32 && dh != 64 && dh != 128) return hipErrorInvalidValue;
+  // the fp16 copy of dO; d_stride = H dh is a multiple of 32, so rows are whole f32x4s
+  const int64_t n4 = total_rows * a.d_stride / 4;
+  const int blocks = (int)((n4 + 255) / 256 < 2048 ? (n4 + 255) / 256 : 2048);
+  bwd_clear_kernel<<<1, 64, 0, stream>>>(a.d_max);
+  bwd_absmax_kernel<<<blocks, 256, 0, stream>>>(a.d_out, n4, a.d_max);
+  bwd_cast_kernel<<<blocks, 256, 0, stream>>>(a.d_out, n4, a.d_max, a.d_h);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   switch (dh) {
     case 32: return launch_bwd_dh<32>(a, cap, stream);
     case 64: return launch_bwd_dh<64>(a, cap, stream);
-    case 128: return launch_bwd_dh<128>(a, cap, stream);
-    default: return hipErrorInvalidValue;
+    default: return launch_bwd_dh<128>(a, cap, stream);
   }
 }
 

@@ -46,6 +46,9 @@ struct AttnBwdArgs {
   int64_t stride;
   const float *d_out;         // upstream gradient of the attention output [T][H*dv]
   int64_t d_stride;
+  uint16_t *d_h;              // workspace [T][H*dv]: d_out x 2^-e in fp16 (same stride)
+  uint32_t *d_max;            // workspace [1]: bits of max |d_out| (e is its exponent)
+  const int2 *stat;           // (min, max) timestamp of each 32-row block, when ts is set
   const float *rab_pos;       // [rab_heads][pos_buckets] or nullptr
   const float *rab_time;      // [rab_heads][time_buckets] or nullptr
   int pos_buckets, time_buckets, rab_per_head;
@@ -56,8 +59,10 @@ struct AttnBwdArgs {
   int num_heads;
 };
 
-// dQ, dK, dV for every row (two kernels; tiles of 128 rows from the schedule's list).
-hipError_t launch_attention_bwd(const AttnBwdArgs &a, int dh, int64_t cap, hipStream_t stream);
+// dQ, dK, dV for every row: the scaled fp16 copy of d_out, then two kernels over the
+// schedule's (sequence, 128-row tile) list.  stat must be filled when ts is set.
+hipError_t launch_attention_bwd(const AttnBwdArgs &a, int dh, int64_t cap, int64_t total_rows,
+                                hipStream_t stream);
 
 constexpr int kAttnBlockMMin = 128;  // query rows per workgroup: 128, or 256 for long rows
 constexpr int kAttnBlockN = 64;      // keys per LDS stage

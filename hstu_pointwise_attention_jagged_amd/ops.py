@@ -21,8 +21,8 @@ __all__ = ["HSTUError", "LayerDims", "DeviceWeights", "DeviceJagged", "hstu_laye
            "hstu_attn_workspace_bytes", "hstu_mfalcon_workspace_bytes", "hstu_validate_jagged",
            "hstu_sl_workspace_bytes", "hstu_stochastic_length", "hstu_stack_fwd",
            "hstu_stack_fwd_mfalcon", "hstu_stack_workspace_bytes",
-           "hstu_stack_mfalcon_workspace_bytes", "hstu_attn_bwd", "profile_enable", "profile_reset",
-           "profile_collect"]
+           "hstu_stack_mfalcon_workspace_bytes", "hstu_attn_bwd", "hstu_attn_bwd_workspace_bytes",
+           "profile_enable", "profile_reset", "profile_collect"]
 
 
 class HSTUError(RuntimeError):
@@ -365,6 +365,12 @@ def hstu_stochastic_length(raw: DeviceJagged, u_keep: torch.Tensor, keys: torch.
                                     ws.numel() * ws.element_size(), _stream(stream))
     _raise(st, "hstu_stochastic_length")
     return kept, new_off, new_ts, x_out
+
+
+def hstu_attn_bwd_workspace_bytes(dims: LayerDims, seq: DeviceJagged) -> int:
+    lib = _lib.load()
+    d, s = dims.c(), seq.c()
+    return int(lib.hstu_attn_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(s)))
 
 
 def hstu_attn_bwd(dims: LayerDims, seq: DeviceJagged, q: torch.Tensor, k: torch.Tensor,

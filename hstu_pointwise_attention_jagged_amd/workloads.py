@@ -176,6 +176,17 @@ def draw_x(rng: np.random.Generator, total: int, d: int) -> np.ndarray:
     return round_bf16(rng.standard_normal((total, d), dtype=np.float32))
 
 
+def draw_attention_grad_inputs(rng: np.random.Generator, total: int, width: int):
+    """Inputs of the attention gradient: Q, K, V as fp16 values (float32 arrays holding
+    fp16-exact numbers) drawn N(0.2, 0.6^2), the mean and spread of the projected and
+    activated rows the forward attends over (scores of mean about 5 and spread about 4.5
+    at 128 features), and the upstream gradient dO drawn N(0, 1) in float32."""
+    q, k, v = (round_f16(np.float32(0.2) + np.float32(0.6) *
+                         rng.standard_normal((total, width), dtype=np.float32)) for _ in range(3))
+    g = rng.standard_normal((total, width), dtype=np.float32)
+    return q, k, v, g
+
+
 def draw_weights(rng: np.random.Generator, dims: LayerDims, *, bias: bool = False,
                  affine: bool = False, rab: bool = True, rab_std: float = 0.02) -> LayerWeights:
     d, h = dims.d_model, dims.num_heads

@@ -38,13 +38,18 @@ def silu_grad(x: np.ndarray) -> np.ndarray:
 
 
 def attention_bwd(q, k, v, d_out, offsets, timestamps, num_heads: int, dqk: int, dv: int,
-                  rab_pos=None, rab_time=None):
+                  rab_pos=None, rab_time=None, *, rows=None):
     """Gradients of hstu_ref.attention (causal, no prefix) with respect to q, k, v and the
     two bias tables, for the upstream gradient d_out [T][H*dv].
 
     Returns (dq [T][H*dqk], dk [T][H*dqk], dv [T][H*dv], d_rab_pos, d_rab_time); a table
     gradient has the table's shape (rows 1 or H), or is None when the table is None.
+    rows: if given, only these global rows of dq, dk and dv are computed (the others stay
+    0) and the table gradients are None; see _attention_bwd_rows.
     """
+    if rows is not None:
+        return _attention_bwd_rows(q, k, v, d_out, offsets, timestamps, num_heads, dqk, dv,
+                                   rab_pos, rab_time, rows)
     q, k, v, g = (np.asarray(a, dtype=np.float64) for a in (q, k, v, d_out))
     offsets = np.asarray(offsets, dtype=np.int64)
     ts = None if timestamps is None else np.asarray(timestamps, dtype=np.int64)
@@ -90,3 +95,53 @@ def attention_bwd(q, k, v, d_out, offsets, timestamps, num_heads: int, dqk: int,
     if dT is not None and np.ndim(rab_time) == 1:
         dT = dT[0]
     return dq, dk, dvv, dP, dT
+
+
+def _attention_bwd_rows(q, k, v, d_out, offsets, timestamps, num_heads, dqk, dv, rab_pos,
+                        rab_time, rows):
+    """The same gradients at chosen rows only, for sequences too long for the full pair
+    matrices.  Row r of dq needs the pairs (r, j <= r) of its sequence; row r of dk and dv
+    needs the pairs (i >= r, r).  Each is formed from its own slice of S, A and dA, with
+    the same formulas as attention_bwd."""
+    q, k, v, g = (np.asarray(a, dtype=np.float64) for a in (q, k, v, d_out))
+    offsets = np.asarray(offsets, dtype=np.int64)
+    ts = None if timestamps is None else np.asarray(timestamps, dtype=np.int64)
+    use_time = rab_time is not None and ts is not None
+    P = None if rab_pos is None else np.atleast_2d(np.asarray(rab_pos, dtype=np.float64))
+    Tt = None if rab_time is None else np.atleast_2d(np.asarray(rab_time, dtype=np.float64))
+    dq, dk, dvv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    rows = np.unique(np.asarray(rows, dtype=np.int64))
+    seq_of = np.searchsorted(offsets, rows, side="right") - 1
+    for b in np.unique(seq_of):
+        s0, s1 = int(offsets[b]), int(offsets[b + 1])
+        n = s1 - s0
+        r = rows[seq_of == b] - s0          # local rows
+        i = np.arange(n)
+
+        def bias(qi, kj, h):
+            # rab for the pairs (qi[:, None], kj[None, :]) of head h
+            out = np.zeros((qi.size, kj.size))
+            if P is not None:
+                rp = P[0] if P.shape[0] == 1 else P[h]
+                out += rp[ref.pos_bucket(np.maximum(qi[:, None] - kj[None, :], 0), P.shape[1])]
+            if use_time:
+                rt = Tt[0] if Tt.shape[0] == 1 else Tt[h]
+                out += rt[ref.time_bucket(ts[s0 + qi][:, None], ts[s0 + kj][None, :], Tt.shape[1])]
+            return out
+
+        for h in range(num_heads):
+            cq, cv = slice(h * dqk, (h + 1) * dqk), slice(h * dv, (h + 1) * dv)
+            qh, kh, vh, gh = q[s0:s1, cq], k[s0:s1, cq], v[s0:s1, cv], g[s0:s1, cv]
+            # rows as queries: pairs (r, j)
+            sq = qh[r] @ kh.T + bias(r, i, h)
+            ok = i[None, :] <= r[:, None]
+            dsq = np.where(ok, (gh[r] @ vh.T) * silu_grad(sq), 0.0)
+            dq[s0 + r, cq] = dsq @ kh
+            # rows as keys: pairs (i, r)
+            sk = qh @ kh[r].T + bias(i, r, h)
+            ok = i[:, None] >= r[None, :]
+            ak = np.where(ok, ref.silu(sk), 0.0)
+            dsk = np.where(ok, (gh @ vh[r].T) * silu_grad(sk), 0.0)
+            dk[s0 + r, cq] = dsk.T @ qh
+            dvv[s0 + r, cv] = ak.T @ gh
+    return dq, dk, dvv, None, None

@@ -3,7 +3,10 @@
 dQ, dK and dV from the HIP kernels are compared element by element with
 oracle/hstu_bwd.attention_bwd on the same fp16-exact Q, K, V and the same fp32 upstream
 gradient, on jagged batches with empty, one-token and ragged users, at head sizes 32, 64
-and 128, with shared and per-head bias tables.  Bar: the error divided by the standard
+and 128, with shared and per-head bias tables, and at the full 8 x 8192-token size (8 heads
+of 128, the launch that bench.py times) on sampled rows that the oracle computes one by
+one: first and last rows of sequences, both sides of a 128-row tile edge, and the middle
+of a sequence.  Bar: the error divided by the standard
 deviation of the oracle's tensor, max <= 2e-2 and mean <= 2e-3 (the bar of the raw
 attention output; the kernels round dO, A and dS to fp16 for the matrix products).  Two
 runs must agree bit for bit.
@@ -36,36 +39,52 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def _case(seed, lengths, H, dh, per_head, scale=0.25):
+def _case(seed, lengths, H, dh, per_head, scale=0.25, g_scale=1.0, pos_buckets=64,
+          time_buckets=32):
     rng = np.random.default_rng(seed)
     seq = wl.jagged_from_lengths(rng, lengths)
     T = seq.total
     q, k, v = (wl.round_f16(scale * rng.standard_normal((T, H * dh), dtype=np.float32))
                for _ in range(3))
-    P = (0.5 * rng.standard_normal((H if per_head else 1, 64))).astype(np.float32)
-    Tt = (0.5 * rng.standard_normal((H if per_head else 1, 32))).astype(np.float32)
-    g = rng.standard_normal((T, H * dh)).astype(np.float32)
+    P = (0.5 * rng.standard_normal((H if per_head else 1, pos_buckets))).astype(np.float32)
+    Tt = (0.5 * rng.standard_normal((H if per_head else 1, time_buckets))).astype(np.float32)
+    g = (g_scale * rng.standard_normal((T, H * dh))).astype(np.float32)
     return seq, q, k, v, P, Tt, g
 
 
 def _gpu_bwd(seq, q, k, v, P, Tt, g, H, dh):
-    dims = ops.LayerDims(d_model=max(64, H * dh), num_heads=H, dqk=dh, dv=dh, pos_buckets=64,
-                         time_buckets=32, rab_heads=P.shape[0])
+    rows = (P if P is not None else Tt if Tt is not None else np.zeros((1, 1))).shape[0]
+    dims = ops.LayerDims(d_model=max(64, H * dh), num_heads=H, dqk=dh, dv=dh,
+                         pos_buckets=P.shape[1] if P is not None else 64,
+                         time_buckets=Tt.shape[1] if Tt is not None else 32, rab_heads=rows)
     buf = dev.f16_tensor(np.concatenate([q, k, v], axis=1))
     hq = H * dh
+    opt = lambda a: None if a is None else torch.from_numpy(a).cuda()  # noqa: E731
     return ops.hstu_attn_bwd(dims, dev.jagged_of(seq), buf[:, :hq], buf[:, hq:2 * hq],
                              buf[:, 2 * hq:], torch.from_numpy(g).cuda(), row_stride=buf.stride(0),
-                             rab_pos=torch.from_numpy(P).cuda(), rab_time=torch.from_numpy(Tt).cuda())
+                             rab_pos=opt(P), rab_time=opt(Tt))
 
 
-@pytest.mark.parametrize("seed,lengths,H,dh,per_head", [
-    (0, [5, 17, 32, 64, 0, 1, 100], 2, 32, False),
-    (1, [33, 200, 7, 129], 2, 64, True),
-    (2, [300, 45, 0, 160], 2, 128, False),
-])
-def test_attention_gradients_match_oracle(seed, lengths, H, dh, per_head):
-    seq, q, k, v, P, Tt, g = _case(seed, lengths, H, dh, per_head)
-    say(f"[bwd] lengths={lengths} H={H} dh={dh} per_head_rab={per_head}")
+# (seed, lengths, H, dh, per-head tables, dO scale, position buckets, time buckets, tables)
+CASES = [
+    (0, [5, 17, 32, 64, 0, 1, 100], 2, 32, False, 1.0, 64, 32, True),
+    (1, [33, 200, 7, 129], 2, 64, True, 1.0, 64, 32, True),
+    (2, [300, 45, 0, 160], 2, 128, False, 1.0, 64, 32, True),
+    # long rows, few position buckets: most blocks take one or two bias values
+    (3, [1500, 700, 31], 1, 64, False, 1e-7, 8, 16, True),     # tiny upstream gradient
+    (4, [1000, 97], 2, 128, True, 300.0, 8, 16, True),         # large upstream gradient
+    (5, [400, 129], 2, 128, False, 1.0, 64, 32, False),        # no bias tables
+]
+
+
+@pytest.mark.parametrize("seed,lengths,H,dh,per_head,g_scale,pb,tb,tables", CASES)
+def test_attention_gradients_match_oracle(seed, lengths, H, dh, per_head, g_scale, pb, tb, tables):
+    seq, q, k, v, P, Tt, g = _case(seed, lengths, H, dh, per_head, g_scale=g_scale,
+                                   pos_buckets=pb, time_buckets=tb)
+    if not tables:
+        P = Tt = None
+    say(f"[bwd] lengths={lengths} H={H} dh={dh} per_head_rab={per_head} dO x{g_scale} "
+        f"buckets={pb}/{tb} tables={tables}")
     got = _gpu_bwd(seq, q, k, v, P, Tt, g, H, dh)
     torch.cuda.synchronize()
     again = _gpu_bwd(seq, q, k, v, P, Tt, g, H, dh)
@@ -76,6 +95,39 @@ def test_attention_gradients_match_oracle(seed, lengths, H, dh, per_head):
         assert np.array_equal(gt.cpu().numpy(), ag.cpu().numpy()), f"{name} not deterministic"
         sd = float(np.std(wt)) or 1.0
         err = np.abs(gn - wt) / sd
+        say(f"      {name}: max_rel={err.max():.3e} mean_rel={err.mean():.3e} (std {sd:.3g})")
+        assert np.all(np.isfinite(gn))
+        assert err.max() <= MAX_REL and err.mean() <= MEAN_REL, name
+
+
+def test_zero_upstream_gradient_gives_zero():
+    seq, q, k, v, P, Tt, g = _case(6, [70, 130], 2, 64, False)
+    g[:] = 0.0
+    say("[bwd] dO = 0")
+    for t in _gpu_bwd(seq, q, k, v, P, Tt, g, 2, 64):
+        assert torch.count_nonzero(t).item() == 0
+
+
+def test_attention_gradients_full_size_sampled_rows():
+    w = wl.config(2)
+    d = w.dims
+    H, dh = d.num_heads, d.dqk
+    seq = w.seq
+    rng = np.random.default_rng(2002)
+    q, k, v, g = wl.draw_attention_grad_inputs(rng, seq.total, H * dh)
+    P, Tt = w.weights.rab_pos, w.weights.rab_time
+    say(f"[bwd full] B={seq.batch} T={seq.total} H={H} dh={dh}")
+    got = _gpu_bwd(seq, q, k, v, P, Tt, g, H, dh)
+    torch.cuda.synchronize()
+    off = seq.offsets.astype(np.int64)
+    rows = [0, 1, 127, 128, 4095, 8191, int(off[3]) + 2000, int(off[7]) + 8063,
+            int(off[7]) + 8064, int(off[8]) - 1]
+    want = bwd.attention_bwd(q, k, v, g, off, seq.timestamps, H, dh, dh, P, Tt, rows=rows)
+    for name, gt, wt in zip(("dq", "dk", "dv"), got, want[:3]):
+        gn = gt[rows].cpu().numpy().astype(np.float64)
+        wr = wt[rows]
+        sd = float(np.std(wr)) or 1.0
+        err = np.abs(gn - wr) / sd
         say(f"      {name}: max_rel={err.max():.3e} mean_rel={err.mean():.3e} (std {sd:.3g})")
         assert np.all(np.isfinite(gn))
         assert err.max() <= MAX_REL and err.mean() <= MEAN_REL, name

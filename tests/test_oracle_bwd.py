@@ -77,3 +77,18 @@ def test_masked_and_future_tokens_get_no_gradient_from_the_past():
     assert np.all(dk[1:] == 0) and np.all(dv[1:] == 0)  # row 0 attends to key 0 only
     assert np.all(dq[1:] == 0)
     assert np.any(dq[0] != 0) and np.any(dk[0] != 0)
+
+
+def test_sampled_rows_equal_the_full_gradient():
+    # the row-sampled path (used at sizes where the full pair matrices do not fit) must
+    # give the full gradient's values at the chosen rows and zeros elsewhere
+    off, ts, q, k, v, P, Tt, G, H, dh = _case(4, [7, 0, 12, 1, 30])
+    full = bwd.attention_bwd(q, k, v, G, off, ts, H, dh, dh, P, Tt)
+    rows = [0, 5, 6, 7, 18, 19, 20, 21, 49]
+    part = bwd.attention_bwd(q, k, v, G, off, ts, H, dh, dh, P, Tt, rows=rows)
+    mask = np.zeros(q.shape[0], dtype=bool)
+    mask[rows] = True
+    for f, p_ in zip(full[:3], part[:3]):
+        np.testing.assert_allclose(p_[mask], f[mask], rtol=1e-12, atol=1e-12)
+        assert np.all(p_[~mask] == 0)
+    assert part[3] is None and part[4] is None
