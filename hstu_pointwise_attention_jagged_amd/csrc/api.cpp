@@ -503,6 +503,7 @@ hstu_status_t hstu_attn_bwd(const hstu_dims_t *dims, const float *rab_pos, const
   if (seq->batch == 0 || seq->total_tokens == 0) return HSTU_OK;
   if ((st = check_ws(ws, ws_bytes, attn_bwd_ws_bytes(dims, seq))) != HSTU_OK) return st;
   if (attn_block_m(seq->max_seq_len) != 128) return HSTU_ERR_UNSUPPORTED;  // the kernels' tile
+  if (!rows_addressable(seq->max_seq_len, row_stride)) return HSTU_ERR_UNSUPPORTED;
 
   LayerWs lw{};
   carve_attn((char *)ws, seq, nullptr, lw);

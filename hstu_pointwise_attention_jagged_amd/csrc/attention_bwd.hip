@@ -69,35 +69,73 @@ struct BwdLayout {
   static constexpr int CPR = DH / 8;   // 16-byte chunks per row
 };
 
+// Buffer resource over the DH-wide head slice of rows [0, n) of one sequence (row pitch
+// `stride` elements, first row at base): loads past the last row return zero, so a tile
+// that runs past the sequence end needs no branch.  The host keeps the byte count below
+// 2^31 (max_seq_len + 64 rows of the pitch).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t *base, int64_t stride,
+                                                            int n, int dh) {
+  const uint32_t bytes = n > 0 ? (uint32_t)(((int64_t)(n - 1) * stride + dh) * 2) : 0u;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), 0, (int)bytes,
+                                           0x00020000);  // raw buffer, 32-bit data format
+}
+
+// Load of a value that no thread writes while the kernel runs, through the constant
+// address space: with a uniform address it becomes a scalar load.
+template <class T>
+__device__ __forceinline__ T ld_const(const T *ptr) {
+  return *(const __attribute__((address_space(4))) T *)ptr;
+}
+
+// (min, max) timestamps of the 32-row block starting at row ptr - stat, as two scalar words
+__device__ __forceinline__ int2 ld_stat(const int2 *ptr) {
+  const int32_t *w = reinterpret_cast<const int32_t *>(ptr);
+  return int2{ld_const(w), ld_const(w + 1)};
+}
+
+// Timestamps of rows [0, n) of one sequence, zero past the end (or everywhere without ts)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ts_rsrc(const int32_t *ts, int s0, int n) {
+  return __builtin_amdgcn_make_buffer_rsrc(ts ? const_cast<int32_t *>(ts + s0) : nullptr, 0,
+                                           ts ? n * 4 : 0, 0x00020000);
+}
+
+__device__ __forceinline__ int32_t load_ts(__amdgpu_buffer_rsrc_t rs, int row, int r0) {
+  return __builtin_amdgcn_raw_buffer_load_b32(rs, row * 4, r0 * 4, 0);
+}
+
 // Registers of one tile of ROWS rows of an fp16 matrix, spread over the workgroup:
-// chunk tid + 256 c for c < N.  Rows at or past the sequence end read as zero.
+// chunk tid + 256 c for c < N.  Each lane's byte offset within the tile is fixed; the
+// tile's first row goes in the uniform offset.
 template <int DH, int ROWS>
 struct TileRegs {
   static constexpr int CHUNKS = ROWS * BwdLayout<DH>::CPR;
   static constexpr int N = (CHUNKS + kThreads - 1) / kThreads;
   u32x4 v[N];
 
-  __device__ __forceinline__ void load(const uint16_t *base, int64_t stride, int r0, int n) {
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int64_t stride, int r0) {
     constexpr int CPR = BwdLayout<DH>::CPR;
+    const int soff = (int)((int64_t)r0 * stride * 2);
 #pragma unroll
     for (int c = 0; c < N; ++c) {
       const int idx = threadIdx.x + c * kThreads;
       const int r = idx / CPR, ch = idx % CPR;
       v[c] = u32x4{0, 0, 0, 0};
-      if (idx < CHUNKS && r0 + r < n)
-        v[c] = *reinterpret_cast<const u32x4 *>(base + (int64_t)(r0 + r) * stride + ch * 8);
+      if (CHUNKS % kThreads == 0 || idx < CHUNKS)
+        v[c] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (r * (int)stride + ch * 8) * 2, soff, 0));
     }
   }
-  // into a row copy and/or a transposed-read copy
+  // into a row copy and, with TR, a transposed-read copy too
+  template <bool TR>
   __device__ __forceinline__ void store(unsigned char *row_copy, unsigned char *tr_copy) const {
     using L = BwdLayout<DH>;
 #pragma unroll
     for (int c = 0; c < N; ++c) {
       const int idx = threadIdx.x + c * kThreads;
-      if (idx >= CHUNKS) break;
+      if (CHUNKS % kThreads != 0 && idx >= CHUNKS) break;
       const int r = idx / L::CPR, ch = idx % L::CPR;
-      if (row_copy) *reinterpret_cast<u32x4 *>(row_copy + r * L::ROWP + ch * 16) = v[c];
-      if (tr_copy) *reinterpret_cast<u32x4 *>(tr_copy + r * L::TRP + ch * 16) = v[c];
+      *reinterpret_cast<u32x4 *>(row_copy + r * L::ROWP + ch * 16) = v[c];
+      if constexpr (TR) *reinterpret_cast<u32x4 *>(tr_copy + r * L::TRP + ch * 16) = v[c];
     }
   }
 };
@@ -259,12 +297,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(AttnBwdArgs p)
   __shared__ float ptab[kMaxPos], ttab[kMaxTime];
 
   const int item = blockIdx.x;
-  if (item >= *p.n_work) return;
+  if (item >= ld_const(p.n_work)) return;
   const int h = blockIdx.y;
-  const int b = p.work[2 * item], qt = p.work[2 * item + 1];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = ld_const(p.work + 2 * item), qt = ld_const(p.work + 2 * item + 1);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar row ranges
   const int lrow = lane & 31, half = lane >> 5;
-  const int s0 = p.offsets[b], n = p.offsets[b + 1] - s0;
+  const int s0 = ld_const(p.offsets + b), n = ld_const(p.offsets + b + 1) - s0;
   BiasCtx bc;
   load_tables(p, h, ptab, ttab, bc);
 
@@ -274,7 +313,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(AttnBwdArgs p)
   const int qi = qbase + lrow;
   const bool q_ok = qi < n;
   const int32_t qts = bc.use_time ? p.ts[s0 + (q_ok ? qi : 0)] : 0;
-  const int2 tq = (bc.use_time && wave_rows) ? p.stat[s0 + qbase] : int2{0, 0};
+  const int2 tq = (bc.use_time && wave_rows) ? ld_stat(p.stat + s0 + qbase) : int2{0, 0};
   f16x8 qf[KS], dof[KS];
   {
     const uint16_t *qr = p.q + (int64_t)(s0 + qi) * p.stride + h * DH;
@@ -289,23 +328,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(AttnBwdArgs p)
 #pragma unroll
   for (int f = 0; f < FT; ++f) acc[f] = f32x16{};
 
-  const uint16_t *kbase_p = p.k + (int64_t)s0 * p.stride + h * DH;
-  const uint16_t *vbase_p = p.v + (int64_t)s0 * p.stride + h * DH;
+  const __amdgpu_buffer_rsrc_t krs = rows_rsrc(p.k + (int64_t)s0 * p.stride + h * DH, p.stride, n, DH);
+  const __amdgpu_buffer_rsrc_t vrs = rows_rsrc(p.v + (int64_t)s0 * p.stride + h * DH, p.stride, n, DH);
   const int k_end = min(n, q0 + kOwnRows);  // keys j <= i < q0 + 128
   const int n_tiles = (k_end + TK - 1) / TK;
+  const __amdgpu_buffer_rsrc_t trs = ts_rsrc(bc.use_time ? p.ts : nullptr, s0, n);
   TileRegs<DH, TK> rk, rv;
   int32_t rts = 0;
   auto prefetch = [&](int j0) __attribute__((always_inline)) {
-    rk.load(kbase_p, p.stride, j0, n);
-    rv.load(vbase_p, p.stride, j0, n);
-    if (tid < TK) rts = (bc.use_time && j0 + tid < n) ? p.ts[s0 + j0 + tid] : 0;
+    rk.load(krs, p.stride, j0);
+    rv.load(vrs, p.stride, j0);
+    if (tid < TK) rts = load_ts(trs, tid, j0);
   };
   prefetch(0);
   for (int t = 0; t < n_tiles; ++t) {
     const int j0 = t * TK;
     __syncthreads();  // the previous tile is no longer read (and the tables are written)
-    rk.store(k_row, k_tr);
-    rv.store(v_row, nullptr);
+    rk.template store<true>(k_row, k_tr);
+    rv.template store<false>(v_row, nullptr);
     if (tid < TK) k_ts[tid] = rts;
     __syncthreads();
     if (t + 1 < n_tiles) prefetch(j0 + TK);
@@ -317,7 +357,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(AttnBwdArgs p)
       const unsigned char *ktr = k_tr + blk * 32 * L::TRP;
       const unsigned char *vr = v_row + blk * 32 * L::ROWP;
       const int32_t *kts = k_ts + blk * 32 + 4 * half;
-      const int2 tk = bc.use_time ? p.stat[s0 + kb] : int2{0, 0};
+      const int2 tk = bc.use_time ? ld_stat(p.stat + s0 + kb) : int2{0, 0};
       const BlockBias bb = classify(bc, qbase, kb, tq, tk);
       // S^T with its bias, dA^T; lane: query lrow, keys 8 (i / 4) + 4 half + i % 4
       f32x16 s, da = f32x16{};
@@ -379,7 +419,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(AttnBwdArgs p)
 // At DH = 128 the dK and dV accumulators (128 registers) and the K fragments take one
 // workgroup per CU (up to 512 registers per lane); smaller heads fit two.
 template <int DH>
-__global__ __launch_bounds__(kThreads, DH == 128 ? 1 : 2) void attn_bwd_dkv_kernel(AttnBwdArgs p) {
+__global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkv_kernel(AttnBwdArgs p) {
   using L = BwdLayout<DH>;
   constexpr int KS = L::KS, FT = L::FT;
   constexpr int TQ = kDkvQueries;
@@ -392,15 +432,16 @@ __global__ __launch_bounds__(kThreads, DH == 128 ? 1 : 2) void attn_bwd_dkv_kern
   __shared__ float ptab[kMaxPos], ttab[kMaxTime];
 
   const int item = blockIdx.x;
-  if (item >= *p.n_work) return;
+  if (item >= ld_const(p.n_work)) return;
   const int h = blockIdx.y;
-  const int b = p.work[2 * item];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = ld_const(p.work + 2 * item);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar row ranges
   const int lrow = lane & 31, half = lane >> 5;
-  const int s0 = p.offsets[b], n = p.offsets[b + 1] - s0;
+  const int s0 = ld_const(p.offsets + b), n = ld_const(p.offsets + b + 1) - s0;
   // the list is ordered for the query tiles (tile t visits t + 1 key tiles); key tile
   // nt - 1 - t visits as many query tiles, so the reversal keeps the longest items first
-  const int kt = (n + kOwnRows - 1) / kOwnRows - 1 - p.work[2 * item + 1];
+  const int kt = (n + kOwnRows - 1) / kOwnRows - 1 - ld_const(p.work + 2 * item + 1);
   BiasCtx bc;
   load_tables(p, h, ptab, ttab, bc);
 
@@ -410,7 +451,7 @@ __global__ __launch_bounds__(kThreads, DH == 128 ? 1 : 2) void attn_bwd_dkv_kern
   const int kj = kbase + lrow;
   const bool k_ok = kj < n;
   const int32_t kts = bc.use_time ? p.ts[s0 + (k_ok ? kj : 0)] : 0;
-  const int2 tk = (bc.use_time && wave_rows) ? p.stat[s0 + kbase] : int2{0, 0};
+  const int2 tk = (bc.use_time && wave_rows) ? ld_stat(p.stat + s0 + kbase) : int2{0, 0};
   f16x8 kf[KS];
   {
     const uint16_t *kr = p.k + (int64_t)(s0 + kj) * p.stride + h * DH;
@@ -419,35 +460,37 @@ __global__ __launch_bounds__(kThreads, DH == 128 ? 1 : 2) void attn_bwd_dkv_kern
   }
   {  // the workgroup's V rows, read as B operands of dA = dO V^T
     TileRegs<DH, kOwnRows> rv;
-    rv.load(p.v + (int64_t)s0 * p.stride + h * DH, p.stride, k0, n);
-    rv.store(v_own, nullptr);
+    rv.load(rows_rsrc(p.v + (int64_t)s0 * p.stride + h * DH, p.stride, n, DH), p.stride, k0);
+    rv.template store<false>(v_own, nullptr);
   }
   const unsigned char *vw = v_own + wave * 32 * L::ROWP;
   f32x16 dk_acc[FT], dv_acc[FT];
 #pragma unroll
   for (int f = 0; f < FT; ++f) dk_acc[f] = dv_acc[f] = f32x16{};
 
-  const uint16_t *qbase_p = p.q + (int64_t)s0 * p.stride + h * DH;
-  const uint16_t *dbase_p = p.d_h + (int64_t)s0 * p.d_stride + h * DH;
+  const __amdgpu_buffer_rsrc_t qrs = rows_rsrc(p.q + (int64_t)s0 * p.stride + h * DH, p.stride, n, DH);
+  const __amdgpu_buffer_rsrc_t drs =
+      rows_rsrc(p.d_h + (int64_t)s0 * p.d_stride + h * DH, p.d_stride, n, DH);
   const int n_tiles = (n - k0 + TQ - 1) / TQ;  // queries i >= k0 see these keys
+  const __amdgpu_buffer_rsrc_t trs = ts_rsrc(bc.use_time ? p.ts : nullptr, s0, n);
   TileRegs<DH, TQ> rq, rd;
   int32_t rts = 0;
   auto prefetch = [&](int i0) __attribute__((always_inline)) {
-    rq.load(qbase_p, p.stride, i0, n);
-    rd.load(dbase_p, p.d_stride, i0, n);
-    if (tid < TQ) rts = (bc.use_time && i0 + tid < n) ? p.ts[s0 + i0 + tid] : 0;
+    rq.load(qrs, p.stride, i0);
+    rd.load(drs, p.d_stride, i0);
+    if (tid < TQ) rts = load_ts(trs, tid, i0);
   };
   prefetch(k0);
   for (int t = 0; t < n_tiles; ++t) {
     const int i0 = k0 + t * TQ;
     __syncthreads();  // the previous tile is no longer read (tables and V rows written)
-    rq.store(q_row, q_tr);
-    rd.store(d_row, d_tr);
+    rq.template store<true>(q_row, q_tr);
+    rd.template store<true>(d_row, d_tr);
     if (tid < TQ) q_ts[tid] = rts;
     __syncthreads();
     if (t + 1 < n_tiles) prefetch(i0 + TQ);
     if (!wave_rows || i0 + 31 < kbase) continue;  // every query precedes this wave's keys
-    const int2 tq = bc.use_time ? p.stat[s0 + i0] : int2{0, 0};
+    const int2 tq = bc.use_time ? ld_stat(p.stat + s0 + i0) : int2{0, 0};
     const BlockBias bb = classify(bc, i0, kbase, tq, tk);
     const int32_t *qtsp = q_ts + 4 * half;
     // S and dA; lane: key lrow, queries 8 (e / 4) + 4 half + e % 4 of the tile
@@ -471,29 +514,26 @@ __global__ __launch_bounds__(kThreads, DH == 128 ? 1 : 2) void attn_bwd_dkv_kern
       s = mfma32_f16(row_frag<DH>(q_row, lane, ks), kf[ks], s);
       da = mfma32_f16(row_frag<DH>(d_row, lane, ks), row_frag<DH>(vw, lane, ks), da);
     }
-    float a[16], ds[16];
-    if (i0 < kbase + 31) {  // straddles the diagonal: queries before the key are masked
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int qi = i0 + 8 * (e >> 2) + 4 * half + (e & 3);
-        float av, g;
-        silu_and_grad(s[e], av, g);
-        const bool ok = kj <= qi;
-        a[e] = ok ? av : 0.0f;
-        ds[e] = ok ? da[e] * g : 0.0f;
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float g;
-        silu_and_grad(s[e], a[e], g);
-        ds[e] = da[e] * g;
-      }
-    }
-    // dV^T += dO^T A and dK^T += Q^T dS over the tile's 32 queries
+    // A and dS, then dV^T += dO^T A and dK^T += Q^T dS, over the tile's queries in two
+    // halves of 16 (8 values per lane each), so that only one half is live in registers
+    const bool diag = i0 < kbase + 31;  // straddles the diagonal: earlier queries masked
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
-      const f16x8 aop = pack8(a + 8 * s2), dop = pack8(ds + 8 * s2);
+      float a[8], ds[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int e = 8 * s2 + j;
+        float av, g;
+        silu_and_grad(s[e], av, g);
+        a[j] = av;
+        ds[j] = da[e] * g;
+        if (diag) {
+          const bool ok = kj <= i0 + 8 * (e >> 2) + 4 * half + (e & 3);
+          a[j] = ok ? a[j] : 0.0f;
+          ds[j] = ok ? ds[j] : 0.0f;
+        }
+      }
+      const f16x8 aop = pack8(a), dop = pack8(ds);
 #pragma unroll
       for (int f = 0; f < FT; ++f) {
         dv_acc[f] = mfma32_f16(tr_frag<DH>(d_tr, lane, f, s2), aop, dv_acc[f]);
