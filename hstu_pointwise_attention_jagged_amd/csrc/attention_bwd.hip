@@ -245,10 +245,12 @@ __global__ __launch_bounds__(64) void bwd_clear_kernel(uint32_t *d_max) {
   if (threadIdx.x == 0) *d_max = 0u;
 }
 
-// max |d_out| over n4 groups of 4 floats: wave maxima of the magnitude bits (ordered as
-// unsigned integers for non-negative floats), then one atomic per wave
+// max |d_out| over n4 groups of 4 floats: the magnitude bits (ordered as unsigned
+// integers for non-negative floats) reduced per wave, then per workgroup, then one atomic
+// per workgroup
 __global__ __launch_bounds__(256) void bwd_absmax_kernel(const float *d_out, int64_t n4,
                                                          uint32_t *d_max) {
+  __shared__ uint32_t wmax[4];
   uint32_t m = 0u;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
     const f32x4 v = reinterpret_cast<const f32x4 *>(d_out)[i];
@@ -257,7 +259,9 @@ __global__ __launch_bounds__(256) void bwd_absmax_kernel(const float *d_out, int
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
-  if ((threadIdx.x & 63) == 0) atomicMax(d_max, m);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) atomicMax(d_max, max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])));
 }
 
 __global__ __launch_bounds__(256) void bwd_cast_kernel(const float *d_out, int64_t n4,
@@ -578,7 +582,7 @@ hipError_t launch_attention_bwd(const AttnBwdArgs &a, int dh, int64_t cap, int64
   if (dh != 32 && dh != 64 && dh != 128) return hipErrorInvalidValue;
   // the fp16 copy of dO; d_stride = H dh is a multiple of 32, so rows are whole f32x4s
   const int64_t n4 = total_rows * a.d_stride / 4;
-  const int blocks = (int)((n4 + 255) / 256 < 2048 ? (n4 + 255) / 256 : 2048);
+  const int blocks = (int)((n4 + 255) / 256 < 1024 ? (n4 + 255) / 256 : 1024);
   bwd_clear_kernel<<<1, 64, 0, stream>>>(a.d_max);
   bwd_absmax_kernel<<<blocks, 256, 0, stream>>>(a.d_out, n4, a.d_max);
   bwd_cast_kernel<<<blocks, 256, 0, stream>>>(a.d_out, n4, a.d_max, a.d_h);
