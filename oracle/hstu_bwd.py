@@ -18,8 +18,21 @@ with SiLU'(x) = sigma(x) (1 + x (1 - sigma(x))).  There is no softmax, so no row
 statistics enter the gradient.  The pages do not discuss training-time gradients; this
 is the derivative of the forward that the forward oracle (hstu_ref.attention) computes.
 
-Parity status: pinned by central finite differences of hstu_ref.attention on small
-jagged batches (tests/test_oracle_bwd.py).
+layer_bwd differentiates the whole layer (equations 1-3, the composition that
+hstu_ref.layer_fwd computes) by the chain rule, for the upstream gradient dY:
+
+    f2:        dG = dY w2,   dw2 = dY^T G,   db2 = sum_t dY
+    gate:      dU = dG (.) N,   dN = dG (.) U
+    LayerNorm: N = xhat gamma + beta, xhat = (O - mean) / sigma over each H*dv row,
+               dgamma = sum_t dN (.) xhat,  dbeta = sum_t dN,  dxhat = dN gamma,
+               dO = (dxhat - mean(dxhat) - xhat mean(dxhat (.) xhat)) / sigma
+    attention: dQ, dK, dV, d rab from attention_bwd
+    f1:        dZ = [dU | dV | dQ | dK] (.) SiLU'(Z),  Z = X w1^T + b1,
+               dX = dZ w1,   dw1 = dZ^T X,   db1 = sum_t dZ
+
+Parity status: attention_bwd and layer_bwd are pinned by central finite differences of
+hstu_ref.attention and hstu_ref.layer_fwd on small jagged batches
+(tests/test_oracle_bwd.py).
 """
 
 from __future__ import annotations
@@ -145,3 +158,78 @@ def _attention_bwd_rows(q, k, v, d_out, offsets, timestamps, num_heads, dqk, dv,
             dk[s0 + r, cq] = dsk.T @ qh
             dvv[s0 + r, cv] = ak.T @ gh
     return dq, dk, dvv, None, None
+
+
+def _layernorm_parts(o, eps):
+    mu = o.mean(axis=1, keepdims=True)
+    var = ((o - mu) ** 2).mean(axis=1, keepdims=True)
+    sigma = np.sqrt(var + eps)
+    return (o - mu) / sigma, sigma
+
+
+def layer_bwd(x, weights, offsets, timestamps, num_heads: int, dqk: int, dv: int, d_y,
+              eps: float = 1e-5, *, rows=None):
+    """Gradients of hstu_ref.layer_fwd (causal) for the upstream gradient d_y [T][d].
+
+    Returns a dict with dx [T][d] and the parameter gradients dw1, db1, dw2, db2, dgamma,
+    dbeta, drab_pos, drab_time (dgamma / dbeta / drab_* are None when that parameter is
+    None; db1 and db2 are the gradients of a bias added there, formed in any case).
+    rows: if given, only these rows of dx are formed (others 0) and every parameter
+    gradient is None; the forward and dO are formed for the whole of each sequence that
+    holds one of the rows, which the key-side gradients of those rows need.
+    """
+    x = ref._f64(x)
+    g_y = ref._f64(d_y)
+    w1, w2 = ref._f64(weights.w1), ref._f64(weights.w2)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    ts = None if timestamps is None else np.asarray(timestamps, dtype=np.int64)
+    hv, hq = num_heads * dv, num_heads * dqk
+    T = x.shape[0]
+    if rows is not None:
+        rows = np.unique(np.asarray(rows, dtype=np.int64))
+        seqs = np.unique(np.searchsorted(offsets, rows, side="right") - 1)
+        dx = np.zeros_like(x)
+        for b in seqs:
+            s0, s1 = int(offsets[b]), int(offsets[b + 1])
+            sub = layer_bwd(x[s0:s1], weights, np.array([0, s1 - s0]),
+                            None if ts is None else ts[s0:s1], num_heads, dqk, dv,
+                            g_y[s0:s1], eps)
+            r = rows[(rows >= s0) & (rows < s1)]
+            dx[r] = sub["dx"][r - s0]
+        return dict(dx=dx, dw1=None, db1=None, dw2=None, db2=None, dgamma=None, dbeta=None,
+                    drab_pos=None, drab_time=None)
+    # forward pieces
+    z = x @ w1.T
+    if weights.b1 is not None:
+        z = z + ref._f64(weights.b1)[None, :]
+    phi = ref.silu(z)
+    u, v, q, k = (phi[:, :hv], phi[:, hv:2 * hv], phi[:, 2 * hv:2 * hv + hq],
+                  phi[:, 2 * hv + hq:2 * hv + 2 * hq])
+    o = ref.attention(q, k, v, offsets, ts, num_heads, dqk, dv, weights.rab_pos,
+                      weights.rab_time, workers=1)
+    xhat, sigma = _layernorm_parts(o, eps)
+    gamma = None if weights.ln_gamma is None else ref._f64(weights.ln_gamma)
+    beta = None if weights.ln_beta is None else ref._f64(weights.ln_beta)
+    n = xhat * (gamma[None, :] if gamma is not None else 1.0)
+    if beta is not None:
+        n = n + beta[None, :]
+    gate = n * u
+    # f2
+    d_gate = g_y @ w2
+    dw2 = g_y.T @ gate
+    db2 = g_y.sum(axis=0)
+    # gate and LayerNorm
+    du = d_gate * n
+    dn = d_gate * u
+    dgamma = (dn * xhat).sum(axis=0) if gamma is not None else None
+    dbeta = dn.sum(axis=0) if beta is not None else None
+    dxhat = dn * (gamma[None, :] if gamma is not None else 1.0)
+    do = (dxhat - dxhat.mean(axis=1, keepdims=True)
+          - xhat * (dxhat * xhat).mean(axis=1, keepdims=True)) / sigma
+    # attention
+    dq, dk, dvv, dP, dT = attention_bwd(q, k, v, do, offsets, ts, num_heads, dqk, dv,
+                                        weights.rab_pos, weights.rab_time)
+    # f1 and SiLU
+    dz = np.concatenate([du, dvv, dq, dk], axis=1) * silu_grad(z)
+    return dict(dx=dz @ w1, dw1=dz.T @ x, db1=dz.sum(axis=0), dw2=dw2, db2=db2,
+                dgamma=dgamma, dbeta=dbeta, drab_pos=dP, drab_time=dT)

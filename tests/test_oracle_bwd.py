@@ -1,4 +1,4 @@
-"""Pins of the attention-gradient oracle (CPU only).
+"""Pins of the gradient oracles (CPU only).
 
 oracle/hstu_bwd.attention_bwd must be the derivative of oracle/hstu_ref.attention: every
 gradient entry (q, k, v and both bias tables) is compared with a central finite
@@ -10,6 +10,9 @@ a wrong sign, a transposed operand or a wrong mask in the gradient fails these c
 import numpy as np
 import pytest
 
+import dataclasses
+
+from hstu_pointwise_attention_jagged_amd import workloads as wl
 from oracle import hstu_bwd as bwd
 from oracle import hstu_ref as ref
 
@@ -92,3 +95,74 @@ def test_sampled_rows_equal_the_full_gradient():
         np.testing.assert_allclose(p_[mask], f[mask], rtol=1e-12, atol=1e-12)
         assert np.all(p_[~mask] == 0)
     assert part[3] is None and part[4] is None
+
+
+def _layer_case(seed, lengths, d=8, H=2, dh=4, affine=True, bias=True, per_head=True):
+    rng = np.random.default_rng(seed)
+    seq = wl.jagged_from_lengths(rng, lengths)
+    T = seq.total
+    n1 = 2 * H * (dh + dh)
+    w = wl.LayerWeights(
+        w1=rng.standard_normal((n1, d)) / np.sqrt(d), w2=rng.standard_normal((d, H * dh)) / np.sqrt(H * dh),
+        b1=0.3 * rng.standard_normal(n1) if bias else None,
+        b2=0.3 * rng.standard_normal(d) if bias else None,
+        ln_gamma=1 + 0.2 * rng.standard_normal(H * dh) if affine else None,
+        ln_beta=0.2 * rng.standard_normal(H * dh) if affine else None,
+        rab_pos=0.3 * rng.standard_normal((H if per_head else 1, 6)),
+        rab_time=0.3 * rng.standard_normal((H if per_head else 1, 5)))
+    x = rng.standard_normal((T, d))
+    G = rng.standard_normal((T, d))
+    return seq, w, x, G, H, dh
+
+
+def _layer_loss(seq, w, x, G, H, dh):
+    y = ref.layer_fwd(x, w, seq.offsets, seq.timestamps, H, dh, dh, 1e-5, workers=1)
+    return float(np.sum(y * G))
+
+
+@pytest.mark.parametrize("seed,lengths,affine,bias,per_head", [
+    (10, [3, 5, 0, 4], True, True, True),
+    (11, [7, 1], False, False, False),
+])
+def test_layer_gradient_matches_finite_differences(seed, lengths, affine, bias, per_head):
+    # every input and parameter of one layer against a central difference of
+    # L = sum(layer_fwd(...) * G); a wrong term anywhere in the chain (f2, the gate, the
+    # LayerNorm backward, the attention, SiLU' or f1) fails one of these entries
+    seq, w, x, G, H, dh = _layer_case(seed, lengths, affine=affine, bias=bias, per_head=per_head)
+    got = bwd.layer_bwd(x, w, seq.offsets, seq.timestamps, H, dh, dh, G)
+    eps = 1e-6
+    targets = {"dx": ("x", x)}
+    for name, field in (("dw1", "w1"), ("db1", "b1"), ("dw2", "w2"), ("db2", "b2"),
+                        ("dgamma", "ln_gamma"), ("dbeta", "ln_beta"),
+                        ("drab_pos", "rab_pos"), ("drab_time", "rab_time")):
+        if getattr(w, field) is not None:
+            targets[name] = (field, getattr(w, field))
+    for gname, (field, val) in targets.items():
+        num = np.zeros_like(val, dtype=np.float64)
+        for idx in np.ndindex(val.shape):
+            vals = []
+            for sgn in (1, -1):
+                pv = np.array(val, dtype=np.float64, copy=True)
+                pv[idx] += sgn * eps
+                if field == "x":
+                    vals.append(_layer_loss(seq, w, pv, G, H, dh))
+                else:
+                    vals.append(_layer_loss(seq, dataclasses.replace(w, **{field: pv}), x, G, H, dh))
+            num[idx] = (vals[0] - vals[1]) / (2 * eps)
+        scale = max(1.0, float(np.abs(num).max()))
+        np.testing.assert_allclose(got[gname], num, rtol=0, atol=5e-6 * scale, err_msg=gname)
+    if not bias:  # the bias gradients are still formed: those of a zero bias
+        assert got["db1"] is not None and got["db2"] is not None
+    if not affine:
+        assert got["dgamma"] is None and got["dbeta"] is None
+
+
+def test_layer_gradient_rows_equal_the_full_gradient():
+    seq, w, x, G, H, dh = _layer_case(12, [9, 0, 14, 6])
+    full = bwd.layer_bwd(x, w, seq.offsets, seq.timestamps, H, dh, dh, G)
+    rows = [0, 8, 9, 15, 22, 28]
+    part = bwd.layer_bwd(x, w, seq.offsets, seq.timestamps, H, dh, dh, G, rows=rows)
+    np.testing.assert_allclose(part["dx"][rows], full["dx"][rows], rtol=1e-12, atol=1e-12)
+    mask = np.ones(x.shape[0], dtype=bool)
+    mask[rows] = False
+    assert np.all(part["dx"][mask] == 0) and part["dw1"] is None
