@@ -9,7 +9,7 @@ per layer.  Inputs and weights are resident in HBM before the timed region.
 Prints one JSON line on stdout; progress goes to stderr.
 
 Besides the step, the line carries separate measurements of Stochastic Length, M-FALCON
-serving and the attention gradients (hstu_attn_bwd).
+serving, the attention gradients (hstu_attn_bwd) and one layer's backward (hstu_layer_bwd).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers 24] [--no-cpu-baseline]
 """
@@ -216,6 +216,50 @@ def bwd_measure(torch, np, ops, dev, wl, reps=10):
                     "HIP events on the launch stream"}
 
 
+def layer_bwd_measure(torch, np, ops, dev, wl, reps=5):
+    """One layer's backward (hstu_layer_bwd: dX and the gradients of w1, b1, w2, b2) on the
+    8 x 8192-token batch, d = 1024, 8 heads of 128, for dY drawn N(0, 1) on the device.
+    Useful FLOPs: the input and weight gradients of f1 and f2 (2 x 2 T d 2H(dqk+dv) and
+    2 x 2 T H dv d) and the attention gradient's five products per allowed pair and head;
+    the forward pieces the call recomputes (f1 and the attention) are not counted."""
+    w = wl.config(2)
+    d = w.dims
+    dims, seq = dev.dims_of(d), dev.jagged_of(w.seq)
+    rng = np.random.default_rng(1001)
+    dw = dev.weights_of(wl.draw_weights(rng, d, bias=True))
+    x = dev.bf16_tensor(w.x)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4004)
+    d_y = torch.randn((w.seq.total, d.d_model), generator=gen, device="cuda")
+    ws = torch.empty(ops.hstu_layer_bwd_workspace_bytes(dims, seq), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def run():
+        return ops.hstu_layer_bwd(dims, dw, seq, x, d_y, workspace=ws, stream=stream)
+
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    T, dm, H = w.seq.total, d.d_model, d.num_heads
+    n1 = 2 * H * (d.dqk + d.dv)
+    att = sum(10 * d.dqk * H * int(n) * (int(n) + 1) // 2 for n in w.seq.lengths)
+    flops = 2 * 2 * T * dm * n1 + 2 * 2 * T * H * d.dv * dm + att
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": "layer backward (dX, dw1, db1, dw2, db2), 8 x 8192 tokens, d=1024, "
+                        "8 heads x 128, causal, rab pos+time",
+            "ms": round(ms, 4), "useful_flops": flops, "tflops": round(tf, 2),
+            "pct_mfma_peak": round(100 * tf / PEAK_MFMA_TFLOPS, 2),
+            "note": "one hstu_layer_bwd call, HIP events on the launch stream; it recomputes Z, "
+                    "U|V|Q|K and the attention output from X (not counted as useful work)"}
+
+
 def mfalcon_measure(torch, np, ops, dev, wl, n_layers=4, bm=1024, reps=3):
     """M-FALCON serving through an n_layers stack on the 16-user workload: the history
     pass (4096 tokens per user, every layer's K/V kept) and the scoring of 1024
@@ -418,6 +462,8 @@ def main():
     out["mfalcon_serving"] = [mfalcon_measure(torch, np, ops, dev, wl, bm=bm) for bm in (1024, 128)]
     log("attention gradients (dQ, dK, dV) on the 8 x 8192 batch")
     out["attention_backward"] = bwd_measure(torch, np, ops, dev, wl)
+    log("layer backward on the 8 x 8192 batch")
+    out["layer_backward"] = layer_bwd_measure(torch, np, ops, dev, wl)
     if not args.no_cpu_baseline:
         log("cpu baseline: fp64 oracle, one layer on two 8192-token sequences")
         out["cpu_baseline"] = cpu_baseline(w, args.layers)

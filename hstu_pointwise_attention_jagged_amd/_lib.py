@@ -33,6 +33,12 @@ class Weights(ctypes.Structure):
                 ("rab_time", c_void_p)]
 
 
+class LayerGrads(ctypes.Structure):
+    _fields_ = [("w1", c_void_p), ("b1", c_void_p), ("w2", c_void_p), ("b2", c_void_p),
+                ("ln_gamma", c_void_p), ("ln_beta", c_void_p), ("rab_pos", c_void_p),
+                ("rab_time", c_void_p)]
+
+
 class Jagged(ctypes.Structure):
     _fields_ = [("batch", c_int32), ("total_tokens", c_int32), ("max_seq_len", c_int32),
                 ("seq_offsets", c_void_p), ("timestamps", c_void_p)]
@@ -66,6 +72,10 @@ EXPORTS = {
     "hstu_stack_fwd_mfalcon": (c_int32, [ctypes.POINTER(Dims), c_int32, ctypes.POINTER(Weights),
                                          ctypes.POINTER(Jagged), c_void_p, ctypes.POINTER(Jagged),
                                          c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "hstu_layer_bwd_workspace_bytes": (c_size_t, [ctypes.POINTER(Dims), ctypes.POINTER(Jagged)]),
+    "hstu_layer_bwd": (c_int32, [ctypes.POINTER(Dims), ctypes.POINTER(Weights), ctypes.POINTER(Jagged),
+                                 c_void_p, c_void_p, c_void_p, ctypes.POINTER(LayerGrads), c_void_p,
+                                 c_size_t, c_void_p]),
     "hstu_attn_bwd_workspace_bytes": (c_size_t, [ctypes.POINTER(Dims), ctypes.POINTER(Jagged)]),
     "hstu_attn_bwd": (c_int32, [ctypes.POINTER(Dims), c_void_p, c_void_p, ctypes.POINTER(Jagged),
                                 c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p,

@@ -2,7 +2,8 @@
 
 Every HIP source is compiled with packed-FP32 instruction selection disabled
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``); the objects are linked into
-``libhstu.so`` next to this file, where the Python binding loads it from.
+``libhstu.so`` next to this file, where the Python binding loads it from.  The library
+links rocBLAS (the plain GEMMs of the layer backward).
 """
 
 from __future__ import annotations
@@ -19,7 +20,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhstu.so")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 
-HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+HIPCC = os.environ.get("HIPCC", f"{ROCM}/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -53,7 +55,9 @@ def build(verbose: bool = False) -> str:
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
     tmp = LIB + ".tmp"
     # -z defs: an undefined symbol (such as a kernel stub the compiler dropped) fails the link
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", "-o", tmp, *objs]
+    # rocBLAS serves the plain GEMMs of the layer backward
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", "-o", tmp, *objs,
+           f"-L{ROCM}/lib", "-lrocblas", f"-Wl,-rpath,{ROCM}/lib"]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

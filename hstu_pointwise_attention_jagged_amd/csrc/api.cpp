@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <mutex>
+#include <utility>
 #include <vector>
 
 #include "../../include/hstu.h"
@@ -545,6 +546,185 @@ hstu_status_t hstu_attn_bwd(const hstu_dims_t *dims, const float *rab_pos, const
   const int64_t cap = attn_work_capacity(seq->batch, seq->total_tokens);
   e = launch_attention_bwd(a, dims->dqk, cap, seq->total_tokens, sst);
   if (e != hipSuccess) return hip_fail(e);
+  return HSTU_OK;
+}
+
+// ------------------------------------------------------------------------------------
+// Layer backward
+// ------------------------------------------------------------------------------------
+namespace {
+
+constexpr int kColsumParts = 256;
+
+struct LayerBwdWs {
+  uint16_t *z, *uvqk, *d_h, *dy16, *g16, *dz;
+  float *o, *dg, *d_o, *part_cols, *part_gamma, *part_beta;
+  uint32_t *d_max;
+  char *attn;
+};
+
+// z, U|V|Q|K (fp16 [T][n1]), O, dG, dO (fp32 [T][hdv]), the attention scratch, the
+// scaled fp16 dO and its maximum, dY and G in bf16, dZ (bf16 [T][n1]), and the partial
+// column sums of the bias and LayerNorm gradients.
+size_t layer_bwd_ws(const hstu_dims_t *d, const hstu_jagged_t *s, LayerBwdWs *w) {
+  const size_t T = (size_t)s->total_tokens, hdv = (size_t)d->num_heads * d->dv;
+  const size_t n1 = 2 * (size_t)d->num_heads * (d->dqk + d->dv), dm = (size_t)d->d_model;
+  const size_t waves = (size_t)norm_gate_bwd_waves((int)T);
+  const size_t sizes[] = {T * n1 * 2, T * n1 * 2, T * hdv * 4, attn_ws_bytes(s, nullptr),
+                          T * hdv * 2, kAlign, T * dm * 2, T * hdv * 4, T * hdv * 4,
+                          T * hdv * 2, T * n1 * 2, kColsumParts * (n1 > dm ? n1 : dm) * 4,
+                          waves * hdv * 4, waves * hdv * 4};
+  size_t off[sizeof(sizes) / sizeof(sizes[0]) + 1] = {0};
+  for (size_t i = 0; i < sizeof(sizes) / sizeof(sizes[0]); ++i) off[i + 1] = off[i] + align_up(sizes[i]);
+  if (w != nullptr) {
+    char *b = (char *)w->attn;  // the base is passed in through attn
+    w->z = (uint16_t *)(b + off[0]);
+    w->uvqk = (uint16_t *)(b + off[1]);
+    w->o = (float *)(b + off[2]);
+    w->attn = b + off[3];
+    w->d_h = (uint16_t *)(b + off[4]);
+    w->d_max = (uint32_t *)(b + off[5]);
+    w->dy16 = (uint16_t *)(b + off[6]);
+    w->dg = (float *)(b + off[7]);
+    w->d_o = (float *)(b + off[8]);
+    w->g16 = (uint16_t *)(b + off[9]);
+    w->dz = (uint16_t *)(b + off[10]);
+    w->part_cols = (float *)(b + off[11]);
+    w->part_gamma = (float *)(b + off[12]);
+    w->part_beta = (float *)(b + off[13]);
+  }
+  return off[sizeof(sizes) / sizeof(sizes[0])];
+}
+
+}  // namespace
+
+size_t hstu_layer_bwd_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_t *seq) {
+  if (check_dims(dims) != HSTU_OK || check_seq(seq) != HSTU_OK) return 0;
+  return layer_bwd_ws(dims, seq, nullptr);
+}
+
+hstu_status_t hstu_layer_bwd(const hstu_dims_t *dims, const hstu_weights_t *w,
+                             const hstu_jagged_t *seq, const uint16_t *x, const float *d_y,
+                             float *d_x, const hstu_layer_grads_t *grads, void *ws,
+                             size_t ws_bytes, void *stream) {
+  hstu_status_t st;
+  if ((st = check_dims(dims)) != HSTU_OK) return st;
+  if ((st = check_seq(seq)) != HSTU_OK) return st;
+  if ((st = check_weights(w)) != HSTU_OK) return st;
+  if (grads == nullptr || grads->w1 == nullptr || grads->w2 == nullptr) return HSTU_ERR_INVALID_ARG;
+  if (grads->rab_pos != nullptr || grads->rab_time != nullptr) return HSTU_ERR_INVALID_ARG;
+  if ((grads->ln_gamma != nullptr && w->ln_gamma == nullptr) ||
+      (grads->ln_beta != nullptr && w->ln_beta == nullptr))
+    return HSTU_ERR_INVALID_ARG;
+  const void *gr[] = {grads->w1, grads->b1, grads->w2, grads->b2, grads->ln_gamma, grads->ln_beta};
+  for (const void *g : gr)
+    if (!aligned16(g)) return HSTU_ERR_INVALID_ARG;
+  if (seq->total_tokens > 0 && (x == nullptr || d_y == nullptr || d_x == nullptr))
+    return HSTU_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(d_y) || !aligned16(d_x)) return HSTU_ERR_INVALID_ARG;
+  if (seq->total_tokens > 0 && ((const void *)d_x == (const void *)x ||
+                                (const void *)d_x == (const void *)d_y))
+    return HSTU_ERR_INVALID_ARG;
+  for (const void *g : gr)
+    if (g != nullptr && g == (const void *)d_x) return HSTU_ERR_INVALID_ARG;
+  hipStream_t sst = (hipStream_t)stream;
+  const int T = seq->total_tokens;
+  const int dm = dims->d_model, hdv = dims->num_heads * dims->dv, hqk = dims->num_heads * dims->dqk;
+  const int n1 = 2 * (hdv + hqk);
+  if (seq->batch == 0 || T == 0) {  // no token: every formed gradient is zero
+    hipError_t e = hipSuccess;
+    const std::pair<float *, int64_t> z[] = {{grads->w1, (int64_t)n1 * dm}, {grads->b1, n1},
+                                             {grads->w2, (int64_t)dm * hdv}, {grads->b2, dm},
+                                             {grads->ln_gamma, hdv}, {grads->ln_beta, hdv}};
+    for (const auto &p : z)
+      if (e == hipSuccess) e = launch_fill_zero(p.first, p.second, sst);
+    return e == hipSuccess ? HSTU_OK : hip_fail(e);
+  }
+  if ((st = check_ws(ws, ws_bytes, layer_bwd_ws(dims, seq, nullptr))) != HSTU_OK) return st;
+  if (!rows_addressable(seq->max_seq_len, n1)) return HSTU_ERR_UNSUPPORTED;
+  if (attn_block_m(seq->max_seq_len) != 128) return HSTU_ERR_UNSUPPORTED;
+
+  LayerBwdWs b{};
+  b.attn = (char *)ws;
+  layer_bwd_ws(dims, seq, &b);
+  LayerWs lw{};
+  carve_attn(b.attn, seq, nullptr, lw);
+  lw.o = b.o;
+  const uint16_t *q = b.uvqk + 2 * hdv, *k = b.uvqk + 2 * hdv + hqk, *v = b.uvqk + hdv;
+  AttnArgs aa = attn_args(dims, w->rab_pos, w->rab_time, seq, q, k, v, n1, b.o, lw);
+  if ((st = run_setup(seq, aa, lw, nullptr, false, sst)) != HSTU_OK) return st;
+  hipError_t e;
+#define HSTU_TRY(call)            \
+  do {                            \
+    e = (call);                   \
+    if (e != hipSuccess) return hip_fail(e); \
+  } while (0)
+  // forward pieces: Z, U|V|Q|K = SiLU(Z), the attention output O
+  HSTU_TRY(launch_gemm(x, w->w1, w->b1, b.z, T, n1, dm, ACT_NONE, OUT_F16, sst));
+  HSTU_TRY(launch_silu_f16(b.z, b.uvqk, (int64_t)T * n1, sst));
+  const int64_t cap = attn_work_capacity(seq->batch, T);
+  HSTU_TRY(launch_attention(aa, dims->dqk, seq->max_seq_len, cap, sst));
+  // f2: dG = dY w2, then the gate and LayerNorm backward, then dw2 = dY^T G, db2
+  HSTU_TRY(launch_cast_bf16(d_y, b.dy16, (int64_t)T * dm, sst));
+  HSTU_TRY(blas_gemm_bf16(false, false, T, hdv, dm, b.dy16, dm, w->w2, hdv, b.dg, hdv, 0.0f, sst));
+  NormGateBwdArgs ng{};
+  ng.o = b.o;
+  ng.dg = b.dg;
+  ng.u = b.uvqk;
+  ng.zu = b.z;
+  ng.u_stride = n1;
+  ng.gamma = w->ln_gamma;
+  ng.beta = w->ln_beta;
+  ng.eps = dims->ln_eps;
+  ng.g = b.g16;
+  ng.dzu = b.dz;
+  ng.dz_stride = n1;
+  ng.d_o = b.d_o;
+  ng.part_gamma = grads->ln_gamma != nullptr ? b.part_gamma : nullptr;
+  ng.part_beta = grads->ln_beta != nullptr ? b.part_beta : nullptr;
+  ng.T = T;
+  ng.hdv = hdv;
+  HSTU_TRY(launch_norm_gate_bwd(ng, sst));
+  HSTU_TRY(blas_gemm_bf16(true, false, dm, hdv, T, b.dy16, dm, b.g16, hdv, grads->w2, hdv, 0.0f, sst));
+  if (grads->b2 != nullptr)
+    HSTU_TRY(launch_colsum(d_y, false, T, dm, dm, b.part_cols, kColsumParts, grads->b2, sst));
+  const int waves = norm_gate_bwd_waves(T);
+  if (grads->ln_gamma != nullptr) HSTU_TRY(launch_sum_parts(b.part_gamma, waves, hdv, grads->ln_gamma, sst));
+  if (grads->ln_beta != nullptr) HSTU_TRY(launch_sum_parts(b.part_beta, waves, hdv, grads->ln_beta, sst));
+  // attention: dZ of the V, Q, K columns
+  AttnBwdArgs a{};
+  a.offsets = seq->seq_offsets;
+  a.ts = seq->timestamps;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.stride = n1;
+  a.d_out = b.d_o;
+  a.d_stride = hdv;
+  a.d_h = b.d_h;
+  a.d_max = b.d_max;
+  a.stat = (w->rab_time != nullptr && seq->timestamps != nullptr) ? lw.kstat : nullptr;
+  a.rab_pos = w->rab_pos;
+  a.rab_time = w->rab_time;
+  a.pos_buckets = dims->pos_buckets;
+  a.time_buckets = dims->time_buckets;
+  a.rab_per_head = dims->rab_heads == dims->num_heads && dims->num_heads > 1;
+  a.work = lw.work;
+  a.n_work = lw.n_work;
+  a.num_heads = dims->num_heads;
+  a.z = b.z;
+  a.dz = b.dz;
+  a.z_stride = n1;
+  a.zq_off = 2 * hdv;
+  a.zk_off = 2 * hdv + hqk;
+  a.zv_off = hdv;
+  HSTU_TRY(launch_attention_bwd(a, dims->dqk, cap, T, sst));
+  // f1: dX = dZ w1, dw1 = dZ^T X, db1
+  HSTU_TRY(blas_gemm_bf16(false, false, T, dm, n1, b.dz, n1, w->w1, dm, d_x, dm, 0.0f, sst));
+  HSTU_TRY(blas_gemm_bf16(true, false, n1, dm, T, b.dz, n1, x, dm, grads->w1, dm, 0.0f, sst));
+  if (grads->b1 != nullptr)
+    HSTU_TRY(launch_colsum(b.dz, true, T, n1, n1, b.part_cols, kColsumParts, grads->b1, sst));
+#undef HSTU_TRY
   return HSTU_OK;
 }
 

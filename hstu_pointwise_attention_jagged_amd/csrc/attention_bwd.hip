@@ -275,6 +275,25 @@ __global__ __launch_bounds__(256) void bwd_cast_kernel(const float *d_out, int64
   }
 }
 
+// bf16 dz = acc x inv x SiLU'(z) for one lane's 4 x FT values of a row: features
+// f 32 + g 8 + (0..3) from element base (the lane's 4-feature offset already added)
+template <int FT>
+__device__ __forceinline__ void store_dz(const f32x16 *acc, float inv, const AttnBwdArgs &p,
+                                         int64_t base) {
+#pragma unroll
+  for (int f = 0; f < FT; ++f)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int64_t e = base + f * 32 + g * 8;
+      const u32x2 zz = *reinterpret_cast<const u32x2 *>(p.z + e);
+      const float z[4] = {f16_lo(zz[0]), f16_hi(zz[0]), f16_lo(zz[1]), f16_hi(zz[1])};
+      float r[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r[j] = acc[f][4 * g + j] * inv * silu_grad(z[j]);
+      *reinterpret_cast<u32x2 *>(p.dz + e) = u32x2{pack_bf16(r[0], r[1]), pack_bf16(r[2], r[3])};
+    }
+}
+
 __device__ __forceinline__ void load_tables(const AttnBwdArgs &p, int h, float *ptab, float *ttab,
                                             BiasCtx &bc) {
   const int rrow = p.rab_per_head ? h : 0;
@@ -406,14 +425,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(AttnBwdArgs p)
   if (q_ok) {
     float inv;
     (void)d_scale(p.d_max, inv);
-    float *orow = p.dq + (int64_t)(s0 + qi) * p.g_stride + h * DH + half * 4;
+    if (p.dz != nullptr) {
+      store_dz<FT>(acc, inv, p, (int64_t)(s0 + qi) * p.z_stride + p.zq_off + h * DH + half * 4);
+    } else {
+      float *orow = p.dq + (int64_t)(s0 + qi) * p.g_stride + h * DH + half * 4;
 #pragma unroll
-    for (int f = 0; f < FT; ++f)
+      for (int f = 0; f < FT; ++f)
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<f32x4 *>(orow + f * 32 + g * 8) =
-            f32x4{acc[f][4 * g] * inv, acc[f][4 * g + 1] * inv, acc[f][4 * g + 2] * inv,
-                  acc[f][4 * g + 3] * inv};
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<f32x4 *>(orow + f * 32 + g * 8) =
+              f32x4{acc[f][4 * g] * inv, acc[f][4 * g + 1] * inv, acc[f][4 * g + 2] * inv,
+                    acc[f][4 * g + 3] * inv};
+    }
   }
 }
 
@@ -545,7 +568,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkv_kernel(AttnBwdArgs p
       }
     }
   }
-  if (k_ok) {
+  if (k_ok && p.dz != nullptr) {
+    float inv;
+    (void)d_scale(p.d_max, inv);
+    const int64_t rb = (int64_t)(s0 + kj) * p.z_stride + h * DH + half * 4;
+    store_dz<FT>(dk_acc, inv, p, rb + p.zk_off);
+    store_dz<FT>(dv_acc, inv, p, rb + p.zv_off);
+  } else if (k_ok) {
     float inv;
     (void)d_scale(p.d_max, inv);
     float *kr = p.dk + (int64_t)(s0 + kj) * p.g_stride + h * DH + half * 4;

@@ -357,6 +357,11 @@ hipError_t launch_gemm(const uint16_t *A, const uint16_t *W, const float *bias, 
     return wide ? launch_tile<128, 128, ACT_SILU, OUT_F16>(A, W, bias, out, M, N, K, stream)
                 : launch_tile<128, 64, ACT_SILU, OUT_F16>(A, W, bias, out, M, N, K, stream);
   }
+  if (act == ACT_NONE && out_type == OUT_F16) {  // pre-activations (the backward's recompute)
+    if (big) return launch_big<ACT_NONE, OUT_F16>(A, W, bias, out, M, N, K, stream);
+    return wide ? launch_tile<128, 128, ACT_NONE, OUT_F16>(A, W, bias, out, M, N, K, stream)
+                : launch_tile<128, 64, ACT_NONE, OUT_F16>(A, W, bias, out, M, N, K, stream);
+  }
   if (act == ACT_NONE && out_type == OUT_BF16) {
     if (big) return launch_big<ACT_NONE, OUT_BF16>(A, W, bias, out, M, N, K, stream);
     return wide ? launch_tile<128, 128, ACT_NONE, OUT_BF16>(A, W, bias, out, M, N, K, stream)

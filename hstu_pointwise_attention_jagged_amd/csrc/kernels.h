@@ -49,6 +49,12 @@ struct AttnBwdArgs {
   uint16_t *d_h;              // workspace [T][H*dv]: d_out x 2^-e in fp16 (same stride)
   uint32_t *d_max;            // workspace [1]: bits of max |d_out| (e is its exponent)
   const int2 *stat;           // (min, max) timestamp of each 32-row block, when ts is set
+  // Output form.  z == nullptr: fp32 dq, dk, dv (g_stride).  Otherwise the gradients of
+  // the pre-activations: bf16 dz = grad * SiLU'(z) at row r, column off + h dh + c of z
+  // and dz (pitch z_stride), with off = zq_off, zk_off, zv_off for Q, K, V.
+  const uint16_t *z;
+  uint16_t *dz;
+  int64_t z_stride, zq_off, zk_off, zv_off;
   const float *rab_pos;       // [rab_heads][pos_buckets] or nullptr
   const float *rab_time;      // [rab_heads][time_buckets] or nullptr
   int pos_buckets, time_buckets, rab_per_head;
@@ -58,6 +64,40 @@ struct AttnBwdArgs {
   const int32_t *n_work;      // [1]
   int num_heads;
 };
+
+// Backward of LayerNorm + gate for every row (see layer_bwd.hip).
+struct NormGateBwdArgs {
+  const float *o;       // [T][hdv] attention output
+  const float *dg;      // [T][hdv] gradient of the gate product G
+  const uint16_t *u;    // fp16 gate U, row pitch u_stride
+  const uint16_t *zu;   // fp16 pre-activations of U, row pitch u_stride
+  int64_t u_stride;
+  const float *gamma, *beta;  // [hdv] or nullptr
+  float eps;
+  uint16_t *g;          // bf16 [T][hdv]: G = LayerNorm(O) U
+  uint16_t *dzu;        // bf16 gate columns of dZ, row pitch dz_stride
+  int64_t dz_stride;
+  float *d_o;           // [T][hdv]: gradient of O
+  float *part_gamma, *part_beta;  // [norm_gate_bwd_waves(T)][hdv] partial sums or nullptr
+  int T, hdv;
+};
+constexpr int kNgWaves = 1024;  // most waves (and partial rows) of the norm-gate backward
+int norm_gate_bwd_waves(int T);
+hipError_t launch_norm_gate_bwd(const NormGateBwdArgs &a, hipStream_t stream);
+hipError_t launch_silu_f16(const uint16_t *z, uint16_t *out, int64_t n, hipStream_t stream);
+hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t stream);  // a kernel, not a memset
+hipError_t launch_cast_bf16(const float *src, uint16_t *dst, int64_t n, hipStream_t stream);
+// out[c] = sum of column c of a [rows][cols] matrix (fp32, or bf16 when bf16), through
+// n_parts partial rows in `partial` ([n_parts][cols]); fixed summation order.
+hipError_t launch_colsum(const void *a, bool bf16, int rows, int cols, int64_t stride,
+                         float *partial, int n_parts, float *out, hipStream_t stream);
+hipError_t launch_sum_parts(const float *partial, int n_parts, int cols, float *out,
+                            hipStream_t stream);
+// Row-major C[M][N] (fp32, pitch ldc) = op(A) op(B) + beta C with bf16 A, B (rocBLAS):
+// op(A) = A [M][K] (pitch lda), or A^T with A [K][M] when a_trans; likewise B.
+hipError_t blas_gemm_bf16(bool a_trans, bool b_trans, int M, int N, int K, const uint16_t *A,
+                          int64_t lda, const uint16_t *B, int64_t ldb, float *C, int64_t ldc,
+                          float beta, hipStream_t stream);
 
 // dQ, dK, dV for every row: the scaled fp16 copy of d_out, then two kernels over the
 // schedule's (sequence, 128-row tile) list.  stat must be filled when ts is set.

@@ -22,6 +22,7 @@ __all__ = ["HSTUError", "LayerDims", "DeviceWeights", "DeviceJagged", "hstu_laye
            "hstu_sl_workspace_bytes", "hstu_stochastic_length", "hstu_stack_fwd",
            "hstu_stack_fwd_mfalcon", "hstu_stack_workspace_bytes",
            "hstu_stack_mfalcon_workspace_bytes", "hstu_attn_bwd", "hstu_attn_bwd_workspace_bytes",
+           "hstu_layer_bwd", "hstu_layer_bwd_workspace_bytes",
            "profile_enable", "profile_reset", "profile_collect"]
 
 
@@ -365,6 +366,47 @@ def hstu_stochastic_length(raw: DeviceJagged, u_keep: torch.Tensor, keys: torch.
                                     ws.numel() * ws.element_size(), _stream(stream))
     _raise(st, "hstu_stochastic_length")
     return kept, new_off, new_ts, x_out
+
+
+def hstu_layer_bwd_workspace_bytes(dims: LayerDims, seq: DeviceJagged) -> int:
+    lib = _lib.load()
+    d, s = dims.c(), seq.c()
+    return int(lib.hstu_layer_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(s)))
+
+
+def hstu_layer_bwd(dims: LayerDims, w: DeviceWeights, seq: DeviceJagged, x: torch.Tensor,
+                   d_y: torch.Tensor, *, bias_grads: bool = True,
+                   workspace: Optional[torch.Tensor] = None, stream=None):
+    """Backward of one causal layer for the upstream gradient d_y (fp32 [T][d]).
+
+    Returns (d_x, grads): d_x fp32 [T][d]; grads a dict of fp32 tensors w1, w2 and, when
+    asked for, b1, b2 (bias_grads) and ln_gamma / ln_beta (when the weights have them)."""
+    lib = _lib.load()
+    _check(x, torch.bfloat16, "x")
+    _check(d_y, torch.float32, "d_y")
+    dev = x.device
+    n1 = dims.uvqk_width
+    f32 = dict(dtype=torch.float32, device=dev)
+    d_x = torch.empty((seq.total_tokens, dims.d_model), **f32)
+    grads = {"w1": torch.empty((n1, dims.d_model), **f32),
+             "w2": torch.empty((dims.d_model, dims.hdv), **f32)}
+    if bias_grads:
+        grads["b1"] = torch.empty(n1, **f32)
+        grads["b2"] = torch.empty(dims.d_model, **f32)
+    if w.ln_gamma is not None:
+        grads["ln_gamma"] = torch.empty(dims.hdv, **f32)
+    if w.ln_beta is not None:
+        grads["ln_beta"] = torch.empty(dims.hdv, **f32)
+    gc = _lib.LayerGrads(*(_ptr(grads.get(n)) for n in
+                           ("w1", "b1", "w2", "b2", "ln_gamma", "ln_beta", "rab_pos", "rab_time")))
+    d, wc, s = dims.c(), w.c(), seq.c()
+    need = int(lib.hstu_layer_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(s)))
+    ws = _workspace(need, dev, workspace)
+    st = lib.hstu_layer_bwd(ctypes.byref(d), ctypes.byref(wc), ctypes.byref(s), _ptr(x), _ptr(d_y),
+                            _ptr(d_x), ctypes.byref(gc), _ptr(ws), ws.numel() * ws.element_size(),
+                            _stream(stream))
+    _raise(st, "hstu_layer_bwd")
+    return d_x, grads
 
 
 def hstu_attn_bwd_workspace_bytes(dims: LayerDims, seq: DeviceJagged) -> int:

@@ -261,6 +261,41 @@ hstu_status_t hstu_attn_bwd(const hstu_dims_t *dims, const float *rab_pos,
                             int64_t row_stride, const float *d_out, float *dq, float *dk,
                             float *dv, void *ws, size_t ws_bytes, void *stream);
 
+/* Gradients of the layer's parameters: device fp32 buffers owned by the caller, in the
+ * layouts of hstu_weights_t.  A NULL entry is not formed.                            */
+typedef struct {
+  float *w1;        /* [2H(dv+dqk)][d], required                                       */
+  float *b1;        /* [2H(dv+dqk)]: gradient of a bias added after f1 (also when the  */
+                    /* weights have none) or NULL                                      */
+  float *w2;        /* [d][H*dv], required                                             */
+  float *b2;        /* [d] or NULL, likewise                                           */
+  float *ln_gamma;  /* [H*dv] or NULL; must be NULL when the weights have no ln_gamma  */
+  float *ln_beta;   /* [H*dv] or NULL; must be NULL when the weights have no ln_beta   */
+  float *rab_pos;   /* must be NULL: gradients of the bias tables are not formed       */
+  float *rab_time;  /* must be NULL                                                    */
+} hstu_layer_grads_t;
+
+/* Workspace (bytes) needed by hstu_layer_bwd; 0 when the arguments are invalid.       */
+size_t hstu_layer_bwd_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_t *seq);
+
+/* Backward of one causal layer (equations 1-3) for the upstream gradient d_y of its
+ * output: dX and the parameter gradients, by the chain rule through f2, the U gate,
+ * LayerNorm, the pointwise attention (as hstu_attn_bwd), SiLU and f1.  The forward
+ * pieces it needs (Z = X w1^T + b1, U|V|Q|K, the attention output) are recomputed from
+ * x, so the forward keeps no activations for it.  Matrix products take bf16 operands
+ * (dY, G = LayerNorm(O) U and dZ rounded to bf16; the attention's as in hstu_attn_bwd)
+ * with fp32 accumulation; every result is fp32 and deterministic.
+ *   x    (device) bf16 [T][d], the layer input
+ *   d_y  (device) fp32 [T][d];   d_x (device) fp32 [T][d]
+ *   grads: see hstu_layer_grads_t; an empty batch sets every formed gradient to 0.
+ * HSTU_ERR_INVALID_ARG for a null or misaligned pointer, d_x equal to another buffer,
+ * a required gradient missing or a gradient asked for a parameter the weights lack;
+ * otherwise the shape rules and errors of hstu_layer_fwd.                            */
+hstu_status_t hstu_layer_bwd(const hstu_dims_t *dims, const hstu_weights_t *w,
+                             const hstu_jagged_t *seq, const uint16_t *x, const float *d_y,
+                             float *d_x, const hstu_layer_grads_t *grads, void *ws,
+                             size_t ws_bytes, void *stream);
+
 /* Debug check of device offsets: off[0] == 0, non-decreasing, off[B] == total_tokens,
  * every length <= max_seq_len.  Synchronises the stream.  Returns HSTU_OK or
  * HSTU_ERR_INVALID_ARG.                                                              */

@@ -167,38 +167,11 @@ def _layernorm_parts(o, eps):
     return (o - mu) / sigma, sigma
 
 
-def layer_bwd(x, weights, offsets, timestamps, num_heads: int, dqk: int, dv: int, d_y,
-              eps: float = 1e-5, *, rows=None):
-    """Gradients of hstu_ref.layer_fwd (causal) for the upstream gradient d_y [T][d].
-
-    Returns a dict with dx [T][d] and the parameter gradients dw1, db1, dw2, db2, dgamma,
-    dbeta, drab_pos, drab_time (dgamma / dbeta / drab_* are None when that parameter is
-    None; db1 and db2 are the gradients of a bias added there, formed in any case).
-    rows: if given, only these rows of dx are formed (others 0) and every parameter
-    gradient is None; the forward and dO are formed for the whole of each sequence that
-    holds one of the rows, which the key-side gradients of those rows need.
-    """
-    x = ref._f64(x)
-    g_y = ref._f64(d_y)
+def _forward_and_d_o(x, weights, offsets, ts, num_heads, dqk, dv, g_y, eps, workers):
+    """The forward pieces the gradient needs and everything up to dO (the attention
+    output's gradient), for every row."""
     w1, w2 = ref._f64(weights.w1), ref._f64(weights.w2)
-    offsets = np.asarray(offsets, dtype=np.int64)
-    ts = None if timestamps is None else np.asarray(timestamps, dtype=np.int64)
     hv, hq = num_heads * dv, num_heads * dqk
-    T = x.shape[0]
-    if rows is not None:
-        rows = np.unique(np.asarray(rows, dtype=np.int64))
-        seqs = np.unique(np.searchsorted(offsets, rows, side="right") - 1)
-        dx = np.zeros_like(x)
-        for b in seqs:
-            s0, s1 = int(offsets[b]), int(offsets[b + 1])
-            sub = layer_bwd(x[s0:s1], weights, np.array([0, s1 - s0]),
-                            None if ts is None else ts[s0:s1], num_heads, dqk, dv,
-                            g_y[s0:s1], eps)
-            r = rows[(rows >= s0) & (rows < s1)]
-            dx[r] = sub["dx"][r - s0]
-        return dict(dx=dx, dw1=None, db1=None, dw2=None, db2=None, dgamma=None, dbeta=None,
-                    drab_pos=None, drab_time=None)
-    # forward pieces
     z = x @ w1.T
     if weights.b1 is not None:
         z = z + ref._f64(weights.b1)[None, :]
@@ -206,7 +179,7 @@ def layer_bwd(x, weights, offsets, timestamps, num_heads: int, dqk: int, dv: int
     u, v, q, k = (phi[:, :hv], phi[:, hv:2 * hv], phi[:, 2 * hv:2 * hv + hq],
                   phi[:, 2 * hv + hq:2 * hv + 2 * hq])
     o = ref.attention(q, k, v, offsets, ts, num_heads, dqk, dv, weights.rab_pos,
-                      weights.rab_time, workers=1)
+                      weights.rab_time, workers=workers)
     xhat, sigma = _layernorm_parts(o, eps)
     gamma = None if weights.ln_gamma is None else ref._f64(weights.ln_gamma)
     beta = None if weights.ln_beta is None else ref._f64(weights.ln_beta)
@@ -214,22 +187,58 @@ def layer_bwd(x, weights, offsets, timestamps, num_heads: int, dqk: int, dv: int
     if beta is not None:
         n = n + beta[None, :]
     gate = n * u
-    # f2
-    d_gate = g_y @ w2
-    dw2 = g_y.T @ gate
-    db2 = g_y.sum(axis=0)
-    # gate and LayerNorm
-    du = d_gate * n
+    d_gate = g_y @ w2                       # f2
+    du = d_gate * n                         # the gate
     dn = d_gate * u
-    dgamma = (dn * xhat).sum(axis=0) if gamma is not None else None
-    dbeta = dn.sum(axis=0) if beta is not None else None
     dxhat = dn * (gamma[None, :] if gamma is not None else 1.0)
-    do = (dxhat - dxhat.mean(axis=1, keepdims=True)
+    do = (dxhat - dxhat.mean(axis=1, keepdims=True)  # LayerNorm
           - xhat * (dxhat * xhat).mean(axis=1, keepdims=True)) / sigma
-    # attention
-    dq, dk, dvv, dP, dT = attention_bwd(q, k, v, do, offsets, ts, num_heads, dqk, dv,
-                                        weights.rab_pos, weights.rab_time)
-    # f1 and SiLU
-    dz = np.concatenate([du, dvv, dq, dk], axis=1) * silu_grad(z)
-    return dict(dx=dz @ w1, dw1=dz.T @ x, db1=dz.sum(axis=0), dw2=dw2, db2=db2,
-                dgamma=dgamma, dbeta=dbeta, drab_pos=dP, drab_time=dT)
+    return dict(z=z, u=u, v=v, q=q, k=k, xhat=xhat, gate=gate, du=du, dn=dn, do=do,
+                gamma=gamma, beta=beta)
+
+
+def layer_bwd(x, weights, offsets, timestamps, num_heads: int, dqk: int, dv: int, d_y,
+              eps: float = 1e-5, *, rows=None, workers=None):
+    """Gradients of hstu_ref.layer_fwd (causal) for the upstream gradient d_y [T][d].
+
+    Returns a dict with dx [T][d] and the parameter gradients dw1, db1, dw2, db2, dgamma,
+    dbeta, drab_pos, drab_time (dgamma / dbeta / drab_* are None when that parameter is
+    None; db1 and db2 are the gradients of a bias added there, formed in any case).
+    rows: if given, only these rows of dx are formed (others 0) and every parameter
+    gradient is None.  The forward and dO are then formed for the whole of each sequence
+    that holds one of the rows (the key-side gradients of a row need dO of every later
+    query), and the attention gradient at those rows only.
+    """
+    x = ref._f64(x)
+    g_y = ref._f64(d_y)
+    w1 = ref._f64(weights.w1)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    ts = None if timestamps is None else np.asarray(timestamps, dtype=np.int64)
+    if rows is not None:
+        rows = np.unique(np.asarray(rows, dtype=np.int64))
+        seqs = np.unique(np.searchsorted(offsets, rows, side="right") - 1)
+        dx = np.zeros_like(x)
+        for b in seqs:
+            s0, s1 = int(offsets[b]), int(offsets[b + 1])
+            off_b = np.array([0, s1 - s0])
+            ts_b = None if ts is None else ts[s0:s1]
+            f = _forward_and_d_o(x[s0:s1], weights, off_b, ts_b, num_heads, dqk, dv,
+                                 g_y[s0:s1], eps, workers)
+            r = rows[(rows >= s0) & (rows < s1)] - s0
+            dq, dk, dvv, _, _ = attention_bwd(f["q"], f["k"], f["v"], f["do"], off_b, ts_b,
+                                              num_heads, dqk, dv, weights.rab_pos,
+                                              weights.rab_time, rows=r)
+            dz = np.concatenate([f["du"][r], dvv[r], dq[r], dk[r]], axis=1) * silu_grad(f["z"][r])
+            dx[s0 + r] = dz @ w1
+        return dict(dx=dx, dw1=None, db1=None, dw2=None, db2=None, dgamma=None, dbeta=None,
+                    drab_pos=None, drab_time=None)
+    f = _forward_and_d_o(x, weights, offsets, ts, num_heads, dqk, dv, g_y, eps,
+                         1 if workers is None else workers)
+    dq, dk, dvv, dP, dT = attention_bwd(f["q"], f["k"], f["v"], f["do"], offsets, ts,
+                                        num_heads, dqk, dv, weights.rab_pos, weights.rab_time)
+    dz = np.concatenate([f["du"], dvv, dq, dk], axis=1) * silu_grad(f["z"])  # f1 and SiLU
+    return dict(dx=dz @ w1, dw1=dz.T @ x, db1=dz.sum(axis=0), dw2=g_y.T @ f["gate"],
+                db2=g_y.sum(axis=0),
+                dgamma=(f["dn"] * f["xhat"]).sum(axis=0) if f["gamma"] is not None else None,
+                dbeta=f["dn"].sum(axis=0) if f["beta"] is not None else None,
+                drab_pos=dP, drab_time=dT)

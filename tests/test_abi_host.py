@@ -242,3 +242,25 @@ def test_attn_bwd_argument_checks(lib):
     assert call(dims=_dims(dqk=48, dv=48)) == _lib.HSTU_ERR_UNSUPPORTED
     # empty batch: nothing to do, nothing launched
     assert call(seq=_lib.Jagged(0, 0, 0, FAKE, None), ws=None, ws_bytes=0) == _lib.HSTU_OK
+
+
+def test_layer_bwd_argument_checks(lib):
+    d, s = _dims(), _seq()
+    need = lib.hstu_layer_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(s))
+    assert need > lib.hstu_layer_workspace_bytes(ctypes.byref(d), ctypes.byref(s))
+    w = _lib.Weights(FAKE, None, FAKE, None, None, None, None, None)
+    G = FAKE + (1 << 24)
+
+    def call(grads, weights=w, x=FAKE, dy=FAKE + 4096, dx=FAKE + 8192, ws_bytes=need, seq=s):
+        return lib.hstu_layer_bwd(ctypes.byref(d), ctypes.byref(weights), ctypes.byref(seq), x, dy,
+                                  dx, ctypes.byref(grads), FAKE, ws_bytes, None)
+    ok = _lib.LayerGrads(G, None, G + 65536, None, None, None, None, None)
+    assert call(_lib.LayerGrads(None, None, G, None, None, None, None, None)) == _lib.HSTU_ERR_INVALID_ARG
+    assert call(_lib.LayerGrads(G, None, G + 65536, None, None, None, G + 8, None)) == _lib.HSTU_ERR_INVALID_ARG
+    # a LayerNorm gradient for weights without the affine parameters
+    assert call(_lib.LayerGrads(G, None, G + 65536, None, G + 4096, None, None, None)) == _lib.HSTU_ERR_INVALID_ARG
+    assert call(ok, dx=FAKE) == _lib.HSTU_ERR_INVALID_ARG        # d_x aliases x
+    assert call(ok, dx=FAKE + 4) == _lib.HSTU_ERR_INVALID_ARG    # misaligned
+    assert call(_lib.LayerGrads(G, None, G + 65536, None, None, None, None, None),
+                dx=G) == _lib.HSTU_ERR_INVALID_ARG                # d_x aliases a gradient
+    assert call(ok, ws_bytes=need - 1) == _lib.HSTU_ERR_WORKSPACE
