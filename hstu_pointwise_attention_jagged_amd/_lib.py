@@ -79,7 +79,8 @@ EXPORTS = {
     "hstu_attn_bwd_workspace_bytes": (c_size_t, [ctypes.POINTER(Dims), ctypes.POINTER(Jagged)]),
     "hstu_attn_bwd": (c_int32, [ctypes.POINTER(Dims), c_void_p, c_void_p, ctypes.POINTER(Jagged),
                                 c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p,
-                                c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+                                c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                c_void_p]),
     "hstu_sl_workspace_bytes": (c_size_t, [ctypes.POINTER(Jagged)]),
     "hstu_stochastic_length": (c_int32, [ctypes.POINTER(Jagged), c_void_p, c_void_p, c_int32, c_double,
                                          c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int64,

@@ -464,9 +464,16 @@ hstu_status_t hstu_stack_fwd_mfalcon(const hstu_dims_t *dims, int32_t n_layers,
 
 // The schedule and block statistics of the forward, then the fp16 copy of d_out and the
 // word that holds max |d_out|.
+// Per-work-item bins of the bias-table gradients: [H][cap][pos_buckets + time_buckets].
+static size_t rab_part_bytes(const hstu_dims_t *d, const hstu_jagged_t *s) {
+  return align_up((size_t)attn_work_capacity(s->batch, s->total_tokens) * d->num_heads *
+                  (d->pos_buckets + d->time_buckets) * sizeof(float));
+}
+
 static size_t attn_bwd_ws_bytes(const hstu_dims_t *d, const hstu_jagged_t *s) {
   return attn_ws_bytes(s, nullptr) +
-         align_up((size_t)s->total_tokens * d->num_heads * d->dv * sizeof(uint16_t)) + kAlign;
+         align_up((size_t)s->total_tokens * d->num_heads * d->dv * sizeof(uint16_t)) + kAlign +
+         rab_part_bytes(d, s);
 }
 
 size_t hstu_attn_bwd_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_t *seq) {
@@ -477,10 +484,13 @@ size_t hstu_attn_bwd_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_
 hstu_status_t hstu_attn_bwd(const hstu_dims_t *dims, const float *rab_pos, const float *rab_time,
                             const hstu_jagged_t *seq, const uint16_t *q, const uint16_t *k,
                             const uint16_t *v, int64_t row_stride, const float *d_out,
-                            float *dq, float *dk, float *dv, void *ws, size_t ws_bytes,
-                            void *stream) {
+                            float *dq, float *dk, float *dv, float *d_rab_pos,
+                            float *d_rab_time, void *ws, size_t ws_bytes, void *stream) {
   hstu_status_t st;
   if ((st = check_attn_dims(dims)) != HSTU_OK) return st;
+  if ((d_rab_pos != nullptr && rab_pos == nullptr) || (d_rab_time != nullptr && rab_time == nullptr))
+    return HSTU_ERR_INVALID_ARG;
+  if (!aligned16(d_rab_pos) || !aligned16(d_rab_time)) return HSTU_ERR_INVALID_ARG;
   if ((st = check_seq(seq)) != HSTU_OK) return st;
   const int64_t hq = (int64_t)dims->num_heads * dims->dqk;
   if (seq->total_tokens > 0 && (q == nullptr || k == nullptr || v == nullptr ||
@@ -491,6 +501,7 @@ hstu_status_t hstu_attn_bwd(const hstu_dims_t *dims, const float *rab_pos, const
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(d_out) || !aligned16(dq) ||
       !aligned16(dk) || !aligned16(dv))
     return HSTU_ERR_INVALID_ARG;
+  const int rab_rows = dims->rab_heads == dims->num_heads && dims->num_heads > 1 ? dims->num_heads : 1;
   if (seq->total_tokens > 0) {  // three distinct outputs, none of them an input
     const void *outs[3] = {dq, dk, dv};
     const void *ins[4] = {q, k, v, d_out};
@@ -501,7 +512,12 @@ hstu_status_t hstu_attn_bwd(const hstu_dims_t *dims, const float *rab_pos, const
         if (outs[i] == in) return HSTU_ERR_INVALID_ARG;
     }
   }
-  if (seq->batch == 0 || seq->total_tokens == 0) return HSTU_OK;
+  if (seq->batch == 0 || seq->total_tokens == 0) {  // no pair: the table gradients are zero
+    hipError_t e = launch_fill_zero(d_rab_pos, (int64_t)rab_rows * dims->pos_buckets, (hipStream_t)stream);
+    if (e == hipSuccess)
+      e = launch_fill_zero(d_rab_time, (int64_t)rab_rows * dims->time_buckets, (hipStream_t)stream);
+    return e == hipSuccess ? HSTU_OK : hip_fail(e);
+  }
   if ((st = check_ws(ws, ws_bytes, attn_bwd_ws_bytes(dims, seq))) != HSTU_OK) return st;
   if (attn_block_m(seq->max_seq_len) != 128) return HSTU_ERR_UNSUPPORTED;  // the kernels' tile
   if (!rows_addressable(seq->max_seq_len, row_stride)) return HSTU_ERR_UNSUPPORTED;
@@ -512,6 +528,12 @@ hstu_status_t hstu_attn_bwd(const hstu_dims_t *dims, const float *rab_pos, const
   AttnBwdArgs a{};
   a.d_h = (uint16_t *)tail;
   a.d_max = (uint32_t *)(tail + align_up((size_t)seq->total_tokens * hq * sizeof(uint16_t)));
+  if (d_rab_pos != nullptr || d_rab_time != nullptr) {
+    a.rab_part = (float *)(tail + align_up((size_t)seq->total_tokens * hq * sizeof(uint16_t)) + kAlign);
+    a.rab_cap = attn_work_capacity(seq->batch, seq->total_tokens);
+    a.d_rab_pos = d_rab_pos;
+    a.d_rab_time = d_rab_time;
+  }
   const bool use_time = rab_time != nullptr && seq->timestamps != nullptr;
   a.stat = use_time ? lw.kstat : nullptr;
   a.offsets = seq->seq_offsets;
@@ -558,7 +580,7 @@ constexpr int kColsumParts = 256;
 
 struct LayerBwdWs {
   uint16_t *z, *uvqk, *d_h, *dy16, *g16, *dz;
-  float *o, *dg, *d_o, *part_cols, *part_gamma, *part_beta;
+  float *o, *dg, *d_o, *part_cols, *part_gamma, *part_beta, *rab_part;
   uint32_t *d_max;
   char *attn;
 };
@@ -573,7 +595,7 @@ size_t layer_bwd_ws(const hstu_dims_t *d, const hstu_jagged_t *s, LayerBwdWs *w)
   const size_t sizes[] = {T * n1 * 2, T * n1 * 2, T * hdv * 4, attn_ws_bytes(s, nullptr),
                           T * hdv * 2, kAlign, T * dm * 2, T * hdv * 4, T * hdv * 4,
                           T * hdv * 2, T * n1 * 2, kColsumParts * (n1 > dm ? n1 : dm) * 4,
-                          waves * hdv * 4, waves * hdv * 4};
+                          waves * hdv * 4, waves * hdv * 4, rab_part_bytes(d, s)};
   size_t off[sizeof(sizes) / sizeof(sizes[0]) + 1] = {0};
   for (size_t i = 0; i < sizeof(sizes) / sizeof(sizes[0]); ++i) off[i + 1] = off[i] + align_up(sizes[i]);
   if (w != nullptr) {
@@ -592,6 +614,7 @@ size_t layer_bwd_ws(const hstu_dims_t *d, const hstu_jagged_t *s, LayerBwdWs *w)
     w->part_cols = (float *)(b + off[11]);
     w->part_gamma = (float *)(b + off[12]);
     w->part_beta = (float *)(b + off[13]);
+    w->rab_part = (float *)(b + off[14]);
   }
   return off[sizeof(sizes) / sizeof(sizes[0])];
 }
@@ -612,11 +635,14 @@ hstu_status_t hstu_layer_bwd(const hstu_dims_t *dims, const hstu_weights_t *w,
   if ((st = check_seq(seq)) != HSTU_OK) return st;
   if ((st = check_weights(w)) != HSTU_OK) return st;
   if (grads == nullptr || grads->w1 == nullptr || grads->w2 == nullptr) return HSTU_ERR_INVALID_ARG;
-  if (grads->rab_pos != nullptr || grads->rab_time != nullptr) return HSTU_ERR_INVALID_ARG;
+  if ((grads->rab_pos != nullptr && w->rab_pos == nullptr) ||
+      (grads->rab_time != nullptr && w->rab_time == nullptr))
+    return HSTU_ERR_INVALID_ARG;
   if ((grads->ln_gamma != nullptr && w->ln_gamma == nullptr) ||
       (grads->ln_beta != nullptr && w->ln_beta == nullptr))
     return HSTU_ERR_INVALID_ARG;
-  const void *gr[] = {grads->w1, grads->b1, grads->w2, grads->b2, grads->ln_gamma, grads->ln_beta};
+  const void *gr[] = {grads->w1, grads->b1, grads->w2, grads->b2, grads->ln_gamma, grads->ln_beta,
+                      grads->rab_pos, grads->rab_time};
   for (const void *g : gr)
     if (!aligned16(g)) return HSTU_ERR_INVALID_ARG;
   if (seq->total_tokens > 0 && (x == nullptr || d_y == nullptr || d_x == nullptr))
@@ -631,11 +657,14 @@ hstu_status_t hstu_layer_bwd(const hstu_dims_t *dims, const hstu_weights_t *w,
   const int T = seq->total_tokens;
   const int dm = dims->d_model, hdv = dims->num_heads * dims->dv, hqk = dims->num_heads * dims->dqk;
   const int n1 = 2 * (hdv + hqk);
+  const int rab_rows = dims->rab_heads == dims->num_heads && dims->num_heads > 1 ? dims->num_heads : 1;
   if (seq->batch == 0 || T == 0) {  // no token: every formed gradient is zero
     hipError_t e = hipSuccess;
     const std::pair<float *, int64_t> z[] = {{grads->w1, (int64_t)n1 * dm}, {grads->b1, n1},
                                              {grads->w2, (int64_t)dm * hdv}, {grads->b2, dm},
-                                             {grads->ln_gamma, hdv}, {grads->ln_beta, hdv}};
+                                             {grads->ln_gamma, hdv}, {grads->ln_beta, hdv},
+                                             {grads->rab_pos, (int64_t)rab_rows * dims->pos_buckets},
+                                             {grads->rab_time, (int64_t)rab_rows * dims->time_buckets}};
     for (const auto &p : z)
       if (e == hipSuccess) e = launch_fill_zero(p.first, p.second, sst);
     return e == hipSuccess ? HSTU_OK : hip_fail(e);
@@ -718,6 +747,12 @@ hstu_status_t hstu_layer_bwd(const hstu_dims_t *dims, const hstu_weights_t *w,
   a.zq_off = 2 * hdv;
   a.zk_off = 2 * hdv + hqk;
   a.zv_off = hdv;
+  if (grads->rab_pos != nullptr || grads->rab_time != nullptr) {
+    a.rab_part = b.rab_part;
+    a.rab_cap = cap;
+    a.d_rab_pos = grads->rab_pos;
+    a.d_rab_time = grads->rab_time;
+  }
   HSTU_TRY(launch_attention_bwd(a, dims->dqk, cap, T, sst));
   // f1: dX = dZ w1, dw1 = dZ^T X, db1
   HSTU_TRY(blas_gemm_bf16(false, false, T, dm, n1, b.dz, n1, w->w1, dm, d_x, dm, 0.0f, sst));

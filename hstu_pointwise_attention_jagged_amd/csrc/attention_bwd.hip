@@ -46,6 +46,8 @@ constexpr int dq_keys() { return DH == 128 ? 32 : 64; }
 constexpr int kDkvQueries = 32;        // queries per tile streamed by the dK/dV kernel
 constexpr int kMaxPos = 1024;
 constexpr int kMaxTime = 64;
+constexpr int kTimeReps = 16;                   // copies of a wave's time bins
+constexpr int kTimeRepPitch = kMaxTime + 1;     // so that copy r starts r banks further
 constexpr float kNegLog2e = -1.4426950408889634f;
 
 enum BlockKind { KIND_CONST = 0, KIND_TWO = 1, KIND_GENERAL = 2 };
@@ -205,6 +207,7 @@ __device__ __forceinline__ float rab(const BiasCtx &c, int qi, int kj, int32_t q
 // chosen (the lower bucket is then below the upper one, at most 31).
 struct BlockBias {
   int kind;
+  int tb;  // the lower time bucket (CONST: the block's; TWO: hi pairs take tb + 1)
   float lo, hi;
   uint32_t thr;
 };
@@ -223,6 +226,7 @@ __device__ __forceinline__ BlockBias classify(const BiasCtx &c, int q_lo, int k_
   r.lo = base + (c.use_time ? c.ttab[tb_lo] : 0.0f);
   r.hi = base + (c.use_time ? c.ttab[tb_hi] : 0.0f);
   r.thr = (uint32_t)(((uint64_t)1 << (tb_lo + 1)) - 1);
+  r.tb = tb_lo;
   return r;
 }
 
@@ -318,6 +322,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(AttnBwdArgs p)
   __shared__ __attribute__((aligned(16))) unsigned char v_row[TK * L::ROWP];
   __shared__ int32_t k_ts[TK];
   __shared__ float ptab[kMaxPos], ttab[kMaxTime];
+  // per-wave sums of dS per bucket: position bins, and time bins in kTimeReps copies
+  // (lane l adds into copy l % kTimeReps, whose bins sit one bank apart)
+  __shared__ float rpos[kWaves][kMaxPos];
+  __shared__ float rtime[kWaves][kTimeReps][kTimeRepPitch];
 
   const int item = blockIdx.x;
   if (item >= ld_const(p.n_work)) return;
@@ -350,6 +358,34 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(AttnBwdArgs p)
   f32x16 acc[FT];
 #pragma unroll
   for (int f = 0; f < FT; ++f) acc[f] = f32x16{};
+
+  // Gradients of the bias tables: every allowed pair's dS goes to its position and time
+  // bucket.  Blocks whose position bucket is P - 1 throughout add their dS to a per-lane
+  // sum pos_run; CONST blocks add theirs to t_run for the current time bucket t_run_b,
+  // which changes only a few times along a wave's blocks, and TWO blocks reduce their two
+  // time sums at once.  GENERAL blocks add each pair to the wave's bins with LDS atomics:
+  // the time bucket is mostly shared by a wave's lanes, so each lane adds into its own
+  // copy of the time bins.  The workgroup's bins are summed in a fixed order.
+  const int PB = p.pos_buckets;
+  const bool want_rab = p.rab_part != nullptr && (bc.use_pos || bc.use_time);
+  float *wpos = rpos[wave];
+  float *wtime = &rtime[wave][0][0];
+  float *ltime = &rtime[wave][lane % kTimeReps][0];
+  if (want_rab) {
+    for (int i = lane; i < PB; i += 64) wpos[i] = 0.0f;
+    for (int i = lane; i < kTimeReps * kTimeRepPitch; i += 64) wtime[i] = 0.0f;
+  }
+  float pos_run = 0.0f, t_run = 0.0f;
+  int t_run_b = 0;
+  auto wave_sum = [&](float v) __attribute__((always_inline)) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+  };
+  auto time_add = [&](float v, int b) __attribute__((always_inline)) {
+    v = wave_sum(v);
+    if (lane == 0) wtime[b] += v;
+  };
 
   const __amdgpu_buffer_rsrc_t krs = rows_rsrc(p.k + (int64_t)s0 * p.stride + h * DH, p.stride, n, DH);
   const __amdgpu_buffer_rsrc_t vrs = rows_rsrc(p.v + (int64_t)s0 * p.stride + h * DH, p.stride, n, DH);
@@ -384,12 +420,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(AttnBwdArgs p)
       const BlockBias bb = classify(bc, qbase, kb, tq, tk);
       // S^T with its bias, dA^T; lane: query lrow, keys 8 (i / 4) + 4 half + i % 4
       f32x16 s, da = f32x16{};
+      const int64_t lim = (int64_t)qts - (int64_t)bb.thr + 1;  // TWO: hi when ts_k < lim
+      const int32_t klim = (int32_t)(lim < (int64_t)INT32_MIN ? (int64_t)INT32_MIN : lim);
       if (bb.kind == KIND_CONST) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[i] = bb.lo;
       } else if (bb.kind == KIND_TWO) {
-        const int64_t lim = (int64_t)qts - (int64_t)bb.thr + 1;  // hi when ts_k < lim
-        const int32_t klim = (int32_t)(lim < (int64_t)INT32_MIN ? (int64_t)INT32_MIN : lim);
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[i] = kts[8 * (i >> 2) + (i & 3)] < klim ? bb.hi : bb.lo;
       } else {
@@ -413,6 +449,47 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(AttnBwdArgs p)
 #pragma unroll
         for (int i = 0; i < 16; ++i) ds[i] = da[i] * silu_grad(s[i]);
       }
+      if (want_rab) {
+        if (bb.kind == KIND_CONST) {
+          float sum = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sum += ds[i];
+          pos_run += sum;
+          if (bc.use_time) {
+            if (bb.tb != t_run_b) {
+              time_add(t_run, t_run_b);
+              t_run = 0.0f;
+              t_run_b = bb.tb;
+            }
+            t_run += sum;
+          }
+        } else if (bb.kind == KIND_TWO) {
+          float shi = 0.0f, slo = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const bool hi = kts[8 * (i >> 2) + (i & 3)] < klim;
+            shi += hi ? ds[i] : 0.0f;
+            slo += hi ? 0.0f : ds[i];
+          }
+          pos_run += shi + slo;
+          time_add(slo, bb.tb);
+          time_add(shi, bb.tb + 1);
+        } else {
+          const bool pos_each = bc.use_pos && qbase - (kb + 31) < PB - 1;  // near the diagonal
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kj = kb + 8 * (i >> 2) + 4 * half + (i & 3);
+            if (q_ok && kj <= qi) {
+              if (pos_each) atomicAdd(&wpos[min(qi - kj, PB - 1)], ds[i]);
+              else pos_run += ds[i];
+              if (bc.use_time)
+                atomicAdd(&ltime[min(time_log2_bucket(qts, kts[8 * (i >> 2) + (i & 3)]),
+                                     p.time_buckets - 1)],
+                          ds[i]);
+            }
+          }
+        }
+      }
       // dQ^T += K^T dS^T over the block's 32 keys
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
@@ -420,6 +497,26 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(AttnBwdArgs p)
 #pragma unroll
         for (int f = 0; f < FT; ++f) acc[f] = mfma32_f16(tr_frag<DH>(ktr, lane, f, s2), bop, acc[f]);
       }
+    }
+  }
+  if (want_rab) {  // flush the runs, then the workgroup's bins in a fixed order
+    if (bc.use_time) time_add(t_run, t_run_b);
+    if (bc.use_pos) {
+      const float v = wave_sum(pos_run);
+      if (lane == 0) wpos[PB - 1] += v;
+    }
+    __syncthreads();
+    const int nb = PB + p.time_buckets;
+    float *dst = p.rab_part + ((int64_t)h * p.rab_cap + item) * nb;
+    for (int i = tid; i < nb; i += kThreads) {
+      float t = 0.0f;
+      if (i < PB) {
+        for (int w = 0; w < kWaves; ++w) t += rpos[w][i];
+      } else {
+        for (int w = 0; w < kWaves; ++w)
+          for (int r = 0; r < kTimeReps; ++r) t += rtime[w][r][i - PB];
+      }
+      dst[i] = t;
     }
   }
   if (q_ok) {
@@ -443,8 +540,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(AttnBwdArgs p)
 // -------------------------------------------------------------------------------------
 // dK, dV: keys owned, queries streamed
 // -------------------------------------------------------------------------------------
-// At DH = 128 the dK and dV accumulators (128 registers) and the K fragments take one
-// workgroup per CU (up to 512 registers per lane); smaller heads fit two.
+// Two workgroups per CU at every head size: at DH = 128 the dK and dV accumulators (128
+// registers), the K fragments (32) and one half of A and dS at a time fit 256 registers.
 template <int DH>
 __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkv_kernel(AttnBwdArgs p) {
   using L = BwdLayout<DH>;
@@ -593,6 +690,36 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkv_kernel(AttnBwdArgs p
   }
 }
 
+// d rab[row][bin] = 2^e x the sum over the heads of the row (all heads when the tables
+// are shared) and the work items of the dQ kernel's per-item bins.  One workgroup per
+// (row, bin): thread t sums every 256th (head, item) entry from t, then the 256 partial
+// sums are combined in a fixed tree order, so the result does not depend on scheduling.
+__global__ __launch_bounds__(256) void rab_reduce_kernel(AttnBwdArgs p, float *d_pos, float *d_time) {
+  __shared__ float wsum[kWaves];
+  const int nb = p.pos_buckets + p.time_buckets;
+  const int row = blockIdx.x / nb, bin = blockIdx.x % nb;
+  const int items = ld_const(p.n_work);
+  const int h0 = p.rab_per_head ? row : 0, nh = p.rab_per_head ? 1 : p.num_heads;
+  float s = 0.0f;
+  for (int idx = threadIdx.x; idx < nh * items; idx += 256) {
+    const int h = h0 + idx / items, it = idx % items;
+    s += p.rab_part[((int64_t)h * p.rab_cap + it) * nb + bin];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  float inv;
+  (void)d_scale(p.d_max, inv);
+  const float t = ((wsum[0] + wsum[1]) + (wsum[2] + wsum[3])) * inv;
+  if (bin < p.pos_buckets) {
+    if (d_pos) d_pos[row * p.pos_buckets + bin] = t;
+  } else if (d_time) {
+    d_time[row * p.time_buckets + bin - p.pos_buckets] = t;
+  }
+}
+
 template <int DH>
 hipError_t launch_bwd_dh(const AttnBwdArgs &a, int64_t cap, hipStream_t stream) {
   const dim3 grid((unsigned)cap, (unsigned)a.num_heads);
@@ -618,10 +745,15 @@ hipError_t launch_attention_bwd(const AttnBwdArgs &a, int dh, int64_t cap, int64
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   switch (dh) {
-    case 32: return launch_bwd_dh<32>(a, cap, stream);
-    case 64: return launch_bwd_dh<64>(a, cap, stream);
-    default: return launch_bwd_dh<128>(a, cap, stream);
+    case 32: e = launch_bwd_dh<32>(a, cap, stream); break;
+    case 64: e = launch_bwd_dh<64>(a, cap, stream); break;
+    default: e = launch_bwd_dh<128>(a, cap, stream); break;
   }
+  if (e != hipSuccess || a.rab_part == nullptr) return e;
+  const int rows = a.rab_per_head ? a.num_heads : 1;
+  rab_reduce_kernel<<<rows * (a.pos_buckets + a.time_buckets), 256, 0, stream>>>(a, a.d_rab_pos,
+                                                                                 a.d_rab_time);
+  return hipGetLastError();
 }
 
 }  // namespace hstu

@@ -55,6 +55,13 @@ struct AttnBwdArgs {
   const uint16_t *z;
   uint16_t *dz;
   int64_t z_stride, zq_off, zk_off, zv_off;
+  // Gradients of the bias tables (rab_part == nullptr: not formed): per-work-item bins
+  // [H][rab_cap][pos_buckets + time_buckets], reduced into d_rab_pos [rows][pos_buckets]
+  // and d_rab_time [rows][time_buckets] (either may be nullptr), rows = H when the
+  // tables are per head, else 1.
+  float *rab_part;
+  int64_t rab_cap;
+  float *d_rab_pos, *d_rab_time;
   const float *rab_pos;       // [rab_heads][pos_buckets] or nullptr
   const float *rab_time;      // [rab_heads][time_buckets] or nullptr
   int pos_buckets, time_buckets, rab_per_head;

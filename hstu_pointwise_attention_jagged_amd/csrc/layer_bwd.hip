@@ -157,36 +157,65 @@ __global__ __launch_bounds__(64 * kNgRows) void norm_gate_bwd_kernel(NormGateBwd
 }
 
 // Column sums of rows [chunk * rows_per, ...) of a [rows][cols] matrix (row pitch stride):
-// thread t of block (x, chunk) owns column 256 x + t.
+// thread t of block (x, chunk) owns the VEC columns VEC (256 x + t) .. + VEC - 1 and reads
+// them with one 16-byte load per row (VEC = 8 bf16 or 4 fp32 values).
 template <typename T>
-__device__ __forceinline__ float load_as_f32(const T *p);
+struct Vec16;
 template <>
-__device__ __forceinline__ float load_as_f32<float>(const float *p) { return *p; }
+struct Vec16<float> {
+  static constexpr int N = 4;
+  __device__ static void add(const float *p, float *acc) {
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] += v[j];
+  }
+};
 template <>
-__device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t *p) {
-  return __builtin_bit_cast(float, (uint32_t)*p << 16);  // bf16
-}
+struct Vec16<uint16_t> {  // bf16
+  static constexpr int N = 8;
+  __device__ static void add(const uint16_t *p, float *acc) {
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[2 * j] += __builtin_bit_cast(float, v[j] << 16);
+      acc[2 * j + 1] += __builtin_bit_cast(float, v[j] & 0xffff0000u);
+    }
+  }
+};
 
 template <typename T>
 __global__ __launch_bounds__(256) void colsum_partial_kernel(const T *a, int rows, int cols,
                                                              int64_t stride, int rows_per,
                                                              float *partial) {
-  const int col = blockIdx.x * 256 + threadIdx.x;
+  constexpr int VEC = Vec16<T>::N;
+  const int col = (blockIdx.x * 256 + threadIdx.x) * VEC;
   if (col >= cols) return;
   const int r0 = blockIdx.y * rows_per, r1 = min(rows, r0 + rows_per);
-  float s = 0.f;
-  for (int r = r0; r < r1; ++r) s += load_as_f32(a + (int64_t)r * stride + col);
-  partial[(int64_t)blockIdx.y * cols + col] = s;
+  float acc[VEC] = {};
+  for (int r = r0; r < r1; ++r) Vec16<T>::add(a + (int64_t)r * stride + col, acc);
+  float *dst = partial + (int64_t)blockIdx.y * cols + col;
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) dst[j] = acc[j];
 }
 
-// out[col] = sum over k < n_parts of partial[k][col], in order of k
+// out[col] = sum over k < n_parts of partial[k][col]: 16 threads per column each take
+// every 16th part from their first, then the 16 sums are added in a fixed order.
 __global__ __launch_bounds__(256) void sum_parts_kernel(const float *partial, int n_parts, int cols,
                                                         float *out) {
-  const int col = blockIdx.x * 256 + threadIdx.x;
-  if (col >= cols) return;
+  __shared__ float sums[16][17];
+  const int c = threadIdx.x & 15, g = threadIdx.x >> 4;
+  const int col = blockIdx.x * 16 + c;
   float s = 0.f;
-  for (int k = 0; k < n_parts; ++k) s += partial[(int64_t)k * cols + col];
-  out[col] = s;
+  if (col < cols)
+    for (int k = g; k < n_parts; k += 16) s += partial[(int64_t)k * cols + col];
+  sums[g][c] = s;
+  __syncthreads();
+  if (g == 0 && col < cols) {
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t += sums[i][c];
+    out[col] = t;
+  }
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float *p, int64_t n) {
@@ -232,7 +261,8 @@ hipError_t launch_colsum(const void *a, bool bf16, int rows, int cols, int64_t s
                          float *partial, int n_parts, float *out, hipStream_t stream) {
   if (cols <= 0) return hipSuccess;
   const int rows_per = (rows + n_parts - 1) / n_parts;
-  const dim3 grid((cols + 255) / 256, n_parts);
+  const int vec = bf16 ? 8 : 4;  // columns per thread; cols is a multiple of 64
+  const dim3 grid((cols / vec + 255) / 256, n_parts);
   if (bf16)
     colsum_partial_kernel<uint16_t><<<grid, 256, 0, stream>>>((const uint16_t *)a, rows, cols,
                                                                stride, rows_per, partial);
@@ -247,7 +277,7 @@ hipError_t launch_colsum(const void *a, bool bf16, int rows, int cols, int64_t s
 hipError_t launch_sum_parts(const float *partial, int n_parts, int cols, float *out,
                             hipStream_t stream) {
   if (cols <= 0) return hipSuccess;
-  sum_parts_kernel<<<(cols + 255) / 256, 256, 0, stream>>>(partial, n_parts, cols, out);
+  sum_parts_kernel<<<(cols + 15) / 16, 256, 0, stream>>>(partial, n_parts, cols, out);
   return hipGetLastError();
 }
 

@@ -380,7 +380,8 @@ def hstu_layer_bwd(dims: LayerDims, w: DeviceWeights, seq: DeviceJagged, x: torc
     """Backward of one causal layer for the upstream gradient d_y (fp32 [T][d]).
 
     Returns (d_x, grads): d_x fp32 [T][d]; grads a dict of fp32 tensors w1, w2 and, when
-    asked for, b1, b2 (bias_grads) and ln_gamma / ln_beta (when the weights have them)."""
+    asked for, b1, b2 (bias_grads), and ln_gamma, ln_beta, rab_pos, rab_time for those
+    the weights have."""
     lib = _lib.load()
     _check(x, torch.bfloat16, "x")
     _check(d_y, torch.float32, "d_y")
@@ -397,6 +398,10 @@ def hstu_layer_bwd(dims: LayerDims, w: DeviceWeights, seq: DeviceJagged, x: torc
         grads["ln_gamma"] = torch.empty(dims.hdv, **f32)
     if w.ln_beta is not None:
         grads["ln_beta"] = torch.empty(dims.hdv, **f32)
+    if w.rab_pos is not None:
+        grads["rab_pos"] = torch.empty_like(w.rab_pos)
+    if w.rab_time is not None:
+        grads["rab_time"] = torch.empty_like(w.rab_time)
     gc = _lib.LayerGrads(*(_ptr(grads.get(n)) for n in
                            ("w1", "b1", "w2", "b2", "ln_gamma", "ln_beta", "rab_pos", "rab_time")))
     d, wc, s = dims.c(), w.c(), seq.c()
@@ -418,9 +423,10 @@ def hstu_attn_bwd_workspace_bytes(dims: LayerDims, seq: DeviceJagged) -> int:
 def hstu_attn_bwd(dims: LayerDims, seq: DeviceJagged, q: torch.Tensor, k: torch.Tensor,
                   v: torch.Tensor, d_out: torch.Tensor, *, row_stride: Optional[int] = None,
                   rab_pos: Optional[torch.Tensor] = None, rab_time: Optional[torch.Tensor] = None,
-                  workspace: Optional[torch.Tensor] = None, stream=None):
+                  rab_grads: bool = False, workspace: Optional[torch.Tensor] = None, stream=None):
     """Gradients of the causal attention for d_out (fp32 [T][H*dv]).  Returns (dq, dk, dv),
-    fp32 [T][H*dh] each."""
+    fp32 [T][H*dh] each, and with rab_grads also the gradients of the given bias tables
+    (fp32, the tables' shapes; None for a table not given)."""
     lib = _lib.load()
     for n, t in (("q", q), ("k", k), ("v", v)):
         if t.dtype != torch.float16 or not t.is_cuda:
@@ -432,14 +438,18 @@ def hstu_attn_bwd(dims: LayerDims, seq: DeviceJagged, q: torch.Tensor, k: torch.
     dq = torch.empty((T, dims.hdv), dtype=torch.float32, device=q.device)
     dk = torch.empty_like(dq)
     dv = torch.empty_like(dq)
+    d_pos = torch.empty_like(rab_pos) if rab_grads and rab_pos is not None else None
+    d_time = torch.empty_like(rab_time) if rab_grads and rab_time is not None else None
     d, s = dims.c(), seq.c()
     need = int(lib.hstu_attn_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(s)))
     ws = _workspace(need, q.device, workspace)
     st = lib.hstu_attn_bwd(ctypes.byref(d), _ptr(rab_pos), _ptr(rab_time), ctypes.byref(s),
                            _ptr(q), _ptr(k), _ptr(v), int(row_stride), _ptr(d_out), _ptr(dq),
-                           _ptr(dk), _ptr(dv), _ptr(ws), ws.numel() * ws.element_size(),
-                           _stream(stream))
+                           _ptr(dk), _ptr(dv), _ptr(d_pos), _ptr(d_time), _ptr(ws),
+                           ws.numel() * ws.element_size(), _stream(stream))
     _raise(st, "hstu_attn_bwd")
+    if rab_grads:
+        return dq, dk, dv, d_pos, d_time
     return dq, dk, dv
 
 

@@ -244,8 +244,11 @@ size_t hstu_attn_bwd_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_
  * prefix) for the upstream gradient d_out of its output:
  *     dA = dO V^T, dS = dA * SiLU'(S) on allowed pairs (0 elsewhere), dQ = dS K,
  *     dK = dS^T Q, dV = A^T dO,  with S = Q K^T + rab, A = SiLU(S).
- * The bias tables are inputs only (their gradients are not formed).  Every row of dq,
- * dk and dv is written; the result is deterministic (no atomics).
+ * With d_rab_pos / d_rab_time (device fp32, the shape of the table: [rab_heads][buckets]),
+ * the tables' gradients too: the sum of dS over the allowed pairs of each bucket (over
+ * all heads when the table is shared).  Either may be NULL (not formed); each must be
+ * NULL when its table is.  An empty batch sets them to 0.  Every row of dq, dk and dv is
+ * written; the result is deterministic (fixed summation orders).
  *   q, k, v    (device) fp16, as for hstu_attn_fwd (row_stride elements between rows)
  *   d_out      (device) fp32 [T][H*dv]; rounded to fp16 for the matrix products
  *   dq, dk, dv (device) fp32 [T][H*dqk], [T][H*dqk], [T][H*dv]
@@ -259,7 +262,8 @@ hstu_status_t hstu_attn_bwd(const hstu_dims_t *dims, const float *rab_pos,
                             const float *rab_time, const hstu_jagged_t *seq,
                             const uint16_t *q, const uint16_t *k, const uint16_t *v,
                             int64_t row_stride, const float *d_out, float *dq, float *dk,
-                            float *dv, void *ws, size_t ws_bytes, void *stream);
+                            float *dv, float *d_rab_pos, float *d_rab_time, void *ws,
+                            size_t ws_bytes, void *stream);
 
 /* Gradients of the layer's parameters: device fp32 buffers owned by the caller, in the
  * layouts of hstu_weights_t.  A NULL entry is not formed.                            */
@@ -271,8 +275,8 @@ typedef struct {
   float *b2;        /* [d] or NULL, likewise                                           */
   float *ln_gamma;  /* [H*dv] or NULL; must be NULL when the weights have no ln_gamma  */
   float *ln_beta;   /* [H*dv] or NULL; must be NULL when the weights have no ln_beta   */
-  float *rab_pos;   /* must be NULL: gradients of the bias tables are not formed       */
-  float *rab_time;  /* must be NULL                                                    */
+  float *rab_pos;   /* [rab_heads][pos_buckets] or NULL; NULL when the table is        */
+  float *rab_time;  /* [rab_heads][time_buckets] or NULL; likewise                     */
 } hstu_layer_grads_t;
 
 /* Workspace (bytes) needed by hstu_layer_bwd; 0 when the arguments are invalid.       */

@@ -228,9 +228,9 @@ def test_attn_bwd_argument_checks(lib):
     assert need > 0
 
     def call(dims=d, q=FAKE, dout=FAKE + 8192, dq=FAKE + 16384, dk=FAKE + 32768, dv=FAKE + 65536,
-             stride=192, ws=FAKE, ws_bytes=need, seq=s):
+             stride=192, ws=FAKE, ws_bytes=need, seq=s, d_pos=None):
         return lib.hstu_attn_bwd(ctypes.byref(dims), None, None, ctypes.byref(seq), q, q + 128,
-                                 q + 256, stride, dout, dq, dk, dv, ws, ws_bytes, None)
+                                 q + 256, stride, dout, dq, dk, dv, d_pos, None, ws, ws_bytes, None)
     assert call(stride=32) == _lib.HSTU_ERR_INVALID_ARG          # smaller than H*dqk
     assert call(stride=196) == _lib.HSTU_ERR_INVALID_ARG         # not a multiple of 8
     assert call(dq=None) == _lib.HSTU_ERR_INVALID_ARG
@@ -240,6 +240,7 @@ def test_attn_bwd_argument_checks(lib):
     assert call(ws_bytes=need - 1) == _lib.HSTU_ERR_WORKSPACE
     assert call(dims=_dims(dv=64)) == _lib.HSTU_ERR_UNSUPPORTED
     assert call(dims=_dims(dqk=48, dv=48)) == _lib.HSTU_ERR_UNSUPPORTED
+    assert call(d_pos=FAKE + (1 << 20)) == _lib.HSTU_ERR_INVALID_ARG  # gradient of a table not given
     # empty batch: nothing to do, nothing launched
     assert call(seq=_lib.Jagged(0, 0, 0, FAKE, None), ws=None, ws_bytes=0) == _lib.HSTU_OK
 
@@ -256,7 +257,8 @@ def test_layer_bwd_argument_checks(lib):
                                   dx, ctypes.byref(grads), FAKE, ws_bytes, None)
     ok = _lib.LayerGrads(G, None, G + 65536, None, None, None, None, None)
     assert call(_lib.LayerGrads(None, None, G, None, None, None, None, None)) == _lib.HSTU_ERR_INVALID_ARG
-    assert call(_lib.LayerGrads(G, None, G + 65536, None, None, None, G + 8, None)) == _lib.HSTU_ERR_INVALID_ARG
+    # a bias-table gradient for weights without that table
+    assert call(_lib.LayerGrads(G, None, G + 65536, None, None, None, G + 4096, None)) == _lib.HSTU_ERR_INVALID_ARG
     # a LayerNorm gradient for weights without the affine parameters
     assert call(_lib.LayerGrads(G, None, G + 65536, None, G + 4096, None, None, None)) == _lib.HSTU_ERR_INVALID_ARG
     assert call(ok, dx=FAKE) == _lib.HSTU_ERR_INVALID_ARG        # d_x aliases x

@@ -3,7 +3,8 @@
 dQ, dK and dV from the HIP kernels are compared element by element with
 oracle/hstu_bwd.attention_bwd on the same fp16-exact Q, K, V and the same fp32 upstream
 gradient, on jagged batches with empty, one-token and ragged users, at head sizes 32, 64
-and 128, with shared and per-head bias tables, and at the full 8 x 8192-token size (8 heads
+and 128, with shared and per-head bias tables (whose gradients are compared too), and at the
+full 8 x 8192-token size (8 heads
 of 128, the launch that bench.py times) on sampled rows that the oracle computes one by
 one: first and last rows of sequences, both sides of a 128-row tile edge, and the middle
 of a sequence.  Bar: the error divided by the standard
@@ -62,7 +63,7 @@ def _gpu_bwd(seq, q, k, v, P, Tt, g, H, dh):
     opt = lambda a: None if a is None else torch.from_numpy(a).cuda()  # noqa: E731
     return ops.hstu_attn_bwd(dims, dev.jagged_of(seq), buf[:, :hq], buf[:, hq:2 * hq],
                              buf[:, 2 * hq:], torch.from_numpy(g).cuda(), row_stride=buf.stride(0),
-                             rab_pos=opt(P), rab_time=opt(Tt))
+                             rab_pos=opt(P), rab_time=opt(Tt), rab_grads=True)
 
 
 # (seed, lengths, H, dh, per-head tables, dO scale, position buckets, time buckets, tables)
@@ -90,7 +91,10 @@ def test_attention_gradients_match_oracle(seed, lengths, H, dh, per_head, g_scal
     again = _gpu_bwd(seq, q, k, v, P, Tt, g, H, dh)
     torch.cuda.synchronize()
     want = bwd.attention_bwd(q, k, v, g, seq.offsets, seq.timestamps, H, dh, dh, P, Tt)
-    for name, gt, ag, wt in zip(("dq", "dk", "dv"), got, again, want[:3]):
+    for name, gt, ag, wt in zip(("dq", "dk", "dv", "d_rab_pos", "d_rab_time"), got, again, want):
+        if wt is None:
+            assert gt is None
+            continue
         gn = gt.cpu().numpy().astype(np.float64)
         assert np.array_equal(gt.cpu().numpy(), ag.cpu().numpy()), f"{name} not deterministic"
         sd = float(np.std(wt)) or 1.0
@@ -105,7 +109,7 @@ def test_zero_upstream_gradient_gives_zero():
     g[:] = 0.0
     say("[bwd] dO = 0")
     for t in _gpu_bwd(seq, q, k, v, P, Tt, g, 2, 64):
-        assert torch.count_nonzero(t).item() == 0
+        assert t is None or torch.count_nonzero(t).item() == 0
 
 
 def test_attention_gradients_full_size_sampled_rows():
@@ -123,7 +127,7 @@ def test_attention_gradients_full_size_sampled_rows():
     rows = [0, 1, 127, 128, 4095, 8191, int(off[3]) + 2000, int(off[7]) + 8063,
             int(off[7]) + 8064, int(off[8]) - 1]
     want = bwd.attention_bwd(q, k, v, g, off, seq.timestamps, H, dh, dh, P, Tt, rows=rows)
-    for name, gt, wt in zip(("dq", "dk", "dv"), got, want[:3]):
+    for name, gt, wt in zip(("dq", "dk", "dv"), got[:3], want[:3]):
         gn = gt[rows].cpu().numpy().astype(np.float64)
         wr = wt[rows]
         sd = float(np.std(wr)) or 1.0

@@ -1,6 +1,7 @@
 """GPU parity of the layer backward (hstu_layer_bwd) against the fp64 oracle.
 
-dX and every parameter gradient (w1, b1, w2, b2, LayerNorm gamma and beta) from the GPU
+dX and every parameter gradient (w1, b1, w2, b2, LayerNorm gamma and beta, both bias
+tables) from the GPU
 are compared element by element with oracle/hstu_bwd.layer_bwd on the same bf16-exact
 inputs and weights, at head sizes 32, 64 and 128 on jagged batches (several tiles and
 ragged tails), with and without biases and affine LayerNorm; and at the full 8 x 8192
@@ -34,7 +35,7 @@ pytestmark = pytest.mark.gpu
 
 MAX_REL, MEAN_REL = 5e-2, 5e-3
 NAMES = {"w1": "dw1", "b1": "db1", "w2": "dw2", "b2": "db2", "ln_gamma": "dgamma",
-         "ln_beta": "dbeta"}
+         "ln_beta": "dbeta", "rab_pos": "drab_pos", "rab_time": "drab_time"}
 
 
 def say(msg):
@@ -113,6 +114,8 @@ def test_layer_gradients_full_size_sampled_rows():
     torch.cuda.synchronize()
     assert torch.equal(d_x, d_x2) and torch.equal(grads["w1"], grads2["w1"]), "not repeatable"
     assert torch.equal(grads["w2"], grads2["w2"]) and torch.equal(grads["b1"], grads2["b1"])
+    assert torch.equal(grads["rab_pos"], grads2["rab_pos"])
+    assert torch.equal(grads["rab_time"], grads2["rab_time"])
     off = w.seq.offsets.astype(np.int64)
     rows = [int(off[5]) + r for r in (0, 1, 127, 128, 4095, 8190, 8191)]
     want = bwd.layer_bwd(w.x, weights, w.seq.offsets, w.seq.timestamps, d.num_heads, d.dqk,
