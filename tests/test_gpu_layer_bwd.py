@@ -102,6 +102,37 @@ def test_layer_gradients_match_oracle(cfg, kw, bias, affine):
     assert ("ln_gamma" in grads) == affine
 
 
+def test_layer_gradients_zero_length_and_one_token_users():
+    d = wl.LayerDims(d_model=128, num_heads=2, dqk=64, dv=64, rab_heads=2)
+    w = wl.random_layer(31, [0, 1, 37, 0, 200, 1], d)
+    rng = np.random.default_rng(731)
+    weights = wl.draw_weights(rng, d, bias=True, affine=True)
+    d_y = rng.standard_normal((w.seq.total, d.d_model)).astype(np.float32)
+    say(f"[layer bwd] lengths {w.seq.lengths.tolist()} per-head tables")
+    d_x, grads = _run(w, weights, d_y)
+    torch.cuda.synchronize()
+    want = bwd.layer_bwd(w.x, weights, w.seq.offsets, w.seq.timestamps, d.num_heads, d.dqk,
+                         d.dv, d_y, d.ln_eps)
+    _check_rows("dx", d_x, want["dx"])
+    for k, t in grads.items():
+        _check(k, t, want[NAMES[k]])
+
+
+def test_layer_gradients_of_an_empty_batch_are_zero():
+    d = wl.LayerDims(d_model=64, num_heads=2, dqk=32, dv=32)
+    w = wl.random_layer(32, [0, 0, 0], d)
+    weights = wl.draw_weights(np.random.default_rng(732), d, bias=True, affine=True)
+    say("[layer bwd] three empty users")
+    d_x, grads = ops.hstu_layer_bwd(dev.dims_of(d), dev.weights_of(weights), dev.jagged_of(w.seq),
+                                    torch.zeros((0, d.d_model), dtype=torch.bfloat16, device="cuda"),
+                                    torch.zeros((0, d.d_model), dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    assert d_x.shape == (0, d.d_model)
+    assert set(grads) == set(NAMES)
+    for k, t in grads.items():
+        assert torch.count_nonzero(t).item() == 0, k
+
+
 def test_layer_gradients_full_size_sampled_rows():
     w = wl.config(2)
     d = w.dims
