@@ -297,10 +297,10 @@ def mfalcon_measure(torch, np, ops, dev, wl, n_layers=4, bm=1024, reps=3):
         ops.hstu_stack_fwd(dims, dw, hist, x_h, keep_caches=True, y=y_h, uvqk=caches,
                            workspace=ws_h, stream=stream)
 
-    def score():
+    def score(st=None):
         for mc, xc in mbs:
             ops.hstu_stack_fwd_mfalcon(dims, dw, hist, caches, mc, xc, y_cand=y_c, uvqk_cand=u_c,
-                                       workspace=ws_c, stream=stream)
+                                       workspace=ws_c, stream=st or stream)
 
     def timed_ms(fn):
         fn()
@@ -315,6 +315,43 @@ def mfalcon_measure(torch, np, ops, dev, wl, n_layers=4, bm=1024, reps=3):
 
     hist_ms = timed_ms(history)
     score_ms = timed_ms(score)
+    # the same micro-batch loop captured once in a HIP graph and replayed (the launches of
+    # every micro-batch and layer in one submission); checked bit for bit against eager
+    score()
+    torch.cuda.synchronize()
+    y_ref = y_c.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        score(torch.cuda.current_stream())
+    y_c.zero_()
+    graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(y_c, y_ref), "graph replay differs from the eager micro-batch loop"
+    graph_ms = timed_ms(graph.replay)
+    # micro-batches spread over 4 streams (default priority), each with its own workspace
+    # and outputs: a small micro-batch fills only part of the GPU, and micro-batches are
+    # independent of one another
+    n_st = min(4, len(mbs))
+    streams = [torch.cuda.Stream() for _ in range(n_st)]
+    bufs = [(torch.empty_like(ws_c), torch.empty_like(y_c), torch.empty_like(u_c)) for _ in range(n_st)]
+
+    def score_streams():
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        for i, (mc, xc) in enumerate(mbs):
+            st = streams[i % n_st]
+            st.wait_event(ev)
+            wsb, yb, ub = bufs[i % n_st]
+            ops.hstu_stack_fwd_mfalcon(dims, dw, hist, caches, mc, xc, y_cand=yb, uvqk_cand=ub,
+                                       workspace=wsb, stream=st)
+        for st in streams:
+            stream.wait_stream(st)
+
+    score_streams()
+    torch.cuda.synchronize()
+    last = (len(mbs) - 1) % n_st
+    assert torch.equal(bufs[last][1], y_ref), "multi-stream scoring differs from the eager loop"
+    streams_ms = timed_ms(score_streams)
     H, dq, dv_, dm = d.num_heads, d.dqk, d.dv, d.d_model
     n_h = int(w.seq.lengths[0])
     n_cand = int(cand.total)
@@ -327,6 +364,10 @@ def mfalcon_measure(torch, np, ops, dev, wl, n_layers=4, bm=1024, reps=3):
             "history_tflops": round(n_layers * (f1 + att + f2) / (hist_ms * 1e-3) / 1e12, 1),
             "score_ms": round(score_ms, 3),
             "candidates_per_s": round(n_cand / (score_ms * 1e-3), 1),
+            "score_ms_graph": round(graph_ms, 3),
+            "candidates_per_s_graph": round(n_cand / (graph_ms * 1e-3), 1),
+            "score_ms_4_streams": round(streams_ms, 3),
+            "candidates_per_s_4_streams": round(n_cand / (streams_ms * 1e-3), 1),
             "score_tflops": round(n_layers * n_cand * per_cand / (score_ms * 1e-3) / 1e12, 1)}
 
 
