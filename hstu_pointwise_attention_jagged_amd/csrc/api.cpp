@@ -476,9 +476,44 @@ static size_t attn_bwd_ws_bytes(const hstu_dims_t *d, const hstu_jagged_t *s) {
          rab_part_bytes(d, s);
 }
 
+// Stored dS of the attention backward: per head, an upper bound on the 32 x 32 blocks of
+// every sequence's causal triangle that the host can form from T, B and the longest
+// length L: the sum of nb (nb + 1) / 2 with nb = ceil(n / 32) <= ceil(L / 32) and the sum
+// of nb at most ceil(T / 32) + B.  0 when the buffer would pass kDsCapBytes (then the dQ
+// kernel forms dS again).
+constexpr size_t kDsCapBytes = (size_t)32 << 30;
+
+static int64_t ds_head_blocks(const hstu_jagged_t *s) {
+  const int64_t nb_max = ((int64_t)s->max_seq_len + 31) / 32;
+  return (((int64_t)s->total_tokens + 31) / 32 + s->batch) * (nb_max + 1) / 2 + 1;
+}
+
+static size_t ds_bytes(const hstu_dims_t *d, const hstu_jagged_t *s) {
+  if (s->total_tokens == 0) return 0;
+  const size_t bytes = align_up((size_t)(s->batch + 1) * sizeof(int64_t)) +
+                       align_up((size_t)ds_head_blocks(s) * d->num_heads * 2048);
+  return bytes <= kDsCapBytes ? bytes : 0;
+}
+
 size_t hstu_attn_bwd_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_t *seq) {
   if (check_attn_dims(dims) != HSTU_OK || check_seq(seq) != HSTU_OK) return 0;
+  return attn_bwd_ws_bytes(dims, seq) + ds_bytes(dims, seq);
+}
+
+size_t hstu_attn_bwd_min_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_t *seq) {
+  if (check_attn_dims(dims) != HSTU_OK || check_seq(seq) != HSTU_OK) return 0;
   return attn_bwd_ws_bytes(dims, seq);
+}
+
+// Points a at the stored-dS region that follows `base` when the workspace holds it.
+static void attach_ds(AttnBwdArgs &a, const hstu_dims_t *d, const hstu_jagged_t *s, char *base,
+                      size_t have) {
+  const size_t need = ds_bytes(d, s);
+  if (need == 0 || have < need) return;
+  a.tri_base = (int64_t *)base;
+  a.ds_buf = (uint16_t *)(base + align_up((size_t)(s->batch + 1) * sizeof(int64_t)));
+  a.ds_head_blocks = ds_head_blocks(s);
+  a.batch = s->batch;
 }
 
 hstu_status_t hstu_attn_bwd(const hstu_dims_t *dims, const float *rab_pos, const float *rab_time,
@@ -526,6 +561,10 @@ hstu_status_t hstu_attn_bwd(const hstu_dims_t *dims, const float *rab_pos, const
   carve_attn((char *)ws, seq, nullptr, lw);
   char *tail = (char *)ws + attn_ws_bytes(seq, nullptr);
   AttnBwdArgs a{};
+  {
+    const size_t base = attn_bwd_ws_bytes(dims, seq);
+    attach_ds(a, dims, seq, (char *)ws + base, ws_bytes - base);
+  }
   a.d_h = (uint16_t *)tail;
   a.d_max = (uint32_t *)(tail + align_up((size_t)seq->total_tokens * hq * sizeof(uint16_t)));
   if (d_rab_pos != nullptr || d_rab_time != nullptr) {
@@ -622,6 +661,11 @@ size_t layer_bwd_ws(const hstu_dims_t *d, const hstu_jagged_t *s, LayerBwdWs *w)
 }  // namespace
 
 size_t hstu_layer_bwd_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_t *seq) {
+  if (check_dims(dims) != HSTU_OK || check_seq(seq) != HSTU_OK) return 0;
+  return layer_bwd_ws(dims, seq, nullptr) + ds_bytes(dims, seq);
+}
+
+size_t hstu_layer_bwd_min_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_t *seq) {
   if (check_dims(dims) != HSTU_OK || check_seq(seq) != HSTU_OK) return 0;
   return layer_bwd_ws(dims, seq, nullptr);
 }
@@ -747,6 +791,10 @@ hstu_status_t hstu_layer_bwd(const hstu_dims_t *dims, const hstu_weights_t *w,
   a.zq_off = 2 * hdv;
   a.zk_off = 2 * hdv + hqk;
   a.zv_off = hdv;
+  {
+    const size_t base = layer_bwd_ws(dims, seq, nullptr);
+    attach_ds(a, dims, seq, (char *)ws + base, ws_bytes - base);
+  }
   if (grads->rab_pos != nullptr || grads->rab_time != nullptr) {
     a.rab_part = b.rab_part;
     a.rab_cap = cap;

@@ -127,6 +127,17 @@ struct TileRegs {
             u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (r * (int)stride + ch * 8) * 2, soff, 0));
     }
   }
+  // into a transposed-read copy only
+  __device__ __forceinline__ void store_tr(unsigned char *tr_copy) const {
+    using L = BwdLayout<DH>;
+#pragma unroll
+    for (int c = 0; c < N; ++c) {
+      const int idx = threadIdx.x + c * kThreads;
+      if (CHUNKS % kThreads != 0 && idx >= CHUNKS) break;
+      const int r = idx / L::CPR, ch = idx % L::CPR;
+      *reinterpret_cast<u32x4 *>(tr_copy + r * L::TRP + ch * 16) = v[c];
+    }
+  }
   // into a row copy and, with TR, a transposed-read copy too
   template <bool TR>
   __device__ __forceinline__ void store(unsigned char *row_copy, unsigned char *tr_copy) const {
@@ -309,6 +320,116 @@ __device__ __forceinline__ void load_tables(const AttnBwdArgs &p, int h, float *
     for (int i = threadIdx.x; i < p.time_buckets; i += kThreads) ttab[i] = p.rab_time[rrow * p.time_buckets + i];
 }
 
+// Sums of dS per bias bucket for one wave: the gradients of the bias tables, every
+// allowed pair's dS going to its position and time bucket.  Blocks whose position bucket
+// is P - 1 throughout add their dS to a per-lane sum pos_run; CONST blocks add theirs to
+// t_run for the current time bucket t_run_b, which changes only a few times along a
+// wave's blocks, and TWO blocks reduce their two time sums at once.  GENERAL blocks add
+// each pair to the wave's bins with LDS atomics: the time bucket is mostly shared by a
+// wave's lanes, so each lane adds into its own copy of the time bins.
+struct RabAcc {
+  float *wpos, *wtime, *ltime;
+  int PB, TB, lane;
+  bool use_pos, use_time;
+  float pos_run, t_run;
+  int t_run_b;
+
+  __device__ __forceinline__ void init(float *pos_bins, float *time_bins, int lane_,
+                                       const BiasCtx &bc) {
+    wpos = pos_bins;
+    wtime = time_bins;
+    ltime = time_bins + (lane_ % kTimeReps) * kTimeRepPitch;
+    PB = bc.pos_buckets;
+    TB = bc.time_buckets;
+    lane = lane_;
+    use_pos = bc.use_pos;
+    use_time = bc.use_time;
+    pos_run = t_run = 0.0f;
+    t_run_b = 0;
+    for (int i = lane; i < PB; i += 64) wpos[i] = 0.0f;
+    for (int i = lane; i < kTimeReps * kTimeRepPitch; i += 64) wtime[i] = 0.0f;
+  }
+  __device__ __forceinline__ static float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+  }
+  __device__ __forceinline__ void time_add(float v, int b) {
+    v = wave_sum(v);
+    if (lane == 0) wtime[b] += v;
+  }
+  // One 32 x 32 block: the lane's query qi (q_ok) and its 16 values ds[i] for the keys
+  // kb + 8 (i / 4) + 4 half + i % 4, whose timestamps are kts[8 (i / 4) + i % 4].
+  __device__ __forceinline__ void block(const BlockBias &bb, const float *ds, const int32_t *kts,
+                                        int32_t klim, int kb, int qbase, int qi, bool q_ok,
+                                        int half, int32_t qts) {
+    if (bb.kind == KIND_CONST) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sum += ds[i];
+      pos_run += sum;
+      if (use_time) {
+        if (bb.tb != t_run_b) {
+          time_add(t_run, t_run_b);
+          t_run = 0.0f;
+          t_run_b = bb.tb;
+        }
+        t_run += sum;
+      }
+    } else if (bb.kind == KIND_TWO) {
+      float shi = 0.0f, slo = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const bool hi = kts[8 * (i >> 2) + (i & 3)] < klim;
+        shi += hi ? ds[i] : 0.0f;
+        slo += hi ? 0.0f : ds[i];
+      }
+      pos_run += shi + slo;
+      time_add(slo, bb.tb);
+      time_add(shi, bb.tb + 1);
+    } else {
+      const bool pos_each = use_pos && qbase - (kb + 31) < PB - 1;  // near the diagonal
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kj = kb + 8 * (i >> 2) + 4 * half + (i & 3);
+        if (q_ok && kj <= qi) {
+          if (pos_each) atomicAdd(&wpos[min(qi - kj, PB - 1)], ds[i]);
+          else pos_run += ds[i];
+          if (use_time)
+            atomicAdd(&ltime[min(time_log2_bucket(qts, kts[8 * (i >> 2) + (i & 3)]), TB - 1)], ds[i]);
+        }
+      }
+    }
+  }
+  __device__ __forceinline__ void flush() {
+    if (use_time) time_add(t_run, t_run_b);
+    if (use_pos) {
+      const float v = wave_sum(pos_run);
+      if (lane == 0) wpos[PB - 1] += v;
+    }
+  }
+};
+
+// The workgroup's bins (after a barrier), summed in a fixed order, into its slot of the
+// per-work-item partials.
+__device__ __forceinline__ void rab_write(const AttnBwdArgs &p, const float (*rpos)[kMaxPos],
+                                          const float (*rtime)[kTimeReps][kTimeRepPitch], int h,
+                                          int item) {
+  const int PB = p.pos_buckets;
+  const int nb = PB + p.time_buckets;
+  float *dst = p.rab_part + ((int64_t)h * p.rab_cap + item) * nb;
+  for (int i = threadIdx.x; i < nb; i += kThreads) {
+    float t = 0.0f;
+    if (i < PB) {
+      for (int w = 0; w < kWaves; ++w) t += rpos[w][i];
+    } else {
+      for (int w = 0; w < kWaves; ++w)
+        for (int r = 0; r < kTimeReps; ++r) t += rtime[w][r][i - PB];
+    }
+    dst[i] = t;
+  }
+}
+
 // -------------------------------------------------------------------------------------
 // dQ: queries owned, keys streamed
 // -------------------------------------------------------------------------------------
@@ -359,33 +480,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(AttnBwdArgs p)
 #pragma unroll
   for (int f = 0; f < FT; ++f) acc[f] = f32x16{};
 
-  // Gradients of the bias tables: every allowed pair's dS goes to its position and time
-  // bucket.  Blocks whose position bucket is P - 1 throughout add their dS to a per-lane
-  // sum pos_run; CONST blocks add theirs to t_run for the current time bucket t_run_b,
-  // which changes only a few times along a wave's blocks, and TWO blocks reduce their two
-  // time sums at once.  GENERAL blocks add each pair to the wave's bins with LDS atomics:
-  // the time bucket is mostly shared by a wave's lanes, so each lane adds into its own
-  // copy of the time bins.  The workgroup's bins are summed in a fixed order.
-  const int PB = p.pos_buckets;
   const bool want_rab = p.rab_part != nullptr && (bc.use_pos || bc.use_time);
-  float *wpos = rpos[wave];
-  float *wtime = &rtime[wave][0][0];
-  float *ltime = &rtime[wave][lane % kTimeReps][0];
-  if (want_rab) {
-    for (int i = lane; i < PB; i += 64) wpos[i] = 0.0f;
-    for (int i = lane; i < kTimeReps * kTimeRepPitch; i += 64) wtime[i] = 0.0f;
-  }
-  float pos_run = 0.0f, t_run = 0.0f;
-  int t_run_b = 0;
-  auto wave_sum = [&](float v) __attribute__((always_inline)) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
-  };
-  auto time_add = [&](float v, int b) __attribute__((always_inline)) {
-    v = wave_sum(v);
-    if (lane == 0) wtime[b] += v;
-  };
+  RabAcc ra;
+  if (want_rab) ra.init(rpos[wave], &rtime[wave][0][0], lane, bc);
 
   const __amdgpu_buffer_rsrc_t krs = rows_rsrc(p.k + (int64_t)s0 * p.stride + h * DH, p.stride, n, DH);
   const __amdgpu_buffer_rsrc_t vrs = rows_rsrc(p.v + (int64_t)s0 * p.stride + h * DH, p.stride, n, DH);
@@ -449,47 +546,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(AttnBwdArgs p)
 #pragma unroll
         for (int i = 0; i < 16; ++i) ds[i] = da[i] * silu_grad(s[i]);
       }
-      if (want_rab) {
-        if (bb.kind == KIND_CONST) {
-          float sum = 0.0f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sum += ds[i];
-          pos_run += sum;
-          if (bc.use_time) {
-            if (bb.tb != t_run_b) {
-              time_add(t_run, t_run_b);
-              t_run = 0.0f;
-              t_run_b = bb.tb;
-            }
-            t_run += sum;
-          }
-        } else if (bb.kind == KIND_TWO) {
-          float shi = 0.0f, slo = 0.0f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const bool hi = kts[8 * (i >> 2) + (i & 3)] < klim;
-            shi += hi ? ds[i] : 0.0f;
-            slo += hi ? 0.0f : ds[i];
-          }
-          pos_run += shi + slo;
-          time_add(slo, bb.tb);
-          time_add(shi, bb.tb + 1);
-        } else {
-          const bool pos_each = bc.use_pos && qbase - (kb + 31) < PB - 1;  // near the diagonal
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int kj = kb + 8 * (i >> 2) + 4 * half + (i & 3);
-            if (q_ok && kj <= qi) {
-              if (pos_each) atomicAdd(&wpos[min(qi - kj, PB - 1)], ds[i]);
-              else pos_run += ds[i];
-              if (bc.use_time)
-                atomicAdd(&ltime[min(time_log2_bucket(qts, kts[8 * (i >> 2) + (i & 3)]),
-                                     p.time_buckets - 1)],
-                          ds[i]);
-            }
-          }
-        }
-      }
+      if (want_rab) ra.block(bb, ds, kts, klim, kb, qbase, qi, q_ok, half, qts);
       // dQ^T += K^T dS^T over the block's 32 keys
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
@@ -500,24 +557,185 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(AttnBwdArgs p)
     }
   }
   if (want_rab) {  // flush the runs, then the workgroup's bins in a fixed order
-    if (bc.use_time) time_add(t_run, t_run_b);
-    if (bc.use_pos) {
-      const float v = wave_sum(pos_run);
-      if (lane == 0) wpos[PB - 1] += v;
-    }
+    ra.flush();
     __syncthreads();
-    const int nb = PB + p.time_buckets;
-    float *dst = p.rab_part + ((int64_t)h * p.rab_cap + item) * nb;
-    for (int i = tid; i < nb; i += kThreads) {
-      float t = 0.0f;
-      if (i < PB) {
-        for (int w = 0; w < kWaves; ++w) t += rpos[w][i];
-      } else {
-        for (int w = 0; w < kWaves; ++w)
-          for (int r = 0; r < kTimeReps; ++r) t += rtime[w][r][i - PB];
-      }
-      dst[i] = t;
+    rab_write(p, rpos, rtime, h, item);
+  }
+  if (q_ok) {
+    float inv;
+    (void)d_scale(p.d_max, inv);
+    if (p.dz != nullptr) {
+      store_dz<FT>(acc, inv, p, (int64_t)(s0 + qi) * p.z_stride + p.zq_off + h * DH + half * 4);
+    } else {
+      float *orow = p.dq + (int64_t)(s0 + qi) * p.g_stride + h * DH + half * 4;
+#pragma unroll
+      for (int f = 0; f < FT; ++f)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<f32x4 *>(orow + f * 32 + g * 8) =
+              f32x4{acc[f][4 * g] * inv, acc[f][4 * g + 1] * inv, acc[f][4 * g + 2] * inv,
+                    acc[f][4 * g + 3] * inv};
     }
+  }
+}
+
+// -------------------------------------------------------------------------------------
+// dQ from the stored dS
+// -------------------------------------------------------------------------------------
+// First block of each sequence's causal triangle of 32 x 32 blocks: tri[b] = the sum over
+// b' < b of nb' (nb' + 1) / 2, nb' = ceil(n_b' / 32); tri[B] = the total.  One workgroup:
+// per-thread runs of sequences, then an exclusive scan of the runs.
+__global__ __launch_bounds__(1024) void tri_base_kernel(const int32_t *offsets, int B, int64_t *tri) {
+  __shared__ int64_t part[1024];
+  const int t = threadIdx.x, per = (B + 1023) / 1024;
+  const int b0 = min(B, t * per), b1 = min(B, b0 + per);
+  auto blocks = [&](int b) {
+    const int64_t nb = (offsets[b + 1] - offsets[b] + 31) / 32;
+    return nb * (nb + 1) / 2;
+  };
+  int64_t sum = 0;
+  for (int b = b0; b < b1; ++b) sum += blocks(b);
+  part[t] = sum;
+  __syncthreads();
+  if (t == 0) {
+    int64_t run = 0;
+    for (int i = 0; i < 1024; ++i) {
+      const int64_t v = part[i];
+      part[i] = run;
+      run += v;
+    }
+    tri[B] = run;
+  }
+  __syncthreads();
+  int64_t run = part[t];
+  for (int b = b0; b < b1; ++b) {
+    tri[b] = run;
+    run += blocks(b);
+  }
+}
+
+// Transposed operand of a stored block dS^T [key][query] (rows of 64 bytes) for k-step
+// s2: keys 16 s2 + 8 (e / 4) + 4 (lane / 32) + e % 4 (e = 0..7) of query lane % 32, the
+// key order of tr_frag
+__device__ __forceinline__ f16x8 ds_frag(const unsigned char *blk, int lane, int s2) {
+  const int row = 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int col = (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+  const u32x2 lo = tr_read(blk + (16 * s2 + row) * 64 + col);
+  const u32x2 hi = tr_read(blk + (16 * s2 + 8 + row) * 64 + col);
+  return as_f16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+// A workgroup owns 128 queries and streams 64-key tiles: the K rows (transposed-read
+// copy) and, per wave, the two stored dS blocks of its 32 queries.  Per block
+// dQ^T += K^T dS^T (8 MFMAs at DH = 128), both operands through the transposing read; no
+// scores, dA or SiLU' are formed again.  The bias-table sums read the same dS values.
+template <int DH>
+__global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_ds_kernel(AttnBwdArgs p) {
+  using L = BwdLayout<DH>;
+  constexpr int FT = L::FT;
+  constexpr int TK = 64;
+  constexpr int DSB = 2048;  // bytes of a stored block
+  __shared__ __attribute__((aligned(16))) unsigned char k_tr[TK * L::TRP];
+  __shared__ __attribute__((aligned(16))) unsigned char ds_l[kWaves][TK / 32][DSB];
+  __shared__ int32_t k_ts[TK];
+  __shared__ float ptab[kMaxPos], ttab[kMaxTime];
+  __shared__ float rpos[kWaves][kMaxPos];
+  __shared__ float rtime[kWaves][kTimeReps][kTimeRepPitch];
+
+  const int item = blockIdx.x;
+  if (item >= ld_const(p.n_work)) return;
+  const int h = blockIdx.y;
+  const int b = ld_const(p.work + 2 * item), qt = ld_const(p.work + 2 * item + 1);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lrow = lane & 31, half = lane >> 5;
+  const int s0 = ld_const(p.offsets + b), n = ld_const(p.offsets + b + 1) - s0;
+  BiasCtx bc;
+  load_tables(p, h, ptab, ttab, bc);
+
+  const int q0 = qt * kOwnRows;
+  const int qbase = q0 + wave * 32;
+  const bool wave_rows = qbase < n;
+  const int qi = qbase + lrow;
+  const bool q_ok = qi < n;
+  const bool want_rab = p.rab_part != nullptr && (bc.use_pos || bc.use_time);
+  const int32_t qts = (want_rab && bc.use_time) ? p.ts[s0 + (q_ok ? qi : 0)] : 0;
+  const int2 tq = (want_rab && bc.use_time && wave_rows) ? ld_stat(p.stat + s0 + qbase) : int2{0, 0};
+  RabAcc ra;
+  if (want_rab) ra.init(rpos[wave], &rtime[wave][0][0], lane, bc);
+  f32x16 acc[FT];
+#pragma unroll
+  for (int f = 0; f < FT; ++f) acc[f] = f32x16{};
+
+  const __amdgpu_buffer_rsrc_t krs = rows_rsrc(p.k + (int64_t)s0 * p.stride + h * DH, p.stride, n, DH);
+  const __amdgpu_buffer_rsrc_t trs = ts_rsrc(bc.use_time ? p.ts : nullptr, s0, n);
+  const int k_end = min(n, q0 + kOwnRows);
+  const int n_tiles = (k_end + TK - 1) / TK;
+  const int64_t head0 = (int64_t)h * p.ds_head_blocks + ld_const(p.tri_base + b);
+  const int nq_blocks = (n + 31) / 32;
+  // the tile's stored blocks: 16-byte piece c of the 16 KB, c = tid + 256 i: wave c / 256,
+  // block (c / 128) % 2 of the tile, piece c % 128; absent blocks (after the diagonal or
+  // past the sequence) read as zero
+  TileRegs<DH, TK> rk;
+  u32x4 rds[4];
+  int32_t rts = 0;
+  auto prefetch = [&](int j0) __attribute__((always_inline)) {
+    rk.load(krs, p.stride, j0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      const int qb = q0 / 32 + (c >> 8), kb = j0 / 32 + ((c >> 7) & 1);
+      rds[i] = u32x4{0, 0, 0, 0};
+      if (qb < nq_blocks && kb <= qb)
+        rds[i] = *reinterpret_cast<const u32x4 *>(
+            p.ds_buf + (head0 + (int64_t)qb * (qb + 1) / 2 + kb) * 1024 + (c & 127) * 8);
+    }
+    if (tid < TK) rts = load_ts(trs, tid, j0);
+  };
+  prefetch(0);
+  for (int t = 0; t < n_tiles; ++t) {
+    const int j0 = t * TK;
+    __syncthreads();  // the previous tile is no longer read (and the tables are written)
+    rk.store_tr(k_tr);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i;
+      *reinterpret_cast<u32x4 *>(&ds_l[c >> 8][(c >> 7) & 1][(c & 127) * 16]) = rds[i];
+    }
+    if (tid < TK) k_ts[tid] = rts;
+    __syncthreads();
+    if (t + 1 < n_tiles) prefetch(j0 + TK);
+#pragma unroll
+    for (int blk = 0; blk < TK / 32; ++blk) {
+      const int kb = j0 + 32 * blk;
+      if (!wave_rows || kb > qbase + 31 || kb >= n) continue;  // uniform per wave
+      const unsigned char *ktr = k_tr + blk * 32 * L::TRP;
+      const f16x8 d0 = ds_frag(ds_l[wave][blk], lane, 0), d1 = ds_frag(ds_l[wave][blk], lane, 1);
+#pragma unroll
+      for (int f = 0; f < FT; ++f) {
+        acc[f] = mfma32_f16(tr_frag<DH>(ktr, lane, f, 0), d0, acc[f]);
+        acc[f] = mfma32_f16(tr_frag<DH>(ktr, lane, f, 1), d1, acc[f]);
+      }
+      if (want_rab) {
+        float ds[16];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          ds[e] = (float)d0[e];
+          ds[8 + e] = (float)d1[e];
+        }
+        const int32_t *kts = k_ts + blk * 32 + 4 * half;
+        const int2 tk = bc.use_time ? ld_stat(p.stat + s0 + kb) : int2{0, 0};
+        const BlockBias bb = classify(bc, qbase, kb, tq, tk);
+        const int64_t lim = (int64_t)qts - (int64_t)bb.thr + 1;  // TWO: hi when ts_k < lim
+        const int32_t klim = (int32_t)(lim < (int64_t)INT32_MIN ? (int64_t)INT32_MIN : lim);
+        ra.block(bb, ds, kts, klim, kb, qbase, qi, q_ok, half, qts);
+      }
+    }
+  }
+  if (want_rab) {
+    ra.flush();
+    __syncthreads();
+    rab_write(p, rpos, rtime, h, item);
   }
   if (q_ok) {
     float inv;
@@ -566,6 +784,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkv_kernel(AttnBwdArgs p
   // the list is ordered for the query tiles (tile t visits t + 1 key tiles); key tile
   // nt - 1 - t visits as many query tiles, so the reversal keeps the longest items first
   const int kt = (n + kOwnRows - 1) / kOwnRows - 1 - ld_const(p.work + 2 * item + 1);
+  const int64_t tri0 = p.ds_buf != nullptr ? ld_const(p.tri_base + b) : 0;
   BiasCtx bc;
   load_tables(p, h, ptab, ttab, bc);
 
@@ -641,6 +860,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkv_kernel(AttnBwdArgs p
     // A and dS, then dV^T += dO^T A and dK^T += Q^T dS, over the tile's queries in two
     // halves of 16 (8 values per lane each), so that only one half is live in registers
     const bool diag = i0 < kbase + 31;  // straddles the diagonal: earlier queries masked
+    uint16_t *ds_row = nullptr;  // this lane's row of the stored block (query block i0 / 32)
+    if (p.ds_buf != nullptr) {
+      const int qb = i0 / 32, kbb = kbase / 32;
+      const int64_t blk = (int64_t)h * p.ds_head_blocks + tri0 + (int64_t)qb * (qb + 1) / 2 + kbb;
+      ds_row = p.ds_buf + blk * 1024 + lrow * 32 + 4 * half;
+    }
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       float a[8], ds[8];
@@ -658,6 +883,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkv_kernel(AttnBwdArgs p
         }
       }
       const f16x8 aop = pack8(a), dop = pack8(ds);
+      if (ds_row != nullptr) {  // dS^T of the block, row = this lane's key: queries 8 g + 4 half + 0..3
+        const u32x4 w = __builtin_bit_cast(u32x4, dop);
+        *reinterpret_cast<u32x2 *>(ds_row + 16 * s2) = u32x2{w[0], w[1]};
+        *reinterpret_cast<u32x2 *>(ds_row + 16 * s2 + 8) = u32x2{w[2], w[3]};
+      }
 #pragma unroll
       for (int f = 0; f < FT; ++f) {
         dv_acc[f] = mfma32_f16(tr_frag<DH>(d_tr, lane, f, s2), aop, dv_acc[f]);
@@ -723,6 +953,12 @@ __global__ __launch_bounds__(256) void rab_reduce_kernel(AttnBwdArgs p, float *d
 template <int DH>
 hipError_t launch_bwd_dh(const AttnBwdArgs &a, int64_t cap, hipStream_t stream) {
   const dim3 grid((unsigned)cap, (unsigned)a.num_heads);
+  if (a.ds_buf != nullptr) {  // dK/dV store dS, then dQ reads it
+    tri_base_kernel<<<1, 1024, 0, stream>>>(a.offsets, a.batch, a.tri_base);
+    attn_bwd_dkv_kernel<DH><<<grid, dim3(kThreads), 0, stream>>>(a);
+    attn_bwd_dq_ds_kernel<DH><<<grid, dim3(kThreads), 0, stream>>>(a);
+    return hipGetLastError();
+  }
   attn_bwd_dq_kernel<DH><<<grid, dim3(kThreads), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -62,6 +62,14 @@ struct AttnBwdArgs {
   float *rab_part;
   int64_t rab_cap;
   float *d_rab_pos, *d_rab_time;
+  // dS stored by the dK/dV kernel for the dQ kernel (ds_buf == nullptr: the dQ kernel forms
+  // dS again).  Per head, each sequence's causal triangle of 32 x 32 blocks, block (qb, kb)
+  // (kb <= qb) of sequence b at h ds_head_blocks + tri_base[b] + qb (qb + 1) / 2 + kb, each
+  // block dS^T [key][query] in fp16 (2 KB).  tri_base [B + 1] is formed on the device.
+  uint16_t *ds_buf;
+  int64_t ds_head_blocks;
+  int64_t *tri_base;
+  int batch;
   const float *rab_pos;       // [rab_heads][pos_buckets] or nullptr
   const float *rab_time;      // [rab_heads][time_buckets] or nullptr
   int pos_buckets, time_buckets, rab_per_head;

@@ -368,10 +368,13 @@ def hstu_stochastic_length(raw: DeviceJagged, u_keep: torch.Tensor, keys: torch.
     return kept, new_off, new_ts, x_out
 
 
-def hstu_layer_bwd_workspace_bytes(dims: LayerDims, seq: DeviceJagged) -> int:
+def hstu_layer_bwd_workspace_bytes(dims: LayerDims, seq: DeviceJagged, minimum: bool = False) -> int:
+    """Workspace of hstu_layer_bwd: the size that enables the stored-dS path, or with
+    minimum=True the least that runs at all."""
     lib = _lib.load()
     d, s = dims.c(), seq.c()
-    return int(lib.hstu_layer_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(s)))
+    fn = lib.hstu_layer_bwd_min_workspace_bytes if minimum else lib.hstu_layer_bwd_workspace_bytes
+    return int(fn(ctypes.byref(d), ctypes.byref(s)))
 
 
 def hstu_layer_bwd(dims: LayerDims, w: DeviceWeights, seq: DeviceJagged, x: torch.Tensor,
@@ -414,10 +417,13 @@ def hstu_layer_bwd(dims: LayerDims, w: DeviceWeights, seq: DeviceJagged, x: torc
     return d_x, grads
 
 
-def hstu_attn_bwd_workspace_bytes(dims: LayerDims, seq: DeviceJagged) -> int:
+def hstu_attn_bwd_workspace_bytes(dims: LayerDims, seq: DeviceJagged, minimum: bool = False) -> int:
+    """Workspace of hstu_attn_bwd: the size that enables the stored-dS path, or with
+    minimum=True the least that runs at all."""
     lib = _lib.load()
     d, s = dims.c(), seq.c()
-    return int(lib.hstu_attn_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(s)))
+    fn = lib.hstu_attn_bwd_min_workspace_bytes if minimum else lib.hstu_attn_bwd_workspace_bytes
+    return int(fn(ctypes.byref(d), ctypes.byref(s)))
 
 
 def hstu_attn_bwd(dims: LayerDims, seq: DeviceJagged, q: torch.Tensor, k: torch.Tensor,

@@ -240,8 +240,14 @@ hstu_status_t hstu_stochastic_length(const hstu_jagged_t *raw, const double *u_k
                                      const uint16_t *x_raw, uint16_t *x_out, int64_t row_elems,
                                      void *ws, size_t ws_bytes, void *stream);
 
-/* Workspace (bytes) needed by hstu_attn_bwd; 0 when the arguments are invalid.     */
+/* Workspace (bytes) of hstu_attn_bwd: hstu_attn_bwd_workspace_bytes for the faster path,
+ * which keeps dS (fp16, 2 KB per 32 x 32 block of each causal triangle and head: 4.3 GB
+ * at 8 x 8192 tokens and 8 heads) so that dQ needs no second pass over the scores; it
+ * equals the minimum when that buffer would exceed 32 GiB.  A workspace of at least
+ * hstu_attn_bwd_min_workspace_bytes but less than the first runs the path that forms
+ * dS twice.  Both give the same results to rounding.  0 when the arguments are invalid. */
 size_t hstu_attn_bwd_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_t *seq);
+size_t hstu_attn_bwd_min_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_t *seq);
 
 /* Gradients of equation (2) (the causal attention computed by hstu_attn_fwd without a
  * prefix) for the upstream gradient d_out of its output:
@@ -255,12 +261,13 @@ size_t hstu_attn_bwd_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_
  *   q, k, v    (device) fp16, as for hstu_attn_fwd (row_stride elements between rows)
  *   d_out      (device) fp32 [T][H*dv]; rounded to fp16 for the matrix products
  *   dq, dk, dv (device) fp32 [T][H*dqk], [T][H*dqk], [T][H*dv]
- *   ws         >= hstu_attn_bwd_workspace_bytes(dims, seq)
+ *   ws         >= hstu_attn_bwd_min_workspace_bytes(dims, seq); with
+ *              hstu_attn_bwd_workspace_bytes(dims, seq) bytes the faster path runs
  * The caller owns every buffer.  HSTU_ERR_INVALID_ARG for a null or misaligned pointer,
  * an output equal to another output or to an input, or row_stride < H*dqk or not a
  * multiple of 8; HSTU_ERR_UNSUPPORTED for dqk != dv or dqk not in {32, 64, 128};
- * HSTU_ERR_WORKSPACE for a short or misaligned workspace.  An empty batch returns HSTU_OK
- * without launching anything.                                                       */
+ * HSTU_ERR_WORKSPACE for a workspace below the minimum or misaligned.  An empty batch
+ * launches nothing but the zeroing of the table gradients.                          */
 hstu_status_t hstu_attn_bwd(const hstu_dims_t *dims, const float *rab_pos,
                             const float *rab_time, const hstu_jagged_t *seq,
                             const uint16_t *q, const uint16_t *k, const uint16_t *v,
@@ -282,8 +289,11 @@ typedef struct {
   float *rab_time;  /* [rab_heads][time_buckets] or NULL; likewise                     */
 } hstu_layer_grads_t;
 
-/* Workspace (bytes) needed by hstu_layer_bwd; 0 when the arguments are invalid.       */
+/* Workspace (bytes) of hstu_layer_bwd, as for hstu_attn_bwd: the first enables the
+ * stored-dS path of the attention gradient, the second is the minimum.  0 when the
+ * arguments are invalid.                                                              */
 size_t hstu_layer_bwd_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_t *seq);
+size_t hstu_layer_bwd_min_workspace_bytes(const hstu_dims_t *dims, const hstu_jagged_t *seq);
 
 /* Backward of one causal layer (equations 1-3) for the upstream gradient d_y of its
  * output: dX and the parameter gradients, by the chain rule through f2, the U gate,

@@ -224,8 +224,11 @@ def test_stack_bad_arguments_rejected(lib):
 
 def test_attn_bwd_argument_checks(lib):
     d, s = _dims(), _seq()
-    need = lib.hstu_attn_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(s))
-    assert need > 0
+    need = lib.hstu_attn_bwd_min_workspace_bytes(ctypes.byref(d), ctypes.byref(s))
+    fast = lib.hstu_attn_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(s))
+    assert 0 < need < fast  # the faster path keeps dS: 2 KB per block of each triangle and head
+    # 4 sequences (T = 118, longest 64): at most (ceil(118/32) + 4) x (2 + 1) / 2 + 1 blocks
+    assert fast - need >= 2 * ((4 + 4) * 3 // 2 + 1) * 2048
 
     def call(dims=d, q=FAKE, dout=FAKE + 8192, dq=FAKE + 16384, dk=FAKE + 32768, dv=FAKE + 65536,
              stride=192, ws=FAKE, ws_bytes=need, seq=s, d_pos=None):
@@ -247,8 +250,9 @@ def test_attn_bwd_argument_checks(lib):
 
 def test_layer_bwd_argument_checks(lib):
     d, s = _dims(), _seq()
-    need = lib.hstu_layer_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(s))
+    need = lib.hstu_layer_bwd_min_workspace_bytes(ctypes.byref(d), ctypes.byref(s))
     assert need > lib.hstu_layer_workspace_bytes(ctypes.byref(d), ctypes.byref(s))
+    assert lib.hstu_layer_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(s)) > need
     w = _lib.Weights(FAKE, None, FAKE, None, None, None, None, None)
     G = FAKE + (1 << 24)
 

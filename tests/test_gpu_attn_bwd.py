@@ -53,7 +53,7 @@ def _case(seed, lengths, H, dh, per_head, scale=0.25, g_scale=1.0, pos_buckets=6
     return seq, q, k, v, P, Tt, g
 
 
-def _gpu_bwd(seq, q, k, v, P, Tt, g, H, dh):
+def _gpu_bwd(seq, q, k, v, P, Tt, g, H, dh, path="stored"):
     rows = (P if P is not None else Tt if Tt is not None else np.zeros((1, 1))).shape[0]
     dims = ops.LayerDims(d_model=max(64, H * dh), num_heads=H, dqk=dh, dv=dh,
                          pos_buckets=P.shape[1] if P is not None else 64,
@@ -61,9 +61,14 @@ def _gpu_bwd(seq, q, k, v, P, Tt, g, H, dh):
     buf = dev.f16_tensor(np.concatenate([q, k, v], axis=1))
     hq = H * dh
     opt = lambda a: None if a is None else torch.from_numpy(a).cuda()  # noqa: E731
-    return ops.hstu_attn_bwd(dims, dev.jagged_of(seq), buf[:, :hq], buf[:, hq:2 * hq],
-                             buf[:, 2 * hq:], torch.from_numpy(g).cuda(), row_stride=buf.stride(0),
-                             rab_pos=opt(P), rab_time=opt(Tt), rab_grads=True)
+    js = dev.jagged_of(seq)
+    # "stored": the workspace that keeps dS for the dQ kernel; "recompute": the minimum,
+    # with which the dQ kernel forms dS again
+    ws = torch.empty(max(256, ops.hstu_attn_bwd_workspace_bytes(dims, js, minimum=path == "recompute")),
+                     dtype=torch.uint8, device="cuda")
+    return ops.hstu_attn_bwd(dims, js, buf[:, :hq], buf[:, hq:2 * hq], buf[:, 2 * hq:],
+                             torch.from_numpy(g).cuda(), row_stride=buf.stride(0), rab_pos=opt(P),
+                             rab_time=opt(Tt), rab_grads=True, workspace=ws)
 
 
 # (seed, lengths, H, dh, per-head tables, dO scale, position buckets, time buckets, tables)
@@ -78,17 +83,19 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("path", ["stored", "recompute"])
 @pytest.mark.parametrize("seed,lengths,H,dh,per_head,g_scale,pb,tb,tables", CASES)
-def test_attention_gradients_match_oracle(seed, lengths, H, dh, per_head, g_scale, pb, tb, tables):
+def test_attention_gradients_match_oracle(seed, lengths, H, dh, per_head, g_scale, pb, tb, tables,
+                                          path):
     seq, q, k, v, P, Tt, g = _case(seed, lengths, H, dh, per_head, g_scale=g_scale,
                                    pos_buckets=pb, time_buckets=tb)
     if not tables:
         P = Tt = None
-    say(f"[bwd] lengths={lengths} H={H} dh={dh} per_head_rab={per_head} dO x{g_scale} "
+    say(f"[bwd] {path} lengths={lengths} H={H} dh={dh} per_head_rab={per_head} dO x{g_scale} "
         f"buckets={pb}/{tb} tables={tables}")
-    got = _gpu_bwd(seq, q, k, v, P, Tt, g, H, dh)
+    got = _gpu_bwd(seq, q, k, v, P, Tt, g, H, dh, path)
     torch.cuda.synchronize()
-    again = _gpu_bwd(seq, q, k, v, P, Tt, g, H, dh)
+    again = _gpu_bwd(seq, q, k, v, P, Tt, g, H, dh, path)
     torch.cuda.synchronize()
     want = bwd.attention_bwd(q, k, v, g, seq.offsets, seq.timestamps, H, dh, dh, P, Tt)
     for name, gt, ag, wt in zip(("dq", "dk", "dv", "d_rab_pos", "d_rab_time"), got, again, want):

@@ -73,26 +73,32 @@ def _check_rows(name, got, want):
     assert row_err.max() <= ROW_REL and mean_rel <= MEAN_REL, name
 
 
-def _run(w, weights, d_y):
+def _run(w, weights, d_y, minimum=False):
     d = w.dims
-    return ops.hstu_layer_bwd(dev.dims_of(d), dev.weights_of(weights), dev.jagged_of(w.seq),
-                              dev.bf16_tensor(w.x), torch.from_numpy(d_y).cuda())
+    dims, seq = dev.dims_of(d), dev.jagged_of(w.seq)
+    ws = None
+    if minimum:  # the least workspace: the attention gradient forms dS twice
+        ws = torch.empty(ops.hstu_layer_bwd_workspace_bytes(dims, seq, minimum=True),
+                         dtype=torch.uint8, device="cuda")
+    return ops.hstu_layer_bwd(dims, dev.weights_of(weights), seq, dev.bf16_tensor(w.x),
+                              torch.from_numpy(d_y).cuda(), workspace=ws)
 
 
-@pytest.mark.parametrize("cfg,kw,bias,affine", [
-    (0, {}, True, True),
-    (1, {"batch": 12}, False, False),
-    (2, {"batch": 2, "seq_len": 600}, True, True),
+@pytest.mark.parametrize("cfg,kw,bias,affine,minimum", [
+    (0, {}, True, True, False),
+    (1, {"batch": 12}, False, False, False),
+    (2, {"batch": 2, "seq_len": 600}, True, True, False),
+    (2, {"batch": 2, "seq_len": 600}, True, True, True),
 ])
-def test_layer_gradients_match_oracle(cfg, kw, bias, affine):
+def test_layer_gradients_match_oracle(cfg, kw, bias, affine, minimum):
     w = wl.config(cfg, **kw)
     d = w.dims
     rng = np.random.default_rng(700 + cfg)
     weights = wl.draw_weights(rng, d, bias=bias, affine=affine)
     d_y = rng.standard_normal((w.seq.total, d.d_model)).astype(np.float32)
     say(f"[layer bwd] config {cfg} {kw} T={w.seq.total} d={d.d_model} H={d.num_heads}x{d.dqk} "
-        f"bias={bias} affine={affine}")
-    d_x, grads = _run(w, weights, d_y)
+        f"bias={bias} affine={affine} minimum workspace={minimum}")
+    d_x, grads = _run(w, weights, d_y, minimum)
     torch.cuda.synchronize()
     want = bwd.layer_bwd(w.x, weights, w.seq.offsets, w.seq.timestamps, d.num_heads, d.dqk,
                          d.dv, d_y, d.ln_eps)
