@@ -490,7 +490,7 @@ static int64_t ds_head_blocks(const hstu_jagged_t *s) {
 
 static size_t ds_bytes(const hstu_dims_t *d, const hstu_jagged_t *s) {
   if (s->total_tokens == 0) return 0;
-  const size_t bytes = align_up((size_t)(s->batch + 1) * sizeof(int64_t)) +
+  const size_t bytes = align_up((size_t)(s->batch + 1) * sizeof(int64_t)) + 2048 +
                        align_up((size_t)ds_head_blocks(s) * d->num_heads * 2048);
   return bytes <= kDsCapBytes ? bytes : 0;
 }
@@ -511,7 +511,8 @@ static void attach_ds(AttnBwdArgs &a, const hstu_dims_t *d, const hstu_jagged_t 
   const size_t need = ds_bytes(d, s);
   if (need == 0 || have < need) return;
   a.tri_base = (int64_t *)base;
-  a.ds_buf = (uint16_t *)(base + align_up((size_t)(s->batch + 1) * sizeof(int64_t)));
+  a.ds_dump = (uint16_t *)(base + align_up((size_t)(s->batch + 1) * sizeof(int64_t)));
+  a.ds_buf = a.ds_dump + 1024;
   a.ds_head_blocks = ds_head_blocks(s);
   a.batch = s->batch;
 }

@@ -105,6 +105,17 @@ __device__ __forceinline__ int32_t load_ts(__amdgpu_buffer_rsrc_t rs, int row, i
   return __builtin_amdgcn_raw_buffer_load_b32(rs, row * 4, r0 * 4, 0);
 }
 
+// Workgroup barrier that orders LDS only: this wave's LDS reads and writes are complete
+// (lgkmcnt 0), while its global loads and stores stay in flight (the barrier of
+// __syncthreads also waits for every store, which here would hold each wave at every
+// tile until its dS stores had reached memory).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63 (no wait), expcnt 7 (no wait), lgkmcnt 0
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Registers of one tile of ROWS rows of an fp16 matrix, spread over the workgroup:
 // chunk tid + 256 c for c < N.  Each lane's byte offset within the tile is fixed; the
 // tile's first row goes in the uniform offset.
@@ -367,15 +378,7 @@ struct RabAcc {
       float sum = 0.0f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) sum += ds[i];
-      pos_run += sum;
-      if (use_time) {
-        if (bb.tb != t_run_b) {
-          time_add(t_run, t_run_b);
-          t_run = 0.0f;
-          t_run_b = bb.tb;
-        }
-        t_run += sum;
-      }
+      add_const(bb, sum);
     } else if (bb.kind == KIND_TWO) {
       float shi = 0.0f, slo = 0.0f;
 #pragma unroll
@@ -399,6 +402,18 @@ struct RabAcc {
             atomicAdd(&ltime[min(time_log2_bucket(qts, kts[8 * (i >> 2) + (i & 3)]), TB - 1)], ds[i]);
         }
       }
+    }
+  }
+  // a CONST block, given the sum of the lane's 16 values
+  __device__ __forceinline__ void add_const(const BlockBias &bb, float sum) {
+    pos_run += sum;
+    if (use_time) {
+      if (bb.tb != t_run_b) {
+        time_add(t_run, t_run_b);
+        t_run = 0.0f;
+        t_run_b = bb.tb;
+      }
+      t_run += sum;
     }
   }
   __device__ __forceinline__ void flush() {
@@ -614,14 +629,27 @@ __global__ __launch_bounds__(1024) void tri_base_kernel(const int32_t *offsets, 
   }
 }
 
-// Transposed operand of a stored block dS^T [key][query] (rows of 64 bytes) for k-step
-// s2: keys 16 s2 + 8 (e / 4) + 4 (lane / 32) + e % 4 (e = 0..7) of query lane % 32, the
-// key order of tr_frag
+// A stored block in LDS: its two 1 KB halves (the dK/dV kernel's lanes 0..63, 16 bytes
+// each) at kDsHalf bytes apart, lanes 32..63 of a half 64 bytes further on, so that the
+// transposing reads below fall on distinct banks.
+constexpr int kDsHalf = 1088;
+constexpr int kDsBlock = 2 * kDsHalf;
+__device__ __forceinline__ int ds_lds_offset(int piece) {  // 16-byte piece of the 2 KB block
+  const int half = piece >> 6, L = piece & 63;
+  return half * kDsHalf + L * 16 + (L >= 32 ? 64 : 0);
+}
+
+// Transposed operand of a stored block for k-step s2: keys 16 s2 + 8 (e / 4) +
+// 4 (lane / 32) + e % 4 (e = 0..7) of query lane % 32, the key order of tr_frag.  The
+// transposing read takes, per 16-lane group, 4 keys x 4 groups of 4 queries; queries
+// 4 m .. 4 m + 3 of key k sit in the dK/dV lane k + 32 (m % 2) of half m / 4, at values
+// 4 ((m / 2) % 2) .. + 3.
 __device__ __forceinline__ f16x8 ds_frag(const unsigned char *blk, int lane, int s2) {
-  const int row = 4 * (lane >> 5) + ((lane & 15) >> 2);
-  const int col = (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
-  const u32x2 lo = tr_read(blk + (16 * s2 + row) * 64 + col);
-  const u32x2 hi = tr_read(blk + (16 * s2 + 8 + row) * 64 + col);
+  const int g = lane >> 4, c = lane & 3, jr = (lane & 15) >> 2;
+  const int base = (g & 1) * kDsHalf + 64 * (c & 1) + 8 * (c >> 1) + 32 * (c & 1) * 16;
+  const int k = 16 * s2 + 4 * (lane >> 5) + jr;
+  const u32x2 lo = tr_read(blk + base + k * 16);
+  const u32x2 hi = tr_read(blk + base + (k + 8) * 16);
   return as_f16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 
@@ -634,9 +662,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_ds_kernel(AttnBwdArgs
   using L = BwdLayout<DH>;
   constexpr int FT = L::FT;
   constexpr int TK = 64;
-  constexpr int DSB = 2048;  // bytes of a stored block
   __shared__ __attribute__((aligned(16))) unsigned char k_tr[TK * L::TRP];
-  __shared__ __attribute__((aligned(16))) unsigned char ds_l[kWaves][TK / 32][DSB];
+  __shared__ __attribute__((aligned(16))) unsigned char ds_l[kWaves][TK / 32][kDsBlock];
   __shared__ int32_t k_ts[TK];
   __shared__ float ptab[kMaxPos], ttab[kMaxTime];
   __shared__ float rpos[kWaves][kMaxPos];
@@ -687,8 +714,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_ds_kernel(AttnBwdArgs
       const int qb = q0 / 32 + (c >> 8), kb = j0 / 32 + ((c >> 7) & 1);
       rds[i] = u32x4{0, 0, 0, 0};
       if (qb < nq_blocks && kb <= qb)
-        rds[i] = *reinterpret_cast<const u32x4 *>(
-            p.ds_buf + (head0 + (int64_t)qb * (qb + 1) / 2 + kb) * 1024 + (c & 127) * 8);
+        rds[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+            p.ds_buf + (head0 + (int64_t)qb * (qb + 1) / 2 + kb) * 1024 + (c & 127) * 8));
     }
     if (tid < TK) rts = load_ts(trs, tid, j0);
   };
@@ -700,11 +727,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_ds_kernel(AttnBwdArgs
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = tid + 256 * i;
-      *reinterpret_cast<u32x4 *>(&ds_l[c >> 8][(c >> 7) & 1][(c & 127) * 16]) = rds[i];
+      *reinterpret_cast<u32x4 *>(&ds_l[c >> 8][(c >> 7) & 1][ds_lds_offset(c & 127)]) = rds[i];
     }
     if (tid < TK) k_ts[tid] = rts;
     __syncthreads();
     if (t + 1 < n_tiles) prefetch(j0 + TK);
+    int2 tks[TK / 32];  // the blocks' key timestamp ranges, loaded ahead of their use
+#pragma unroll
+    for (int blk = 0; blk < TK / 32; ++blk)
+      tks[blk] = (want_rab && bc.use_time && j0 + 32 * blk < n) ? ld_stat(p.stat + s0 + j0 + 32 * blk)
+                                                                : int2{0, 0};
 #pragma unroll
     for (int blk = 0; blk < TK / 32; ++blk) {
       const int kb = j0 + 32 * blk;
@@ -717,18 +749,28 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_ds_kernel(AttnBwdArgs
         acc[f] = mfma32_f16(tr_frag<DH>(ktr, lane, f, 1), d1, acc[f]);
       }
       if (want_rab) {
-        float ds[16];
+        const BlockBias bb = classify(bc, qbase, kb, tq, tks[blk]);
+        if (bb.kind == KIND_CONST) {  // the lane's sum by packed dot products with ones
+          typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+          const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
+          float sum = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          ds[e] = (float)d0[e];
-          ds[8 + e] = (float)d1[e];
+          for (int e = 0; e < 8; e += 2) {
+            sum = __builtin_amdgcn_fdot2(h2{d0[e], d0[e + 1]}, one, sum, false);
+            sum = __builtin_amdgcn_fdot2(h2{d1[e], d1[e + 1]}, one, sum, false);
+          }
+          ra.add_const(bb, sum);
+        } else {
+          float ds[16];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            ds[e] = (float)d0[e];
+            ds[8 + e] = (float)d1[e];
+          }
+          const int64_t lim = (int64_t)qts - (int64_t)bb.thr + 1;  // TWO: hi when ts_k < lim
+          const int32_t klim = (int32_t)(lim < (int64_t)INT32_MIN ? (int64_t)INT32_MIN : lim);
+          ra.block(bb, ds, k_ts + blk * 32 + 4 * half, klim, kb, qbase, qi, q_ok, half, qts);
         }
-        const int32_t *kts = k_ts + blk * 32 + 4 * half;
-        const int2 tk = bc.use_time ? ld_stat(p.stat + s0 + kb) : int2{0, 0};
-        const BlockBias bb = classify(bc, qbase, kb, tq, tk);
-        const int64_t lim = (int64_t)qts - (int64_t)bb.thr + 1;  // TWO: hi when ts_k < lim
-        const int32_t klim = (int32_t)(lim < (int64_t)INT32_MIN ? (int64_t)INT32_MIN : lim);
-        ra.block(bb, ds, kts, klim, kb, qbase, qi, q_ok, half, qts);
       }
     }
   }
@@ -818,21 +860,34 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkv_kernel(AttnBwdArgs p
   const __amdgpu_buffer_rsrc_t trs = ts_rsrc(bc.use_time ? p.ts : nullptr, s0, n);
   TileRegs<DH, TQ> rq, rd;
   int32_t rts = 0;
+  // Every tile's loads are issued by every thread on every path (past the sequence end
+  // they read zero), and with dS kept every path then issues two stores, so the wait for a
+  // tile's loads has the same form on every path and leaves the stores in flight.
   auto prefetch = [&](int i0) __attribute__((always_inline)) {
     rq.load(qrs, p.stride, i0);
     rd.load(drs, p.d_stride, i0);
-    if (tid < TQ) rts = load_ts(trs, tid, i0);
+    rts = load_ts(trs, tid, i0);
+  };
+  auto dump_stores = [&]() __attribute__((always_inline)) {
+    __builtin_nontemporal_store(u32x4{0, 0, 0, 0}, reinterpret_cast<u32x4 *>(p.ds_dump + 8 * lane));
+    __builtin_nontemporal_store(u32x4{0, 0, 0, 0}, reinterpret_cast<u32x4 *>(p.ds_dump + 512 + 8 * lane));
   };
   prefetch(k0);
+  if (p.ds_buf != nullptr) dump_stores();
   for (int t = 0; t < n_tiles; ++t) {
     const int i0 = k0 + t * TQ;
-    __syncthreads();  // the previous tile is no longer read (tables and V rows written)
+    lds_barrier();  // the previous tile is no longer read (tables and V rows written)
     rq.template store<true>(q_row, q_tr);
     rd.template store<true>(d_row, d_tr);
     if (tid < TQ) q_ts[tid] = rts;
-    __syncthreads();
-    if (t + 1 < n_tiles) prefetch(i0 + TQ);
-    if (!wave_rows || i0 + 31 < kbase) continue;  // every query precedes this wave's keys
+    lds_barrier();
+    prefetch(i0 + TQ);
+    if (!wave_rows || i0 + 31 < kbase) {  // every query precedes this wave's keys
+      // (loads and stores share one in-order counter: a skipped block writes zeros to a
+      // slot that nothing reads, so that this path too issues two stores)
+      if (p.ds_buf != nullptr) dump_stores();
+      continue;
+    }
     const int2 tq = bc.use_time ? ld_stat(p.stat + s0 + i0) : int2{0, 0};
     const BlockBias bb = classify(bc, i0, kbase, tq, tk);
     const int32_t *qtsp = q_ts + 4 * half;
@@ -860,11 +915,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkv_kernel(AttnBwdArgs p
     // A and dS, then dV^T += dO^T A and dK^T += Q^T dS, over the tile's queries in two
     // halves of 16 (8 values per lane each), so that only one half is live in registers
     const bool diag = i0 < kbase + 31;  // straddles the diagonal: earlier queries masked
-    uint16_t *ds_row = nullptr;  // this lane's row of the stored block (query block i0 / 32)
+    uint16_t *ds_blk = nullptr;  // the stored block (query block i0 / 32, this wave's keys)
     if (p.ds_buf != nullptr) {
       const int qb = i0 / 32, kbb = kbase / 32;
-      const int64_t blk = (int64_t)h * p.ds_head_blocks + tri0 + (int64_t)qb * (qb + 1) / 2 + kbb;
-      ds_row = p.ds_buf + blk * 1024 + lrow * 32 + 4 * half;
+      ds_blk = p.ds_buf + ((int64_t)h * p.ds_head_blocks + tri0 + (int64_t)qb * (qb + 1) / 2 + kbb) * 1024;
     }
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
@@ -883,11 +937,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkv_kernel(AttnBwdArgs p
         }
       }
       const f16x8 aop = pack8(a), dop = pack8(ds);
-      if (ds_row != nullptr) {  // dS^T of the block, row = this lane's key: queries 8 g + 4 half + 0..3
-        const u32x4 w = __builtin_bit_cast(u32x4, dop);
-        *reinterpret_cast<u32x2 *>(ds_row + 16 * s2) = u32x2{w[0], w[1]};
-        *reinterpret_cast<u32x2 *>(ds_row + 16 * s2 + 8) = u32x2{w[2], w[3]};
-      }
+      if (ds_blk != nullptr)  // the lane's 8 values of this half: 1 KB per wave, contiguous;
+        // streamed past the caches, which hold the Q and dO tiles that other workgroups reuse
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, dop),
+                                    reinterpret_cast<u32x4 *>(ds_blk + 512 * s2 + 8 * lane));
 #pragma unroll
       for (int f = 0; f < FT; ++f) {
         dv_acc[f] = mfma32_f16(tr_frag<DH>(d_tr, lane, f, s2), aop, dv_acc[f]);

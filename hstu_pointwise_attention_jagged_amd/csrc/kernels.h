@@ -65,8 +65,11 @@ struct AttnBwdArgs {
   // dS stored by the dK/dV kernel for the dQ kernel (ds_buf == nullptr: the dQ kernel forms
   // dS again).  Per head, each sequence's causal triangle of 32 x 32 blocks, block (qb, kb)
   // (kb <= qb) of sequence b at h ds_head_blocks + tri_base[b] + qb (qb + 1) / 2 + kb, each
-  // block dS^T [key][query] in fp16 (2 KB).  tri_base [B + 1] is formed on the device.
+  // block 2 KB of fp16 in the dK/dV kernel's register order: [half s][lane L][8], holding
+  // dS of key L % 32 and query 8 (e / 4) + 4 (L / 32) + e % 4, e = 8 s + 0..7.
+  // tri_base [B + 1] is formed on the device.
   uint16_t *ds_buf;
+  uint16_t *ds_dump;  // 2 KB that skipped blocks write (never read)
   int64_t ds_head_blocks;
   int64_t *tri_base;
   int batch;
