@@ -12,16 +12,21 @@
 //    that brings that maximum into [0.5, 1).  Every gradient is linear in dO, so the
 //    kernels multiply their results by 2^e (exact); tiny training gradients keep their
 //    fp16 precision and dA, dS stay far from the fp16 range limit.
-//  * attn_bwd_dq_kernel: a workgroup of 4 waves owns 128 query rows (32 per wave, their Q
-//    and dO fragments in registers) and streams key tiles of K and V through LDS.  Per
-//    32 x 32 block: S^T = K Q^T and dA^T = V dO^T (each lane holds 16 keys of one query),
-//    dS^T elementwise, then dQ^T += K^T dS^T with the K^T operand taken from row-major K
-//    by the transposing LDS read.
-//  * attn_bwd_dkv_kernel: a workgroup owns 128 key rows (K fragments in registers, V rows
-//    in LDS) and streams 32-query tiles of Q and dO.  Per block: S = Q K^T and dA = dO V^T
-//    (each lane holds 16 queries of one key), A and dS elementwise, then dV^T += dO^T A
-//    and dK^T += Q^T dS through transposing reads of Q and dO.
-// Both kernels load the next tile into registers while the current one is computed.  The
+//  * attn_bwd_dkv_kernel: a workgroup of 4 waves owns 128 key rows (K fragments in
+//    registers, V rows in LDS) and streams 32-query tiles of Q and dO.  Per 32 x 32 block:
+//    S = Q K^T and dA = dO V^T (each lane holds 16 queries of one key), A and dS
+//    elementwise, then dV^T += dO^T A and dK^T += Q^T dS through transposing LDS reads of Q
+//    and dO.  When the workspace holds it, each block of dS is also stored (fp16).
+//  * attn_bwd_dq_ds_kernel (dS stored): a workgroup owns 128 query rows and streams K tiles
+//    and the stored dS blocks through LDS; per block dQ^T += K^T dS^T, both operands by the
+//    transposing read.  The five products of the gradient each run once.
+//  * attn_bwd_dq_kernel (dS not stored): a workgroup owns 128 query rows (Q and dO
+//    fragments in registers) and streams key tiles of K and V.  Per block: S^T = K Q^T and
+//    dA^T = V dO^T (each lane holds 16 keys of one query), dS^T elementwise, then
+//    dQ^T += K^T dS^T: S and dA are formed a second time.
+//  * the dQ kernels also sum dS per bias bucket when the tables' gradients are asked for;
+//    rab_reduce_kernel adds the workgroups' sums in a fixed order.
+// The kernels load the next tile into registers while the current one is computed.  The
 // bias of a 32 x 32 block is classified once per wave from the blocks' timestamp ranges
 // and position gap (the log2 time bucket is monotone in the gap): one value for the whole
 // block (CONST), two values split by a time threshold (TWO), or per element (GENERAL,
