@@ -6,8 +6,10 @@
 //   dA = dO V^T,  dS = dA * SiLU'(S) (0 on masked pairs),  dQ = dS K,  dK = dS^T Q,
 //   dV = A^T dO,  SiLU'(x) = sigma(x) (1 + x (1 - sigma(x))).
 //
-// No softmax, so no row statistics: each gradient is a plain sum over pairs, computed
-// without atomics on the gradients (deterministic) in these launches:
+// No softmax, so no row statistics: each gradient is a plain sum over pairs.  dQ, dK and
+// dV are computed without atomics (fixed summation orders); the bias tables' sums add
+// into per-wave LDS bins with LDS atomics, where only the lanes of one wave meet at an
+// address.  The launches:
 //  * prep: max |dO| over the batch, then dO x 2^-e in fp16, with 2^e the power of two
 //    that brings that maximum into [0.5, 1).  Every gradient is linear in dO, so the
 //    kernels multiply their results by 2^e (exact); tiny training gradients keep their

@@ -257,7 +257,9 @@ size_t hstu_attn_bwd_min_workspace_bytes(const hstu_dims_t *dims, const hstu_jag
  * the tables' gradients too: the sum of dS over the allowed pairs of each bucket (over
  * all heads when the table is shared).  Either may be NULL (not formed); each must be
  * NULL when its table is.  An empty batch sets them to 0.  Every row of dq, dk and dv is
- * written; the result is deterministic (fixed summation orders).
+ * written.  dq, dk and dv are deterministic (fixed summation orders); the tables' sums
+ * add per wave in LDS with atomics, so their order between a wave's lanes is the
+ * hardware's.
  *   q, k, v    (device) fp16, as for hstu_attn_fwd (row_stride elements between rows)
  *   d_out      (device) fp32 [T][H*dv]; rounded to fp16 for the matrix products
  *   dq, dk, dv (device) fp32 [T][H*dqk], [T][H*dqk], [T][H*dv]
