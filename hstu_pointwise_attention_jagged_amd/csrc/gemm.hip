@@ -14,7 +14,8 @@
 //    first half of the previous stage; 16-byte chunks are
 //    XOR-swizzled by row so the operand reads are bank-conflict free without padding.
 //    Operand fragments are double-buffered in registers across k-steps, and workgroup
-//    ids are remapped so each XCD works through a contiguous range of tiles.
+//    ids are remapped so each XCD works through a contiguous range of tiles.  The
+//    finished tile goes back through LDS so that every store writes whole rows.
 //  * gemm_kernel (any N multiple of 64): 128 x 128 (or 128 x 64) tiles with register
 //    prefetch, for the small shapes.
 #include "common.h"
@@ -157,6 +158,7 @@ constexpr int kBigBK = 64;      // K per LDS stage
 constexpr int kBigStages = 2;   // ring of stages; loads run kBigStages - 1 stages ahead
 constexpr int kCPR = kBigBK / 8;  // 16-byte chunks per row
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
+constexpr int kOutPitch = kBigTile * 2 + 16;  // bytes per output row staged in LDS
 
 // LDS byte offset of 16-byte chunk c (0..7) of row r in a [rows][64] bf16 stage; the
 // chunk is XOR-swizzled by row pair so that 16 lanes reading one chunk of 16
@@ -288,30 +290,43 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm256_kernel(const uint16_t 
     }
   }
 
-  // epilogue: lane holds token (lane % 32) and features 8g + 4*(lane/32) + 0..3
+  // Epilogue through LDS.  A lane holds token (lane % 32) and features 8g + 4*(lane/32)
+  // + 0..3 of each MFMA tile, so direct stores would scatter 8-byte pieces over 32 rows
+  // per instruction; instead the finished 16-bit tile is staged in LDS (free once every
+  // wave is past its last operand read) and written back as whole 512-byte rows.
+  __syncthreads();
 #pragma unroll
   for (int j = 0; j < MT; ++j) {
-    const int m = m0 + wm * TM + j * 32 + lrow;
-    if (m >= M) continue;
+    const int r = wm * TM + j * 32 + lrow;
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * TN + i * 32 + 8 * g + 4 * lk;
+        const int c = wn * TN + i * 32 + 8 * g + 4 * lk;
         float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
         float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
         if (bias != nullptr) {
-          const f32x4 bb = *reinterpret_cast<const f32x4 *>(bias + n);
+          const f32x4 bb = *reinterpret_cast<const f32x4 *>(bias + n0 + c);
           v0 += bb[0]; v1 += bb[1]; v2 += bb[2]; v3 += bb[3];
         }
         if (ACT == ACT_SILU) {
           v0 = silu_f32(v0); v1 = silu_f32(v1); v2 = silu_f32(v2); v3 = silu_f32(v3);
         }
-        u32x2 pk = OUT == OUT_F16 ? u32x2{pack_f16_sat(v0, v1), pack_f16_sat(v2, v3)}
-                                  : u32x2{pack_bf16(v0, v1), pack_bf16(v2, v3)};
-        *reinterpret_cast<u32x2 *>(out + (int64_t)m * N + n) = pk;
+        const u32x2 pk = OUT == OUT_F16 ? u32x2{pack_f16_sat(v0, v1), pack_f16_sat(v2, v3)}
+                                        : u32x2{pack_bf16(v0, v1), pack_bf16(v2, v3)};
+        *reinterpret_cast<u32x2 *>(smem + r * kOutPitch + c * 2) = pk;
       }
     }
+  }
+  __syncthreads();
+  // each wave instruction stores two whole rows of the tile (64 lanes x 16 bytes)
+  constexpr int kRowChunks = kBigTile * 2 / 16;
+#pragma unroll
+  for (int it = 0; it < kBigTile * kRowChunks / kBigThreads; ++it) {
+    const int ch = it * kBigThreads + tid;
+    const int r = ch / kRowChunks, c16 = ch % kRowChunks;
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(smem + r * kOutPitch + c16 * 16);
+    if (m0 + r < M) *reinterpret_cast<u32x4 *>(out + (int64_t)(m0 + r) * N + n0 + c16 * 8) = v;
   }
 }
 
@@ -322,7 +337,8 @@ hipError_t launch_big(const uint16_t *A, const uint16_t *W, const float *bias, u
   const int tm = (M + kBigTile - 1) / kBigTile;
   const int total = tm * tn;
   const int grid = (total + 7) / 8 * 8;
-  const size_t lds = 2 * (size_t)kBigStages * kBigTile * kBigBK * 2;  // stages x 2 operands
+  // operand stages (2 operands each), reused for the output tile in the epilogue
+  const size_t lds = std::max(2 * (size_t)kBigStages * kBigTile * kBigBK * 2, (size_t)kBigTile * kOutPitch);
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void *)gemm256_kernel<ACT, OUT>,
