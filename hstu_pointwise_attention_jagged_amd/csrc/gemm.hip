@@ -319,14 +319,21 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm256_kernel(const uint16_t 
     }
   }
   __syncthreads();
-  // each wave instruction stores two whole rows of the tile (64 lanes x 16 bytes)
+  // Each wave instruction stores two whole rows of the tile (64 lanes x 16 bytes).  The
+  // fp16 products (U, V, Q, K: four times the model width) outgrow the last-level cache
+  // and are streamed past it with non-temporal stores, which keeps the operands cached;
+  // the bf16 output (the next layer's input) is stored normally.
   constexpr int kRowChunks = kBigTile * 2 / 16;
 #pragma unroll
   for (int it = 0; it < kBigTile * kRowChunks / kBigThreads; ++it) {
     const int ch = it * kBigThreads + tid;
     const int r = ch / kRowChunks, c16 = ch % kRowChunks;
     const u32x4 v = *reinterpret_cast<const u32x4 *>(smem + r * kOutPitch + c16 * 16);
-    if (m0 + r < M) *reinterpret_cast<u32x4 *>(out + (int64_t)(m0 + r) * N + n0 + c16 * 8) = v;
+    u32x4 *dst = reinterpret_cast<u32x4 *>(out + (int64_t)(m0 + r) * N + n0 + c16 * 8);
+    if (m0 + r < M) {
+      if constexpr (OUT == OUT_F16) __builtin_nontemporal_store(v, dst);
+      else *dst = v;
+    }
   }
 }
 
