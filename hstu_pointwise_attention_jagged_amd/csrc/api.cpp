@@ -616,7 +616,7 @@ hstu_status_t hstu_attn_bwd(const hstu_dims_t *dims, const float *rab_pos, const
 // ------------------------------------------------------------------------------------
 namespace {
 
-constexpr int kColsumParts = 256;
+constexpr int kColsumParts = 1024;
 
 struct LayerBwdWs {
   uint16_t *z, *uvqk, *d_h, *dy16, *g16, *dz;

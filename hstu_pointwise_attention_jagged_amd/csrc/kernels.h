@@ -99,7 +99,7 @@ struct NormGateBwdArgs {
   float *part_gamma, *part_beta;  // [norm_gate_bwd_waves(T)][hdv] partial sums or nullptr
   int T, hdv;
 };
-constexpr int kNgWaves = 1024;  // most waves (and partial rows) of the norm-gate backward
+constexpr int kNgWaves = 4096;  // most waves (and partial rows) of the norm-gate backward
 int norm_gate_bwd_waves(int T);
 hipError_t launch_norm_gate_bwd(const NormGateBwdArgs &a, hipStream_t stream);
 hipError_t launch_silu_f16(const uint16_t *z, uint16_t *out, int64_t n, hipStream_t stream);

@@ -192,6 +192,8 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const T *a, int row
   if (col >= cols) return;
   const int r0 = blockIdx.y * rows_per, r1 = min(rows, r0 + rows_per);
   float acc[VEC] = {};
+  // unrolled so that several rows' loads are in flight; the adds stay in row order
+#pragma unroll 8
   for (int r = r0; r < r1; ++r) Vec16<T>::add(a + (int64_t)r * stride + col, acc);
   float *dst = partial + (int64_t)blockIdx.y * cols + col;
 #pragma unroll
