@@ -63,6 +63,10 @@ EXPORTS = {
     "hstu_attn_fwd": (c_int32, [ctypes.POINTER(Dims), c_void_p, c_void_p, ctypes.POINTER(Jagged),
                                 c_void_p, c_void_p, c_void_p, c_int64, ctypes.POINTER(Prefix),
                                 c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "hstu_attn_noalloc_max_scratch_bytes": (c_size_t, []),
+    "hstu_attn_fwd_noalloc": (c_int32, [ctypes.POINTER(Dims), c_void_p, c_void_p, ctypes.POINTER(Jagged),
+                                        c_void_p, c_void_p, c_void_p, c_int64, ctypes.POINTER(Prefix),
+                                        c_int32, c_void_p, c_void_p]),
     "hstu_stack_workspace_bytes": (c_size_t, [ctypes.POINTER(Dims), ctypes.POINTER(Jagged)]),
     "hstu_stack_mfalcon_workspace_bytes": (c_size_t, [ctypes.POINTER(Dims), ctypes.POINTER(Jagged),
                                                       ctypes.POINTER(Jagged)]),

@@ -812,11 +812,23 @@ hstu_status_t hstu_layer_bwd(const hstu_dims_t *dims, const hstu_weights_t *w,
   return HSTU_OK;
 }
 
-hstu_status_t hstu_attn_fwd(const hstu_dims_t *dims, const float *rab_pos, const float *rab_time,
-                            const hstu_jagged_t *seq, const uint16_t *q, const uint16_t *k,
-                            const uint16_t *v, int64_t row_stride, const hstu_prefix_t *prefix,
-                            hstu_mask_t mask, float *out, void *ws, size_t ws_bytes,
-                            void *stream) {
+}  // extern "C"
+
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+// Host checks of an attention call; on success max_prefix is the prefix's longest length.
+hstu_status_t check_attn_call(const hstu_dims_t *dims, const hstu_jagged_t *seq,
+                              const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                              int64_t row_stride, const hstu_prefix_t *prefix, hstu_mask_t mask,
+                              const float *out, int &max_prefix) {
   hstu_status_t st;
   if ((st = check_attn_dims(dims)) != HSTU_OK) return st;
   if ((st = check_seq(seq)) != HSTU_OK) return st;
@@ -826,7 +838,7 @@ hstu_status_t hstu_attn_fwd(const hstu_dims_t *dims, const float *rab_pos, const
     return HSTU_ERR_INVALID_ARG;
   if (row_stride < hq || row_stride % 8 != 0) return HSTU_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return HSTU_ERR_INVALID_ARG;
-  int max_prefix = 0;
+  max_prefix = 0;
   if (prefix != nullptr) {
     if ((st = check_seq(prefix->seq)) != HSTU_OK) return st;
     if (prefix->seq->batch != seq->batch) return HSTU_ERR_INVALID_ARG;
@@ -840,14 +852,23 @@ hstu_status_t hstu_attn_fwd(const hstu_dims_t *dims, const float *rab_pos, const
     max_prefix = prefix->seq->max_seq_len;
   }
   if (seq->batch == 0 || seq->total_tokens == 0) return HSTU_OK;
-  const hstu_jagged_t *pre_seq = prefix != nullptr ? prefix->seq : nullptr;
-  if ((st = check_ws(ws, ws_bytes, attn_ws_bytes(seq, pre_seq))) != HSTU_OK) return st;
   if (!rows_addressable(seq->max_seq_len, row_stride) ||
       (prefix != nullptr && !rows_addressable(prefix->seq->max_seq_len, prefix->row_stride)))
     return HSTU_ERR_UNSUPPORTED;
+  return HSTU_OK;
+}
 
+// Schedule, key-block timestamp ranges and the attention kernel of a checked call, with
+// their scratch carved from ws (attn_ws_bytes(seq, prefix seq) bytes, 256-byte aligned).
+// `profile` brackets the launches with the optional timing events.
+hstu_status_t launch_attn_call(const hstu_dims_t *dims, const float *rab_pos,
+                               const float *rab_time, const hstu_jagged_t *seq, const uint16_t *q,
+                               const uint16_t *k, const uint16_t *v, int64_t row_stride,
+                               const hstu_prefix_t *prefix, hstu_mask_t mask, float *out,
+                               int max_prefix, char *ws, hipStream_t sst, bool profile) {
+  const hstu_jagged_t *pre_seq = prefix != nullptr ? prefix->seq : nullptr;
   LayerWs lw{};
-  carve_attn((char *)ws, seq, pre_seq, lw);
+  carve_attn(ws, seq, pre_seq, lw);
   AttnArgs aa = attn_args(dims, rab_pos, rab_time, seq, q, k, v, row_stride, out, lw);
   aa.mask = mask == HSTU_MASK_CAUSAL ? 0 : 1;
   if (prefix != nullptr) {
@@ -857,18 +878,84 @@ hstu_status_t hstu_attn_fwd(const hstu_dims_t *dims, const float *rab_pos, const
     aa.pv = prefix->v;
     aa.p_stride = prefix->row_stride;
   }
-  hipStream_t sst = (hipStream_t)stream;
-  hipError_t e = timed(0, sst, [&] {
+  auto maybe_timed = [&](int id, auto &&fn) { return profile ? timed(id, sst, fn) : fn(); };
+  hipError_t e = maybe_timed(0, [&] {
     return launch_schedule(seq->seq_offsets, aa.p_offsets, seq->batch, aa.mask, seq->max_seq_len,
                            max_prefix, lw.work, lw.n_work, sst);
   });
   if (e != hipSuccess) return hip_fail(e);
-  e = timed(0, sst, [&] { return launch_stats(aa, seq, pre_seq, sst); });
+  e = maybe_timed(0, [&] { return launch_stats(aa, seq, pre_seq, sst); });
   if (e != hipSuccess) return hip_fail(e);
   const int64_t cap = attn_work_capacity(seq->batch, seq->total_tokens);
-  e = timed(2, sst, [&] { return launch_attention(aa, dims->dqk, seq->max_seq_len, cap, sst); });
+  e = maybe_timed(2, [&] { return launch_attention(aa, dims->dqk, seq->max_seq_len, cap, sst); });
   if (e != hipSuccess) return hip_fail(e);
   return HSTU_OK;
+}
+
+// ------------------------------------------------------------------------------------
+// Scratch of hstu_attn_fwd_noalloc: a static device array (one copy per GPU, held until
+// the process ends) instead of a caller workspace.  In host code `scratch` only names the
+// symbol; its device address on the current GPU comes from hipGetSymbolAddress, taken
+// once per device and cached here, and only that address is ever handed to a kernel.
+// ------------------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current GPU's scratch array, looked up on first use.
+hstu_status_t scratch_on_current_device(char **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return HSTU_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    if (ptr == nullptr) return hip_fail(hipErrorInvalidSymbol);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = (char *)g_scratch_ptr[dev];
+  return HSTU_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hstu_status_t hstu_attn_fwd(const hstu_dims_t *dims, const float *rab_pos, const float *rab_time,
+                            const hstu_jagged_t *seq, const uint16_t *q, const uint16_t *k,
+                            const uint16_t *v, int64_t row_stride, const hstu_prefix_t *prefix,
+                            hstu_mask_t mask, float *out, void *ws, size_t ws_bytes,
+                            void *stream) {
+  int max_prefix = 0;
+  hstu_status_t st = check_attn_call(dims, seq, q, k, v, row_stride, prefix, mask, out, max_prefix);
+  if (st != HSTU_OK) return st;
+  if (seq->batch == 0 || seq->total_tokens == 0) return HSTU_OK;
+  const hstu_jagged_t *pre_seq = prefix != nullptr ? prefix->seq : nullptr;
+  if ((st = check_ws(ws, ws_bytes, attn_ws_bytes(seq, pre_seq))) != HSTU_OK) return st;
+  return launch_attn_call(dims, rab_pos, rab_time, seq, q, k, v, row_stride, prefix, mask, out,
+                          max_prefix, (char *)ws, (hipStream_t)stream, true);
+}
+
+size_t hstu_attn_noalloc_max_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+hstu_status_t hstu_attn_fwd_noalloc(const hstu_dims_t *dims, const float *rab_pos,
+                                    const float *rab_time, const hstu_jagged_t *seq,
+                                    const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                    int64_t row_stride, const hstu_prefix_t *prefix,
+                                    hstu_mask_t mask, float *out, void *stream) {
+  int max_prefix = 0;
+  hstu_status_t st = check_attn_call(dims, seq, q, k, v, row_stride, prefix, mask, out, max_prefix);
+  if (st != HSTU_OK) return st;
+  if (seq->batch == 0 || seq->total_tokens == 0) return HSTU_OK;
+  const hstu_jagged_t *pre_seq = prefix != nullptr ? prefix->seq : nullptr;
+  if (attn_ws_bytes(seq, pre_seq) > kNoAllocScratchBytes) return HSTU_ERR_WORKSPACE;
+  char *ws = nullptr;
+  if ((st = scratch_on_current_device(&ws)) != HSTU_OK) return st;
+  return launch_attn_call(dims, rab_pos, rab_time, seq, q, k, v, row_stride, prefix, mask, out,
+                          max_prefix, ws, (hipStream_t)stream, false);
 }
 
 size_t hstu_sl_workspace_bytes(const hstu_jagged_t *raw) {

@@ -17,7 +17,8 @@ import torch
 from . import _lib
 
 __all__ = ["HSTUError", "LayerDims", "DeviceWeights", "DeviceJagged", "hstu_layer_fwd",
-           "hstu_layer_fwd_mfalcon", "hstu_attn_fwd", "hstu_layer_workspace_bytes",
+           "hstu_layer_fwd_mfalcon", "hstu_attn_fwd", "hstu_attn_fwd_noalloc", "hstu_attn_noalloc_max_scratch_bytes",
+           "hstu_layer_workspace_bytes",
            "hstu_attn_workspace_bytes", "hstu_mfalcon_workspace_bytes", "hstu_validate_jagged",
            "hstu_sl_workspace_bytes", "hstu_stochastic_length", "hstu_stack_fwd",
            "hstu_stack_fwd_mfalcon", "hstu_stack_workspace_bytes",
@@ -319,6 +320,42 @@ def hstu_attn_fwd(dims: LayerDims, seq: DeviceJagged, q: torch.Tensor, k: torch.
                            ctypes.byref(pref) if pref is not None else None, m, _ptr(out),
                            _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _raise(st, "hstu_attn_fwd")
+    return out
+
+
+def hstu_attn_noalloc_max_scratch_bytes() -> int:
+    return int(_lib.load().hstu_attn_noalloc_max_scratch_bytes())
+
+
+def hstu_attn_fwd_noalloc(dims: LayerDims, seq: DeviceJagged, q: torch.Tensor, k: torch.Tensor,
+                          v: torch.Tensor, out: torch.Tensor, *, row_stride: Optional[int] = None,
+                          rab_pos: Optional[torch.Tensor] = None,
+                          rab_time: Optional[torch.Tensor] = None, prefix: Optional[tuple] = None,
+                          mask: str = "causal", stream=None) -> torch.Tensor:
+    """hstu_attn_fwd without a workspace (the library's static per-GPU scratch); the
+    caller passes the fp32 output [T][H*dv].  Arguments as for hstu_attn_fwd."""
+    lib = _lib.load()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.float16 or not t.is_cuda:
+            raise TypeError(f"{n}: expected an fp16 device tensor")
+    _check(out, torch.float32, "out")
+    if row_stride is None:
+        row_stride = q.stride(0)
+    d, s = dims.c(), seq.c()
+    pref = None
+    if prefix is not None:
+        pseq, kp, vp, pstride = prefix
+        for n, t in (("k_p", kp), ("v_p", vp)):
+            if t.dtype != torch.float16 or not t.is_cuda:
+                raise TypeError(f"{n}: expected an fp16 device tensor")
+        ps = pseq.c()
+        pref = _lib.Prefix(ctypes.pointer(ps), _ptr(kp), _ptr(vp), int(pstride))
+    m = {"causal": _lib.MASK_CAUSAL, "self_only": _lib.MASK_SELF_ONLY}[mask]
+    st = lib.hstu_attn_fwd_noalloc(ctypes.byref(d), _ptr(rab_pos), _ptr(rab_time), ctypes.byref(s),
+                                   _ptr(q), _ptr(k), _ptr(v), int(row_stride),
+                                   ctypes.byref(pref) if pref is not None else None, m, _ptr(out),
+                                   _stream(stream))
+    _raise(st, "hstu_attn_fwd_noalloc")
     return out
 
 

@@ -207,6 +207,25 @@ hstu_status_t hstu_attn_fwd(const hstu_dims_t *dims, const float *rab_pos,
                             hstu_mask_t mask, float *out, void *ws, size_t ws_bytes,
                             void *stream);
 
+/* For callers that cannot allocate memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): hstu_attn_fwd with the same
+ * arguments and results (the same kernels, bit for bit) but no workspace argument.
+ * Its scratch (the jagged tile schedule and the key-block timestamp ranges) lives in a
+ * static device array of hstu_attn_noalloc_max_scratch_bytes() bytes (16 MiB), one copy
+ * per GPU, held from its first use until the process ends; the call uses the copy of
+ * the current device (the stream must belong to it).  It calls no hipMalloc, hipFree
+ * or allocating routine.  A batch whose scratch, hstu_attn_workspace_bytes(dims, seq,
+ * prefix seq), exceeds that size returns HSTU_ERR_WORKSPACE before any launch (about
+ * two million tokens, batch and prefix together).  Every call on one GPU shares that
+ * GPU's array and rewrites it before reading it: calls that overlap in time on one GPU
+ * (for instance on two streams) race and must not be issued.                        */
+size_t hstu_attn_noalloc_max_scratch_bytes(void);
+hstu_status_t hstu_attn_fwd_noalloc(const hstu_dims_t *dims, const float *rab_pos,
+                                    const float *rab_time, const hstu_jagged_t *seq,
+                                    const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                    int64_t row_stride, const hstu_prefix_t *prefix,
+                                    hstu_mask_t mask, float *out, void *stream);
+
 /* Workspace (bytes) needed by hstu_stochastic_length for this raw batch (256-byte
  * aligned); 0 when the batch description is invalid.                               */
 size_t hstu_sl_workspace_bytes(const hstu_jagged_t *raw);

@@ -270,3 +270,32 @@ def test_layer_bwd_argument_checks(lib):
     assert call(_lib.LayerGrads(G, None, G + 65536, None, None, None, None, None),
                 dx=G) == _lib.HSTU_ERR_INVALID_ARG                # d_x aliases a gradient
     assert call(ok, ws_bytes=need - 1) == _lib.HSTU_ERR_WORKSPACE
+
+
+def test_noalloc_attention_rejects_before_any_device_call(lib):
+    d = _dims()
+    cap = lib.hstu_attn_noalloc_max_scratch_bytes()
+    assert cap == 16 << 20
+    # same host checks as hstu_attn_fwd
+    s = _seq()
+    assert lib.hstu_attn_fwd_noalloc(ctypes.byref(d), None, None, ctypes.byref(s), FAKE, FAKE,
+                                     FAKE, 32, None, 0, FAKE, None) == _lib.HSTU_ERR_INVALID_ARG
+    assert lib.hstu_attn_fwd_noalloc(ctypes.byref(d), None, None, ctypes.byref(s), FAKE, FAKE,
+                                     FAKE, 256, None, 7, FAKE, None) == _lib.HSTU_ERR_INVALID_ARG
+    # a batch whose scratch (8 B per token plus the work list) exceeds the static array
+    big = _seq(B=2048, T=2_200_000, L=4096)
+    need = lib.hstu_attn_workspace_bytes(ctypes.byref(d), ctypes.byref(big), None)
+    assert need > cap
+    assert lib.hstu_attn_fwd_noalloc(ctypes.byref(d), None, None, ctypes.byref(big), FAKE, FAKE,
+                                     FAKE, 256, None, 0, FAKE, None) == _lib.HSTU_ERR_WORKSPACE
+    # a prefix batch counts too
+    s2 = _seq(B=2048, T=1_000_000, L=4096)
+    pre = _seq(B=2048, T=1_200_000, L=4096)
+    pref = _lib.Prefix(ctypes.pointer(pre), FAKE, FAKE, 256)
+    assert lib.hstu_attn_fwd_noalloc(ctypes.byref(d), None, None, ctypes.byref(s2), FAKE, FAKE,
+                                     FAKE, 256, ctypes.byref(pref), 1, FAKE,
+                                     None) == _lib.HSTU_ERR_WORKSPACE
+    # an empty batch launches nothing and needs no scratch
+    e = _lib.Jagged(0, 0, 0, FAKE, None)
+    assert lib.hstu_attn_fwd_noalloc(ctypes.byref(d), None, None, ctypes.byref(e), FAKE, FAKE,
+                                     FAKE, 256, None, 0, FAKE, None) == _lib.HSTU_OK
