@@ -96,7 +96,7 @@ hstu_status_t check_dims(const hstu_dims_t *d) {
   if (!(d->ln_eps >= 0.0f) || !std::isfinite(d->ln_eps)) return HSTU_ERR_INVALID_ARG;
   if (d->dqk != d->dv) return HSTU_ERR_UNSUPPORTED;
   if (d->dqk != 32 && d->dqk != 64 && d->dqk != 128) return HSTU_ERR_UNSUPPORTED;
-  if (d->d_model % 64 != 0) return HSTU_ERR_UNSUPPORTED;
+  if (d->d_model % 64 != 0 || d->d_model > kGemmMaxK) return HSTU_ERR_UNSUPPORTED;
   const int64_t hdv = (int64_t)d->num_heads * d->dv;
   if (hdv % 64 != 0 || hdv > 2048) return HSTU_ERR_UNSUPPORTED;
   if (d->pos_buckets > 1024 || d->time_buckets > 64) return HSTU_ERR_UNSUPPORTED;

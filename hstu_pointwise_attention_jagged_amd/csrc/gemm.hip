@@ -202,10 +202,13 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm256_kernel(const uint16_t 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 3, wn = wave >> 2;  // 4 wave rows of tokens, 2 of features
 
-  const __amdgpu_buffer_rsrc_t ar =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(A), 0, (int)((int64_t)M * K * 2), kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t wr =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(W), 0, (int)((int64_t)N * K * 2), kRsrcWord3);
+  // Descriptors over this tile's own row panels (256 rows of A from m0, 256 rows of W from
+  // n0), so that every offset below stays under 256 K 2 bytes (the host keeps K <= 2^21)
+  // whatever the number of rows; rows of A past M lie outside the range and read as zero.
+  const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(A + (int64_t)m0 * K), 0, min(kBigTile, M - m0) * K * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(W + (int64_t)n0 * K), 0, kBigTile * K * 2, kRsrcWord3);
 
   // Each wave instruction fills 1 KB of LDS = 8 rows x 8 chunks; lane -> (row, chunk)
   // is fixed by the LDS position, the global chunk is the swizzled one.
@@ -217,10 +220,10 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm256_kernel(const uint16_t 
     const int r = seg * (64 / kCPR) + lrow8;
     const int c = lchunk ^ ((r >> 1) & 7);  // global chunk stored at lchunk
     if (j < SEGS) {
-      const int xoff = (int)(((int64_t)(m0 + r) * K + k0 + c * 8) * 2);
+      const int xoff = (r * K + k0 + c * 8) * 2;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, xs + stage * STAGE + seg * 1024, 16, xoff, 0, 0, 0);
     } else {
-      const int woff = (int)(((int64_t)(n0 + r) * K + k0 + c * 8) * 2);
+      const int woff = (r * K + k0 + c * 8) * 2;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, wsm + stage * STAGE + seg * 1024, 16, woff, 0, 0, 0);
     }
   };
@@ -373,6 +376,7 @@ hipError_t launch_tile(const uint16_t *A, const uint16_t *W, const float *bias, 
 hipError_t launch_gemm(const uint16_t *A, const uint16_t *W, const float *bias, uint16_t *out,
                        int M, int N, int K, Act act, OutType out_type, hipStream_t stream) {
   if (M == 0) return hipSuccess;
+  if (K > kGemmMaxK) return hipErrorInvalidValue;  // 32-bit offsets within a 256-row panel
   const bool big = (N % kBigTile) == 0 && M >= kBigTile;
   const bool wide = (N % 128) == 0;
   if (act == ACT_SILU && out_type == OUT_F16) {

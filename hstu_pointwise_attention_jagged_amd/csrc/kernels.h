@@ -10,6 +10,10 @@ enum Act { ACT_NONE = 0, ACT_SILU = 1 };
 
 enum OutType { OUT_BF16 = 0, OUT_F16 = 1 };
 
+// Largest reduction width of launch_gemm: a 256-row operand panel (256 K bf16 values)
+// stays addressable with 32-bit byte offsets.
+constexpr int kGemmMaxK = 1 << 21;
+
 // out[M][N] = act(A[M][K] . W[N][K]^T + bias[N]): bf16 inputs, fp32 accumulation, output
 // bf16 or fp16 (saturated to the finite range).  Requires K % 64 == 0, N % 64 == 0.
 hipError_t launch_gemm(const uint16_t *A, const uint16_t *W, const float *bias, uint16_t *out,

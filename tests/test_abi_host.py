@@ -68,6 +68,7 @@ def _call_layer(lib, dims, seq=None, ws_bytes=1 << 30, x=FAKE, y=FAKE + 4096, uv
     (dict(dqk=48, dv=48), _lib.HSTU_ERR_UNSUPPORTED),
     (dict(dqk=32, dv=64), _lib.HSTU_ERR_UNSUPPORTED),
     (dict(d_model=96), _lib.HSTU_ERR_UNSUPPORTED),
+    (dict(d_model=(1 << 21) + 64), _lib.HSTU_ERR_UNSUPPORTED),  # 32-bit panel offsets
     (dict(num_heads=3, dqk=32, dv=32), _lib.HSTU_ERR_UNSUPPORTED),  # H*dv = 96
     (dict(num_heads=0), _lib.HSTU_ERR_INVALID_ARG),
     (dict(rab_heads=3), _lib.HSTU_ERR_INVALID_ARG),
