@@ -54,6 +54,7 @@ constexpr int kMaxTime = 64;
 constexpr float kNegLog2e = -1.4426950408889634f;  // scores are carried as -log2(e) x
 constexpr float kNegLn2 = -0.6931471805599453f;     // undoes that scale on the output
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
+constexpr int kModeFp16Ovfl = (0 << 11) | (23 << 6) | 1;  // hwreg(HW_REG_MODE, 23, 1)
 
 enum BiasKind { BIAS_CONST = 0, BIAS_TWO = 1, BIAS_GENERAL = 2 };
 
@@ -174,6 +175,11 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
 
   const int item = blockIdx.x;
   if (item >= ld_const(p.n_work)) return;
+  // MODE.FP16_OVFL: an fp16 result that overflows clamps to +-65504 instead of becoming
+  // infinite.  The weights A are packed to fp16 in the scaled domain (A / -ln 2), so a
+  // score whose SiLU exceeds 65504 ln 2 (about 45403) contributes that value instead of
+  // turning the row infinite, at no cost per element.
+  __builtin_amdgcn_s_setreg(kModeFp16Ovfl, 1);
   const int h = blockIdx.y;
   const int b = ld_const(p.work + 2 * item), qt = ld_const(p.work + 2 * item + 1);
   const int tid = threadIdx.x, lane = tid & 63;

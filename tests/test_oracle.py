@@ -203,6 +203,36 @@ def test_mfalcon_microbatch_and_permutation_invariance():
     np.testing.assert_allclose(np.delete(y2, 1, axis=0), np.delete(y_all, 1, axis=0), rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("seed", [41, 42])
+def test_causal_with_prefix_equals_causal_on_concatenation(seed):
+    """Causal attention over (prefix keys, own keys): query i of a sequence sits at position
+    n_p + i and sees every prefix key and its own keys j <= i.  That is the plain causal
+    attention of the concatenated sequence (prefix rows, then own rows), read at the own
+    rows; the concatenated run is the already pinned causal path."""
+    rng = np.random.default_rng(seed)
+    H, dh = 2, 4
+    n_p, n_o = [0, 7, 3, 12], [5, 1, 9, 0]
+    pre = wl.jagged_from_lengths(rng, n_p)
+    own = wl.jagged_from_lengths(rng, n_o)
+    kp, vp = (rng.standard_normal((pre.total, H * dh)) for _ in range(2))
+    q, k, v = (rng.standard_normal((own.total, H * dh)) for _ in range(3))
+    P = rng.standard_normal((1, 5))
+    Tt = rng.standard_normal((1, 6))
+    got = ref.attention(q, k, v, own.offsets, own.timestamps, H, dh, dh, P, Tt,
+                        prefix=(kp, vp, pre.offsets, pre.timestamps), mask=ref.CAUSAL)
+    for b in range(own.batch):
+        p0, p1 = pre.offsets[b], pre.offsets[b + 1]
+        s0, s1 = own.offsets[b], own.offsets[b + 1]
+        if s1 == s0:
+            continue
+        cq = np.concatenate([np.zeros((p1 - p0, H * dh)), q[s0:s1]])
+        ck = np.concatenate([kp[p0:p1], k[s0:s1]])
+        cv = np.concatenate([vp[p0:p1], v[s0:s1]])
+        cts = np.concatenate([pre.timestamps[p0:p1], own.timestamps[s0:s1]])
+        whole = ref.attention(cq, ck, cv, np.array([0, len(ck)]), cts, H, dh, dh, P, Tt)
+        np.testing.assert_allclose(got[s0:s1], whole[p1 - p0:], rtol=0, atol=1e-12)
+
+
 # ----------------------------------------------------------------------------------
 # rab indices: golden buckets and decodable probes
 # ----------------------------------------------------------------------------------
