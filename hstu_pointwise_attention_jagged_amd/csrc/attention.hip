@@ -23,8 +23,12 @@
 //    fp32.  Scores are carried scaled by -log2(e) so SiLU costs exp2, add, reciprocal
 //    and multiply per element.
 //  * The key loop is a pipeline over 32-key blocks: each step computes the scores of
-//    block b+1, the weights of block b and the P.V product of block b-1 as one
-//    straight-line basic block, so the SiLU arithmetic overlaps the MFMAs.
+//    block b+1, the weights of block b and the P.V product of block b-1, which are
+//    independent.  Inside a step they are software-pipelined by hand: score MFMA i and
+//    P.V MFMA i alternate, each with a share of the SiLU arithmetic beside it, and the
+//    K / V fragments are read two MFMAs ahead; scheduling groups pin that issue order.
+//  * Whether a batch has prefix (history) keys is a template parameter, so the plain
+//    causal path carries no segment selection.
 //  * The rab index math is integer only: relative position clamp, and the log2 time
 //    bucket from the bit length of (1 + gap).  Each wave classifies every 32-key block
 //    with scalar arithmetic, from its queries' position / timestamp range and the key
@@ -117,7 +121,8 @@ struct BlockInfo {
                   // bit 1 masked: the mask applies per element; bit 2 prefix (history) rows;
                   // bits 3-4 BiasKind; bits 5-10 the lower time bucket of the block
   int g;          // block index in the wave's key sequence (prefix blocks first)
-  float lo, hi;   // bias values (CONST: lo; TWO: lo / hi)
+  int l;          // lane of the block table that describes the block
+  uint32_t c;     // CONST: the bias as the fp16 word of the bias MFMA operand
   __device__ bool live() const { return bits & 1u; }
   __device__ bool masked() const { return bits & 2u; }
   __device__ bool pre() const { return bits & 4u; }
@@ -126,7 +131,7 @@ struct BlockInfo {
   __device__ uint32_t thr() const { return (uint32_t)(((uint64_t)1 << (((bits >> 5) & 63u) + 1)) - 1); }
 };
 
-template <int DH, int MASK, int NW>
+template <int DH, int MASK, int NW, bool PRE>
 __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
   using L = TileLayout<DH>;
   constexpr int NT = 64 * NW;          // threads per workgroup
@@ -189,12 +194,12 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
   const int s0 = ld_const(p.offsets + b);
   const int n = ld_const(p.offsets + b + 1) - s0;
   const int q0 = qt * BM;
-  const bool has_prefix = p.p_offsets != nullptr;
+  constexpr bool has_prefix = PRE;
   const int p0 = has_prefix ? ld_const(p.p_offsets + b) : 0;
   const int n_p = has_prefix ? ld_const(p.p_offsets + b + 1) - p0 : 0;
   const bool use_pos = p.rab_pos != nullptr;
   const bool use_time = p.rab_time != nullptr && p.ts != nullptr &&
-                        (p.p_offsets == nullptr || p.p_ts != nullptr);
+                        (!PRE || p.p_ts != nullptr);
   const int rrow = p.rab_per_head ? h : 0;
 
   // Scores are carried scaled by -log2(e): t = -log2(e) (q.k + bias), so that
@@ -241,8 +246,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
       float x[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = kNegLog2e * (float)raw[e];
-      const u32x4 sc = {pack_f16_sat(x[0], x[1]), pack_f16_sat(x[2], x[3]),
-                        pack_f16_sat(x[4], x[5]), pack_f16_sat(x[6], x[7])};
+      const u32x4 sc = {pack_f16(x[0], x[1]), pack_f16(x[2], x[3]),
+                        pack_f16(x[4], x[5]), pack_f16(x[6], x[7])};
       qf[ks] = as_f16x8(sc);
     }
   }
@@ -285,7 +290,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
   const int ts_off = lane * 4;
 
   auto seg_of = [&](int t, int &kbase, int &limit) __attribute__((always_inline)) {
-    const bool pre = t < n_pt;
+    const bool pre = PRE && t < n_pt;
     kbase = pre ? t * kBN : own_start + (t - n_pt) * kBN;
     limit = n + (pre ? n_p - n : 0);  // arithmetic, not a select between the captured variables
     return pre;
@@ -363,13 +368,13 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
   //   - bias kind: CONST when every relative position is past the last position bucket and
   //     the smallest and largest gap share one time bucket (the bucket being monotone in
   //     the gap); TWO when the gaps span exactly buckets b and b + 1; GENERAL otherwise.
-  int tab_bits = 0, tab_lo = 0, tab_hi = 0;
+  int tab_bits = 0, tab_lo = 0, tab_hi = 0, tab_c = 0;
   int cbase = 0;
   auto build_table = [&](int c0) __attribute__((always_inline)) {
     const int g = c0 + lane;
     const int t = g >> 1;
     const bool valid = t < n_tiles;
-    const bool pre = t < n_pt;
+    const bool pre = PRE && t < n_pt;
     const int kbase = pre ? t * kBN : own_start + (t - n_pt) * kBN;
     const int limit = n + (pre ? n_p - n : 0);
     const int k0 = kbase + (g & 1) * 32;
@@ -395,26 +400,29 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
     tab_bits = (lv ? 1 : 0) | (mk ? 2 : 0) | (pre ? 4 : 0) | (kind << 3) | (tb_lo << 5);
     tab_lo = __builtin_bit_cast(int, __shfl(tsum, tb_lo, 64));
     tab_hi = __builtin_bit_cast(int, __shfl(tsum, tb_hi, 64));
+    tab_c = (int)pack_f16(__builtin_bit_cast(float, tab_lo), 0.0f);  // CONST bias as the MFMA word
     cbase = c0;
   };
   auto fetch = [&](int g) __attribute__((always_inline)) {
     const int l = g - cbase;
     BlockInfo bi;
     bi.bits = (uint32_t)__builtin_amdgcn_readlane(tab_bits, l);
-    bi.lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(tab_lo, l));
-    bi.hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(tab_hi, l));
+    bi.c = (uint32_t)__builtin_amdgcn_readlane(tab_c, l);
+    bi.l = l;
     bi.g = g;
     return bi;
   };
   // first key index of a block within its segment
   const int own_k0_shift = own_start - n_pt * kBN;
   auto k0_of = [&](const BlockInfo &bi) __attribute__((always_inline)) {
-    return bi.g * 32 + (bi.pre() ? 0 : own_k0_shift);
+    return bi.g * 32 + ((PRE && bi.pre()) ? 0 : own_k0_shift);
   };
 
   f32x16 acc_o[FT];
 #pragma unroll
   for (int f = 0; f < FT; ++f) acc_o[f] = f32x16{};
+  // B operand of the constant-bias MFMA: the bias word (k = 0) and three zero words
+  u32x4 bq = {0u, 0u, 0u, 0u};
 
   // ---- the three parts of a step ----
   // Score accumulator init with the block's bias (CONST / TWO / GENERAL), from the key
@@ -423,11 +431,12 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
     constexpr int KIND = decltype(kind_c)::value;
     const int32_t *kts = tsb + blk * 32 + 4 * half;
     if constexpr (KIND == BIAS_CONST) {
-      const u32x4 qb = {pack_f16_sat(bi.lo, 0.0f), 0u, 0u, 0u};
-      s = mfma32_f16(kf_one, as_f16x8(qb), f32x16{});
+      bq.x = bi.c;
+      s = mfma32_f16(kf_one, as_f16x8(bq), f32x16{});
     } else if constexpr (KIND == BIAS_TWO) {
       const int32_t klim = key_limit(qts, bi.thr());
-      const float hi = bi.hi, lo = bi.lo;
+      const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(tab_hi, bi.l));
+      const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(tab_lo, bi.l));
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int4 t4 = *reinterpret_cast<const int4 *>(kts + 8 * g);
@@ -447,7 +456,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
           float x = 0.0f;
           if (use_pos) {
             const int kidx = k0_of(bi) + 8 * g + 4 * half + r;
-            const int kpos = bi.pre() ? kidx : (MASK == 0 ? n_p + kidx : n_p);
+            const int kpos = (PRE && bi.pre()) ? kidx : (MASK == 0 ? n_p + kidx : n_p);
             x += ptab[min(max(qpos - kpos, 0), p.pos_buckets - 1)];
           }
           if (use_time) x += ttab[min(time_log2_bucket(qts, kt4[r]), p.time_buckets - 1)];
@@ -456,39 +465,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
       }
     }
   };
-  // S^T += K Q^T over the block's 32 keys (K stage ks_buf).  Lane: row lrow of the block,
-  // logical chunk 2 ks + half at its swizzled position; the swizzle of row blk 32 + lrow
-  // is that of lrow, and it only flips bits below the row pitch, so the address of k-step
-  // ks is k_base ^ (32 ks).  Fragments are read in groups of four ahead of their MFMAs.
+  // K fragment of score k-step ks: row lrow of the block, logical chunk 2 ks + half at its
+  // swizzled position; the swizzle of row blk 32 + lrow is that of lrow, and it only flips
+  // bits below the row pitch, so the address of k-step ks is k_base ^ (32 ks).
   const int k_base = lrow * L::ROW + ((half ^ L::kswz(lrow)) * 16);
-  auto s_mma = [&](f32x16 &s, const unsigned char *ks_buf, int blk) __attribute__((always_inline)) {
-    const unsigned char *kb = ks_buf + blk * 32 * L::ROW;
-    constexpr int G = KS < 4 ? KS : 4;
-#pragma unroll
-    for (int g0 = 0; g0 < KS; g0 += G) {
-      f16x8 kf[G];
-#pragma unroll
-      for (int i = 0; i < G; ++i)
-        kf[i] = as_f16x8(*reinterpret_cast<const u32x4 *>(kb + (k_base ^ ((g0 + i) * 32))));
-#pragma unroll
-      for (int i = 0; i < G; ++i) s = mfma32_f16(kf[i], qf[g0 + i], s);
-    }
-  };
-  // A / (-ln 2) = t / (1 + 2^t) of the scaled scores t (masked), packed into the P^T
-  // operand: k-step s2 takes s[8 s2 .. 8 s2 + 7]
-  auto silu_half = [&](const f32x16 &s, f16x8 &pf, int s2, const BlockInfo &bi, auto masked_c) __attribute__((always_inline)) {
-    (void)bi;
-    (void)masked_c;
-    float a[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float t = s[8 * s2 + e];
-      a[e] = t * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
-    }
-    const u32x4 pk = {pack_f16(a[0], a[1]), pack_f16(a[2], a[3]), pack_f16(a[4], a[5]),
-                      pack_f16(a[6], a[7])};
-    pf = as_f16x8(pk);
-  };
   // O^T += V^T P^T over the block's 32 keys (V stage vs_buf).  The V^T operand comes from
   // row-major V through transposing reads: in each 16-lane group, lane 4 j + q names row
   // (key) kb + j at features 4 q .. 4 q + 3 of its 16-feature slice, and lane i receives
@@ -504,19 +484,65 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
     v_base = vr * L::ROW + (((((lane >> 4) & 1) * 2 + ((lane & 3) >> 1)) ^ L::vswz(vr)) * 16) +
              (lane & 1) * 8;
   }
-  auto pv = [&](const f16x8 (&pf)[2], const unsigned char *vs_buf, int blk) __attribute__((always_inline)) {
-    const unsigned char *vb = vs_buf + blk * 32 * L::ROW;
+  // The step's three independent parts as one software pipeline of KS iterations:
+  // iteration i issues score MFMA i (S^T += K Q^T, k-step i), P.V MFMA i (k-step i / FT,
+  // feature tile i % FT) and the SiLU of 16 / KS score elements of the cur block, with
+  // the K and V fragments read two iterations ahead.  The scheduling groups below keep
+  // that order, so that consecutive MFMAs are independent, each has VALU work beside it,
+  // and no MFMA waits on a fragment read.
+  auto fused = [&](f32x16 &s, const unsigned char *ks_buf, int nblk, const f32x16 &sc,
+                   f16x8 (&pc)[2], const f16x8 (&pp)[2], const unsigned char *vs_buf,
+                   int pblk) __attribute__((always_inline)) {
+    const unsigned char *kb = ks_buf + nblk * 32 * L::ROW;
+    const unsigned char *vb = vs_buf + pblk * 32 * L::ROW;
+    constexpr int EPI = 16 / KS;  // SiLU elements per iteration
+    f16x8 kf[KS], vf[KS];
+    auto rk = [&](int i) __attribute__((always_inline)) {
+      kf[i] = as_f16x8(*reinterpret_cast<const u32x4 *>(kb + (k_base ^ (i * 32))));
+    };
+    auto rv = [&](int i) __attribute__((always_inline)) {
+      const int s2 = i / FT, f = i % FT;
+      const u32x2 lo = lds_read_tr16(vb + (16 * s2) * L::ROW + (v_base ^ (64 * f)));
+      const u32x2 hi = lds_read_tr16(vb + (16 * s2 + 8) * L::ROW + (v_base ^ (64 * f)));
+      vf[i] = as_f16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+    };
+    float a[16];
+    rk(0);
+    rv(0);
+    if constexpr (KS > 1) {
+      rk(1);
+      rv(1);
+    }
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      u32x4 w[FT];
-#pragma unroll
-      for (int f = 0; f < FT; ++f) {
-        const u32x2 lo = lds_read_tr16(vb + (16 * s2) * L::ROW + (v_base ^ (64 * f)));
-        const u32x2 hi = lds_read_tr16(vb + (16 * s2 + 8) * L::ROW + (v_base ^ (64 * f)));
-        w[f] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    for (int i = 0; i < KS; ++i) {
+      if (i + 2 < KS) {
+        rk(i + 2);
+        rv(i + 2);
       }
+      s = mfma32_f16(kf[i], qf[i], s);
 #pragma unroll
-      for (int f = 0; f < FT; ++f) acc_o[f] = mfma32_f16(as_f16x8(w[f]), pf[s2], acc_o[f]);
+      for (int e = EPI * i; e < EPI * (i + 1); ++e) {
+        const float t = sc[e];
+        a[e] = t * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
+      }
+      acc_o[i % FT] = mfma32_f16(vf[i], pp[i / FT], acc_o[i % FT]);
+    }
+    pc[0] = as_f16x8(u32x4{pack_f16(a[0], a[1]), pack_f16(a[2], a[3]), pack_f16(a[4], a[5]),
+                           pack_f16(a[6], a[7])});
+    pc[1] = as_f16x8(u32x4{pack_f16(a[8], a[9]), pack_f16(a[10], a[11]), pack_f16(a[12], a[13]),
+                           pack_f16(a[14], a[15])});
+    // issue order: 6 fragment reads, then per iteration score MFMA, 3 reads, half of the
+    // SiLU work, P.V MFMA, the other half
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // score MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);          // fragment reads
+      __builtin_amdgcn_sched_group_barrier(0x400, EPI, 0);        // exp
+      __builtin_amdgcn_sched_group_barrier(0x002, EPI, 0);        // add
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // P.V MFMA
+      __builtin_amdgcn_sched_group_barrier(0x400, EPI, 0);        // rcp
+      __builtin_amdgcn_sched_group_barrier(0x002, EPI + EPI / 2, 0);  // mul, pack
     }
   };
 
@@ -559,10 +585,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
       s_init(s_next, bn, tst, nblk, KGen{});
     else
       s_init(s_next, bn, tst, nblk, KConst{});
-    s_mma(s_next, kst, nblk);
-    silu_half(s_cur, p_cur[0], 0, bc, std::false_type{});
-    pv(p_prev, vst, pblk);
-    silu_half(s_cur, p_cur[1], 1, bc, std::false_type{});
+    fused(s_next, kst, nblk, s_cur, p_cur, p_prev, vst, pblk);
   };
 
   // Tile t's blocks are 2t (blk 0) and 2t + 1 (blk 1).  Iteration t runs steps 2t + 1 and
@@ -637,16 +660,18 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
   }
 }
 
-template <int DH, int MASK, int NW>
+template <int DH, int MASK, int NW, bool PRE>
 hipError_t launch_one(const AttnArgs &a, int64_t cap, hipStream_t stream) {
   const dim3 grid((unsigned)cap, (unsigned)a.num_heads);
-  attn_kernel<DH, MASK, NW><<<grid, dim3(64 * NW), 0, stream>>>(a);
+  attn_kernel<DH, MASK, NW, PRE><<<grid, dim3(64 * NW), 0, stream>>>(a);
   return hipGetLastError();
 }
 
 template <int DH, int NW>
 hipError_t launch_dh(const AttnArgs &a, int64_t cap, hipStream_t stream) {
-  return a.mask == 0 ? launch_one<DH, 0, NW>(a, cap, stream) : launch_one<DH, 1, NW>(a, cap, stream);
+  if (a.mask != 0) return launch_one<DH, 1, NW, true>(a, cap, stream);
+  return a.p_offsets != nullptr ? launch_one<DH, 0, NW, true>(a, cap, stream)
+                                : launch_one<DH, 0, NW, false>(a, cap, stream);
 }
 
 }  // namespace
