@@ -165,6 +165,17 @@ constexpr int kOutPitch = kBigTile * 2 + 16;  // bytes per output row staged in 
 // consecutive rows hit distinct banks.
 __device__ __forceinline__ int swz(int r, int c) { return (r * kCPR + (c ^ ((r >> 1) & 7))) * 16; }
 
+// Raw buffer descriptor over `bytes` bytes at `base`, both uniform over the workgroup:
+// built from scalar copies, so that the descriptor is scalar (a descriptor the compiler
+// cannot prove uniform makes it loop over lanes for every load).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void *base, int bytes) {
+  const uint64_t b = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  void *p = (void *)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, 0, __builtin_amdgcn_readfirstlane(bytes), kRsrcWord3);
+}
+
 // s_waitcnt vmcnt(n) (n <= 15), not waiting on the other counters.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -205,10 +216,8 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm256_kernel(const uint16_t 
   // Descriptors over this tile's own row panels (256 rows of A from m0, 256 rows of W from
   // n0), so that every offset below stays under 256 K 2 bytes (the host keeps K <= 2^21)
   // whatever the number of rows; rows of A past M lie outside the range and read as zero.
-  const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t *>(A + (int64_t)m0 * K), 0, min(kBigTile, M - m0) * K * 2, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t *>(W + (int64_t)n0 * K), 0, kBigTile * K * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t ar = uniform_rsrc(A + (int64_t)m0 * K, min(kBigTile, M - m0) * K * 2);
+  const __amdgpu_buffer_rsrc_t wr = uniform_rsrc(W + (int64_t)n0 * K, kBigTile * K * 2);
 
   // Each wave instruction fills 1 KB of LDS = 8 rows x 8 chunks; lane -> (row, chunk)
   // is fixed by the LDS position, the global chunk is the swizzled one.
