@@ -288,7 +288,12 @@ __global__ __launch_bounds__(256) void bwd_absmax_kernel(const float *d_out, int
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
     const f32x4 v = reinterpret_cast<const f32x4 *>(d_out)[i];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) m = max(m, __builtin_bit_cast(uint32_t, v[j]) & 0x7fffffffu);
+    for (int j = 0; j < 4; ++j) {
+      // copy to a scalar first: a bit cast taken straight from a vector element is
+      // miscompiled by this compiler (only element 0 survives)
+      const float x = v[j];
+      m = max(m, __builtin_bit_cast(uint32_t, x) & 0x7fffffffu);
+    }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));

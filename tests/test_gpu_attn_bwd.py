@@ -116,6 +116,30 @@ def test_attention_gradients_match_oracle(seed, lengths, H, dh, per_head, g_scal
         assert err.max() <= MAX_REL and err.mean() <= MEAN_REL, name
 
 
+def test_upstream_gradient_maximum_off_every_fourth_column():
+    """The scale of the fp16 copy of dO comes from max |dO| over every element.  An upstream
+    gradient that is zero except large entries in columns 1, 2 and 3 (mod 4) must be scaled
+    by its true maximum: otherwise the entries overflow fp16 and the gradients turn
+    non-finite."""
+    H, dh = 2, 64
+    seq, q, k, v, P, Tt, _ = _case(21, [40, 130, 7], H, dh, False)
+    g = np.zeros((seq.total, H * dh), np.float32)
+    rng = np.random.default_rng(22)
+    rows = rng.integers(0, seq.total, 12)
+    cols = 4 * rng.integers(0, H * dh // 4, 12) + 1 + np.arange(12) % 3
+    g[rows, cols] = 1e6 * (1.0 + rng.random(12)).astype(np.float32)
+    say("[bwd] dO with its maximum off the columns 0 mod 4")
+    got = _gpu_bwd(seq, q, k, v, P, Tt, g, H, dh)
+    torch.cuda.synchronize()
+    want = bwd.attention_bwd(q, k, v, g, seq.offsets, seq.timestamps, H, dh, dh, P, Tt)
+    for name, gt, wt in zip(("dq", "dk", "dv"), got, want):
+        gn = gt.cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(gn)), name
+        err = np.abs(gn - wt) / float(np.std(wt))
+        say(f"      {name}: max_rel={err.max():.3e} mean_rel={err.mean():.3e}")
+        assert err.max() <= MAX_REL and err.mean() <= MEAN_REL, name
+
+
 def test_zero_upstream_gradient_gives_zero():
     seq, q, k, v, P, Tt, g = _case(6, [70, 130], 2, 64, False)
     g[:] = 0.0
