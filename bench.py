@@ -3,7 +3,7 @@
 A step is one forward pass of a 24-layer HSTU stack (independent random weights per
 layer, Y of layer l is X of layer l+1) over the 8 x 8192-token batch, d = 1024, 8 heads
 of 128, causal mask with positional + log-time relative bias: every kernel of the hot
-path (jagged schedule, f1 + SiLU, pointwise attention, LayerNorm + gate, f2) runs once
+path (jagged schedule, f1 + SiLU, pointwise attention, f2 with LayerNorm + gate) runs once
 per layer.  Inputs and weights are resident in HBM before the timed region.
 
 Prints one JSON line on stdout; progress goes to stderr.
@@ -433,7 +433,7 @@ def main():
 
     def step():
         # the whole stack in one call: the batch's schedule is built once, then every
-        # layer runs f1, attention, norm-gate and f2
+        # layer runs f1, attention and f2 (LayerNorm and the gate formed in its staging)
         y, _ = ops.hstu_stack_fwd(dims, layer_w, seq, x0, y=bufs[0], uvqk=uvqk, workspace=ws,
                                   stream=stream)
         return y
@@ -480,7 +480,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 I/O and f1/f2 operands, fp16 attention operands, fp32 accumulate",
+        "dtype": "bf16 I/O and f1 operands, fp16 attention and f2 operands, fp32 accumulate",
         "data": "synthetic",
         "config": {"workload": f"uniform 8x8192 jagged batch, d=1024, 8 heads x 128, causal, "
                                f"rab pos+time, {args.layers}-layer stack",

@@ -18,7 +18,7 @@ c_int32, c_int64, c_float, c_double, c_void_p, c_size_t = (
 
 HSTU_OK, HSTU_ERR_INVALID_ARG, HSTU_ERR_UNSUPPORTED, HSTU_ERR_WORKSPACE, HSTU_ERR_HIP = range(5)
 MASK_CAUSAL, MASK_SELF_ONLY = 0, 1
-KERNEL_IDS = {"schedule": 0, "f1_gemm_silu": 1, "attention": 2, "norm_gate": 3, "f2_gemm": 4}
+KERNEL_IDS = {"schedule": 0, "f1_gemm_silu": 1, "attention": 2, "f2_prep": 3, "f2_gemm": 4}
 
 
 class Dims(ctypes.Structure):

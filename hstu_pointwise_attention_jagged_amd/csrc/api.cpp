@@ -24,7 +24,7 @@ inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // ---------------------------------------------------------------- profiling ---------
 constexpr int kNumKernels = 5;
-const char *kKernelNames[kNumKernels] = {"schedule", "f1_gemm_silu", "attention", "norm_gate",
+const char *kKernelNames[kNumKernels] = {"schedule", "f1_gemm_silu", "attention", "f2_prep",
                                          "f2_gemm"};
 
 struct ProfRecord {
@@ -128,9 +128,13 @@ size_t attn_ws_bytes(const hstu_jagged_t *s, const hstu_jagged_t *pre) {
   return bytes;
 }
 
+// Layer scratch: the attention's standardised per-head output (fp16 [T][H dv]) and its
+// per-(row, head) statistics (float2 [T][H]), w2 as fp16 and gamma | beta as fp16 for f2,
+// then the attention scratch.
 size_t layer_ws_bytes(const hstu_dims_t *d, const hstu_jagged_t *s, const hstu_jagged_t *pre) {
   const size_t T = (size_t)s->total_tokens, hdv = (size_t)d->num_heads * d->dv;
-  return align_up(T * hdv * sizeof(float)) + align_up(T * hdv * sizeof(uint16_t)) +
+  return align_up(T * hdv * sizeof(uint16_t)) + align_up(T * d->num_heads * 8) +
+         align_up((size_t)d->d_model * hdv * sizeof(uint16_t)) + align_up(2 * hdv * sizeof(uint16_t)) +
          attn_ws_bytes(s, pre);
 }
 
@@ -140,8 +144,11 @@ size_t stack_ws_bytes(const hstu_dims_t *d, const hstu_jagged_t *s, const hstu_j
 }
 
 struct LayerWs {
-  float *o;
-  uint16_t *g;
+  float *o;         // raw attention output (attention alone, layer backward)
+  uint16_t *cn;     // or: standardised per-head output and its statistics (layer forward)
+  float2 *stats;
+  uint16_t *w2h;    // w2 as fp16
+  uint16_t *gb;     // gamma | beta as fp16
   int32_t *work;
   int32_t *n_work;
   int2 *kstat;
@@ -163,11 +170,15 @@ LayerWs carve_layer(void *ws, const hstu_dims_t *d, const hstu_jagged_t *s,
                     const hstu_jagged_t *pre) {
   const size_t T = (size_t)s->total_tokens, hdv = (size_t)d->num_heads * d->dv;
   char *p = (char *)ws;
-  LayerWs w;
-  w.o = (float *)p;
-  p += align_up(T * hdv * sizeof(float));
-  w.g = (uint16_t *)p;
+  LayerWs w{};
+  w.cn = (uint16_t *)p;
   p += align_up(T * hdv * sizeof(uint16_t));
+  w.stats = (float2 *)p;
+  p += align_up(T * d->num_heads * 8);
+  w.w2h = (uint16_t *)p;
+  p += align_up((size_t)d->d_model * hdv * sizeof(uint16_t));
+  w.gb = (uint16_t *)p;
+  p += align_up(2 * hdv * sizeof(uint16_t));
   carve_attn(p, s, pre, w);
   return w;
 }
@@ -207,6 +218,8 @@ AttnArgs attn_args(const hstu_dims_t *d, const float *rab_pos, const float *rab_
   a.rab_per_head = d->rab_heads == d->num_heads && d->num_heads > 1;
   a.out = out;
   a.out_stride = (int64_t)d->num_heads * d->dv;
+  a.cn = w.cn;
+  a.stats = w.stats;
   a.work = w.work;
   a.n_work = w.n_work;
   a.kstat = w.kstat;
@@ -245,16 +258,33 @@ hstu_status_t run_layer(const hstu_dims_t *d, const hstu_weights_t *w, const hst
     const hstu_status_t r = run_setup(s, aa, lw, pre, false, st);
     if (r != HSTU_OK) return r;
   }
+  const bool affine = w->ln_gamma != nullptr || w->ln_beta != nullptr;
   e = timed(1, st, [&] { return launch_gemm(x, w->w1, w->b1, uvqk, T, n1, d->d_model, ACT_SILU, OUT_F16, st); });
+  if (e != hipSuccess) return hip_fail(e);
+  e = timed(3, st, [&] {
+    return launch_gate_prep(w->w2, (int64_t)d->d_model * hdv, w->ln_gamma, w->ln_beta, hdv, lw.w2h,
+                            affine ? lw.gb : nullptr, st);
+  });
   if (e != hipSuccess) return hip_fail(e);
   const int64_t cap = attn_work_capacity(s->batch, T);
   e = timed(2, st, [&] { return launch_attention(aa, d->dqk, s->max_seq_len, cap, st); });
   if (e != hipSuccess) return hip_fail(e);
-  e = timed(3, st, [&] {
-    return launch_norm_gate(lw.o, uvqk, n1, w->ln_gamma, w->ln_beta, d->ln_eps, lw.g, T, hdv, st);
-  });
-  if (e != hipSuccess) return hip_fail(e);
-  e = timed(4, st, [&] { return launch_gemm(lw.g, w->w2, w->b2, y, T, d->d_model, hdv, ACT_NONE, OUT_BF16, st); });
+  GateGemmArgs ga{};
+  ga.w = lw.w2h;
+  ga.c = lw.cn;
+  ga.u = uvqk;  // U is the first H dv columns of each row
+  ga.u_stride = n1;
+  ga.stats = lw.stats;
+  ga.gb = affine ? reinterpret_cast<const _Float16 *>(lw.gb) : nullptr;
+  ga.bias = w->b2;
+  ga.out = y;
+  ga.M = T;
+  ga.N = d->d_model;
+  ga.K = hdv;
+  ga.H = d->num_heads;
+  ga.dv = d->dv;
+  ga.eps = d->ln_eps;
+  e = timed(4, st, [&] { return launch_gate_gemm(ga, affine, st); });
   if (e != hipSuccess) return hip_fail(e);
   return HSTU_OK;
 }

@@ -646,17 +646,57 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
   }
   __builtin_amdgcn_s_waitcnt(7 << 4);  // drain the dummy batches before the stores
 
-  // epilogue: lane holds query lrow, features 32f + 8g + 4*half + 0..3 -> fp32 rows
-  if (q_ok) {
-    float *orow = p.out + (int64_t)(s0 + qi) * p.out_stride + h * DH + half * 4;
+  // epilogue: lane holds query lrow, features 32f + 8g + 4*half + 0..3 (the other half of
+  // the head's features sits in lane ^ 32)
+#pragma unroll
+  for (int f = 0; f < FT; ++f) acc_o[f] *= kNegLn2;
+  if (p.cn == nullptr) {  // the raw aggregation, fp32 rows
+    if (q_ok) {
+      float *orow = p.out + (int64_t)(s0 + qi) * p.out_stride + h * DH + half * 4;
+#pragma unroll
+      for (int f = 0; f < FT; ++f)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 v = {acc_o[f][4 * g], acc_o[f][4 * g + 1], acc_o[f][4 * g + 2], acc_o[f][4 * g + 3]};
+          *reinterpret_cast<f32x4 *>(orow + f * 32 + g * 8) = v;
+        }
+    }
+  } else {
+    // Inside the layer the aggregation only feeds the LayerNorm of equation 3, taken over
+    // all H dv features of a row.  This head's part is summarised by its mean and biased
+    // variance (two passes over registers) and stored standardised with them, as fp16
+    // (|value| <= sqrt(DH)); f2 combines the heads' statistics exactly and rebuilds the
+    // normalised row from these parts.
+    float sum = 0.f;
 #pragma unroll
     for (int f = 0; f < FT; ++f)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 v = {kNegLn2 * acc_o[f][4 * g], kNegLn2 * acc_o[f][4 * g + 1],
-                   kNegLn2 * acc_o[f][4 * g + 2], kNegLn2 * acc_o[f][4 * g + 3]};
-        *reinterpret_cast<f32x4 *>(orow + f * 32 + g * 8) = v;
+      for (int i = 0; i < 16; ++i) sum += acc_o[f][i];
+    sum += __shfl_xor(sum, 32, 64);
+    const float mean = sum * (1.0f / DH);
+    float m2 = 0.f;
+#pragma unroll
+    for (int f = 0; f < FT; ++f)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float d = acc_o[f][i] - mean;
+        m2 += d * d;
       }
+    m2 += __shfl_xor(m2, 32, 64);
+    const float var = m2 * (1.0f / DH);
+    const float inv = var > 0.f ? __builtin_amdgcn_rsqf(var) : 0.f;
+    if (q_ok) {
+      uint16_t *crow = p.cn + (int64_t)(s0 + qi) * p.out_stride + h * DH + half * 4;
+#pragma unroll
+      for (int f = 0; f < FT; ++f)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const u32x2 v = {pack_f16((acc_o[f][4 * g] - mean) * inv, (acc_o[f][4 * g + 1] - mean) * inv),
+                           pack_f16((acc_o[f][4 * g + 2] - mean) * inv, (acc_o[f][4 * g + 3] - mean) * inv)};
+          *reinterpret_cast<u32x2 *>(crow + f * 32 + g * 8) = v;
+        }
+      if (half == 0) p.stats[(int64_t)(s0 + qi) * p.num_heads + h] = float2{mean, var};
+    }
   }
 }
 

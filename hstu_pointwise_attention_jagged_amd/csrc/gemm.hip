@@ -380,7 +380,289 @@ hipError_t launch_tile(const uint16_t *A, const uint16_t *W, const float *bias, 
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------
+// f2 with LayerNorm and the U gate formed in its operand staging (equation 3:
+// Y = f2(LayerNorm(A(X)V) (.) U)).  The attention leaves each head's part of a row
+// standardised (c, fp16) with its mean and biased variance; the LayerNorm over the whole
+// row is rebuilt exactly from those:  mu = mean of the head means, var = mean of
+// (head variance + (head mean - mu)^2), rstd = 1 / sqrt(var + eps), and for a feature of
+// head h:  (o - mu) rstd = c a_h + b_h  with  a_h = sqrt(var_h) rstd, b_h = (mu_h - mu) rstd.
+// G = ((c a_h + b_h) gamma + beta) U is formed in packed fp16 by the thread that stages it
+// and written to LDS in the layout of the direct-to-LDS tiles; W2 (converted to fp16 once
+// per call) arrives by direct-to-LDS loads.  Tiles, waves and epilogue as gemm256_kernel;
+// the MFMA is v_mfma_f32_32x32x16_f16.
+// ---------------------------------------------------------------------------------
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+constexpr int kGateTableBytes = 2048 * 4;  // gamma | beta as fp16 pairs, K <= 2048
+
+template <bool AFF>
+__global__ __launch_bounds__(kBigThreads, 1) void gate_gemm_kernel(GateGemmArgs g) {
+  constexpr int TM = 64, TN = 128;  // wave tile: tokens x features
+  constexpr int MT = TM / 32, NT = TN / 32;
+  constexpr int STAGE = kBigTile * kBigBK * 2;             // bytes of one operand stage
+  constexpr int SEGS = STAGE / 1024 / (kBigThreads / 64);  // 1 KB W segments per wave
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  unsigned char *xs = smem;                        // G stages
+  unsigned char *wsm = smem + kBigStages * STAGE;  // W stages
+  // tables in arrays of their own, so that the compiler can tell them apart from the
+  // direct-to-LDS writes in flight to the stages (and puts no load wait before reading them)
+  __shared__ h2 gbt[kGateTableBytes / 4];          // gamma | beta, fp16
+  __shared__ float2 rst[kBigTile];                 // (mean, 1 / std) of the tile's rows
+  // an fp16 result that overflows clamps to +-65504 (G saturates instead of turning inf)
+  __builtin_amdgcn_s_setreg((0 << 11) | (23 << 6) | 1, 1);
+
+  const int M = g.M, N = g.N, K = g.K;
+  const int nwg = gridDim.x;
+  const int per_xcd = (nwg + 7) / 8;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int lin = xcd * per_xcd + slot;
+  if (slot >= per_xcd || lin >= g.n_tiles_total) return;
+  const int tile_n = lin % g.n_tiles_n;
+  const int tile_m = lin / g.n_tiles_n;
+  const int m0 = tile_m * kBigTile, n0 = tile_n * kBigTile;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 3, wn = wave >> 2;
+
+  if constexpr (AFF) {
+    for (int i = tid; i < K; i += kBigThreads) gbt[i] = h2{g.gb[i], g.gb[K + i]};
+  }
+  const __amdgpu_buffer_rsrc_t wr = uniform_rsrc(g.w + (int64_t)n0 * K, min(kBigTile, N - n0) * K * 2);
+  const int lrow8 = lane / kCPR, lchunk = lane % kCPR;
+  auto issue_w = [&](int kt) {
+    const int stage = kt % kBigStages, k0 = kt * kBigBK;
+#pragma unroll
+    for (int j = 0; j < SEGS; ++j) {
+      const int seg = j * 8 + wave;
+      const int r = seg * (64 / kCPR) + lrow8;
+      const int c = lchunk ^ ((r >> 1) & 7);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, wsm + stage * STAGE + seg * 1024, 16,
+                                               (r * K + k0 + c * 8) * 2, 0, 0, 0);
+    }
+  };
+
+  // Staging of G: wave w forms rows 32 w .. 32 w + 31 of the tile; lane l takes 16-byte
+  // chunk l % 8 (8 features of one head, dv >= 32) of rows 32 w + l / 8 + 8 j, j = 0..3,
+  // so that each load instruction reads 8 whole 128-byte row slices.
+  const int gc = lane & 7;
+  int grow_[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 32 * wave + (lane >> 3) + 8 * j;
+    grow_[j] = m0 + r < M ? m0 + r : 0;
+  }
+  // the LayerNorm statistics (mean, 1 / std) of the tile's rows from the heads' (mean,
+  // variance), into LDS (lanes 0..31 of wave w: row 32 w + lane)
+  if (lane < 32) {
+    const int r = m0 + 32 * wave + lane;
+    const float2 *srow = g.stats + (int64_t)(r < M ? r : 0) * g.H;
+    float m = 0.f;
+    for (int h = 0; h < g.H; ++h) m += srow[h].x;
+    m *= 1.0f / g.H;
+    float v = 0.f;
+    for (int h = 0; h < g.H; ++h) {
+      const float2 st = srow[h];
+      v += st.y + (st.x - m) * (st.x - m);
+    }
+    v *= 1.0f / g.H;
+    rst[32 * wave + lane] = float2{m, __builtin_amdgcn_rsqf(v + g.eps)};
+  }
+
+  u32x4 cv[4], uv[4];
+  float2 hs[4];
+  // c, U and the head statistics of chunk j of this lane for stage kt: exactly three load
+  // instructions, issued by every lane, so that the waits in the k loop can count them.
+  // Rows past M read row 0 and form rows of G that only reach output rows past M, which
+  // are never stored; nothing selects on the loaded values, which would force a wait for
+  // them right here.
+  auto load_chunk = [&](int kt, int j) {
+    const int f0 = kt * kBigBK + 8 * gc;
+    const int64_t r = grow_[j];
+    cv[j] = *reinterpret_cast<const u32x4 *>(g.c + r * K + f0);
+    uv[j] = *reinterpret_cast<const u32x4 *>(g.u + r * g.u_stride + f0);
+    hs[j] = g.stats[r * g.H + f0 / g.dv];
+  };
+  // G of chunk j of this lane for stage kt (registers -> LDS)
+  float2 rsr[4];  // (mean, 1 / std) of the rows of this lane's chunks, read once
+  auto store_chunk = [&](int kt, int j) {
+    const int stage = kt % kBigStages, f0 = kt * kBigBK + 8 * gc;
+    const int r = 32 * wave + (lane >> 3) + 8 * j;
+    const float2 rs = rsr[j];
+    const float a = __builtin_amdgcn_sqrtf(hs[j].y) * rs.y, b = (hs[j].x - rs.x) * rs.y;
+    const h2 a2 = {(_Float16)a, (_Float16)a}, b2 = {(_Float16)b, (_Float16)b};
+    // vector elements are copied to scalars before any bit cast: a bit cast taken
+    // straight from a vector element is miscompiled by this compiler (only element 0
+    // survives)
+    uint32_t out[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t ce = cv[j][e], ue = uv[j][e];
+      h2 t = __builtin_elementwise_fma(__builtin_bit_cast(h2, ce), a2, b2);
+      if constexpr (AFF) {
+        const h2 gb = gbt[f0 + 2 * e], gb1 = gbt[f0 + 2 * e + 1];
+        t = __builtin_elementwise_fma(t, h2{gb[0], gb1[0]}, h2{gb[1], gb1[1]});
+      }
+      out[e] = __builtin_bit_cast(uint32_t, t * __builtin_bit_cast(h2, ue));
+    }
+    *reinterpret_cast<u32x4 *>(xs + stage * STAGE + swz(r, gc)) = u32x4{out[0], out[1], out[2], out[3]};
+  };
+
+  f32x16 acc[NT][MT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i)
+#pragma unroll
+    for (int j = 0; j < MT; ++j) acc[i][j] = f32x16{};
+
+  // Pipeline: W of stage kt + 1 goes out by direct-to-LDS loads at the top of iteration kt;
+  // chunk j of this lane's G of stage kt + 1 is formed after MFMA k-step j of stage kt,
+  // from registers loaded one iteration earlier, and the registers are refilled at once
+  // with the same chunk of stage kt + 2.  The loop body has no branch: past the last stage
+  // the loads repeat the last stage and the G / W writes go to the free buffer, so the
+  // wait counts below are exact.  Loads complete in order: the top of iteration kt waits
+  // for W of stage kt while the 12 later loads of stage kt + 1 fly on.
+  constexpr int NGL = 12;  // loads of one stage's four chunks
+  const int nk = K / kBigBK;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) load_chunk(0, j);
+  issue_w(0);
+  __syncthreads();  // the row statistics and the gamma / beta table
+#pragma unroll
+  for (int j = 0; j < 4; ++j) rsr[j] = rst[32 * wave + (lane >> 3) + 8 * j];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    store_chunk(0, j);
+    load_chunk(min(1, nk - 1), j);
+  }
+
+  const int lrow = lane & 31, lk = lane >> 5;
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vmcnt<NGL>();
+    __syncthreads();  // every wave's G of stage kt is in LDS; stage kt - 1 is free
+    issue_w(min(kt + 1, nk - 1));
+    const unsigned char *xst = xs + (kt % kBigStages) * STAGE;
+    const unsigned char *wst = wsm + (kt % kBigStages) * STAGE;
+#pragma unroll
+    for (int ks = 0; ks < kBigBK / 16; ++ks) {
+      // fragments of k-step ks; the G chunk formed meanwhile covers their LDS latency
+      f16x8 wf[NT], xf[MT];
+      const int c = ks * 2 + lk;
+#pragma unroll
+      for (int i = 0; i < NT; ++i)
+        wf[i] = as_f16x8(*reinterpret_cast<const u32x4 *>(wst + swz(wn * TN + i * 32 + lrow, c)));
+#pragma unroll
+      for (int j = 0; j < MT; ++j)
+        xf[j] = as_f16x8(*reinterpret_cast<const u32x4 *>(xst + swz(wm * TM + j * 32 + lrow, c)));
+      // chunk ks of stage kt + 1 was loaded one iteration ago; 13 loads followed it (the
+      // other chunks of its stage, W of stage kt + 1, this stage's refills before it)
+      // nothing that uses chunk ks's registers may be scheduled above its wait
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<NGL + SEGS - 3>();
+      store_chunk(kt + 1, ks);
+      load_chunk(min(kt + 2, nk - 1), ks);
+#pragma unroll
+      for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int j = 0; j < MT; ++j) acc[i][j] = mfma32_f16(wf[i], xf[j], acc[i][j]);
+    }
+  }
+  wait_vmcnt<0>();  // the repeated last-stage loads land before LDS is reused below
+
+  // epilogue through LDS, whole-row bf16 stores (as gemm256_kernel)
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < MT; ++j) {
+    const int r = wm * TM + j * 32 + lrow;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = wn * TN + i * 32 + 8 * q + 4 * lk;
+        float v0 = acc[i][j][4 * q + 0], v1 = acc[i][j][4 * q + 1];
+        float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+        if (g.bias != nullptr && n0 + c < N) {
+          const f32x4 bb = *reinterpret_cast<const f32x4 *>(g.bias + n0 + c);
+          v0 += bb[0]; v1 += bb[1]; v2 += bb[2]; v3 += bb[3];
+        }
+        *reinterpret_cast<u32x2 *>(smem + r * kOutPitch + c * 2) = u32x2{pack_bf16(v0, v1), pack_bf16(v2, v3)};
+      }
+    }
+  }
+  __syncthreads();
+  constexpr int kRowChunks = kBigTile * 2 / 16;
+#pragma unroll
+  for (int it = 0; it < kBigTile * kRowChunks / kBigThreads; ++it) {
+    const int ch = it * kBigThreads + tid;
+    const int r = ch / kRowChunks, c16 = ch % kRowChunks;
+    if (m0 + r < M && n0 + c16 * 8 < N) {
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(smem + r * kOutPitch + c16 * 16);
+      *reinterpret_cast<u32x4 *>(g.out + (int64_t)(m0 + r) * N + n0 + c16 * 8) = v;
+    }
+  }
+}
+
+// W2 (bf16) -> fp16, and gamma / beta (fp32, either may be absent: 1 / 0) -> fp16 [2][K].
+__global__ __launch_bounds__(256) void gate_prep_kernel(const uint16_t *__restrict__ w2, int64_t n_w,
+                                                        const float *__restrict__ gamma,
+                                                        const float *__restrict__ beta, int K,
+                                                        uint16_t *__restrict__ w2h,
+                                                        _Float16 *__restrict__ gb) {
+  __builtin_amdgcn_s_setreg((0 << 11) | (23 << 6) | 1, 1);  // saturate, as the f2 kernel
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i * 8 < n_w) {
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(w2 + i * 8);
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[e] = pack_f16(__builtin_bit_cast(float, v[e] << 16), __builtin_bit_cast(float, v[e] & 0xffff0000u));
+    *reinterpret_cast<u32x4 *>(w2h + i * 8) = o;
+  }
+  if (gb != nullptr && i < K) {
+    gb[i] = (_Float16)(gamma != nullptr ? gamma[i] : 1.0f);
+    gb[K + i] = (_Float16)(beta != nullptr ? beta[i] : 0.0f);
+  }
+}
+
 }  // namespace
+
+size_t gate_gemm_lds_bytes(int K) {
+  (void)K;  // the tables are static arrays sized for the largest K
+  const size_t stages = 2 * (size_t)kBigStages * kBigTile * kBigBK * 2;
+  return std::max(stages, (size_t)kBigTile * kOutPitch);
+}
+
+hipError_t launch_gate_prep(const uint16_t *w2, int64_t n_w, const float *gamma, const float *beta,
+                            int K, uint16_t *w2h, uint16_t *gb, hipStream_t stream) {
+  const int64_t work = std::max<int64_t>((n_w + 7) / 8, K);
+  gate_prep_kernel<<<dim3((unsigned)((work + 255) / 256)), 256, 0, stream>>>(
+      w2, n_w, gamma, beta, K, w2h, reinterpret_cast<_Float16 *>(gb));
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_gemm(const GateGemmArgs &a, bool affine, hipStream_t stream) {
+  if (a.M == 0) return hipSuccess;
+  if (a.K % kBigBK != 0 || a.K > 2048 || a.N % 64 != 0 || a.dv < 32 || a.dv % 32 != 0 ||
+      a.H <= 0 || a.N > kGemmMaxK)
+    return hipErrorInvalidValue;
+  GateGemmArgs g = a;
+  g.n_tiles_n = (a.N + kBigTile - 1) / kBigTile;
+  g.n_tiles_total = ((a.M + kBigTile - 1) / kBigTile) * g.n_tiles_n;
+  const int grid = (g.n_tiles_total + 7) / 8 * 8;
+  const size_t lds = gate_gemm_lds_bytes(a.K);
+  // the attribute allows the largest table (K = 2048); each launch asks for what it needs
+  static bool attr_set[2] = {false, false};
+  auto fn = affine ? (const void *)gate_gemm_kernel<true> : (const void *)gate_gemm_kernel<false>;
+  if (!attr_set[affine]) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)gate_gemm_lds_bytes(2048));  // fixed size
+    if (e != hipSuccess) return e;
+    attr_set[affine] = true;
+  }
+  if (affine)
+    gate_gemm_kernel<true><<<dim3(grid), dim3(kBigThreads), lds, stream>>>(g);
+  else
+    gate_gemm_kernel<false><<<dim3(grid), dim3(kBigThreads), lds, stream>>>(g);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm(const uint16_t *A, const uint16_t *W, const float *bias, uint16_t *out,
                        int M, int N, int K, Act act, OutType out_type, hipStream_t stream) {

@@ -19,6 +19,28 @@ constexpr int kGemmMaxK = 1 << 21;
 hipError_t launch_gemm(const uint16_t *A, const uint16_t *W, const float *bias, uint16_t *out,
                        int M, int N, int K, Act act, OutType out_type, hipStream_t stream);
 
+// f2 with the LayerNorm and the U gate of equation 3 formed in its operand staging:
+// out[M][N] = G w^T + bias, G = ((o - mu) rstd gamma + beta) U per row, where o is given
+// per head as c (standardised fp16, [M][K]) with stats (mean, biased variance) [M][H].
+struct GateGemmArgs {
+  const uint16_t *w;        // fp16 [N][K] (w2 converted by launch_gate_prep)
+  const uint16_t *c;        // fp16 [M][K]
+  const uint16_t *u;        // fp16 gate rows, pitch u_stride
+  int64_t u_stride;
+  const float2 *stats;      // [M][H]
+  const _Float16 *gb;       // fp16 [2][K] gamma | beta, or nullptr (no affine)
+  const float *bias;        // [N] or nullptr
+  uint16_t *out;            // bf16 [M][N]
+  int M, N, K, H, dv;
+  float eps;
+  int n_tiles_n, n_tiles_total;  // set by the launcher
+};
+// w2 (bf16, n_w values) -> fp16 w2h; gamma / beta (either may be nullptr) -> fp16 gb [2][K]
+// when gb is not nullptr.
+hipError_t launch_gate_prep(const uint16_t *w2, int64_t n_w, const float *gamma, const float *beta,
+                            int K, uint16_t *w2h, uint16_t *gb, hipStream_t stream);
+hipError_t launch_gate_gemm(const GateGemmArgs &a, bool affine, hipStream_t stream);
+
 // Attention parameters (device pointers unless noted).
 struct AttnArgs {
   const int32_t *offsets;   // [B+1]
@@ -32,8 +54,10 @@ struct AttnArgs {
   const float *rab_pos;     // [rab_heads][pos_buckets] or nullptr
   const float *rab_time;    // [rab_heads][time_buckets] or nullptr
   int pos_buckets, time_buckets, rab_per_head;
-  float *out;               // [T][H*dv]
-  int64_t out_stride;
+  float *out;               // [T][H*dv] raw aggregation (when cn is nullptr)
+  int64_t out_stride;       // elements between rows of out / cn
+  uint16_t *cn;             // or: [T][H*dv] fp16, each head's part standardised with
+  float2 *stats;            //     its (mean, biased variance), stats [T][H]
   const int2 *kstat;        // [T] at each 32-key block start: (min, max) ts of the block
   const int2 *p_kstat;      // [T_p] same for prefix rows
   const int32_t *work;      // [2*cap] (b, q-tile) pairs, longest first
@@ -149,11 +173,6 @@ hipError_t launch_attention(const AttnArgs &a, int dh, int max_seq_len, int64_t 
 // block's timestamps (other entries are not written).
 hipError_t launch_block_stats(const int32_t *ts, const int32_t *offsets, int B, int max_seq_len,
                               int2 *stat, hipStream_t stream);
-
-// G[T][HDV] = LayerNorm(O) * gamma + beta, times U (fp16 row of uvqk), as bf16.
-hipError_t launch_norm_gate(const float *O, const uint16_t *U, int64_t u_stride,
-                            const float *gamma, const float *beta, float eps, uint16_t *G,
-                            int T, int HDV, hipStream_t stream);
 
 // Stochastic Length over a raw jagged batch (stochastic_length.hip): new offsets and the
 // raw indices of the kept tokens, plus (if given) their timestamps and feature rows.

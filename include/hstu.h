@@ -17,12 +17,18 @@
  *  - Pointers marked (device) are HIP device pointers; everything else is host memory
  *    read during the call only.  bf16 and fp16 tensors are passed as uint16_t bit
  *    patterns.
- *  - Precision: X, Y, w1, w2 and the f2 operand are bf16; the f1 output U|V|Q|K and the
- *    attention weights A are fp16 (same MFMA rate on gfx950, 3 more mantissa bits, which
- *    the layer needs to stay within 2e-2 / 2e-3 of an fp64 reference); every product
- *    accumulates in fp32.  f1 outputs saturate at +-65504.  A is rounded to fp16 as
- *    A / -ln 2 (the kernel's scaled domain), so a weight above 65504 ln 2 (about 45403)
- *    saturates at that value instead of overflowing.
+ *  - Precision: X, Y, w1 and w2 are bf16; the f1 output U|V|Q|K and the attention
+ *    weights A are fp16 (same MFMA rate on gfx950, 3 more mantissa bits, which the layer
+ *    needs to stay within 2e-2 / 2e-3 of an fp64 reference); every product accumulates
+ *    in fp32.  f1 outputs saturate at +-65504.  A is rounded to fp16 as A / -ln 2 (the
+ *    kernel's scaled domain), so a weight above 65504 ln 2 (about 45403) saturates at
+ *    that value instead of overflowing.  The forward layer's f2 runs in fp16 as well:
+ *    each head's attention output leaves the attention kernel normalised by that head's
+ *    mean and standard deviation (fp16, magnitude at most sqrt(dv)), the f2 GEMM forms
+ *    G = LayerNorm(AV) * U in fp16 while staging it (saturating at +-65504) and
+ *    multiplies it by an fp16 copy of w2 made on each call (w2 entries below 2^-14 keep
+ *    fewer significant bits there, entries above 65504 saturate).  hstu_layer_bwd forms
+ *    its own G in bf16.
  *  - Row-major layouts.  Weights are "out x in": f1(X) = X w1^T + b1, f2(G) = G w2^T + b2.
  *  - U|V|Q|K layout of the f1 output: columns [0,H*dv) = U, [H*dv,2H*dv) = V,
  *    then H*dqk columns of Q and H*dqk of K; head h owns columns [h*dh,(h+1)*dh) of
@@ -351,7 +357,8 @@ int hstu_last_hip_error(void);
  * While enabled, every kernel the library launches is bracketed by two events; the
  * durations are collected by hstu_profile_collect, which synchronises the events.
  * Kernel ids: 0 schedule and key-block timestamp ranges, 1 f1 GEMM, 2 attention,
- * 3 norm-gate, 4 f2 GEMM.                                                           */
+ * 3 f2 operand preparation (w2, gamma, beta to fp16), 4 f2 GEMM with the LayerNorm and
+ * the U gate formed in its operand staging.                                         */
 void hstu_profile_enable(int on);
 void hstu_profile_reset(void);
 /* Adds up finished records: total_ms[k] and launches[k] for k in [0, 5).           */

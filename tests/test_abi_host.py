@@ -97,8 +97,8 @@ def test_bad_arguments_rejected(lib):
 def test_workspace_checks(lib):
     d, s = _dims(), _seq()
     need = lib.hstu_layer_workspace_bytes(ctypes.byref(d), ctypes.byref(s))
-    T, hdv = 118, 64
-    assert need >= T * hdv * 6
+    T, hdv, H, dm = 118, 64, 2, 64
+    assert need >= T * hdv * 2 + T * H * 8 + dm * hdv * 2  # standardised O, stats, fp16 w2
     assert need % 256 == 0
     assert _call_layer(lib, d, ws_bytes=need - 1) == _lib.HSTU_ERR_WORKSPACE
     assert _call_layer(lib, d, ws=None) == _lib.HSTU_ERR_WORKSPACE
