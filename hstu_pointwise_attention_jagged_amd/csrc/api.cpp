@@ -229,7 +229,6 @@ AttnArgs attn_args(const hstu_dims_t *d, const float *rab_pos, const float *rab_
   return a;
 }
 
-// f1 -> attention -> norm-gate -> f2 for one batch whose attention args are ready.
 // Jagged tile schedule and key-block timestamp ranges of a batch (and its prefix).  They
 // depend only on the batch, so a stack of layers builds them once; `all_stats` asks for
 // the ranges whenever timestamps exist (a later layer of a stack may use the time term).
@@ -246,6 +245,8 @@ hstu_status_t run_setup(const hstu_jagged_t *s, const AttnArgs &aa, const LayerW
   return HSTU_OK;
 }
 
+// f1 -> attention -> f2 (LayerNorm and gate in its staging) for one batch whose attention
+// args are ready.
 hstu_status_t run_layer(const hstu_dims_t *d, const hstu_weights_t *w, const hstu_jagged_t *s,
                         const uint16_t *x, uint16_t *y, uint16_t *uvqk, const AttnArgs &aa,
                         const LayerWs &lw, const hstu_jagged_t *pre, hipStream_t st,
@@ -259,7 +260,11 @@ hstu_status_t run_layer(const hstu_dims_t *d, const hstu_weights_t *w, const hst
     if (r != HSTU_OK) return r;
   }
   const bool affine = w->ln_gamma != nullptr || w->ln_beta != nullptr;
-  e = timed(1, st, [&] { return launch_gemm(x, w->w1, w->b1, uvqk, T, n1, d->d_model, ACT_SILU, OUT_F16, st); });
+  // T may be a capacity: the GEMMs read the true row count, seq_offsets[B], on the device
+  const int32_t *t_dev = s->seq_offsets + s->batch;
+  e = timed(1, st, [&] {
+    return launch_gemm(x, w->w1, w->b1, uvqk, T, n1, d->d_model, ACT_SILU, OUT_F16, st, t_dev);
+  });
   if (e != hipSuccess) return hip_fail(e);
   e = timed(3, st, [&] {
     return launch_gate_prep(w->w2, (int64_t)d->d_model * hdv, w->ln_gamma, w->ln_beta, hdv, lw.w2h,
@@ -278,6 +283,7 @@ hstu_status_t run_layer(const hstu_dims_t *d, const hstu_weights_t *w, const hst
   ga.gb = affine ? reinterpret_cast<const _Float16 *>(lw.gb) : nullptr;
   ga.bias = w->b2;
   ga.out = y;
+  ga.m_dev = t_dev;
   ga.M = T;
   ga.N = d->d_model;
   ga.K = hdv;
@@ -1036,7 +1042,7 @@ hstu_status_t hstu_validate_jagged(const hstu_jagged_t *seq, void *stream) {
                                 hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e);
-  if (off[0] != 0 || off[seq->batch] != seq->total_tokens) return HSTU_ERR_INVALID_ARG;
+  if (off[0] != 0 || off[seq->batch] > seq->total_tokens) return HSTU_ERR_INVALID_ARG;
   for (int b = 0; b < seq->batch; ++b) {
     const int64_t n = (int64_t)off[b + 1] - off[b];
     if (n < 0 || n > seq->max_seq_len) return HSTU_ERR_INVALID_ARG;

@@ -33,8 +33,9 @@ template <int BM, int BN, int ACT, int OUT>
 __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const uint16_t *__restrict__ A,
                                                            const uint16_t *__restrict__ W,
                                                            const float *__restrict__ bias,
-                                                           uint16_t *__restrict__ out, int M,
-                                                           int N, int K, int n_tiles_n) {
+                                                           uint16_t *__restrict__ out,
+                                                           const int32_t *__restrict__ m_dev,
+                                                           int M_cap, int N, int K, int n_tiles_n) {
   constexpr int WM = 2, WN = 2;            // waves along tokens / features
   constexpr int TMW = BM / WM, TNW = BN / WN;
   constexpr int MT = TMW / 32, NT = TNW / 32;
@@ -49,6 +50,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const uint16_t *__res
   const int tile_n = blockIdx.x % n_tiles_n;
   const int tile_m = blockIdx.x / n_tiles_n;
   const int m0 = tile_m * BM, n0 = tile_n * BN;
+  const int M = m_dev != nullptr ? min(M_cap, *m_dev) : M_cap;  // rows present
+  if (m0 >= M) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
 
@@ -187,8 +190,9 @@ template <int ACT, int OUT>
 __global__ __launch_bounds__(kBigThreads, 2) void gemm256_kernel(const uint16_t *__restrict__ A,
                                                                   const uint16_t *__restrict__ W,
                                                                   const float *__restrict__ bias,
-                                                                  uint16_t *__restrict__ out, int M,
-                                                                  int N, int K, int n_tiles_n,
+                                                                  uint16_t *__restrict__ out,
+                                                                  const int32_t *__restrict__ m_dev,
+                                                                  int M_cap, int N, int K, int n_tiles_n,
                                                                   int n_tiles_total) {
   constexpr int TM = 64, TN = 128;  // wave tile: tokens x features
   constexpr int MT = TM / 32, NT = TN / 32;
@@ -209,6 +213,8 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm256_kernel(const uint16_t 
   const int tile_n = lin % n_tiles_n;
   const int tile_m = lin / n_tiles_n;
   const int m0 = tile_m * kBigTile, n0 = tile_n * kBigTile;
+  const int M = m_dev != nullptr ? min(M_cap, *m_dev) : M_cap;  // rows present
+  if (m0 >= M) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 3, wn = wave >> 2;  // 4 wave rows of tokens, 2 of features
@@ -351,7 +357,7 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm256_kernel(const uint16_t 
 
 template <int ACT, int OUT>
 hipError_t launch_big(const uint16_t *A, const uint16_t *W, const float *bias, uint16_t *out,
-                      int M, int N, int K, hipStream_t stream) {
+                      int M, int N, int K, hipStream_t stream, const int32_t *m_dev) {
   const int tn = N / kBigTile;
   const int tm = (M + kBigTile - 1) / kBigTile;
   const int total = tm * tn;
@@ -365,18 +371,18 @@ hipError_t launch_big(const uint16_t *A, const uint16_t *W, const float *bias, u
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  gemm256_kernel<ACT, OUT><<<dim3(grid), dim3(kBigThreads), lds, stream>>>(A, W, bias, out, M, N,
-                                                                           K, tn, total);
+  gemm256_kernel<ACT, OUT><<<dim3(grid), dim3(kBigThreads), lds, stream>>>(A, W, bias, out, m_dev,
+                                                                           M, N, K, tn, total);
   return hipGetLastError();
 }
 
 template <int BM, int BN, int ACT, int OUT>
 hipError_t launch_tile(const uint16_t *A, const uint16_t *W, const float *bias, uint16_t *out,
-                       int M, int N, int K, hipStream_t stream) {
+                       int M, int N, int K, hipStream_t stream, const int32_t *m_dev) {
   const int tn = N / BN;
   const int tm = (M + BM - 1) / BM;
-  gemm_kernel<BM, BN, ACT, OUT><<<dim3(tm * tn), dim3(kThreads), 0, stream>>>(A, W, bias, out, M, N,
-                                                                         K, tn);
+  gemm_kernel<BM, BN, ACT, OUT><<<dim3(tm * tn), dim3(kThreads), 0, stream>>>(A, W, bias, out, m_dev,
+                                                                         M, N, K, tn);
   return hipGetLastError();
 }
 
@@ -411,7 +417,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gate_gemm_kernel(GateGemmArgs 
   // an fp16 result that overflows clamps to +-65504 (G saturates instead of turning inf)
   __builtin_amdgcn_s_setreg((0 << 11) | (23 << 6) | 1, 1);
 
-  const int M = g.M, N = g.N, K = g.K;
+  const int N = g.N, K = g.K;
   const int nwg = gridDim.x;
   const int per_xcd = (nwg + 7) / 8;
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
@@ -420,6 +426,8 @@ __global__ __launch_bounds__(kBigThreads, 1) void gate_gemm_kernel(GateGemmArgs 
   const int tile_n = lin % g.n_tiles_n;
   const int tile_m = lin / g.n_tiles_n;
   const int m0 = tile_m * kBigTile, n0 = tile_n * kBigTile;
+  const int M = g.m_dev != nullptr ? min(g.M, *g.m_dev) : g.M;  // rows present
+  if (m0 >= M) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 3, wn = wave >> 2;
@@ -665,25 +673,26 @@ hipError_t launch_gate_gemm(const GateGemmArgs &a, bool affine, hipStream_t stre
 }
 
 hipError_t launch_gemm(const uint16_t *A, const uint16_t *W, const float *bias, uint16_t *out,
-                       int M, int N, int K, Act act, OutType out_type, hipStream_t stream) {
+                       int M, int N, int K, Act act, OutType out_type, hipStream_t stream,
+                       const int32_t *m_dev) {
   if (M == 0) return hipSuccess;
   if (K > kGemmMaxK) return hipErrorInvalidValue;  // 32-bit offsets within a 256-row panel
   const bool big = (N % kBigTile) == 0 && M >= kBigTile;
   const bool wide = (N % 128) == 0;
   if (act == ACT_SILU && out_type == OUT_F16) {
-    if (big) return launch_big<ACT_SILU, OUT_F16>(A, W, bias, out, M, N, K, stream);
-    return wide ? launch_tile<128, 128, ACT_SILU, OUT_F16>(A, W, bias, out, M, N, K, stream)
-                : launch_tile<128, 64, ACT_SILU, OUT_F16>(A, W, bias, out, M, N, K, stream);
+    if (big) return launch_big<ACT_SILU, OUT_F16>(A, W, bias, out, M, N, K, stream, m_dev);
+    return wide ? launch_tile<128, 128, ACT_SILU, OUT_F16>(A, W, bias, out, M, N, K, stream, m_dev)
+                : launch_tile<128, 64, ACT_SILU, OUT_F16>(A, W, bias, out, M, N, K, stream, m_dev);
   }
   if (act == ACT_NONE && out_type == OUT_F16) {  // pre-activations (the backward's recompute)
-    if (big) return launch_big<ACT_NONE, OUT_F16>(A, W, bias, out, M, N, K, stream);
-    return wide ? launch_tile<128, 128, ACT_NONE, OUT_F16>(A, W, bias, out, M, N, K, stream)
-                : launch_tile<128, 64, ACT_NONE, OUT_F16>(A, W, bias, out, M, N, K, stream);
+    if (big) return launch_big<ACT_NONE, OUT_F16>(A, W, bias, out, M, N, K, stream, m_dev);
+    return wide ? launch_tile<128, 128, ACT_NONE, OUT_F16>(A, W, bias, out, M, N, K, stream, m_dev)
+                : launch_tile<128, 64, ACT_NONE, OUT_F16>(A, W, bias, out, M, N, K, stream, m_dev);
   }
   if (act == ACT_NONE && out_type == OUT_BF16) {
-    if (big) return launch_big<ACT_NONE, OUT_BF16>(A, W, bias, out, M, N, K, stream);
-    return wide ? launch_tile<128, 128, ACT_NONE, OUT_BF16>(A, W, bias, out, M, N, K, stream)
-                : launch_tile<128, 64, ACT_NONE, OUT_BF16>(A, W, bias, out, M, N, K, stream);
+    if (big) return launch_big<ACT_NONE, OUT_BF16>(A, W, bias, out, M, N, K, stream, m_dev);
+    return wide ? launch_tile<128, 128, ACT_NONE, OUT_BF16>(A, W, bias, out, M, N, K, stream, m_dev)
+                : launch_tile<128, 64, ACT_NONE, OUT_BF16>(A, W, bias, out, M, N, K, stream, m_dev);
   }
   return hipErrorInvalidValue;
 }

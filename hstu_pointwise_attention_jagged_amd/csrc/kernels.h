@@ -16,8 +16,11 @@ constexpr int kGemmMaxK = 1 << 21;
 
 // out[M][N] = act(A[M][K] . W[N][K]^T + bias[N]): bf16 inputs, fp32 accumulation, output
 // bf16 or fp16 (saturated to the finite range).  Requires K % 64 == 0, N % 64 == 0.
+// With m_dev (device), only rows below min(M, *m_dev) are computed and written: M is then
+// a capacity and the true row count is read on the device.
 hipError_t launch_gemm(const uint16_t *A, const uint16_t *W, const float *bias, uint16_t *out,
-                       int M, int N, int K, Act act, OutType out_type, hipStream_t stream);
+                       int M, int N, int K, Act act, OutType out_type, hipStream_t stream,
+                       const int32_t *m_dev = nullptr);
 
 // f2 with the LayerNorm and the U gate of equation 3 formed in its operand staging:
 // out[M][N] = G w^T + bias, G = ((o - mu) rstd gamma + beta) U per row, where o is given
@@ -31,6 +34,7 @@ struct GateGemmArgs {
   const _Float16 *gb;       // fp16 [2][K] gamma | beta, or nullptr (no affine)
   const float *bias;        // [N] or nullptr
   uint16_t *out;            // bf16 [M][N]
+  const int32_t *m_dev;     // (device) true row count, or nullptr: M rows (else M is a capacity)
   int M, N, K, H, dv;
   float eps;
   int n_tiles_n, n_tiles_total;  // set by the launcher

@@ -86,7 +86,7 @@ class DeviceWeights:
 @dataclasses.dataclass
 class DeviceJagged:
     offsets: torch.Tensor                   # int32 [B+1] on the device
-    total_tokens: int                       # host copy of offsets[B]
+    total_tokens: int                       # host copy of offsets[B] (forward calls: or a capacity above it)
     max_seq_len: int                        # host upper bound on lengths
     timestamps: Optional[torch.Tensor] = None  # int32 [T] on the device
 

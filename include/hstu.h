@@ -50,6 +50,15 @@
  *  - Device-side jagged offsets are a precondition (0 = off[0] <= ... <= off[B] = T,
  *    max length <= max_seq_len); they are not re-validated on the hot path.  Use
  *    hstu_validate_jagged when in doubt.  Zero-length sequences are legal.
+ *  - Token capacity: the forward entry points (hstu_layer_fwd, hstu_layer_fwd_mfalcon,
+ *    hstu_stack_fwd, hstu_stack_fwd_mfalcon, hstu_attn_fwd, hstu_attn_fwd_noalloc) also
+ *    accept total_tokens above off[B], as a capacity: row buffers and workspaces are then
+ *    sized for total_tokens rows, the kernels take the true count off[B] from the device,
+ *    and output rows from off[B] on are left as they were.  A batch built on the device
+ *    (hstu_stochastic_length) thus feeds a layer with no copy to the host: pass the raw
+ *    token count as total_tokens and the raw max_seq_len (or the subsample length, if
+ *    larger) as max_seq_len.  Work scales with off[B], not with the capacity.  The
+ *    backward entry points need total_tokens == off[B].
  *  - Supported shapes: dqk == dv in {32, 64, 128}; 1 <= pos_buckets <= 1024;
  *    1 <= time_buckets <= 64; rab_heads 1 or num_heads.  The layer entry points also
  *    need d_model and num_heads*dv to be multiples of 64, d_model <= 2^21 and
@@ -106,7 +115,8 @@ typedef struct {
 
 typedef struct {
   int32_t batch;              /* B >= 0                                                */
-  int32_t total_tokens;       /* T = seq_offsets[B] (host copy)                        */
+  int32_t total_tokens;       /* T = seq_offsets[B] (host copy), or a capacity above   */
+                              /* it for the forward entry points (see above)           */
   int32_t max_seq_len;        /* upper bound on every sequence length (host)           */
   const int32_t *seq_offsets; /* (device) [B+1], non-decreasing, off[0] = 0            */
   const int32_t *timestamps;  /* (device) [T] or NULL (time term off)                  */
@@ -205,7 +215,7 @@ hstu_status_t hstu_stack_fwd_mfalcon(const hstu_dims_t *dims, int32_t n_layers,
  *   q, k, v (device) fp16; row t of head h at q + t*row_stride + h*dqk (same for k,v
  *           with dqk / dv)
  *   prefix  NULL or the keys preceding each sequence (required for SELF_ONLY)
- *   out     (device) fp32 [T][H*dv], every row written
+ *   out     (device) fp32 [T][H*dv], every row below off[B] written
  *   ws      >= hstu_attn_workspace_bytes(dims, seq, prefix ? prefix->seq : NULL)     */
 hstu_status_t hstu_attn_fwd(const hstu_dims_t *dims, const float *rab_pos,
                             const float *rab_time, const hstu_jagged_t *seq,
@@ -342,9 +352,9 @@ hstu_status_t hstu_layer_bwd(const hstu_dims_t *dims, const hstu_weights_t *w,
                              float *d_x, const hstu_layer_grads_t *grads, void *ws,
                              size_t ws_bytes, void *stream);
 
-/* Debug check of device offsets: off[0] == 0, non-decreasing, off[B] == total_tokens,
- * every length <= max_seq_len.  Synchronises the stream.  Returns HSTU_OK or
- * HSTU_ERR_INVALID_ARG.                                                              */
+/* Debug check of device offsets: off[0] == 0, non-decreasing, off[B] <= total_tokens
+ * (equal, unless total_tokens is meant as a capacity), every length <= max_seq_len.
+ * Synchronises the stream.  Returns HSTU_OK or HSTU_ERR_INVALID_ARG.                  */
 hstu_status_t hstu_validate_jagged(const hstu_jagged_t *seq, void *stream);
 
 /* Static description of a status code.                                              */

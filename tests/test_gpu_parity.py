@@ -395,6 +395,12 @@ def test_validate_jagged():
     short = dev.jagged_of(good)
     short.max_seq_len = 5
     assert not ops.hstu_validate_jagged(short)
+    cap = dev.jagged_of(good)  # total_tokens as a capacity above off[B]
+    cap.total_tokens = 40
+    assert ops.hstu_validate_jagged(cap)
+    under = dev.jagged_of(good)
+    under.total_tokens = 11
+    assert not ops.hstu_validate_jagged(under)
 
 
 # ----------------------------------------------------------------------------------

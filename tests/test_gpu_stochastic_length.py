@@ -142,25 +142,41 @@ def test_sl_all_kept_and_empty_batch():
 
 
 def test_sl_batch_built_on_device_feeds_the_layer():
+    """Stochastic Length then the layer with no copy to the host in between: the layer
+    gets the raw token count as its capacity and reads the kept count from the device
+    offsets.  Rows past the kept count keep their previous contents."""
     w = wl.config(3)
     r = w.raw
-    kept, new_off, new_ts, x_out, _ = _device_sl(r.seq, r.u_keep, r.keys, r.n_target, r.alpha, r.x)
+    d = w.dims
+    raw = dev.jagged_of(r.seq)
+    ut = torch.from_numpy(np.ascontiguousarray(r.u_keep, dtype=np.float64)).cuda()
+    kt = torch.from_numpy(np.ascontiguousarray(r.keys, dtype=np.uint32).view(np.int32)).cuda()
+    xt = dev.bf16_tensor(r.x)
+    T_raw = r.seq.total
+    L = int(np.floor(float(r.n_target) ** (r.alpha / 2)))
+    y = torch.full((T_raw, d.d_model), 7.0, dtype=torch.bfloat16, device="cuda")
+    u = torch.full((T_raw, d.uvqk_width), 7.0, dtype=torch.float16, device="cuda")
+    torch.cuda.synchronize()
+    # one stream, no synchronisation and no host read of the new offsets in between
+    kept, new_off, new_ts, x_out = ops.hstu_stochastic_length(raw, ut, kt, n_target=r.n_target,
+                                                              alpha=r.alpha, x=xt)
+    seq_dev = ops.DeviceJagged(offsets=new_off, total_tokens=T_raw,
+                               max_seq_len=max(L, int(r.seq.lengths.max())), timestamps=new_ts)
+    ops.hstu_layer_fwd(dev.dims_of(d), dev.weights_of(w.weights), seq_dev, x_out, y=y, uvqk=u)
+    torch.cuda.synchronize()
     want_kept, want_off = sl.select(r.seq.offsets, r.u_keep, r.keys, r.n_target, r.alpha)
     np.testing.assert_array_equal(new_off.cpu().numpy(), want_off)
     T_new = int(want_off[-1])
+    assert T_new < T_raw
+    assert torch.all(y[T_new:] == 7.0) and torch.all(u[T_new:] == 7.0), "rows past off[B] written"
     lens = np.diff(want_off)
-    d = w.dims
-    seq_dev = ops.DeviceJagged(offsets=new_off, total_tokens=T_new, max_seq_len=int(lens.max()),
-                               timestamps=new_ts[:T_new])
-    y, _ = ops.hstu_layer_fwd(dev.dims_of(d), dev.weights_of(w.weights), seq_dev, x_out[:T_new])
-    torch.cuda.synchronize()
-    got = dev.bf16_to_numpy(y).astype(np.float64)
+    got = dev.bf16_to_numpy(y[:T_new]).astype(np.float64)
     b_long = int(np.argmax(lens))
     rows = [0, int(want_off[b_long]), int(want_off[b_long + 1] - 1), int(want_off[5] + 3), T_new - 1]
     want = ref.layer_fwd(r.x[want_kept], w.weights, want_off, r.seq.timestamps[want_kept],
                          d.num_heads, d.dqk, d.dv, d.ln_eps, rows=rows)
     err = np.abs(got[rows] - want[rows])
-    say(f"[sl] layer on the device-built batch: T={T_new} max_abs={err.max():.3e} "
-        f"mean_abs={err.mean():.3e}")
+    say(f"[sl] layer on the device-built batch: capacity {T_raw}, kept {T_new}, "
+        f"max_abs={err.max():.3e} mean_abs={err.mean():.3e}")
     assert np.all(np.isfinite(got))
     assert err.max() <= 2e-2 and err.mean() <= 2e-3
