@@ -12,6 +12,7 @@ Besides the step, the line carries separate measurements of Stochastic Length, M
 serving, the attention gradients (hstu_attn_bwd) and one layer's backward (hstu_layer_bwd).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers 24] [--no-cpu-baseline]
+                  [--only-step]
 """
 
 from __future__ import annotations
@@ -108,13 +109,44 @@ def write_traffic_record(d, copy_bytes):
     log(f"wrote {TRAFFIC_RECORD}: {rec['bytes_per_launch'] / 1e6:.1f} MB per launch")
 
 
+def host_info():
+    """CPU model, visible logical CPUs and numpy's BLAS library with its thread count."""
+    model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    info = {"cpu_model": model, "logical_cpus_visible": os.cpu_count(),
+            "cpus_in_affinity": len(os.sched_getaffinity(0))}
+    try:
+        import numpy  # noqa: F401  (loads the BLAS library that threadpoolctl reports)
+        import threadpoolctl
+        info["blas"] = [{k: p.get(k) for k in ("internal_api", "version", "num_threads",
+                                               "threading_layer", "architecture")}
+                        for p in threadpoolctl.threadpool_info() if p.get("user_api") == "blas"]
+    except Exception as e:  # threadpoolctl missing or failing: say so
+        info["blas"] = f"unavailable ({type(e).__name__})"
+    return info
+
+
+# Host threads the oracle may use: one GPU's share of the host cores (16), or fewer when
+# fewer are available to the process.
+CPU_SHARE_PER_GPU = 16
+
+
 def cpu_baseline(w, layers, n_seq=2):
-    """fp64 oracle on the first n_seq 8192-token sequences of the same batch, one layer."""
+    """fp64 oracle on the first n_seq 8192-token sequences of the same batch, one layer.
+    Its attention runs on a pool of `cores` threads; its matrix products run in numpy's
+    BLAS, whose own thread count is reported with the host description."""
     import numpy as np
     from oracle import hstu_ref
 
     d = w.dims
-    cores = min(os.cpu_count() or 1, 16)
+    cores = min(len(os.sched_getaffinity(0)), CPU_SHARE_PER_GPU)
     s0, s1 = int(w.seq.offsets[0]), int(w.seq.offsets[n_seq])
     x = w.x[s0:s1]
     off = (w.seq.offsets[: n_seq + 1] - s0).astype(np.int32)
@@ -125,7 +157,7 @@ def cpu_baseline(w, layers, n_seq=2):
     lengths = [int(n) for n in np.diff(off)]
     f1, att, f2 = useful_flops(lengths, d.d_model, d.num_heads, d.dqk, d.dv)
     return {"value": round((f1 + att + f2) / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "host": host_info(),
             "sample": f"one layer (not the {layers}-layer stack) on {n_seq} of the 8 sequences "
                       f"({sum(lengths)} tokens), fp64 NumPy, {dt:.1f} s",
             "seconds": round(dt, 3)}
@@ -165,6 +197,136 @@ def sl_measure(torch, np, ops, dev, wl, reps=20):
                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(alg / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                          "algorithmic_bytes": alg}}
+
+
+def _events_ms(torch, stream, fn, reps):
+    """Average time of fn over reps calls, HIP events on the launch stream."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def _kernel_ms(torch, ops, fn, reps=3):
+    """Per-kernel average times (ms) of fn from the library's event timing (run untimed)."""
+    torch.cuda.synchronize()
+    ops.profile_reset()
+    ops.profile_enable(True)
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    ops.profile_enable(False)
+    k = ops.profile_collect()
+    ops.profile_reset()
+    return {n: round(v[0] / v[1], 4) for n, v in k.items() if v[1]}
+
+
+def zipf_measure(torch, np, ops, dev, wl, layers=24, reps=20):
+    """The 64-user batch (lengths truncated Zipf s = 1.2 on [16, 1024], d = 256, 4 heads of
+    64): one layer alone and a stack of `layers` layers in one call, useful FLOPs as for
+    the main step."""
+    w = wl.config(1)
+    d = w.dims
+    dims, seq = dev.dims_of(d), dev.jagged_of(w.seq)
+    rng = np.random.default_rng(1100)
+    lw = [dev.weights_of(w.weights)] + [dev.weights_of(wl.draw_weights(rng, d))
+                                         for _ in range(layers - 1)]
+    x = dev.bf16_tensor(w.x)
+    T = w.seq.total
+    y = torch.empty_like(x)
+    u = torch.empty((T, d.uvqk_width), dtype=torch.float16, device="cuda")
+    ws = torch.empty(ops.hstu_stack_workspace_bytes(dims, seq), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def one():
+        ops.hstu_layer_fwd(dims, lw[0], seq, x, y=y, uvqk=u, workspace=ws, stream=stream)
+
+    def stack():
+        ops.hstu_stack_fwd(dims, lw, seq, x, y=y, uvqk=u, workspace=ws, stream=stream)
+
+    one()
+    stack()
+    torch.cuda.synchronize()
+    layer_ms = _events_ms(torch, stream, one, reps)
+    stack_ms = _events_ms(torch, stream, stack, max(reps // 4, 3))
+    f1, att, f2 = useful_flops(w.seq.lengths.tolist(), d.d_model, d.num_heads, d.dqk, d.dv)
+    fl = f1 + att + f2
+    return {"workload": f"{w.seq.batch} users, lengths truncated Zipf s=1.2 on [16, 1024] "
+                        f"({T} tokens, longest {int(w.seq.lengths.max())}), d={d.d_model}, "
+                        f"{d.num_heads} heads x {d.dqk}, causal, rab pos+time",
+            "useful_tflop_per_layer": round(fl / 1e12, 6),
+            "layer_ms": round(layer_ms, 4), "layer_tflops": round(fl / (layer_ms * 1e-3) / 1e12, 2),
+            "stack_layers": layers, "stack_ms": round(stack_ms, 4),
+            "stack_tflops": round(layers * fl / (stack_ms * 1e-3) / 1e12, 2),
+            "pct_mfma_peak_stack": round(100 * layers * fl / (stack_ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 2),
+            "layer_kernel_avg_ms": _kernel_ms(torch, ops, one)}
+
+
+def sl_layer_measure(torch, np, ops, dev, wl, reps=10):
+    """Stochastic Length then one layer on the batch it builds (128 users, raw lengths
+    log-uniform on [256, 4096], N = 4096, alpha = 1.6, d = 512, 8 heads of 64), with no
+    host copy in between: the layer takes the raw token count as its capacity and reads
+    the kept count from the device offsets.  Useful FLOPs count the kept tokens only."""
+    w = wl.config(3)
+    r = w.raw
+    d = w.dims
+    dims = dev.dims_of(d)
+    raw = dev.jagged_of(r.seq)
+    u_keep = torch.from_numpy(r.u_keep.astype(np.float64)).cuda()
+    keys = torch.from_numpy(r.keys.view(np.int32)).cuda()
+    x = dev.bf16_tensor(r.x)
+    wts = dev.weights_of(w.weights)
+    T_raw = r.seq.total
+    L = int(np.floor(float(r.n_target) ** (r.alpha / 2)))
+    max_len = max(L, int(r.seq.lengths.max()))
+    stream = torch.cuda.current_stream()
+    sl_ws = torch.empty(max(int(ops.hstu_sl_workspace_bytes(raw)), 1), dtype=torch.uint8,
+                        device="cuda")
+    y = torch.empty((T_raw, d.d_model), dtype=torch.bfloat16, device="cuda")
+    u = torch.empty((T_raw, d.uvqk_width), dtype=torch.float16, device="cuda")
+    state = {}
+
+    def sl():
+        state["sl"] = ops.hstu_stochastic_length(raw, u_keep, keys, x=x, workspace=sl_ws,
+                                                 stream=stream)
+
+    sl()
+    _, new_off, new_ts, x_out = state["sl"]
+    seq = ops.DeviceJagged(offsets=new_off, total_tokens=T_raw, max_seq_len=max_len,
+                           timestamps=new_ts)
+    lws = torch.empty(ops.hstu_layer_workspace_bytes(dims, seq), dtype=torch.uint8, device="cuda")
+
+    def layer():
+        ops.hstu_layer_fwd(dims, wts, seq, x_out, y=y, uvqk=u, workspace=lws, stream=stream)
+
+    def both():
+        # SL writes into fresh outputs each call; the layer reads the ones made once above
+        # (identical contents: the draws are the same), so the pair runs back to back
+        sl()
+        layer()
+
+    layer()
+    torch.cuda.synchronize()
+    both_ms = _events_ms(torch, stream, both, reps)
+    layer_ms = _events_ms(torch, stream, layer, reps)
+    lengths = np.diff(new_off.cpu().numpy()).tolist()  # after the timed regions
+    f1, att, f2 = useful_flops(lengths, d.d_model, d.num_heads, d.dqk, d.dv)
+    fl = f1 + att + f2
+    return {"workload": f"stochastic length on {r.seq.batch} users (raw lengths log-uniform on "
+                        f"[256, 4096], N=4096, alpha=1.6), then one layer on the kept batch, "
+                        f"d={d.d_model}, {d.num_heads} heads x {d.dqk}, causal, rab pos+time",
+            "raw_tokens": T_raw, "kept_tokens": int(sum(lengths)),
+            "useful_tflop_per_layer": round(fl / 1e12, 5),
+            "sl_plus_layer_ms": round(both_ms, 4), "layer_ms": round(layer_ms, 4),
+            "layer_tflops": round(fl / (layer_ms * 1e-3) / 1e12, 2),
+            "pct_mfma_peak_layer": round(100 * fl / (layer_ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS, 2),
+            "layer_kernel_avg_ms": _kernel_ms(torch, ops, layer),
+            "note": "one stream, no host synchronisation between SL and the layer; the layer's "
+                    "total_tokens is the raw count (a capacity), its kernels read the kept count "
+                    "from the device offsets"}
 
 
 def bwd_measure(torch, np, ops, dev, wl, reps=10):
@@ -378,6 +540,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--layers", type=int, default=24)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-step", action="store_true",
+                    help="time the stack only (no side measurements, no CPU baseline): the "
+                         "short run that counter collection wraps")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run 4 device-to-device copies of this many bytes (counter "
                          "calibration for HBM traffic) and exit")
@@ -497,10 +662,17 @@ def main():
         "cpu_baseline": None,
         "host": platform.node(),
     }
+    if args.only_step:
+        print(json.dumps(out), flush=True)
+        return
     log("stochastic length on the 128-user raw batch")
     out["stochastic_length"] = sl_measure(torch, np, ops, dev, wl)
     log("M-FALCON serving through a 4-layer stack, micro-batches of 1024 and 128 per user")
     out["mfalcon_serving"] = [mfalcon_measure(torch, np, ops, dev, wl, bm=bm) for bm in (1024, 128)]
+    log("64-user Zipf batch: one layer and a 24-layer stack")
+    out["zipf_64_users"] = zipf_measure(torch, np, ops, dev, wl)
+    log("stochastic length then a layer on the kept batch, no host copy between")
+    out["sl_then_layer"] = sl_layer_measure(torch, np, ops, dev, wl)
     log("attention gradients (dQ, dK, dV) on the 8 x 8192 batch")
     out["attention_backward"] = bwd_measure(torch, np, ops, dev, wl)
     log("layer backward on the 8 x 8192 batch")

@@ -179,11 +179,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void *base,
   return __builtin_amdgcn_make_buffer_rsrc(p, 0, __builtin_amdgcn_readfirstlane(bytes), kRsrcWord3);
 }
 
-// s_waitcnt vmcnt(n) (n <= 15), not waiting on the other counters.
+// s_waitcnt vmcnt(n) (n <= 63: low 4 bits in [3:0], high 2 bits in [15:14]), not waiting
+// on the other counters.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 16, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((15 << 8) | (7 << 4) | N);
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | (15 << 8) | (7 << 4) | (N & 15));
 }
 
 template <int ACT, int OUT>
@@ -204,17 +205,19 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm256_kernel(const uint16_t 
   unsigned char *wsm = smem + kBigStages * STAGE;  // [kBigStages][STAGE]
 
   // Workgroups are dealt to the 8 XCDs round-robin; give each XCD a contiguous range of
-  // tiles (feature tile fastest) so that the tiles sharing X rows share one L2.
-  const int nwg = gridDim.x;
-  const int per_xcd = (nwg + 7) / 8;
+  // the tiles present (feature tile fastest) so that the tiles sharing X rows share one
+  // L2.  The range comes from the rows present, which may be fewer than the grid was
+  // sized for: the work then still spreads over every XCD, and the surplus workgroups
+  // (the highest slots) exit.
+  const int M = m_dev != nullptr ? min(M_cap, *m_dev) : M_cap;  // rows present
+  const int tiles = min(n_tiles_total, (M + kBigTile - 1) / kBigTile * n_tiles_n);
+  const int per_xcd = (tiles + 7) / 8;
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
   const int lin = xcd * per_xcd + slot;
-  if (slot >= per_xcd || lin >= n_tiles_total) return;
+  if (slot >= per_xcd || lin >= tiles) return;
   const int tile_n = lin % n_tiles_n;
   const int tile_m = lin / n_tiles_n;
   const int m0 = tile_m * kBigTile, n0 = tile_n * kBigTile;
-  const int M = m_dev != nullptr ? min(M_cap, *m_dev) : M_cap;  // rows present
-  if (m0 >= M) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 3, wn = wave >> 2;  // 4 wave rows of tokens, 2 of features
@@ -418,16 +421,16 @@ __global__ __launch_bounds__(kBigThreads, 1) void gate_gemm_kernel(GateGemmArgs 
   __builtin_amdgcn_s_setreg((0 << 11) | (23 << 6) | 1, 1);
 
   const int N = g.N, K = g.K;
-  const int nwg = gridDim.x;
-  const int per_xcd = (nwg + 7) / 8;
+  // XCD-contiguous tile ranges over the tiles present (as gemm256_kernel)
+  const int M = g.m_dev != nullptr ? min(g.M, *g.m_dev) : g.M;  // rows present
+  const int tiles = min(g.n_tiles_total, (M + kBigTile - 1) / kBigTile * g.n_tiles_n);
+  const int per_xcd = (tiles + 7) / 8;
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
   const int lin = xcd * per_xcd + slot;
-  if (slot >= per_xcd || lin >= g.n_tiles_total) return;
+  if (slot >= per_xcd || lin >= tiles) return;
   const int tile_n = lin % g.n_tiles_n;
   const int tile_m = lin / g.n_tiles_n;
   const int m0 = tile_m * kBigTile, n0 = tile_n * kBigTile;
-  const int M = g.m_dev != nullptr ? min(g.M, *g.m_dev) : g.M;  // rows present
-  if (m0 >= M) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 3, wn = wave >> 2;
