@@ -55,9 +55,8 @@ def build(verbose: bool = False) -> str:
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
     tmp = LIB + ".tmp"
     # -z defs: an undefined symbol (such as a kernel stub the compiler dropped) fails the link
-    # rocBLAS serves the plain GEMMs of the layer backward
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", "-o", tmp, *objs,
-           f"-L{ROCM}/lib", "-lrocblas", f"-Wl,-rpath,{ROCM}/lib"]
+           f"-Wl,-rpath,{ROCM}/lib"]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -3,6 +3,7 @@
 // validates, carves the caller's workspace and enqueues launches on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <mutex>
 #include <utility>
@@ -656,22 +657,25 @@ constexpr int kColsumParts = 1024;
 
 struct LayerBwdWs {
   uint16_t *z, *uvqk, *d_h, *dy16, *g16, *dz;
-  float *o, *dg, *d_o, *part_cols, *part_gamma, *part_beta, *rab_part;
+  float *o, *dg, *d_o, *part_cols, *part_gamma, *part_beta, *rab_part, *tn_part;
   uint32_t *d_max;
   char *attn;
 };
 
 // z, U|V|Q|K (fp16 [T][n1]), O, dG, dO (fp32 [T][hdv]), the attention scratch, the
-// scaled fp16 dO and its maximum, dY and G in bf16, dZ (bf16 [T][n1]), and the partial
-// column sums of the bias and LayerNorm gradients.
+// scaled fp16 dO and its maximum, dY and G in bf16, dZ (bf16 [T][n1]), the partial
+// column sums of the bias and LayerNorm gradients, and the split partials of the two
+// weight-gradient products (dw2 = dY^T G, dw1 = dZ^T X; one region, used in turn).
 size_t layer_bwd_ws(const hstu_dims_t *d, const hstu_jagged_t *s, LayerBwdWs *w) {
   const size_t T = (size_t)s->total_tokens, hdv = (size_t)d->num_heads * d->dv;
   const size_t n1 = 2 * (size_t)d->num_heads * (d->dqk + d->dv), dm = (size_t)d->d_model;
   const size_t waves = (size_t)norm_gate_bwd_waves((int)T);
+  const size_t tn = std::max(gemm_tn_partial_bytes((int)dm, (int)hdv, (int)T),
+                             gemm_tn_partial_bytes((int)n1, (int)dm, (int)T));
   const size_t sizes[] = {T * n1 * 2, T * n1 * 2, T * hdv * 4, attn_ws_bytes(s, nullptr),
                           T * hdv * 2, kAlign, T * dm * 2, T * hdv * 4, T * hdv * 4,
                           T * hdv * 2, T * n1 * 2, kColsumParts * (n1 > dm ? n1 : dm) * 4,
-                          waves * hdv * 4, waves * hdv * 4, rab_part_bytes(d, s)};
+                          waves * hdv * 4, waves * hdv * 4, rab_part_bytes(d, s), tn};
   size_t off[sizeof(sizes) / sizeof(sizes[0]) + 1] = {0};
   for (size_t i = 0; i < sizeof(sizes) / sizeof(sizes[0]); ++i) off[i + 1] = off[i] + align_up(sizes[i]);
   if (w != nullptr) {
@@ -691,6 +695,7 @@ size_t layer_bwd_ws(const hstu_dims_t *d, const hstu_jagged_t *s, LayerBwdWs *w)
     w->part_gamma = (float *)(b + off[12]);
     w->part_beta = (float *)(b + off[13]);
     w->rab_part = (float *)(b + off[14]);
+    w->tn_part = (float *)(b + off[15]);
   }
   return off[sizeof(sizes) / sizeof(sizes[0])];
 }
@@ -776,7 +781,7 @@ hstu_status_t hstu_layer_bwd(const hstu_dims_t *dims, const hstu_weights_t *w,
   HSTU_TRY(launch_attention(aa, dims->dqk, seq->max_seq_len, cap, sst));
   // f2: dG = dY w2, then the gate and LayerNorm backward, then dw2 = dY^T G, db2
   HSTU_TRY(launch_cast_bf16(d_y, b.dy16, (int64_t)T * dm, sst));
-  HSTU_TRY(blas_gemm_bf16(false, false, T, hdv, dm, b.dy16, dm, w->w2, hdv, b.dg, hdv, 0.0f, sst));
+  HSTU_TRY(launch_gemm_nn_f32(b.dy16, dm, w->w2, hdv, b.dg, T, hdv, dm, sst));
   NormGateBwdArgs ng{};
   ng.o = b.o;
   ng.dg = b.dg;
@@ -795,7 +800,7 @@ hstu_status_t hstu_layer_bwd(const hstu_dims_t *dims, const hstu_weights_t *w,
   ng.T = T;
   ng.hdv = hdv;
   HSTU_TRY(launch_norm_gate_bwd(ng, sst));
-  HSTU_TRY(blas_gemm_bf16(true, false, dm, hdv, T, b.dy16, dm, b.g16, hdv, grads->w2, hdv, 0.0f, sst));
+  HSTU_TRY(launch_gemm_tn_f32(b.dy16, dm, b.g16, hdv, grads->w2, dm, hdv, T, b.tn_part, sst));
   if (grads->b2 != nullptr)
     HSTU_TRY(launch_colsum(d_y, false, T, dm, dm, b.part_cols, kColsumParts, grads->b2, sst));
   const int waves = norm_gate_bwd_waves(T);
@@ -840,8 +845,8 @@ hstu_status_t hstu_layer_bwd(const hstu_dims_t *dims, const hstu_weights_t *w,
   }
   HSTU_TRY(launch_attention_bwd(a, dims->dqk, cap, T, sst));
   // f1: dX = dZ w1, dw1 = dZ^T X, db1
-  HSTU_TRY(blas_gemm_bf16(false, false, T, dm, n1, b.dz, n1, w->w1, dm, d_x, dm, 0.0f, sst));
-  HSTU_TRY(blas_gemm_bf16(true, false, n1, dm, T, b.dz, n1, x, dm, grads->w1, dm, 0.0f, sst));
+  HSTU_TRY(launch_gemm_nn_f32(b.dz, n1, w->w1, dm, d_x, T, dm, n1, sst));
+  HSTU_TRY(launch_gemm_tn_f32(b.dz, n1, x, dm, grads->w1, n1, dm, T, b.tn_part, sst));
   if (grads->b1 != nullptr)
     HSTU_TRY(launch_colsum(b.dz, true, T, n1, n1, b.part_cols, kColsumParts, grads->b1, sst));
 #undef HSTU_TRY

@@ -77,13 +77,6 @@ __device__ __forceinline__ T ld_const(const T *ptr) {
   return *(const __attribute__((address_space(4))) T *)ptr;
 }
 
-// ds_read_b64_tr_b16: transposing 8-byte LDS read (lane layout in the P.V step below)
-__device__ __forceinline__ u32x2 lds_read_tr16(const unsigned char *p) {
-  typedef short s16x4 __attribute__((ext_vector_type(4)));
-  return __builtin_bit_cast(
-      u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)p));
-}
-
 // For thr >= 1, (max(0, ts_q - ts_k) >= thr) holds exactly when ts_k < key_limit(ts_q,
 // thr) over the full int32 range: the difference is taken in 64 bits, and a limit below
 // INT32_MIN (no key passes) clamps to INT32_MIN, which no int32 is below.

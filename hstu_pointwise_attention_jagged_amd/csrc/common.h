@@ -38,6 +38,15 @@ __device__ __forceinline__ f16x8 as_f16x8(const u32x4 &v) {
 }
 
 // Two fp32 -> packed bf16 (round to nearest even; v_cvt_pk_bf16_f32).
+// ds_read_b64_tr_b16, gfx950's transposing 8-byte LDS read: in each group of 16 lanes,
+// lane 4 j + q gives the address of 4 consecutive 16-bit values (columns 4 q .. 4 q + 3
+// of row j of a 4 x 16 block) and lane i receives column i, rows 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const unsigned char *p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(
+      u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)p));
+}
+
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   bf16x2 p = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, p);

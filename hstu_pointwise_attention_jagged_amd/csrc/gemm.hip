@@ -187,67 +187,106 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | (15 << 8) | (7 << 4) | (N & 15));
 }
 
-template <int ACT, int OUT>
-__global__ __launch_bounds__(kBigThreads, 2) void gemm256_kernel(const uint16_t *__restrict__ A,
-                                                                  const uint16_t *__restrict__ W,
-                                                                  const float *__restrict__ bias,
-                                                                  uint16_t *__restrict__ out,
-                                                                  const int32_t *__restrict__ m_dev,
-                                                                  int M_cap, int N, int K, int n_tiles_n,
-                                                                  int n_tiles_total) {
+// Operand layouts: KC, the operand's rows are the output's rows (or columns) and K is
+// contiguous (X [M][K], W [N][K]); KR, the operand's rows are K (X [K][M], W [K][N]).
+// A KC stage is [256 rows][64 k] read with 16-byte reads; a KR stage is the natural
+// [64 k][256 columns] slice, read with the transposing ds_read_b64_tr_b16, whose lane
+// layout is chosen to give the same k order as the 16-byte read, so the two layouts mix.
+template <int LX, int LW, int ACT, int OUT>
+__global__ __launch_bounds__(kBigThreads, 2) void gemm256_kernel(GemmArgs g) {
   constexpr int TM = 64, TN = 128;  // wave tile: tokens x features
   constexpr int MT = TM / 32, NT = TN / 32;
   constexpr int STAGE = kBigTile * kBigBK * 2;  // bytes of one operand stage (32 KB)
   constexpr int SEGS = STAGE / 1024 / (kBigThreads / 64);  // 1 KB segments per wave
-  constexpr int LOADS = 2 * SEGS;                           // buffer loads per thread per stage
+  static_assert(OUT != OUT_F32 || ACT == ACT_NONE, "fp32 output is a plain product");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   unsigned char *xs = smem;                       // [kBigStages][STAGE]
   unsigned char *wsm = smem + kBigStages * STAGE;  // [kBigStages][STAGE]
+  const int N = g.N;
 
   // Workgroups are dealt to the 8 XCDs round-robin; give each XCD a contiguous range of
-  // the tiles present (feature tile fastest) so that the tiles sharing X rows share one
-  // L2.  The range comes from the rows present, which may be fewer than the grid was
-  // sized for: the work then still spreads over every XCD, and the surplus workgroups
-  // (the highest slots) exit.
-  const int M = m_dev != nullptr ? min(M_cap, *m_dev) : M_cap;  // rows present
-  const int tiles = min(n_tiles_total, (M + kBigTile - 1) / kBigTile * n_tiles_n);
-  const int per_xcd = (tiles + 7) / 8;
+  // the units present (K split, then tile; feature tile fastest) so that the tiles
+  // sharing operand panels share one L2.  The range comes from the rows present, which
+  // may be fewer than the grid was sized for: the work then still spreads over every XCD,
+  // and the surplus workgroups (the highest slots) exit.
+  const int M = g.m_dev != nullptr ? min(g.M, *g.m_dev) : g.M;  // rows present
+  const int tiles = min(g.n_tiles_total, (M + kBigTile - 1) / kBigTile * g.n_tiles_n);
+  const int units = tiles * g.splits;
+  const int per_xcd = (units + 7) / 8;
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
   const int lin = xcd * per_xcd + slot;
-  if (slot >= per_xcd || lin >= tiles) return;
-  const int tile_n = lin % n_tiles_n;
-  const int tile_m = lin / n_tiles_n;
-  const int m0 = tile_m * kBigTile, n0 = tile_n * kBigTile;
+  if (slot >= per_xcd || lin >= units) return;
+  const int split = lin / tiles, tl = lin % tiles;
+  const int m0 = (tl / g.n_tiles_n) * kBigTile, n0 = (tl % g.n_tiles_n) * kBigTile;
+  const int kb = split * g.k_split, ke = min(g.K, kb + g.k_split);
+  const int nk = (ke - kb + kBigBK - 1) / kBigBK;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 3, wn = wave >> 2;  // 4 wave rows of tokens, 2 of features
 
-  // Descriptors over this tile's own row panels (256 rows of A from m0, 256 rows of W from
-  // n0), so that every offset below stays under 256 K 2 bytes (the host keeps K <= 2^21)
-  // whatever the number of rows; rows of A past M lie outside the range and read as zero.
-  const __amdgpu_buffer_rsrc_t ar = uniform_rsrc(A + (int64_t)m0 * K, min(kBigTile, M - m0) * K * 2);
-  const __amdgpu_buffer_rsrc_t wr = uniform_rsrc(W + (int64_t)n0 * K, kBigTile * K * 2);
+  // Descriptors.  KC: over the tile's 256-row panel (offsets below 256 ld 2 bytes, ld <=
+  // 2^21), rows past the matrix read as zero.  KR: over the split's K rows from the
+  // tile's first column (offsets below k_split ld 2 bytes <= 2^31), rows past K read as
+  // zero; columns past the matrix read whatever follows and only reach output rows or
+  // columns that are not stored.
+  const __amdgpu_buffer_rsrc_t xr =
+      LX == KC ? uniform_rsrc(g.x + (int64_t)m0 * g.ldx, min(kBigTile, M - m0) * (int)g.ldx * 2)
+               : uniform_rsrc(g.x + (int64_t)kb * g.ldx + m0, (ke - kb) * (int)g.ldx * 2);
+  const __amdgpu_buffer_rsrc_t wr =
+      LW == KC ? uniform_rsrc(g.w + (int64_t)n0 * g.ldw, min(kBigTile, N - n0) * (int)g.ldw * 2)
+               : uniform_rsrc(g.w + (int64_t)kb * g.ldw + n0, (ke - kb) * (int)g.ldw * 2);
+  const int ldx = (int)g.ldx, ldw = (int)g.ldw;
 
-  // Each wave instruction fills 1 KB of LDS = 8 rows x 8 chunks; lane -> (row, chunk)
-  // is fixed by the LDS position, the global chunk is the swizzled one.
-  const int lrow8 = lane / kCPR, lchunk = lane % kCPR;
+  // Each wave instruction fills 1 KB of LDS.  KC: 8 rows x 8 chunks, lane -> (row lane /
+  // 8, chunk lane % 8), the global chunk being the swizzled one.  KR: 2 k rows x 32
+  // chunks, lane -> (k row lane / 32, chunk lane % 32), 16-byte chunks XOR-swizzled by
+  // 4 (k % 4) so that the transposing reads of 32 lanes hit distinct banks.
+  auto issue_op = [&](auto layout, const __amdgpu_buffer_rsrc_t &rs, int ld, unsigned char *dst, int k0,
+                      int j) __attribute__((always_inline)) {
+    constexpr int L = decltype(layout)::value;
+    const int seg = j * 8 + wave;
+    if constexpr (L == KC) {
+      const int r = seg * (64 / kCPR) + lane / kCPR;
+      const int c = (lane % kCPR) ^ ((r >> 1) & 7);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + seg * 1024, 16, (r * ld + kb + k0 + c * 8) * 2, 0, 0, 0);
+    } else {
+      const int kr = seg * 2 + (lane >> 5);
+      const int c = (lane & 31) ^ ((kr & 3) << 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst + seg * 1024, 16, ((k0 + kr) * ld + c * 8) * 2, 0, 0, 0);
+    }
+  };
   // load j of this wave for stage kt: X segment j (j < SEGS) or W segment j - SEGS
   auto issue_one = [&](int kt, int j) {
     const int stage = kt % kBigStages, k0 = kt * kBigBK;
-    const int seg = (j % SEGS) * 8 + wave;   // 8-row segment of the 256-row tile
-    const int r = seg * (64 / kCPR) + lrow8;
-    const int c = lchunk ^ ((r >> 1) & 7);  // global chunk stored at lchunk
-    if (j < SEGS) {
-      const int xoff = (r * K + k0 + c * 8) * 2;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, xs + stage * STAGE + seg * 1024, 16, xoff, 0, 0, 0);
-    } else {
-      const int woff = (r * K + k0 + c * 8) * 2;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, wsm + stage * STAGE + seg * 1024, 16, woff, 0, 0, 0);
-    }
+    if (j < SEGS)
+      issue_op(std::integral_constant<int, LX>{}, xr, ldx, xs + stage * STAGE, k0, j);
+    else
+      issue_op(std::integral_constant<int, LW>{}, wr, ldw, wsm + stage * STAGE, k0, j - SEGS);
   };
-  auto issue = [&](int kt) {
+
+  // Per-lane parts of the fragment reads.  KC: 16-byte read of chunk 2 ks + lane / 32 of
+  // row (block + lane % 32).  KR: two transposing reads; in each 16-lane group lane 4 j + q
+  // names k row 8 (lane / 32) + j (then + 4) at columns 16 ((lane / 16) % 2) + 4 q ..+3 of
+  // the 32-column block, and receives the four k values of column lane % 32: k
+  // 8 (lane / 32) + 0..7 over the two reads, as the 16-byte read gives.
+  const int lrow = lane & 31, lk = lane >> 5;
+  const int tr_j = (lane & 15) >> 2;
+  const int tr_base = (8 * lk + tr_j) * 512 + (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) * 16 + (lane & 1) * 8;
+  auto tr_off = [&](int col_block) { return tr_base + (((col_block >> 3) ^ (tr_j << 2)) << 4); };
+  int xo[MT], wo[NT];
 #pragma unroll
-    for (int j = 0; j < LOADS; ++j) issue_one(kt, j);
+  for (int j = 0; j < MT; ++j) xo[j] = LX == KC ? 0 : tr_off(wm * TM + j * 32);
+#pragma unroll
+  for (int i = 0; i < NT; ++i) wo[i] = LW == KC ? 0 : tr_off(wn * TN + i * 32);
+  auto read_op = [&](auto layout, const unsigned char *st, int row_block, int off, int ks) __attribute__((always_inline)) {
+    constexpr int L = decltype(layout)::value;
+    if constexpr (L == KC) {
+      return as_bf16x8(*reinterpret_cast<const u32x4 *>(st + swz(row_block + lrow, ks * 2 + lk)));
+    } else {
+      const u32x2 lo = lds_read_tr16(st + ks * 16 * 512 + off);
+      const u32x2 hi = lds_read_tr16(st + ks * 16 * 512 + 4 * 512 + off);
+      return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+    }
   };
 
   f32x16 acc[NT][MT];
@@ -256,42 +295,32 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm256_kernel(const uint16_t 
 #pragma unroll
     for (int j = 0; j < MT; ++j) acc[i][j] = f32x16{};
 
-  const int nk = K / kBigBK;
   // prologue: stages 0 .. kBigStages-2 in flight
 #pragma unroll
   for (int kt = 0; kt < kBigStages - 1; ++kt)
-    if (kt < nk) issue(kt);
+    if (kt < nk)
+#pragma unroll
+      for (int j = 0; j < 2 * SEGS; ++j) issue_one(kt, j);
 
-  const int lrow = lane & 31, lk = lane >> 5;
   for (int kt = 0; kt < nk; ++kt) {
-    // stage kt has landed for this wave once at most (stages issued after it) remain
-    if constexpr (kBigStages == 2) {
-      wait_vmcnt<0>();
-    } else {
-      const int ahead = min(nk - 1 - kt, kBigStages - 2);
-      if (ahead >= 2) wait_vmcnt<2 * LOADS>();
-      else if (ahead == 1) wait_vmcnt<LOADS>();
-      else wait_vmcnt<0>();
-    }
+    static_assert(kBigStages == 2, "one stage in flight");
+    wait_vmcnt<0>();  // this wave's loads of stage kt (the only ones in flight)
     // stage kt complete for all waves; stage kt-1 free for reuse.  A bare barrier: the
-    // wait above already covers this wave's direct-to-LDS loads of stage kt, and the
-    // later stages stay in flight.
+    // wait above already covers this wave's direct-to-LDS loads.
     __builtin_amdgcn_s_barrier();
-    const bool more = kt + kBigStages - 1 < nk;
-
+    const bool more = kt + 1 < nk;
     const unsigned char *xst = xs + (kt % kBigStages) * STAGE;
     const unsigned char *wst = wsm + (kt % kBigStages) * STAGE;
     // operand fragments double-buffered in registers: k-step ks+1 is read while the
     // MFMAs of k-step ks run
     bf16x8 wf[2][NT], xf[2][MT];
     auto read_frags = [&](int ks, int set) {
-      const int c = ks * 2 + lk;
 #pragma unroll
       for (int i = 0; i < NT; ++i)
-        wf[set][i] = as_bf16x8(*reinterpret_cast<const u32x4 *>(wst + swz(wn * TN + i * 32 + lrow, c)));
+        wf[set][i] = read_op(std::integral_constant<int, LW>{}, wst, wn * TN + i * 32, wo[i], ks);
 #pragma unroll
       for (int j = 0; j < MT; ++j)
-        xf[set][j] = as_bf16x8(*reinterpret_cast<const u32x4 *>(xst + swz(wm * TM + j * 32 + lrow, c)));
+        xf[set][j] = read_op(std::integral_constant<int, LX>{}, xst, wm * TM + j * 32, xo[j], ks);
     };
     read_frags(0, 0);
 #pragma unroll
@@ -302,7 +331,7 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm256_kernel(const uint16_t 
       // the workgroup on the CU's vector-memory queue at once
       if (ks < 2 && more) {
 #pragma unroll
-        for (int j = ks * (LOADS / 2); j < (ks + 1) * (LOADS / 2); ++j) issue_one(kt + kBigStages - 1, j);
+        for (int j = ks * SEGS; j < (ks + 1) * SEGS; ++j) issue_one(kt + 1, j);
       }
 #pragma unroll
       for (int i = 0; i < NT; ++i)
@@ -313,69 +342,115 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm256_kernel(const uint16_t 
 
   // Epilogue through LDS.  A lane holds token (lane % 32) and features 8g + 4*(lane/32)
   // + 0..3 of each MFMA tile, so direct stores would scatter 8-byte pieces over 32 rows
-  // per instruction; instead the finished 16-bit tile is staged in LDS (free once every
-  // wave is past its last operand read) and written back as whole 512-byte rows.
-  __syncthreads();
+  // per instruction; instead the finished tile is staged in LDS (free once every wave is
+  // past its last operand read) and written back as whole rows, 16-byte chunks past N
+  // skipped.
+  if constexpr (OUT == OUT_F32) {
+    // fp32 rows of 1 KB: the tile goes out in two halves of 128 rows (waves 0, 1, 4, 5
+    // then 2, 3, 6, 7); with splits, split s writes its own [M][N] slice
+    constexpr int kPitch32 = kBigTile * 4 + 16;
+    float *out = reinterpret_cast<float *>(g.out) + (int64_t)split * g.M * N;
 #pragma unroll
-  for (int j = 0; j < MT; ++j) {
-    const int r = wm * TM + j * 32 + lrow;
+    for (int h = 0; h < 2; ++h) {
+      __syncthreads();
+      if ((wm >> 1) == h) {
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
+        for (int j = 0; j < MT; ++j) {
+          const int r = (wm & 1) * TM + j * 32 + lrow;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c = wn * TN + i * 32 + 8 * g + 4 * lk;
-        float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
-        float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-        if (bias != nullptr) {
-          const f32x4 bb = *reinterpret_cast<const f32x4 *>(bias + n0 + c);
-          v0 += bb[0]; v1 += bb[1]; v2 += bb[2]; v3 += bb[3];
+          for (int i = 0; i < NT; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int c = wn * TN + i * 32 + 8 * q + 4 * lk;
+              *reinterpret_cast<f32x4 *>(smem + r * kPitch32 + c * 4) =
+                  f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            }
         }
-        if (ACT == ACT_SILU) {
-          v0 = silu_f32(v0); v1 = silu_f32(v1); v2 = silu_f32(v2); v3 = silu_f32(v3);
-        }
-        const u32x2 pk = OUT == OUT_F16 ? u32x2{pack_f16_sat(v0, v1), pack_f16_sat(v2, v3)}
-                                        : u32x2{pack_bf16(v0, v1), pack_bf16(v2, v3)};
-        *reinterpret_cast<u32x2 *>(smem + r * kOutPitch + c * 2) = pk;
+      }
+      __syncthreads();
+      constexpr int kRowChunks = kBigTile * 4 / 16;
+#pragma unroll
+      for (int it = 0; it < 128 * kRowChunks / kBigThreads; ++it) {
+        const int ch = it * kBigThreads + tid;
+        const int r = ch / kRowChunks, c16 = ch % kRowChunks;
+        const int m = m0 + h * 128 + r, n = n0 + c16 * 4;
+        if (m < M && n < N)
+          *reinterpret_cast<u32x4 *>(out + (int64_t)m * N + n) =
+              *reinterpret_cast<const u32x4 *>(smem + r * kPitch32 + c16 * 16);
       }
     }
-  }
-  __syncthreads();
-  // Each wave instruction stores two whole rows of the tile (64 lanes x 16 bytes).  The
-  // fp16 products (U, V, Q, K: four times the model width) outgrow the last-level cache
-  // and are streamed past it with non-temporal stores, which keeps the operands cached;
-  // the bf16 output (the next layer's input) is stored normally.
-  constexpr int kRowChunks = kBigTile * 2 / 16;
+  } else {
+    uint16_t *out = reinterpret_cast<uint16_t *>(g.out);
+    __syncthreads();
 #pragma unroll
-  for (int it = 0; it < kBigTile * kRowChunks / kBigThreads; ++it) {
-    const int ch = it * kBigThreads + tid;
-    const int r = ch / kRowChunks, c16 = ch % kRowChunks;
-    const u32x4 v = *reinterpret_cast<const u32x4 *>(smem + r * kOutPitch + c16 * 16);
-    u32x4 *dst = reinterpret_cast<u32x4 *>(out + (int64_t)(m0 + r) * N + n0 + c16 * 8);
-    if (m0 + r < M) {
-      if constexpr (OUT == OUT_F16) __builtin_nontemporal_store(v, dst);
-      else *dst = v;
+    for (int j = 0; j < MT; ++j) {
+      const int r = wm * TM + j * 32 + lrow;
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = wn * TN + i * 32 + 8 * q + 4 * lk;
+          float v0 = acc[i][j][4 * q + 0], v1 = acc[i][j][4 * q + 1];
+          float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+          if (g.bias != nullptr && n0 + c < N) {
+            const f32x4 bb = *reinterpret_cast<const f32x4 *>(g.bias + n0 + c);
+            v0 += bb[0]; v1 += bb[1]; v2 += bb[2]; v3 += bb[3];
+          }
+          if (ACT == ACT_SILU) {
+            v0 = silu_f32(v0); v1 = silu_f32(v1); v2 = silu_f32(v2); v3 = silu_f32(v3);
+          }
+          const u32x2 pk = OUT == OUT_F16 ? u32x2{pack_f16_sat(v0, v1), pack_f16_sat(v2, v3)}
+                                          : u32x2{pack_bf16(v0, v1), pack_bf16(v2, v3)};
+          *reinterpret_cast<u32x2 *>(smem + r * kOutPitch + c * 2) = pk;
+        }
+      }
+    }
+    __syncthreads();
+    // Each wave instruction stores two whole rows of the tile (64 lanes x 16 bytes).  The
+    // fp16 products (U, V, Q, K: four times the model width) outgrow the last-level cache
+    // and are streamed past it with non-temporal stores, which keeps the operands cached;
+    // the bf16 output (the next layer's input) is stored normally.
+    constexpr int kRowChunks = kBigTile * 2 / 16;
+#pragma unroll
+    for (int it = 0; it < kBigTile * kRowChunks / kBigThreads; ++it) {
+      const int ch = it * kBigThreads + tid;
+      const int r = ch / kRowChunks, c16 = ch % kRowChunks;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(smem + r * kOutPitch + c16 * 16);
+      u32x4 *dst = reinterpret_cast<u32x4 *>(out + (int64_t)(m0 + r) * N + n0 + c16 * 8);
+      if (m0 + r < M && n0 + c16 * 8 < N) {
+        if constexpr (OUT == OUT_F16) __builtin_nontemporal_store(v, dst);
+        else *dst = v;
+      }
     }
   }
 }
 
-template <int ACT, int OUT>
-hipError_t launch_big(const uint16_t *A, const uint16_t *W, const float *bias, uint16_t *out,
-                      int M, int N, int K, hipStream_t stream, const int32_t *m_dev) {
-  const int tn = N / kBigTile;
-  const int tm = (M + kBigTile - 1) / kBigTile;
-  const int total = tm * tn;
-  const int grid = (total + 7) / 8 * 8;
+// out[i] = sum over s (in order) of part[s][i], n a multiple of 4
+__global__ __launch_bounds__(256) void sum_splits_kernel(const float *__restrict__ part, int splits,
+                                                         int64_t n, float *__restrict__ out) {
+  const int64_t n4 = n / 4;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    f32x4 acc = reinterpret_cast<const f32x4 *>(part)[i];
+    for (int s = 1; s < splits; ++s) acc += reinterpret_cast<const f32x4 *>(part + (int64_t)s * n)[i];
+    reinterpret_cast<f32x4 *>(out)[i] = acc;
+  }
+}
+
+template <int LX, int LW, int ACT, int OUT>
+hipError_t launch_big(const GemmArgs &a, hipStream_t stream) {
+  const int units = a.n_tiles_total * a.splits;
+  const int grid = (units + 7) / 8 * 8;
   // operand stages (2 operands each), reused for the output tile in the epilogue
-  const size_t lds = std::max(2 * (size_t)kBigStages * kBigTile * kBigBK * 2, (size_t)kBigTile * kOutPitch);
+  const size_t lds = std::max(2 * (size_t)kBigStages * kBigTile * kBigBK * 2,
+                              OUT == OUT_F32 ? (size_t)128 * (kBigTile * 4 + 16) : (size_t)kBigTile * kOutPitch);
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)gemm256_kernel<ACT, OUT>,
+    hipError_t e = hipFuncSetAttribute((const void *)gemm256_kernel<LX, LW, ACT, OUT>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  gemm256_kernel<ACT, OUT><<<dim3(grid), dim3(kBigThreads), lds, stream>>>(A, W, bias, out, m_dev,
-                                                                           M, N, K, tn, total);
+  gemm256_kernel<LX, LW, ACT, OUT><<<dim3(grid), dim3(kBigThreads), lds, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -682,22 +757,103 @@ hipError_t launch_gemm(const uint16_t *A, const uint16_t *W, const float *bias, 
   if (K > kGemmMaxK) return hipErrorInvalidValue;  // 32-bit offsets within a 256-row panel
   const bool big = (N % kBigTile) == 0 && M >= kBigTile;
   const bool wide = (N % 128) == 0;
+  GemmArgs a{};
+  a.x = A;
+  a.ldx = K;
+  a.w = W;
+  a.ldw = K;
+  a.bias = bias;
+  a.out = out;
+  a.m_dev = m_dev;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.k_split = K;
+  a.splits = 1;
+  a.n_tiles_n = N / kBigTile;
+  a.n_tiles_total = (M + kBigTile - 1) / kBigTile * a.n_tiles_n;
   if (act == ACT_SILU && out_type == OUT_F16) {
-    if (big) return launch_big<ACT_SILU, OUT_F16>(A, W, bias, out, M, N, K, stream, m_dev);
+    if (big) return launch_big<KC, KC, ACT_SILU, OUT_F16>(a, stream);
     return wide ? launch_tile<128, 128, ACT_SILU, OUT_F16>(A, W, bias, out, M, N, K, stream, m_dev)
                 : launch_tile<128, 64, ACT_SILU, OUT_F16>(A, W, bias, out, M, N, K, stream, m_dev);
   }
   if (act == ACT_NONE && out_type == OUT_F16) {  // pre-activations (the backward's recompute)
-    if (big) return launch_big<ACT_NONE, OUT_F16>(A, W, bias, out, M, N, K, stream, m_dev);
+    if (big) return launch_big<KC, KC, ACT_NONE, OUT_F16>(a, stream);
     return wide ? launch_tile<128, 128, ACT_NONE, OUT_F16>(A, W, bias, out, M, N, K, stream, m_dev)
                 : launch_tile<128, 64, ACT_NONE, OUT_F16>(A, W, bias, out, M, N, K, stream, m_dev);
   }
   if (act == ACT_NONE && out_type == OUT_BF16) {
-    if (big) return launch_big<ACT_NONE, OUT_BF16>(A, W, bias, out, M, N, K, stream, m_dev);
+    if (big) return launch_big<KC, KC, ACT_NONE, OUT_BF16>(a, stream);
     return wide ? launch_tile<128, 128, ACT_NONE, OUT_BF16>(A, W, bias, out, M, N, K, stream, m_dev)
                 : launch_tile<128, 64, ACT_NONE, OUT_BF16>(A, W, bias, out, M, N, K, stream, m_dev);
   }
   return hipErrorInvalidValue;
+}
+
+// Splits of the reduction for C = X^T W over K = T tokens: enough (tile, split) units to
+// fill the GPU twice over, each split a multiple of 64 rows and at least 512 rows long.
+static int tn_k_split(int M, int N, int K) {
+  const int tiles = ((M + kBigTile - 1) / kBigTile) * ((N + kBigTile - 1) / kBigTile);
+  int splits = std::max(1, 512 / tiles);
+  int ks = (K + splits - 1) / splits;
+  ks = std::max(512, (ks + kBigBK - 1) / kBigBK * kBigBK);
+  return ks;
+}
+
+size_t gemm_tn_partial_bytes(int M, int N, int K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  const int ks = tn_k_split(M, N, K);
+  const int splits = (K + ks - 1) / ks;
+  return splits > 1 ? (size_t)splits * M * N * sizeof(float) : 0;
+}
+
+hipError_t launch_gemm_nn_f32(const uint16_t *X, int64_t ldx, const uint16_t *W, int64_t ldw,
+                              float *out, int M, int N, int K, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (K <= 0 || K % kBigBK != 0 || N % 64 != 0 || ldx > kGemmMaxK || ldx < K || ldw < N ||
+      (int64_t)K * ldw * 2 >= ((int64_t)1 << 31))
+    return hipErrorInvalidValue;
+  GemmArgs a{};
+  a.x = X;
+  a.ldx = ldx;
+  a.w = W;
+  a.ldw = ldw;
+  a.out = out;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.k_split = K;
+  a.splits = 1;
+  a.n_tiles_n = (N + kBigTile - 1) / kBigTile;
+  a.n_tiles_total = (M + kBigTile - 1) / kBigTile * a.n_tiles_n;
+  return launch_big<KC, KR, ACT_NONE, OUT_F32>(a, stream);
+}
+
+hipError_t launch_gemm_tn_f32(const uint16_t *X, int64_t ldx, const uint16_t *W, int64_t ldw,
+                              float *out, int M, int N, int K, float *partial, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (K <= 0 || N % 64 != 0 || M % 4 != 0 || ldx < M || ldw < N) return hipErrorInvalidValue;
+  GemmArgs a{};
+  a.x = X;
+  a.ldx = ldx;
+  a.w = W;
+  a.ldw = ldw;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.k_split = tn_k_split(M, N, K);
+  a.splits = (K + a.k_split - 1) / a.k_split;
+  if ((int64_t)a.k_split * std::max(ldx, ldw) * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  if (a.splits > 1 && partial == nullptr) return hipErrorInvalidValue;
+  a.out = a.splits > 1 ? (void *)partial : (void *)out;
+  a.n_tiles_n = (N + kBigTile - 1) / kBigTile;
+  a.n_tiles_total = (M + kBigTile - 1) / kBigTile * a.n_tiles_n;
+  hipError_t e = launch_big<KR, KR, ACT_NONE, OUT_F32>(a, stream);
+  if (e != hipSuccess || a.splits == 1) return e;
+  const int64_t n = (int64_t)M * N;
+  const int blocks = (int)std::min<int64_t>((n / 4 + 255) / 256, 4096);
+  sum_splits_kernel<<<blocks, 256, 0, stream>>>(partial, a.splits, n, out);
+  return hipGetLastError();
 }
 
 }  // namespace hstu

@@ -8,7 +8,27 @@ namespace hstu {
 
 enum Act { ACT_NONE = 0, ACT_SILU = 1 };
 
-enum OutType { OUT_BF16 = 0, OUT_F16 = 1 };
+enum OutType { OUT_BF16 = 0, OUT_F16 = 1, OUT_F32 = 2 };
+
+// Operand layouts of the 256 x 256 GEMM: KC, rows are output rows (or columns) with K
+// contiguous; KR, rows are K.
+enum Layout { KC = 0, KR = 1 };
+
+// C[M][N] = sum_k X(m, k) W(n, k) (+ bias[n], activation): X(m, k) = x[m ldx + k] (KC) or
+// x[k ldx + m] (KR), likewise W with ldw.  With splits > 1, split s sums k in
+// [s k_split, (s + 1) k_split) into its own [M][N] fp32 slice of out.
+struct GemmArgs {
+  const uint16_t *x;
+  int64_t ldx;
+  const uint16_t *w;
+  int64_t ldw;
+  const float *bias;        // [N] or nullptr
+  void *out;
+  const int32_t *m_dev;     // (device) rows present, or nullptr
+  int M, N, K;
+  int k_split, splits;
+  int n_tiles_n, n_tiles_total;
+};
 
 // Largest reduction width of launch_gemm: a 256-row operand panel (256 K bf16 values)
 // stays addressable with 32-bit byte offsets.
@@ -21,6 +41,17 @@ constexpr int kGemmMaxK = 1 << 21;
 hipError_t launch_gemm(const uint16_t *A, const uint16_t *W, const float *bias, uint16_t *out,
                        int M, int N, int K, Act act, OutType out_type, hipStream_t stream,
                        const int32_t *m_dev = nullptr);
+
+// Backward products with fp32 output, bf16 operands, fixed summation order:
+// NN  out[M][N] = X[M][K] . W[K][N]     (X rows of ldx, W rows of ldw; K % 64 == 0)
+// TN  out[M][N] = X[K][M]^T . W[K][N]   (the reduction over K = tokens runs in splits
+//     whose [M][N] partials, in `partial`, are then added in split order; `partial`
+//     holds gemm_tn_partial_bytes(M, N, K) bytes, 0 when one split suffices)
+hipError_t launch_gemm_nn_f32(const uint16_t *X, int64_t ldx, const uint16_t *W, int64_t ldw,
+                              float *out, int M, int N, int K, hipStream_t stream);
+hipError_t launch_gemm_tn_f32(const uint16_t *X, int64_t ldx, const uint16_t *W, int64_t ldw,
+                              float *out, int M, int N, int K, float *partial, hipStream_t stream);
+size_t gemm_tn_partial_bytes(int M, int N, int K);
 
 // f2 with the LayerNorm and the U gate of equation 3 formed in its operand staging:
 // out[M][N] = G w^T + bias, G = ((o - mu) rstd gamma + beta) U per row, where o is given
@@ -143,11 +174,6 @@ hipError_t launch_colsum(const void *a, bool bf16, int rows, int cols, int64_t s
                          float *partial, int n_parts, float *out, hipStream_t stream);
 hipError_t launch_sum_parts(const float *partial, int n_parts, int cols, float *out,
                             hipStream_t stream);
-// Row-major C[M][N] (fp32, pitch ldc) = op(A) op(B) + beta C with bf16 A, B (rocBLAS):
-// op(A) = A [M][K] (pitch lda), or A^T with A [K][M] when a_trans; likewise B.
-hipError_t blas_gemm_bf16(bool a_trans, bool b_trans, int M, int N, int K, const uint16_t *A,
-                          int64_t lda, const uint16_t *B, int64_t ldb, float *C, int64_t ldc,
-                          float beta, hipStream_t stream);
 
 // dQ, dK, dV for every row: the scaled fp16 copy of d_out, then two kernels over the
 // schedule's (sequence, 128-row tile) list.  stat must be filled when ts is set.

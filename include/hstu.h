@@ -39,11 +39,9 @@
  *    time gap is taken over the full int32 range without overflow.
  *  - Ownership: the caller owns every buffer.  The library allocates no device memory
  *    and keeps no pointer after a call returns; scratch memory comes from the caller's
- *    workspace.  One exception: hstu_layer_bwd runs its plain GEMMs through rocBLAS,
- *    which on the first such call on a device creates a handle with its own device
- *    workspace, kept until the process ends.  Calls are asynchronous on `stream` (a
- *    hipStream_t, NULL = default stream) and never synchronise, except
- *    hstu_validate_jagged.
+ *    workspace (hstu_attn_fwd_noalloc: from a fixed static array, see there).  Calls are
+ *    asynchronous on `stream` (a hipStream_t, NULL = default stream) and never
+ *    synchronise, except hstu_validate_jagged.
  *  - Errors: host-checkable problems return a status before anything is launched and
  *    leave all outputs untouched; a failed launch returns HSTU_ERR_HIP and the HIP
  *    error code is available from hstu_last_hip_error().  No exception crosses the ABI.
