@@ -31,8 +31,9 @@ sys.path.insert(0, ROOT)
 METRIC = "HSTU jagged attn+layer fwd TFLOP/s (bf16) and % MFMA peak at N=8192, 1 GPU"
 PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 MFMA
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attention_traffic.json")
-ATTN_SRC = os.path.join(ROOT, "hstu_pointwise_attention_jagged_amd", "csrc", "attention.hip")
+PEAK_FLOP_PER_CLOCK = 256 * 4 * 1024  # CUs x SIMDs x dense fp16/bf16 MFMA FLOP per clock
+COUNTER_RECORD = os.path.join(ROOT, "profiles", "layer_counters.json")
+CSRC = os.path.join(ROOT, "hstu_pointwise_attention_jagged_amd", "csrc")
 
 
 def log(msg):
@@ -57,56 +58,120 @@ def file_sha(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def traffic_record():
-    """HBM bytes per attention launch from committed counter runs, if still current."""
+def _kernel_sources_sha():
+    """sha256 of the kernel sources a counter record describes."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def counter_record():
+    """The committed counter record, if the kernel sources are unchanged since it was taken."""
     try:
-        with open(TRAFFIC_RECORD) as f:
+        with open(COUNTER_RECORD) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("attention_hip_sha256") != file_sha(ATTN_SRC):
-        return None  # kernel changed since the counters were taken
-    return rec.get("bytes_per_launch")
+    if rec.get("kernel_sources_sha256") != _kernel_sources_sha():
+        return None  # kernels changed since the counters were taken
+    return rec
 
 
-def _counter_kib(db, kernel_substr):
-    """Per-dispatch counter values (KiB) of the kernels whose name contains kernel_substr."""
-    import sqlite3
-    con = sqlite3.connect(db)
-    vals = [v for name, v in con.execute("select name, counter_value from pmc_events")
-            if kernel_substr in name]
-    con.close()
-    return vals
+# kernels of one c2 layer: (label, name substring, useful FLOPs, algorithmic HBM bytes)
+def _layer_kernels():
+    T, d, H, dh = 65536, 1024, 8, 128
+    n1 = 2 * H * 2 * dh
+    f1, att, f2 = useful_flops([8192] * 8, d, H, dh, dh)
+    return [
+        ("f1 GEMM + SiLU", "gemm256_kernel<0, 0, 1, 1>", f1, 2 * (T * d + n1 * d + T * n1)),
+        ("attention", "attn_kernel<128, 0, 4", att, 2 * 3 * T * H * dh + 2 * T * H * dh + 8 * T * H),
+        ("f2 GEMM with LayerNorm + gate", "gate_gemm_kernel", f2,
+         2 * 2 * T * H * dh + 8 * T * H + 2 * d * H * dh + 2 * T * d),
+        ("f2 operand preparation", "gate_prep_kernel", 0, 2 * 2 * d * H * dh),
+    ]
 
 
-def write_traffic_record(d, copy_bytes):
-    """HBM bytes per attention launch, from FETCH_SIZE / WRITE_SIZE scaled by a plain copy."""
-    att_fetch = _counter_kib(os.path.join(d, "pmc_fetch", "pmc_results.db"), "attn_kernel")
-    att_write = _counter_kib(os.path.join(d, "pmc_write", "pmc_results.db"), "attn_kernel")
-    cp_fetch = _counter_kib(os.path.join(d, "pmc_cfetch", "pmc_results.db"), "copyBuffer")
-    cp_write = _counter_kib(os.path.join(d, "pmc_cwrite", "pmc_results.db"), "copyBuffer")
-    fetch_scale = copy_bytes / (1024.0 * sum(cp_fetch) / len(cp_fetch))
-    write_scale = copy_bytes / (1024.0 * sum(cp_write) / len(cp_write))
-    fetch_b = 1024.0 * sum(att_fetch) / len(att_fetch) * fetch_scale
-    write_b = 1024.0 * sum(att_write) / len(att_write) * write_scale
-    rec = {
-        "kernel": "attn_kernel (8 x 8192 tokens, 8 heads x 128, causal, rab pos+time)",
-        "attention_hip_sha256": file_sha(ATTN_SRC),
-        "fetch_kib_per_launch": sum(att_fetch) / len(att_fetch),
-        "write_kib_per_launch": sum(att_write) / len(att_write),
-        "copy_bytes": copy_bytes,
-        "copy_fetch_kib": sum(cp_fetch) / len(cp_fetch),
-        "copy_write_kib": sum(cp_write) / len(cp_write),
-        "fetch_scale": fetch_scale,
-        "write_scale": write_scale,
-        "fetch_bytes_per_launch": fetch_b,
-        "write_bytes_per_launch": write_b,
-        "bytes_per_launch": fetch_b + write_b,
-    }
-    with open(TRAFFIC_RECORD, "w") as f:
-        json.dump(rec, f, indent=1)
+def _read_pmc(path):
+    """{kernel name: {counter: [values per dispatch]}, ...} and durations (ns) per name."""
+    import csv
+    vals, durs = {}, {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            vals.setdefault(name, {}).setdefault(r["Counter_Name"], {})[r["Dispatch_Id"]] = float(r["Counter_Value"])
+            durs.setdefault(name, {})[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    avg = lambda d: sum(d.values()) / max(len(d), 1)
+    return ({n: {c: avg(v) for c, v in cs.items()} for n, cs in vals.items()},
+            {n: avg(d) for n, d in durs.items()})
+
+
+def write_counter_record(d, copy_bytes):
+    """Per-kernel counter summary of one c2 layer from the rocprofv3 --pmc passes under d:
+    sq1, sq2 (SQ and GRBM counters), fetch, write (FETCH_SIZE, WRITE_SIZE) over
+    `bench.py --layers 1 --steps 1 --warmup 1 --only-step`, and cfetch, cwrite (the same
+    two counters over `bench.py --copy-bytes copy_bytes`), all in CSV."""
+    runs = {k: _read_pmc(os.path.join(d, k, "pmc_counter_collection.csv"))
+            for k in ("sq1", "sq2", "fetch", "write", "cfetch", "cwrite")}
+    copy = lambda k, c: [v[c] for n, v in runs[k][0].items() if "copyBuffer" in n][0]
+    fetch_scale = copy_bytes / (1024.0 * copy("cfetch", "FETCH_SIZE"))
+    write_scale = copy_bytes / (1024.0 * copy("cwrite", "WRITE_SIZE"))
+    simds = 256 * 4
+    kernels = {}
+    for label, sub, flops, alg in _layer_kernels():
+        def pick(k, c):
+            for n, v in runs[k][0].items():
+                if sub in n and c in v:
+                    return v[c], runs[k][1][n]
+            return None, None
+        gui, dur = pick("sq1", "GRBM_GUI_ACTIVE")
+        if gui is None:
+            continue
+        xcds = 8  # GRBM_GUI_ACTIVE adds up the 8 XCDs' busy cycles
+        clk = gui / xcds / dur  # GHz
+        cyc = dur * clk  # shader cycles over the dispatch
+        g = lambda k, c: pick(k, c)[0] or 0.0
+        mfma = g("sq1", "SQ_INSTS_MFMA")
+        rec = {"ms": dur / 1e6, "clock_ghz": clk,
+               "mfma_busy_frac": g("sq1", "SQ_VALU_MFMA_BUSY_CYCLES") / (simds * cyc),
+               "valu_busy_frac": 4 * g("sq1", "SQ_ACTIVE_INST_VALU") / (simds * cyc),
+               "sq_busy_frac": g("sq1", "SQ_BUSY_CYCLES") / (32 * cyc),
+               "mfma_insts": mfma,
+               "valu_per_mfma": (g("sq2", "SQ_INSTS_VALU") - mfma) / mfma if mfma else None,
+               "trans_per_mfma": g("sq2", "SQ_INSTS_VALU_TRANS_F32") / mfma if mfma else None,
+               "salu_per_mfma": g("sq2", "SQ_INSTS_SALU") / mfma if mfma else None,
+               "lds_per_mfma": g("sq2", "SQ_INSTS_LDS") / mfma if mfma else None,
+               "lds_bank_conflict_frac": (g("sq2", "SQ_LDS_BANK_CONFLICT") / g("sq2", "SQ_ACTIVE_INST_LDS")
+                                          if g("sq2", "SQ_ACTIVE_INST_LDS") else None),
+               "fetch_bytes": 1024.0 * g("fetch", "FETCH_SIZE") * fetch_scale,
+               "write_bytes": 1024.0 * g("write", "WRITE_SIZE") * write_scale,
+               "algorithmic_bytes": alg, "useful_flops": flops}
+        rec["hbm_gbs"] = (rec["fetch_bytes"] + rec["write_bytes"]) / dur
+        rec["tflops"] = flops / dur / 1e3 if flops else None
+        rec["peak_tflops_at_clock"] = PEAK_FLOP_PER_CLOCK * clk / 1e3
+        kernels[label] = rec
+    out = {"workload": "one layer, 8 x 8192 tokens, d=1024, 8 heads x 128, causal, rab pos+time",
+           "kernel_sources_sha256": _kernel_sources_sha(), "copy_bytes": copy_bytes,
+           "fetch_scale": fetch_scale, "write_scale": write_scale, "kernels": kernels}
+    with open(COUNTER_RECORD, "w") as f:
+        json.dump(out, f, indent=1)
         f.write("\n")
-    log(f"wrote {TRAFFIC_RECORD}: {rec['bytes_per_launch'] / 1e6:.1f} MB per launch")
+    log(f"wrote {COUNTER_RECORD}")
+    hdr = ("| kernel | ms | clock GHz | TFLOP/s | % of peak at that clock | MFMA busy | VALU busy | "
+           "VALU / MFMA | trans / MFMA | SALU / MFMA | LDS / MFMA | HBM fetch + write MB | "
+           "algorithmic MB | HBM GB/s |")
+    print(hdr)
+    print("|" + "---|" * 14)
+    for k, r in kernels.items():
+        f = lambda x, p=2: "-" if x is None else f"{x:.{p}f}"
+        pct = None if not r["tflops"] else 100 * r["tflops"] / r["peak_tflops_at_clock"]
+        print(f"| {k} | {r['ms']:.4f} | {r['clock_ghz']:.2f} | {f(r['tflops'], 0)} | {f(pct, 1)} | "
+              f"{100 * r['mfma_busy_frac']:.1f}% | {100 * r['valu_busy_frac']:.1f}% | {f(r['valu_per_mfma'])} | "
+              f"{f(r['trans_per_mfma'])} | {f(r['salu_per_mfma'])} | {f(r['lds_per_mfma'])} | "
+              f"{(r['fetch_bytes'] + r['write_bytes']) / 1e6:.0f} | {r['algorithmic_bytes'] / 1e6:.0f} | "
+              f"{r['hbm_gbs']:.0f} |")
 
 
 def host_info():
@@ -546,14 +611,12 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run 4 device-to-device copies of this many bytes (counter "
                          "calibration for HBM traffic) and exit")
-    ap.add_argument("--traffic-record", metavar="DIR", default=None,
-                    help="only write profiles/attention_traffic.json from the rocprofv3 counter "
-                         "databases DIR/{pmc_fetch,pmc_write,pmc_cfetch,pmc_cwrite}/pmc_results.db "
-                         "(attention FETCH_SIZE / WRITE_SIZE, then the same counters over a "
-                         "--copy-bytes run) and exit")
+    ap.add_argument("--counter-record", metavar="DIR", default=None,
+                    help="only write profiles/layer_counters.json (and print its table) from the "
+                         "rocprofv3 --pmc CSV passes DIR/{sq1,sq2,fetch,write,cfetch,cwrite} and exit")
     args = ap.parse_args()
-    if args.traffic_record:
-        write_traffic_record(args.traffic_record, args.copy_bytes or (1 << 30))
+    if args.counter_record:
+        write_counter_record(args.counter_record, args.copy_bytes or (1 << 30))
         return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); the jagged batch would "
@@ -619,6 +682,7 @@ def main():
     elapsed = time.perf_counter() - t0
     ops.profile_enable(False)
     kern = ops.profile_collect()
+    clock_ghz = ops.profile_clock_ghz()  # shader clock during the last attention launch
     ops.profile_reset()
 
     lengths = w.seq.lengths.tolist()
@@ -631,7 +695,9 @@ def main():
     att_avg_ms = att_ms / max(att_n, 1)
     achieved = att / (att_avg_ms * 1e-3) / 1e12
     per_kernel = {k: round(v[0] / max(v[1], 1), 4) for k, v in kern.items()}
-    traffic = traffic_record()
+    rec = counter_record()
+    att_rec = (rec or {}).get("kernels", {}).get("attention")
+    traffic = att_rec["fetch_bytes"] + att_rec["write_bytes"] if att_rec else None
     log(f"step {ms:.2f} ms, {tflops:.1f} TFLOP/s; per-kernel avg ms {per_kernel}")
 
     out = {
@@ -658,7 +724,14 @@ def main():
                      "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
                      "traffic": traffic,
-                     "algorithmic_flops_per_launch": att, "avg_launch_ms": round(att_avg_ms, 4)},
+                     "algorithmic_flops_per_launch": att, "avg_launch_ms": round(att_avg_ms, 4),
+                     # the same peak at the shader clock measured during the timed
+                     # attention launches (core-clock against real-time counter in the
+                     # kernel; 256 CUs x 4 SIMDs x 1024 FLOP per clock), and the fraction of it
+                     "clock_ghz_measured": round(clock_ghz, 3) if clock_ghz else None,
+                     "peak_at_measured_clock": round(PEAK_FLOP_PER_CLOCK * clock_ghz / 1e3, 1) if clock_ghz else None,
+                     "frac_at_measured_clock": (round(achieved / (PEAK_FLOP_PER_CLOCK * clock_ghz / 1e3), 4)
+                                                if clock_ghz else None)},
         "cpu_baseline": None,
         "host": platform.node(),
     }

@@ -98,6 +98,7 @@ EXPORTS = {
     "hstu_profile_reset": (None, []),
     "hstu_profile_collect": (c_int32, [ctypes.POINTER(c_double), ctypes.POINTER(c_int64)]),
     "hstu_kernel_name": (ctypes.c_char_p, [ctypes.c_int]),
+    "hstu_profile_clock_ghz": (c_int32, [ctypes.POINTER(c_double)]),
 }
 
 _LIB = None

@@ -24,6 +24,7 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // ---------------------------------------------------------------- profiling ---------
+uint64_t *clock_samples();  // below: this device's copy of the clock-sample array
 constexpr int kNumKernels = 5;
 const char *kKernelNames[kNumKernels] = {"schedule", "f1_gemm_silu", "attention", "f2_prep",
                                          "f2_gemm"};
@@ -68,6 +69,11 @@ hipError_t timed(int id, hipStream_t stream, F &&launch) {
     g_prof_records.push_back({id, a, b});
   }
   return err;
+}
+
+bool profiling() {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  return g_prof_on;
 }
 
 hstu_status_t hip_fail(hipError_t e) {
@@ -273,7 +279,9 @@ hstu_status_t run_layer(const hstu_dims_t *d, const hstu_weights_t *w, const hst
   });
   if (e != hipSuccess) return hip_fail(e);
   const int64_t cap = attn_work_capacity(s->batch, T);
-  e = timed(2, st, [&] { return launch_attention(aa, d->dqk, s->max_seq_len, cap, st); });
+  AttnArgs at = aa;
+  if (profiling()) at.clk = clock_samples();  // lifetime clocks of the first workgroups
+  e = timed(2, st, [&] { return launch_attention(at, d->dqk, s->max_seq_len, cap, st); });
   if (e != hipSuccess) return hip_fail(e);
   GateGemmArgs ga{};
   ga.w = lw.w2h;
@@ -863,6 +871,29 @@ constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
 
 static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
+// Clock samples of the attention kernel while profiling (kClockSlots pairs per GPU).
+static __device__ __align__(256) uint64_t clk_samples[2 * kClockSlots];
+
+namespace {
+
+std::mutex g_clk_mu;
+uint64_t *g_clk_ptr[64] = {};
+
+// This device's copy of clk_samples (its address taken once per device), or nullptr.
+uint64_t *clock_samples() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(g_clk_mu);
+  if (g_clk_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(clk_samples)) != hipSuccess) return nullptr;
+    g_clk_ptr[dev] = (uint64_t *)p;
+  }
+  return g_clk_ptr[dev];
+}
+
+}  // namespace
+
 namespace {
 
 // Host checks of an attention call; on success max_prefix is the prefix's longest length.
@@ -1074,6 +1105,7 @@ void hstu_profile_enable(int on) {
 }
 
 void hstu_profile_reset(void) {
+  if (uint64_t *p = clock_samples()) (void)hipMemset(p, 0, 2 * kClockSlots * sizeof(uint64_t));
   std::lock_guard<std::mutex> lk(g_prof_mu);
   for (auto &r : g_prof_records) {
     g_event_pool.push_back(r.start);
@@ -1097,6 +1129,23 @@ hstu_status_t hstu_profile_collect(double *total_ms, int64_t *launches) {
     total_ms[r.id] += ms;
     launches[r.id] += 1;
   }
+  return HSTU_OK;
+}
+
+hstu_status_t hstu_profile_clock_ghz(double *ghz) {
+  if (ghz == nullptr) return HSTU_ERR_INVALID_ARG;
+  *ghz = 0.0;
+  uint64_t *p = clock_samples();
+  if (p == nullptr) return HSTU_ERR_HIP;
+  uint64_t h[2 * kClockSlots];
+  hipError_t e = hipMemcpy(h, p, sizeof(h), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e);
+  double core = 0.0, real = 0.0;
+  for (int i = 0; i < kClockSlots; ++i) {
+    core += (double)h[2 * i];
+    real += (double)h[2 * i + 1];
+  }
+  if (real > 0.0) *ghz = core / real * 0.1;  // the real-time counter runs at 100 MHz
   return HSTU_OK;
 }
 

@@ -173,6 +173,11 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
 
   const int item = blockIdx.x;
   if (item >= ld_const(p.n_work)) return;
+  uint64_t clk0 = 0, rt0 = 0;  // lifetime clocks, when profiling
+  if (p.clk != nullptr) {
+    clk0 = __builtin_amdgcn_s_memtime();
+    rt0 = __builtin_amdgcn_s_memrealtime();
+  }
   // MODE.FP16_OVFL: an fp16 result that overflows clamps to +-65504 instead of becoming
   // infinite.  The weights A are packed to fp16 in the scaled domain (A / -ln 2), so a
   // score whose SiLU exceeds 65504 ln 2 (about 45403) contributes that value instead of
@@ -690,6 +695,11 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
         }
       if (half == 0) p.stats[(int64_t)(s0 + qi) * p.num_heads + h] = float2{mean, var};
     }
+  }
+  if (p.clk != nullptr && item < kClockSlots && threadIdx.x == 0) {
+    const uint64_t clk1 = __builtin_amdgcn_s_memtime(), rt1 = __builtin_amdgcn_s_memrealtime();
+    p.clk[2 * item] = clk1 - clk0;
+    p.clk[2 * item + 1] = rt1 - rt0;
   }
 }
 

@@ -210,14 +210,31 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm256_kernel(GemmArgs g) {
   // may be fewer than the grid was sized for: the work then still spreads over every XCD,
   // and the surplus workgroups (the highest slots) exit.
   const int M = g.m_dev != nullptr ? min(g.M, *g.m_dev) : g.M;  // rows present
-  const int tiles = min(g.n_tiles_total, (M + kBigTile - 1) / kBigTile * g.n_tiles_n);
-  const int units = tiles * g.splits;
-  const int per_xcd = (units + 7) / 8;
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
-  const int lin = xcd * per_xcd + slot;
-  if (slot >= per_xcd || lin >= units) return;
-  const int split = lin / tiles, tl = lin % tiles;
-  const int m0 = (tl / g.n_tiles_n) * kBigTile, n0 = (tl % g.n_tiles_n) * kBigTile;
+  int split = 0, m0, n0;
+  if (g.splits == 1) {
+    // XCD x owns feature tiles [x % xn, +1) x nb and row panels [x / xn, +1) x mh (feature
+    // tile fastest): the W panels an XCD uses stay in its L2 while the row panels stream
+    // past, each read by xn XCDs
+    const int xn = g.xcd_n, nb = g.n_tiles_n / xn;
+    const int tm = (M + kBigTile - 1) / kBigTile;
+    const int mh = (tm + 8 / xn - 1) / (8 / xn);
+    const int m_lo = (xcd / xn) * mh, count = (min(tm, m_lo + mh) - m_lo) * nb;
+    if (slot >= count) return;
+    m0 = (m_lo + slot / nb) * kBigTile;
+    n0 = ((xcd % xn) * nb + slot % nb) * kBigTile;
+  } else {
+    // splits: each XCD a contiguous range of (split, tile) units, tile fastest
+    const int tiles = g.n_tiles_total;
+    const int units = tiles * g.splits;
+    const int per_xcd = (units + 7) / 8;
+    const int lin = xcd * per_xcd + slot;
+    if (slot >= per_xcd || lin >= units) return;
+    split = lin / tiles;
+    const int tl = lin % tiles;
+    m0 = (tl / g.n_tiles_n) * kBigTile;
+    n0 = (tl % g.n_tiles_n) * kBigTile;
+  }
   const int kb = split * g.k_split, ke = min(g.K, kb + g.k_split);
   const int nk = (ke - kb + kBigBK - 1) / kBigBK;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -436,10 +453,24 @@ __global__ __launch_bounds__(256) void sum_splits_kernel(const float *__restrict
   }
 }
 
+// XCDs along the feature tiles: the fewest (1, 2, 4 or 8, dividing the feature tile
+// count) that keep each XCD's W panels within 2 MB of its 4 MB L2.
+static int xcd_split_n(int n_tiles_n, int64_t panel_bytes) {
+  for (int xn = 1; xn < 8; xn *= 2)
+    if (n_tiles_n % xn == 0 && (int64_t)(n_tiles_n / xn) * panel_bytes <= ((int64_t)2 << 20)) return xn;
+  return n_tiles_n % 8 == 0 ? 8 : (n_tiles_n % 4 == 0 ? 4 : (n_tiles_n % 2 == 0 ? 2 : 1));
+}
+
 template <int LX, int LW, int ACT, int OUT>
-hipError_t launch_big(const GemmArgs &a, hipStream_t stream) {
-  const int units = a.n_tiles_total * a.splits;
-  const int grid = (units + 7) / 8 * 8;
+hipError_t launch_big(GemmArgs a, hipStream_t stream) {
+  int grid;
+  if (a.splits == 1) {
+    a.xcd_n = xcd_split_n(a.n_tiles_n, (int64_t)kBigTile * a.K * 2);
+    const int tm = (a.M + kBigTile - 1) / kBigTile, xm = 8 / a.xcd_n;
+    grid = 8 * ((tm + xm - 1) / xm) * (a.n_tiles_n / a.xcd_n);
+  } else {
+    grid = (a.n_tiles_total * a.splits + 7) / 8 * 8;
+  }
   // operand stages (2 operands each), reused for the output tile in the epilogue
   const size_t lds = std::max(2 * (size_t)kBigStages * kBigTile * kBigBK * 2,
                               OUT == OUT_F32 ? (size_t)128 * (kBigTile * 4 + 16) : (size_t)kBigTile * kOutPitch);

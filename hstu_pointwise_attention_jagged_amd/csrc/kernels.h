@@ -28,6 +28,7 @@ struct GemmArgs {
   int M, N, K;
   int k_split, splits;
   int n_tiles_n, n_tiles_total;
+  int xcd_n;                // set by the launcher: XCDs along the feature tiles
 };
 
 // Largest reduction width of launch_gemm: a 256-row operand panel (256 K bf16 values)
@@ -99,7 +100,11 @@ struct AttnArgs {
   const int32_t *n_work;    // [1]
   int num_heads;
   int mask;                 // 0 causal, 1 self-only
+  // profiling only, or nullptr: workgroup w < kClockSlots writes the core-clock and the
+  // 100 MHz real-time ticks of its lifetime to clk[2 w], clk[2 w + 1]
+  uint64_t *clk;
 };
+constexpr int kClockSlots = 64;
 
 // Attention gradients (attention_bwd.hip), causal mask, no prefix.
 struct AttnBwdArgs {

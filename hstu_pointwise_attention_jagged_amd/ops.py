@@ -24,7 +24,7 @@ __all__ = ["HSTUError", "LayerDims", "DeviceWeights", "DeviceJagged", "hstu_laye
            "hstu_stack_fwd_mfalcon", "hstu_stack_workspace_bytes",
            "hstu_stack_mfalcon_workspace_bytes", "hstu_attn_bwd", "hstu_attn_bwd_workspace_bytes",
            "hstu_layer_bwd", "hstu_layer_bwd_workspace_bytes",
-           "profile_enable", "profile_reset", "profile_collect"]
+           "profile_enable", "profile_reset", "profile_collect", "profile_clock_ghz"]
 
 
 class HSTUError(RuntimeError):
@@ -521,3 +521,12 @@ def profile_collect() -> dict:
     cnt = (ctypes.c_int64 * 5)()
     _raise(lib.hstu_profile_collect(tot, cnt), "hstu_profile_collect")
     return {lib.hstu_kernel_name(i).decode(): (tot[i], cnt[i]) for i in range(5)}
+
+
+def profile_clock_ghz() -> float:
+    """Shader clock (GHz) during the last attention launch made inside a layer while
+    profiling was enabled, 0.0 if none (include/hstu.h)."""
+    lib = _lib.load()
+    v = ctypes.c_double(0.0)
+    _raise(lib.hstu_profile_clock_ghz(ctypes.byref(v)), "hstu_profile_clock_ghz")
+    return float(v.value)
