@@ -204,16 +204,26 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
   // SiLU(x) = x / (1 + e^-x) = -ln(2) t / (1 + 2^t).  Q and the bias tables are scaled
   // once here, each score element costs exp2, add, reciprocal and multiply, and the
   // factor -ln(2) is applied to the output accumulators once, at the end.
-  // relative-bias tables of this head, scaled -> LDS
-  if (use_pos)
-    for (int i = tid; i < p.pos_buckets; i += NT)
-      ptab[i] = kNegLog2e * p.rab_pos[rrow * p.pos_buckets + i];
-  if (use_time)
-    for (int i = tid; i < p.time_buckets; i += NT)
-      ttab[i] = kNegLog2e * p.rab_time[rrow * p.time_buckets + i];
-  __syncthreads();
-  // bias of every relative position past the last bucket
-  const float pos_last = use_pos ? __builtin_bit_cast(float, sgpr(__builtin_bit_cast(int, ptab[p.pos_buckets - 1]))) : 0.0f;
+  // Prologue.  Every global read that the key loop depends on goes out before any of them
+  // is waited for: the bias tables, the queries' timestamps, Q, the key timestamp ranges
+  // of the first block table, then the first K / V batches.  They are consumed in that
+  // order, so the prologue costs one memory round trip instead of one per step, and the
+  // K / V batches stay in flight through the rest of it.
+  // relative-bias tables of this head (into LDS, scaled, below)
+  constexpr int PJ = (kMaxPos + NT - 1) / NT;
+  static_assert(kMaxTime <= NT, "one time bucket per thread");
+  float pv[PJ], tv = 0.0f;
+  if (use_pos) {
+#pragma unroll
+    for (int j = 0; j < PJ; ++j)
+      if (j * NT < p.pos_buckets) pv[j] = p.rab_pos[rrow * p.pos_buckets + min(tid + j * NT, p.pos_buckets - 1)];
+  }
+  {  // no branch around the load (a branch drew the scaling, and so a wait, up to it);
+     // without the time term the range is empty and the load reads zero
+    const __amdgpu_buffer_rsrc_t rtt =
+        make_rsrc(use_time ? p.rab_time + rrow * p.time_buckets : nullptr, use_time ? p.time_buckets * 4u : 0u);
+    tv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rtt, min(tid, kMaxTime - 1) * 4, 0, 0));
+  }
 
   // this wave's queries: local index qi, position, timestamp; Q fragments in registers
   const int qbase = q0 + wave * 32;  // wave-uniform
@@ -222,38 +232,18 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
   const bool wave_has_rows = qbase < n;
   const int qpos = MASK == 0 ? n_p + qi : n_p;
   const int32_t qts = use_time ? p.ts[s0 + (q_ok ? qi : n - 1)] : 0;
-  // timestamp range of the wave's queries, wave-uniform on every path
-  int32_t qmn = q_ok ? qts : INT32_MAX, qmx = q_ok ? qts : INT32_MIN;
-  if (use_time) {
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) {
-      qmn = min(qmn, __shfl_xor(qmn, o, 64));
-      qmx = max(qmx, __shfl_xor(qmx, o, 64));
-    }
-  }
-  const int32_t qts_min = sgpr(qmn), qts_max = sgpr(qmx);
   const int qpos_min = MASK == 0 ? n_p + qbase : n_p;
   const int qmax = qbase + 31;
-  f16x8 qf[KS];
+  // Q rows of this head through a descriptor over the sequence's rows: rows past its end
+  // read as zero, with no branch around the loads
+  u32x4 qraw[KS];
   {
-    const uint16_t *qrow = p.q + (int64_t)(s0 + qi) * p.stride + h * DH + half * 8;
+    const __amdgpu_buffer_rsrc_t rq =
+        make_rsrc(p.q + (int64_t)s0 * p.stride + h * DH, (uint32_t)n * (uint32_t)p.stride * 2u);
+    const int qoff = (qi * (int)p.stride + half * 8) * 2;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 v = q_ok ? *reinterpret_cast<const u32x4 *>(qrow + ks * 16) : u32x4{0, 0, 0, 0};
-      const f16x8 raw = as_f16x8(v);
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = kNegLog2e * (float)raw[e];
-      const u32x4 sc = {pack_f16(x[0], x[1]), pack_f16(x[2], x[3]),
-                        pack_f16(x[4], x[5]), pack_f16(x[6], x[7])};
-      qf[ks] = as_f16x8(sc);
-    }
+    for (int ks = 0; ks < KS; ++ks) qraw[ks] = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + ks * 32, 0, 0);
   }
-  // Complete the Q loads here, on every path: otherwise the wait-count pass can see them
-  // as possibly in flight inside the key loop and drain all vector loads there, which
-  // would also wait for the tile prefetch.  The empty asm only names the registers.
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) asm("" : "+v"(qf[ks]));
   // A operand of one extra k-step that adds a per-block constant to every score: 1 at
   // k = 0 for every key row (lanes 0-31 hold k = 0..7), 0 elsewhere.  Its B operand holds
   // the constant (fp16) at k = 0, so a constant-bias block starts its score chain with
@@ -352,10 +342,6 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
     }
   };
 
-  // The bias of a block on the constant or two-bucket path is pos_last plus one entry of
-  // the time table: lane i of tsum holds that sum for bucket i (at most 64 buckets).
-  float tsum = pos_last;
-  if (use_time && lane < p.time_buckets) tsum += ttab[lane];
   // Block table.  Block g of the wave's key sequence covers keys 32 (g mod 2) .. + 31 of
   // tile g / 2.  Lane i of the table describes block cbase + i: every lane classifies its
   // block in vector code, from the wave's query position / timestamp range and the
@@ -366,41 +352,121 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
   //   - bias kind: CONST when every relative position is past the last position bucket and
   //     the smallest and largest gap share one time bucket (the bucket being monotone in
   //     the gap); TWO when the gaps span exactly buckets b and b + 1; GENERAL otherwise.
+  // A table is built in two parts: the block's geometry and the load of its key timestamp
+  // range, then (once that has landed) the classification.
   int tab_bits = 0, tab_lo = 0, tab_hi = 0, tab_c = 0;
   int cbase = 0;
-  auto build_table = [&](int c0) __attribute__((always_inline)) {
+  struct TabLoad {
+    int2 r;
+    int k0;
+    bool lv, mk, pre;
+  };
+  auto table_load = [&](int c0) __attribute__((always_inline)) {
+    TabLoad tl;
     const int g = c0 + lane;
     const int t = g >> 1;
     const bool valid = t < n_tiles;
-    const bool pre = PRE && t < n_pt;
-    const int kbase = pre ? t * kBN : own_start + (t - n_pt) * kBN;
-    const int limit = n + (pre ? n_p - n : 0);
-    const int k0 = kbase + (g & 1) * 32;
-    bool lv = valid && k0 < limit && wave_has_rows;
-    bool mk = false;
+    tl.pre = PRE && t < n_pt;
+    const int kbase = tl.pre ? t * kBN : own_start + (t - n_pt) * kBN;
+    const int limit = n + (tl.pre ? n_p - n : 0);
+    tl.k0 = kbase + (g & 1) * 32;
+    tl.lv = valid && tl.k0 < limit && wave_has_rows;
     if (MASK == 0) {
-      lv = lv && (pre || k0 <= qmax);
-      mk = !pre && k0 + 31 > qbase;
+      tl.lv = tl.lv && (tl.pre || tl.k0 <= qmax);
+      tl.mk = !tl.pre && tl.k0 + 31 > qbase;
     } else {
-      lv = lv && (pre || (k0 <= qmax && k0 + 31 >= qbase));
-      mk = !pre;
+      tl.lv = tl.lv && (tl.pre || (tl.k0 <= qmax && tl.k0 + 31 >= qbase));
+      tl.mk = !tl.pre;
     }
-    const int kpos_max = pre ? k0 + 31 : (MASK == 0 ? n_p + k0 + 31 : n_p);
+    tl.r = int2{0, 0};
+    if (use_time && tl.lv) tl.r = tl.pre ? p.p_kstat[p0 + tl.k0] : p.kstat[s0 + tl.k0];
+    return tl;
+  };
+  // Batch b (issued in iteration b, or before the loop for b < -1) loads K of tile
+  // b + 1 + LEAD into K stage (b mod NS) and V of tile b + LEAD into V stage
+  // ((b - 1) mod NS): the stages that iteration b - 1 finished reading.  Iteration t
+  // reads K of tile t + 1 and V of tile t, which batch t - LEAD brought; its barrier
+  // waits for that batch and leaves the LEAD - 1 newer batches in flight.
+  auto batch = [&](int b, auto r_c, auto part_c) __attribute__((always_inline)) {  // r_c = b mod NS
+    constexpr int R = decltype(r_c)::value;
+    issue_batch(b + 1 + LEAD, b + LEAD, std::integral_constant<int, R>{},
+                std::integral_constant<int, (R + NS - 1) % NS>{}, part_c);
+  };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using CLast = std::integral_constant<int, NS - 1>;
+  // the first table's loads, then the first K / V batches (the last prologue loads)
+  const TabLoad tl0 = table_load(0);
+  if constexpr (NS == 3) {
+    batch(-3, C0{}, std::integral_constant<int, 2>{});
+    batch(-2, C1{}, std::integral_constant<int, 2>{});
+  } else {
+    batch(-2, C0{}, std::integral_constant<int, 2>{});
+  }
+
+  // the bias tables into LDS, scaled; the writes made visible to the workgroup without
+  // waiting for the K / V batches (lgkmcnt(0) only, then a bare barrier)
+  if (use_pos) {
+#pragma unroll
+    for (int j = 0; j < PJ; ++j)
+      if (j * NT < p.pos_buckets && tid + j * NT < p.pos_buckets) ptab[tid + j * NT] = kNegLog2e * pv[j];
+  }
+  if (use_time && tid < p.time_buckets) ttab[tid] = kNegLog2e * tv;
+  __builtin_amdgcn_s_waitcnt((3 << 14) | (7 << 4) | 15);  // lgkmcnt(0), vmcnt / expcnt not waited
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  // bias of every relative position past the last bucket
+  const float pos_last = use_pos ? __builtin_bit_cast(float, sgpr(__builtin_bit_cast(int, ptab[p.pos_buckets - 1]))) : 0.0f;
+  // timestamp range of the wave's queries, wave-uniform on every path
+  int32_t qmn = q_ok ? qts : INT32_MAX, qmx = q_ok ? qts : INT32_MIN;
+  if (use_time) {
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {
+      qmn = min(qmn, __shfl_xor(qmn, o, 64));
+      qmx = max(qmx, __shfl_xor(qmx, o, 64));
+    }
+  }
+  const int32_t qts_min = sgpr(qmn), qts_max = sgpr(qmx);
+  // Q fragments, scaled by -log2(e)
+  f16x8 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const f16x8 raw = as_f16x8(qraw[ks]);
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = kNegLog2e * (float)raw[e];
+    const u32x4 sc = {pack_f16(x[0], x[1]), pack_f16(x[2], x[3]),
+                      pack_f16(x[4], x[5]), pack_f16(x[6], x[7])};
+    qf[ks] = as_f16x8(sc);
+  }
+  // Complete the Q loads here, on every path: otherwise the wait-count pass can see them
+  // as possibly in flight inside the key loop and drain all vector loads there, which
+  // would also wait for the tile prefetch.  The empty asm only names the registers.
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) asm("" : "+v"(qf[ks]));
+
+  // The bias of a block on the constant or two-bucket path is pos_last plus one entry of
+  // the time table: lane i of tsum holds that sum for bucket i (at most 64 buckets).
+  float tsum = pos_last;
+  if (use_time && lane < p.time_buckets) tsum += ttab[lane];
+  auto table_fin = [&](int c0, const TabLoad &tl) __attribute__((always_inline)) {
+    const int kpos_max = tl.pre ? tl.k0 + 31 : (MASK == 0 ? n_p + tl.k0 + 31 : n_p);
     const bool pos_general = use_pos && qpos_min - kpos_max < p.pos_buckets - 1;
     int tb_lo = 0, tb_hi = 0;
     if (use_time) {
-      int2 r = {0, 0};
-      if (lv) r = pre ? p.p_kstat[p0 + k0] : p.kstat[s0 + k0];
-      tb_lo = min(time_log2_bucket(qts_min, r.y), p.time_buckets - 1);
-      tb_hi = min(time_log2_bucket(qts_max, r.x), p.time_buckets - 1);
+      tb_lo = min(time_log2_bucket(qts_min, tl.r.y), p.time_buckets - 1);
+      tb_hi = min(time_log2_bucket(qts_max, tl.r.x), p.time_buckets - 1);
     }
     const int kind = pos_general || tb_hi > tb_lo + 1 ? BIAS_GENERAL : (tb_hi == tb_lo ? BIAS_CONST : BIAS_TWO);
-    tab_bits = (lv ? 1 : 0) | (mk ? 2 : 0) | (pre ? 4 : 0) | (kind << 3) | (tb_lo << 5);
+    tab_bits = (tl.lv ? 1 : 0) | (tl.mk ? 2 : 0) | (tl.pre ? 4 : 0) | (kind << 3) | (tb_lo << 5);
     tab_lo = __builtin_bit_cast(int, __shfl(tsum, tb_lo, 64));
     tab_hi = __builtin_bit_cast(int, __shfl(tsum, tb_hi, 64));
     tab_c = (int)pack_f16(__builtin_bit_cast(float, tab_lo), 0.0f);  // CONST bias as the MFMA word
     cbase = c0;
   };
+  auto build_table = [&](int c0) __attribute__((always_inline)) { table_fin(c0, table_load(c0)); };
+  table_fin(0, tl0);
   auto fetch = [&](int g) __attribute__((always_inline)) {
     const int l = g - cbase;
     BlockInfo bi;
@@ -593,16 +659,6 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
   f32x16 sc0 = {}, sc1 = {};        // scores of the even / odd block in flight
   f16x8 pe[2] = {}, po[2] = {};     // P^T of the even / odd block
   BlockInfo cur0{}, cur1{}, nxt0{}, nxt1{};
-  // Batch b (issued in iteration b, or before the loop for b < -1) loads K of tile
-  // b + 1 + LEAD into K stage (b mod NS) and V of tile b + LEAD into V stage
-  // ((b - 1) mod NS): the stages that iteration b - 1 finished reading.  Iteration t
-  // reads K of tile t + 1 and V of tile t, which batch t - LEAD brought; its barrier
-  // waits for that batch and leaves the LEAD - 1 newer batches in flight.
-  auto batch = [&](int b, auto r_c, auto part_c) __attribute__((always_inline)) {  // r_c = b mod NS
-    constexpr int R = decltype(r_c)::value;
-    issue_batch(b + 1 + LEAD, b + LEAD, std::integral_constant<int, R>{},
-                std::integral_constant<int, (R + NS - 1) % NS>{}, part_c);
-  };
   auto iteration = [&](int t, auto r_c) __attribute__((always_inline)) {  // r_c = t mod NS
     constexpr int R = decltype(r_c)::value;
     constexpr int KR = (R + 1) % NS;
@@ -626,16 +682,6 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
     batch(t, r_c, std::integral_constant<int, 1>{});
     step(sc1, nxt1, kst, tst, 1, sc0, pe, nxt0, po, cur1, vst, 1);
   };
-  using C0 = std::integral_constant<int, 0>;
-  using C1 = std::integral_constant<int, 1>;
-  using CLast = std::integral_constant<int, NS - 1>;
-  build_table(0);
-  if constexpr (NS == 3) {
-    batch(-3, C0{}, std::integral_constant<int, 2>{});
-    batch(-2, C1{}, std::integral_constant<int, 2>{});
-  } else {
-    batch(-2, C0{}, std::integral_constant<int, 2>{});
-  }
   for (int t = -1; t < n_tiles; t += NS) {
     iteration(t, CLast{});
     if (t + 1 < n_tiles) iteration(t + 1, C0{});
