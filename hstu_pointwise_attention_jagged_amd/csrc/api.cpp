@@ -35,7 +35,7 @@ struct ProfRecord {
 };
 
 std::mutex g_prof_mu;
-bool g_prof_on = false;
+int g_prof_mask = 0;  // bit k: time the launches of kernel id k
 std::vector<ProfRecord> g_prof_records;
 std::vector<hipEvent_t> g_event_pool;
 
@@ -56,7 +56,7 @@ hipError_t timed(int id, hipStream_t stream, F &&launch) {
   hipEvent_t a = nullptr, b = nullptr;
   {
     std::lock_guard<std::mutex> lk(g_prof_mu);
-    if (g_prof_on) {
+    if ((g_prof_mask >> id) & 1) {
       a = pool_event();
       b = pool_event();
     }
@@ -71,9 +71,9 @@ hipError_t timed(int id, hipStream_t stream, F &&launch) {
   return err;
 }
 
-bool profiling() {
+bool attention_profiled() {
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  return g_prof_on;
+  return (g_prof_mask >> 2) & 1;
 }
 
 hstu_status_t hip_fail(hipError_t e) {
@@ -280,7 +280,7 @@ hstu_status_t run_layer(const hstu_dims_t *d, const hstu_weights_t *w, const hst
   if (e != hipSuccess) return hip_fail(e);
   const int64_t cap = attn_work_capacity(s->batch, T);
   AttnArgs at = aa;
-  if (profiling()) at.clk = clock_samples();  // lifetime clocks of the first workgroups
+  if (attention_profiled()) at.clk = clock_samples();  // lifetime clocks of the first workgroups
   e = timed(2, st, [&] { return launch_attention(at, d->dqk, s->max_seq_len, cap, st); });
   if (e != hipSuccess) return hip_fail(e);
   GateGemmArgs ga{};
@@ -1101,7 +1101,7 @@ int hstu_last_hip_error(void) { return g_last_hip_error; }
 
 void hstu_profile_enable(int on) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  g_prof_on = on != 0;
+  g_prof_mask = on & ((1 << kNumKernels) - 1);
 }
 
 void hstu_profile_reset(void) {

@@ -506,8 +506,13 @@ def hstu_validate_jagged(seq: DeviceJagged, stream=None) -> bool:
     return True
 
 
-def profile_enable(on: bool = True):
-    _lib.load().hstu_profile_enable(1 if on else 0)
+def profile_enable(on: bool = True, kernels=None):
+    """Event timing of the library's launches: every kernel (on=True), none (False), or
+    the kernel names in `kernels` (keys of _lib.KERNEL_IDS)."""
+    mask = 0
+    if on:
+        mask = -1 if kernels is None else sum(1 << _lib.KERNEL_IDS[k] for k in kernels)
+    _lib.load().hstu_profile_enable(mask)
 
 
 def profile_reset():

@@ -362,8 +362,10 @@ const char *hstu_status_str(hstu_status_t status);
 int hstu_last_hip_error(void);
 
 /* Optional per-kernel timing with HIP events on the launch stream (off by default).
- * While enabled, every kernel the library launches is bracketed by two events; the
- * durations are collected by hstu_profile_collect, which synchronises the events.
+ * `on` is a bitmask of kernel ids (bit k: kernel id k; -1: all, 0: none).  Every launch
+ * of a selected kernel is bracketed by two events on its stream; the durations are
+ * collected by hstu_profile_collect, which synchronises the events.  Each event pair adds
+ * a little time between launches, so a timed run can select only the kernel it reports.
  * Kernel ids: 0 schedule and key-block timestamp ranges, 1 f1 GEMM, 2 attention,
  * 3 f2 operand preparation (w2, gamma, beta to fp16), 4 f2 GEMM with the LayerNorm and
  * the U gate formed in its operand staging.                                         */
@@ -373,7 +375,7 @@ void hstu_profile_reset(void);
 hstu_status_t hstu_profile_collect(double *total_ms, int64_t *launches);
 const char *hstu_kernel_name(int kernel_id);
 /* Average shader (core) clock in GHz over the lifetime of the first 64 workgroups of the
- * last attention launch that ran inside a layer while profiling was enabled (the core
+ * last attention launch that ran inside a layer while the attention (id 2) was profiled (the core
  * clock counter against the 100 MHz real-time counter), 0 if none since the last
  * hstu_profile_reset.  Synchronises the device.                                       */
 hstu_status_t hstu_profile_clock_ghz(double *ghz);
