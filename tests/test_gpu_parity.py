@@ -441,3 +441,52 @@ def test_mfalcon_matches_oracle_and_microbatch_bitwise():
         err = np.abs(got.astype(np.float64) - want)
         say(f"        {name}: max_abs={err.max():.3e} mean_abs={err.mean():.3e}")
         assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS
+
+
+@pytest.mark.parametrize("lengths,cap_extra,d_model,heads,dh", [
+    ([37, 0, 91, 5], 163, 128, 2, 64),       # the 128-tile GEMM path (M < 256)
+    ([300, 1, 512, 77], 700, 256, 4, 64),    # the 256-tile GEMM path, ragged tails
+])
+def test_token_capacity_matches_exact_count(lengths, cap_extra, d_model, heads, dh):
+    """total_tokens above seq_offsets[B] (a capacity): the layer, a 2-layer stack and the
+    attention alone give the exact-count results bit for bit, and rows from seq_offsets[B]
+    on are left as they were."""
+    d = wl.LayerDims(d_model=d_model, num_heads=heads, dqk=dh, dv=dh)
+    w = wl.random_layer(77, lengths, d)
+    T = w.seq.total
+    cap = T + cap_extra
+    dims, wts = dev.dims_of(d), dev.weights_of(w.weights)
+    exact = dev.jagged_of(w.seq)
+    capj = dev.jagged_of(w.seq)
+    capj.total_tokens = cap
+    ts = torch.zeros(cap, dtype=torch.int32, device="cuda")
+    ts[:T] = capj.timestamps
+    capj.timestamps = ts
+    xc = torch.zeros((cap, d.d_model), dtype=torch.bfloat16, device="cuda")
+    xc[:T] = dev.bf16_tensor(w.x)
+    say(f"[capacity] lengths {lengths} T={T} capacity={cap} d={d_model} {heads}x{dh}")
+    y0, u0 = ops.hstu_layer_fwd(dims, wts, exact, xc[:T])
+    y1 = torch.full((cap, d.d_model), 7.0, dtype=torch.bfloat16, device="cuda")
+    u1 = torch.full((cap, d.uvqk_width), 7.0, dtype=torch.float16, device="cuda")
+    ops.hstu_layer_fwd(dims, wts, capj, xc, y=y1, uvqk=u1)
+    lw = [wts, dev.weights_of(wl.draw_weights(np.random.default_rng(78), d))]
+    s0, _ = ops.hstu_stack_fwd(dims, lw, exact, xc[:T])
+    s1 = torch.full((cap, d.d_model), 7.0, dtype=torch.bfloat16, device="cuda")
+    ops.hstu_stack_fwd(dims, lw, capj, xc, y=s1)
+    hq = heads * dh
+    q, k, v = u0[:, 2 * hq:3 * hq], u0[:, 3 * hq:], u0[:, hq:2 * hq]
+    a0 = ops.hstu_attn_fwd(dims, exact, q, k, v, row_stride=u0.stride(0),
+                           rab_pos=wts.rab_pos, rab_time=wts.rab_time)
+    ucap = torch.zeros((cap, d.uvqk_width), dtype=torch.float16, device="cuda")
+    ucap[:T] = u0
+    qc, kc, vc = ucap[:, 2 * hq:3 * hq], ucap[:, 3 * hq:], ucap[:, hq:2 * hq]
+    a1 = torch.full((cap, hq), 7.0, dtype=torch.float32, device="cuda")
+    ops.hstu_attn_fwd(dims, capj, qc, kc, vc, row_stride=ucap.stride(0), rab_pos=wts.rab_pos,
+                      rab_time=wts.rab_time, out=a1)
+    torch.cuda.synchronize()
+    assert torch.equal(y1[:T].view(torch.int16), y0.view(torch.int16))
+    assert torch.equal(u1[:T].view(torch.int16), u0.view(torch.int16))
+    assert torch.all(y1[T:] == 7.0) and torch.all(u1[T:] == 7.0)
+    assert torch.equal(s1[:T].view(torch.int16), s0.view(torch.int16))
+    assert torch.all(s1[T:] == 7.0)
+    assert torch.equal(a1[:T], a0) and torch.all(a1[T:] == 7.0)
