@@ -12,7 +12,7 @@ Besides the step, the line carries separate measurements of Stochastic Length, M
 serving, the attention gradients (hstu_attn_bwd) and one layer's backward (hstu_layer_bwd).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers 24] [--no-cpu-baseline]
-                  [--only-step]
+                  [--only-step] [--only-backward]
 """
 
 from __future__ import annotations
@@ -609,6 +609,9 @@ def main():
     ap.add_argument("--only-step", action="store_true",
                     help="time the stack only (no side measurements, no CPU baseline): the "
                          "short run that counter collection wraps")
+    ap.add_argument("--only-backward", action="store_true",
+                    help="only time one layer backward on the 8 x 8192 batch (after two untimed "
+                         "calls) and print it: the short run that backward counter collection wraps")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run 4 device-to-device copies of this many bytes (counter "
                          "calibration for HBM traffic) and exit")
@@ -643,6 +646,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"copied {args.copy_bytes} bytes 4 times")
+        return
+    if args.only_backward:
+        log("layer backward on the 8 x 8192 batch")
+        print(json.dumps({"layer_backward": layer_bwd_measure(torch, np, ops, dev, wl, reps=1)}), flush=True)
         return
     log("building inputs (8 x 8192 tokens, d=1024, 8x128 heads)")
     w = wl.config(2)
