@@ -475,17 +475,40 @@ def layer_bwd_measure(torch, np, ops, dev, wl, reps=5):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
+    # the training pair: the forward keeps U|V|Q|K and the attention output's parts, and
+    # the backward reuses them (only Z is formed again)
+    _, uvqk, cn, stats = ops.hstu_layer_fwd_train(dims, dw, seq, x)
+
+    def run_saved():
+        return ops.hstu_layer_bwd(dims, dw, seq, x, d_y, workspace=ws, stream=stream,
+                                  saved=(uvqk, cn, stats))
+
+    for _ in range(2):
+        run_saved()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        run_saved()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_saved = e0.elapsed_time(e1) / reps
     T, dm, H = w.seq.total, d.d_model, d.num_heads
     n1 = 2 * H * (d.dqk + d.dv)
     att = sum(10 * d.dqk * H * int(n) * (int(n) + 1) // 2 for n in w.seq.lengths)
     flops = 2 * 2 * T * dm * n1 + 2 * 2 * T * H * d.dv * dm + att
     tf = flops / (ms * 1e-3) / 1e12
+    tf_saved = flops / (ms_saved * 1e-3) / 1e12
     return {"workload": "layer backward (dX, dw1, db1, dw2, db2), 8 x 8192 tokens, d=1024, "
                         "8 heads x 128, causal, rab pos+time",
             "ms": round(ms, 4), "useful_flops": flops, "tflops": round(tf, 2),
             "pct_mfma_peak": round(100 * tf / PEAK_MFMA_TFLOPS, 2),
             "note": "one hstu_layer_bwd call, HIP events on the launch stream; it recomputes Z, "
-                    "U|V|Q|K and the attention output from X (not counted as useful work)"}
+                    "U|V|Q|K and the attention output from X (not counted as useful work)",
+            "saved_activations": {
+                "ms": round(ms_saved, 4), "tflops": round(tf_saved, 2),
+                "pct_mfma_peak": round(100 * tf_saved / PEAK_MFMA_TFLOPS, 2),
+                "note": "one hstu_layer_bwd_saved call on the U|V|Q|K and attention-output parts "
+                        "that hstu_layer_fwd_train kept; it recomputes only Z"}}
 
 
 def mfalcon_measure(torch, np, ops, dev, wl, n_layers=4, bm=1024, reps=3):

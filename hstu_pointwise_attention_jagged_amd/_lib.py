@@ -82,6 +82,12 @@ EXPORTS = {
     "hstu_layer_bwd": (c_int32, [ctypes.POINTER(Dims), ctypes.POINTER(Weights), ctypes.POINTER(Jagged),
                                  c_void_p, c_void_p, c_void_p, ctypes.POINTER(LayerGrads), c_void_p,
                                  c_size_t, c_void_p]),
+    "hstu_layer_fwd_train": (c_int32, [ctypes.POINTER(Dims), ctypes.POINTER(Weights), ctypes.POINTER(Jagged),
+                                       c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                       c_size_t, c_void_p]),
+    "hstu_layer_bwd_saved": (c_int32, [ctypes.POINTER(Dims), ctypes.POINTER(Weights), ctypes.POINTER(Jagged),
+                                       c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                       ctypes.POINTER(LayerGrads), c_void_p, c_size_t, c_void_p]),
     "hstu_attn_bwd_workspace_bytes": (c_size_t, [ctypes.POINTER(Dims), ctypes.POINTER(Jagged)]),
     "hstu_attn_bwd": (c_int32, [ctypes.POINTER(Dims), c_void_p, c_void_p, ctypes.POINTER(Jagged),
                                 c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p,

@@ -358,6 +358,37 @@ hstu_status_t hstu_layer_fwd(const hstu_dims_t *dims, const hstu_weights_t *w,
   return run_layer(dims, w, seq, x, y, uvqk, aa, lw, nullptr, (hipStream_t)stream);
 }
 
+hstu_status_t hstu_layer_fwd_train(const hstu_dims_t *dims, const hstu_weights_t *w,
+                                   const hstu_jagged_t *seq, const uint16_t *x, uint16_t *y,
+                                   uint16_t *uvqk, uint16_t *cn, float *stats, void *ws,
+                                   size_t ws_bytes, void *stream) {
+  hstu_status_t st;
+  if ((st = check_dims(dims)) != HSTU_OK) return st;
+  if ((st = check_seq(seq)) != HSTU_OK) return st;
+  if ((st = check_weights(w)) != HSTU_OK) return st;
+  if (seq->total_tokens > 0 &&
+      (x == nullptr || y == nullptr || uvqk == nullptr || cn == nullptr || stats == nullptr))
+    return HSTU_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(uvqk) || !aligned16(cn) || !aligned16(stats))
+    return HSTU_ERR_INVALID_ARG;
+  if ((void *)x == (void *)y || (void *)cn == (void *)y || (void *)cn == (void *)uvqk ||
+      (void *)stats == (void *)y || (void *)stats == (void *)uvqk || (void *)stats == (void *)cn)
+    return HSTU_ERR_INVALID_ARG;
+  if (seq->batch == 0 || seq->total_tokens == 0) return HSTU_OK;
+  if ((st = check_ws(ws, ws_bytes, layer_ws_bytes(dims, seq, nullptr))) != HSTU_OK) return st;
+  if (!rows_addressable(seq->max_seq_len, 2 * (int64_t)dims->num_heads * (dims->dqk + dims->dv)))
+    return HSTU_ERR_UNSUPPORTED;
+
+  LayerWs lw = carve_layer(ws, dims, seq, nullptr);
+  lw.cn = cn;  // the attention's standardised output and statistics go to the caller
+  lw.stats = reinterpret_cast<float2 *>(stats);
+  const int hdv = dims->num_heads * dims->dv, hqk = dims->num_heads * dims->dqk;
+  const int64_t n1 = 2 * (int64_t)(hdv + hqk);
+  AttnArgs aa = attn_args(dims, w->rab_pos, w->rab_time, seq, uvqk + 2 * hdv,
+                          uvqk + 2 * hdv + hqk, uvqk + hdv, n1, lw.o, lw);
+  return run_layer(dims, w, seq, x, y, uvqk, aa, lw, nullptr, (hipStream_t)stream);
+}
+
 hstu_status_t hstu_layer_fwd_mfalcon(const hstu_dims_t *dims, const hstu_weights_t *w,
                                      const hstu_jagged_t *hist, const uint16_t *hist_uvqk,
                                      const hstu_jagged_t *cand, const uint16_t *x_cand,
@@ -720,10 +751,21 @@ size_t hstu_layer_bwd_min_workspace_bytes(const hstu_dims_t *dims, const hstu_ja
   return layer_bwd_ws(dims, seq, nullptr);
 }
 
-hstu_status_t hstu_layer_bwd(const hstu_dims_t *dims, const hstu_weights_t *w,
-                             const hstu_jagged_t *seq, const uint16_t *x, const float *d_y,
-                             float *d_x, const hstu_layer_grads_t *grads, void *ws,
-                             size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Saved forward activations (hstu_layer_fwd_train): U|V|Q|K and the attention's
+// standardised output with its statistics; all nullptr to recompute them from x.
+struct SavedActs {
+  const uint16_t *uvqk, *cn;
+  const float2 *stats;
+};
+
+hstu_status_t layer_bwd(const hstu_dims_t *dims, const hstu_weights_t *w,
+                        const hstu_jagged_t *seq, const uint16_t *x, const float *d_y,
+                        float *d_x, const hstu_layer_grads_t *grads, void *ws,
+                        size_t ws_bytes, void *stream, const SavedActs &sv) {
   hstu_status_t st;
   if ((st = check_dims(dims)) != HSTU_OK) return st;
   if ((st = check_seq(seq)) != HSTU_OK) return st;
@@ -747,6 +789,15 @@ hstu_status_t hstu_layer_bwd(const hstu_dims_t *dims, const hstu_weights_t *w,
     return HSTU_ERR_INVALID_ARG;
   for (const void *g : gr)
     if (g != nullptr && g == (const void *)d_x) return HSTU_ERR_INVALID_ARG;
+  const bool saved = sv.uvqk != nullptr;
+  if (saved) {
+    const void *sp[] = {sv.uvqk, sv.cn, sv.stats};
+    for (const void *q : sp) {
+      if (!aligned16(q) || q == (const void *)d_x) return HSTU_ERR_INVALID_ARG;
+      for (const void *g : gr)
+        if (g != nullptr && g == q) return HSTU_ERR_INVALID_ARG;
+    }
+  }
   hipStream_t sst = (hipStream_t)stream;
   const int T = seq->total_tokens;
   const int dm = dims->d_model, hdv = dims->num_heads * dims->dv, hqk = dims->num_heads * dims->dqk;
@@ -773,7 +824,8 @@ hstu_status_t hstu_layer_bwd(const hstu_dims_t *dims, const hstu_weights_t *w,
   LayerWs lw{};
   carve_attn(b.attn, seq, nullptr, lw);
   lw.o = b.o;
-  const uint16_t *q = b.uvqk + 2 * hdv, *k = b.uvqk + 2 * hdv + hqk, *v = b.uvqk + hdv;
+  const uint16_t *uvqk = saved ? sv.uvqk : b.uvqk;
+  const uint16_t *q = uvqk + 2 * hdv, *k = uvqk + 2 * hdv + hqk, *v = uvqk + hdv;
   AttnArgs aa = attn_args(dims, w->rab_pos, w->rab_time, seq, q, k, v, n1, b.o, lw);
   if ((st = run_setup(seq, aa, lw, nullptr, false, sst)) != HSTU_OK) return st;
   hipError_t e;
@@ -782,18 +834,24 @@ hstu_status_t hstu_layer_bwd(const hstu_dims_t *dims, const hstu_weights_t *w,
     e = (call);                   \
     if (e != hipSuccess) return hip_fail(e); \
   } while (0)
-  // forward pieces: Z, U|V|Q|K = SiLU(Z), the attention output O
+  // forward pieces: Z (for SiLU'), then U|V|Q|K = SiLU(Z) and the attention output O
+  // unless the forward saved them
   HSTU_TRY(launch_gemm(x, w->w1, w->b1, b.z, T, n1, dm, ACT_NONE, OUT_F16, sst));
-  HSTU_TRY(launch_silu_f16(b.z, b.uvqk, (int64_t)T * n1, sst));
   const int64_t cap = attn_work_capacity(seq->batch, T);
-  HSTU_TRY(launch_attention(aa, dims->dqk, seq->max_seq_len, cap, sst));
+  if (!saved) {
+    HSTU_TRY(launch_silu_f16(b.z, b.uvqk, (int64_t)T * n1, sst));
+    HSTU_TRY(launch_attention(aa, dims->dqk, seq->max_seq_len, cap, sst));
+  }
   // f2: dG = dY w2, then the gate and LayerNorm backward, then dw2 = dY^T G, db2
   HSTU_TRY(launch_cast_bf16(d_y, b.dy16, (int64_t)T * dm, sst));
   HSTU_TRY(launch_gemm_nn_f32(b.dy16, dm, w->w2, hdv, b.dg, T, hdv, dm, sst));
   NormGateBwdArgs ng{};
-  ng.o = b.o;
+  ng.o = saved ? nullptr : b.o;
+  ng.cn = sv.cn;
+  ng.stats = sv.stats;
+  ng.dv = dims->dv;
   ng.dg = b.dg;
-  ng.u = b.uvqk;
+  ng.u = uvqk;
   ng.zu = b.z;
   ng.u_stride = n1;
   ng.gamma = w->ln_gamma;
@@ -859,6 +917,31 @@ hstu_status_t hstu_layer_bwd(const hstu_dims_t *dims, const hstu_weights_t *w,
     HSTU_TRY(launch_colsum(b.dz, true, T, n1, n1, b.part_cols, kColsumParts, grads->b1, sst));
 #undef HSTU_TRY
   return HSTU_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hstu_status_t hstu_layer_bwd(const hstu_dims_t *dims, const hstu_weights_t *w,
+                             const hstu_jagged_t *seq, const uint16_t *x, const float *d_y,
+                             float *d_x, const hstu_layer_grads_t *grads, void *ws,
+                             size_t ws_bytes, void *stream) {
+  return layer_bwd(dims, w, seq, x, d_y, d_x, grads, ws, ws_bytes, stream, SavedActs{});
+}
+
+hstu_status_t hstu_layer_bwd_saved(const hstu_dims_t *dims, const hstu_weights_t *w,
+                                   const hstu_jagged_t *seq, const uint16_t *x,
+                                   const uint16_t *uvqk, const uint16_t *cn, const float *stats,
+                                   const float *d_y, float *d_x, const hstu_layer_grads_t *grads,
+                                   void *ws, size_t ws_bytes, void *stream) {
+  if (seq != nullptr && seq->total_tokens > 0 && (uvqk == nullptr || cn == nullptr || stats == nullptr))
+    return HSTU_ERR_INVALID_ARG;
+  if (uvqk == nullptr) {  // empty batch: no activation to read, the ordinary path zeroes
+    return layer_bwd(dims, w, seq, x, d_y, d_x, grads, ws, ws_bytes, stream, SavedActs{});
+  }
+  return layer_bwd(dims, w, seq, x, d_y, d_x, grads, ws, ws_bytes, stream,
+                   SavedActs{uvqk, cn, reinterpret_cast<const float2 *>(stats)});
 }
 
 }  // extern "C"

@@ -153,7 +153,10 @@ struct AttnBwdArgs {
 
 // Backward of LayerNorm + gate for every row (see layer_bwd.hip).
 struct NormGateBwdArgs {
-  const float *o;       // [T][hdv] attention output
+  const float *o;       // [T][hdv] attention output, or nullptr: then O = cn sqrt(var) + mean
+  const uint16_t *cn;   //   per head, from the forward's standardised fp16 output cn [T][hdv]
+  const float2 *stats;  //   and its (mean, biased variance) per row and head [T][hdv / dv]
+  int dv;               //   (head width)
   const float *dg;      // [T][hdv] gradient of the gate product G
   const uint16_t *u;    // fp16 gate U, row pitch u_stride
   const uint16_t *zu;   // fp16 pre-activations of U, row pitch u_stride

@@ -5,7 +5,8 @@
 //  * silu_f16_kernel: U|V|Q|K = SiLU(Z) from the recomputed pre-activations Z (fp16), the
 //    operands of the attention that the backward re-forms.
 //  * cast_bf16_kernel: the fp32 upstream gradient dY as the bf16 GEMM operand.
-//  * norm_gate_bwd_kernel: one wave per row.  From the attention output O, the gate U, its
+//  * norm_gate_bwd_kernel: one wave per row.  From the attention output O (fp32, or rebuilt
+//    per head as cn sqrt(var) + mean from the forward's standardised output), the gate U, its
 //    pre-activation Z_U and dG = dY w2, it forms N = LayerNorm(O) (two-pass statistics, as
 //    the forward), G = N U (bf16, the operand of dw2 = dY^T G), dZ_U = dG N SiLU'(Z_U)
 //    (bf16, into the dZ rows) and dO = (dxhat - mean(dxhat) - xhat mean(dxhat xhat)) / sigma
@@ -70,7 +71,6 @@ __global__ __launch_bounds__(64 * kNgRows) void norm_gate_bwd_kernel(NormGateBwd
 #pragma unroll
   for (int c = 0; c < C; ++c) sg[c] = sb[c] = f32x4{0, 0, 0, 0};
   for (int row = wave; row < p.T; row += n_waves) {
-    const float *orow = p.o + (int64_t)row * HDV;
     const float *grow = p.dg + (int64_t)row * HDV;
     const uint16_t *urow = p.u + (int64_t)row * p.u_stride;
     const uint16_t *zrow = p.zu + (int64_t)row * p.u_stride;
@@ -79,7 +79,18 @@ __global__ __launch_bounds__(64 * kNgRows) void norm_gate_bwd_kernel(NormGateBwd
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const int e = (lane + 64 * c) * 4;
-      x[c] = e < HDV ? *reinterpret_cast<const f32x4 *>(orow + e) : f32x4{0, 0, 0, 0};
+      x[c] = f32x4{0, 0, 0, 0};
+      if (e < HDV) {
+        if (p.o != nullptr) {
+          x[c] = *reinterpret_cast<const f32x4 *>(p.o + (int64_t)row * HDV + e);
+        } else {  // the 4 features share a head (dv is a multiple of 32)
+          const u32x2 cc = *reinterpret_cast<const u32x2 *>(p.cn + (int64_t)row * HDV + e);
+          const float2 st = p.stats[(int64_t)row * (HDV / p.dv) + e / p.dv];
+          const float sd = __builtin_amdgcn_sqrtf(st.y);
+          x[c] = f32x4{f16_lo(cc[0]) * sd + st.x, f16_hi(cc[0]) * sd + st.x,
+                       f16_lo(cc[1]) * sd + st.x, f16_hi(cc[1]) * sd + st.x};
+        }
+      }
       sum += (x[c][0] + x[c][1]) + (x[c][2] + x[c][3]);
     }
     const float mean = wave_sum64(sum) * inv_n;

@@ -175,6 +175,27 @@ def hstu_layer_fwd(dims: LayerDims, w: DeviceWeights, seq: DeviceJagged, x: torc
     return y, uvqk
 
 
+def hstu_layer_fwd_train(dims: LayerDims, w: DeviceWeights, seq: DeviceJagged, x: torch.Tensor, *,
+                         workspace: Optional[torch.Tensor] = None, stream=None):
+    """hstu_layer_fwd that also returns what hstu_layer_bwd_saved reuses.  Returns
+    (y bf16 [T][d], uvqk fp16 [T][2H(dv+dqk)], cn fp16 [T][H*dv], stats fp32 [T][H][2])."""
+    lib = _lib.load()
+    _check(x, torch.bfloat16, "x")
+    T = seq.total_tokens
+    y = torch.empty((T, dims.d_model), dtype=torch.bfloat16, device=x.device)
+    uvqk = torch.empty((T, dims.uvqk_width), dtype=torch.float16, device=x.device)
+    cn = torch.empty((T, dims.hdv), dtype=torch.float16, device=x.device)
+    stats = torch.empty((T, dims.num_heads, 2), dtype=torch.float32, device=x.device)
+    d, wc, s = dims.c(), w.c(), seq.c()
+    need = int(lib.hstu_layer_workspace_bytes(ctypes.byref(d), ctypes.byref(s)))
+    ws = _workspace(need, x.device, workspace)
+    st = lib.hstu_layer_fwd_train(ctypes.byref(d), ctypes.byref(wc), ctypes.byref(s), _ptr(x), _ptr(y),
+                                  _ptr(uvqk), _ptr(cn), _ptr(stats), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream))
+    _raise(st, "hstu_layer_fwd_train")
+    return y, uvqk, cn, stats
+
+
 def hstu_layer_fwd_mfalcon(dims: LayerDims, w: DeviceWeights, hist: DeviceJagged,
                            hist_uvqk: torch.Tensor, cand: DeviceJagged, x_cand: torch.Tensor, *,
                            y_cand: Optional[torch.Tensor] = None,
@@ -416,15 +437,21 @@ def hstu_layer_bwd_workspace_bytes(dims: LayerDims, seq: DeviceJagged, minimum: 
 
 def hstu_layer_bwd(dims: LayerDims, w: DeviceWeights, seq: DeviceJagged, x: torch.Tensor,
                    d_y: torch.Tensor, *, bias_grads: bool = True,
-                   workspace: Optional[torch.Tensor] = None, stream=None):
+                   workspace: Optional[torch.Tensor] = None, stream=None, saved=None):
     """Backward of one causal layer for the upstream gradient d_y (fp32 [T][d]).
 
     Returns (d_x, grads): d_x fp32 [T][d]; grads a dict of fp32 tensors w1, w2 and, when
     asked for, b1, b2 (bias_grads), and ln_gamma, ln_beta, rab_pos, rab_time for those
-    the weights have."""
+    the weights have.  saved: (uvqk, cn, stats) from hstu_layer_fwd_train on the same x and
+    weights, to run hstu_layer_bwd_saved instead of recomputing them."""
     lib = _lib.load()
     _check(x, torch.bfloat16, "x")
     _check(d_y, torch.float32, "d_y")
+    if saved is not None:
+        uvqk, cn, stats = saved
+        _check(uvqk, torch.float16, "uvqk")
+        _check(cn, torch.float16, "cn")
+        _check(stats, torch.float32, "stats")
     dev = x.device
     n1 = dims.uvqk_width
     f32 = dict(dtype=torch.float32, device=dev)
@@ -447,10 +474,17 @@ def hstu_layer_bwd(dims: LayerDims, w: DeviceWeights, seq: DeviceJagged, x: torc
     d, wc, s = dims.c(), w.c(), seq.c()
     need = int(lib.hstu_layer_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(s)))
     ws = _workspace(need, dev, workspace)
-    st = lib.hstu_layer_bwd(ctypes.byref(d), ctypes.byref(wc), ctypes.byref(s), _ptr(x), _ptr(d_y),
-                            _ptr(d_x), ctypes.byref(gc), _ptr(ws), ws.numel() * ws.element_size(),
-                            _stream(stream))
-    _raise(st, "hstu_layer_bwd")
+    if saved is None:
+        st = lib.hstu_layer_bwd(ctypes.byref(d), ctypes.byref(wc), ctypes.byref(s), _ptr(x), _ptr(d_y),
+                                _ptr(d_x), ctypes.byref(gc), _ptr(ws), ws.numel() * ws.element_size(),
+                                _stream(stream))
+        _raise(st, "hstu_layer_bwd")
+    else:
+        st = lib.hstu_layer_bwd_saved(ctypes.byref(d), ctypes.byref(wc), ctypes.byref(s), _ptr(x),
+                                      _ptr(uvqk), _ptr(cn), _ptr(stats), _ptr(d_y), _ptr(d_x),
+                                      ctypes.byref(gc), _ptr(ws), ws.numel() * ws.element_size(),
+                                      _stream(stream))
+        _raise(st, "hstu_layer_bwd_saved")
     return d_x, grads
 
 

@@ -350,6 +350,34 @@ hstu_status_t hstu_layer_bwd(const hstu_dims_t *dims, const hstu_weights_t *w,
                              float *d_x, const hstu_layer_grads_t *grads, void *ws,
                              size_t ws_bytes, void *stream);
 
+/* The forward of hstu_layer_fwd for training (same arguments, results and errors), which
+ * also hands the caller what hstu_layer_bwd_saved reuses instead of recomputing: the
+ * attention output of equation 2 for each row and head, as it enters the LayerNorm of
+ * equation 3 ("Actions Speak Louder than Words" as retold on chenhuiyu.github.io,
+ * section "HSTU Layer 到底改了什么"), in the parts the layer itself keeps.
+ *   cn    (device) fp16 [T][H*dv]: each head's dv outputs standardised over that head,
+ *                  (o - mean) / sqrt(var) (0 when var = 0), |value| <= sqrt(dv)
+ *   stats (device) fp32 [T][H][2]: (mean, biased variance) of those dv outputs, so that
+ *                  o = cn * sqrt(var) + mean
+ * cn, stats may not alias y, uvqk or each other (HSTU_ERR_INVALID_ARG).            */
+hstu_status_t hstu_layer_fwd_train(const hstu_dims_t *dims, const hstu_weights_t *w,
+                                   const hstu_jagged_t *seq, const uint16_t *x, uint16_t *y,
+                                   uint16_t *uvqk, uint16_t *cn, float *stats, void *ws,
+                                   size_t ws_bytes, void *stream);
+
+/* hstu_layer_bwd with the activations that hstu_layer_fwd_train wrote for the same x,
+ * weights and batch (uvqk, cn, stats as documented there): U|V|Q|K and the attention
+ * output are read instead of recomputed; only Z = X w1^T + b1 (for SiLU') is formed
+ * again.  The gradients are those of the forward as it ran (its fp16 U|V|Q|K and
+ * standardised output), so they differ from hstu_layer_bwd's, which rebuilds both from
+ * x, by rounding only.  Same workspace, other arguments and errors as hstu_layer_bwd;
+ * uvqk, cn, stats may not alias d_x or a gradient (HSTU_ERR_INVALID_ARG).            */
+hstu_status_t hstu_layer_bwd_saved(const hstu_dims_t *dims, const hstu_weights_t *w,
+                                   const hstu_jagged_t *seq, const uint16_t *x,
+                                   const uint16_t *uvqk, const uint16_t *cn, const float *stats,
+                                   const float *d_y, float *d_x, const hstu_layer_grads_t *grads,
+                                   void *ws, size_t ws_bytes, void *stream);
+
 /* Debug check of device offsets: off[0] == 0, non-decreasing, off[B] <= total_tokens
  * (equal, unless total_tokens is meant as a capacity), every length <= max_seq_len.
  * Synchronises the stream.  Returns HSTU_OK or HSTU_ERR_INVALID_ARG.                  */

@@ -273,6 +273,41 @@ def test_layer_bwd_argument_checks(lib):
     assert call(ok, ws_bytes=need - 1) == _lib.HSTU_ERR_WORKSPACE
 
 
+def test_saved_activation_entry_points_check_their_arguments(lib):
+    """hstu_layer_fwd_train and hstu_layer_bwd_saved reject missing, misaligned or aliased
+    activation buffers before any device call."""
+    d, s = _dims(), _seq()
+    w = _lib.Weights(FAKE, None, FAKE, None, None, None, None, None)
+    need = lib.hstu_layer_workspace_bytes(ctypes.byref(d), ctypes.byref(s))
+    X, Y, U, C, S = (FAKE + i * (1 << 20) for i in range(5))
+
+    def fwd(cn=C, stats=S, uvqk=U, ws_bytes=need):
+        return lib.hstu_layer_fwd_train(ctypes.byref(d), ctypes.byref(w), ctypes.byref(s), X, Y,
+                                        uvqk, cn, stats, FAKE, ws_bytes, None)
+    assert fwd(cn=None) == _lib.HSTU_ERR_INVALID_ARG
+    assert fwd(stats=None) == _lib.HSTU_ERR_INVALID_ARG
+    assert fwd(cn=C + 2) == _lib.HSTU_ERR_INVALID_ARG      # misaligned
+    assert fwd(cn=U) == _lib.HSTU_ERR_INVALID_ARG          # aliases uvqk
+    assert fwd(stats=Y) == _lib.HSTU_ERR_INVALID_ARG       # aliases y
+    assert fwd(ws_bytes=need - 1) == _lib.HSTU_ERR_WORKSPACE
+
+    bneed = lib.hstu_layer_bwd_min_workspace_bytes(ctypes.byref(d), ctypes.byref(s))
+    G = FAKE + (1 << 28)
+    ok = _lib.LayerGrads(G, None, G + 65536, None, None, None, None, None)
+
+    def bwd(uvqk=U, cn=C, stats=S, dx=FAKE + (1 << 27), grads=ok, ws_bytes=bneed):
+        return lib.hstu_layer_bwd_saved(ctypes.byref(d), ctypes.byref(w), ctypes.byref(s), X, uvqk,
+                                        cn, stats, FAKE + (1 << 26), dx, ctypes.byref(grads), FAKE,
+                                        ws_bytes, None)
+    assert bwd(uvqk=None) == _lib.HSTU_ERR_INVALID_ARG
+    assert bwd(stats=None) == _lib.HSTU_ERR_INVALID_ARG
+    assert bwd(cn=C + 8) == _lib.HSTU_ERR_INVALID_ARG      # misaligned
+    assert bwd(dx=C) == _lib.HSTU_ERR_INVALID_ARG          # d_x aliases cn
+    assert bwd(grads=_lib.LayerGrads(S, None, G + 65536, None, None, None, None, None)) == \
+        _lib.HSTU_ERR_INVALID_ARG                            # a gradient aliases stats
+    assert bwd(ws_bytes=bneed - 1) == _lib.HSTU_ERR_WORKSPACE
+
+
 def test_noalloc_attention_rejects_before_any_device_call(lib):
     d = _dims()
     cap = lib.hstu_attn_noalloc_max_scratch_bytes()

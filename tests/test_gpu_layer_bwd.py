@@ -161,3 +161,57 @@ def test_layer_gradients_full_size_sampled_rows():
                          d.dv, d_y, d.ln_eps, rows=rows)
     _check_rows("dx rows", d_x[rows], want["dx"][rows])
     _check("b2", grads["b2"], d_y.astype(np.float64).sum(axis=0))
+
+
+@pytest.mark.parametrize("cfg,kw", [(0, {}), (2, {"batch": 2, "seq_len": 600})])
+def test_saved_activations_path(cfg, kw):
+    """hstu_layer_fwd_train gives hstu_layer_fwd's y and U|V|Q|K bit for bit plus the
+    attention output in parts (per-head standardised fp16 values and their mean and
+    variance); hstu_layer_bwd_saved on those parts meets the oracle bar, and differs from
+    the recomputing backward by rounding only.
+
+    Bar of the rebuilt output: cn is rounded to fp16 with |cn| <= sqrt(dv), so o = cn sd +
+    mean is off by at most sqrt(dv) 2^-11 sd per element; 8e-3 sd covers dv = 128 (5.5e-3)."""
+    w = wl.config(cfg, **kw)
+    d = w.dims
+    rng = np.random.default_rng(750 + cfg)
+    weights = wl.draw_weights(rng, d, bias=True, affine=True)
+    d_y = rng.standard_normal((w.seq.total, d.d_model)).astype(np.float32)
+    dims, seq = dev.dims_of(d), dev.jagged_of(w.seq)
+    dw, x = dev.weights_of(weights), dev.bf16_tensor(w.x)
+    T, H, dv, hdv = w.seq.total, d.num_heads, d.dv, d.num_heads * d.dv
+    say(f"[layer bwd saved] config {cfg} {kw} T={T} d={d.d_model} H={H}x{d.dqk}")
+    y0, u0 = ops.hstu_layer_fwd(dims, dw, seq, x)
+    y1, u1, cn, stats = ops.hstu_layer_fwd_train(dims, dw, seq, x)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(u0, u1)
+    # the attention output rebuilt from its parts against the attention alone (fp32 output)
+    hq = H * d.dqk
+    o = ops.hstu_attn_fwd(dims, seq, u1[:, 2 * hdv:2 * hdv + hq], u1[:, 2 * hdv + hq:],
+                          u1[:, hdv:2 * hdv], row_stride=u1.stride(0), rab_pos=dw.rab_pos,
+                          rab_time=dw.rab_time)
+    sd = stats[..., 1].clamp_min(0).sqrt()
+    rebuilt = cn.float().view(T, H, dv) * sd[..., None] + stats[..., 0:1]
+    err = (rebuilt - o.view(T, H, dv)).abs().amax(dim=2)
+    ratio = (err / sd.clamp_min(1e-30)).max().item()
+    say(f"      rebuilt output: max error / head sd = {ratio:.3e}")
+    assert ratio <= 8e-3
+    d_yt = torch.from_numpy(d_y).cuda()
+    d_x, grads = ops.hstu_layer_bwd(dims, dw, seq, x, d_yt, saved=(u1, cn, stats))
+    d_x_r, grads_r = ops.hstu_layer_bwd(dims, dw, seq, x, d_yt)
+    torch.cuda.synchronize()
+    want = bwd.layer_bwd(w.x, weights, w.seq.offsets, w.seq.timestamps, d.num_heads, d.dqk,
+                         d.dv, d_y, d.ln_eps)
+    _check_rows("dx", d_x, want["dx"])
+    for k, t in grads.items():
+        _check(k, t, want[NAMES[k]])
+    assert set(grads) == set(grads_r)
+    # The two paths differ by rounding only: the saved one uses the forward's fp16 U|V|Q|K
+    # (SiLU of the fp32 pre-activation) and fp16 standardised output, the other rounds Z to
+    # fp16 before SiLU and recomputes the output in fp32.  Each meets the oracle bar
+    # MAX_REL, so their difference, in the same units, is held to MAX_REL as well.
+    for k, t in list(grads.items()) + [("dx", d_x)]:
+        r = grads_r[k] if k != "dx" else d_x_r
+        rel = ((t - r).abs().max() / r.double().std().clamp_min(1e-30)).item()
+        say(f"      {k}: saved vs recomputed max diff / std = {rel:.3e}")
+        assert rel <= MAX_REL, k
