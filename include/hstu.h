@@ -48,8 +48,9 @@
  *  - Device-side jagged offsets are a precondition (0 = off[0] <= ... <= off[B] = T,
  *    max length <= max_seq_len); they are not re-validated on the hot path.  Use
  *    hstu_validate_jagged when in doubt.  Zero-length sequences are legal.
- *  - Token capacity: the forward entry points (hstu_layer_fwd, hstu_layer_fwd_mfalcon,
- *    hstu_stack_fwd, hstu_stack_fwd_mfalcon, hstu_attn_fwd, hstu_attn_fwd_noalloc) also
+ *  - Token capacity: the forward entry points (hstu_layer_fwd, hstu_layer_fwd_train,
+ *    hstu_layer_fwd_mfalcon, hstu_stack_fwd, hstu_stack_fwd_mfalcon, hstu_attn_fwd,
+ *    hstu_attn_fwd_noalloc) also
  *    accept total_tokens above off[B], as a capacity: row buffers and workspaces are then
  *    sized for total_tokens rows, the kernels take the true count off[B] from the device,
  *    and output rows from off[B] on are left as they were.  A batch built on the device
