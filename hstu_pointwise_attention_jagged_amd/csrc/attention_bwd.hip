@@ -377,10 +377,10 @@ struct RabAcc {
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
     return v;
   }
-  __device__ __forceinline__ void time_add(float v, int b) {
-    v = wave_sum(v);
-    if (lane == 0) wtime[b] += v;
-  }
+  // the lane's value into its own copy of the time bins (lane % kTimeReps): one LDS atomic,
+  // no cross-lane sum (six dependent shuffles per call cost more than the whole block's
+  // bin update); the copies are summed once, in rab_write
+  __device__ __forceinline__ void time_add(float v, int b) { atomicAdd(&ltime[b], v); }
   // One 32 x 32 block: the lane's query qi (q_ok) and its 16 values ds[i] for the keys
   // kb + 8 (i / 4) + 4 half + i % 4, whose timestamps are kts[8 (i / 4) + i % 4].
   __device__ __forceinline__ void block(const BlockBias &bb, const float *ds, const int32_t *kts,
