@@ -176,16 +176,26 @@ def hstu_layer_fwd(dims: LayerDims, w: DeviceWeights, seq: DeviceJagged, x: torc
 
 
 def hstu_layer_fwd_train(dims: LayerDims, w: DeviceWeights, seq: DeviceJagged, x: torch.Tensor, *,
+                         y: Optional[torch.Tensor] = None, uvqk: Optional[torch.Tensor] = None,
+                         cn: Optional[torch.Tensor] = None, stats: Optional[torch.Tensor] = None,
                          workspace: Optional[torch.Tensor] = None, stream=None):
     """hstu_layer_fwd that also returns what hstu_layer_bwd_saved reuses.  Returns
     (y bf16 [T][d], uvqk fp16 [T][2H(dv+dqk)], cn fp16 [T][H*dv], stats fp32 [T][H][2])."""
     lib = _lib.load()
     _check(x, torch.bfloat16, "x")
     T = seq.total_tokens
-    y = torch.empty((T, dims.d_model), dtype=torch.bfloat16, device=x.device)
-    uvqk = torch.empty((T, dims.uvqk_width), dtype=torch.float16, device=x.device)
-    cn = torch.empty((T, dims.hdv), dtype=torch.float16, device=x.device)
-    stats = torch.empty((T, dims.num_heads, 2), dtype=torch.float32, device=x.device)
+    if y is None:
+        y = torch.empty((T, dims.d_model), dtype=torch.bfloat16, device=x.device)
+    if uvqk is None:
+        uvqk = torch.empty((T, dims.uvqk_width), dtype=torch.float16, device=x.device)
+    if cn is None:
+        cn = torch.empty((T, dims.hdv), dtype=torch.float16, device=x.device)
+    if stats is None:
+        stats = torch.empty((T, dims.num_heads, 2), dtype=torch.float32, device=x.device)
+    _check(y, torch.bfloat16, "y")
+    _check(uvqk, torch.float16, "uvqk")
+    _check(cn, torch.float16, "cn")
+    _check(stats, torch.float32, "stats")
     d, wc, s = dims.c(), w.c(), seq.c()
     need = int(lib.hstu_layer_workspace_bytes(ctypes.byref(d), ctypes.byref(s)))
     ws = _workspace(need, x.device, workspace)

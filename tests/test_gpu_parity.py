@@ -448,9 +448,9 @@ def test_mfalcon_matches_oracle_and_microbatch_bitwise():
     ([300, 1, 512, 77], 700, 256, 4, 64),    # the 256-tile GEMM path, ragged tails
 ])
 def test_token_capacity_matches_exact_count(lengths, cap_extra, d_model, heads, dh):
-    """total_tokens above seq_offsets[B] (a capacity): the layer, a 2-layer stack and the
-    attention alone give the exact-count results bit for bit, and rows from seq_offsets[B]
-    on are left as they were."""
+    """total_tokens above seq_offsets[B] (a capacity): the layer, the training forward, a
+    2-layer stack and the attention alone give the exact-count results bit for bit, and
+    rows from seq_offsets[B] on are left as they were."""
     d = wl.LayerDims(d_model=d_model, num_heads=heads, dqk=dh, dv=dh)
     w = wl.random_layer(77, lengths, d)
     T = w.seq.total
@@ -490,3 +490,14 @@ def test_token_capacity_matches_exact_count(lengths, cap_extra, d_model, heads, 
     assert torch.equal(s1[:T].view(torch.int16), s0.view(torch.int16))
     assert torch.all(s1[T:] == 7.0)
     assert torch.equal(a1[:T], a0) and torch.all(a1[T:] == 7.0)
+    # the training forward: y, U|V|Q|K and the attention output's parts
+    t0 = ops.hstu_layer_fwd_train(dims, wts, exact, xc[:T])
+    t1 = (torch.full((cap, d.d_model), 7.0, dtype=torch.bfloat16, device="cuda"),
+          torch.full((cap, d.uvqk_width), 7.0, dtype=torch.float16, device="cuda"),
+          torch.full((cap, heads * dh), 7.0, dtype=torch.float16, device="cuda"),
+          torch.full((cap, heads, 2), 7.0, dtype=torch.float32, device="cuda"))
+    ops.hstu_layer_fwd_train(dims, wts, capj, xc, y=t1[0], uvqk=t1[1], cn=t1[2], stats=t1[3])
+    torch.cuda.synchronize()
+    assert torch.equal(t0[0].view(torch.int16), y0.view(torch.int16))
+    for a, b in zip(t0, t1):
+        assert torch.equal(b[:T], a) and torch.all(b[T:] == 7.0)
