@@ -163,7 +163,7 @@ def test_layer_gradients_full_size_sampled_rows():
     _check("b2", grads["b2"], d_y.astype(np.float64).sum(axis=0))
 
 
-@pytest.mark.parametrize("cfg,kw", [(0, {}), (2, {"batch": 2, "seq_len": 600})])
+@pytest.mark.parametrize("cfg,kw", [(0, {}), (1, {"batch": 12}), (2, {"batch": 2, "seq_len": 600})])
 def test_saved_activations_path(cfg, kw):
     """hstu_layer_fwd_train gives hstu_layer_fwd's y and U|V|Q|K bit for bit plus the
     attention output in parts (per-head standardised fp16 values and their mean and
