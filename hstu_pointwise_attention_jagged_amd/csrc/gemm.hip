@@ -25,6 +25,13 @@ namespace hstu {
 
 namespace {
 
+// Rows present: min(cap, *m_dev), or cap without m_dev.  The count is read through the
+// constant address space, so it is a scalar load (the first thing every workgroup waits
+// for; a vector load took a full round trip through the vector memory path).
+__device__ __forceinline__ int rows_present(const int32_t *m_dev, int cap) {
+  return m_dev != nullptr ? min(cap, *(const __attribute__((address_space(4))) int32_t *)m_dev) : cap;
+}
+
 constexpr int kBK = 64;          // K per stage
 constexpr int kPitch = kBK + 8;  // LDS row pitch in bf16 (144 bytes: conflict-free 16B reads)
 constexpr int kThreads = 256;
@@ -50,7 +57,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const uint16_t *__res
   const int tile_n = blockIdx.x % n_tiles_n;
   const int tile_m = blockIdx.x / n_tiles_n;
   const int m0 = tile_m * BM, n0 = tile_n * BN;
-  const int M = m_dev != nullptr ? min(M_cap, *m_dev) : M_cap;  // rows present
+  const int M = rows_present(m_dev, M_cap);
   if (m0 >= M) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -209,7 +216,7 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm256_kernel(GemmArgs g) {
   // sharing operand panels share one L2.  The range comes from the rows present, which
   // may be fewer than the grid was sized for: the work then still spreads over every XCD,
   // and the surplus workgroups (the highest slots) exit.
-  const int M = g.m_dev != nullptr ? min(g.M, *g.m_dev) : g.M;  // rows present
+  const int M = rows_present(g.m_dev, g.M);
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
   int split = 0, m0, n0;
   if (g.splits == 1) {
@@ -528,7 +535,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gate_gemm_kernel(GateGemmArgs 
 
   const int N = g.N, K = g.K;
   // XCD-contiguous tile ranges over the tiles present (as gemm256_kernel)
-  const int M = g.m_dev != nullptr ? min(g.M, *g.m_dev) : g.M;  // rows present
+  const int M = rows_present(g.m_dev, g.M);
   const int tiles = min(g.n_tiles_total, (M + kBigTile - 1) / kBigTile * g.n_tiles_n);
   const int per_xcd = (tiles + 7) / 8;
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
@@ -570,16 +577,42 @@ __global__ __launch_bounds__(kBigThreads, 1) void gate_gemm_kernel(GateGemmArgs 
   }
   // the LayerNorm statistics (mean, 1 / std) of the tile's rows from the heads' (mean,
   // variance), into LDS (lanes 0..31 of wave w: row 32 w + lane)
+  // (heads in groups of 8 loads issued together, the first group kept for the second
+  // pass: a loop of one load per head, each waited for in turn, made 16 round trips per
+  // tile before the first MFMA; indices past the last head read the last head again and
+  // are left out of the sums after all 8 are issued)
   if (lane < 32) {
     const int r = m0 + 32 * wave + lane;
     const float2 *srow = g.stats + (int64_t)(r < M ? r : 0) * g.H;
+    float2 st0[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st0[i] = srow[min(i, g.H - 1)];
     float m = 0.f;
-    for (int h = 0; h < g.H; ++h) m += srow[h].x;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m += i < g.H ? st0[i].x : 0.f;
+    for (int h0 = 8; h0 < g.H; h0 += 8) {
+      float2 st[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) st[i] = srow[min(h0 + i, g.H - 1)];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m += h0 + i < g.H ? st[i].x : 0.f;
+    }
     m *= 1.0f / g.H;
     float v = 0.f;
-    for (int h = 0; h < g.H; ++h) {
-      const float2 st = srow[h];
-      v += st.y + (st.x - m) * (st.x - m);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float d = st0[i].x - m;
+      v += i < g.H ? st0[i].y + d * d : 0.f;
+    }
+    for (int h0 = 8; h0 < g.H; h0 += 8) {
+      float2 st[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) st[i] = srow[min(h0 + i, g.H - 1)];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float d = st[i].x - m;
+        v += h0 + i < g.H ? st[i].y + d * d : 0.f;
+      }
     }
     v *= 1.0f / g.H;
     rst[32 * wave + lane] = float2{m, __builtin_amdgcn_rsqf(v + g.eps)};
