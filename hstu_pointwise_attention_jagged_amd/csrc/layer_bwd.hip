@@ -60,7 +60,8 @@ __global__ __launch_bounds__(256) void cast_bf16_kernel(const float *src, uint16
 
 constexpr int kNgRows = 4;  // waves (rows in flight) per workgroup
 
-template <int C>  // float4 chunks per lane (HDV <= 256 * C)
+// C: float4 chunks per lane (HDV <= 256 * C); REBUILD: O comes from cn and the head stats
+template <int C, bool REBUILD>
 __global__ __launch_bounds__(64 * kNgRows) void norm_gate_bwd_kernel(NormGateBwdArgs p) {
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * kNgRows + (threadIdx.x >> 6);
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(64 * kNgRows) void norm_gate_bwd_kernel(NormGateBwd
       const int e = (lane + 64 * c) * 4;
       x[c] = f32x4{0, 0, 0, 0};
       if (e < HDV) {
-        if (p.o != nullptr) {
+        if constexpr (!REBUILD) {
           x[c] = *reinterpret_cast<const f32x4 *>(p.o + (int64_t)row * HDV + e);
         } else {  // the 4 features share a head (dv is a multiple of 32)
           const u32x2 cc = *reinterpret_cast<const u32x2 *>(p.cn + (int64_t)row * HDV + e);
@@ -260,14 +261,20 @@ hipError_t launch_cast_bf16(const float *src, uint16_t *dst, int64_t n, hipStrea
 
 int norm_gate_bwd_waves(int T) { return T < kNgWaves ? ((T + kNgRows - 1) / kNgRows) * kNgRows : kNgWaves; }
 
+template <bool REBUILD>
+static hipError_t launch_ng(const NormGateBwdArgs &a, int blocks, hipStream_t stream) {
+  if (a.hdv <= 256) norm_gate_bwd_kernel<1, REBUILD><<<blocks, 64 * kNgRows, 0, stream>>>(a);
+  else if (a.hdv <= 512) norm_gate_bwd_kernel<2, REBUILD><<<blocks, 64 * kNgRows, 0, stream>>>(a);
+  else if (a.hdv <= 1024) norm_gate_bwd_kernel<4, REBUILD><<<blocks, 64 * kNgRows, 0, stream>>>(a);
+  else norm_gate_bwd_kernel<8, REBUILD><<<blocks, 64 * kNgRows, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_norm_gate_bwd(const NormGateBwdArgs &a, hipStream_t stream) {
   if (a.T <= 0) return hipSuccess;
   const int blocks = norm_gate_bwd_waves(a.T) / kNgRows;
-  if (a.hdv <= 256) norm_gate_bwd_kernel<1><<<blocks, 64 * kNgRows, 0, stream>>>(a);
-  else if (a.hdv <= 512) norm_gate_bwd_kernel<2><<<blocks, 64 * kNgRows, 0, stream>>>(a);
-  else if (a.hdv <= 1024) norm_gate_bwd_kernel<4><<<blocks, 64 * kNgRows, 0, stream>>>(a);
-  else norm_gate_bwd_kernel<8><<<blocks, 64 * kNgRows, 0, stream>>>(a);
-  return hipGetLastError();
+  if (a.o == nullptr) return launch_ng<true>(a, blocks, stream);
+  return launch_ng<false>(a, blocks, stream);
 }
 
 hipError_t launch_colsum(const void *a, bool bf16, int rows, int cols, int64_t stride,
