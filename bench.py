@@ -58,13 +58,17 @@ def file_sha(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
+# the sources the forward layer's kernels (f1, attention, f2 and its operand preparation) are
+# compiled from, with the headers they include and the host code that launches them
+_LAYER_KERNEL_SOURCES = ("attention.hip", "gemm.hip", "common.h", "kernels.h", "api.cpp")
+
+
 def _kernel_sources_sha():
     """sha256 of the kernel sources a counter record describes."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in _LAYER_KERNEL_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
