@@ -750,6 +750,247 @@ __global__ __launch_bounds__(kBigThreads, 1) void gate_gemm_kernel(GateGemmArgs 
   }
 }
 
+// The same product for rows of at most kGateTabHeads heads, with the per-head LayerNorm
+// coefficients (a_h, b_h) of the tile's rows computed once per tile into an LDS table
+// (fp16 pairs) instead of being loaded and derived per staged chunk.  That
+// leaves two loads per chunk (c and U, by buffer loads whose stage and row group ride in the
+// scalar offset, so the per-lane offsets are two registers), and the registers it frees
+// double-buffer the operand fragments as in gemm256_kernel: the fragments of k-step ks + 1
+// are read while the MFMAs of k-step ks run.  Rows past M read as zero (buffer range) and
+// form zero rows of G, which only reach output rows that are not stored.  The arithmetic of
+// a, b and G is that of gate_gemm_kernel, so both give the same bits.
+constexpr int kGateTabHeads = 16;
+
+template <bool AFF>
+__global__ __launch_bounds__(kBigThreads, 1) void gate_gemm_tab_kernel(GateGemmArgs g) {
+  constexpr int TM = 64, TN = 128;  // wave tile: tokens x features
+  constexpr int MT = TM / 32, NT = TN / 32;
+  constexpr int STAGE = kBigTile * kBigBK * 2;             // bytes of one operand stage
+  constexpr int SEGS = STAGE / 1024 / (kBigThreads / 64);  // 1 KB W segments per wave
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  unsigned char *xs = smem;                        // G stages
+  unsigned char *wsm = smem + kBigStages * STAGE;  // W stages
+  __shared__ h2 gbt[kGateTableBytes / 4];              // gamma | beta, fp16
+  // (a_h, b_h) fp16 of head h and tile row r = 32 w + l + 8 j (l < 8, j < 4) at
+  // h 256 + 32 w + 4 l + j: the four rows a lane stages in one stage are one 16-byte read
+  __shared__ __attribute__((aligned(16))) uint32_t abt[kGateTabHeads * kBigTile];
+  // an fp16 result that overflows clamps to +-65504 (G saturates instead of turning inf)
+  __builtin_amdgcn_s_setreg((0 << 11) | (23 << 6) | 1, 1);
+
+  const int N = g.N, K = g.K, H = g.H;
+  // XCD-contiguous tile ranges over the tiles present (as gemm256_kernel)
+  const int M = rows_present(g.m_dev, g.M);
+  const int tiles = min(g.n_tiles_total, (M + kBigTile - 1) / kBigTile * g.n_tiles_n);
+  const int per_xcd = (tiles + 7) / 8;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int lin = xcd * per_xcd + slot;
+  if (slot >= per_xcd || lin >= tiles) return;
+  const int tile_n = lin % g.n_tiles_n;
+  const int tile_m = lin / g.n_tiles_n;
+  const int m0 = tile_m * kBigTile, n0 = tile_n * kBigTile;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 3, wn = wave >> 2;
+  const int rows = min(kBigTile, M - m0);
+
+  // the heads' statistics of row 32 w + lane (lanes 0..31 of wave w), all loads issued at once
+  float2 st[kGateTabHeads];
+  if (lane < 32) {
+    const int r = m0 + 32 * wave + lane;
+    const float2 *srow = g.stats + (int64_t)(r < M ? r : 0) * H;
+#pragma unroll
+    for (int i = 0; i < kGateTabHeads; ++i) st[i] = srow[min(i, H - 1)];
+  }
+
+  const __amdgpu_buffer_rsrc_t wr = uniform_rsrc(g.w + (int64_t)n0 * K, min(kBigTile, N - n0) * K * 2);
+  const int lrow8 = lane / kCPR, lchunk = lane % kCPR;
+  auto issue_w = [&](int kt) {
+    const int stage = kt % kBigStages, k0 = kt * kBigBK;
+#pragma unroll
+    for (int j = 0; j < SEGS; ++j) {
+      const int seg = j * 8 + wave;
+      const int r = seg * (64 / kCPR) + lrow8;
+      const int c = lchunk ^ ((r >> 1) & 7);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, wsm + stage * STAGE + seg * 1024, 16,
+                                               (r * K + k0 + c * 8) * 2, 0, 0, 0);
+    }
+  };
+
+  // Staging of G: wave w forms rows 32 w .. 32 w + 31 of the tile; lane l takes 16-byte
+  // chunk l % 8 (8 features of one head, dv >= 32) of rows 32 w + l / 8 + 8 j, j = 0..3.
+  // The lane's offsets cover row 32 w + l / 8; row group j and the stage go in the scalar
+  // offset.
+  const int gc = lane & 7;
+  const int grl = 32 * wave + (lane >> 3);
+  const int ustride = (int)g.u_stride;
+  const __amdgpu_buffer_rsrc_t cr = uniform_rsrc(g.c + (int64_t)m0 * K, rows * K * 2);
+  const __amdgpu_buffer_rsrc_t ur = uniform_rsrc(g.u + (int64_t)m0 * g.u_stride, rows * ustride * 2);
+  const int cvo = (grl * K + 8 * gc) * 2, uvo = (grl * ustride + 8 * gc) * 2;
+  u32x4 cv[4], uv[4];
+  // c and U of chunk j of this lane for stage kt: exactly two load instructions, issued by
+  // every lane, so that the waits in the k loop can count them
+  auto load_chunk = [&](int kt, int j) {
+    const int so = kt * kBigBK * 2;
+    cv[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(cr, cvo, so + j * 8 * K * 2, 0));
+    uv[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ur, uvo, so + j * 8 * ustride * 2, 0));
+  };
+#pragma unroll
+  for (int j = 0; j < 4; ++j) load_chunk(0, j);
+  issue_w(0);
+
+  if constexpr (AFF) {
+    for (int i = tid; i < K; i += kBigThreads) gbt[i] = h2{g.gb[i], g.gb[K + i]};
+  }
+  // LayerNorm of the row from its heads' (mean, variance), then each head's (a_h, b_h)
+  if (lane < 32) {
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < kGateTabHeads; ++i) m += i < H ? st[i].x : 0.f;
+    m *= 1.0f / H;
+    float v = 0.f;
+#pragma unroll
+    for (int i = 0; i < kGateTabHeads; ++i) {
+      const float d = st[i].x - m;
+      v += i < H ? st[i].y + d * d : 0.f;
+    }
+    v *= 1.0f / H;
+    const float rstd = __builtin_amdgcn_rsqf(v + g.eps);
+    const int slot = 32 * wave + 4 * (lane & 7) + (lane >> 3);  // row 32 w + lane
+#pragma unroll
+    for (int i = 0; i < kGateTabHeads; ++i)
+      if (i < H) abt[i * kBigTile + slot] = pack_f16(__builtin_amdgcn_sqrtf(st[i].y) * rstd, (st[i].x - m) * rstd);
+  }
+
+  // (a, b) of this lane's four rows for the head of its chunk in a stage; hb, kmod: the
+  // head of the stage's first feature and that feature's place in it (a stage's 64
+  // features cross at most one head boundary, since dv is a multiple of 32)
+  // (the stage past the last, whose G is formed and never read, clamps to the last head)
+  auto read_ab = [&](int hb, int kmod) {
+    const int h = min(hb + (kmod + 8 * gc >= g.dv ? 1 : 0), H - 1);
+    return *reinterpret_cast<const u32x4 *>(abt + h * kBigTile + 32 * wave + 4 * (lane >> 3));
+  };
+  // G of chunk j of this lane for stage kt (registers -> LDS), ab: the row's (a, b)
+  auto store_chunk = [&](int kt, int j, uint32_t abw) {
+    const int stage = kt % kBigStages, f0 = kt * kBigBK + 8 * gc;
+    const int r = grl + 8 * j;
+    const h2 ab = __builtin_bit_cast(h2, abw);
+    const h2 a2 = {ab[0], ab[0]}, b2 = {ab[1], ab[1]};
+    uint32_t out[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t ce = cv[j][e], ue = uv[j][e];
+      h2 t = __builtin_elementwise_fma(__builtin_bit_cast(h2, ce), a2, b2);
+      if constexpr (AFF) {
+        const h2 gb = gbt[f0 + 2 * e], gb1 = gbt[f0 + 2 * e + 1];
+        t = __builtin_elementwise_fma(t, h2{gb[0], gb1[0]}, h2{gb[1], gb1[1]});
+      }
+      out[e] = __builtin_bit_cast(uint32_t, t * __builtin_bit_cast(h2, ue));
+    }
+    *reinterpret_cast<u32x4 *>(xs + stage * STAGE + swz(r, gc)) = u32x4{out[0], out[1], out[2], out[3]};
+  };
+
+  f32x16 acc[NT][MT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i)
+#pragma unroll
+    for (int j = 0; j < MT; ++j) acc[i][j] = f32x16{};
+
+  // Pipeline as gate_gemm_kernel with two loads per chunk: W of stage kt + 1 goes out at the
+  // top of iteration kt; chunk j of stage kt + 1 is formed after k-step j's fragment reads
+  // of stage kt, from registers loaded one iteration earlier, and refilled at once with the
+  // same chunk of stage kt + 2.  Past the last stage the loads repeat the last stage and the
+  // G / W writes go to the free buffer, so the wait counts are exact.
+  constexpr int NGL = 8;  // loads of one stage's four chunks
+  const int nk = K / kBigBK;
+  const int dv = g.dv;
+  __syncthreads();  // the (a, b) and gamma / beta tables
+  {
+    const u32x4 ab0 = read_ab(0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      store_chunk(0, j, ab0[j]);
+      load_chunk(min(1, nk - 1), j);
+    }
+  }
+  // head and in-head offset of the first feature of stage 1
+  int hb1 = kBigBK / dv, kmod1 = kBigBK - hb1 * dv;
+
+  const int lrow = lane & 31, lk = lane >> 5;
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vmcnt<NGL>();
+    __syncthreads();  // every wave's G of stage kt is in LDS; stage kt - 1 is free
+    issue_w(min(kt + 1, nk - 1));
+    const u32x4 ab1 = read_ab(hb1, kmod1);  // for the G of stage kt + 1
+    const unsigned char *xst = xs + (kt % kBigStages) * STAGE;
+    const unsigned char *wst = wsm + (kt % kBigStages) * STAGE;
+    f16x8 wf[2][NT], xf[2][MT];
+    auto read_frags = [&](int ks, int set) __attribute__((always_inline)) {
+      const int c = ks * 2 + lk;
+#pragma unroll
+      for (int i = 0; i < NT; ++i)
+        wf[set][i] = as_f16x8(*reinterpret_cast<const u32x4 *>(wst + swz(wn * TN + i * 32 + lrow, c)));
+#pragma unroll
+      for (int j = 0; j < MT; ++j)
+        xf[set][j] = as_f16x8(*reinterpret_cast<const u32x4 *>(xst + swz(wm * TM + j * 32 + lrow, c)));
+    };
+    read_frags(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < kBigBK / 16; ++ks) {
+      if (ks + 1 < kBigBK / 16) read_frags(ks + 1, (ks + 1) & 1);
+      // chunk ks of stage kt + 1 was loaded one iteration ago; 10 loads followed it (the
+      // other chunks of its stage, W of stage kt + 1, this stage's refills before it);
+      // nothing that uses chunk ks's registers may be scheduled above its wait
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<NGL + SEGS - 2>();
+      store_chunk(kt + 1, ks, ab1[ks]);
+      load_chunk(min(kt + 2, nk - 1), ks);
+#pragma unroll
+      for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int j = 0; j < MT; ++j) acc[i][j] = mfma32_f16(wf[ks & 1][i], xf[ks & 1][j], acc[i][j]);
+    }
+    // the next stage's first feature
+    kmod1 += kBigBK;
+    while (kmod1 >= dv) {
+      kmod1 -= dv;
+      ++hb1;
+    }
+  }
+  wait_vmcnt<0>();  // the repeated last-stage loads land before LDS is reused below
+
+  // epilogue through LDS, whole-row bf16 stores (as gemm256_kernel)
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < MT; ++j) {
+    const int r = wm * TM + j * 32 + lrow;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = wn * TN + i * 32 + 8 * q + 4 * lk;
+        float v0 = acc[i][j][4 * q + 0], v1 = acc[i][j][4 * q + 1];
+        float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+        if (g.bias != nullptr && n0 + c < N) {
+          const f32x4 bb = *reinterpret_cast<const f32x4 *>(g.bias + n0 + c);
+          v0 += bb[0]; v1 += bb[1]; v2 += bb[2]; v3 += bb[3];
+        }
+        *reinterpret_cast<u32x2 *>(smem + r * kOutPitch + c * 2) = u32x2{pack_bf16(v0, v1), pack_bf16(v2, v3)};
+      }
+    }
+  }
+  __syncthreads();
+  constexpr int kRowChunks = kBigTile * 2 / 16;
+#pragma unroll
+  for (int it = 0; it < kBigTile * kRowChunks / kBigThreads; ++it) {
+    const int ch = it * kBigThreads + tid;
+    const int r = ch / kRowChunks, c16 = ch % kRowChunks;
+    if (m0 + r < M && n0 + c16 * 8 < N) {
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(smem + r * kOutPitch + c16 * 16);
+      *reinterpret_cast<u32x4 *>(g.out + (int64_t)(m0 + r) * N + n0 + c16 * 8) = v;
+    }
+  }
+}
+
 // W2 (bf16) -> fp16, and gamma / beta (fp32, either may be absent: 1 / 0) -> fp16 [2][K].
 __global__ __launch_bounds__(256) void gate_prep_kernel(const uint16_t *__restrict__ w2, int64_t n_w,
                                                         const float *__restrict__ gamma,
@@ -799,15 +1040,22 @@ hipError_t launch_gate_gemm(const GateGemmArgs &a, bool affine, hipStream_t stre
   const int grid = (g.n_tiles_total + 7) / 8 * 8;
   const size_t lds = gate_gemm_lds_bytes(a.K);
   // the attribute allows the largest table (K = 2048); each launch asks for what it needs
-  static bool attr_set[2] = {false, false};
-  auto fn = affine ? (const void *)gate_gemm_kernel<true> : (const void *)gate_gemm_kernel<false>;
-  if (!attr_set[affine]) {
+  // the table kernel for rows of at most kGateTabHeads heads, else per-chunk statistics
+  const bool tab = a.H <= kGateTabHeads;
+  static bool attr_set[2][2] = {{false, false}, {false, false}};
+  const void *fn = tab ? (affine ? (const void *)gate_gemm_tab_kernel<true> : (const void *)gate_gemm_tab_kernel<false>)
+                       : (affine ? (const void *)gate_gemm_kernel<true> : (const void *)gate_gemm_kernel<false>);
+  if (!attr_set[tab][affine]) {
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)gate_gemm_lds_bytes(2048));  // fixed size
     if (e != hipSuccess) return e;
-    attr_set[affine] = true;
+    attr_set[tab][affine] = true;
   }
-  if (affine)
+  if (tab && affine)
+    gate_gemm_tab_kernel<true><<<dim3(grid), dim3(kBigThreads), lds, stream>>>(g);
+  else if (tab)
+    gate_gemm_tab_kernel<false><<<dim3(grid), dim3(kBigThreads), lds, stream>>>(g);
+  else if (affine)
     gate_gemm_kernel<true><<<dim3(grid), dim3(kBigThreads), lds, stream>>>(g);
   else
     gate_gemm_kernel<false><<<dim3(grid), dim3(kBigThreads), lds, stream>>>(g);

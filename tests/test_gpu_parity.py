@@ -338,6 +338,21 @@ def test_layer_ragged_with_empty_sequences():
     _layer_check(wl.random_layer(5, [0, 1, 127, 128, 129, 0, 300, 2], dims, bias=True), tag="ragged")
 
 
+@pytest.mark.parametrize("heads,dh,affine", [
+    (16, 32, False),  # the most heads of the LDS coefficient table; two heads per 64 features
+    (3, 64, True),    # an odd head count, with gamma and beta
+    (18, 32, True),   # more heads than the table holds: per-chunk statistics
+    (24, 64, False),
+])
+def test_layer_head_counts(heads, dh, affine):
+    """The f2 kernel takes a row's LayerNorm from its heads' statistics, from an LDS table
+    of per-head coefficients (up to 16 heads) or per staged chunk (more heads); two row
+    tiles, the second ragged."""
+    dims = wl.LayerDims(d_model=128, num_heads=heads, dqk=dh, dv=dh)
+    _layer_check(wl.random_layer(11 + heads, [300, 5, 129], dims, affine=affine),
+                 tag=f"heads={heads} dh={dh} affine={affine}")
+
+
 def test_layer_zipf_config():
     _layer_check(wl.config(1))
 
