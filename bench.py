@@ -58,7 +58,7 @@ def file_sha(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-# the sources the forward layer's kernels (f1, attention, f2 and its operand preparation) are
+# the sources the forward layer's kernels (f1 with the f2 operand preparation, attention, f2) are
 # compiled from, with the headers they include and the host code that launches them
 _LAYER_KERNEL_SOURCES = ("attention.hip", "gemm.hip", "common.h", "kernels.h", "api.cpp")
 
@@ -90,11 +90,11 @@ def _layer_kernels():
     n1 = 2 * H * 2 * dh
     f1, att, f2 = useful_flops([8192] * 8, d, H, dh, dh)
     return [
-        ("f1 GEMM + SiLU", "gemm256_kernel<0, 0, 1, 1>", f1, 2 * (T * d + n1 * d + T * n1)),
+        # f1 with the f2 operand conversion in its tail (w2 read as bf16, written as fp16)
+        ("f1 GEMM + SiLU", "gemm256_kernel<0, 0, 1, 1>", f1, 2 * (T * d + n1 * d + T * n1) + 2 * 2 * d * H * dh),
         ("attention", "attn_kernel<128, 0, 4", att, 2 * 3 * T * H * dh + 2 * T * H * dh + 8 * T * H),
         ("f2 GEMM with LayerNorm + gate", "gate_gemm_kernel", f2,
          2 * 2 * T * H * dh + 8 * T * H + 2 * d * H * dh + 2 * T * d),
-        ("f2 operand preparation", "gate_prep_kernel", 0, 2 * 2 * d * H * dh),
     ]
 
 

@@ -269,13 +269,17 @@ hstu_status_t run_layer(const hstu_dims_t *d, const hstu_weights_t *w, const hst
   const bool affine = w->ln_gamma != nullptr || w->ln_beta != nullptr;
   // T may be a capacity: the GEMMs read the true row count, seq_offsets[B], on the device
   const int32_t *t_dev = s->seq_offsets + s->batch;
+  // f1, with the f2 operand conversion (w2, gamma, beta to fp16) riding along
+  W2Prep prep;
+  prep.w2 = w->w2;
+  prep.n_w = (int64_t)d->d_model * hdv;
+  prep.gamma = w->ln_gamma;
+  prep.beta = w->ln_beta;
+  prep.K = hdv;
+  prep.w2h = lw.w2h;
+  prep.gb = affine ? reinterpret_cast<_Float16 *>(lw.gb) : nullptr;
   e = timed(1, st, [&] {
-    return launch_gemm(x, w->w1, w->b1, uvqk, T, n1, d->d_model, ACT_SILU, OUT_F16, st, t_dev);
-  });
-  if (e != hipSuccess) return hip_fail(e);
-  e = timed(3, st, [&] {
-    return launch_gate_prep(w->w2, (int64_t)d->d_model * hdv, w->ln_gamma, w->ln_beta, hdv, lw.w2h,
-                            affine ? lw.gb : nullptr, st);
+    return launch_gemm(x, w->w1, w->b1, uvqk, T, n1, d->d_model, ACT_SILU, OUT_F16, st, t_dev, &prep);
   });
   if (e != hipSuccess) return hip_fail(e);
   const int64_t cap = attn_work_capacity(s->batch, T);

@@ -194,6 +194,28 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | (15 << 8) | (7 << 4) | (N & 15));
 }
 
+// Item i of the f2 operand conversion: 8 values of w2 (bf16 -> fp16) and entry i of the
+// gamma | beta table.  The caller has set MODE.FP16_OVFL (values past the fp16 range clamp
+// to +-65504, as in the f2 kernel).
+__device__ __forceinline__ void gate_prep_item(const W2Prep &q, int64_t i) {
+  if (i * 8 < q.n_w) {
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(q.w2 + i * 8);
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[e] = pack_f16(__builtin_bit_cast(float, v[e] << 16), __builtin_bit_cast(float, v[e] & 0xffff0000u));
+    *reinterpret_cast<u32x4 *>(q.w2h + i * 8) = o;
+  }
+  if (q.gb != nullptr && i < q.K) {
+    q.gb[i] = (_Float16)(q.gamma != nullptr ? q.gamma[i] : 1.0f);
+    q.gb[q.K + i] = (_Float16)(q.beta != nullptr ? q.beta[i] : 0.0f);
+  }
+}
+
+__host__ __device__ inline int64_t gate_prep_work(const W2Prep &q) {
+  return std::max<int64_t>((q.n_w + 7) / 8, q.K);
+}
+
 // Operand layouts: KC, the operand's rows are the output's rows (or columns) and K is
 // contiguous (X [M][K], W [N][K]); KR, the operand's rows are K (X [K][M], W [K][N]).
 // A KC stage is [256 rows][64 k] read with 16-byte reads; a KR stage is the natural
@@ -206,6 +228,18 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm256_kernel(GemmArgs g) {
   constexpr int STAGE = kBigTile * kBigBK * 2;  // bytes of one operand stage (32 KB)
   constexpr int SEGS = STAGE / 1024 / (kBigThreads / 64);  // 1 KB segments per wave
   static_assert(OUT != OUT_F32 || ACT == ACT_NONE, "fp32 output is a plain product");
+  if constexpr (ACT == ACT_SILU) {
+    // workgroups past the product's grid: the f2 operand conversion (W2Prep); they are
+    // dispatched after every tile of the product, so they run in its tail
+    if ((int)blockIdx.x >= g.prep.grid_gemm) {
+      __builtin_amdgcn_s_setreg((0 << 11) | (23 << 6) | 1, 1);  // MODE.FP16_OVFL
+      const int64_t work = gate_prep_work(g.prep);
+      for (int64_t i = (int64_t)((int)blockIdx.x - g.prep.grid_gemm) * kBigThreads + threadIdx.x; i < work;
+           i += (int64_t)g.prep.blocks * kBigThreads)
+        gate_prep_item(g.prep, i);
+      return;
+    }
+  }
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   unsigned char *xs = smem;                       // [kBigStages][STAGE]
   unsigned char *wsm = smem + kBigStages * STAGE;  // [kBigStages][STAGE]
@@ -477,6 +511,13 @@ hipError_t launch_big(GemmArgs a, hipStream_t stream) {
     grid = 8 * ((tm + xm - 1) / xm) * (a.n_tiles_n / a.xcd_n);
   } else {
     grid = (a.n_tiles_total * a.splits + 7) / 8 * 8;
+  }
+  a.prep.grid_gemm = grid;
+  if (ACT == ACT_SILU && a.prep.w2h != nullptr) {
+    // the f2 operand conversion: up to 64 more workgroups, about 4 items per thread
+    const int64_t work = gate_prep_work(a.prep);
+    a.prep.blocks = (int)std::min<int64_t>(64, std::max<int64_t>(1, (work + 4 * kBigThreads - 1) / (4 * kBigThreads)));
+    grid += a.prep.blocks;
   }
   // operand stages (2 operands each), reused for the output tile in the epilogue
   const size_t lds = std::max(2 * (size_t)kBigStages * kBigTile * kBigBK * 2,
@@ -991,26 +1032,10 @@ __global__ __launch_bounds__(kBigThreads, 1) void gate_gemm_tab_kernel(GateGemmA
   }
 }
 
-// W2 (bf16) -> fp16, and gamma / beta (fp32, either may be absent: 1 / 0) -> fp16 [2][K].
-__global__ __launch_bounds__(256) void gate_prep_kernel(const uint16_t *__restrict__ w2, int64_t n_w,
-                                                        const float *__restrict__ gamma,
-                                                        const float *__restrict__ beta, int K,
-                                                        uint16_t *__restrict__ w2h,
-                                                        _Float16 *__restrict__ gb) {
+// The f2 operand conversion as its own launch, one item per thread.
+__global__ __launch_bounds__(256) void gate_prep_kernel(W2Prep q) {
   __builtin_amdgcn_s_setreg((0 << 11) | (23 << 6) | 1, 1);  // saturate, as the f2 kernel
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i * 8 < n_w) {
-    const u32x4 v = *reinterpret_cast<const u32x4 *>(w2 + i * 8);
-    u32x4 o;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      o[e] = pack_f16(__builtin_bit_cast(float, v[e] << 16), __builtin_bit_cast(float, v[e] & 0xffff0000u));
-    *reinterpret_cast<u32x4 *>(w2h + i * 8) = o;
-  }
-  if (gb != nullptr && i < K) {
-    gb[i] = (_Float16)(gamma != nullptr ? gamma[i] : 1.0f);
-    gb[K + i] = (_Float16)(beta != nullptr ? beta[i] : 0.0f);
-  }
+  gate_prep_item(q, (int64_t)blockIdx.x * 256 + threadIdx.x);
 }
 
 }  // namespace
@@ -1023,9 +1048,16 @@ size_t gate_gemm_lds_bytes(int K) {
 
 hipError_t launch_gate_prep(const uint16_t *w2, int64_t n_w, const float *gamma, const float *beta,
                             int K, uint16_t *w2h, uint16_t *gb, hipStream_t stream) {
-  const int64_t work = std::max<int64_t>((n_w + 7) / 8, K);
-  gate_prep_kernel<<<dim3((unsigned)((work + 255) / 256)), 256, 0, stream>>>(
-      w2, n_w, gamma, beta, K, w2h, reinterpret_cast<_Float16 *>(gb));
+  W2Prep q;
+  q.w2 = w2;
+  q.n_w = n_w;
+  q.gamma = gamma;
+  q.beta = beta;
+  q.K = K;
+  q.w2h = w2h;
+  q.gb = reinterpret_cast<_Float16 *>(gb);
+  const int64_t work = gate_prep_work(q);
+  gate_prep_kernel<<<dim3((unsigned)((work + 255) / 256)), 256, 0, stream>>>(q);
   return hipGetLastError();
 }
 
@@ -1064,8 +1096,14 @@ hipError_t launch_gate_gemm(const GateGemmArgs &a, bool affine, hipStream_t stre
 
 hipError_t launch_gemm(const uint16_t *A, const uint16_t *W, const float *bias, uint16_t *out,
                        int M, int N, int K, Act act, OutType out_type, hipStream_t stream,
-                       const int32_t *m_dev) {
-  if (M == 0) return hipSuccess;
+                       const int32_t *m_dev, const W2Prep *prep) {
+  // the f2 operand conversion in its own launch, after the product
+  auto prep_alone = [&](hipError_t e) {
+    if (e != hipSuccess || prep == nullptr || prep->w2h == nullptr) return e;
+    return launch_gate_prep(prep->w2, prep->n_w, prep->gamma, prep->beta, prep->K, prep->w2h,
+                            reinterpret_cast<uint16_t *>(prep->gb), stream);
+  };
+  if (M == 0) return prep_alone(hipSuccess);
   if (K > kGemmMaxK) return hipErrorInvalidValue;  // 32-bit offsets within a 256-row panel
   const bool big = (N % kBigTile) == 0 && M >= kBigTile;
   const bool wide = (N % 128) == 0;
@@ -1085,19 +1123,22 @@ hipError_t launch_gemm(const uint16_t *A, const uint16_t *W, const float *bias, 
   a.n_tiles_n = N / kBigTile;
   a.n_tiles_total = (M + kBigTile - 1) / kBigTile * a.n_tiles_n;
   if (act == ACT_SILU && out_type == OUT_F16) {
-    if (big) return launch_big<KC, KC, ACT_SILU, OUT_F16>(a, stream);
-    return wide ? launch_tile<128, 128, ACT_SILU, OUT_F16>(A, W, bias, out, M, N, K, stream, m_dev)
-                : launch_tile<128, 64, ACT_SILU, OUT_F16>(A, W, bias, out, M, N, K, stream, m_dev);
+    if (big) {
+      if (prep != nullptr) a.prep = *prep;
+      return launch_big<KC, KC, ACT_SILU, OUT_F16>(a, stream);
+    }
+    return prep_alone(wide ? launch_tile<128, 128, ACT_SILU, OUT_F16>(A, W, bias, out, M, N, K, stream, m_dev)
+                           : launch_tile<128, 64, ACT_SILU, OUT_F16>(A, W, bias, out, M, N, K, stream, m_dev));
   }
   if (act == ACT_NONE && out_type == OUT_F16) {  // pre-activations (the backward's recompute)
-    if (big) return launch_big<KC, KC, ACT_NONE, OUT_F16>(a, stream);
-    return wide ? launch_tile<128, 128, ACT_NONE, OUT_F16>(A, W, bias, out, M, N, K, stream, m_dev)
-                : launch_tile<128, 64, ACT_NONE, OUT_F16>(A, W, bias, out, M, N, K, stream, m_dev);
+    if (big) return prep_alone(launch_big<KC, KC, ACT_NONE, OUT_F16>(a, stream));
+    return prep_alone(wide ? launch_tile<128, 128, ACT_NONE, OUT_F16>(A, W, bias, out, M, N, K, stream, m_dev)
+                           : launch_tile<128, 64, ACT_NONE, OUT_F16>(A, W, bias, out, M, N, K, stream, m_dev));
   }
   if (act == ACT_NONE && out_type == OUT_BF16) {
-    if (big) return launch_big<KC, KC, ACT_NONE, OUT_BF16>(a, stream);
-    return wide ? launch_tile<128, 128, ACT_NONE, OUT_BF16>(A, W, bias, out, M, N, K, stream, m_dev)
-                : launch_tile<128, 64, ACT_NONE, OUT_BF16>(A, W, bias, out, M, N, K, stream, m_dev);
+    if (big) return prep_alone(launch_big<KC, KC, ACT_NONE, OUT_BF16>(a, stream));
+    return prep_alone(wide ? launch_tile<128, 128, ACT_NONE, OUT_BF16>(A, W, bias, out, M, N, K, stream, m_dev)
+                           : launch_tile<128, 64, ACT_NONE, OUT_BF16>(A, W, bias, out, M, N, K, stream, m_dev));
   }
   return hipErrorInvalidValue;
 }

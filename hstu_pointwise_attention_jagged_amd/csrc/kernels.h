@@ -17,6 +17,22 @@ enum Layout { KC = 0, KR = 1 };
 // C[M][N] = sum_k X(m, k) W(n, k) (+ bias[n], activation): X(m, k) = x[m ldx + k] (KC) or
 // x[k ldx + m] (KR), likewise W with ldw.  With splits > 1, split s sums k in
 // [s k_split, (s + 1) k_split) into its own [M][N] fp32 slice of out.
+// The f2 operand conversion, w2 (bf16, n_w values) -> fp16 w2h and gamma / beta (fp32,
+// either may be nullptr: 1 / 0) -> fp16 gb [2][K] when gb is not nullptr.  Given to the
+// f1 launch_gemm, it runs as extra workgroups of the same launch (large tiles: they are
+// dispatched after every tile of the product and finish in its tail) or as its own launch
+// right after the product (small tiles).
+struct W2Prep {
+  const uint16_t *w2 = nullptr;
+  int64_t n_w = 0;
+  const float *gamma = nullptr, *beta = nullptr;
+  int K = 0;
+  uint16_t *w2h = nullptr;  // nullptr: nothing to convert
+  _Float16 *gb = nullptr;
+  int blocks = 0;     // set by the launcher: workgroups of the conversion
+  int grid_gemm = 0;  // set by the launcher: workgroups below this one run the product
+};
+
 struct GemmArgs {
   const uint16_t *x;
   int64_t ldx;
@@ -29,6 +45,7 @@ struct GemmArgs {
   int k_split, splits;
   int n_tiles_n, n_tiles_total;
   int xcd_n;                // set by the launcher: XCDs along the feature tiles
+  W2Prep prep;              // f1 only: the f2 operand conversion as a side job
 };
 
 // Largest reduction width of launch_gemm: a 256-row operand panel (256 K bf16 values)
@@ -38,10 +55,11 @@ constexpr int kGemmMaxK = 1 << 21;
 // out[M][N] = act(A[M][K] . W[N][K]^T + bias[N]): bf16 inputs, fp32 accumulation, output
 // bf16 or fp16 (saturated to the finite range).  Requires K % 64 == 0, N % 64 == 0.
 // With m_dev (device), only rows below min(M, *m_dev) are computed and written: M is then
-// a capacity and the true row count is read on the device.
+// a capacity and the true row count is read on the device.  With prep, the f2 operand
+// conversion runs beside the product (see W2Prep).
 hipError_t launch_gemm(const uint16_t *A, const uint16_t *W, const float *bias, uint16_t *out,
                        int M, int N, int K, Act act, OutType out_type, hipStream_t stream,
-                       const int32_t *m_dev = nullptr);
+                       const int32_t *m_dev = nullptr, const W2Prep *prep = nullptr);
 
 // Backward products with fp32 output, bf16 operands, fixed summation order:
 // NN  out[M][N] = X[M][K] . W[K][N]     (X rows of ldx, W rows of ldw; K % 64 == 0)

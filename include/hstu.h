@@ -395,9 +395,10 @@ int hstu_last_hip_error(void);
  * of a selected kernel is bracketed by two events on its stream; the durations are
  * collected by hstu_profile_collect, which synchronises the events.  Each event pair adds
  * a little time between launches, so a timed run can select only the kernel it reports.
- * Kernel ids: 0 schedule and key-block timestamp ranges, 1 f1 GEMM, 2 attention,
- * 3 f2 operand preparation (w2, gamma, beta to fp16), 4 f2 GEMM with the LayerNorm and
- * the U gate formed in its operand staging.                                         */
+ * Kernel ids: 0 schedule and key-block timestamp ranges, 1 f1 GEMM (with the f2 operand
+ * preparation, w2, gamma and beta to fp16, that runs in the same launch or right after
+ * it), 2 attention, 3 reserved (no launch records under it), 4 f2 GEMM with the
+ * LayerNorm and the U gate formed in its operand staging.                            */
 void hstu_profile_enable(int on);
 void hstu_profile_reset(void);
 /* Adds up finished records: total_ms[k] and launches[k] for k in [0, 5).           */
