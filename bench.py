@@ -93,7 +93,7 @@ def _layer_kernels():
         # f1 with the f2 operand conversion in its tail (w2 read as bf16, written as fp16)
         ("f1 GEMM + SiLU", "gemm256_kernel<0, 0, 1, 1>", f1, 2 * (T * d + n1 * d + T * n1) + 2 * 2 * d * H * dh),
         ("attention", "attn_kernel<128, 0, 4", att, 2 * 3 * T * H * dh + 2 * T * H * dh + 8 * T * H),
-        ("f2 GEMM with LayerNorm + gate", "gate_gemm_kernel", f2,
+        ("f2 GEMM with LayerNorm + gate", "gate_gemm_tab_kernel", f2,
          2 * 2 * T * H * dh + 8 * T * H + 2 * d * H * dh + 2 * T * d),
     ]
 
