@@ -650,9 +650,9 @@ def main():
         write_counter_record(args.counter_record, args.copy_bytes or (1 << 30))
         return
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); the jagged batch would "
-              "shard by sequence with no exchange across GPUs, which this build does not run.",
-              file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); the library has no "
+              "multi-GPU path (the jagged batch would shard by sequence, with no exchange across "
+              "GPUs).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
