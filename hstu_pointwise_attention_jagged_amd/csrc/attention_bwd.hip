@@ -68,11 +68,14 @@ __device__ __forceinline__ u32x2 tr_read(const unsigned char *p) {
 }
 
 // LDS pitches: row copies (16-byte fragment reads of one chunk across 32 rows) and
-// transposed-read copies (4 rows x 4 feature groups per 16 lanes)
+// transposed-read copies.  LDS has 64 four-byte banks and a transposing read serves 32
+// lanes at a time: 4 rows x 64 bytes, so the rows' pitch must step 16 banks (mod 64) for
+// the 4 rows to fall on distinct banks (a pitch of 16 banks plus a multiple of 64).
 template <int DH>
 struct BwdLayout {
   static constexpr int ROWP = DH * 2 + 16;
-  static constexpr int TRP = DH * 2 + 32;
+  static constexpr int TRP = DH * 2 + (DH == 32 ? 0 : 64);
+  static_assert((TRP / 4) % 64 == 16 || (TRP / 4) % 64 == 48, "transposed-read pitch");
   static constexpr int KS = DH / 16;   // k-steps over the head dimension
   static constexpr int FT = DH / 32;   // 32-wide feature tiles
   static constexpr int CPR = DH / 8;   // 16-byte chunks per row
@@ -643,8 +646,10 @@ __global__ __launch_bounds__(1024) void tri_base_kernel(const int32_t *offsets, 
 
 // A stored block in LDS: its two 1 KB halves (the dK/dV kernel's lanes 0..63, 16 bytes
 // each) at kDsHalf bytes apart, lanes 32..63 of a half 64 bytes further on, so that the
-// transposing reads below fall on distinct banks.
-constexpr int kDsHalf = 1088;
+// transposing reads below fall on distinct banks: the reads of lanes 0..15 cover banks
+// 0..31 of one half, those of lanes 16..31 the same pattern in the other half, which
+// kDsHalf (288 banks, 32 mod 64) moves onto banks 32..63.
+constexpr int kDsHalf = 1152;
 constexpr int kDsBlock = 2 * kDsHalf;
 __device__ __forceinline__ int ds_lds_offset(int piece) {  // 16-byte piece of the 2 KB block
   const int half = piece >> 6, L = piece & 63;
