@@ -353,6 +353,21 @@ def test_layer_head_counts(heads, dh, affine):
                  tag=f"heads={heads} dh={dh} affine={affine}")
 
 
+@pytest.mark.parametrize("keep", ["gamma", "beta"])
+@pytest.mark.parametrize("lengths", [[5, 17, 32, 64], [300, 5, 129]])
+def test_layer_gamma_or_beta_alone(keep, lengths):
+    """LayerNorm with only gamma or only beta (the other 1 or 0): the f2 operand conversion
+    runs after the small-tile f1 (first batch, 118 rows) or in the tail of the large-tile f1
+    launch (second, 434 rows)."""
+    dims = wl.LayerDims(d_model=128, num_heads=2, dqk=64, dv=64)
+    w = wl.random_layer(21, lengths, dims, affine=True)
+    if keep == "gamma":
+        w.weights.ln_beta = None
+    else:
+        w.weights.ln_gamma = None
+    _layer_check(w, tag=f"{keep} only")
+
+
 def test_layer_zipf_config():
     _layer_check(wl.config(1))
 
