@@ -294,6 +294,33 @@ def _kernel_ms(torch, ops, fn, reps=3):
     return {n: round(v[0] / v[1], 4) for n, v in k.items() if v[1]}
 
 
+def attention_by_layer(torch, ops, dims, layer_w, seq, x0, stream, every=4):
+    """The stack's layers run one call at a time (outside the timed region): for every
+    `every`-th layer, the attention launch's time, the shader clock during it and the
+    standard deviation of the layer's input.  With no residual path the activations shrink
+    layer by layer, and the attention's clock rises as its operands draw less power."""
+    rows = []
+    x = x0
+    for l, wt in enumerate(layer_w):
+        keep = l % every == 0 or l == len(layer_w) - 1
+        if keep:
+            torch.cuda.synchronize()
+            ops.profile_reset()
+            ops.profile_enable(True, kernels=["attention"])
+        y, _ = ops.hstu_layer_fwd(dims, wt, seq, x, stream=stream)
+        if keep:
+            torch.cuda.synchronize()
+            ops.profile_enable(False)
+            ms, n = ops.profile_collect()["attention"]
+            rows.append({"layer": l, "attention_ms": round(ms / max(n, 1), 4),
+                         "clock_ghz": round(ops.profile_clock_ghz(), 3),
+                         "input_std": float(f"{float(x.float().std()):.3g}")})
+            ops.profile_reset()
+        x = y
+    torch.cuda.synchronize()
+    return rows
+
+
 def zipf_measure(torch, np, ops, dev, wl, layers=24, reps=20):
     """The 64-user batch (lengths truncated Zipf s = 1.2 on [16, 1024], d = 256, 4 heads of
     64): one layer alone and a stack of `layers` layers in one call, useful FLOPs as for
@@ -719,10 +746,11 @@ def main():
     elapsed = time.perf_counter() - t0
     ops.profile_enable(False)
     kern = ops.profile_collect()
-    clock_ghz = ops.profile_clock_ghz()  # shader clock during the last attention launch
+    clock_ghz = ops.profile_clock_ghz()  # average shader clock over the timed attention launches
     ops.profile_reset()
     # the other kernels' averages from one more step, outside the timed region
     per_kernel = _kernel_ms(torch, ops, step, reps=1)
+    by_layer = attention_by_layer(torch, ops, dims, layer_w, seq, x0, stream)
 
     lengths = w.seq.lengths.tolist()
     f1, att, f2 = useful_flops(lengths, d.d_model, d.num_heads, d.dqk, d.dv)
@@ -771,6 +799,7 @@ def main():
                      "peak_at_measured_clock": round(PEAK_FLOP_PER_CLOCK * clock_ghz / 1e3, 1) if clock_ghz else None,
                      "frac_at_measured_clock": (round(achieved / (PEAK_FLOP_PER_CLOCK * clock_ghz / 1e3), 4)
                                                 if clock_ghz else None)},
+        "attention_by_layer": by_layer,
         "cpu_baseline": None,
         "host": platform.node(),
     }

@@ -747,8 +747,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel(AttnArgs p) {
   }
   if (p.clk != nullptr && blockIdx.x < kClockSlots && threadIdx.x == 0) {
     const uint64_t clk1 = __builtin_amdgcn_s_memtime(), rt1 = __builtin_amdgcn_s_memrealtime();
-    p.clk[2 * blockIdx.x] = clk1 - clk0;
-    p.clk[2 * blockIdx.x + 1] = rt1 - rt0;
+    // added up over launches (one writer per slot and launch, launches in stream order)
+    p.clk[2 * blockIdx.x] += clk1 - clk0;
+    p.clk[2 * blockIdx.x + 1] += rt1 - rt0;
   }
 }
 

@@ -118,7 +118,7 @@ struct AttnArgs {
   const int32_t *n_work;    // [1]
   int num_heads;
   int mask;                 // 0 causal, 1 self-only
-  // profiling only, or nullptr: workgroup w < kClockSlots writes the core-clock and the
+  // profiling only, or nullptr: workgroup w < kClockSlots adds the core-clock and the
   // 100 MHz real-time ticks of its lifetime to clk[2 w], clk[2 w + 1]
   uint64_t *clk;
 };

@@ -573,8 +573,8 @@ def profile_collect() -> dict:
 
 
 def profile_clock_ghz() -> float:
-    """Shader clock (GHz) during the last attention launch made inside a layer while
-    profiling was enabled, 0.0 if none (include/hstu.h)."""
+    """Average shader clock (GHz) over the attention launches made inside a layer while
+    profiling was enabled since the last profile_reset, 0.0 if none (include/hstu.h)."""
     lib = _lib.load()
     v = ctypes.c_double(0.0)
     _raise(lib.hstu_profile_clock_ghz(ctypes.byref(v)), "hstu_profile_clock_ghz")

@@ -404,10 +404,10 @@ void hstu_profile_reset(void);
 /* Adds up finished records: total_ms[k] and launches[k] for k in [0, 5).           */
 hstu_status_t hstu_profile_collect(double *total_ms, int64_t *launches);
 const char *hstu_kernel_name(int kernel_id);
-/* Average shader (core) clock in GHz over the lifetime of the first 64 workgroups of the
- * last attention launch that ran inside a layer while the attention (id 2) was profiled (the core
- * clock counter against the 100 MHz real-time counter), 0 if none since the last
- * hstu_profile_reset.  Synchronises the device.                                       */
+/* Average shader (core) clock in GHz over the lifetimes of the first 64 workgroups of
+ * every attention launch that ran inside a layer while the attention (id 2) was profiled
+ * since the last hstu_profile_reset (the core clock counter against the 100 MHz real-time
+ * counter, both added up over those launches), 0 if none.  Synchronises the device.   */
 hstu_status_t hstu_profile_clock_ghz(double *ghz);
 
 #ifdef __cplusplus
