@@ -407,7 +407,9 @@ const char *hstu_kernel_name(int kernel_id);
 /* Average shader (core) clock in GHz over the lifetimes of the first 64 workgroups of
  * every attention launch that ran inside a layer while the attention (id 2) was profiled
  * since the last hstu_profile_reset (the core clock counter against the 100 MHz real-time
- * counter, both added up over those launches), 0 if none.  Synchronises the device.   */
+ * counter, both added up over those launches), 0 if none.  The sums are plain adds: two
+ * profiled attention launches running at once on different streams may lose samples.
+ * Synchronises the device.                                                            */
 hstu_status_t hstu_profile_clock_ghz(double *ghz);
 
 #ifdef __cplusplus
