@@ -2,8 +2,9 @@
 
 Every HIP source is compiled with packed-FP32 instruction selection disabled
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``); the objects are linked into
-``libhstu.so`` next to this file, where the Python binding loads it from.  The library
-links rocBLAS (the plain GEMMs of the layer backward).
+``libhstu.so`` next to this file, where the Python binding loads it from.  Every
+product, forward and backward, runs on the library's own kernels: it links the HIP
+runtime only.
 """
 
 from __future__ import annotations

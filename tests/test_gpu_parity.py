@@ -393,9 +393,19 @@ def test_layer_stochastic_length_batch_sampled_rows():
     w.x = w.raw.x[kept]
     lens = np.diff(new_off)
     say(f"[sl] kept T={new_off[-1]} of {w.raw.seq.total}; full users={int(np.sum(lens > 776))}")
+    # every kept user: its first and last row and one row in between; the longest user
+    # also at every 128-row tile boundary
+    rng = np.random.default_rng(3)
+    rows = set()
+    for b in range(len(lens)):
+        if lens[b] == 0:
+            continue
+        a, e = int(new_off[b]), int(new_off[b + 1])
+        rows |= {a, e - 1, int(a + rng.integers(0, e - a))}
     b_long = int(np.argmax(lens))
-    rows = [int(new_off[b_long]), int(new_off[b_long + 1] - 1), int(new_off[5] + 3), int(new_off[-1] - 1)]
-    _layer_check(w, rows=rows, tag="stochastic length")
+    for t in range(0, int(lens[b_long]), 128):
+        rows |= {int(new_off[b_long] + t), int(min(new_off[b_long] + t + 127, new_off[b_long + 1] - 1))}
+    _layer_check(w, rows=sorted(rows), tag=f"stochastic length, {len(rows)} rows of every kept user")
 
 
 def test_layer_deterministic_and_guard_band():
