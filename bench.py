@@ -346,9 +346,12 @@ def zipf_measure(torch, np, ops, dev, wl, layers=24, reps=20):
 
     one()
     stack()
+    stack()
     torch.cuda.synchronize()
-    layer_ms = _events_ms(torch, stream, one, reps)
-    stack_ms = _events_ms(torch, stream, stack, max(reps // 4, 3))
+    # medians over three timed groups: a call this short is easily disturbed by one slow
+    # launch (a 9 ms stack among 1.7 ms ones has been seen once)
+    layer_ms = float(np.median([_events_ms(torch, stream, one, reps) for _ in range(3)]))
+    stack_ms = float(np.median([_events_ms(torch, stream, stack, max(reps // 4, 3)) for _ in range(3)]))
     f1, att, f2 = useful_flops(w.seq.lengths.tolist(), d.d_model, d.num_heads, d.dqk, d.dv)
     fl = f1 + att + f2
     return {"workload": f"{w.seq.batch} users, lengths truncated Zipf s=1.2 on [16, 1024] "
